@@ -1,0 +1,216 @@
+/* csa.h -- C ABI of libcsa: compressed sparse attention (CSA) and heavily
+ * compressed attention (HCA) on one AMD Instinct MI355X (gfx950).
+ *
+ * The method (DeepSeek-V4 hybrid attention) as the public pages describe it:
+ *   - CSA compresses every m tokens' key/value pairs into one entry, scores
+ *     the entries against the query with a light FP4 "lightning indexer",
+ *     keeps the top-k and attends only over those (blog.nickys.cn DeepSeek-V4
+ *     post, section 三大架构改动 §1 CSA; "DeepSeek-V4 技术分析报告", §3 架构层);
+ *   - HCA compresses every m' >> m tokens into one entry and attends densely
+ *     over all entries (blog.nickys.cn, 三大架构改动 §2 HCA);
+ *   - both add an uncompressed sliding-window branch so each token fully sees
+ *     its nearest neighbours (sz-guanghua.com.cn ifanr repost, 百萬長上下文);
+ *   - the indexer's query-key path is MXFP4 ("DeepSeek V4技术揭秘", §一);
+ *   - the KV cache mixes BF16 and FP8 ("DeepSeek-V4 技术分析报告", 工程层).
+ * The pooling rule and the indexer score formula are not given on the pages;
+ * this library fixes them as documented on each call.
+ *
+ * Conventions for every call
+ *   - Every pointer argument is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees or synchronizes; work is enqueued on
+ *     `stream` (a hipStream_t; NULL = the default stream) and runs
+ *     asynchronously.
+ *   - Arrays are dense, row-major, last dimension innermost, unless a
+ *     leading-dimension argument says otherwise.
+ *   - head dimension d must be 128.
+ *   - bf16 values are raw bit patterns (uint16); fp8 values are OCP E4M3FN
+ *     codes (uint8; 0x7F/0xFF = NaN are never produced and must not be fed).
+ *   - MXFP4 (OCP MX v1.0): E2M1 codes, two per byte, element 2i in the LOW
+ *     nibble of byte i; one E8M0 scale byte per 32 consecutive elements
+ *     (value 2^(e-127); 0xFF = NaN must not be fed).
+ *   - Positions: query i of sequence b sits at absolute position
+ *     q_pos0[b] + i.  Compressed entry e (block size m) covers positions
+ *     [e*m, (e+1)*m) and is visible to position t iff e < floor((t+1)/m).
+ *     Row r of a raw window buffer holds position raw_pos0[b] + r.
+ *   - Argument errors return CSA_EINVAL (unsupported but well-formed
+ *     combinations CSA_ENOTSUP) before anything is enqueued and leave every
+ *     output untouched.  A HIP launch error returns CSA_EHIP.  Conditions
+ *     that depend on device-resident data (positions) cannot be checked on
+ *     the host; they are documented as preconditions per call.
+ *   - Results are bitwise reproducible run to run: work splits depend only
+ *     on the shape arguments and every reduction has a fixed order.
+ *   - The library keeps no state; calls on different streams may overlap
+ *     provided their outputs and workspaces do not alias.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_EINVAL = 1,     /* invalid argument (shape, pointer, enum)          */
+  CSA_ENOTSUP = 2,    /* valid but unsupported combination               */
+  CSA_EHIP = 3,       /* HIP runtime error while enqueueing               */
+  CSA_EWORKSPACE = 4  /* workspace missing or smaller than required       */
+} csa_status_t;
+
+typedef enum {
+  CSA_BF16 = 0,       /* bf16 bit patterns                                 */
+  CSA_F32 = 1,        /* IEEE fp32                                         */
+  CSA_FP8_E4M3 = 2    /* OCP E4M3FN codes + one fp32 scale per entry       */
+} csa_dtype_t;
+
+typedef enum {
+  CSA_OP_TOPK = 0,
+  CSA_OP_SPARSE_ATTN = 1,
+  CSA_OP_DENSE_ATTN = 2
+} csa_op_t;
+
+/* ---------------------------------------------------------------------
+ * csa_compress_kv -- pool each complete block of m tokens into one entry.
+ *
+ * Passage: every m tokens' key/value pairs become one entry, so the sequence
+ * shrinks to 1/m (blog.nickys.cn, 三大架构改动 §1 CSA); HCA uses the same
+ * operation with a far larger block m' (§2 HCA).
+ * Pooling rule (fixed by this library): one scalar logit z per token, shared
+ * by K and V; for block e, a_j = softmax(z[e*m .. e*m+m-1])_j and
+ *   k_out[e] = sum_j a_j * k[e*m + j],  v_out[e] = sum_j a_j * v[e*m + j],
+ * accumulated in fp32.  Storage: CSA_BF16 (round to nearest even),
+ * CSA_F32, or CSA_FP8_E4M3 with per-entry scale = amax/448 (1 if amax == 0)
+ * and code = RNE_e4m3(x / scale) saturated at +-448, separately for K and V.
+ *
+ *   k, v        [B, ld_in, d] in in_dtype (CSA_BF16 or CSA_F32); rows 0..L-1
+ *               of each sequence are pooled
+ *   logits      [B, ld_in] fp32
+ *   L           tokens to pool per sequence; L % m == 0; L <= ld_in
+ *   k_out,v_out [B, ld_out, d] in out_dtype; entries 0..L/m-1 are written
+ *   k_scale_out, v_scale_out  [B, ld_out] fp32; required iff out_dtype is
+ *               CSA_FP8_E4M3, ignored otherwise
+ * Pointers may be offset by the caller to pool a tail (e.g. the block just
+ * completed during decoding) into any entry slot.
+ * ------------------------------------------------------------------- */
+csa_status_t csa_compress_kv(const void* k, const void* v, int32_t in_dtype,
+                             const float* logits, int32_t B, int32_t L, int32_t ld_in,
+                             int32_t d, int32_t m, void* k_out, void* v_out,
+                             float* k_scale_out, float* v_scale_out, int32_t ld_out,
+                             int32_t out_dtype, void* stream);
+
+/* ---------------------------------------------------------------------
+ * csa_indexer_scores -- lightning-indexer relevance of every compressed entry.
+ *
+ * Passage: the indexer scores each query token against each compressed block
+ * in FP4 (sz-guanghua.com.cn ifanr repost, 百萬長上下文); MXFP4 on the
+ * indexer's query-key path ("DeepSeek V4技术揭秘", §一).
+ * Score (fixed by this library):
+ *   scores[b,i,e] = sum_h w[b,i,h] * max(0, q[b,i,h,:] . kx[b,e,:])
+ * for e < nvis = floor((t+1)/m), t = q_pos0[b] + i; -inf for nvis <= e < cap.
+ * Products of MXFP4 values are exact; sums are fp32.
+ *
+ *   q_codes [B, T_q, H_I, d_I/2] u8     q_e8m0 [B, T_q, H_I, d_I/32] u8
+ *   w       [B, T_q, H_I] fp32
+ *   k_codes [B, cap, d_I/2] u8          k_e8m0 [B, cap, d_I/32] u8
+ *   q_pos0  [B] int32 (device)
+ *   scores  [B, T_q, cap] fp32 (output)
+ * Limits: H_I in {4, 8, 16}; d_I a multiple of 32, 32 <= d_I <= 512.
+ * Precondition: nvis(t) <= cap (entries at or past cap are taken as absent).
+ * ------------------------------------------------------------------- */
+csa_status_t csa_indexer_scores(const uint8_t* q_codes, const uint8_t* q_e8m0,
+                                const float* w, const uint8_t* k_codes,
+                                const uint8_t* k_e8m0, const int32_t* q_pos0, int32_t B,
+                                int32_t T_q, int32_t H_I, int32_t d_I, int32_t cap,
+                                int32_t m, float* scores, void* stream);
+
+/* ---------------------------------------------------------------------
+ * csa_topk -- keep the k most relevant visible entries per query.
+ *
+ * Passage: keep the k compressed entries most relevant to the query
+ * (blog.nickys.cn, 三大架构改动 §1 CSA).
+ * Rule (fixed by this library): candidates are e < min(nvis(t), cap);
+ * larger score first, equal scores (with -0 == +0) by lower index; the first
+ * min(k, candidates) are written in ASCENDING index order, then -1 up to k.
+ *
+ *   scores [B, T_q, cap] fp32 (NaN must not occur)
+ *   idx    [B, T_q, k] int32 (output)
+ *   ws, ws_bytes  workspace of csa_workspace_size(CSA_OP_TOPK, ...) bytes
+ *                 (may be NULL when that size is 0)
+ * ------------------------------------------------------------------- */
+csa_status_t csa_topk(const float* scores, const int32_t* q_pos0, int32_t B, int32_t T_q,
+                      int32_t cap, int32_t m, int32_t k, int32_t* idx, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * csa_sparse_attn -- attention over the selected entries plus the window.
+ *
+ * Passage: attention runs only over the k selected compressed entries, with a
+ * few uncompressed sliding-window entries kept as well (blog.nickys.cn,
+ * 三大架构改动 §1 CSA; "DeepSeek-V4 技术分析报告", 滑动窗口分支).
+ * For each query (t) and head h, one softmax over the union (no de-duplication)
+ *   { sm * q[h].ck[e] : e in idx[b,i,:], e >= 0 } U
+ *   { sm * q[h].k_win[p - raw_pos0] : max(0, t-W+1) <= p <= t }
+ * and out = sum p * value.  All H query heads share the single KV head.
+ * An empty key set gives out = 0, lse = -inf.
+ *
+ *   q        [B, T_q, H, d] in io_dtype (CSA_BF16 or CSA_F32)
+ *   ck, cv   [B, cap, d] compressed entries in ckv_dtype (BF16, F32 or
+ *            FP8_E4M3 with ck_scale, cv_scale [B, cap] fp32)
+ *   idx      [B, T_q, k] int32, -1 = empty slot (csa_topk output)
+ *   k_win, v_win [B, L_raw, d] raw tokens in io_dtype
+ *   raw_pos0 [B], q_pos0 [B] int32 (device)
+ *   sm_scale logit scale (pass 1/sqrt(d) for the usual choice)
+ *   out      [B, T_q, H, d] in io_dtype;  lse [B, T_q, H] fp32 or NULL
+ *   ws       workspace of csa_workspace_size(CSA_OP_SPARSE_ATTN, B, T_q, H, d, k + W)
+ *            bytes, zero-filled ONCE after allocation; every call leaves it
+ *            zero-filled again.  Calls that share a workspace must be ordered.
+ * Limits: H a multiple of 16 in [16, 128]; W >= 0; k >= 1.
+ * Preconditions: idx entries are -1 or in [0, cap); the raw buffer covers
+ * window(t) (rows outside [0, L_raw) are skipped).
+ * ------------------------------------------------------------------- */
+csa_status_t csa_sparse_attn(const void* q, int32_t io_dtype, const void* ck, const void* cv,
+                             const float* ck_scale, const float* cv_scale, int32_t ckv_dtype,
+                             int32_t cap, const int32_t* idx, int32_t k, const void* k_win,
+                             const void* v_win, const int32_t* raw_pos0, int32_t L_raw,
+                             const int32_t* q_pos0, int32_t W, int32_t B, int32_t T_q,
+                             int32_t H, int32_t d, float sm_scale, void* out, float* lse,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * hca_dense_attn -- attention over ALL visible compressed entries + window.
+ *
+ * Passage: HCA makes no sparse selection and attends densely over every
+ * compressed entry (blog.nickys.cn, 三大架构改动 §2 HCA); the window branch as
+ * for CSA (sz-guanghua.com.cn ifanr repost, 百萬長上下文).
+ * Key set for query t: entries e < min(floor((t+1)/m_prime), cap) and
+ * window(t); otherwise exactly as csa_sparse_attn.
+ * ws: csa_workspace_size(CSA_OP_DENSE_ATTN, B, T_q, H, d, cap + W) bytes, same
+ * zero-fill contract as csa_sparse_attn.
+ * ------------------------------------------------------------------- */
+csa_status_t hca_dense_attn(const void* q, int32_t io_dtype, const void* ck, const void* cv,
+                            const float* ck_scale, const float* cv_scale, int32_t ckv_dtype,
+                            int32_t cap, int32_t m_prime, const void* k_win, const void* v_win,
+                            const int32_t* raw_pos0, int32_t L_raw, const int32_t* q_pos0,
+                            int32_t W, int32_t B, int32_t T_q, int32_t H, int32_t d,
+                            float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Workspace bytes a call needs.  n_keys = k + W (CSA) or cap + W (HCA);
+ * for CSA_OP_TOPK pass T_q and n_keys = cap.  Returns 0 when none is needed
+ * and (size_t)-1 for invalid arguments. */
+size_t csa_workspace_size(int32_t op, int32_t B, int32_t T_q, int32_t H, int32_t d,
+                          int32_t n_keys);
+
+/* Static text for a status code. */
+const char* csa_status_str(int32_t status);
+
+/* ABI version (major*100 + minor). */
+int32_t csa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H */

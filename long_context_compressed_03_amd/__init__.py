@@ -1,0 +1,220 @@
+"""Python binding of libcsa (CSA / HCA compressed attention for MI355X, gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of libcsa.so,
+called through its C ABI (include/csa.h).  torch provides device memory and
+the current stream.  There is no fallback: if the library is not built or no
+GPU is present, the calls raise.
+
+Tensor conventions
+  bf16   torch.bfloat16 (or int16/uint16 holding the bit patterns)
+  f32    torch.float32
+  fp8    torch.uint8 / torch.float8_e4m3fn holding OCP E4M3FN codes
+  MXFP4  torch.uint8: packed E2M1 codes (low nibble first) and E8M0 scales
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcsa.so")
+
+CSA_OK, CSA_EINVAL, CSA_ENOTSUP, CSA_EHIP, CSA_EWORKSPACE = range(5)
+CSA_BF16, CSA_F32, CSA_FP8_E4M3 = 0, 1, 2
+CSA_OP_TOPK, CSA_OP_SPARSE_ATTN, CSA_OP_DENSE_ATTN = 0, 1, 2
+DTYPES = {"bf16": CSA_BF16, "f32": CSA_F32, "fp8": CSA_FP8_E4M3}
+
+EXPORTS = ["csa_compress_kv", "csa_indexer_scores", "csa_topk", "csa_sparse_attn",
+           "hca_dense_attn", "csa_workspace_size", "csa_status_str", "csa_abi_version"]
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+
+
+class CsaError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+def load(path=LIB_PATH):
+    """Load libcsa.so and declare the C signatures.  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m long_context_compressed_03_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.csa_compress_kv.argtypes = [_P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P]
+    lib.csa_indexer_scores.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]
+    lib.csa_topk.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _S, _P]
+    lib.csa_sparse_attn.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _P, _I, _P, _P, _P, _I, _P, _I,
+                                    _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
+    lib.hca_dense_attn.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _P, _I,
+                                   _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
+    for fn in ["csa_compress_kv", "csa_indexer_scores", "csa_topk", "csa_sparse_attn",
+               "hca_dense_attn"]:
+        getattr(lib, fn).restype = _I
+    lib.csa_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
+    lib.csa_workspace_size.restype = _S
+    lib.csa_status_str.argtypes = [_I]
+    lib.csa_status_str.restype = ctypes.c_char_p
+    lib.csa_abi_version.argtypes = []
+    lib.csa_abi_version.restype = _I
+    _lib = lib
+    return lib
+
+
+def status_str(status):
+    return load().csa_status_str(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != CSA_OK:
+        raise CsaError(fn, status)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dt_of(t):
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return CSA_BF16
+    if t.dtype == torch.float32:
+        return CSA_F32
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return CSA_FP8_E4M3
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+# ---------------------------------------------------------------- calls --
+
+def csa_compress_kv(k, v, logits, m, k_out, v_out, k_scale_out=None, v_scale_out=None, L=None,
+                    row0=0, entry0=0, stream=None):
+    """Pool every complete block of m rows of k/v [B, ld_in, 128] into k_out/v_out [B, ld_out, 128].
+
+    Rows row0 .. row0+L-1 of each sequence are pooled into entries entry0 .. entry0+L/m-1
+    (default: all ld_in rows into entries from 0).  Output storage type follows k_out's
+    dtype (bf16, f32, or uint8 = fp8 with per-entry scales in k_scale_out/v_scale_out
+    [B, ld_out]).
+    """
+    B, ld_in, d = k.shape
+    ld_out = k_out.shape[1]
+    L = ld_in - row0 if L is None else L
+    if row0 < 0 or entry0 < 0 or row0 + L > ld_in or entry0 + L // max(m, 1) > ld_out:
+        raise ValueError("row or entry range outside the buffers")
+    out_dt = _dt_of(k_out)
+
+    def off(t, n):
+        return None if t is None else ctypes.c_void_p(_ptr(t).value + n * t.element_size())
+    st = load().csa_compress_kv(off(k, row0 * d), off(v, row0 * d), _dt_of(k), off(logits, row0),
+                                B, L, ld_in, d, m, off(k_out, entry0 * d), off(v_out, entry0 * d),
+                                off(k_scale_out, entry0), off(v_scale_out, entry0), ld_out, out_dt,
+                                _stream(stream))
+    _check("csa_compress_kv", st)
+
+
+def csa_indexer_scores(q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, m, scores=None, stream=None):
+    """Indexer scores [B, T_q, cap] fp32 for MXFP4 queries [B,T_q,H_I,d_I/2] and keys [B,cap,d_I/2]."""
+    B, T_q, H_I, half = q_codes.shape
+    cap = k_codes.shape[1]
+    if scores is None:
+        scores = torch.empty((B, T_q, cap), dtype=torch.float32, device=q_codes.device)
+    st = load().csa_indexer_scores(_ptr(q_codes), _ptr(q_e8m0), _ptr(w), _ptr(k_codes),
+                                   _ptr(k_e8m0), _ptr(q_pos0), B, T_q, H_I, 2 * half, cap, m,
+                                   _ptr(scores), _stream(stream))
+    _check("csa_indexer_scores", st)
+    return scores
+
+
+def csa_topk(scores, q_pos0, m, k, idx=None, stream=None):
+    """Top-k visible entries per query row: idx [B, T_q, k] int32, ascending, -1 padded."""
+    B, T_q, cap = scores.shape
+    if idx is None:
+        idx = torch.empty((B, T_q, k), dtype=torch.int32, device=scores.device)
+    ws = _workspace(scores.device, load().csa_workspace_size(CSA_OP_TOPK, B, T_q, 0, 128, cap))
+    st = load().csa_topk(_ptr(scores), _ptr(q_pos0), B, T_q, cap, m, k, _ptr(idx), _ws_ptr(ws),
+                         _ws_len(ws), _stream(stream))
+    _check("csa_topk", st)
+    return idx
+
+
+_WS = {}
+
+
+def _workspace(device, nbytes):
+    """Zero-filled, cached per device and grown on demand (the kernels keep it zero)."""
+    if nbytes == ctypes.c_size_t(-1).value:
+        raise CsaError("csa_workspace_size", CSA_EINVAL)
+    if nbytes == 0:
+        return None
+    key = (device.type, device.index)
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        _WS[key] = buf
+    return buf
+
+
+def _ws_ptr(ws):
+    return None if ws is None else ctypes.c_void_p(ws.data_ptr())
+
+
+def _ws_len(ws):
+    return 0 if ws is None else ws.numel()
+
+
+def _attn_common(q, ck, ck_scale, out, lse):
+    B, T_q, H, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    return B, T_q, H, d, out
+
+
+def csa_sparse_attn(q, ck, cv, idx, k_win, v_win, raw_pos0, q_pos0, W, ck_scale=None,
+                    cv_scale=None, sm_scale=None, out=None, lse=None, stream=None):
+    """CSA attention over idx-selected compressed entries plus window(t)."""
+    B, T_q, H, d, out = _attn_common(q, ck, ck_scale, out, lse)
+    k = idx.shape[-1]
+    cap = ck.shape[1]
+    sm = d ** -0.5 if sm_scale is None else sm_scale
+    lib = load()
+    ws = _workspace(q.device, lib.csa_workspace_size(CSA_OP_SPARSE_ATTN, B, T_q, H, d, k + W))
+    st = lib.csa_sparse_attn(_ptr(q), _dt_of(q), _ptr(ck), _ptr(cv), _ptr(ck_scale),
+                             _ptr(cv_scale), _dt_of(ck), cap, _ptr(idx), k, _ptr(k_win),
+                             _ptr(v_win), _ptr(raw_pos0), k_win.shape[1], _ptr(q_pos0), W, B,
+                             T_q, H, d, sm, _ptr(out), _ptr(lse), _ws_ptr(ws), _ws_len(ws),
+                             _stream(stream))
+    _check("csa_sparse_attn", st)
+    return out
+
+
+def hca_dense_attn(q, ck, cv, m_prime, k_win, v_win, raw_pos0, q_pos0, W, ck_scale=None,
+                   cv_scale=None, sm_scale=None, out=None, lse=None, stream=None):
+    """HCA attention over all visible compressed entries plus window(t)."""
+    B, T_q, H, d, out = _attn_common(q, ck, ck_scale, out, lse)
+    cap = ck.shape[1]
+    sm = d ** -0.5 if sm_scale is None else sm_scale
+    lib = load()
+    ws = _workspace(q.device, lib.csa_workspace_size(CSA_OP_DENSE_ATTN, B, T_q, H, d, cap + W))
+    st = lib.hca_dense_attn(_ptr(q), _dt_of(q), _ptr(ck), _ptr(cv), _ptr(ck_scale),
+                            _ptr(cv_scale), _dt_of(ck), cap, m_prime, _ptr(k_win), _ptr(v_win),
+                            _ptr(raw_pos0), k_win.shape[1], _ptr(q_pos0), W, B, T_q, H, d, sm,
+                            _ptr(out), _ptr(lse), _ws_ptr(ws), _ws_len(ws), _stream(stream))
+    _check("hca_dense_attn", st)
+    return out

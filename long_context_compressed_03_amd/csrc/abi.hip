@@ -1,0 +1,31 @@
+// Host-only entry points of the C ABI: workspace sizing, status text, version.
+#include "common.hpp"
+
+size_t csa_attn_workspace_size(long rows, int H, int n_list);
+
+extern "C" size_t csa_workspace_size(int32_t op, int32_t B, int32_t T_q, int32_t H, int32_t d, int32_t n_keys) {
+  if (B < 0 || T_q < 0 || n_keys < 0) return size_t(-1);
+  switch (op) {
+    case CSA_OP_TOPK:
+      return 0;
+    case CSA_OP_SPARSE_ATTN:
+    case CSA_OP_DENSE_ATTN:
+      if (d != kHeadDim || H < 16 || H > 128 || H % 16 != 0) return size_t(-1);
+      return csa_attn_workspace_size(long(B) * T_q, H, n_keys);
+    default:
+      return size_t(-1);
+  }
+}
+
+extern "C" const char* csa_status_str(int32_t status) {
+  switch (status) {
+    case CSA_OK: return "CSA_OK";
+    case CSA_EINVAL: return "CSA_EINVAL: invalid argument";
+    case CSA_ENOTSUP: return "CSA_ENOTSUP: unsupported combination";
+    case CSA_EHIP: return "CSA_EHIP: HIP runtime error";
+    case CSA_EWORKSPACE: return "CSA_EWORKSPACE: workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int32_t csa_abi_version(void) { return 100; }

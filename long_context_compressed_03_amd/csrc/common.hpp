@@ -1,0 +1,120 @@
+// Shared device helpers for the gfx950 (CDNA4) kernels of libcsa.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/csa.h"
+
+#define CSA_DEV __device__ __forceinline__
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kHeadDim = 128;
+
+// ----------------------------------------------------------------- bf16 --
+CSA_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// Round fp32 to the nearest bf16, ties to even (finite inputs).
+CSA_DEV uint16_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// --------------------------------------------------------- fp8 E4M3FN --
+// Decode an OCP E4M3FN code (not NaN) to fp32.  Every E4M3 value is also an
+// exact bf16 value (3 mantissa bits, exponents -9 .. 8).
+CSA_DEV float e4m3_to_f32(uint32_t c) {
+  uint32_t s = (c & 0x80u) << 24;
+  uint32_t e = (c >> 3) & 0xFu;
+  uint32_t mnt = c & 7u;
+  float mag;
+  if (e == 0) {
+    mag = float(mnt) * 0.001953125f;  // mnt * 2^-9
+  } else {
+    mag = __uint_as_float(((e + 120u) << 23) | (mnt << 20));  // 2^(e-7) * (1 + mnt/8)
+  }
+  return __uint_as_float(__float_as_uint(mag) | s);
+}
+
+// Round fp32 to E4M3FN, nearest-even, saturating at +-448.
+CSA_DEV uint32_t f32_to_e4m3(float x) {
+  uint32_t s = (__float_as_uint(x) >> 24) & 0x80u;
+  float a = fabsf(x);
+  uint32_t code;
+  if (a >= 448.f) {
+    code = 0x7Eu;
+  } else if (a < 0.015625f) {               // below 2^-6: subnormal grid 2^-9
+    code = uint32_t(__builtin_rintf(a * 512.f));  // 0..8; 8 == smallest normal code
+  } else {
+    int e = int((__float_as_uint(a) >> 23) & 0xFFu) - 127;  // -6 .. 8
+    float sc = a * __uint_as_float(uint32_t(127 + 3 - e) << 23);  // a * 2^(3-e) in [8, 16)
+    uint32_t r = uint32_t(__builtin_rintf(sc));                   // 8 .. 16
+    if (r == 16u) { r = 8u; e += 1; }
+    code = (uint32_t(e + 7) << 3) | (r - 8u);
+    if (code > 0x7Eu) code = 0x7Eu;
+  }
+  return code | s;
+}
+
+// ------------------------------------------------------ wave reductions --
+CSA_DEV float wave_max_xor(float v, int lane_mask) { return fmaxf(v, __shfl_xor(v, lane_mask)); }
+
+template <int kLanes>
+CSA_DEV float group_max(float v) {
+#pragma unroll
+  for (int o = kLanes / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+template <int kLanes>
+CSA_DEV float group_sum(float v) {
+#pragma unroll
+  for (int o = kLanes / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Block-wide exclusive prefix sum of one uint32 per thread (blockDim.x a
+// multiple of 64, at most 1024).  `smem` needs blockDim.x/64 + 1 words.
+// Returns the exclusive prefix; *total receives the block sum.
+CSA_DEV uint32_t block_exclusive_scan(uint32_t v, uint32_t* smem, uint32_t* total) {
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) smem[wid] = incl;
+  __syncthreads();
+  if (wid == 0) {
+    uint32_t x = lane < nw ? smem[lane] : 0u;
+    uint32_t xi = x;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      uint32_t t = __shfl_up(xi, o);
+      if (lane >= o) xi += t;
+    }
+    if (lane < nw) smem[lane] = xi - x;  // exclusive wave offsets
+    if (lane == nw - 1) smem[16] = xi;
+  }
+  __syncthreads();
+  uint32_t r = smem[wid] + incl - v;
+  *total = smem[16];
+  __syncthreads();
+  return r;
+}
+
+// --------------------------------------------------------------- status --
+#define CSA_CHECK_LAUNCH()                                   \
+  do {                                                       \
+    if (hipGetLastError() != hipSuccess) return CSA_EHIP;    \
+  } while (0)
+
+static inline bool csa_dtype_ok(int32_t dt) { return dt == CSA_BF16 || dt == CSA_F32 || dt == CSA_FP8_E4M3; }

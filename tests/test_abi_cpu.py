@@ -1,0 +1,120 @@
+"""The C-ABI library loads, exports every declared call, and rejects bad arguments on the host.
+
+No GPU is needed: argument validation returns before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+LIB = os.path.join(ROOT, "long_context_compressed_03_amd", "libcsa.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libcsa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa_\w+|hca_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    import long_context_compressed_03_amd as csa
+    lib = ctypes.CDLL(LIB)
+    names = declared_functions()
+    assert {"csa_compress_kv", "csa_indexer_scores", "csa_topk", "csa_sparse_attn",
+            "hca_dense_attn"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(csa.EXPORTS)
+
+
+def test_status_strings_and_version():
+    import long_context_compressed_03_amd as csa
+    lib = csa.load()
+    assert lib.csa_abi_version() == 100
+    for s in range(5):
+        assert lib.csa_status_str(s).decode().startswith("CSA_")
+
+
+def _p(x=0x1000):
+    return ctypes.c_void_p(x)
+
+
+def test_compress_rejects_bad_arguments():
+    import long_context_compressed_03_amd as csa
+    lib = csa.load()
+    ok = dict(k=_p(), v=_p(), in_dt=0, lg=_p(), B=2, L=8, ld_in=8, d=128, m=4, ko=_p(), vo=_p(),
+              ks=None, vs=None, ld_out=2, out_dt=0, st=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.csa_compress_kv(a["k"], a["v"], a["in_dt"], a["lg"], a["B"], a["L"], a["ld_in"],
+                                   a["d"], a["m"], a["ko"], a["vo"], a["ks"], a["vs"], a["ld_out"],
+                                   a["out_dt"], a["st"])
+    assert call(k=None) == csa.CSA_EINVAL
+    assert call(d=64) == csa.CSA_EINVAL
+    assert call(L=7) == csa.CSA_EINVAL            # L % m != 0
+    assert call(m=0) == csa.CSA_EINVAL
+    assert call(ld_in=4) == csa.CSA_EINVAL        # L > ld_in
+    assert call(ld_out=1) == csa.CSA_EINVAL       # too few output slots
+    assert call(out_dt=2) == csa.CSA_EINVAL       # fp8 needs scale outputs
+    assert call(in_dt=2) == csa.CSA_EINVAL        # fp8 input not accepted
+    assert call(out_dt=7) == csa.CSA_EINVAL
+    assert call(B=0) == csa.CSA_OK                # empty: nothing to do, nothing launched
+
+
+def test_indexer_rejects_bad_arguments():
+    import long_context_compressed_03_amd as csa
+    lib = csa.load()
+
+    def call(H_I=8, d_I=128, m=4, q=_p(), B=1, T=1, cap=16):
+        return lib.csa_indexer_scores(q, _p(), _p(), _p(), _p(), _p(), B, T, H_I, d_I, cap, m,
+                                      _p(), None)
+    assert call(q=None) == csa.CSA_EINVAL
+    assert call(H_I=3) == csa.CSA_ENOTSUP
+    assert call(d_I=48) == csa.CSA_EINVAL
+    assert call(d_I=1024) == csa.CSA_EINVAL
+    assert call(m=0) == csa.CSA_EINVAL
+    assert call(B=0) == csa.CSA_OK
+
+
+def test_topk_and_attention_reject_bad_arguments():
+    import long_context_compressed_03_amd as csa
+    lib = csa.load()
+    assert lib.csa_topk(_p(), _p(), 1, 1, 10, 4, 0, _p(), None, 0, None) == csa.CSA_EINVAL
+    assert lib.csa_topk(None, _p(), 1, 1, 10, 4, 3, _p(), None, 0, None) == csa.CSA_EINVAL
+
+    def sparse(H=64, d=128, k=1024, W=128, io=0, ckv=0, idx=_p(), ck_scale=None, ws=None, nws=0,
+               B=1, T=1):
+        return lib.csa_sparse_attn(_p(), io, _p(), _p(), ck_scale, ck_scale, ckv, 16, idx, k,
+                                   _p(), _p(), _p(), 8, _p(), W, B, T, H, d, 0.1, _p(), None,
+                                   ws, nws, None)
+    assert sparse(d=64) == csa.CSA_EINVAL
+    assert sparse(H=24) == csa.CSA_ENOTSUP
+    assert sparse(k=0) == csa.CSA_EINVAL
+    assert sparse(idx=None) == csa.CSA_EINVAL
+    assert sparse(ckv=2) == csa.CSA_EINVAL        # fp8 cache without scales
+    assert sparse(io=0, ckv=1) == csa.CSA_ENOTSUP  # bf16 queries over an fp32 cache
+    # decode shapes split the key list: the workspace is mandatory
+    need = lib.csa_workspace_size(csa.CSA_OP_SPARSE_ATTN, 1, 1, 64, 128, 1024 + 128)
+    assert need > 0
+    assert sparse() == csa.CSA_EWORKSPACE
+    assert sparse(ws=_p(), nws=need - 1) == csa.CSA_EWORKSPACE
+    assert lib.csa_workspace_size(csa.CSA_OP_SPARSE_ATTN, 1, 1, 24, 128, 12) == \
+        ctypes.c_size_t(-1).value
+    assert lib.hca_dense_attn(_p(), 0, _p(), _p(), None, None, 0, 16, 0, _p(), _p(), _p(), 8,
+                              _p(), 4, 1, 1, 64, 128, 0.1, _p(), None, None, 0,
+                              None) == csa.CSA_EINVAL  # m_prime < 1
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    import long_context_compressed_03_amd as csa
+    x = torch.zeros(1, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        csa.csa_compress_kv(x, x, torch.zeros(1, 8), 4, torch.zeros(1, 2, 128, dtype=torch.bfloat16),
+                            torch.zeros(1, 2, 128, dtype=torch.bfloat16))
