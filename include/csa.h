@@ -165,8 +165,8 @@ csa_status_t csa_topk(const float* scores, const int32_t* q_pos0, int32_t B, int
  *   sm_scale logit scale (pass 1/sqrt(d) for the usual choice)
  *   out      [B, T_q, H, d] in io_dtype;  lse [B, T_q, H] fp32 or NULL
  *   ws       workspace of csa_workspace_size(CSA_OP_SPARSE_ATTN, B, T_q, H, d, k + W)
- *            bytes, zero-filled ONCE after allocation; every call leaves it
- *            zero-filled again.  Calls that share a workspace must be ordered.
+ *            bytes (no initial contents needed; may be NULL when that size is
+ *            0).  Calls that share a workspace must be ordered on one stream.
  * Limits: H a multiple of 16 in [16, 128]; W >= 0; k >= 1.
  * Preconditions: idx entries are -1 or in [0, cap); the raw buffer covers
  * window(t) (rows outside [0, L_raw) are skipped).
@@ -188,7 +188,7 @@ csa_status_t csa_sparse_attn(const void* q, int32_t io_dtype, const void* ck, co
  * Key set for query t: entries e < min(floor((t+1)/m_prime), cap) and
  * window(t); otherwise exactly as csa_sparse_attn.
  * ws: csa_workspace_size(CSA_OP_DENSE_ATTN, B, T_q, H, d, cap + W) bytes, same
- * zero-fill contract as csa_sparse_attn.
+ * contract as csa_sparse_attn.
  * ------------------------------------------------------------------- */
 csa_status_t hca_dense_attn(const void* q, int32_t io_dtype, const void* ck, const void* cv,
                             const float* ck_scale, const float* cv_scale, int32_t ckv_dtype,

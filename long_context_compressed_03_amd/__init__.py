@@ -158,7 +158,7 @@ _WS = {}
 
 
 def _workspace(device, nbytes):
-    """Zero-filled, cached per device and grown on demand (the kernels keep it zero)."""
+    """Scratch for split partial results, cached per device and grown on demand."""
     if nbytes == ctypes.c_size_t(-1).value:
         raise CsaError("csa_workspace_size", CSA_EINVAL)
     if nbytes == 0:
@@ -166,7 +166,7 @@ def _workspace(device, nbytes):
     key = (device.type, device.index)
     buf = _WS.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _WS[key] = buf
     return buf
 

@@ -8,44 +8,55 @@
 // selected/visible entries and the window keys form one key list under one
 // softmax (this library's reading of "additionally keep").
 //
-// All query heads share the single KV head, so the heads are the M dimension
-// of the matrix-core tiles: a key row is fetched once and used by every head.
-// One block owns one query (all H heads, one wave per 16 heads) and one
-// contiguous split of its key list.  Keys are gathered in chunks of 32 into
-// LDS (K row-major; V transposed so the P*V operand reads 8 keys of one head
-// dimension as two 8-byte words), then per wave:
-//   S^T[32 keys x 16 heads] = K * Q^T       (bf16 MFMA 16x16x32, Q in VGPRs)
-//   online softmax per head (fp32, exp2 domain)
-//   O^T[128 x 16 heads]    += V^T * P^T     (P^T straight from S^T's C layout;
-//                                            the contraction order of the 32
-//                                            keys is permuted to match it)
-// fp8 (E4M3FN) entries are widened to bf16 exactly; the per-entry K scale is
-// applied to the logits and the V scale folded into P before the P*V product.
-// The fp32 variant uses the fp32 MFMA 16x16x4 with the same data flow (V stays
-// row-major there: the 4-wide contraction lines up with S^T's rows).
+// All query heads share the single KV head, so heads are the M dimension of
+// the matrix-core tiles and a gathered key row serves every head.  Keys are
+// gathered in chunks of 64 into LDS (K row-major; V transposed so a P*V
+// operand reads 4 or 8 keys of one head dimension as 8-byte words); the next
+// chunk's rows are already in flight in registers while the current one is
+// computed.  Per 16-head tile:
+//   S^T[keys x 16 heads] = K * Q^T    (bf16 MFMA 16x16x32, Q held in VGPRs)
+//   online softmax per head in fp32, exp2 domain
+//   O^T[128 x 16 heads] += V^T * P^T  (P^T taken straight from S^T's C layout)
+// fp8 (E4M3FN) entries are widened to bf16 exactly; the per-entry K scale
+// multiplies the logits and the V scale is folded into P.  The fp32 variant
+// runs the same data flow on the fp32 MFMA 16x16x4 (V row-major there).
 //
-// Split-K: with few queries (decode) each query's key list is cut into
-// fixed-size splits (a function of the shape only); every split writes its
-// unnormalised O, running max and sum to the workspace and the last block to
-// finish (agent-scope atomic counter) merges the splits in split order, so the
-// result is bitwise reproducible.  The last block also re-arms the counter.
+// A block owns one query and one split of its key list; its 8 waves take the
+// head tiles (w % 4, and w % 4 + 4 when H > 64) over one key half each of
+// every chunk, so each gathered row serves all heads from LDS, every SIMD has
+// two waves to interleave, and each wave's dependent chain per chunk is half
+// a chunk long; the two key halves merge through LDS at the end.  With few query rows (decoding) the key list
+// is cut into short splits so that every CU gets work and each block's chain
+// of dependent loads stays short; each split writes its unnormalised O,
+// running max and sum, and a second small kernel merges the splits in split
+// order (a kernel boundary instead of device-scope fences, which on this chip
+// write back and invalidate the XCD's whole L2).  The split depends only on
+// the shape and every reduction has a fixed order: results are bitwise
+// reproducible run to run.
 #include "common.hpp"
 
 namespace {
 
-constexpr int kNK = 32;                 // keys per chunk
-constexpr int kKPad = 8;                // bf16 pad per K row in LDS
-constexpr int kVPad = 4;                // bf16 pad per V^T row in LDS
-constexpr int kF32Pad = 4;              // fp32 pad per row in LDS
+constexpr int kNK = 64;                       // keys per chunk
+constexpr int kThreads = 512;                 // 8 waves
+constexpr int kKRow = kHeadDim + 8;           // bf16 per K row in LDS
+constexpr int kVRow = kNK + 8;                // bf16 per V^T row in LDS
+constexpr int kFRow = kHeadDim + 4;           // fp32 per K/V row in LDS (fp32 path)
+constexpr int kMaxSplits = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-CSA_DEV v4f mfma_bf16(const v8bf& a, const v8bf& b, v4f c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+CSA_DEV v4f mfma_k32(const u32x4& a, const u32x4& b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0,
+                                                 0);
+}
+CSA_DEV v4f mfma_k16(const u32x2& a, const u32x2& b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4s, a), __builtin_bit_cast(v4s, b), c, 0, 0,
+                                                   0);
 }
 CSA_DEV v4f mfma_f32(float a, float b, v4f c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
-
-CSA_DEV v8bf as_v8bf(u32x4 u) { return __builtin_bit_cast(v8bf, u); }
 
 struct AttnArgs {
   const void* q;
@@ -53,412 +64,565 @@ struct AttnArgs {
   const void* cv;
   const float* ck_scale;
   const float* cv_scale;
-  int cap;
-  const int32_t* idx;   // sparse only
-  int k;                // sparse: list length; dense: m_prime
+  const int32_t* idx;      // sparse only
   const void* k_win;
   const void* v_win;
   const int32_t* raw_pos0;
-  int L_raw;
   const int32_t* q_pos0;
+  void* out;
+  float* lse;
+  float* part_ml;          // [rows, n_splits, H, 2]: running max (log2 domain), sum
+  float* part_o;           // [rows, n_splits, H, 128]: unnormalised output
+  int cap;
+  int k;                   // sparse: list length; dense: m_prime
+  int L_raw;
   int W;
   int T_q;
   int H;
-  float sm_log2;        // sm_scale * log2(e)
-  void* out;
-  float* lse;
-  int n_list;           // key-list length (k + W or cap + W)
-  int split_len;        // keys per split (multiple of kNK)
+  int n_list;              // key-list length (k + W or cap + W)
+  int split_len;           // keys per split (multiple of kNK)
   int n_splits;
-  uint32_t* counters;   // [rows]
-  float* part_ml;       // [rows, n_splits, H, 2]
-  float* part_o;        // [rows, n_splits, H, 128]
+  float sm_log2;           // sm_scale * log2(e)
 };
 
-// Where key-list slot j of query (b, t) comes from.  Returns false for an
-// empty / invisible slot.  *from_ckv tells which buffer; *row is its row.
+// Source of key-list slot j for query (b, i) at position t.
+// 0 = empty / invisible, 1 = compressed entry `row`, 2 = raw window `row`.
+// `e` is idx[b, i, j] for sparse slots j < k (loaded by the caller so that
+// the index loads of several slots are in flight together); `raw0` is
+// raw_pos0[b].
 template <bool kDense>
-CSA_DEV bool key_source(const AttnArgs& a, int b, int i, int t, int j, bool* from_ckv, long* row) {
+CSA_DEV int key_source(const AttnArgs& a, int b, int t, int raw0, int j, int e, long* row) {
   int head_len;
   if constexpr (kDense) {
     head_len = a.cap;
     if (j < a.cap) {
       const int nv = min((t + 1) / a.k, a.cap);
-      *from_ckv = true;
       *row = long(b) * a.cap + j;
-      return j < nv;
+      return j < nv ? 1 : 0;
     }
   } else {
     head_len = a.k;
     if (j < a.k) {
-      const int e = a.idx[(long(b) * a.T_q + i) * a.k + j];
-      *from_ckv = true;
       *row = long(b) * a.cap + e;
-      return e >= 0 && e < a.cap;
+      return (e >= 0 && e < a.cap) ? 1 : 0;
     }
   }
   const int w = j - head_len;
-  if (w >= a.W) return false;
+  if (w >= a.W) return 0;
   const int p = t - a.W + 1 + w;
-  const int r = p - a.raw_pos0[b];
-  *from_ckv = false;
+  const int r = p - raw0;
   *row = long(b) * a.L_raw + r;
-  return p >= 0 && r >= 0 && r < a.L_raw;
+  return (p >= 0 && r >= 0 && r < a.L_raw) ? 2 : 0;
 }
 
-// --------------------------------------------------------------------------
-// Load 16 consecutive head-dim values [16*dc, 16*dc+16) of a K or V row as
-// fp32 (valid) or zeros.
+// Registers holding one gather item: two keys x 8 head dims of K and V.
+template <int kIO>
+struct Pre {
+  static constexpr int R = kIO == CSA_F32 ? 2 : 1;  // 16-byte words per 8 dims of the widest source
+  u32x4 k[2][R], v[2][R];
+  float sk[2], sv[2];
+  int src[2];
+};
+
 template <int kDT>
-CSA_DEV void load16(const void* base, long row, int dc, float* x) {
-  if constexpr (kDT == CSA_BF16) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + row * kHeadDim + dc * 16);
-    u32x4 u0 = p[0], u1 = p[1];
-    uint32_t w[8] = {u0[0], u0[1], u0[2], u0[3], u1[0], u1[1], u1[2], u1[3]};
+CSA_DEV void load_part(const void* base, long row, int dg, u32x4* dst) {
+  // 8 head dims [8*dg, 8*dg + 8) of `row`
+  if constexpr (kDT == CSA_FP8_E4M3) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(base) + row * kHeadDim + dg * 8);
+    dst[0] = u32x4{w[0], w[1], 0u, 0u};
+  } else if constexpr (kDT == CSA_BF16) {
+    dst[0] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + row * kHeadDim + dg * 8);
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + row * kHeadDim + dg * 8);
+    dst[0] = p[0];
+    dst[1] = p[1];
+  }
+}
+
+// Gather item of thread tid: key pair kp = tid % 32 (keys 2kp, 2kp+1 of the
+// chunk), head dims [8*dg, 8*dg+8) with dg = tid / 32.
+template <int kIO, int kCKV, bool kDense>
+CSA_DEV void prefetch(const AttnArgs& a, Pre<kIO>& pr, int b, int i, int t, int raw0, int jc, int j_end) {
+  const int kp = threadIdx.x & 31;
+  const int dg = threadIdx.x >> 5;
+  // phase 1: the selected-entry indices of both slots (both loads in flight)
+  int e[2] = {-1, -1};
+  if constexpr (!kDense) {
+    const int32_t* ip = a.idx + (long(b) * a.T_q + i) * a.k;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      x[2 * i] = __uint_as_float(w[i] << 16);
-      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    for (int x = 0; x < 2; ++x) {
+      const int j = jc + 2 * kp + x;
+      if (j < j_end && j < a.k) e[x] = ip[j];
     }
-  } else if constexpr (kDT == CSA_F32) {
-    const v4f* p = reinterpret_cast<const v4f*>(static_cast<const float*>(base) + row * kHeadDim + dc * 16);
+  }
+  // phase 2: rows of both slots
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v4f v = p[i];
-      x[4 * i] = v[0]; x[4 * i + 1] = v[1]; x[4 * i + 2] = v[2]; x[4 * i + 3] = v[3];
+  for (int x = 0; x < 2; ++x) {
+    const int j = jc + 2 * kp + x;
+    long row = 0;
+    const int src = j < j_end ? key_source<kDense>(a, b, t, raw0, j, e[x], &row) : 0;
+    pr.src[x] = src;
+    pr.sk[x] = 1.f;
+    pr.sv[x] = 1.f;
+    if (src == 1) {
+      load_part<kCKV>(a.ck, row, dg, pr.k[x]);
+      load_part<kCKV>(a.cv, row, dg, pr.v[x]);
+      if constexpr (kCKV == CSA_FP8_E4M3) {
+        pr.sk[x] = a.ck_scale[row];
+        pr.sv[x] = a.cv_scale[row];
+      }
+    } else if (src == 2) {
+      load_part<kIO>(a.k_win, row, dg, pr.k[x]);
+      load_part<kIO>(a.v_win, row, dg, pr.v[x]);
+    }
+  }
+}
+
+// 8 values of a gathered part as fp32 (src 0 -> zeros)
+template <int kIO, int kCKV>
+CSA_DEV void part_f32(const u32x4* w, int src, float* x) {
+  if (src == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+  } else if (kCKV == CSA_FP8_E4M3 && src == 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = e4m3_to_f32((w[0][e >> 2] >> (8 * (e & 3))) & 0xFFu);
+  } else if constexpr (kIO == CSA_BF16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t u = w[0][e];
+      x[2 * e] = __uint_as_float(u << 16);
+      x[2 * e + 1] = __uint_as_float(u & 0xFFFF0000u);
     }
   } else {
-    const u32x4 u = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(base) + row * kHeadDim + dc * 16);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = e4m3_to_f32((u[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+    for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(w[e >> 2][e & 3]);
   }
+}
+
+// LDS layout of one chunk
+struct LdsBf16 {
+  uint16_t K[kNK][kKRow];
+  uint16_t Vt[kHeadDim][kVRow];
+  float sk[kNK];
+  float sv[kNK];
+  int valid[kNK];
+};
+struct LdsF32 {
+  float K[kNK][kFRow];
+  float V[kNK][kFRow];
+  float sk[kNK];
+  float sv[kNK];
+  int valid[kNK];
+};
+template <int kIO>
+using LdsChunk = typename std::conditional<kIO == CSA_BF16, LdsBf16, LdsF32>::type;
+
+// Hand-over of one key half's state to the other at the end of a block.
+template <int kHTW>
+struct LdsHalf {
+  float o[4 * kHTW][16][kHeadDim + 4];
+  float m[4 * kHTW][16];
+  float l[4 * kHTW][16];
+};
+
+template <int kIO, int kHTW>
+constexpr size_t lds_bytes() {
+  return sizeof(LdsChunk<kIO>) > sizeof(LdsHalf<kHTW>) ? sizeof(LdsChunk<kIO>) : sizeof(LdsHalf<kHTW>);
 }
 
 template <int kIO, int kCKV>
-struct Smem;
-
-// bf16 compute path
-template <int kCKV>
-struct Smem<CSA_BF16, kCKV> {
-  uint16_t K[kNK][kHeadDim + kKPad];
-  uint16_t Vt[kHeadDim][kNK + kVPad];
-  float sk[kNK];
-  float sv[kNK];
-  int valid[kNK];
-  uint32_t flag;
-};
-// fp32 compute path
-template <int kCKV>
-struct Smem<CSA_F32, kCKV> {
-  float K[kNK][kHeadDim + kF32Pad];
-  float V[kNK][kHeadDim + kF32Pad];
-  float sk[kNK];
-  float sv[kNK];
-  int valid[kNK];
-  uint32_t flag;
-};
-
-template <int kIO, int kCKV, bool kDense>
-CSA_DEV void gather_chunk(const AttnArgs& a, Smem<kIO, kCKV>& s, int b, int i, int t, int j0, int j_end) {
-  for (int u = threadIdx.x; u < kNK * 8; u += blockDim.x) {
-    const int kk = u >> 3;
-    const int dc = u & 7;
-    const int j = j0 + kk;
-    bool from_ckv = false;
-    long row = 0;
-    const bool ok = j < j_end && key_source<kDense>(a, b, i, t, j, &from_ckv, &row);
-    float xk[16], xv[16];
-    float sck = 1.f, scv = 1.f;
-    if (!ok) {
+CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr) {
+  const int kp = threadIdx.x & 31;
+  const int dg = threadIdx.x >> 5;
+  float xk[2][8], xv[2][8];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) { xk[e] = 0.f; xv[e] = 0.f; }
-    } else if (from_ckv) {
-      load16<kCKV>(a.ck, row, dc, xk);
-      load16<kCKV>(a.cv, row, dc, xv);
-      if constexpr (kCKV == CSA_FP8_E4M3) {
-        sck = a.ck_scale[row];
-        scv = a.cv_scale[row];
-      }
-    } else {
-      load16<kIO>(a.k_win, row, dc, xk);
-      load16<kIO>(a.v_win, row, dc, xv);
+  for (int e = 0; e < 2; ++e) {
+    part_f32<kIO, kCKV>(pr.k[e], pr.src[e], xk[e]);
+    part_f32<kIO, kCKV>(pr.v[e], pr.src[e], xv[e]);
+  }
+  if constexpr (kIO == CSA_BF16) {
+    // values are exact in bf16 (bf16 inputs or E4M3 codes): keep the top halves
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      uint32_t w[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+        w[x] = (__float_as_uint(xk[e][2 * x]) >> 16) | (__float_as_uint(xk[e][2 * x + 1]) & 0xFFFF0000u);
+      *reinterpret_cast<u32x4*>(&s.K[2 * kp + e][dg * 8]) = u32x4{w[0], w[1], w[2], w[3]};
     }
-    if constexpr (kIO == CSA_BF16) {
-      // values are exact in bf16 (bf16 inputs, or E4M3 codes)
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        const uint32_t w = (__float_as_uint(xk[e]) >> 16) | (__float_as_uint(xk[e + 1]) & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t*>(&s.K[kk][dc * 16 + e]) = w;
+    for (int x = 0; x < 8; ++x)
+      *reinterpret_cast<uint32_t*>(&s.Vt[dg * 8 + x][2 * kp]) =
+          (__float_as_uint(xv[0][x]) >> 16) | (__float_as_uint(xv[1][x]) & 0xFFFF0000u);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int x = 0; x < 8; x += 4) {
+        *reinterpret_cast<v4f*>(&s.K[2 * kp + e][dg * 8 + x]) = v4f{xk[e][x], xk[e][x + 1], xk[e][x + 2], xk[e][x + 3]};
+        *reinterpret_cast<v4f*>(&s.V[2 * kp + e][dg * 8 + x]) = v4f{xv[e][x], xv[e][x + 1], xv[e][x + 2], xv[e][x + 3]};
       }
+  }
+  if (dg == 0) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s.Vt[dc * 16 + e][kk] = uint16_t(__float_as_uint(xv[e]) >> 16);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; e += 4) {
-        *reinterpret_cast<v4f*>(&s.K[kk][dc * 16 + e]) = v4f{xk[e], xk[e + 1], xk[e + 2], xk[e + 3]};
-        *reinterpret_cast<v4f*>(&s.V[kk][dc * 16 + e]) = v4f{xv[e], xv[e + 1], xv[e + 2], xv[e + 3]};
-      }
-    }
-    if (dc == 0) {
-      s.sk[kk] = sck;
-      s.sv[kk] = scv;
-      s.valid[kk] = ok ? 1 : 0;
+    for (int e = 0; e < 2; ++e) {
+      s.sk[2 * kp + e] = pr.sk[e];
+      s.sv[2 * kp + e] = pr.sv[e];
+      s.valid[2 * kp + e] = pr.src[e] != 0;
     }
   }
 }
 
-template <int kIO, int kCKV, bool kDense>
-__global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
-  __shared__ Smem<kIO, kCKV> s;
+// S^T for one 16-key tile `kt` of the chunk, scaled to the log2 domain and masked.
+template <int kIO>
+CSA_DEV void logits_tile(const LdsChunk<kIO>& s, const u32x4* qb, const float* qf, int kt, float sm_log2, int col,
+                         int g, float* x) {
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (kIO == CSA_BF16) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc = mfma_k32(*reinterpret_cast<const u32x4*>(&s.K[kt * 16 + col][ks * 32 + g * 8]), qb[ks], acc);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) acc = mfma_f32(s.K[kt * 16 + col][ks * 4 + g], qf[ks], acc);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int kk = kt * 16 + 4 * g + r;
+    x[r] = s.valid[kk] ? acc[r] * s.sk[kk] * sm_log2 : -INFINITY;
+  }
+}
+
+template <int kIO>
+CSA_DEV void store_out4(void* out, long orow, int d4, v4f v) {
+  if constexpr (kIO == CSA_BF16) {
+    const uint32_t w0 = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
+    const uint32_t w1 = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow * kHeadDim + d4 * 4) = u32x2{w0, w1};
+  } else {
+    *reinterpret_cast<v4f*>(static_cast<float*>(out) + orow * kHeadDim + d4 * 4) = v;
+  }
+}
+
+// 8 waves: wave w takes head tiles (w % 4) [+ 4 when kHTW == 2] and key half
+// w / 4 (keys [32*(w/4), 32*(w/4)+32) of every chunk); the two halves merge at
+// the end of the block through LDS.
+template <int kIO, int kCKV, bool kDense, int kHTW>
+__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  LdsChunk<kIO>& s = *reinterpret_cast<LdsChunk<kIO>*>(smem);
+
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  const int col = lane & 15;   // head within the wave's 16 (S^T / O^T column)
+  const int col = lane & 15;
   const int g = lane >> 4;
-  const int split = blockIdx.x;
-  const long qrow = blockIdx.y;            // b * T_q + i
+  const int kh = wid >> 2;
+  const int wt = wid & 3;
+
+  const long qrow = blockIdx.x / a.n_splits;
+  const int split = int(blockIdx.x - qrow * a.n_splits);
   const int b = int(qrow / a.T_q);
   const int i = int(qrow - long(b) * a.T_q);
   const int t = a.q_pos0[b] + i;
-  const int head = wid * 16 + col;
+  const int raw0 = a.W > 0 ? a.raw_pos0[b] : 0;
+  const int n_tiles = a.H / 16;
   const int j_begin = split * a.split_len;
   const int j_end = min(j_begin + a.split_len, a.n_list);
 
-  // ---- Q fragment (B operand of S^T = K Q^T): head `head`, this lane's d-slice
-  constexpr int kQRegs = kIO == CSA_BF16 ? 4 : 32;
-  u32x4 qb[kIO == CSA_BF16 ? 4 : 1];
-  float qf[kIO == CSA_BF16 ? 1 : 32];
-  if constexpr (kIO == CSA_BF16) {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (qrow * a.H + head) * kHeadDim;
+  bool act[kHTW];
+  u32x4 qb[kHTW][4];
+  float qf[kHTW][kIO == CSA_F32 ? 32 : 1];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qb[ks] = *reinterpret_cast<const u32x4*>(qp + ks * 32 + g * 8);
-  } else {
-    const float* qp = static_cast<const float*>(a.q) + (qrow * a.H + head) * kHeadDim;
+  for (int ht = 0; ht < kHTW; ++ht) {
+    const int tile = wt + 4 * ht;
+    act[ht] = tile < n_tiles;
+    if (!act[ht]) continue;
+    const int head = tile * 16 + col;
+    if constexpr (kIO == CSA_BF16) {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (qrow * a.H + head) * kHeadDim;
 #pragma unroll
-    for (int ks = 0; ks < 32; ++ks) qf[ks] = qp[ks * 4 + g];
+      for (int ks = 0; ks < 4; ++ks) qb[ht][ks] = *reinterpret_cast<const u32x4*>(qp + ks * 32 + g * 8);
+    } else {
+      const float* qp = static_cast<const float*>(a.q) + (qrow * a.H + head) * kHeadDim;
+#pragma unroll
+      for (int ks = 0; ks < 32; ++ks) qf[ht][ks] = qp[ks * 4 + g];
+    }
   }
-  (void)kQRegs;
 
-  v4f o[8];
+  v4f o[kHTW][8];
+  float m_run[kHTW], l_run[kHTW];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) o[dt] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;   // running max (log2 domain) of this lane's head
-  float l_run = 0.f;         // this lane's partial sum (its 8 keys per chunk)
+  for (int ht = 0; ht < kHTW; ++ht) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[ht][dt] = v4f{0.f, 0.f, 0.f, 0.f};
+    m_run[ht] = -INFINITY;
+    l_run[ht] = 0.f;
+  }
 
+  Pre<kIO> pr;
+  if (j_begin < j_end) prefetch<kIO, kCKV, kDense>(a, pr, b, i, t, raw0, j_begin, j_end);
   for (int j0 = j_begin; j0 < j_end; j0 += kNK) {
     __syncthreads();
-    gather_chunk<kIO, kCKV, kDense>(a, s, b, i, t, j0, j_end);
+    store_chunk<kIO, kCKV>(s, pr);
     __syncthreads();
+    if (j0 + kNK < j_end) prefetch<kIO, kCKV, kDense>(a, pr, b, i, t, raw0, j0 + kNK, j_end);
+#pragma unroll
+    for (int ht = 0; ht < kHTW; ++ht) {
+      if (!act[ht]) continue;
+      float x[2][4];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) logits_tile<kIO>(s, qb[ht], qf[ht], 2 * kh + kk, a.sm_log2, col, g, x[kk]);
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cmax = fmaxf(cmax, x[kk][r]);
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      const float m_new = fmaxf(m_run[ht], cmax);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[ht] - m_use);
+      m_run[ht] = m_new;
+      float p[2][4];
+      float psum = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[kk][r] = __builtin_amdgcn_exp2f(x[kk][r] - m_use);
+          psum += p[kk][r];
+        }
+      l_run[ht] = l_run[ht] * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[ht][dt] *= alpha;
 
-    // ---- S^T for two 16-key tiles
-    float x[2][4];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
+      // O^T += V^T P^T (P carries the per-entry V scale)
       if constexpr (kIO == CSA_BF16) {
+        // one 32-key step: contraction slot 8g+j <-> key 4g+j (j<4) / 16+4g+(j-4) of the half
+        uint32_t pw[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const u32x4 kv = *reinterpret_cast<const u32x4*>(&s.K[mt * 16 + col][ks * 32 + g * 8]);
-          acc = mfma_bf16(as_v8bf(kv), as_v8bf(qb[ks]), acc);
+        for (int h2 = 0; h2 < 4; ++h2) {
+          const int kk = h2 >> 1;
+          const int r0 = (h2 & 1) * 2;
+          const int key = (2 * kh + kk) * 16 + 4 * g + r0;
+          pw[h2] = uint32_t(f32_to_bf16(p[kk][r0] * s.sv[key])) |
+                   (uint32_t(f32_to_bf16(p[kk][r0 + 1] * s.sv[key + 1])) << 16);
+        }
+        const u32x4 pb = {pw[0], pw[1], pw[2], pw[3]};
+        const int k0 = kh * 32 + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(&s.Vt[dt * 16 + col][k0]);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(&s.Vt[dt * 16 + col][k0 + 16]);
+          o[ht][dt] = mfma_k32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, o[ht][dt]);
         }
       } else {
 #pragma unroll
-        for (int ks = 0; ks < 32; ++ks) acc = mfma_f32(s.K[mt * 16 + col][ks * 4 + g], qf[ks], acc);
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = (2 * kh + kk) * 16 + 4 * g + r;
+            const float pv = p[kk][r] * s.sv[key];
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) o[ht][dt] = mfma_f32(s.V[key][dt * 16 + col], pv, o[ht][dt]);
+          }
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kk = mt * 16 + 4 * g + r;
-        x[mt][r] = s.valid[kk] ? acc[r] * s.sk[kk] * a.sm_log2 : -INFINITY;
-      }
-    }
-    // ---- online softmax (per head = per column; 4 lane groups share a head)
-    float cmax = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);   // m_run == -inf -> 0
-    m_run = m_new;
-    float p[2][4];
-    float psum = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[mt][r] = exp2f(x[mt][r] - m_use);
-        psum += p[mt][r];
-      }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
-
-    // ---- O^T += V^T P^T
-    if constexpr (kIO == CSA_BF16) {
-      uint32_t pw[4];
-#pragma unroll
-      for (int h2 = 0; h2 < 4; ++h2) {
-        const int mt = h2 >> 1;
-        const int r0 = (h2 & 1) * 2;
-        const float p0 = p[mt][r0] * s.sv[mt * 16 + 4 * g + r0];
-        const float p1 = p[mt][r0 + 1] * s.sv[mt * 16 + 4 * g + r0 + 1];
-        pw[h2] = uint32_t(f32_to_bf16(p0)) | (uint32_t(f32_to_bf16(p1)) << 16);
-      }
-      const v8bf pb = as_v8bf(u32x4{pw[0], pw[1], pw[2], pw[3]});
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int d = dt * 16 + col;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(&s.Vt[d][4 * g]);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(&s.Vt[d][16 + 4 * g]);
-        o[dt] = mfma_bf16(as_v8bf(u32x4{lo[0], lo[1], hi[0], hi[1]}), pb, o[dt]);
-      }
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kk = mt * 16 + 4 * g + r;
-          const float pv = p[mt][r] * s.sv[kk];
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt) o[dt] = mfma_f32(s.V[kk][dt * 16 + col], pv, o[dt]);
-        }
     }
   }
 
-  // per-head sum over the 4 lane groups
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-
-  if (a.n_splits == 1) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if constexpr (kIO == CSA_BF16) {
-      uint16_t* op = static_cast<uint16_t*>(a.out) + (qrow * a.H + head) * kHeadDim;
+  float l_tot[kHTW];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const uint32_t w0 = uint32_t(f32_to_bf16(o[dt][0] * inv)) | (uint32_t(f32_to_bf16(o[dt][1] * inv)) << 16);
-        const uint32_t w1 = uint32_t(f32_to_bf16(o[dt][2] * inv)) | (uint32_t(f32_to_bf16(o[dt][3] * inv)) << 16);
-        *reinterpret_cast<u32x2*>(op + dt * 16 + 4 * g) = u32x2{w0, w1};
-      }
-    } else {
-      float* op = static_cast<float*>(a.out) + (qrow * a.H + head) * kHeadDim;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<v4f*>(op + dt * 16 + 4 * g) = o[dt] * inv;
-    }
-    if (a.lse && g == 0)
-      a.lse[qrow * a.H + head] = l_tot > 0.f ? (m_run * kLn2 + logf(l_tot)) : -INFINITY;
-    return;
+  for (int ht = 0; ht < kHTW; ++ht) {
+    l_tot[ht] = l_run[ht] + __shfl_xor(l_run[ht], 16);
+    l_tot[ht] += __shfl_xor(l_tot[ht], 32);
   }
-
-  // ---- split-K: publish this split's partial state
-  {
-    const long base = (qrow * a.n_splits + split) * a.H + head;
-    float* po = a.part_o + base * kHeadDim;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<v4f*>(po + dt * 16 + 4 * g) = o[dt];
-    if (g == 0) {
-      a.part_ml[base * 2] = m_run;
-      a.part_ml[base * 2 + 1] = l_tot;
-    }
-  }
-  __threadfence();
+  // hand the second key half to the first
+  LdsHalf<kHTW>& hf = *reinterpret_cast<LdsHalf<kHTW>*>(smem);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&a.counters[qrow], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s.flag = prev == uint32_t(a.n_splits - 1) ? 1u : 0u;
+  if (kh == 1) {
+#pragma unroll
+    for (int ht = 0; ht < kHTW; ++ht) {
+      if (!act[ht]) continue;
+      const int tile = wt + 4 * ht;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<v4f*>(&hf.o[tile][col][dt * 16 + 4 * g]) = o[ht][dt];
+      if (g == 0) {
+        hf.m[tile][col] = m_run[ht];
+        hf.l[tile][col] = l_tot[ht];
+      }
+    }
   }
   __syncthreads();
-  if (!s.flag) return;
-  __threadfence();
-  // ---- last block: merge the splits in split order
-  const int n_el = a.H * kHeadDim;
-  for (int e = threadIdx.x; e < n_el; e += blockDim.x) {
-    const int h = e / kHeadDim;
-    const int d = e - h * kHeadDim;
-    float M = -INFINITY;
-    for (int sp = 0; sp < a.n_splits; ++sp)
-      M = fmaxf(M, __builtin_nontemporal_load(&a.part_ml[((qrow * a.n_splits + sp) * a.H + h) * 2]));
+  if (kh == 1) return;
+#pragma unroll
+  for (int ht = 0; ht < kHTW; ++ht) {
+    if (!act[ht]) continue;
+    const int tile = wt + 4 * ht;
+    const int head = tile * 16 + col;
+    const float m1 = hf.m[tile][col];
+    const float M = fmaxf(m_run[ht], m1);
     const float Mu = M == -INFINITY ? 0.f : M;
-    float L = 0.f, acc = 0.f;
-    for (int sp = 0; sp < a.n_splits; ++sp) {
-      const long base = (qrow * a.n_splits + sp) * a.H + h;
-      const float ms = __builtin_nontemporal_load(&a.part_ml[base * 2]);
-      const float ls = __builtin_nontemporal_load(&a.part_ml[base * 2 + 1]);
-      const float f = exp2f(ms - Mu);
-      L = fmaf(ls, f, L);
-      acc = fmaf(__builtin_nontemporal_load(&a.part_o[base * kHeadDim + d]), f, acc);
+    const float f0 = __builtin_amdgcn_exp2f(m_run[ht] - Mu);
+    const float f1 = __builtin_amdgcn_exp2f(m1 - Mu);
+    const float L = l_tot[ht] * f0 + hf.l[tile][col] * f1;
+    v4f oo[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      oo[dt] = o[ht][dt] * f0 + *reinterpret_cast<const v4f*>(&hf.o[tile][col][dt * 16 + 4 * g]) * f1;
+    if (a.n_splits == 1) {
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      const long orow = qrow * a.H + head;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) store_out4<kIO>(a.out, orow, dt * 4 + g, oo[dt] * inv);
+      if (a.lse && g == 0) a.lse[orow] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
+    } else {
+      // this split's unnormalised state; the merge kernel combines the splits
+      const long slot = (qrow * a.n_splits + split) * a.H + head;
+      float* po = a.part_o + slot * kHeadDim;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<v4f*>(po + dt * 16 + 4 * g) = oo[dt];
+      if (g == 0) {
+        a.part_ml[slot * 2] = M;
+        a.part_ml[slot * 2 + 1] = L;
+      }
     }
-    const float v = L > 0.f ? acc / L : 0.f;
-    if constexpr (kIO == CSA_BF16)
-      static_cast<uint16_t*>(a.out)[(qrow * a.H + h) * kHeadDim + d] = f32_to_bf16(v);
-    else
-      static_cast<float*>(a.out)[(qrow * a.H + h) * kHeadDim + d] = v;
-    if (a.lse && d == 0) a.lse[qrow * a.H + h] = L > 0.f ? (M * kLn2 + logf(L)) : -INFINITY;
   }
-  if (threadIdx.x == 0) a.counters[qrow] = 0u;
+}
+
+// Merge of the key splits of one (query, head) by one wave: lane x reads
+// split x's (max, sum) (at most 64 splits), the wave reduces them, then lane
+// (h, d4) accumulates splits h, h+2, ... of float4 d4 with the weights taken
+// from the owning lanes; the two halves are added at the end.  Fixed order.
+template <int kIO>
+__global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict__ part_ml,
+                                                        const float* __restrict__ part_o, int n_splits, int H,
+                                                        void* out, float* lse) {
+  const long hid = blockIdx.x;                  // query row * H + head
+  const int lane = threadIdx.x;
+  const long qrow = hid / H;
+  const int head = int(hid - qrow * H);
+  const long base = qrow * n_splits * H + head; // slot of split 0; split x adds x*H
+  float mx = -INFINITY, lx = 0.f;
+  if (lane < n_splits) {
+    mx = part_ml[(base + long(lane) * H) * 2];
+    lx = part_ml[(base + long(lane) * H) * 2 + 1];
+  }
+  float M = mx;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const float Mu = M == -INFINITY ? 0.f : M;
+  const float fx = lane < n_splits ? exp2f(mx - Mu) : 0.f;
+  float L = lx * fx;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+
+  const int half = lane >> 5;
+  const int d4 = lane & 31;
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int kU = 8;
+  for (int x0 = half; x0 < n_splits; x0 += 2 * kU) {
+    v4f pv[kU];
+#pragma unroll
+    for (int y = 0; y < kU; ++y) {
+      const int x = x0 + 2 * y;
+      pv[y] = x < n_splits ? *reinterpret_cast<const v4f*>(part_o + (base + long(x) * H) * kHeadDim + d4 * 4)
+                           : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int y = 0; y < kU; ++y) {
+      const int x = x0 + 2 * y;
+      const float f = __shfl(fx, x < n_splits ? x : 0);
+      if (x < n_splits) acc += pv[y] * f;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], 32);
+  if (half == 0) {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    store_out4<kIO>(out, hid, d4, acc * inv);
+    if (lse && d4 == 0) lse[hid] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
+  }
 }
 
 // ------------------------------------------------------------------ host --
-struct SplitPlan {
-  int split_len, n_splits;
+struct Plan {
+  int n_splits, split_len;
+  long blocks;
 };
 
-SplitPlan plan_splits(long rows, int n_list) {
-  // Enough blocks to fill the 256 CUs about twice; a split is never shorter
-  // than 64 keys and is a multiple of the 32-key chunk.  Depends only on the
-  // shape, never on data or timing.
-  constexpr long kTargetBlocks = 512;
-  SplitPlan p;
-  if (n_list <= 0) return SplitPlan{kNK, 1};
-  long want = (kTargetBlocks + rows - 1) / rows;
+// The work split depends only on (rows, n_list): never on data or timing.
+// Enough blocks to give every CU about two; a split is a whole number of
+// 64-key chunks.
+Plan make_plan(long rows, int n_list) {
+  Plan p{};
+  const long chunks = (max(n_list, 1) + kNK - 1) / kNK;
+  long want = (512 + rows - 1) / rows;
+  if (want > chunks) want = chunks;
+  if (want > kMaxSplits) want = kMaxSplits;
   if (want < 1) want = 1;
-  long len = (n_list + want - 1) / want;
-  len = ((len + kNK - 1) / kNK) * kNK;
-  if (len < 64) len = 64;
-  if (len > n_list) len = ((n_list + kNK - 1) / kNK) * kNK;
-  p.split_len = int(len);
-  p.n_splits = int((n_list + len - 1) / len);
+  const long per = (chunks + want - 1) / want;
+  p.split_len = int(per * kNK);
+  p.n_splits = int((chunks + per - 1) / per);
+  p.blocks = rows * p.n_splits;
   return p;
 }
 
-size_t ws_bytes_for(long rows, int H, int n_splits) {
-  if (n_splits <= 1) return 0;
-  const size_t cnt = ((size_t(rows) * 4 + 255) / 256) * 256;
-  const size_t ml = ((size_t(rows) * n_splits * H * 2 * 4 + 255) / 256) * 256;
-  const size_t po = size_t(rows) * n_splits * H * kHeadDim * 4;
-  return cnt + ml + po;
+size_t plan_ws_bytes(const Plan& p, long rows, int H) {
+  if (p.n_splits <= 1) return 0;
+  const size_t slots = size_t(rows) * p.n_splits * H;
+  const size_t ml = ((slots * 2 * 4 + 255) / 256) * 256;
+  return ml + slots * kHeadDim * 4;
 }
 
-template <int kIO, int kCKV, bool kDense>
-hipError_t launch_attn(const AttnArgs& a, long rows, hipStream_t st) {
-  dim3 grid(a.n_splits, unsigned(rows));
-  hipLaunchKernelGGL((attn_kernel<kIO, kCKV, kDense>), grid, dim3(64 * (a.H / 16)), 0, st, a);
+template <int kIO, int kCKV, bool kDense, int kHTW>
+hipError_t launch_attn(const AttnArgs& a, long blocks, hipStream_t st) {
+  static bool attr = false;   // per instantiation; dynamic LDS above 64 KB needs the opt-in
+  constexpr size_t bytes = lds_bytes<kIO, kHTW>();
+  auto fn = attn_kernel<kIO, kCKV, kDense, kHTW>;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       int(bytes));
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(fn, dim3(unsigned(blocks)), dim3(kThreads), bytes, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_splits == 1) return e;
+  const long heads = blocks / a.n_splits * a.H;
+  hipLaunchKernelGGL(attn_merge_kernel<kIO>, dim3(unsigned(heads)), dim3(64), 0, st, a.part_ml, a.part_o, a.n_splits,
+                     a.H, a.out, a.lse);
   return hipGetLastError();
 }
 
+template <int kIO, int kCKV, bool kDense>
+hipError_t launch_tiles(const AttnArgs& a, long blocks, hipStream_t st) {
+  return a.H <= 64 ? launch_attn<kIO, kCKV, kDense, 1>(a, blocks, st)
+                   : launch_attn<kIO, kCKV, kDense, 2>(a, blocks, st);
+}
+
 template <bool kDense>
-csa_status_t run_attn(AttnArgs a, int io_dtype, int ckv_dtype, int B, int d, void* ws, size_t ws_size,
-                      hipStream_t st) {
+csa_status_t run_attn(AttnArgs a, int io_dtype, int ckv_dtype, int B, void* ws, size_t ws_size, hipStream_t st) {
   const long rows = long(B) * a.T_q;
   if (rows == 0) return CSA_OK;
-  if (rows > 0x7FFFFFFFL) return CSA_ENOTSUP;
-  const SplitPlan p = plan_splits(rows, a.n_list);
-  a.split_len = p.split_len;
+  const Plan p = make_plan(rows, a.n_list);
+  if (p.blocks > 0x7FFFFFFFL) return CSA_ENOTSUP;
   a.n_splits = p.n_splits;
-  const size_t need = ws_bytes_for(rows, a.H, p.n_splits);
+  a.split_len = p.split_len;
+  const size_t need = plan_ws_bytes(p, rows, a.H);
   if (need > 0) {
     if (!ws || ws_size < need) return CSA_EWORKSPACE;
     char* w = static_cast<char*>(ws);
-    const size_t cnt = ((size_t(rows) * 4 + 255) / 256) * 256;
-    const size_t ml = ((size_t(rows) * p.n_splits * a.H * 2 * 4 + 255) / 256) * 256;
-    a.counters = reinterpret_cast<uint32_t*>(w);
-    a.part_ml = reinterpret_cast<float*>(w + cnt);
-    a.part_o = reinterpret_cast<float*>(w + cnt + ml);
+    const size_t slots = size_t(rows) * p.n_splits * a.H;
+    const size_t ml = ((slots * 2 * 4 + 255) / 256) * 256;
+    a.part_ml = reinterpret_cast<float*>(w);
+    a.part_o = reinterpret_cast<float*>(w + ml);
   }
-  (void)d;
   hipError_t err;
-  if (io_dtype == CSA_BF16 && ckv_dtype == CSA_BF16) err = launch_attn<CSA_BF16, CSA_BF16, kDense>(a, rows, st);
-  else if (io_dtype == CSA_BF16 && ckv_dtype == CSA_FP8_E4M3) err = launch_attn<CSA_BF16, CSA_FP8_E4M3, kDense>(a, rows, st);
-  else if (io_dtype == CSA_F32 && ckv_dtype == CSA_F32) err = launch_attn<CSA_F32, CSA_F32, kDense>(a, rows, st);
-  else if (io_dtype == CSA_F32 && ckv_dtype == CSA_FP8_E4M3) err = launch_attn<CSA_F32, CSA_FP8_E4M3, kDense>(a, rows, st);
+  if (io_dtype == CSA_BF16 && ckv_dtype == CSA_BF16) err = launch_tiles<CSA_BF16, CSA_BF16, kDense>(a, p.blocks, st);
+  else if (io_dtype == CSA_BF16 && ckv_dtype == CSA_FP8_E4M3) err = launch_tiles<CSA_BF16, CSA_FP8_E4M3, kDense>(a, p.blocks, st);
+  else if (io_dtype == CSA_F32 && ckv_dtype == CSA_F32) err = launch_tiles<CSA_F32, CSA_F32, kDense>(a, p.blocks, st);
+  else if (io_dtype == CSA_F32 && ckv_dtype == CSA_FP8_E4M3) err = launch_tiles<CSA_F32, CSA_FP8_E4M3, kDense>(a, p.blocks, st);
   else return CSA_ENOTSUP;
   return err == hipSuccess ? CSA_OK : CSA_EHIP;
 }
@@ -484,7 +648,7 @@ csa_status_t check_common(const void* q, int io_dtype, const void* ck, const voi
 }  // namespace
 
 size_t csa_attn_workspace_size(long rows, int H, int n_list) {
-  return ws_bytes_for(rows, H, plan_splits(rows, n_list).n_splits);
+  return plan_ws_bytes(make_plan(rows, n_list), rows, H);
 }
 
 extern "C" csa_status_t csa_sparse_attn(const void* q, int32_t io_dtype, const void* ck, const void* cv,
@@ -497,13 +661,13 @@ extern "C" csa_status_t csa_sparse_attn(const void* q, int32_t io_dtype, const v
                                 q_pos0, W, B, T_q, H, d, out);
   if (c != CSA_OK) return c;
   if (!idx || k < 1) return CSA_EINVAL;
-  if (long(k) + W > 0x7FFFFFFFL) return CSA_ENOTSUP;
+  if (long(k) + W > 0x7FFFFFFFL - kNK) return CSA_ENOTSUP;
   AttnArgs a{};
   a.q = q; a.ck = ck; a.cv = cv; a.ck_scale = ck_scale; a.cv_scale = cv_scale; a.cap = cap;
   a.idx = idx; a.k = k; a.k_win = k_win; a.v_win = v_win; a.raw_pos0 = raw_pos0; a.L_raw = L_raw;
   a.q_pos0 = q_pos0; a.W = W; a.T_q = T_q; a.H = H; a.sm_log2 = sm_scale * kLog2e; a.out = out; a.lse = lse;
   a.n_list = k + W;
-  return run_attn<false>(a, io_dtype, ckv_dtype, B, d, ws, ws_bytes, static_cast<hipStream_t>(stream));
+  return run_attn<false>(a, io_dtype, ckv_dtype, B, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 extern "C" csa_status_t hca_dense_attn(const void* q, int32_t io_dtype, const void* ck, const void* cv,
@@ -516,11 +680,11 @@ extern "C" csa_status_t hca_dense_attn(const void* q, int32_t io_dtype, const vo
                                 q_pos0, W, B, T_q, H, d, out);
   if (c != CSA_OK) return c;
   if (m_prime < 1) return CSA_EINVAL;
-  if (long(cap) + W > 0x7FFFFFFFL) return CSA_ENOTSUP;
+  if (long(cap) + W > 0x7FFFFFFFL - kNK) return CSA_ENOTSUP;
   AttnArgs a{};
   a.q = q; a.ck = ck; a.cv = cv; a.ck_scale = ck_scale; a.cv_scale = cv_scale; a.cap = cap;
   a.idx = nullptr; a.k = m_prime; a.k_win = k_win; a.v_win = v_win; a.raw_pos0 = raw_pos0; a.L_raw = L_raw;
   a.q_pos0 = q_pos0; a.W = W; a.T_q = T_q; a.H = H; a.sm_log2 = sm_scale * kLog2e; a.out = out; a.lse = lse;
   a.n_list = cap + W;
-  return run_attn<true>(a, io_dtype, ckv_dtype, B, d, ws, ws_bytes, static_cast<hipStream_t>(stream));
+  return run_attn<true>(a, io_dtype, ckv_dtype, B, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }

@@ -111,6 +111,29 @@ CSA_DEV uint32_t block_exclusive_scan(uint32_t v, uint32_t* smem, uint32_t* tota
   return r;
 }
 
+// Block-wide AND / OR of one uint32 per thread (blockDim.x a multiple of 64,
+// at most 1024); `smem` needs 16 words.
+CSA_DEV uint32_t block_reduce_and(uint32_t v, uint32_t* smem) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v &= __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) smem[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t r = 0xFFFFFFFFu;
+  for (int w = 0; w < int(blockDim.x >> 6); ++w) r &= smem[w];
+  __syncthreads();
+  return r;
+}
+CSA_DEV uint32_t block_reduce_or(uint32_t v, uint32_t* smem) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) smem[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t r = 0u;
+  for (int w = 0; w < int(blockDim.x >> 6); ++w) r |= smem[w];
+  __syncthreads();
+  return r;
+}
+
 // --------------------------------------------------------------- status --
 #define CSA_CHECK_LAUNCH()                                   \
   do {                                                       \

@@ -6,11 +6,14 @@
 // library's reading.  This is a pure HBM stream: every input byte is read
 // once and every output byte written once, no reuse.
 //
-// Mapping: one 16-lane group owns one entry.  Lane c of the group owns head
-// columns [8c, 8c+8) (16 B of bf16 per row), so each row of the block is read
-// by the group as one contiguous 256-B segment; a 256-thread block covers 16
-// entries.  Rows of a block are walked with 4 loads in flight per lane for
-// each of K and V.
+// Mapping: lane c of a 16-lane group owns head columns [8c, 8c+8) (16 B of
+// bf16 per row), so a row is read by the group as one contiguous 256-B
+// segment.  Short blocks (m < 32, the CSA case): one group owns one entry and
+// a 256-thread block covers 16 entries, walking rows with 4 loads in flight
+// per lane for each of K and V.  Long blocks (the HCA case, m' = 128): the 16
+// groups of a block share one entry, group r taking rows r, r+16, ..., so all
+// rows are in flight at once; the 16 partial sums meet in LDS and are added in
+// group order.
 #include "common.hpp"
 
 namespace {
@@ -127,24 +130,106 @@ __global__ __launch_bounds__(kBlock) void compress_kernel(const void* __restrict
   store_entry<kOut>(v_out, v_scale, entry, lane_c, av);
 }
 
+// One entry per block: 16 groups split the rows, partial sums meet in LDS.
+template <int kInF32, int kOut>
+__global__ __launch_bounds__(kBlock) void compress_long_kernel(const void* __restrict__ k, const void* __restrict__ v,
+                                                               const float* __restrict__ logits, int n_entries,
+                                                               int ld_in, int m, void* k_out, void* v_out,
+                                                               float* k_scale, float* v_scale, int ld_out) {
+  __shared__ float part[2][kEntriesPerBlock][kHeadDim + 4];
+  const int lane_c = threadIdx.x & (kGroup - 1);
+  const int grp = threadIdx.x / kGroup;
+  const int b = blockIdx.x / n_entries;
+  const int e = blockIdx.x - b * n_entries;
+  const size_t row0 = size_t(b) * ld_in + size_t(e) * m;
+  const float* z = logits + row0;
+
+  float ak[8], av[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { ak[i] = 0.f; av[i] = 0.f; }
+  // rows of the first batch are requested before the logit statistics so the
+  // two memory round trips overlap (every group takes part in the first batch)
+  constexpr int kU = 8;
+  float zmax = 0.f, inv = 0.f;
+  for (int j = grp; j < m; j += kU * kEntriesPerBlock) {
+    float kr[kU][8], vr[kU][8];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int r = j + u * kEntriesPerBlock;
+      if (r < m) {
+        load_row8<kInF32>(k, row0 + r, lane_c, kr[u]);
+        load_row8<kInF32>(v, row0 + r, lane_c, vr[u]);
+      }
+    }
+    if (j == grp) {
+      // softmax statistics over all m logits (every group computes the same values)
+      zmax = -INFINITY;
+      for (int x = lane_c; x < m; x += kGroup) zmax = fmaxf(zmax, z[x]);
+      zmax = group_max<kGroup>(zmax);
+      float zsum = 0.f;
+      for (int x = lane_c; x < m; x += kGroup) zsum += expf(z[x] - zmax);
+      zsum = group_sum<kGroup>(zsum);
+      inv = 1.f / zsum;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int r = j + u * kEntriesPerBlock;
+      if (r < m) {
+        const float a = expf(z[r] - zmax) * inv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ak[i] = fmaf(a, kr[u][i], ak[i]);
+          av[i] = fmaf(a, vr[u][i], av[i]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    part[0][grp][lane_c * 8 + i] = ak[i];
+    part[1][grp][lane_c * 8 + i] = av[i];
+  }
+  __syncthreads();
+  if (grp != 0) return;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float sk = 0.f, sv = 0.f;
+    for (int r = 0; r < kEntriesPerBlock; ++r) {
+      sk += part[0][r][lane_c * 8 + i];
+      sv += part[1][r][lane_c * 8 + i];
+    }
+    ak[i] = sk;
+    av[i] = sv;
+  }
+  const size_t entry = size_t(b) * ld_out + e;
+  store_entry<kOut>(k_out, k_scale, entry, lane_c, ak);
+  store_entry<kOut>(v_out, v_scale, entry, lane_c, av);
+}
+
+template <int kInF32, int kOut>
+hipError_t launch_one(dim3 grid_short, long total, hipStream_t st, const void* k, const void* v, const float* lg, int B,
+                      int ne, int ld_in, int m, void* ko, void* vo, float* ks, float* vs, int ld_out) {
+  if (m >= 32)
+    hipLaunchKernelGGL((compress_long_kernel<kInF32, kOut>), dim3(unsigned(total)), dim3(kBlock), 0, st, k, v, lg, ne,
+                       ld_in, m, ko, vo, ks, vs, ld_out);
+  else
+    hipLaunchKernelGGL((compress_kernel<kInF32, kOut>), grid_short, dim3(kBlock), 0, st, k, v, lg, B, ne, ld_in, m, ko,
+                       vo, ks, vs, ld_out);
+  return hipGetLastError();
+}
+
 template <int kInF32>
-hipError_t launch_compress(int out_dt, dim3 grid, hipStream_t st, const void* k, const void* v, const float* lg, int B,
-                           int ne, int ld_in, int m, void* ko, void* vo, float* ks, float* vs, int ld_out) {
+hipError_t launch_compress(int out_dt, dim3 grid, long total, hipStream_t st, const void* k, const void* v,
+                           const float* lg, int B, int ne, int ld_in, int m, void* ko, void* vo, float* ks, float* vs,
+                           int ld_out) {
   switch (out_dt) {
     case CSA_BF16:
-      hipLaunchKernelGGL((compress_kernel<kInF32, CSA_BF16>), grid, dim3(kBlock), 0, st, k, v, lg, B, ne, ld_in, m, ko,
-                         vo, ks, vs, ld_out);
-      break;
+      return launch_one<kInF32, CSA_BF16>(grid, total, st, k, v, lg, B, ne, ld_in, m, ko, vo, ks, vs, ld_out);
     case CSA_F32:
-      hipLaunchKernelGGL((compress_kernel<kInF32, CSA_F32>), grid, dim3(kBlock), 0, st, k, v, lg, B, ne, ld_in, m, ko,
-                         vo, ks, vs, ld_out);
-      break;
+      return launch_one<kInF32, CSA_F32>(grid, total, st, k, v, lg, B, ne, ld_in, m, ko, vo, ks, vs, ld_out);
     default:
-      hipLaunchKernelGGL((compress_kernel<kInF32, CSA_FP8_E4M3>), grid, dim3(kBlock), 0, st, k, v, lg, B, ne, ld_in, m,
-                         ko, vo, ks, vs, ld_out);
-      break;
+      return launch_one<kInF32, CSA_FP8_E4M3>(grid, total, st, k, v, lg, B, ne, ld_in, m, ko, vo, ks, vs, ld_out);
   }
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -165,10 +250,11 @@ extern "C" csa_status_t csa_compress_kv(const void* k, const void* v, int32_t in
   const long blocks = (total + kEntriesPerBlock - 1) / kEntriesPerBlock;
   if (blocks > 0x7FFFFFFFL) return CSA_EINVAL;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (total > 0x7FFFFFFFL) return CSA_EINVAL;
   hipError_t err = in_dtype == CSA_F32
-                       ? launch_compress<1>(out_dtype, dim3(unsigned(blocks)), st, k, v, logits, B, ne, ld_in, m, k_out,
-                                            v_out, k_scale_out, v_scale_out, ld_out)
-                       : launch_compress<0>(out_dtype, dim3(unsigned(blocks)), st, k, v, logits, B, ne, ld_in, m, k_out,
-                                            v_out, k_scale_out, v_scale_out, ld_out);
+                       ? launch_compress<1>(out_dtype, dim3(unsigned(blocks)), total, st, k, v, logits, B, ne, ld_in, m,
+                                            k_out, v_out, k_scale_out, v_scale_out, ld_out)
+                       : launch_compress<0>(out_dtype, dim3(unsigned(blocks)), total, st, k, v, logits, B, ne, ld_in, m,
+                                            k_out, v_out, k_scale_out, v_scale_out, ld_out);
   return err == hipSuccess ? CSA_OK : CSA_EHIP;
 }

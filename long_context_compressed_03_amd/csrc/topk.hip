@@ -1,4 +1,4 @@
-// Top-k selection of compressed entries: exact radix select with the
+// Top-k selection of compressed entries: exact selection with the
 // lower-index tie rule, output in ascending index order.
 //
 // The pages keep the k compressed entries the indexer finds most relevant
@@ -8,22 +8,51 @@
 //
 // One 1024-thread block per query row.  Scores become order-preserving
 // uint32 keys (negative floats bit-inverted, non-negative ones with the sign
-// bit set, -0 folded onto +0).  Radix passes over the top 11, next 11 and last
-// 10 bits narrow the k-th key: after each pass a histogram in LDS and one
-// block scan find the bin holding the k-th largest key; the search stops as
-// soon as that bin is taken whole.  Rows of up to 32768 entries are held in
-// LDS after the first read (one pad word per 32 keeps the per-thread chunk
-// reads of the emission pass free of bank conflicts); longer rows are
-// re-read from L2 on every pass.  Emission: each thread owns a contiguous
-// index range, so two block-wide exclusive scans (equal-key ranks, then output
-// offsets) give every selected index its slot in ascending order.
+// bit set, -0 folded onto +0); key 0 (a NaN pattern) marks "not a candidate".
+// A row is held in registers, 32768 keys at a time: each thread holds 32
+// keys, and the element a lane loads is chosen so that every wave-wide load
+// covers 64 consecutive indices (coalesced 256-byte reads) and every wave
+// ballot of a per-key predicate IS two words of an index-ordered bitmap.
+//
+// On one CU the kernel is bound by per-key VALU work and LDS traffic, so the
+// number of passes over the keys is kept to three:
+//  1. load + key transform + an LDS histogram of the top 14 key bits (sign,
+//     exponent, 5 mantissa bits: a fixed, range-free bucketing);
+//     one wave then finds the bucket holding the k-th largest key;
+//  2. the keys of that bucket (usually a few hundred) are appended to an LDS
+//     list with one atomic per wave, and an exact radix select over the list
+//     finds the k-th key and how many keys equal to it are still needed
+//     (rows whose bucket is too crowded take radix passes over all keys);
+//  3. emission: ballots of "greater" and "equal" give the bitmaps directly;
+//     thread w then owns 32 consecutive indices, and one block scan of the
+//     packed counts gives each selected index its slot: #greater before it +
+//     min(#equal before it, equal keys still needed).
 #include "common.hpp"
 
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kCacheMax = 32768;
-constexpr int kCacheWords = kCacheMax + kCacheMax / 32;
+constexpr int kPer = 8;                        // rounds of 4 keys per thread
+constexpr int kRound = kThreads * 4;           // 4096 consecutive keys per round
+constexpr int kSuper = kRound * kPer;          // 32768 keys in registers
+constexpr int kWords = kSuper / 32;            // bitmap words per super-tile
+constexpr int kBucketShift = 18;               // 14-bit buckets
+constexpr int kBuckets = 1 << (32 - kBucketShift);
+constexpr int kCand = 4096;                    // capacity of the threshold-bucket list
+
+struct Sel {
+  uint32_t bin, remaining, bincount;
+};
+
+struct Shared {
+  uint32_t hist[kBuckets];
+  uint32_t bm_gt[kWords];
+  uint32_t bm_eq[kWords];
+  uint32_t cand[kCand];
+  uint32_t smem[32];
+  uint32_t n_cand;
+  Sel sel;
+};
 
 CSA_DEV uint32_t ordered_key(float s) {
   uint32_t u = __float_as_uint(s);
@@ -31,21 +60,132 @@ CSA_DEV uint32_t ordered_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-CSA_DEV int lds_pos(int x) { return x + (x >> 5); }
+// Index of key (j, c) of this thread within its super-tile.
+CSA_DEV int key_index(int j, int c) { return j * kRound + c * kThreads + threadIdx.x; }
+
+// Keys of super-tile `st`: wave w, lane l, key (j, c) is index j*4096 + c*1024 + 64w + l.
+CSA_DEV void load_keys(const float* __restrict__ src, int nv, int st, uint32_t (&key)[kPer][4]) {
+  const int base = st * kSuper;
+  float v[kPer][4];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int x = base + key_index(j, c);
+      v[j][c] = x < nv ? src[x] : 0.f;
+    }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) key[j][c] = base + key_index(j, c) < nv ? ordered_key(v[j][c]) : 0u;
+}
+
+// The whole block finds, among nb bins counted from the top, the bin where
+// the running count first reaches `remaining`: thread t sums the nb/1024 bins
+// t*per .. from the top (a short stride, so its 16-byte LDS reads spread over
+// the banks), one block scan places the crossing inside one thread's range.
+// Every thread must call it; the result lands in *out.
+CSA_DEV void find_bin(const uint32_t* hist, int nb, uint32_t remaining, Sel* out, uint32_t* smem) {
+  const int tid = threadIdx.x;
+  const int per = nb > kThreads ? nb / kThreads : 1;
+  const int lo = tid * per;                    // bins nb-1-lo ... nb-per-lo (descending)
+  uint32_t mine = 0u;
+  if (lo < nb) {
+    if (per >= 4) {
+      const u32x4* h4 = reinterpret_cast<const u32x4*>(hist + (nb - lo - per));
+      for (int x = 0; x < per / 4; ++x) {
+        const u32x4 v = h4[x];
+        mine += v[0] + v[1] + v[2] + v[3];
+      }
+    } else {
+      for (int x = 0; x < per; ++x) mine += hist[nb - 1 - (lo + x)];
+    }
+  }
+  uint32_t tot;
+  const uint32_t excl = block_exclusive_scan(mine, smem, &tot);
+  if (lo < nb && excl < remaining && remaining <= excl + mine) {
+    uint32_t run = excl;
+    for (int x = 0; x < per; ++x) {
+      const int bin = nb - 1 - (lo + x);
+      const uint32_t c = hist[bin];
+      if (run < remaining && remaining <= run + c) {
+        out->bin = uint32_t(bin);
+        out->remaining = remaining - run;
+        out->bincount = c;
+        break;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+}
+
+CSA_DEV void block_and_or(uint32_t& a, uint32_t& b, uint32_t* smem) {
+  for (int o = 32; o > 0; o >>= 1) {
+    a &= __shfl_xor(a, o);
+    b |= __shfl_xor(b, o);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { smem[w] = a; smem[16 + w] = b; }
+  __syncthreads();
+  a = smem[0];
+  b = smem[16];
+  for (int x = 1; x < kThreads / 64; ++x) { a &= smem[x]; b |= smem[16 + x]; }
+  __syncthreads();
+}
+
+// Exact radix refinement of (prefix, mask) over a set of keys visited by
+// `each(fn)` (fn is called for every key of the set, in any order, on every
+// thread; 0 = absent).  On entry the set's keys all match (key & mask) ==
+// prefix and `remaining` of them are wanted from the top; on return (prefix,
+// mask) select the k-th key and `remaining` counts the keys equal to it that
+// are still needed.
+template <typename Each>
+CSA_DEV void refine(Each each, uint32_t& prefix, uint32_t& mask, uint32_t& remaining, Shared& sh) {
+  const int tid = threadIdx.x;
+  uint32_t k_and = 0xFFFFFFFFu, k_or = 0u;
+  each([&](uint32_t kk) {
+    if (kk != 0u && (kk & mask) == prefix) { k_and &= kk; k_or |= kk; }
+  });
+  block_and_or(k_and, k_or, sh.smem);
+  if (k_or == 0u) return;
+  const int common = (k_and ^ k_or) == 0u ? 32 : __clz(k_and ^ k_or);
+  mask = common == 0 ? 0u : (common == 32 ? 0xFFFFFFFFu : ~(0xFFFFFFFFu >> common));
+  prefix = k_and & mask;
+  int bits_left = 32 - common;
+  while (bits_left > 0) {
+    const int width = bits_left < 11 ? bits_left : 11;
+    const int shift = bits_left - width;
+    const int nb = 1 << width;
+    bits_left = shift;
+    for (int j = tid; j < nb; j += kThreads) sh.hist[j] = 0u;
+    __syncthreads();
+    const uint32_t pm = prefix, mm = mask;
+    each([&](uint32_t kk) {
+      if (kk != 0u && (kk & mm) == pm) atomicAdd(&sh.hist[(kk >> shift) & uint32_t(nb - 1)], 1u);
+    });
+    __syncthreads();
+    find_bin(sh.hist, nb, remaining, &sh.sel, sh.smem);
+    prefix |= sh.sel.bin << shift;
+    mask |= uint32_t(nb - 1) << shift;
+    remaining = sh.sel.remaining;
+    const bool done = sh.sel.bincount == remaining;   // the bin is taken whole
+    __syncthreads();
+    if (done) break;
+  }
+}
 
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores,
                                                         const int32_t* __restrict__ q_pos0, int T_q, int cap, int m,
                                                         int k, int32_t* __restrict__ idx) {
-  extern __shared__ uint32_t lds[];
-  uint32_t* keys = lds;                       // kCacheWords (only when cached)
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t scan_smem[17];
-  __shared__ uint32_t sel_bin, sel_remaining, sel_bincount;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  Shared& sh = *reinterpret_cast<Shared*>(smem_raw);
 
   const int row = blockIdx.x;
   const int b = row / T_q;
   const int i = row - b * T_q;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int t = q_pos0[b] + i;
   int nv = (t + 1) / m;
   nv = max(0, min(nv, cap));
@@ -55,73 +195,139 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     return;
   }
   const float* src = scores + size_t(row) * cap;
-  const bool cached = nv <= kCacheMax;
+  const int n_super = (nv + kSuper - 1) / kSuper;
+  const uint64_t lanes_below = (uint64_t(1) << lane) - 1u;
 
-  uint32_t prefix = 0u, mask = 0u;
-  uint32_t remaining = uint32_t(k);
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nbits = pass == 2 ? 10 : 11;
-    const int nb = 1 << nbits;
-    for (int j = tid; j < nb; j += kThreads) hist[j] = 0u;
-    __syncthreads();
-    for (int x = tid; x < nv; x += kThreads) {
-      uint32_t key;
-      if (pass == 0 || !cached) {
-        key = ordered_key(src[x]);
-        if (pass == 0 && cached) keys[lds_pos(x)] = key;
-      } else {
-        key = keys[lds_pos(x)];
+  // ---- pass 1: keys, bucket histogram
+  for (int j = tid; j < kBuckets; j += kThreads) sh.hist[j] = 0u;
+  if (tid == 0) sh.n_cand = 0u;
+  __syncthreads();
+  uint32_t key[kPer][4];
+#pragma unroll 1
+  for (int st = 0; st < n_super; ++st) {
+    load_keys(src, nv, st, key);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (key[j][c]) atomicAdd(&sh.hist[key[j][c] >> kBucketShift], 1u);
+  }
+  __syncthreads();
+  find_bin(sh.hist, kBuckets, uint32_t(k), &sh.sel, sh.smem);
+  const uint32_t B = sh.sel.bin;
+  uint32_t remaining = sh.sel.remaining;
+  const uint32_t cnt = sh.sel.bincount;
+  uint32_t mask = ~((1u << kBucketShift) - 1u);
+  uint32_t prefix = B << kBucketShift;
+  __syncthreads();
+
+  // visits every key of the row (reloading super-tiles when the row is long)
+  auto each_key = [&](auto fn) {
+#pragma unroll 1
+    for (int st = 0; st < n_super; ++st) {
+      if (n_super > 1) load_keys(src, nv, st, key);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) fn(key[j][c]);
+    }
+  };
+
+  if (cnt != remaining) {
+    if (cnt <= uint32_t(kCand)) {
+      // ---- pass 2: list the threshold bucket, refine over the list
+#pragma unroll 1
+      for (int st = 0; st < n_super; ++st) {
+        if (n_super > 1) load_keys(src, nv, st, key);
+        uint32_t wave_total = 0u;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) wave_total += __popcll(__ballot(key[j][c] && (key[j][c] >> kBucketShift) == B));
+        uint32_t base = 0u;
+        if (lane == 0 && wave_total) base = atomicAdd(&sh.n_cand, wave_total);
+        base = __shfl(base, 0);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const bool want = key[j][c] && (key[j][c] >> kBucketShift) == B;
+            const uint64_t bal = __ballot(want);
+            if (want) sh.cand[base + __popcll(bal & lanes_below)] = key[j][c];
+            base += __popcll(bal);
+          }
       }
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & uint32_t(nb - 1)], 1u);
+      __syncthreads();
+      const int nc = int(sh.n_cand);
+      auto each_cand = [&](auto fn) {
+        for (int x = tid; x < nc; x += kThreads) fn(sh.cand[x]);
+      };
+      refine(each_cand, prefix, mask, remaining, sh);
+    } else {
+      refine(each_key, prefix, mask, remaining, sh);
     }
-    __syncthreads();
-    // bins in descending order: thread tid owns bins hi = nb-1-2*tid and lo = hi-1
-    const int hi = nb - 1 - 2 * tid;
-    const uint32_t c_hi = hi >= 0 ? hist[hi] : 0u;
-    const uint32_t c_lo = hi >= 1 ? hist[hi - 1] : 0u;
-    uint32_t tot;
-    const uint32_t above = block_exclusive_scan(c_hi + c_lo, scan_smem, &tot);
-    if (hi >= 0 && above < remaining && remaining <= above + c_hi) {
-      sel_bin = uint32_t(hi); sel_remaining = remaining - above; sel_bincount = c_hi;
-    }
-    if (hi >= 1 && above + c_hi < remaining && remaining <= above + c_hi + c_lo) {
-      sel_bin = uint32_t(hi - 1); sel_remaining = remaining - above - c_hi; sel_bincount = c_lo;
-    }
-    __syncthreads();
-    prefix |= sel_bin << shift;
-    mask |= uint32_t(nb - 1) << shift;
-    remaining = sel_remaining;
-    const bool whole = sel_bincount == remaining;
-    __syncthreads();
-    if (whole) break;
   }
 
-  // emission: entries with (key & mask) > prefix are in; of those equal, the
-  // first `remaining` by index
-  const int chunk = (nv + kThreads - 1) / kThreads;
-  const int x0 = min(tid * chunk, nv);
-  const int x1 = min(x0 + chunk, nv);
-  uint32_t n_gt = 0, n_eq = 0;
-  for (int x = x0; x < x1; ++x) {
-    const uint32_t key = (cached ? keys[lds_pos(x)] : ordered_key(src[x])) & mask;
-    n_gt += key > prefix;
-    n_eq += key == prefix;
-  }
-  uint32_t tot;
-  const uint32_t eq_before = block_exclusive_scan(n_eq, scan_smem, &tot);
-  const uint32_t take_eq = remaining > eq_before ? min(remaining - eq_before, n_eq) : 0u;
-  uint32_t pos = block_exclusive_scan(n_gt + take_eq, scan_smem, &tot);
-  uint32_t eq_seen = 0;
-  for (int x = x0; x < x1; ++x) {
-    const uint32_t key = (cached ? keys[lds_pos(x)] : ordered_key(src[x])) & mask;
-    bool take = key > prefix;
-    if (key == prefix) {
-      take = eq_seen < take_eq;
-      ++eq_seen;
+  // ---- pass 3: emission in index order
+  uint32_t gt_off = 0u, eq_off = 0u;
+  const int w = tid >> 6;
+#pragma unroll 1
+  for (int st = 0; st < n_super; ++st) {
+    if (n_super > 1) load_keys(src, nv, st, key);
+    __syncthreads();   // earlier readers of the bitmaps are done
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t km = key[j][c] & mask;
+        const uint64_t g = __ballot(key[j][c] && km > prefix);
+        const uint64_t e = __ballot(key[j][c] && km == prefix);
+        // this wave's 64 keys are indices j*4096 + c*1024 + 64w + lane: two bitmap words
+        const int word = (j * kRound + c * kThreads + 64 * w) >> 5;
+        if (lane == 0) {
+          sh.bm_gt[word] = uint32_t(g);
+          sh.bm_gt[word + 1] = uint32_t(g >> 32);
+          sh.bm_eq[word] = uint32_t(e);
+          sh.bm_eq[word + 1] = uint32_t(e >> 32);
+        }
+      }
+    __syncthreads();
+    const uint32_t wg = sh.bm_gt[tid];
+    const uint32_t we = sh.bm_eq[tid];
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan((uint32_t(__popc(we)) << 16) | uint32_t(__popc(wg)), sh.smem, &tot);
+    uint32_t gt_before = gt_off + (ex & 0xFFFFu);
+    uint32_t eq_before = eq_off + (ex >> 16);
+    const int x0 = st * kSuper + tid * 32;
+    uint32_t any = wg | we;
+    while (any) {
+      const int bit = __ffs(any) - 1;
+      any &= any - 1u;
+      if ((wg >> bit) & 1u) {
+        out[gt_before + min(eq_before, remaining)] = x0 + bit;
+        ++gt_before;
+      } else {
+        if (eq_before < remaining) out[gt_before + eq_before] = x0 + bit;
+        ++eq_before;
+      }
     }
-    if (take) out[pos++] = x;
+    gt_off += tot & 0xFFFFu;
+    eq_off += tot >> 16;
   }
+}
+
+hipError_t launch_topk(long rows, hipStream_t st, const float* scores, const int32_t* q_pos0, int T_q, int cap, int m,
+                       int k, int32_t* idx) {
+  static bool attr = false;   // more than 64 KB of LDS needs the opt-in
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(Shared)));
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(topk_kernel, dim3(unsigned(rows)), dim3(kThreads), sizeof(Shared), st, scores, q_pos0, T_q, cap,
+                     m, k, idx);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -135,15 +341,6 @@ extern "C" csa_status_t csa_topk(const float* scores, const int32_t* q_pos0, int
   const long rows = long(B) * T_q;
   if (rows == 0) return CSA_OK;
   if (rows > 0x7FFFFFFFL) return CSA_ENOTSUP;
-  static bool attr_set = false;
-  const size_t dyn = size_t(kCacheWords) * sizeof(uint32_t);
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            int(dyn)) != hipSuccess)
-      return CSA_EHIP;
-    attr_set = true;
-  }
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(topk_kernel, dim3(unsigned(rows)), dim3(kThreads), dyn, st, scores, q_pos0, T_q, cap, m, k, idx);
-  return hipGetLastError() == hipSuccess ? CSA_OK : CSA_EHIP;
+  const hipError_t e = launch_topk(rows, static_cast<hipStream_t>(stream), scores, q_pos0, T_q, cap, m, k, idx);
+  return e == hipSuccess ? CSA_OK : CSA_EHIP;
 }

@@ -48,6 +48,9 @@ COMPRESS_CASES = [
     ("bf16", "bf16", 5, 2, 5 * 19),
     ("f32", "fp8", 4, 1, 4 * 40),
     ("bf16", "bf16", 128, 1, 128 * 3),
+    ("f32", "bf16", 32, 2, 32 * 7),
+    ("bf16", "fp8", 64, 3, 64 * 5 + 0),
+    ("bf16", "f32", 200, 1, 200 * 2),
 ]
 
 
@@ -161,6 +164,10 @@ def test_topk_on_indexer_scores(csa):
     (2, 2, 3000, 2048, [11999, 5000], 30),        # fewer visible than k on row 2
     (1, 1, 32768, 1024, [131071], 1 << 20),       # the 128K decode row shape
     (1, 3, 700, 700, [2799], 3),                  # k == visible count on the last row
+    (1, 2, 33333, 512, [133331], 10),             # unaligned rows, two register tiles
+    (2, 1, 4999, 100, [19995, 100], 50),          # unaligned rows; one row below k
+    (1, 2, 20000, 1000, [79999], 3),              # crowded threshold bin: exact radix passes
+    (3, 1, 32768, 1024, [131071] * 3, 1 << 16),   # the 128K decode shape, several rows
 ])
 def test_topk_random(csa, B, T, cap, k, pos, distinct):
     say(f"topk B={B} T={T} cap={cap} k={k}")
@@ -213,6 +220,10 @@ SPARSE_CASES = [
     ("bf16", "bf16", 1, 520, 16, 300, 20, 8, 528, [680]),
     ("bf16", "bf16", 2, 2, 32, 100, 8, 0, 1, [399, 2]),      # no window; tiny contexts
     ("bf16", "fp8", 1, 1, 128, 256, 64, 128, 128, [1023]),
+    # many query rows: one block per query, waves split the heads
+    ("bf16", "bf16", 1, 300, 64, 600, 100, 32, 332, [2000]),
+    ("f32", "f32", 1, 256, 64, 320, 64, 16, 272, [1000]),
+    ("bf16", "fp8", 1, 260, 64, 320, 40, 128, 388, [1000]),
 ]
 
 
@@ -248,6 +259,8 @@ DENSE_CASES = [
     ("f32", "fp8", 1, 5, 16, 32, 64, 40, 48, [2040]),
     ("bf16", "fp8", 1, 600, 16, 128, 12, 128, 728, [1000]),
     ("bf16", "bf16", 1, 4, 16, 4, 8, 0, 1, [0]),            # empty key sets
+    ("bf16", "bf16", 2, 130, 64, 16, 100, 32, 162, [1400, 30]),   # one block per query
+    ("bf16", "fp8", 1, 300, 64, 128, 20, 128, 428, [2300]),
 ]
 
 
