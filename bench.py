@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="first run 10 plain device copies of 256 MiB (reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -304,7 +306,13 @@ KERNEL_SOURCES = {"indexer_scores": ["indexer.hip", "common.hpp"],
 
 
 def measured_traffic(workload, kernel):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if still current."""
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if still current.
+
+    The summary (profiles/<kernel>_<workload>_pmc.json) holds FETCH_SIZE + WRITE_SIZE
+    per dispatch of the kernel, scaled by what the same counters read for a plain
+    256 MiB device copy, and the hash of the kernel's sources when it was taken; a
+    changed kernel gives null.
+    """
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
@@ -366,6 +374,13 @@ def main():
         raise SystemExit("no GPU visible")
     import long_context_compressed_03_amd as csa
     csa.load()
+    if args.calibrate_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        c = torch.empty_like(a)
+        for _ in range(10):
+            c.copy_(a)
+        torch.cuda.synchronize()
+        del a, c
     st = build(args)
     ms, done, wall = time_step(st, args.steps, args.warmup, not args.no_graph)
     kt = time_kernels(st, reps=max(10 * len(st.copies), 200))
