@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--workload", default="csa_decode_128k",
                    choices=["csa_decode_128k", "hca_decode_1m", "csa_prefill_256k", "pair_1m"])
     p.add_argument("--rotate", type=int, default=0, help="input copies (0 = auto)")
+    p.add_argument("--indexer", default="auto", choices=["auto", "fused", "unfused"],
+                   help="CSA scoring + selection as one fused call or as csa_indexer_scores then "
+                        "csa_topk (auto: fused for prefill chunks, unfused for decode)")
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -55,6 +58,22 @@ def parse():
 # --------------------------------------------------------------------------
 # Workload construction (device tensors)
 
+class Kernel:
+    """One ABI call of a step: fn(copy), its algorithmic bytes and flops, and the peak
+    of the unit its flops run on (MXFP4 or bf16 matrix cores)."""
+
+    def __init__(self, name, fn, nbytes, flops, mfma_peak, src):
+        self.name, self.fn, self.nbytes, self.flops = name, fn, int(nbytes), int(flops)
+        self.mfma_peak, self.src = mfma_peak, src
+
+    @property
+    def bound(self):
+        """The roofline that bounds the call: the larger of bytes/HBM peak and flops/MFMA peak."""
+        t_mem = self.nbytes / (HBM_PEAK_GBS * 1e9)
+        t_mfma = self.flops / (self.mfma_peak * 1e12) if self.flops else 0.0
+        return "mfma" if t_mfma > t_mem else "hbm"
+
+
 class Step:
     """One workload: device inputs (R rotating copies) and the launches of one step."""
 
@@ -62,26 +81,18 @@ class Step:
         self.name = name
         self.q_tokens = q_tokens
         self.copies = []
-        self.kernels = {}     # name -> (fn(copy), algorithmic bytes, flops, bound)
+        self.kernels = {}
         self.order = []
         self.config = {}
+        self.layers = []      # host inputs per layer, for the CPU baseline
 
-    def add(self, name, fn, nbytes, flops, bound):
-        self.kernels[name] = (fn, nbytes, flops, bound)
-        self.order.append(name)
+    def add(self, k):
+        self.kernels[k.name] = k
+        self.order.append(k.name)
 
     def run(self, c):
         for n in self.order:
-            self.kernels[n][0](c)
-
-
-def _dev_copies(tensors, R):
-    import torch
-    base = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in tensors.items()}
-    out = [base]
-    for _ in range(R - 1):
-        out.append({k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in base.items()})
-    return out
+            self.kernels[n].fn(c)
 
 
 def _t(x, kind):
@@ -97,112 +108,172 @@ def _t(x, kind):
     raise ValueError(kind)
 
 
-def csa_decode_tensors(wl, seed=0):
-    """Host inputs of a CSA decode step (wl: csa_synth Workload)."""
-    import torch
+def host_layer(wl, seed=0):
+    """Host inputs of one layer's calls for workload wl (a csa_synth Workload)."""
     from csa_synth import attn_inputs, compress_inputs, indexer_inputs
-    B, cap, W, H = wl.B, wl.cap, wl.W, wl.H
-    kv = compress_inputs(B, wl.L_raw, "bf16", seed=seed, tag=wl.tag * 10 + 1, outliers=wl.outliers)
-    ix = indexer_inputs(B, 1, cap, wl.H_I, wl.d_I, seed=seed, tag=wl.tag * 10 + 2)
-    at = attn_inputs(B, 1, H, cap, 1, "bf16", wl.ckv, seed=seed, tag=wl.tag * 10 + 3,
-                     outliers=wl.outliers)
+    h = {"wl": wl}
+    h["kv"] = compress_inputs(wl.B, wl.L_raw, "bf16", seed=seed, tag=wl.tag * 10 + 1,
+                              outliers=wl.outliers)
+    h["at"] = attn_inputs(wl.B, wl.T_q, wl.H, wl.cap, 1, "bf16", wl.ckv, seed=seed,
+                          tag=wl.tag * 10 + 3, outliers=wl.outliers)
+    if wl.kind == "csa":
+        h["ix"] = indexer_inputs(wl.B, wl.T_q, wl.cap, wl.H_I, wl.d_I, seed=seed,
+                                 tag=wl.tag * 10 + 2)
+    return h
+
+
+def pool_range(wl):
+    """(rows pooled, first raw row, first entry written) of the step's compression: the block
+    a decode query completes, or every block of a prefill chunk."""
+    L = wl.T_q if wl.T_q > 1 else wl.m
+    entry0 = (wl.q_pos0[0] + wl.T_q) // wl.m - L // wl.m
+    return L, wl.L_raw - L, entry0
+
+
+def device_layer(h, prefix):
+    """Host arrays of one layer -> dict of CPU tensors keyed prefix+name."""
+    import torch
+    wl, kv, at = h["wl"], h["kv"], h["at"]
     T = dict(kw=_t(kv["K"], "bf16"), vw=_t(kv["V"], "bf16"), logits=_t(kv["logits"], "f32"),
-             qc=_t(ix["q_codes"], "u8"), qe=_t(ix["q_e8m0"], "u8"), w=_t(ix["w"], "f32"),
-             kc=_t(ix["k_codes"], "u8"), ke=_t(ix["k_e8m0"], "u8"), q=_t(at["q"], "bf16"),
-             pos=_t(np.array(wl.q_pos0), "i32"), raw0=_t(np.array(wl.raw_pos0), "i32"))
+             q=_t(at["q"], "bf16"), pos=_t(np.array(wl.q_pos0), "i32"),
+             raw0=_t(np.array(wl.raw_pos0), "i32"),
+             out=torch.empty((wl.B, wl.T_q, wl.H, 128), dtype=torch.bfloat16))
     if wl.ckv == "fp8":
         T.update(ck=_t(at["cK"], "u8"), cv=_t(at["cV"], "u8"), cks=_t(at["cK_scale"], "f32"),
                  cvs=_t(at["cV_scale"], "f32"))
     else:
         T.update(ck=_t(at["cK"], "bf16"), cv=_t(at["cV"], "bf16"), cks=None, cvs=None)
-    T["scores"] = torch.empty((B, 1, cap), dtype=torch.float32)
-    T["idx"] = torch.empty((B, 1, wl.k), dtype=torch.int32)
-    T["out"] = torch.empty((B, 1, H, 128), dtype=torch.bfloat16)
-    return T
+    if wl.kind == "csa":
+        ix = h["ix"]
+        T.update(qc=_t(ix["q_codes"], "u8"), qe=_t(ix["q_e8m0"], "u8"), w=_t(ix["w"], "f32"),
+                 kc=_t(ix["k_codes"], "u8"), ke=_t(ix["k_e8m0"], "u8"),
+                 scores=torch.empty((wl.B, wl.T_q, wl.cap), dtype=torch.float32),
+                 idx=torch.empty((wl.B, wl.T_q, wl.k), dtype=torch.int32))
+    return {prefix + n: v for n, v in T.items()}
 
 
-def build_csa_decode(wl, R):
+def visible(wl):
+    """Visible compressed entries summed over the step's query rows."""
+    t = np.asarray(wl.q_pos0)[:, None] + np.arange(wl.T_q)[None, :]
+    return int(np.minimum((t + 1) // wl.m, wl.cap).sum())
+
+
+def add_layer(st, h, prefix, indexer="auto"):
+    """The calls of one CSA or HCA layer: compress, (indexer, top-k,) attention."""
     import long_context_compressed_03_amd as csa
-    T = csa_decode_tensors(wl)
-    copies = _dev_copies(T, R)
-    B, cap, m, k, W, H = wl.B, wl.cap, wl.m, wl.k, wl.W, wl.H
-    st = Step(wl.name, B)
-    st.copies = copies
+    wl = h["wl"]
+    p = prefix
+    B, m, W, H, rows = wl.B, wl.m, wl.W, wl.H, wl.B * wl.T_q
+    L, row0, entry0 = pool_range(wl)
     ent = 264 if wl.ckv == "fp8" else 512
-    idx_bytes = wl.d_I // 2 + wl.d_I // 32
+    nvis_sum = visible(wl)
+    name = (lambda n: f"{prefix}{n}") if prefix else (lambda n: n)
 
     def f_compress(c):
-        csa.csa_compress_kv(c["kw"], c["vw"], c["logits"], m, c["ck"], c["cv"], c["cks"], c["cvs"],
-                            L=m, row0=wl.L_raw - m, entry0=cap - 1)
+        csa.csa_compress_kv(c[p + "kw"], c[p + "vw"], c[p + "logits"], m, c[p + "ck"], c[p + "cv"],
+                            c[p + "cks"], c[p + "cvs"], L=L, row0=row0, entry0=entry0)
+    st.add(Kernel(name("compress_kv"), f_compress, B * (L * 516 + (L // m) * ent), 0,
+                  BF16_PEAK_TFLOPS, "compress_kv"))
+    q_bytes = rows * H * 128 * 4          # bf16 query in + bf16 output
+    if wl.kind == "csa":
+        k = wl.k
+        idx_bytes = wl.d_I // 2 + wl.d_I // 32
 
-    def f_indexer(c):
-        csa.csa_indexer_scores(c["qc"], c["qe"], c["w"], c["kc"], c["ke"], c["pos"], m, c["scores"])
+        def f_indexer(c):
+            csa.csa_indexer_scores(c[p + "qc"], c[p + "qe"], c[p + "w"], c[p + "kc"], c[p + "ke"],
+                                   c[p + "pos"], m, c[p + "scores"])
 
-    def f_topk(c):
-        csa.csa_topk(c["scores"], c["pos"], m, k, c["idx"])
+        def f_topk(c):
+            csa.csa_topk(c[p + "scores"], c[p + "pos"], m, k, c[p + "idx"])
 
-    def f_attn(c):
-        csa.csa_sparse_attn(c["q"], c["ck"], c["cv"], c["idx"], c["kw"], c["vw"], c["raw0"], c["pos"],
-                            W, ck_scale=c["cks"], cv_scale=c["cvs"], out=c["out"])
-    st.add("compress_kv", f_compress, B * (m * 512 + m * 4 + ent), 0, "hbm")
-    st.add("indexer_scores", f_indexer, B * cap * (idx_bytes + 4), 2 * B * cap * wl.H_I * wl.d_I,
-           "hbm")
-    st.add("topk", f_topk, B * cap * 4 + B * k * 4, 0, "hbm")
-    st.add("sparse_attn", f_attn, B * (k * ent + W * 512 + H * 128 * 4), 4 * B * H * 128 * (k + W),
-           "hbm")
-    st.config = {"workload": wl.name, "batch": B, "context": wl.q_pos0[0] + 1, "query_heads": H,
-                 "kv_heads": 1, "head_dim": 128, "m": m, "compressed_entries": cap,
-                 "indexer": f"{wl.H_I}x{wl.d_I} MXFP4", "top_k": k, "window": W,
-                 "compressed_kv": wl.ckv, "window_kv": "bf16"}
-    return st
+        def f_attn(c):
+            csa.csa_sparse_attn(c[p + "q"], c[p + "ck"], c[p + "cv"], c[p + "idx"], c[p + "kw"],
+                                c[p + "vw"], c[p + "raw0"], c[p + "pos"], W, ck_scale=c[p + "cks"],
+                                cv_scale=c[p + "cvs"], out=c[p + "out"])
+        fused = indexer == "fused" or (indexer == "auto" and wl.T_q > 1)
+        if fused:
+            def f_fused(c):
+                csa.csa_indexer_topk(c[p + "qc"], c[p + "qe"], c[p + "w"], c[p + "kc"], c[p + "ke"],
+                                     c[p + "pos"], m, k, c[p + "idx"])
+            # keys once, the 16-bit score keys written and read back, the indices
+            st.add(Kernel(name("indexer_topk"), f_fused,
+                          B * wl.cap * idx_bytes + rows * wl.cap * 2 + nvis_sum * 2 + rows * k * 4
+                          + rows * wl.H_I * (idx_bytes + 4),
+                          2 * wl.H_I * wl.d_I * nvis_sum, MXFP4_PEAK_TFLOPS, "indexer_topk"))
+        else:
+            st.add(Kernel(name("indexer_scores"), f_indexer,
+                          B * wl.cap * idx_bytes + rows * wl.cap * 4 + rows * wl.H_I * (idx_bytes + 4),
+                          2 * wl.H_I * wl.d_I * nvis_sum, MXFP4_PEAK_TFLOPS, "indexer_scores"))
+            st.add(Kernel(name("topk"), f_topk, nvis_sum * 4 + rows * k * 4, 0, BF16_PEAK_TFLOPS,
+                          "topk"))
+        # distinct bytes: every selected entry at most once per sequence, the window rows once
+        sel = min(B * wl.cap, rows * k)
+        st.add(Kernel(name("sparse_attn"), f_attn,
+                      sel * ent + B * wl.L_raw * 512 + q_bytes + rows * k * 4,
+                      4 * H * 128 * rows * (k + W), BF16_PEAK_TFLOPS, "sparse_attn"))
+    else:
+        def f_attn(c):
+            csa.hca_dense_attn(c[p + "q"], c[p + "ck"], c[p + "cv"], m, c[p + "kw"], c[p + "vw"],
+                               c[p + "raw0"], c[p + "pos"], W, ck_scale=c[p + "cks"],
+                               cv_scale=c[p + "cvs"], out=c[p + "out"])
+        nv_max = min((wl.q_pos0[0] + wl.T_q) // m, wl.cap)
+        st.add(Kernel(name("dense_attn"), f_attn, B * nv_max * ent + B * wl.L_raw * 512 + q_bytes,
+                      4 * H * 128 * (nvis_sum + rows * W), BF16_PEAK_TFLOPS, "dense_attn"))
 
 
-def build_hca_decode(wl, R):
-    import torch
-    import long_context_compressed_03_amd as csa
-    from csa_synth import attn_inputs, compress_inputs
-    B, cap, mp, W, H = wl.B, wl.cap, wl.m, wl.W, wl.H
-    kv = compress_inputs(B, wl.L_raw, "bf16", seed=0, tag=wl.tag * 10 + 1, outliers=wl.outliers)
-    at = attn_inputs(B, 1, H, cap, 1, "bf16", "fp8", seed=0, tag=wl.tag * 10 + 3,
-                     outliers=wl.outliers)
-    T = dict(kw=_t(kv["K"], "bf16"), vw=_t(kv["V"], "bf16"), logits=_t(kv["logits"], "f32"),
-             q=_t(at["q"], "bf16"), ck=_t(at["cK"], "u8"), cv=_t(at["cV"], "u8"),
-             cks=_t(at["cK_scale"], "f32"), cvs=_t(at["cV_scale"], "f32"),
-             pos=_t(np.array(wl.q_pos0), "i32"), raw0=_t(np.array(wl.raw_pos0), "i32"),
-             out=torch.empty((B, 1, H, 128), dtype=torch.bfloat16))
-    st = Step(wl.name, B)
-    st.copies = _dev_copies(T, R)
+def layer_config(wl):
+    c = {"batch": wl.B, "query_tokens_per_seq": wl.T_q, "context": wl.q_pos0[0] + wl.T_q,
+         "query_heads": wl.H, "kv_heads": 1, "head_dim": 128, "compressed_entries": wl.cap,
+         "window": wl.W, "window_kv": "bf16",
+         "compressed_kv": "fp8_e4m3+fp32 scale" if wl.ckv == "fp8" else wl.ckv}
+    if wl.kind == "csa":
+        c.update(m=wl.m, indexer=f"{wl.H_I}x{wl.d_I} MXFP4", top_k=wl.k)
+    else:
+        c.update(m_prime=wl.m)
+    if wl.outliers:
+        c["outliers"] = "1% x8"
+    return c
 
-    def f_compress(c):
-        csa.csa_compress_kv(c["kw"], c["vw"], c["logits"], mp, c["ck"], c["cv"], c["cks"], c["cvs"],
-                            L=mp, row0=wl.L_raw - mp, entry0=cap - 1)
 
-    def f_attn(c):
-        csa.hca_dense_attn(c["q"], c["ck"], c["cv"], mp, c["kw"], c["vw"], c["raw0"], c["pos"], W,
-                           ck_scale=c["cks"], cv_scale=c["cvs"], out=c["out"])
-    st.add("compress_kv", f_compress, B * (mp * 516 + 264), 0, "hbm")
-    st.add("dense_attn", f_attn, B * (cap * 264 + W * 512 + H * 128 * 4), 4 * B * H * 128 * (cap + W),
-           "hbm")
-    st.config = {"workload": wl.name, "batch": B, "context": wl.q_pos0[0] + 1, "query_heads": H,
-                 "kv_heads": 1, "head_dim": 128, "m_prime": mp, "compressed_entries": cap,
-                 "window": W, "compressed_kv": "fp8_e4m3+fp32 scale", "window_kv": "bf16"}
-    return st
+LAYERS = {
+    "csa_decode_128k": [("", "csa_decode_128k")],
+    "hca_decode_1m": [("", "hca_decode_1m")],
+    "csa_prefill_256k": [("", "csa_prefill_256k")],
+    "pair_1m": [("csa_decode.", "pair_csa_decode_1m"), ("csa_chunk.", "pair_csa_chunk_1m"),
+                ("hca_decode.", "pair_hca_decode_1m"), ("hca_chunk.", "pair_hca_chunk_1m")],
+}
 
 
 def build(args):
+    """Host inputs, R device copies and the step's launches for the chosen workload."""
+    import torch
     from csa_synth import workloads
     wls = workloads()
-    if args.workload == "csa_decode_128k":
-        wl = wls["csa_decode_128k"]
-        per_copy = wl.B * wl.cap * (68 + 4) + wl.B * wl.k * 512 + wl.B * 128 * 512
-        R = args.rotate or max(2, math.ceil(600e6 / per_copy))
-        return build_csa_decode(wl, R)
-    if args.workload == "hca_decode_1m":
-        wl = wls["hca_decode_1m"]
-        per_copy = wl.B * wl.cap * 264
-        R = args.rotate or max(2, math.ceil(600e6 / per_copy))
-        return build_hca_decode(wl, R)
-    raise SystemExit(f"workload {args.workload} is not wired into the benchmark yet")
+    parts = LAYERS[args.workload]
+    hosts = [(prefix, host_layer(wls[name])) for prefix, name in parts]
+    if args.workload == "pair_1m":
+        q_tokens = wls["pair_csa_decode_1m"].B + wls["pair_csa_chunk_1m"].T_q
+    else:
+        q_tokens = hosts[0][1]["wl"].B * hosts[0][1]["wl"].T_q
+    st = Step(args.workload, q_tokens)
+    for prefix, h in hosts:
+        add_layer(st, h, prefix, args.indexer)
+    per_copy = sum(k.nbytes for k in st.kernels.values())
+    R = args.rotate or max(2, math.ceil(600e6 / per_copy))
+    base = {}
+    for prefix, h in hosts:
+        base.update(device_layer(h, prefix))
+    base = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in base.items()}
+    st.copies = [base] + [{k: (v.clone() if isinstance(v, torch.Tensor) else v)
+                           for k, v in base.items()} for _ in range(R - 1)]
+    st.layers = hosts
+    if args.workload == "pair_1m":
+        st.config = {"workload": args.workload, "layers": "CSA then HCA, same query tokens",
+                     **{prefix.rstrip("."): layer_config(h["wl"]) for prefix, h in hosts}}
+    else:
+        st.config = {"workload": args.workload, **layer_config(hosts[0][1]["wl"])}
+    st.config["indexer_topk"] = "fused" if any(n.endswith("indexer_topk") for n in st.order) else "unfused"
+    return st
 
 
 # --------------------------------------------------------------------------
@@ -252,17 +323,17 @@ def time_step(st, steps, warmup, use_graph):
 
 
 def time_kernels(st, reps):
-    """Average duration of each kernel, from HIP events on its stream.
+    """Average duration of each call, from HIP events on its stream.
 
-    Each kernel is captured alone, once per input copy, into a HIP graph; the
+    Each call is captured alone, once per input copy, into a HIP graph; the
     graph is replayed and bracketed by events, so the figure is device time per
-    launch (back-to-back launches, no host gap) over the rotating inputs.
+    call (back-to-back launches, no host gap) over the rotating inputs.
     """
     import torch
     R = len(st.copies)
     res = {}
     for name in st.order:
-        fn = st.kernels[name][0]
+        fn = st.kernels[name].fn
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
@@ -286,7 +357,8 @@ def time_kernels(st, reps):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / (n_rep * R)
         res[name] = {"avg_us": us, "launches": n_rep * R}
-    # restore the step's data flow (each kernel above ran on the previous kernel's outputs)
+        del gr
+    # restore the step's data flow (each call above ran on the previous call's outputs)
     for c in st.copies:
         st.run(c)
     torch.cuda.synchronize()
@@ -300,24 +372,26 @@ def kernel_source_hash(names):
     return h.hexdigest()[:16]
 
 
-KERNEL_SOURCES = {"indexer_scores": ["indexer.hip", "common.hpp"],
-                  "sparse_attn": ["attn.hip", "common.hpp"], "dense_attn": ["attn.hip", "common.hpp"],
-                  "topk": ["topk.hip", "common.hpp"], "compress_kv": ["compress.hip", "common.hpp"]}
+KERNEL_SOURCES = {
+    "indexer_scores": ["indexer.hip", "indexer_core.hpp", "select.hpp", "common.hpp"],
+    "indexer_topk": ["indexer_topk.hip", "indexer_core.hpp", "select.hpp", "common.hpp"],
+    "sparse_attn": ["attn.hip", "common.hpp"], "dense_attn": ["attn.hip", "common.hpp"],
+    "topk": ["topk.hip", "select.hpp", "common.hpp"], "compress_kv": ["compress.hip", "common.hpp"]}
 
 
 def measured_traffic(workload, kernel):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if still current.
+    """HBM bytes per call from a committed rocprofv3 counter summary, if still current.
 
-    The summary (profiles/<kernel>_<workload>_pmc.json) holds FETCH_SIZE + WRITE_SIZE
-    per dispatch of the kernel, scaled by what the same counters read for a plain
-    256 MiB device copy, and the hash of the kernel's sources when it was taken; a
-    changed kernel gives null.
+    The summary (profiles/<call>_<workload>_pmc.json) holds FETCH_SIZE + WRITE_SIZE
+    per call, scaled by what the same counters read for a plain 256 MiB device copy,
+    and the hash of the call's kernel sources when it was taken; a changed kernel
+    gives null.
     """
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel.name.replace('.', '_')}_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    if d.get("source_hash") != kernel_source_hash(KERNEL_SOURCES[kernel]):
+    if d.get("source_hash") != kernel_source_hash(KERNEL_SOURCES[kernel.src]):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -325,41 +399,85 @@ def measured_traffic(workload, kernel):
 # --------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same workload
 
-def cpu_baseline_timed(workload, budget_s):
-    """Time only the oracle's arithmetic (input generation and decoding excluded)."""
-    from csa_synth import attn_inputs, compress_inputs, indexer_inputs, workloads
+def cpu_baseline(st, budget_s):
+    """The oracle, timed on the host on a sample of the step's query rows.
+
+    Per layer: the compression of the step's pooled rows and the decoding of the
+    stored caches of one sequence are timed once; indexer, top-k and attention are
+    timed per sampled query row (decode layers: one row per sequence, chunk layers:
+    rows spread evenly over the chunk).  The step's oracle time is the fixed part
+    plus the mean row time times the step's rows, per layer.  BLAS is held to one
+    thread.  Returns (query-tokens/s, description).
+    """
+    from threadpoolctl import threadpool_limits
     import oracle.attention as oa
     import oracle.compress as oc
     import oracle.indexer as oi
     import oracle.topk as ot
     from oracle.formats import bf16_decode
-    wl = workloads()[workload]
-    done, spent, seed = 0, 0.0, 0
-    wall0 = time.perf_counter()
-    while spent < budget_s and time.perf_counter() - wall0 < 3 * budget_s:
-        kv = compress_inputs(1, wl.L_raw, "bf16", seed=seed, tag=wl.tag * 10 + 1)
-        at = attn_inputs(1, 1, wl.H, wl.cap, 1, "bf16", wl.ckv, seed=seed, tag=wl.tag * 10 + 3)
-        ix = (indexer_inputs(1, 1, wl.cap, wl.H_I, wl.d_I, seed=seed, tag=wl.tag * 10 + 2)
-              if wl.kind == "csa" else None)
-        pos = np.array(wl.q_pos0[:1])
-        raw0 = np.array(wl.raw_pos0[:1])
-        t0 = time.perf_counter()
-        Kw, Vw = bf16_decode(kv["K"]), bf16_decode(kv["V"])
-        oc.compress_kv(Kw[:, -wl.m:], Vw[:, -wl.m:], kv["logits"][:, -wl.m:], wl.m, wl.ckv)
-        cK = oa.decode_kv(at["cK"], wl.ckv, at["cK_scale"])
-        cV = oa.decode_kv(at["cV"], wl.ckv, at["cV_scale"])
-        q = bf16_decode(at["q"])
-        if wl.kind == "csa":
-            s = oi.indexer_scores(ix["q_codes"], ix["q_e8m0"], ix["w"], ix["k_codes"], ix["k_e8m0"],
-                                  pos, wl.m)
-            idx = ot.topk(s.astype(np.float32), pos, wl.m, wl.k)
-            oa.sparse_attn(q, cK, cV, idx, Kw, Vw, raw0, pos, wl.W)
-        else:
-            oa.dense_attn(q, cK, cV, wl.m, Kw, Vw, raw0, pos, wl.W)
-        spent += time.perf_counter() - t0
-        done += 1
-        seed += 1
-    return done, spent
+    total, parts = 0.0, []
+    share = budget_s / len(st.layers)
+    with threadpool_limits(limits=1):
+        for prefix, h in st.layers:
+            wl, kv, at, ix = h["wl"], h["kv"], h["at"], h.get("ix")
+            L, row0, _ = pool_range(wl)
+            sl = slice(row0, row0 + L)
+            t0 = time.perf_counter()
+            Kw, Vw = bf16_decode(kv["K"][:, sl]), bf16_decode(kv["V"][:, sl])
+            oc.compress_kv(Kw, Vw, kv["logits"][:, sl], wl.m, wl.ckv)
+            t_fixed = time.perf_counter() - t0
+
+            def seq_arrays(b):
+                cK = oa.decode_kv(at["cK"][b:b + 1], wl.ckv,
+                                  None if at["cK_scale"] is None else at["cK_scale"][b:b + 1])
+                cV = oa.decode_kv(at["cV"][b:b + 1], wl.ckv,
+                                  None if at["cV_scale"] is None else at["cV_scale"][b:b + 1])
+                return cK, cV, bf16_decode(kv["K"][b:b + 1]), bf16_decode(kv["V"][b:b + 1])
+            if wl.T_q == 1:
+                rows = [(b, 0) for b in range(wl.B)]
+                cached = None
+            else:
+                n_s = 64
+                rows = [(0, int(i)) for i in np.linspace(0, wl.T_q - 1, n_s).round()]
+                t0 = time.perf_counter()
+                cached = seq_arrays(0)
+                t_fixed += time.perf_counter() - t0
+            t_rows = []
+            t_layer0 = time.perf_counter()
+            for b, i in rows:
+                if t_rows and sum(t_rows) > share:
+                    break
+                t = wl.q_pos0[b] + i
+                pos = np.array([t])
+                r0 = np.array([wl.raw_pos0[b]])
+                t0 = time.perf_counter()
+                cK, cV, Kb, Vb = cached if cached is not None else seq_arrays(b)
+                q = bf16_decode(at["q"][b:b + 1, i:i + 1])
+                if wl.kind == "csa":
+                    s = oi.indexer_scores(ix["q_codes"][b:b + 1, i:i + 1],
+                                          ix["q_e8m0"][b:b + 1, i:i + 1], ix["w"][b:b + 1, i:i + 1],
+                                          ix["k_codes"][b:b + 1], ix["k_e8m0"][b:b + 1], pos, wl.m)
+                    idx = ot.topk(s.astype(np.float32), pos, wl.m, wl.k)
+                    oa.sparse_attn(q, cK, cV, idx, Kb, Vb, r0, pos, wl.W)
+                else:
+                    oa.dense_attn(q, cK, cV, wl.m, Kb, Vb, r0, pos, wl.W)
+                t_rows.append(time.perf_counter() - t0)
+                if time.perf_counter() - t_layer0 > 3 * share:
+                    break
+            n_step_rows = wl.B * wl.T_q
+            total += t_fixed + n_step_rows * float(np.mean(t_rows))
+            parts.append(f"{prefix.rstrip('.') or wl.name}: {len(t_rows)} of {n_step_rows} query rows "
+                         f"({sum(t_rows):.1f} s) + pooling of the step's blocks")
+    desc = ("fp64 numpy oracle (compress, indexer, top-k, attention) on a sample of the same "
+            "workload's query rows, scaled to one step; " + "; ".join(parts))
+    return st.q_tokens / total, desc
+
+
+def roofline_entry(k, avg_us):
+    s = avg_us * 1e-6
+    if k.bound == "hbm":
+        return k.nbytes / s / 1e9, HBM_PEAK_GBS, "GB/s"
+    return k.flops / s / 1e12, k.mfma_peak, "TFLOP/s"
 
 
 def main():
@@ -384,37 +502,35 @@ def main():
     st = build(args)
     ms, done, wall = time_step(st, args.steps, args.warmup, not args.no_graph)
     kt = time_kernels(st, reps=max(10 * len(st.copies), 200))
-    # dominant kernel = largest share of the step
+    # dominant call = largest share of the step
     dom = max(st.order, key=lambda n: kt[n]["avg_us"])
-    _, nbytes, flops, bound = st.kernels[dom]
-    avg_s = kt[dom]["avg_us"] * 1e-6
-    achieved = nbytes / avg_s / 1e9
-    roof = {"kernel": dom, "bound": bound, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.workload, dom),
-            "algorithmic_bytes_per_launch": int(nbytes), "avg_launch_us": round(kt[dom]["avg_us"], 3)}
+    k = st.kernels[dom]
+    achieved, peak, unit = roofline_entry(k, kt[dom]["avg_us"])
+    roof = {"kernel": dom, "bound": k.bound, "achieved": round(achieved, 1), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(args.workload, k),
+            "algorithmic_bytes_per_launch": k.nbytes, "algorithmic_flops_per_launch": k.flops,
+            "avg_launch_us": round(kt[dom]["avg_us"], 3)}
     kernels = {}
     for n in st.order:
-        _, b_, f_, _ = st.kernels[n]
-        kernels[n] = {"avg_us": round(kt[n]["avg_us"], 3), "algorithmic_bytes": int(b_),
-                      "GBps": round(b_ / (kt[n]["avg_us"] * 1e-6) / 1e9, 1)}
+        kk = st.kernels[n]
+        a_, p_, u_ = roofline_entry(kk, kt[n]["avg_us"])
+        kernels[n] = {"avg_us": round(kt[n]["avg_us"], 3), "algorithmic_bytes": kk.nbytes,
+                      "algorithmic_flops": kk.flops, "bound": kk.bound, "achieved": round(a_, 1),
+                      "unit": u_, "frac": round(a_ / p_, 4)}
     cpu = None
     if not args.no_cpu_baseline:
-        n_done, spent = cpu_baseline_timed(args.workload if args.workload != "pair_1m" else
-                                           "csa_decode_128k", args.cpu_seconds)
-        cpu = {"value": round(n_done / spent, 3), "unit": "query-tokens/s", "cores": 1,
-               "kind": "oracle",
-               "sample": f"{n_done} single-sequence decode steps of the same workload at full "
-                         f"context (fp64 numpy oracle; compress, indexer, top-k, attention), "
-                         f"{spent:.1f} s of oracle arithmetic; input generation excluded"}
+        v, desc = cpu_baseline(st, args.cpu_seconds)
+        cpu = {"value": round(v, 4), "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
+               "sample": desc}
     q_per_s = st.q_tokens / (ms * 1e-3)
     line = {"metric": METRIC, "value": round(q_per_s, 1), "unit": "query-tokens/s", "n_gpus": 1,
             "steps": done, "warmup": args.warmup, "ms_per_step": round(ms, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "mxfp4+bf16", "data": "synthetic (seeded; shapes of the pages' 128K-1M contexts)",
             "config": st.config, "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
-            "rotation_copies": len(st.copies), "graph": not args.no_graph,
-            "wall_s_timed_region": round(wall, 4)}
+            "query_tokens_per_step": st.q_tokens, "rotation_copies": len(st.copies),
+            "graph": not args.no_graph, "wall_s_timed_region": round(wall, 4)}
     print(json.dumps(line), flush=True)
 
 

@@ -69,7 +69,8 @@ typedef enum {
 typedef enum {
   CSA_OP_TOPK = 0,
   CSA_OP_SPARSE_ATTN = 1,
-  CSA_OP_DENSE_ATTN = 2
+  CSA_OP_DENSE_ATTN = 2,
+  CSA_OP_INDEXER_TOPK = 3
 } csa_op_t;
 
 /* ---------------------------------------------------------------------
@@ -145,6 +146,33 @@ csa_status_t csa_topk(const float* scores, const int32_t* q_pos0, int32_t B, int
                       size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------
+ * csa_indexer_topk -- indexer scores and top-k selection in one call.
+ *
+ * Passages: as csa_indexer_scores and csa_topk (the indexer scores every
+ * query token against every compressed block in FP4, sz-guanghua.com.cn
+ * ifanr repost, 百萬長上下文; CSA keeps the most relevant k entries,
+ * blog.nickys.cn, 三大架构改动 §1 CSA).
+ * Result: idx equals, bit for bit, csa_topk(csa_indexer_scores(...)) on the
+ * same arguments, for any input values; the fp32 scores are never written.
+ * The scoring pass stores 16-bit order-preserving score keys (2 bytes per
+ * (query, entry) instead of 4); the selection re-scores only the entries
+ * whose 16-bit key ties the k-th one, with the scoring pass's own arithmetic.
+ *
+ *   q_codes .. q_pos0, B .. m   as csa_indexer_scores (same layouts, limits
+ *                               and preconditions)
+ *   k         entries to keep; 1 <= k <= 32767 (larger: CSA_ENOTSUP)
+ *   idx       [B, T_q, k] int32 (output), as csa_topk
+ *   ws, ws_bytes  workspace of csa_workspace_size(CSA_OP_INDEXER_TOPK, B, T_q,
+ *             0, 128, cap) = B*T_q*cap*2 bytes (no initial contents needed);
+ *             calls that share a workspace must be ordered on one stream.
+ * ------------------------------------------------------------------- */
+csa_status_t csa_indexer_topk(const uint8_t* q_codes, const uint8_t* q_e8m0, const float* w,
+                              const uint8_t* k_codes, const uint8_t* k_e8m0,
+                              const int32_t* q_pos0, int32_t B, int32_t T_q, int32_t H_I,
+                              int32_t d_I, int32_t cap, int32_t m, int32_t k, int32_t* idx,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
  * csa_sparse_attn -- attention over the selected entries plus the window.
  *
  * Passage: attention runs only over the k selected compressed entries, with a
@@ -199,7 +227,7 @@ csa_status_t hca_dense_attn(const void* q, int32_t io_dtype, const void* ck, con
                             void* stream);
 
 /* Workspace bytes a call needs.  n_keys = k + W (CSA) or cap + W (HCA);
- * for CSA_OP_TOPK pass T_q and n_keys = cap.  Returns 0 when none is needed
+ * for CSA_OP_TOPK and CSA_OP_INDEXER_TOPK pass T_q and n_keys = cap.  Returns 0 when none is needed
  * and (size_t)-1 for invalid arguments. */
 size_t csa_workspace_size(int32_t op, int32_t B, int32_t T_q, int32_t H, int32_t d,
                           int32_t n_keys);

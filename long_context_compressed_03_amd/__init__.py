@@ -21,10 +21,10 @@ LIB_PATH = os.path.join(HERE, "libcsa.so")
 
 CSA_OK, CSA_EINVAL, CSA_ENOTSUP, CSA_EHIP, CSA_EWORKSPACE = range(5)
 CSA_BF16, CSA_F32, CSA_FP8_E4M3 = 0, 1, 2
-CSA_OP_TOPK, CSA_OP_SPARSE_ATTN, CSA_OP_DENSE_ATTN = 0, 1, 2
+CSA_OP_TOPK, CSA_OP_SPARSE_ATTN, CSA_OP_DENSE_ATTN, CSA_OP_INDEXER_TOPK = 0, 1, 2, 3
 DTYPES = {"bf16": CSA_BF16, "f32": CSA_F32, "fp8": CSA_FP8_E4M3}
 
-EXPORTS = ["csa_compress_kv", "csa_indexer_scores", "csa_topk", "csa_sparse_attn",
+EXPORTS = ["csa_compress_kv", "csa_indexer_scores", "csa_indexer_topk", "csa_topk", "csa_sparse_attn",
            "hca_dense_attn", "csa_workspace_size", "csa_status_str", "csa_abi_version"]
 
 _lib = None
@@ -50,12 +50,14 @@ def load(path=LIB_PATH):
     lib = ctypes.CDLL(path)
     lib.csa_compress_kv.argtypes = [_P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P]
     lib.csa_indexer_scores.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]
+    lib.csa_indexer_topk.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _S,
+                                     _P]
     lib.csa_topk.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _S, _P]
     lib.csa_sparse_attn.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _P, _I, _P, _P, _P, _I, _P, _I,
                                     _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
     lib.hca_dense_attn.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _P, _I,
                                    _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
-    for fn in ["csa_compress_kv", "csa_indexer_scores", "csa_topk", "csa_sparse_attn",
+    for fn in ["csa_compress_kv", "csa_indexer_scores", "csa_indexer_topk", "csa_topk", "csa_sparse_attn",
                "hca_dense_attn"]:
         getattr(lib, fn).restype = _I
     lib.csa_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
@@ -151,6 +153,21 @@ def csa_topk(scores, q_pos0, m, k, idx=None, stream=None):
     st = load().csa_topk(_ptr(scores), _ptr(q_pos0), B, T_q, cap, m, k, _ptr(idx), _ws_ptr(ws),
                          _ws_len(ws), _stream(stream))
     _check("csa_topk", st)
+    return idx
+
+
+def csa_indexer_topk(q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, m, k, idx=None, stream=None):
+    """Fused indexer + top-k: idx [B, T_q, k] int32, identical to csa_topk(csa_indexer_scores(...))."""
+    B, T_q, H_I, half = q_codes.shape
+    cap = k_codes.shape[1]
+    if idx is None:
+        idx = torch.empty((B, T_q, k), dtype=torch.int32, device=q_codes.device)
+    lib = load()
+    ws = _workspace(q_codes.device, lib.csa_workspace_size(CSA_OP_INDEXER_TOPK, B, T_q, 0, 128, cap))
+    st = lib.csa_indexer_topk(_ptr(q_codes), _ptr(q_e8m0), _ptr(w), _ptr(k_codes), _ptr(k_e8m0),
+                              _ptr(q_pos0), B, T_q, H_I, 2 * half, cap, m, k, _ptr(idx), _ws_ptr(ws),
+                              _ws_len(ws), _stream(stream))
+    _check("csa_indexer_topk", st)
     return idx
 
 

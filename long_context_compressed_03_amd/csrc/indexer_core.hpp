@@ -1,0 +1,257 @@
+// Lightning-indexer scoring on the CDNA4 block-scaled MXFP4 matrix cores,
+// shared by csa_indexer_scores (fp32 scores out) and csa_indexer_topk (16-bit
+// order-preserving keys out, then exact re-scoring of the boundary entries).
+//
+// The pages say the indexer scores every query token against every compressed
+// block in FP4 (sz-guanghua.com.cn ifanr repost, 百萬長上下文) and that the FP4
+// form on the indexer's query-key path is MXFP4 ("DeepSeek V4技术揭秘", §一).
+// Score (this library's reading):  s(t,e) = sum_h w[t,h] * ReLU(q[t,h] . k[e]).
+//
+// The contraction [query*head rows] x [d_I] x [entries] runs on
+// V_MFMA_SCALE_F32_16X16X128_F8F6F4 with both operands in E2M1 and one E8M0
+// scale per 32 elements, which is exactly the MXFP4 block format: the
+// instruction applies the block scales itself, so operands go from HBM to the
+// matrix core untouched.  Lane layout (checked on gfx950): lane l supplies row
+// (A) / column (B) l%16 and the 32 contraction elements [32*(l/16), +32) of a
+// 128-wide step as 16 bytes, with its block's E8M0 in byte 0 of the scale
+// operand; C lane l holds column l%16, rows 4*(l/16) .. +3.
+//
+// Rows of a 16-row tile are (query, head) pairs, head fastest, so one tile
+// holds 16/H_I whole queries; query i always sits in slot i % (16/H_I) of its
+// tile.  The head sum is 4 rows inside a lane plus, for H_I > 4, a cross-lane
+// add (head_sum).  Every score of a (query, entry) pair is produced by the
+// same instruction sequence on the same operand values wherever it is
+// computed, so a re-scored entry reproduces the first score bit for bit.
+#pragma once
+#include "select.hpp"
+
+namespace csa_ix {
+
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kMaxKSteps = 4;  // d_I <= 512
+
+enum Out { kScoresF32 = 0, kKey16 = 1 };
+
+CSA_DEV v4f mfma_fp4(u32x4 a, int sa, u32x4 b, int sb, v4f c) {
+  v8i av = {int(a[0]), int(a[1]), int(a[2]), int(a[3]), 0, 0, 0, 0};
+  v8i bv = {int(b[0]), int(b[1]), int(b[2]), int(b[3]), 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, sa, 0, sb);
+}
+
+// Weighted ReLU sum over the heads of one query from a 16x16 score tile:
+// lane l holds rows 4*(l/16) .. +3 (heads of one query) of column l%16 in
+// acc, with their weights in wv.  The result is valid on the writer lanes:
+// for H_I = 4 every lane, for 8 the lanes with (l/16) even, for 16 lanes 0..15.
+template <int kHI>
+CSA_DEV float head_sum(v4f acc, const float (&wv)[4], int g, bool& writer) {
+  float p = wv[0] * fmaxf(acc[0], 0.f);
+  p = fmaf(wv[1], fmaxf(acc[1], 0.f), p);
+  p = fmaf(wv[2], fmaxf(acc[2], 0.f), p);
+  p = fmaf(wv[3], fmaxf(acc[3], 0.f), p);
+  writer = true;
+  if constexpr (kHI == 8) {
+    p += __shfl_xor(p, 16);
+    writer = (g & 1) == 0;
+  } else if constexpr (kHI == 16) {
+    p += __shfl_xor(p, 16);
+    p += __shfl_xor(p, 32);
+    writer = g == 0;
+  }
+  return p;
+}
+
+// A operand of one row tile: lane row `col` is (query, head) = (q, h); rows
+// of queries outside [0, T_q) or not selected by `use` are zero.
+template <int kHI, int kKS>
+CSA_DEV void load_a(const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_e8m0, size_t vec, bool use,
+                    int g, int nblk, int row_bytes, u32x4 (&a)[kKS], int (&sa)[kKS]) {
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+    const int c = ks * 4 + g;
+    if (use && c < nblk) {
+      a[ks] = *reinterpret_cast<const u32x4*>(q_codes + vec * row_bytes + c * 16);
+      sa[ks] = q_e8m0[vec * nblk + c];
+    } else {
+      a[ks] = u32x4{0u, 0u, 0u, 0u};
+      sa[ks] = 127;
+    }
+  }
+}
+
+// B operand of one 16-entry fragment: lane column `col` is entry e (absent if !use).
+template <int kKS, bool kStream>
+CSA_DEV void load_b(const uint8_t* __restrict__ kc_seq, const uint8_t* __restrict__ ke_seq, int e, bool use, int g,
+                    int nblk, int row_bytes, u32x4 (&bk)[kKS], int (&sb)[kKS]) {
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+    const int c = ks * 4 + g;
+    if (use && c < nblk) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(kc_seq + size_t(e) * row_bytes + c * 16);
+      bk[ks] = kStream ? __builtin_nontemporal_load(p) : *p;
+      sb[ks] = ke_seq[size_t(e) * nblk + c];
+    } else {
+      bk[ks] = u32x4{0u, 0u, 0u, 0u};
+      sb[ks] = 127;
+    }
+  }
+}
+
+// kHI: indexer heads (4, 8 or 16); kRT: 16-row tiles per block; kKS: 128-wide
+// contraction steps; kFrag: 16-entry fragments per wave per batch of loads;
+// kStream: keys read once (decode) with non-temporal loads; kOut: fp32
+// scores (-inf past nvis) or the top 16 bits of the order-preserving key
+// (0 past nvis).
+//
+// Work split: a block of 4 waves owns kRT row tiles of one sequence; each
+// wave walks its own run of entries, 16 per MFMA, with the A fragments
+// (queries) held in registers for the whole run.
+template <int kHI, int kRT, int kKS, int kFrag, bool kStream, int kOut>
+__global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restrict__ q_codes,
+                                                         const uint8_t* __restrict__ q_e8m0,
+                                                         const float* __restrict__ w,
+                                                         const uint8_t* __restrict__ k_codes,
+                                                         const uint8_t* __restrict__ k_e8m0,
+                                                         const int32_t* __restrict__ q_pos0, int T_q, int d_I,
+                                                         int cap, int m, int entries_per_wave, void* __restrict__ out) {
+  constexpr int kQPT = 16 / kHI;  // queries per row tile
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int b = blockIdx.z;
+  const int q_block = blockIdx.y * kRT * kQPT;
+  const int nblk = d_I >> 5;            // 32-element blocks per vector
+  const int row_bytes = d_I >> 1;
+  const int pos0 = q_pos0[b];
+
+  // ---- A fragments (queries), weights and visibility for this lane's rows
+  u32x4 a[kRT][kKS];
+  int sa[kRT][kKS];
+  float wv[kRT][4];
+  int nv_lane[kRT];  // visible entries of the query whose rows this lane holds in C
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    const int r = rt * 16 + col;
+    const int q = q_block + r / kHI;
+    const int h = r % kHI;
+    load_a<kHI, kKS>(q_codes, q_e8m0, (size_t(b) * T_q + q) * kHI + h, q < T_q, g, nblk, row_bytes, a[rt], sa[rt]);
+    const int rc = rt * 16 + 4 * g;  // first C row this lane holds
+    const int qc = q_block + rc / kHI;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = (rc + i) % kHI;
+      wv[rt][i] = qc < T_q ? w[(size_t(b) * T_q + qc) * kHI + hh] : 0.f;
+    }
+    int nv = 0;
+    if (qc < T_q) nv = min((pos0 + qc + 1) / m, cap);
+    nv_lane[rt] = nv;
+  }
+  // largest visibility among the block's queries (the last valid one)
+  const int q_last = min(q_block + kRT * kQPT, T_q) - 1;
+  const int nv_max = min((pos0 + q_last + 1) / m, cap);
+
+  const int e_wave0 = (blockIdx.x * kWavesPerBlock + wid) * entries_per_wave;
+  const int e_wave1 = min(e_wave0 + entries_per_wave, cap);
+
+  const uint8_t* kc_seq = k_codes + size_t(b) * cap * row_bytes;
+  const uint8_t* ke_seq = k_e8m0 + size_t(b) * cap * nblk;
+
+  for (int e_frag0 = e_wave0; e_frag0 < e_wave1; e_frag0 += 16 * kFrag) {
+    u32x4 bk[kFrag][kKS];
+    int sb[kFrag][kKS];
+#pragma unroll
+    for (int f = 0; f < kFrag; ++f) {
+      const int e = e_frag0 + f * 16 + col;
+      load_b<kKS, kStream>(kc_seq, ke_seq, e, e < nv_max, g, nblk, row_bytes, bk[f], sb[f]);
+    }
+#pragma unroll
+    for (int f = 0; f < kFrag; ++f) {
+      const int e0 = e_frag0 + f * 16;
+      if (e0 >= e_wave1) break;
+      const int e = e0 + col;
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        if (e0 < nv_max) {
+#pragma unroll
+          for (int ks = 0; ks < kKS; ++ks) acc = mfma_fp4(a[rt][ks], sa[rt][ks], bk[f][ks], sb[f][ks], acc);
+        }
+        bool writer;
+        const float p = head_sum<kHI>(acc, wv[rt], g, writer);
+        const int q = q_block + (rt * 16 + 4 * g) / kHI;
+        if (writer && q < T_q && e < e_wave1) {
+          const size_t o = (size_t(b) * T_q + q) * cap + e;
+          if constexpr (kOut == kScoresF32) {
+            static_cast<float*>(out)[o] = e < nv_lane[rt] ? p : -INFINITY;
+          } else {
+            static_cast<uint16_t*>(out)[o] = e < nv_lane[rt] ? uint16_t(csa_sel::ordered_key(p) >> 16) : uint16_t(0);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int kHI, int kRT, int kKS, bool kStream, int kOut>
+hipError_t launch_indexer_ks(const uint8_t* qc, const uint8_t* qe, const float* w, const uint8_t* kc,
+                             const uint8_t* ke, const int32_t* pos, int B, int T_q, int d_I, int cap, int m,
+                             void* out, hipStream_t st) {
+  constexpr int kFrag = 4;
+  constexpr int kQPT = 16 / kHI;
+  const int entries_per_wave = kStream ? 64 : 256;
+  const int per_block = entries_per_wave * kWavesPerBlock;
+  dim3 grid((cap + per_block - 1) / per_block, (T_q + kRT * kQPT - 1) / (kRT * kQPT), B);
+  hipLaunchKernelGGL((indexer_kernel<kHI, kRT, kKS, kFrag, kStream, kOut>), grid, dim3(kBlock), 0, st, qc, qe, w,
+                     kc, ke, pos, T_q, d_I, cap, m, entries_per_wave, out);
+  return hipGetLastError();
+}
+
+template <int kHI, int kRT, bool kStream, int kOut>
+hipError_t launch_indexer_rt(int ks, const uint8_t* qc, const uint8_t* qe, const float* w, const uint8_t* kc,
+                             const uint8_t* ke, const int32_t* pos, int B, int T_q, int d_I, int cap, int m,
+                             void* out, hipStream_t st) {
+  switch (ks) {
+    case 1: return launch_indexer_ks<kHI, kRT, 1, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
+    case 2: return launch_indexer_ks<kHI, kRT, 2, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
+    case 3: return launch_indexer_ks<kHI, kRT, 3, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
+    default: return launch_indexer_ks<kHI, kRT, 4, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
+  }
+}
+
+template <int kHI, int kOut>
+hipError_t launch_indexer_h(int ks, const uint8_t* qc, const uint8_t* qe, const float* w, const uint8_t* kc,
+                            const uint8_t* ke, const int32_t* pos, int B, int T_q, int d_I, int cap, int m,
+                            void* out, hipStream_t st) {
+  // one row tile when the whole call has at most one tile of queries (decode);
+  // several otherwise so every key fragment feeds several MFMAs
+  if (T_q * kHI <= 16)
+    return launch_indexer_rt<kHI, 1, true, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
+  return launch_indexer_rt<kHI, 4, false, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
+}
+
+// Shared argument checks of the two indexer entry points.
+inline csa_status_t check_indexer_args(const void* q_codes, const void* q_e8m0, const void* w, const void* k_codes,
+                                       const void* k_e8m0, const void* q_pos0, int32_t B, int32_t T_q, int32_t H_I,
+                                       int32_t d_I, int32_t cap, int32_t m) {
+  if (!q_codes || !q_e8m0 || !w || !k_codes || !k_e8m0 || !q_pos0) return CSA_EINVAL;
+  if (d_I < 32 || d_I > 128 * kMaxKSteps || d_I % 32 != 0) return CSA_EINVAL;
+  if (B < 0 || T_q < 0 || cap < 0 || m < 1) return CSA_EINVAL;
+  if (H_I != 4 && H_I != 8 && H_I != 16) return CSA_ENOTSUP;
+  if (B > 65535 || T_q > (1 << 24)) return CSA_ENOTSUP;
+  return CSA_OK;
+}
+
+template <int kOut>
+hipError_t launch_indexer(int H_I, const uint8_t* qc, const uint8_t* qe, const float* w, const uint8_t* kc,
+                          const uint8_t* ke, const int32_t* pos, int B, int T_q, int d_I, int cap, int m, void* out,
+                          hipStream_t st) {
+  const int ks = (d_I + 127) / 128;
+  switch (H_I) {
+    case 4: return launch_indexer_h<4, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
+    case 8: return launch_indexer_h<8, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
+    default: return launch_indexer_h<16, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
+  }
+}
+
+}  // namespace csa_ix

@@ -1,0 +1,662 @@
+// csa_indexer_topk: the lightning indexer and the top-k selection fused, so
+// the fp32 scores of a prefill chunk (T_q x cap of them) never reach HBM.
+//
+// Passages: the indexer scores every query token against every compressed
+// block in FP4 (sz-guanghua.com.cn ifanr repost, 百萬長上下文) and CSA keeps the
+// k entries it finds most relevant (blog.nickys.cn DeepSeek-V4 post,
+// 三大架构改动 §1 CSA).  The result is by construction identical, bit for bit,
+// to csa_topk applied to csa_indexer_scores.
+//
+// Two kernels:
+//  1. the indexer kernel of csa_indexer_scores, writing for each visible
+//     (query, entry) the top 16 bits of the order-preserving uint32 key of its
+//     score (half the bytes of the fp32 score) into the workspace;
+//  2. per query row one 1024-thread block.  The row's first 65536 (or 32768)
+//     16-bit keys are held in registers, two per register; keys past that are
+//     streamed from the workspace 16384 at a time.
+//     a. estimate: a histogram of 14-bit buckets over a fixed 1/8 sample of
+//        the held keys gives, from the sample ranks k*(sample/row) -+ a
+//        margin of 4 standard deviations (+16), a window of buckets that
+//        should hold the k-th largest key;
+//     b. one pass counts the keys above the window (one LDS atomic per wave)
+//        and lists the keys inside it (index and 16-bit key);
+//     c. if the window does hold the k-th key, an exact histogram of the
+//        listed 16-bit keys gives the k-th 16-bit key T; otherwise (a miss,
+//        or a window too full for the list) a histogram of 14-bit buckets over
+//        every key does, and T is that bucket;
+//     d. keys above T are selected outright, keys below are not; the entries
+//        whose key equals T are RE-SCORED with the indexer's own instruction
+//        sequence (same MFMA, same operand values, same head-sum order),
+//        which gives back their exact fp32 scores, and an exact radix
+//        refinement over their full 32-bit keys finds the k-th key and how
+//        many keys equal to it are still needed (when T's class holds more
+//        entries than the list, it is re-scored in rounds of 4096 keys);
+//     e. emission as in csa_topk: bitmaps of "greater" and "equal" entries,
+//        one block scan, ascending output with the lower-index tie rule.
+#include "indexer_core.hpp"
+
+namespace {
+
+using namespace csa_sel;
+using namespace csa_ix;
+
+constexpr int kRound = kThreads * 4;   // 4096 consecutive keys per round of loads
+constexpr int kBatch = 4;              // rounds streamed per batch (16 loads in flight)
+constexpr int kList = 4096;            // capacity of the LDS entry lists
+constexpr int kWinPer = kList / (kThreads / 64);   // window-list slots of each wave
+constexpr int kBuckets = 1 << 14;      // 14-bit buckets of the 16-bit keys
+constexpr int kMaxJ = 16;              // rounds held in registers, largest variant
+constexpr int kMaxWords = kMaxJ * kRound / 32;
+static_assert(kMaxJ % kBatch == 0, "chunks are whole batches of rounds");
+
+struct Shared {
+  uint32_t hist[kBuckets];
+  struct {
+    uint32_t gt[kMaxWords];   // index-ordered bitmaps of one chunk: selected outright,
+    uint32_t eq[kMaxWords];   // and equal to the k-th key (taken lowest index first)
+  } bm;
+  int32_t win_idx[kList];     // window entries (index): wave w fills [w*kWinPer, +win_cnt[w])
+  uint16_t win_key[kList];    // their 16-bit keys
+  uint32_t win_cnt[kThreads / 64];
+  int32_t cand_idx[kList];    // entries to re-score
+  uint32_t cand_key[kList];   // their exact 32-bit keys
+  uint32_t smem[32];
+  uint32_t n_win, n_gt, n_cand;
+  Sel sel, sel2;
+};
+
+// 16-bit key (j, c) from the packed registers (c = 0..3 within round j).
+template <int kJ>
+CSA_DEV uint32_t kget(const uint32_t (&P)[kJ][2], int j, int c) {
+  return (P[j][c >> 1] >> ((c & 1) * 16)) & 0xFFFFu;
+}
+
+// Tells the compiler the packed keys may have changed, so values unpacked
+// from them in one phase are recomputed in the next instead of being held in
+// registers across it (which would not fit beside the keys themselves).
+template <int kJ>
+CSA_DEV void opaque(uint32_t (&P)[kJ][2]) {
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) asm volatile("" : "+v"(P[j][0]), "+v"(P[j][1]));
+}
+
+// Index of key (j, c) of thread (w, l) in a chunk: j*4096 + c*1024 + 64w + l,
+// so a wave-wide load reads 64 consecutive keys and a wave ballot is two
+// words of an index-ordered bitmap.
+CSA_DEV int key_offset(int j, int c) { return j * kRound + c * kThreads + int(threadIdx.x); }
+
+// Buffer resource over keys [0, nv) of a row: loads past nv return 0, which
+// is the "absent" key, so no load needs a bounds test of its own.
+CSA_DEV __amdgpu_buffer_rsrc_t row_rsrc(const uint16_t* src, int nv) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), (short)0, nv * 2, 0x00020000);
+}
+
+// Key at index x0 + c*1024 + threadIdx.x for c = 0..3 (x0 a multiple of
+// 4096); the byte offset is all in the VGPR operand, so the range check of
+// the resource covers it.
+CSA_DEV void load4(__amdgpu_buffer_rsrc_t r, int x0, uint32_t (&v)[4]) {
+  const int o0 = (x0 + int(threadIdx.x)) * 2;
+  v[0] = __builtin_amdgcn_raw_buffer_load_b16(r, o0, 0, 0);
+  v[1] = __builtin_amdgcn_raw_buffer_load_b16(r, o0 + 2048, 0, 0);
+  v[2] = __builtin_amdgcn_raw_buffer_load_b16(r, o0 + 4096, 0, 0);
+  v[3] = __builtin_amdgcn_raw_buffer_load_b16(r, o0 + 6144, 0, 0);
+}
+
+// The first chunk (kJ rounds) of a row into registers, every load in flight
+// at once (nothing else is live yet).
+template <int kJ>
+CSA_DEV void load_chunk0(__amdgpu_buffer_rsrc_t r, uint32_t (&P)[kJ][2]) {
+  uint32_t v[kJ][4];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) load4(r, j * kRound, v[j]);
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    P[j][0] = v[j][0] | (v[j][1] << 16);
+    P[j][1] = v[j][2] | (v[j][3] << 16);
+  }
+}
+
+// Streams keys [r_begin, r_end) (r_begin a multiple of 4096) in batches of
+// kBatch rounds; fn(v, base) sees the batch's keys v[j][c] = key at base +
+// key_offset(j, c) (0 past nv).  Every thread must call it.
+template <typename Fn>
+CSA_DEV void stream_batches(__amdgpu_buffer_rsrc_t r, int r_begin, int r_end, Fn fn) {
+#pragma unroll 1
+  for (int base = r_begin; base < r_end; base += kBatch * kRound) {
+    uint32_t v[kBatch][4];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) load4(r, base + j * kRound, v[j]);
+    fn(v, base);
+  }
+}
+
+// Appends to an LDS list the keys of a batch of kR rounds (given by get(j, c))
+// that satisfy in_window and, when n_above is given, counts the keys that
+// satisfy above.  Each thread counts its own keys, one wave scan of the packed
+// counts gives each thread its slots, and one LDS atomic per wave reserves
+// the wave's range (list order is therefore not index order; nothing
+// downstream depends on it).  Entries past the list capacity are counted but
+// not stored.  between() runs between the counting and the storing pass (a
+// register barrier for keys unpacked from packed registers).
+template <int kR, typename Get, typename In, typename Above, typename Between>
+CSA_DEV void list_batch(Get get, int base, In in_window, Above above, int32_t* idx_out, uint16_t* key_out,
+                        uint32_t* n_list, uint32_t* n_above, Between between) {
+  const int lane = threadIdx.x & 63;
+  uint32_t cnt = 0u, n_gt = 0u;
+#pragma unroll
+  for (int j = 0; j < kR; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t kk = get(j, c);
+      cnt += in_window(kk) ? 1u : 0u;
+      if (n_above) n_gt += above(kk) ? 1u : 0u;
+    }
+  // inclusive wave scan of (above << 16 | listed); both totals stay below 2^16
+  const uint32_t packed = (n_gt << 16) | cnt;
+  uint32_t incl = packed;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  const uint32_t wave_tot = __shfl(incl, 63);
+  uint32_t at = 0u;
+  if (lane == 63) {
+    if (wave_tot & 0xFFFFu) at = atomicAdd(n_list, wave_tot & 0xFFFFu);
+    if (n_above && (wave_tot >> 16)) atomicAdd(n_above, wave_tot >> 16);
+  }
+  uint32_t slot = __shfl(at, 63) + ((incl - packed) & 0xFFFFu);
+  between();
+#pragma unroll
+  for (int j = 0; j < kR; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t kk = get(j, c);
+      if (in_window(kk)) {
+        if (slot < uint32_t(kList)) {
+          idx_out[slot] = base + key_offset(j, c);
+          if (key_out) key_out[slot] = uint16_t(kk);
+        }
+        ++slot;
+      }
+    }
+}
+
+// One pass of the window step over a batch of kR rounds (keys from get(j, c),
+// chunk offsets base + key_offset(j, c)): keys above hi16 are counted (a
+// per-wave scalar sum, one LDS atomic at the end) and, when bm_above is given
+// (a batch that is a whole chunk), set in the chunk's index-ordered bitmap;
+// keys in [lo16, hi16] are appended to the wave's own region of the window
+// list at a wave-uniform running count (n_in; a count past the region's size
+// marks an overflow).  lo16 > 0, so absent keys (0) are in neither set.
+template <int kR, typename Get>
+CSA_DEV void window_pass(Get get, int base, uint32_t lo16, uint32_t hi16, uint32_t* bm_above, uint32_t& n_in,
+                         Shared& sh) {
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const uint32_t span = hi16 - lo16;
+  uint32_t n_above = 0u;                 // wave-uniform
+#pragma unroll
+  for (int j = 0; j < kR; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t kk = get(j, c);
+      const uint64_t bab = __ballot(kk > hi16);
+      n_above += uint32_t(__popcll(bab));
+      if (bm_above && lane == 0) {
+        // the wave's 64 keys are indices j*4096 + c*1024 + 64w + l: words
+        // 2w + (j*4096 + c*1024)/32 and the next (a per-wave base plus a constant)
+        uint32_t* wb = bm_above + 2 * wv;
+        wb[(j * kRound + c * kThreads) >> 5] = uint32_t(bab);
+        wb[((j * kRound + c * kThreads) >> 5) + 1] = uint32_t(bab >> 32);
+      }
+      const bool in = kk - lo16 <= span;
+      const uint64_t bin = __ballot(in);
+      const uint32_t slot =
+          n_in + __builtin_amdgcn_mbcnt_hi(uint32_t(bin >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(bin), 0u));
+      if (in && slot < uint32_t(kWinPer)) {
+        sh.win_idx[wv * kWinPer + slot] = base + key_offset(j, c);
+        sh.win_key[wv * kWinPer + slot] = uint16_t(kk);
+      }
+      n_in += uint32_t(__popcll(bin));
+    }
+  if (lane == 0 && n_above) atomicAdd(&sh.n_gt, n_above);
+}
+
+// Visits fn(slot) for every filled slot of the window list (all threads).
+template <typename Fn>
+CSA_DEV void each_window(const Shared& sh, Fn fn) {
+  for (int x = threadIdx.x; x < kList; x += kThreads)
+    if (uint32_t(x % kWinPer) < sh.win_cnt[x / kWinPer]) fn(x);
+}
+
+// Row context for re-scoring: the row's query as the A operand, in the
+// tile slot it occupies in the indexer kernel, and its head weights.
+template <int kHI, int kKS>
+struct Rescore {
+  u32x4 a[kKS];
+  int sa[kKS];
+  float wv[4];
+  bool mine;  // this lane's C rows belong to the row's query
+};
+
+template <int kHI, int kKS>
+CSA_DEV void rescore_setup(Rescore<kHI, kKS>& R, const uint8_t* q_codes, const uint8_t* q_e8m0, const float* w,
+                           size_t qrow, int i, int nblk, int row_bytes) {
+  constexpr int kQPT = 16 / kHI;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int slot = i % kQPT;
+  const bool a_mine = col / kHI == slot;
+  load_a<kHI, kKS>(q_codes, q_e8m0, qrow * kHI + (col % kHI), a_mine, g, nblk, row_bytes, R.a, R.sa);
+  const int rc = 4 * g;
+  R.mine = rc / kHI == slot;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) R.wv[x] = R.mine ? w[qrow * kHI + (rc + x) % kHI] : 0.f;
+}
+
+// Exact keys of the listed entries cand_idx[0..n) into cand_key[0..n); the
+// 16 waves take 16-entry groups in turn.  Ends with a block barrier.
+template <int kHI, int kKS>
+CSA_DEV void rescore_list(const Rescore<kHI, kKS>& R, const uint8_t* kc_seq, const uint8_t* ke_seq, int n,
+                          int nblk, int row_bytes, Shared& sh) {
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int wid = threadIdx.x >> 6;
+  for (int grp = wid; grp * 16 < n; grp += kThreads / 64) {
+    const int j = grp * 16 + col;
+    const int e = j < n ? sh.cand_idx[j] : 0;
+    u32x4 bk[kKS];
+    int sb[kKS];
+    load_b<kKS, false>(kc_seq, ke_seq, e, j < n, g, nblk, row_bytes, bk, sb);
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) acc = mfma_fp4(R.a[ks], R.sa[ks], bk[ks], sb[ks], acc);
+    bool writer;
+    const float p = head_sum<kHI>(acc, R.wv, g, writer);
+    if (writer && R.mine && j < n) sh.cand_key[j] = ordered_key(p);
+  }
+  __syncthreads();
+}
+
+CSA_DEV uint32_t pow2_ceil(uint32_t x) { return x <= 1u ? 1u : 1u << (32 - __clz(x - 1u)); }
+
+template <int kHI, int kKS, int kJ>
+__global__ __launch_bounds__(kThreads) void select_kernel(const uint16_t* __restrict__ key16,
+                                                          const uint8_t* __restrict__ q_codes,
+                                                          const uint8_t* __restrict__ q_e8m0,
+                                                          const float* __restrict__ w,
+                                                          const uint8_t* __restrict__ k_codes,
+                                                          const uint8_t* __restrict__ k_e8m0,
+                                                          const int32_t* __restrict__ q_pos0, int T_q, int d_I,
+                                                          int cap, int m, int k, int32_t* __restrict__ idx) {
+  constexpr int kS = kJ * kRound;          // keys per chunk; chunk 0 stays in registers
+  constexpr int kWPT = kS / 32 / kThreads;  // bitmap words per thread
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  Shared& sh = *reinterpret_cast<Shared*>(smem_raw);
+
+  const int row = blockIdx.x;
+  const int b = row / T_q;
+  const int i = row - b * T_q;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int t = q_pos0[b] + i;
+  const int nv = max(0, min((t + 1) / m, cap));
+  int32_t* out = idx + size_t(row) * k;
+  if (nv <= k) {
+    for (int j = tid; j < k; j += kThreads) out[j] = j < nv ? j : -1;
+    return;
+  }
+  const uint16_t* src = key16 + size_t(row) * cap;
+  const int n_chunks = (nv + kS - 1) / kS;
+  const int nblk = d_I >> 5;
+  const int row_bytes = d_I >> 1;
+  const uint8_t* kc_seq = k_codes + size_t(b) * cap * row_bytes;
+  const uint8_t* ke_seq = k_e8m0 + size_t(b) * cap * nblk;
+
+  for (int j = tid; j < kBuckets; j += kThreads) sh.hist[j] = 0u;
+  for (int j = tid; j < kS / 32; j += kThreads) sh.bm.eq[j] = 0u;
+  if (tid == 0) {
+    sh.n_win = 0u;
+    sh.n_gt = 0u;
+    sh.n_cand = 0u;
+  }
+  const __amdgpu_buffer_rsrc_t rs = row_rsrc(src, nv);
+  uint32_t P[kJ][2];
+  load_chunk0<kJ>(rs, P);
+  __syncthreads();
+
+  // ---- a: sample histogram: keys (j, 0) of the even rounds j of chunk 0
+  // (the first 1024 of every 8192 indices)
+#pragma unroll
+  for (int j = 0; j < kJ; j += 2) {
+    const uint32_t kk = kget<kJ>(P, j, 0);
+    if (kk) atomicAdd(&sh.hist[kk >> 2], 1u);
+  }
+  int n_sample = 0;
+#pragma unroll
+  for (int j = 0; j < kJ; j += 2) n_sample += max(0, min(nv - j * kRound, kThreads));
+  __syncthreads();
+  const int k_s = max(1, int((long(k) * n_sample) / nv));
+  const int margin = 4 * int(sqrtf(float(k_s))) + 16;
+  const uint32_t r_hi = uint32_t(max(1, k_s - margin));
+  const uint32_t r_lo = uint32_t(min(n_sample, k_s + margin));
+  find_bin(sh.hist, kBuckets, r_hi, &sh.sel, sh.smem);
+  find_bin(sh.hist, kBuckets, r_lo, &sh.sel2, sh.smem);
+  const uint32_t b_hi = sh.sel.bin, b_lo = sh.sel2.bin;   // b_lo <= b_hi
+
+  // ---- b: keys above the window counted, keys inside listed
+  {
+    const uint32_t lo16 = b_lo << 2, hi16 = (b_hi << 2) | 3u;
+    uint32_t n_in = 0u;
+    opaque<kJ>(P);
+    window_pass<kJ>([&](int j, int c) { return kget<kJ>(P, j, c); }, 0, lo16, hi16, sh.bm.gt, n_in, sh);
+    stream_batches(rs, kS, nv, [&](uint32_t(&v)[kBatch][4], int base) {
+      window_pass<kBatch>([&](int j, int c) { return v[j][c]; }, base, lo16, hi16, nullptr, n_in, sh);
+    });
+    if (lane == 0) {
+      sh.win_cnt[tid >> 6] = min(n_in, uint32_t(kWinPer));
+      atomicAdd(&sh.n_win, n_in);
+      if (n_in > uint32_t(kWinPer)) atomicAdd(&sh.n_win, uint32_t(kList) + 1u);   // overflow: a miss
+    }
+  }
+  __syncthreads();
+  const uint32_t n_above = sh.n_gt, n_win = sh.n_win;
+  const uint32_t win_bins = pow2_ceil((b_hi - b_lo + 1u) * 4u);
+  const bool hit = n_above < uint32_t(k) && n_above + n_win >= uint32_t(k) && n_win <= uint32_t(kList) &&
+                   win_bins <= uint32_t(kBuckets);
+
+  // ---- c: the k-th 16-bit key T (shift 0) or, on a miss, its 14-bit bucket (shift 2)
+  uint32_t thr, remaining, cnt;
+  int shift;
+  if (hit) {
+    const uint32_t lo16 = b_lo << 2;
+    for (int j = tid; j < int(win_bins); j += kThreads) sh.hist[j] = 0u;
+    __syncthreads();
+    each_window(sh, [&](int x) { atomicAdd(&sh.hist[uint32_t(sh.win_key[x]) - lo16], 1u); });
+    __syncthreads();
+    find_bin(sh.hist, int(win_bins), uint32_t(k) - n_above, &sh.sel, sh.smem);
+    thr = lo16 + sh.sel.bin;
+    remaining = sh.sel.remaining;
+    cnt = sh.sel.bincount;
+    shift = 0;
+  } else {
+    for (int j = tid; j < kBuckets; j += kThreads) sh.hist[j] = 0u;
+    __syncthreads();
+    opaque<kJ>(P);
+#pragma unroll
+    for (int j = 0; j < kJ; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t kk = kget<kJ>(P, j, c);
+        if (kk) atomicAdd(&sh.hist[kk >> 2], 1u);
+      }
+    stream_batches(rs, kS, nv, [&](uint32_t(&v)[kBatch][4], int) {
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (v[j][c]) atomicAdd(&sh.hist[v[j][c] >> 2], 1u);
+    });
+    __syncthreads();
+    find_bin(sh.hist, kBuckets, uint32_t(k), &sh.sel, sh.smem);
+    thr = sh.sel.bin;
+    remaining = sh.sel.remaining;
+    cnt = sh.sel.bincount;
+    shift = 2;
+  }
+  const bool whole = cnt == remaining;   // T's class is taken whole: no re-scoring
+  const bool crowded = !whole && cnt > uint32_t(kList);
+  const int low_bits = 16 + shift;       // exact keys of T's class share their top 32 - low_bits bits
+  uint32_t prefix = thr << low_bits;
+  uint32_t mask = ~((1u << low_bits) - 1u);
+  auto in_class = [&](uint32_t kk) { return kk != 0u && (kk >> shift) == thr; };
+  auto none = [](uint32_t) { return false; };
+
+  // ---- d: exact keys of T's class, radix refinement
+  Rescore<kHI, kKS> R;
+  if (!whole) {
+    rescore_setup<kHI, kKS>(R, q_codes, q_e8m0, w, size_t(b) * T_q + i, i, nblk, row_bytes);
+    if (!crowded) {
+      if (hit) {
+        // the class is a subset of the window list
+        for (int x0 = 0; x0 < kList; x0 += kThreads) {
+          const int x = x0 + tid;
+          const bool want = uint32_t(x % kWinPer) < sh.win_cnt[x / kWinPer] && uint32_t(sh.win_key[x]) == thr;
+          const uint64_t bal = __ballot(want);
+          uint32_t at = 0u;
+          if (lane == 0 && bal) at = atomicAdd(&sh.n_cand, uint32_t(__popcll(bal)));
+          at = __shfl(at, 0);
+          if (want) sh.cand_idx[at + __popcll(bal & ((uint64_t(1) << lane) - 1u))] = sh.win_idx[x];
+        }
+      } else {
+        opaque<kJ>(P);
+        list_batch<kJ>([&](int j, int c) { return kget<kJ>(P, j, c); }, 0, in_class, none, sh.cand_idx, nullptr,
+                       &sh.n_cand, nullptr, [&] { opaque<kJ>(P); });
+        stream_batches(rs, kS, nv, [&](uint32_t(&v)[kBatch][4], int base) {
+          list_batch<kBatch>([&](int j, int c) { return v[j][c]; }, base, in_class, none, sh.cand_idx, nullptr,
+                             &sh.n_cand, nullptr, [] {});
+        });
+      }
+      __syncthreads();
+      const int nc = int(sh.n_cand);
+      rescore_list<kHI, kKS>(R, kc_seq, ke_seq, nc, nblk, row_bytes, sh);
+      auto each_listed = [&](auto fn) {
+        for (int x = tid; x < nc; x += kThreads) fn(sh.cand_key[x]);
+      };
+      refine(each_listed, prefix, mask, remaining, sh);
+    } else {
+      // batches of 16384 keys read from the key row: list, re-score, visit
+      auto each_batch = [&](auto fn) {
+        stream_batches(rs, 0, nv, [&](uint32_t(&v)[kBatch][4], int base) {
+          for (int r = 0; r < kBatch; ++r) {
+            if (tid == 0) sh.n_cand = 0u;
+            __syncthreads();
+            list_batch<1>([&](int, int c) { return v[r][c]; }, base + r * kRound, in_class, none, sh.cand_idx,
+                          nullptr, &sh.n_cand, nullptr, [] {});
+            __syncthreads();
+            const int nc = int(sh.n_cand);
+            rescore_list<kHI, kKS>(R, kc_seq, ke_seq, nc, nblk, row_bytes, sh);
+            for (int x = tid; x < nc; x += kThreads) fn(sh.cand_key[x]);
+            __syncthreads();
+          }
+        });
+      };
+      refine(each_batch, prefix, mask, remaining, sh);
+    }
+  }
+
+  // ---- e: emission in index order, one chunk of kS keys at a time
+  uint32_t gt_off = 0u, eq_off = 0u;
+  const int wv = tid >> 6;
+  auto gt_of = [&](uint32_t kk) {
+    const uint32_t ck = kk >> shift;
+    return kk != 0u && (whole ? ck >= thr : ck > thr);
+  };
+  // bitmap words of the wave's 64 keys at chunk offset off + 64w (off a
+  // multiple of 1024): a per-wave base plus off/32
+  uint32_t* const gt_w = sh.bm.gt + 2 * wv;
+  uint32_t* const eq_w = sh.bm.eq + 2 * wv;
+  auto put_words = [&](int off, uint64_t gbal) {
+    if (lane == 0) {
+      gt_w[off >> 5] = uint32_t(gbal);
+      gt_w[(off >> 5) + 1] = uint32_t(gbal >> 32);
+      eq_w[off >> 5] = 0u;
+      eq_w[(off >> 5) + 1] = 0u;
+    }
+  };
+#pragma unroll 1
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    opaque<kJ>(P);
+    __syncthreads();   // earlier readers of the bitmaps are done
+    if (ch == 0 && hit) {
+      // keys above the window are already marked; add the window keys above T
+      // (and T's class itself when it is taken whole)
+      each_window(sh, [&](int x) {
+        const int e = sh.win_idx[x];
+        const uint32_t kk = sh.win_key[x];
+        if (e < kS && (kk > thr || (whole && kk == thr))) atomicOr(&sh.bm.gt[e >> 5], 1u << (e & 31));
+      });
+    } else if (ch == 0) {
+#pragma unroll
+      for (int j = 0; j < kJ; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) put_words(j * kRound + c * kThreads, __ballot(gt_of(kget<kJ>(P, j, c))));
+    } else {
+      // words of rounds past nv are zero; batches holding keys are streamed
+      const int r_end = min(nv, (ch + 1) * kS);
+      const int w_from = ((r_end - ch * kS + kBatch * kRound - 1) / (kBatch * kRound)) * (kBatch * kRound) / 32;
+      for (int x = w_from + tid; x < kS / 32; x += kThreads) {
+        sh.bm.gt[x] = 0u;
+        sh.bm.eq[x] = 0u;
+      }
+      stream_batches(rs, ch * kS, r_end, [&](uint32_t(&v)[kBatch][4], int base) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            put_words(base - ch * kS + j * kRound + c * kThreads, __ballot(gt_of(v[j][c])));
+      });
+    }
+    __syncthreads();
+    if (!whole) {
+      // T's class in this chunk, by the exact keys
+      auto mark = [&](int e, uint32_t kx) {
+        const int x = e - ch * kS;
+        if (x < 0 || x >= kS) return;
+        const uint32_t km = kx & mask;
+        if (km > prefix) atomicOr(&sh.bm.gt[x >> 5], 1u << (x & 31));
+        else if (km == prefix) atomicOr(&sh.bm.eq[x >> 5], 1u << (x & 31));
+      };
+      if (!crowded) {
+        const int nc = int(sh.n_cand);
+        for (int x = tid; x < nc; x += kThreads) mark(sh.cand_idx[x], sh.cand_key[x]);
+      } else {
+        stream_batches(rs, ch * kS, min(nv, (ch + 1) * kS), [&](uint32_t(&v)[kBatch][4], int base) {
+          for (int r = 0; r < kBatch; ++r) {
+            if (tid == 0) sh.n_cand = 0u;
+            __syncthreads();
+            list_batch<1>([&](int, int c) { return v[r][c]; }, base + r * kRound, in_class, none, sh.cand_idx,
+                          nullptr, &sh.n_cand, nullptr, [] {});
+            __syncthreads();
+            const int nc = int(sh.n_cand);
+            rescore_list<kHI, kKS>(R, kc_seq, ke_seq, nc, nblk, row_bytes, sh);
+            for (int x = tid; x < nc; x += kThreads) mark(sh.cand_idx[x], sh.cand_key[x]);
+            __syncthreads();
+          }
+        });
+      }
+      __syncthreads();
+    }
+    // thread t owns bitmap words [t*kWPT, (t+1)*kWPT); greater counts fit 15
+    // bits (at most k < 32768) and equal counts 17 bits (<= keys per chunk)
+    uint32_t wg[kWPT], we[kWPT];
+    uint32_t n_g = 0u, n_e = 0u;
+#pragma unroll
+    for (int x = 0; x < kWPT; ++x) {
+      wg[x] = sh.bm.gt[tid * kWPT + x];
+      we[x] = sh.bm.eq[tid * kWPT + x];
+      n_g += __popc(wg[x]);
+      n_e += __popc(we[x]);
+    }
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan((n_g << 17) | n_e, sh.smem, &tot);
+    uint32_t gt_before = gt_off + (ex >> 17);
+    uint32_t eq_before = eq_off + (ex & 0x1FFFFu);
+#pragma unroll
+    for (int x = 0; x < kWPT; ++x) {
+      const int x0 = ch * kS + (tid * kWPT + x) * 32;
+      uint32_t any = wg[x] | we[x];
+      while (any) {
+        const int bit = __ffs(any) - 1;
+        any &= any - 1u;
+        if ((wg[x] >> bit) & 1u) {
+          out[gt_before + min(eq_before, remaining)] = x0 + bit;
+          ++gt_before;
+        } else {
+          if (eq_before < remaining) out[gt_before + eq_before] = x0 + bit;
+          ++eq_before;
+        }
+      }
+    }
+    gt_off += tot >> 17;
+    eq_off += tot & 0x1FFFFu;
+  }
+}
+
+template <int kHI, int kKS, int kJ>
+hipError_t launch_select_j(long rows, hipStream_t st, const uint16_t* key16, const uint8_t* qc, const uint8_t* qe,
+                           const float* w, const uint8_t* kc, const uint8_t* ke, const int32_t* pos, int T_q,
+                           int d_I, int cap, int m, int k, int32_t* idx) {
+  static bool attr = false;   // more than 64 KB of LDS needs the opt-in
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<kHI, kKS, kJ>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(Shared)));
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((select_kernel<kHI, kKS, kJ>), dim3(unsigned(rows)), dim3(kThreads), sizeof(Shared), st, key16, qc, qe, w, kc, ke, pos, T_q,
+                     d_I, cap, m, k, idx);
+  return hipGetLastError();
+}
+
+template <int kHI, int kKS>
+hipError_t launch_select_ks(long rows, hipStream_t st, const uint16_t* key16, const uint8_t* qc, const uint8_t* qe,
+                            const float* w, const uint8_t* kc, const uint8_t* ke, const int32_t* pos, int T_q,
+                            int d_I, int cap, int m, int k, int32_t* idx) {
+  // rows of up to 32768 keys are held whole in 8 rounds of registers; longer
+  // rows keep their first 65536 keys in 16 rounds and read the rest
+  if (cap <= 8 * kRound)
+    return launch_select_j<kHI, kKS, 8>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx);
+  return launch_select_j<kHI, kKS, 16>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx);
+}
+
+template <int kHI>
+hipError_t launch_select_h(int ks, long rows, hipStream_t st, const uint16_t* key16, const uint8_t* qc,
+                           const uint8_t* qe, const float* w, const uint8_t* kc, const uint8_t* ke,
+                           const int32_t* pos, int T_q, int d_I, int cap, int m, int k, int32_t* idx) {
+  switch (ks) {
+    case 1: return launch_select_ks<kHI, 1>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx);
+    case 2: return launch_select_ks<kHI, 2>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx);
+    case 3: return launch_select_ks<kHI, 3>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx);
+    default: return launch_select_ks<kHI, 4>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx);
+  }
+}
+
+}  // namespace
+
+// Workspace of csa_indexer_topk: the 16-bit keys of every (query, entry).
+size_t csa_indexer_topk_workspace_size(long rows, int cap) { return size_t(rows) * size_t(cap) * 2u; }
+
+extern "C" csa_status_t csa_indexer_topk(const uint8_t* q_codes, const uint8_t* q_e8m0, const float* w,
+                                         const uint8_t* k_codes, const uint8_t* k_e8m0, const int32_t* q_pos0,
+                                         int32_t B, int32_t T_q, int32_t H_I, int32_t d_I, int32_t cap, int32_t m,
+                                         int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  if (!idx || k < 1) return CSA_EINVAL;
+  const csa_status_t s = csa_ix::check_indexer_args(q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, B, T_q, H_I, d_I,
+                                                    cap, m);
+  if (s != CSA_OK) return s;
+  if (k > 32767) return CSA_ENOTSUP;
+  const long rows = long(B) * T_q;
+  if (rows == 0) return CSA_OK;
+  if (rows > 0x7FFFFFFFL) return CSA_ENOTSUP;
+  const size_t need = csa_indexer_topk_workspace_size(rows, cap);
+  if (need > 0 && (!ws || ws_bytes < need)) return CSA_EWORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint16_t* key16 = static_cast<uint16_t*>(ws);
+  hipError_t err = hipSuccess;
+  if (cap > 0) {
+    err = csa_ix::launch_indexer<csa_ix::kKey16>(H_I, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, B, T_q, d_I, cap,
+                                                 m, key16, st);
+    if (err != hipSuccess) return CSA_EHIP;
+  }
+  const int ks = (d_I + 127) / 128;
+  switch (H_I) {
+    case 4: err = launch_select_h<4>(ks, rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_q, d_I, cap, m, k, idx); break;
+    case 8: err = launch_select_h<8>(ks, rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_q, d_I, cap, m, k, idx); break;
+    default: err = launch_select_h<16>(ks, rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_q, d_I, cap, m, k, idx); break;
+  }
+  return err == hipSuccess ? CSA_OK : CSA_EHIP;
+}

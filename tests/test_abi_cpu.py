@@ -25,8 +25,8 @@ def test_every_declared_symbol_is_exported():
     import long_context_compressed_03_amd as csa
     lib = ctypes.CDLL(LIB)
     names = declared_functions()
-    assert {"csa_compress_kv", "csa_indexer_scores", "csa_topk", "csa_sparse_attn",
-            "hca_dense_attn"} <= set(names)
+    assert {"csa_compress_kv", "csa_indexer_scores", "csa_indexer_topk", "csa_topk",
+            "csa_sparse_attn", "hca_dense_attn"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(csa.EXPORTS)
@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 def test_status_strings_and_version():
     import long_context_compressed_03_amd as csa
     lib = csa.load()
-    assert lib.csa_abi_version() == 100
+    assert lib.csa_abi_version() == 101
     for s in range(5):
         assert lib.csa_status_str(s).decode().startswith("CSA_")
 
@@ -79,6 +79,27 @@ def test_indexer_rejects_bad_arguments():
     assert call(d_I=48) == csa.CSA_EINVAL
     assert call(d_I=1024) == csa.CSA_EINVAL
     assert call(m=0) == csa.CSA_EINVAL
+    assert call(B=0) == csa.CSA_OK
+
+
+def test_indexer_topk_rejects_bad_arguments():
+    import long_context_compressed_03_amd as csa
+    lib = csa.load()
+    need = lib.csa_workspace_size(csa.CSA_OP_INDEXER_TOPK, 1, 2, 0, 128, 16)
+    assert need == 1 * 2 * 16 * 2                 # one 16-bit key per (query, entry)
+
+    def call(k=8, H_I=8, d_I=128, m=4, ws=_p(), nws=need, B=1, T=2, cap=16, idx=_p(), q=_p()):
+        return lib.csa_indexer_topk(q, _p(), _p(), _p(), _p(), _p(), B, T, H_I, d_I, cap, m, k,
+                                    idx, ws, nws, None)
+    assert call(k=0) == csa.CSA_EINVAL
+    assert call(idx=None) == csa.CSA_EINVAL
+    assert call(q=None) == csa.CSA_EINVAL
+    assert call(d_I=48) == csa.CSA_EINVAL
+    assert call(m=0) == csa.CSA_EINVAL
+    assert call(H_I=3) == csa.CSA_ENOTSUP
+    assert call(k=32768) == csa.CSA_ENOTSUP
+    assert call(ws=None) == csa.CSA_EWORKSPACE
+    assert call(nws=need - 1) == csa.CSA_EWORKSPACE
     assert call(B=0) == csa.CSA_OK
 
 

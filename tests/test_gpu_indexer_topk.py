@@ -1,0 +1,116 @@
+"""GPU parity of the fused indexer + top-k call (csa_indexer_topk).
+
+Against the oracle (indexer scores, then top-k with the lower-index tie rule)
+on exact inputs, and bit for bit against the unfused pair of calls
+(csa_topk on csa_indexer_scores) on inputs whose scores are NOT exact in fp32,
+which the fused call promises to reproduce for any input values.  Cases cover
+decode rows, prefill chunks with ragged visibility, rows longer than the part
+the kernel keeps in registers, thresholds that fall inside a bucket of exact
+ties (including one larger than the on-chip candidate list), and thresholds
+that take a whole bucket.
+"""
+import numpy as np
+import pytest
+import torch
+
+from csa_synth import indexer_inputs, streams
+from gpu_helpers import h, say, t_f32, t_i32, t_u8
+from oracle.indexer import indexer_scores
+from oracle.topk import topk
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def csa():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import long_context_compressed_03_amd as m
+    m.load()
+    return m
+
+
+def _dev(x):
+    return (t_u8(x["q_codes"]), t_u8(x["q_e8m0"]), t_f32(x["w"]), t_u8(x["k_codes"]),
+            t_u8(x["k_e8m0"]))
+
+
+def _fused(csa, x, pos, m, k):
+    got = csa.csa_indexer_topk(*_dev(x), t_i32(pos), m, k)
+    torch.cuda.synchronize()
+    return h(got)
+
+
+FUSED_CASES = [
+    # B, T, cap, H_I, d_I, m, k, pos0 list, tie_heavy
+    (1, 1, 1024, 4, 64, 4, 64, [4095], False),                     # tiny decode shape
+    (3, 1, 32768, 8, 128, 4, 1024, [131071, 100000, 2000], False),  # 128K decode rows; one row < k
+    (1, 6, 70000, 8, 128, 4, 2048, [279990], False),               # rows past the register chunk
+    (2, 33, 5000, 8, 128, 4, 100, [19900, 300], False),            # ragged chunk rows; early rows < k
+    (1, 4, 20000, 4, 64, 4, 500, [79990], True),                   # threshold among exact ties
+    (1, 3, 3000, 16, 256, 2, 200, [5990], False),                  # 16 heads, two contraction steps
+]
+
+
+@pytest.mark.parametrize("B,T,cap,H_I,d_I,m,k,pos,tie", FUSED_CASES)
+def test_fused_matches_oracle(csa, B, T, cap, H_I, d_I, m, k, pos, tie):
+    say(f"indexer_topk B={B} T={T} cap={cap} H_I={H_I} d_I={d_I} k={k} tie={tie}")
+    x = indexer_inputs(B, T, cap, H_I, d_I, seed=cap + k, tie_heavy=tie)
+    pos = np.array(pos, np.int32)
+    s = indexer_scores(x["q_codes"], x["q_e8m0"], x["w"], x["k_codes"], x["k_e8m0"], pos, m)
+    ref = topk(s.astype(np.float32), pos, m, k)
+    got = _fused(csa, x, pos, m, k)
+    assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
+
+
+def test_fused_crowded_and_whole_buckets(csa):
+    """Row 0: a zero query, so every visible entry ties at score 0 and the threshold
+    bucket holds all of them (more than the on-chip list: re-scored in rounds).
+    Row 1: exactly k entries score 256 and the rest 0, so the k-th key's bucket is
+    taken whole.  Row 2: its own random query against the same keys."""
+    say("indexer_topk crowded / whole-bucket rows")
+    B, T, cap, H_I, d_I, m, k = 1, 3, 12000, 4, 64, 4, 300
+    x = indexer_inputs(B, T, cap, H_I, d_I, seed=77)
+    x["q_codes"][0, 0] = 0                                   # row 0: zero query
+    x["q_codes"][0, 1] = 0x22                                # row 1: every element +1
+    x["q_e8m0"][0, 1] = 127
+    x["w"][0, 1] = 1.0
+    (r,) = streams(99, 0, 1)
+    hot = np.sort(r.choice(cap, size=k, replace=False))
+    kc = x["k_codes"].copy()
+    ke = x["k_e8m0"].copy()
+    kc[0] = 0                                                # keys: zero ...
+    kc[0, hot] = 0x22                                        # ... except k of them, all +1
+    ke[0] = 127
+    x2 = dict(x, k_codes=kc, k_e8m0=ke)
+    pos = np.array([4 * cap - 1], np.int32)                 # every row sees all cap entries
+    s = indexer_scores(x2["q_codes"], x2["q_e8m0"], x2["w"], kc, ke, pos, m)
+    assert np.all(s[0, 0] == 0) and np.sum(s[0, 1] == 256.0) == k
+    ref = topk(s.astype(np.float32), pos, m, k)
+    assert np.array_equal(ref[0, 0], np.arange(k)) and np.array_equal(ref[0, 1], hot)
+    got = _fused(csa, x2, pos, m, k)
+    assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
+
+
+@pytest.mark.parametrize("B,T,cap,k,pos", [
+    (1, 64, 70000, 2048, [279900]),     # prefill chunk rows past the register chunk
+    (4, 1, 32768, 1024, [131071] * 4),  # decode rows
+])
+def test_fused_equals_unfused_on_inexact_scores(csa, B, T, cap, k, pos):
+    """Non-dyadic head weights and wide block scales make the scores inexact in fp32;
+    the fused call must still select exactly what csa_topk selects on the scores
+    csa_indexer_scores writes."""
+    say(f"indexer_topk vs unfused (inexact) B={B} T={T} cap={cap} k={k}")
+    H_I, d_I, m = 8, 128, 4
+    x = indexer_inputs(B, T, cap, H_I, d_I, seed=cap + T)
+    (r,) = streams(123, cap, 1)
+    x["w"] = r.uniform(0.1, 3.0, size=x["w"].shape).astype(np.float32)
+    x["q_e8m0"] = r.integers(110, 140, size=x["q_e8m0"].shape).astype(np.uint8)
+    x["k_e8m0"] = r.integers(110, 140, size=x["k_e8m0"].shape).astype(np.uint8)
+    pos = np.array(pos, np.int32)
+    d = _dev(x)
+    scores = csa.csa_indexer_scores(*d, t_i32(pos), m)
+    ref = h(csa.csa_topk(scores, t_i32(pos), m, k))
+    got = h(csa.csa_indexer_topk(*d, t_i32(pos), m, k))
+    torch.cuda.synchronize()
+    assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
