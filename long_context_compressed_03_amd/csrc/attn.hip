@@ -17,7 +17,8 @@
 //   S^T[keys x 16 heads] = K * Q^T    (bf16 MFMA 16x16x32, Q held in VGPRs)
 //   online softmax per head in fp32, exp2 domain
 //   O^T[128 x 16 heads] += V^T * P^T  (P^T taken straight from S^T's C layout)
-// fp8 (E4M3FN) entries are widened to bf16 exactly; the per-entry K scale
+// fp8 (E4M3FN) entries are widened to bf16 exactly by the hardware
+// conversion (fp32 variant: in software); the per-entry K scale
 // multiplies the logits and the V scale is folded into P.  The fp32 variant
 // runs the same data flow on the fp32 MFMA 16x16x4 (V row-major there).
 //
@@ -231,31 +232,48 @@ constexpr size_t lds_bytes() {
   return sizeof(LdsChunk<kIO>) > sizeof(LdsHalf<kHTW>) ? sizeof(LdsChunk<kIO>) : sizeof(LdsHalf<kHTW>);
 }
 
+// 8 head dims of a gathered part as four bf16 pairs (src 0 -> zeros).  E4M3
+// codes go through the CDNA4 fp8 -> bf16 conversion, which is exact (every
+// E4M3 value is a bf16 value); the per-entry scale is applied elsewhere.
+template <int kCKV>
+CSA_DEV u32x4 part_bf16(const u32x4* w, int src) {
+  if (src == 0) return u32x4{0u, 0u, 0u, 0u};
+  if (kCKV == CSA_FP8_E4M3 && src == 1) {
+    const uint32_t c0 = w[0][0], c1 = w[0][1];
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, 1.0f, true))};
+  }
+  return w[0];
+}
+
 template <int kIO, int kCKV>
 CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr) {
   const int kp = threadIdx.x & 31;
   const int dg = threadIdx.x >> 5;
-  float xk[2][8], xv[2][8];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    part_f32<kIO, kCKV>(pr.k[e], pr.src[e], xk[e]);
-    part_f32<kIO, kCKV>(pr.v[e], pr.src[e], xv[e]);
-  }
   if constexpr (kIO == CSA_BF16) {
-    // values are exact in bf16 (bf16 inputs or E4M3 codes): keep the top halves
+    // values are exact in bf16 (bf16 inputs or E4M3 codes)
+    u32x4 kw[2], vw[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      uint32_t w[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-        w[x] = (__float_as_uint(xk[e][2 * x]) >> 16) | (__float_as_uint(xk[e][2 * x + 1]) & 0xFFFF0000u);
-      *reinterpret_cast<u32x4*>(&s.K[2 * kp + e][dg * 8]) = u32x4{w[0], w[1], w[2], w[3]};
+      kw[e] = part_bf16<kCKV>(pr.k[e], pr.src[e]);
+      vw[e] = part_bf16<kCKV>(pr.v[e], pr.src[e]);
+      *reinterpret_cast<u32x4*>(&s.K[2 * kp + e][dg * 8]) = kw[e];
     }
+    // V^T: head dim x of keys 2kp and 2kp+1 as one bf16 pair
 #pragma unroll
-    for (int x = 0; x < 8; ++x)
-      *reinterpret_cast<uint32_t*>(&s.Vt[dg * 8 + x][2 * kp]) =
-          (__float_as_uint(xv[0][x]) >> 16) | (__float_as_uint(xv[1][x]) & 0xFFFF0000u);
+    for (int x = 0; x < 4; ++x) {
+      *reinterpret_cast<uint32_t*>(&s.Vt[dg * 8 + 2 * x][2 * kp]) = (vw[0][x] & 0xFFFFu) | (vw[1][x] << 16);
+      *reinterpret_cast<uint32_t*>(&s.Vt[dg * 8 + 2 * x + 1][2 * kp]) = (vw[0][x] >> 16) | (vw[1][x] & 0xFFFF0000u);
+    }
   } else {
+    float xk[2][8], xv[2][8];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      part_f32<kIO, kCKV>(pr.k[e], pr.src[e], xk[e]);
+      part_f32<kIO, kCKV>(pr.v[e], pr.src[e], xv[e]);
+    }
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
@@ -309,7 +327,8 @@ CSA_DEV void store_out4(void* out, long orow, int d4, v4f v) {
 // w / 4 (keys [32*(w/4), 32*(w/4)+32) of every chunk); the two halves merge at
 // the end of the block through LDS.
 template <int kIO, int kCKV, bool kDense, int kHTW>
-__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kIO == CSA_BF16 && kHTW == 1 ? 4 : 1)))
+void attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   LdsChunk<kIO>& s = *reinterpret_cast<LdsChunk<kIO>*>(smem);
 
