@@ -564,6 +564,219 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict_
   }
 }
 
+// ------------------------------------------------- dense, many queries --
+// HCA prefill: consecutive queries of a sequence see nearly the same keys
+// (entries e < floor((t+1)/m') and a window that moves by one position per
+// query), so a block takes kQB = 256/H consecutive queries (H = 32, 64, 128) and streams the
+// UNION of their key lists: entries [0, nvis(last query)) then raw positions
+// [t_first - W + 1, t_last].  Every gathered chunk serves all kQB queries;
+// each key carries a tag (entry index, or raw position) from which each
+// query's wave applies its own visibility.  Wave w takes query w / (8/kQB)
+// and two 16-head tiles; both tiles share every K and V^T fragment it reads
+// from LDS.  Each key takes part exactly as in the one-query kernel, so the
+// arithmetic per (query, head) is the same online softmax over 64-key chunks.
+struct LdsMQ {
+  LdsBf16 c;
+  int tag[kNK];   // >= 0: compressed entry; <= -2: raw position -(tag + 2); -1: empty
+};
+
+template <int kCKV>
+CSA_DEV void prefetch_mq(const AttnArgs& a, Pre<CSA_BF16>& pr, int (&tag)[2], int b, int raw0, int nv_max, int p_lo,
+                         int n_list, int jc) {
+  const int kp = threadIdx.x & 31;
+  const int dg = threadIdx.x >> 5;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int j = jc + 2 * kp + x;
+    long row = 0;
+    int src = 0, tg = -1;
+    if (j < nv_max) {
+      row = long(b) * a.cap + j;
+      src = 1;
+      tg = j;
+    } else if (j < n_list) {
+      const int p = p_lo + (j - nv_max);
+      const int r = p - raw0;
+      if (p >= 0 && r >= 0 && r < a.L_raw) {
+        row = long(b) * a.L_raw + r;
+        src = 2;
+        tg = -(p + 2);
+      }
+    }
+    pr.src[x] = src;
+    tag[x] = tg;
+    pr.sk[x] = 1.f;
+    pr.sv[x] = 1.f;
+    if (src == 1) {
+      load_part<kCKV>(a.ck, row, dg, pr.k[x]);
+      load_part<kCKV>(a.cv, row, dg, pr.v[x]);
+      if constexpr (kCKV == CSA_FP8_E4M3) {
+        pr.sk[x] = a.ck_scale[row];
+        pr.sv[x] = a.cv_scale[row];
+      }
+    } else if (src == 2) {
+      load_part<CSA_BF16>(a.k_win, row, dg, pr.k[x]);
+      load_part<CSA_BF16>(a.v_win, row, dg, pr.v[x]);
+    }
+  }
+}
+
+template <int kCKV, int kQB>
+__global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
+  static_assert(kQB == 2 || kQB == 4 || kQB == 8, "two 16-head tiles per wave");
+  constexpr int kWPQ = 8 / kQB;   // waves per query; each takes two 16-head tiles
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  LdsMQ& s = *reinterpret_cast<LdsMQ*>(smem);
+
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int blocks_per_seq = (a.T_q + kQB - 1) / kQB;
+  const int b = int(blockIdx.x / blocks_per_seq);
+  const int i0 = int(blockIdx.x - long(b) * blocks_per_seq) * kQB;
+  const int qi = wid / kWPQ;
+  const int i = i0 + qi;
+  const bool q_ok = i < a.T_q;
+  const int pos0 = a.q_pos0[b];
+  const int t = pos0 + i;
+  const int raw0 = a.W > 0 ? a.raw_pos0[b] : 0;
+  const int i_last = min(i0 + kQB, a.T_q) - 1;
+  const int nv_max = min((pos0 + i_last + 1) / a.k, a.cap);
+  const int p_lo = pos0 + i0 - a.W + 1;
+  const int n_win = a.W > 0 ? a.W + (i_last - i0) : 0;
+  const int n_list = nv_max + n_win;
+  // this wave's query: visible entries and window
+  const int nv_q = min((t + 1) / a.k, a.cap);
+  const int w_lo = max(0, t - a.W + 1);
+
+  u32x4 qb[2][4];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    const int head = ((wid % kWPQ) * 2 + ht) * 16 + col;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((long(b) * a.T_q + (q_ok ? i : i0)) * a.H + head) * kHeadDim;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qb[ht][ks] = *reinterpret_cast<const u32x4*>(qp + ks * 32 + g * 8);
+  }
+  v4f o[2][8];
+  float m_run[2], l_run[2];
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[ht][dt] = v4f{0.f, 0.f, 0.f, 0.f};
+    m_run[ht] = -INFINITY;
+    l_run[ht] = 0.f;
+  }
+
+  // two chunks in flight: chunk c is stored from one register set while
+  // chunk c + 1 is still loading into the other
+  Pre<CSA_BF16> pr[2];
+  int tag[2][2];
+  if (n_list > 0) prefetch_mq<kCKV>(a, pr[0], tag[0], b, raw0, nv_max, p_lo, n_list, 0);
+  if (n_list > kNK) prefetch_mq<kCKV>(a, pr[1], tag[1], b, raw0, nv_max, p_lo, n_list, kNK);
+  auto step = [&](Pre<CSA_BF16>& prc, int (&tgc)[2], int j0) {
+    __syncthreads();
+    store_chunk<CSA_BF16, kCKV>(s.c, prc);
+    if ((threadIdx.x >> 5) == 0) {
+      s.tag[2 * (threadIdx.x & 31)] = tgc[0];
+      s.tag[2 * (threadIdx.x & 31) + 1] = tgc[1];
+    }
+    __syncthreads();
+    if (j0 + 2 * kNK < n_list) prefetch_mq<kCKV>(a, prc, tgc, b, raw0, nv_max, p_lo, n_list, j0 + 2 * kNK);
+    // S^T for the 4 key tiles x 2 head tiles; K fragments shared by both tiles
+    float x[2][4][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(&s.c.K[kt * 16 + col][ks * 32 + g * 8]);
+        acc[0] = mfma_k32(kf, qb[0][ks], acc[0]);
+        acc[1] = mfma_k32(kf, qb[1][ks], acc[1]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kk = kt * 16 + 4 * g + r;
+        const int tg = s.tag[kk];
+        const bool vis = q_ok && (tg >= 0 ? tg < nv_q : (tg <= -2 && -(tg + 2) >= w_lo && -(tg + 2) <= t));
+        const float scl = s.c.sk[kk] * a.sm_log2;
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht) x[ht][kt][r] = vis ? acc[ht][r] * scl : -INFINITY;
+      }
+    }
+    uint32_t pw[2][2][4];   // [ht][32-key step][pair]
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cmax = fmaxf(cmax, x[ht][kt][r]);
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      const float m_new = fmaxf(m_run[ht], cmax);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[ht] - m_use);
+      m_run[ht] = m_new;
+      float psum = 0.f;
+      float p[4][4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[kt][r] = __builtin_amdgcn_exp2f(x[ht][kt][r] - m_use);
+          psum += p[kt][r];
+        }
+      l_run[ht] = l_run[ht] * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[ht][dt] *= alpha;
+      // 32-key step st covers key tiles 2st, 2st+1: contraction slot 8g+j <->
+      // key (2st)*16 + 4g + j (j < 4) / (2st+1)*16 + 4g + j - 4
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int h2 = 0; h2 < 4; ++h2) {
+          const int kt = 2 * st + (h2 >> 1);
+          const int r0 = (h2 & 1) * 2;
+          const int key = kt * 16 + 4 * g + r0;
+          pw[ht][st][h2] = uint32_t(f32_to_bf16(p[kt][r0] * s.c.sv[key])) |
+                           (uint32_t(f32_to_bf16(p[kt][r0 + 1] * s.c.sv[key + 1])) << 16);
+        }
+    }
+    // O^T += V^T P^T; V^T fragments shared by both tiles
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int k0 = st * 32 + 4 * g;
+      const u32x4 pb0 = {pw[0][st][0], pw[0][st][1], pw[0][st][2], pw[0][st][3]};
+      const u32x4 pb1 = {pw[1][st][0], pw[1][st][1], pw[1][st][2], pw[1][st][3]};
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(&s.c.Vt[dt * 16 + col][k0]);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(&s.c.Vt[dt * 16 + col][k0 + 16]);
+        const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+        o[0][dt] = mfma_k32(vf, pb0, o[0][dt]);
+        o[1][dt] = mfma_k32(vf, pb1, o[1][dt]);
+      }
+    }
+  };
+  for (int j0 = 0; j0 < n_list; j0 += 2 * kNK) {
+    step(pr[0], tag[0], j0);
+    if (j0 + kNK < n_list) step(pr[1], tag[1], j0 + kNK);
+  }
+  if (!q_ok) return;
+#pragma unroll
+  for (int ht = 0; ht < 2; ++ht) {
+    float L = l_run[ht] + __shfl_xor(l_run[ht], 16);
+    L += __shfl_xor(L, 32);
+    const int head = ((wid % kWPQ) * 2 + ht) * 16 + col;
+    const long orow = (long(b) * a.T_q + i) * a.H + head;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) store_out4<CSA_BF16>(a.out, orow, dt * 4 + g, o[ht][dt] * inv);
+    if (a.lse && g == 0) a.lse[orow] = L > 0.f ? m_run[ht] * kLn2 + logf(L) : -INFINITY;
+  }
+}
+
 // ------------------------------------------------------------------ host --
 struct Plan {
   int n_splits, split_len;
@@ -614,6 +827,37 @@ hipError_t launch_attn(const AttnArgs& a, long blocks, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int kCKV, int kQB>
+hipError_t launch_mq_q(const AttnArgs& a, int B, hipStream_t st) {
+  static bool attr = false;
+  constexpr size_t bytes = sizeof(LdsMQ);
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_mq_kernel<kCKV, kQB>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const long blocks = long(B) * ((a.T_q + kQB - 1) / kQB);
+  hipLaunchKernelGGL((attn_mq_kernel<kCKV, kQB>), dim3(unsigned(blocks)), dim3(kThreads), bytes, st, a);
+  return hipGetLastError();
+}
+
+template <int kCKV>
+hipError_t launch_mq(const AttnArgs& a, int B, hipStream_t st) {
+  switch (a.H) {
+    case 32: return launch_mq_q<kCKV, 8>(a, B, st);
+    case 64: return launch_mq_q<kCKV, 4>(a, B, st);
+    default: return launch_mq_q<kCKV, 2>(a, B, st);
+  }
+}
+
+// The many-query dense kernel serves bf16 queries with H in {32, 64, 128}
+// when a sequence has enough queries to fill its blocks and the key lists
+// need no split.
+bool use_mq(int io_dtype, int H, int T_q, const Plan& p) {
+  return io_dtype == CSA_BF16 && (H == 32 || H == 64 || H == 128) && T_q >= 64 && p.n_splits == 1;
+}
+
 template <int kIO, int kCKV, bool kDense>
 hipError_t launch_tiles(const AttnArgs& a, long blocks, hipStream_t st) {
   return a.H <= 64 ? launch_attn<kIO, kCKV, kDense, 1>(a, blocks, st)
@@ -638,6 +882,10 @@ csa_status_t run_attn(AttnArgs a, int io_dtype, int ckv_dtype, int B, void* ws, 
     a.part_o = reinterpret_cast<float*>(w + ml);
   }
   hipError_t err;
+  if (kDense && use_mq(io_dtype, a.H, a.T_q, p) && (ckv_dtype == CSA_BF16 || ckv_dtype == CSA_FP8_E4M3)) {
+    err = ckv_dtype == CSA_BF16 ? launch_mq<CSA_BF16>(a, B, st) : launch_mq<CSA_FP8_E4M3>(a, B, st);
+    return err == hipSuccess ? CSA_OK : CSA_EHIP;
+  }
   if (io_dtype == CSA_BF16 && ckv_dtype == CSA_BF16) err = launch_tiles<CSA_BF16, CSA_BF16, kDense>(a, p.blocks, st);
   else if (io_dtype == CSA_BF16 && ckv_dtype == CSA_FP8_E4M3) err = launch_tiles<CSA_BF16, CSA_FP8_E4M3, kDense>(a, p.blocks, st);
   else if (io_dtype == CSA_F32 && ckv_dtype == CSA_F32) err = launch_tiles<CSA_F32, CSA_F32, kDense>(a, p.blocks, st);

@@ -261,6 +261,12 @@ DENSE_CASES = [
     ("bf16", "bf16", 1, 4, 16, 4, 8, 0, 1, [0]),            # empty key sets
     ("bf16", "bf16", 2, 130, 64, 16, 100, 32, 162, [1400, 30]),   # one block per query
     ("bf16", "fp8", 1, 300, 64, 128, 20, 128, 428, [2300]),
+    # prefill chunks: many queries per block over the union of their key lists
+    ("bf16", "fp8", 1, 522, 64, 16, 300, 64, 586, [4200]),      # ragged last block of 4 queries
+    ("bf16", "bf16", 1, 514, 128, 32, 200, 40, 554, [5000]),    # 2 queries per block
+    ("bf16", "bf16", 2, 300, 32, 8, 700, 16, 316, [4000, 50]),  # 8 per block; sequence at its start
+    ("bf16", "fp8", 1, 512, 64, 64, 100, 0, 1, [3000]),         # no window
+    ("bf16", "bf16", 1, 512, 64, 128, 8, 0, 1, [0]),            # leading queries see no key
 ]
 
 
