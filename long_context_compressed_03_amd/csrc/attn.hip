@@ -142,13 +142,15 @@ CSA_DEV void load_part(const void* base, long row, int dg, u32x4* dst) {
 
 // Gather item of thread tid: key pair kp = tid % 32 (keys 2kp, 2kp+1 of the
 // chunk), head dims [8*dg, 8*dg+8) with dg = tid / 32.
-template <int kIO, int kCKV, bool kDense>
-CSA_DEV void prefetch(const AttnArgs& a, Pre<kIO>& pr, int b, int i, int t, int raw0, int jc, int j_end) {
-  const int kp = threadIdx.x & 31;
-  const int dg = threadIdx.x >> 5;
-  // phase 1: the selected-entry indices of both slots (both loads in flight)
-  int e[2] = {-1, -1};
+//
+// Selected-entry indices of the item's two slots in chunk jc (sparse lists);
+// they are loaded one chunk ahead of the rows they name, so a row load never
+// waits on an index load issued in the same step.
+template <bool kDense>
+CSA_DEV void load_idx(const AttnArgs& a, int (&e)[2], int b, int i, int jc, int j_end) {
+  e[0] = e[1] = -1;
   if constexpr (!kDense) {
+    const int kp = threadIdx.x & 31;
     const int32_t* ip = a.idx + (long(b) * a.T_q + i) * a.k;
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
@@ -156,7 +158,13 @@ CSA_DEV void prefetch(const AttnArgs& a, Pre<kIO>& pr, int b, int i, int t, int 
       if (j < j_end && j < a.k) e[x] = ip[j];
     }
   }
-  // phase 2: rows of both slots
+}
+
+// Rows of the item's two slots of chunk jc (e: their indices from load_idx).
+template <int kIO, int kCKV, bool kDense>
+CSA_DEV void prefetch(const AttnArgs& a, Pre<kIO>& pr, const int (&e)[2], int b, int t, int raw0, int jc, int j_end) {
+  const int kp = threadIdx.x & 31;
+  const int dg = threadIdx.x >> 5;
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int j = jc + 2 * kp + x;
@@ -248,8 +256,9 @@ CSA_DEV u32x4 part_bf16(const u32x4* w, int src) {
   return w[0];
 }
 
+// sk_mul: factor folded into the stored K scale (the logit scale in the log2 domain).
 template <int kIO, int kCKV>
-CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr) {
+CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr, float sk_mul) {
   const int kp = threadIdx.x & 31;
   const int dg = threadIdx.x >> 5;
   if constexpr (kIO == CSA_BF16) {
@@ -285,7 +294,7 @@ CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr) {
   if (dg == 0) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      s.sk[2 * kp + e] = pr.sk[e];
+      s.sk[2 * kp + e] = pr.sk[e] * sk_mul;
       s.sv[2 * kp + e] = pr.sv[e];
       s.valid[2 * kp + e] = pr.src[e] != 0;
     }
@@ -294,8 +303,7 @@ CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr) {
 
 // S^T for one 16-key tile `kt` of the chunk, scaled to the log2 domain and masked.
 template <int kIO>
-CSA_DEV void logits_tile(const LdsChunk<kIO>& s, const u32x4* qb, const float* qf, int kt, float sm_log2, int col,
-                         int g, float* x) {
+CSA_DEV void logits_tile(const LdsChunk<kIO>& s, const u32x4* qb, const float* qf, int kt, int col, int g, float* x) {
   v4f acc = {0.f, 0.f, 0.f, 0.f};
   if constexpr (kIO == CSA_BF16) {
 #pragma unroll
@@ -308,15 +316,15 @@ CSA_DEV void logits_tile(const LdsChunk<kIO>& s, const u32x4* qb, const float* q
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int kk = kt * 16 + 4 * g + r;
-    x[r] = s.valid[kk] ? acc[r] * s.sk[kk] * sm_log2 : -INFINITY;
+    x[r] = s.valid[kk] ? acc[r] * s.sk[kk] : -INFINITY;
   }
 }
 
 template <int kIO>
 CSA_DEV void store_out4(void* out, long orow, int d4, v4f v) {
   if constexpr (kIO == CSA_BF16) {
-    const uint32_t w0 = uint32_t(f32_to_bf16(v[0])) | (uint32_t(f32_to_bf16(v[1])) << 16);
-    const uint32_t w1 = uint32_t(f32_to_bf16(v[2])) | (uint32_t(f32_to_bf16(v[3])) << 16);
+    const uint32_t w0 = pack_bf16x2(v[0], v[1]);
+    const uint32_t w1 = pack_bf16x2(v[2], v[3]);
     *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + orow * kHeadDim + d4 * 4) = u32x2{w0, w1};
   } else {
     *reinterpret_cast<v4f*>(static_cast<float*>(out) + orow * kHeadDim + d4 * 4) = v;
@@ -380,18 +388,24 @@ void attn_kernel(AttnArgs a) {
   }
 
   Pre<kIO> pr;
-  if (j_begin < j_end) prefetch<kIO, kCKV, kDense>(a, pr, b, i, t, raw0, j_begin, j_end);
+  int e_nx[2];
+  load_idx<kDense>(a, e_nx, b, i, j_begin, j_end);
+  if (j_begin < j_end) prefetch<kIO, kCKV, kDense>(a, pr, e_nx, b, t, raw0, j_begin, j_end);
+  load_idx<kDense>(a, e_nx, b, i, j_begin + kNK, j_end);
   for (int j0 = j_begin; j0 < j_end; j0 += kNK) {
     __syncthreads();
-    store_chunk<kIO, kCKV>(s, pr);
+    store_chunk<kIO, kCKV>(s, pr, a.sm_log2);
     __syncthreads();
-    if (j0 + kNK < j_end) prefetch<kIO, kCKV, kDense>(a, pr, b, i, t, raw0, j0 + kNK, j_end);
+    if (j0 + kNK < j_end) {
+      prefetch<kIO, kCKV, kDense>(a, pr, e_nx, b, t, raw0, j0 + kNK, j_end);
+      load_idx<kDense>(a, e_nx, b, i, j0 + 2 * kNK, j_end);
+    }
 #pragma unroll
     for (int ht = 0; ht < kHTW; ++ht) {
       if (!act[ht]) continue;
       float x[2][4];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) logits_tile<kIO>(s, qb[ht], qf[ht], 2 * kh + kk, a.sm_log2, col, g, x[kk]);
+      for (int kk = 0; kk < 2; ++kk) logits_tile<kIO>(s, qb[ht], qf[ht], 2 * kh + kk, col, g, x[kk]);
       float cmax = -INFINITY;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
@@ -399,9 +413,18 @@ void attn_kernel(AttnArgs a) {
         for (int r = 0; r < 4; ++r) cmax = fmaxf(cmax, x[kk][r]);
       cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-      const float m_new = fmaxf(m_run[ht], cmax);
+      // lazy running max: it moves only when a logit exceeds it by more than
+      // 8 (log2 domain), so exponentials stay below 2^8 and waves whose lanes
+      // all keep their max skip the rescale of o and l
+      const bool grow = cmax > m_run[ht] + 8.f;
+      const float m_new = grow ? cmax : m_run[ht];
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[ht] - m_use);
+      if (__ballot(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[ht] - m_use) : 1.f;
+        l_run[ht] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[ht][dt] *= alpha;
+      }
       m_run[ht] = m_new;
       float p[2][4];
       float psum = 0.f;
@@ -412,9 +435,7 @@ void attn_kernel(AttnArgs a) {
           p[kk][r] = __builtin_amdgcn_exp2f(x[kk][r] - m_use);
           psum += p[kk][r];
         }
-      l_run[ht] = l_run[ht] * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[ht][dt] *= alpha;
+      l_run[ht] += psum;
 
       // O^T += V^T P^T (P carries the per-entry V scale)
       if constexpr (kIO == CSA_BF16) {
@@ -425,8 +446,7 @@ void attn_kernel(AttnArgs a) {
           const int kk = h2 >> 1;
           const int r0 = (h2 & 1) * 2;
           const int key = (2 * kh + kk) * 16 + 4 * g + r0;
-          pw[h2] = uint32_t(f32_to_bf16(p[kk][r0] * s.sv[key])) |
-                   (uint32_t(f32_to_bf16(p[kk][r0 + 1] * s.sv[key + 1])) << 16);
+          pw[h2] = pack_bf16x2(p[kk][r0] * s.sv[key], p[kk][r0 + 1] * s.sv[key + 1]);
         }
         const u32x4 pb = {pw[0], pw[1], pw[2], pw[3]};
         const int k0 = kh * 32 + 4 * g;
@@ -577,34 +597,39 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict_
 // arithmetic per (query, head) is the same online softmax over 64-key chunks.
 struct LdsMQ {
   LdsBf16 c;
-  int tag[kNK];   // >= 0: compressed entry; <= -2: raw position -(tag + 2); -1: empty
+  uint32_t vis[kNK];   // bit q: the key is visible to the block's query q
 };
 
+// Gather items of chunk jc of the union list, and for each key the mask of
+// the block's queries (positions t0 + q, q < n_q) that see it: entry j is seen
+// from t >= (j+1)*m' - 1 on, raw position p by t in [p, p + W - 1].
 template <int kCKV>
-CSA_DEV void prefetch_mq(const AttnArgs& a, Pre<CSA_BF16>& pr, int (&tag)[2], int b, int raw0, int nv_max, int p_lo,
-                         int n_list, int jc) {
+CSA_DEV void prefetch_mq(const AttnArgs& a, Pre<CSA_BF16>& pr, uint32_t (&vis)[2], int b, int raw0, int nv_max,
+                         int p_lo, int n_list, int jc, int t0, int n_q) {
   const int kp = threadIdx.x & 31;
   const int dg = threadIdx.x >> 5;
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int j = jc + 2 * kp + x;
     long row = 0;
-    int src = 0, tg = -1;
+    int src = 0, q_from = n_q, q_to = -1;
     if (j < nv_max) {
       row = long(b) * a.cap + j;
       src = 1;
-      tg = j;
+      q_from = max(0, (j + 1) * a.k - 1 - t0);
+      q_to = n_q - 1;
     } else if (j < n_list) {
       const int p = p_lo + (j - nv_max);
       const int r = p - raw0;
       if (p >= 0 && r >= 0 && r < a.L_raw) {
         row = long(b) * a.L_raw + r;
         src = 2;
-        tg = -(p + 2);
+        q_from = max(0, p - t0);
+        q_to = min(n_q - 1, p + a.W - 1 - t0);
       }
     }
     pr.src[x] = src;
-    tag[x] = tg;
+    vis[x] = q_from <= q_to ? ((2u << q_to) - 1u) & ~((1u << q_from) - 1u) : 0u;
     pr.sk[x] = 1.f;
     pr.sv[x] = 1.f;
     if (src == 1) {
@@ -639,16 +664,14 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
   const int i = i0 + qi;
   const bool q_ok = i < a.T_q;
   const int pos0 = a.q_pos0[b];
-  const int t = pos0 + i;
   const int raw0 = a.W > 0 ? a.raw_pos0[b] : 0;
   const int i_last = min(i0 + kQB, a.T_q) - 1;
   const int nv_max = min((pos0 + i_last + 1) / a.k, a.cap);
   const int p_lo = pos0 + i0 - a.W + 1;
   const int n_win = a.W > 0 ? a.W + (i_last - i0) : 0;
   const int n_list = nv_max + n_win;
-  // this wave's query: visible entries and window
-  const int nv_q = min((t + 1) / a.k, a.cap);
-  const int w_lo = max(0, t - a.W + 1);
+  const int t0 = pos0 + i0;
+  const int n_q = i_last - i0 + 1;
 
   u32x4 qb[2][4];
 #pragma unroll
@@ -671,18 +694,19 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
   // two chunks in flight: chunk c is stored from one register set while
   // chunk c + 1 is still loading into the other
   Pre<CSA_BF16> pr[2];
-  int tag[2][2];
-  if (n_list > 0) prefetch_mq<kCKV>(a, pr[0], tag[0], b, raw0, nv_max, p_lo, n_list, 0);
-  if (n_list > kNK) prefetch_mq<kCKV>(a, pr[1], tag[1], b, raw0, nv_max, p_lo, n_list, kNK);
-  auto step = [&](Pre<CSA_BF16>& prc, int (&tgc)[2], int j0) {
+  uint32_t tag[2][2];
+  if (n_list > 0) prefetch_mq<kCKV>(a, pr[0], tag[0], b, raw0, nv_max, p_lo, n_list, 0, t0, n_q);
+  if (n_list > kNK) prefetch_mq<kCKV>(a, pr[1], tag[1], b, raw0, nv_max, p_lo, n_list, kNK, t0, n_q);
+  auto step = [&](Pre<CSA_BF16>& prc, uint32_t (&tgc)[2], int j0) {
     __syncthreads();
-    store_chunk<CSA_BF16, kCKV>(s.c, prc);
+    store_chunk<CSA_BF16, kCKV>(s.c, prc, a.sm_log2);
     if ((threadIdx.x >> 5) == 0) {
-      s.tag[2 * (threadIdx.x & 31)] = tgc[0];
-      s.tag[2 * (threadIdx.x & 31) + 1] = tgc[1];
+      s.vis[2 * (threadIdx.x & 31)] = tgc[0];
+      s.vis[2 * (threadIdx.x & 31) + 1] = tgc[1];
     }
     __syncthreads();
-    if (j0 + 2 * kNK < n_list) prefetch_mq<kCKV>(a, prc, tgc, b, raw0, nv_max, p_lo, n_list, j0 + 2 * kNK);
+    if (j0 + 2 * kNK < n_list)
+      prefetch_mq<kCKV>(a, prc, tgc, b, raw0, nv_max, p_lo, n_list, j0 + 2 * kNK, t0, n_q);
     // S^T for the 4 key tiles x 2 head tiles; K fragments shared by both tiles
     float x[2][4][4];
 #pragma unroll
@@ -697,9 +721,8 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int kk = kt * 16 + 4 * g + r;
-        const int tg = s.tag[kk];
-        const bool vis = q_ok && (tg >= 0 ? tg < nv_q : (tg <= -2 && -(tg + 2) >= w_lo && -(tg + 2) <= t));
-        const float scl = s.c.sk[kk] * a.sm_log2;
+        const bool vis = (s.vis[kk] >> qi) & 1u;
+        const float scl = s.c.sk[kk];
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht) x[ht][kt][r] = vis ? acc[ht][r] * scl : -INFINITY;
       }
@@ -714,9 +737,16 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
         for (int r = 0; r < 4; ++r) cmax = fmaxf(cmax, x[ht][kt][r]);
       cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-      const float m_new = fmaxf(m_run[ht], cmax);
+      // lazy running max, as in the one-query kernel
+      const bool grow = cmax > m_run[ht] + 8.f;
+      const float m_new = grow ? cmax : m_run[ht];
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[ht] - m_use);
+      if (__ballot(grow)) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[ht] - m_use) : 1.f;
+        l_run[ht] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[ht][dt] *= alpha;
+      }
       m_run[ht] = m_new;
       float psum = 0.f;
       float p[4][4];
@@ -727,9 +757,7 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
           p[kt][r] = __builtin_amdgcn_exp2f(x[ht][kt][r] - m_use);
           psum += p[kt][r];
         }
-      l_run[ht] = l_run[ht] * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[ht][dt] *= alpha;
+      l_run[ht] += psum;
       // 32-key step st covers key tiles 2st, 2st+1: contraction slot 8g+j <->
       // key (2st)*16 + 4g + j (j < 4) / (2st+1)*16 + 4g + j - 4
 #pragma unroll
@@ -739,8 +767,7 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
           const int kt = 2 * st + (h2 >> 1);
           const int r0 = (h2 & 1) * 2;
           const int key = kt * 16 + 4 * g + r0;
-          pw[ht][st][h2] = uint32_t(f32_to_bf16(p[kt][r0] * s.c.sv[key])) |
-                           (uint32_t(f32_to_bf16(p[kt][r0 + 1] * s.c.sv[key + 1])) << 16);
+          pw[ht][st][h2] = pack_bf16x2(p[kt][r0] * s.c.sv[key], p[kt][r0 + 1] * s.c.sv[key + 1]);
         }
     }
     // O^T += V^T P^T; V^T fragments shared by both tiles

@@ -19,12 +19,18 @@ constexpr int kHeadDim = 128;
 // ----------------------------------------------------------------- bf16 --
 CSA_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// Round fp32 to the nearest bf16, ties to even (finite inputs).
-CSA_DEV uint16_t f32_to_bf16(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to the nearest bf16, ties to even, packed low/high:
+// one V_CVT_PK_BF16_F32 (checked on gfx950 to round exactly like the
+// integer recipe below on normal, subnormal and tie inputs).
+CSA_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f_t{lo, hi}, v2bf_t));
 }
+
+// Round fp32 to the nearest bf16, ties to even (finite inputs).
+CSA_DEV uint16_t f32_to_bf16(float x) { return uint16_t(pack_bf16x2(x, 0.f)); }
 
 // --------------------------------------------------------- fp8 E4M3FN --
 // Decode an OCP E4M3FN code (not NaN) to fp32.  Every E4M3 value is also an

@@ -39,23 +39,42 @@ CSA_DEV v4f mfma_fp4(u32x4 a, int sa, u32x4 b, int sb, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, sa, 0, sb);
 }
 
+// ReLU as one integer max on the bit pattern: every negative float (and -0)
+// has a negative int pattern and becomes +0; non-negative floats are kept.
+CSA_DEV float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Sum of p over the lane pairs (l, l ^ 16) (kX == 16) or (l, l ^ 32)
+// (kX == 32), taken as (value of the lower lane) + (value of the upper lane)
+// on both lanes, through the CDNA4 row-swap permutes (no LDS round trip).
+template <int kX>
+CSA_DEV float pair_sum(float p) {
+  const uint32_t u = __float_as_uint(p);
+  if constexpr (kX == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+
 // Weighted ReLU sum over the heads of one query from a 16x16 score tile:
 // lane l holds rows 4*(l/16) .. +3 (heads of one query) of column l%16 in
 // acc, with their weights in wv.  The result is valid on the writer lanes:
 // for H_I = 4 every lane, for 8 the lanes with (l/16) even, for 16 lanes 0..15.
 template <int kHI>
 CSA_DEV float head_sum(v4f acc, const float (&wv)[4], int g, bool& writer) {
-  float p = wv[0] * fmaxf(acc[0], 0.f);
-  p = fmaf(wv[1], fmaxf(acc[1], 0.f), p);
-  p = fmaf(wv[2], fmaxf(acc[2], 0.f), p);
-  p = fmaf(wv[3], fmaxf(acc[3], 0.f), p);
+  float p = wv[0] * relu(acc[0]);
+  p = fmaf(wv[1], relu(acc[1]), p);
+  p = fmaf(wv[2], relu(acc[2]), p);
+  p = fmaf(wv[3], relu(acc[3]), p);
   writer = true;
   if constexpr (kHI == 8) {
-    p += __shfl_xor(p, 16);
+    p = pair_sum<16>(p);
     writer = (g & 1) == 0;
   } else if constexpr (kHI == 16) {
-    p += __shfl_xor(p, 16);
-    p += __shfl_xor(p, 32);
+    p = pair_sum<16>(p);
+    p = pair_sum<32>(p);
     writer = g == 0;
   }
   return p;
@@ -157,39 +176,85 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
   const uint8_t* kc_seq = k_codes + size_t(b) * cap * row_bytes;
   const uint8_t* ke_seq = k_e8m0 + size_t(b) * cap * nblk;
 
-  for (int e_frag0 = e_wave0; e_frag0 < e_wave1; e_frag0 += 16 * kFrag) {
-    u32x4 bk[kFrag][kKS];
-    int sb[kFrag][kKS];
+  // output row of each row tile's query (the query whose rows the lane holds)
+  bool q_in[kRT];
+  size_t orow[kRT];
 #pragma unroll
-    for (int f = 0; f < kFrag; ++f) {
-      const int e = e_frag0 + f * 16 + col;
-      load_b<kKS, kStream>(kc_seq, ke_seq, e, e < nv_max, g, nblk, row_bytes, bk[f], sb[f]);
-    }
-#pragma unroll
-    for (int f = 0; f < kFrag; ++f) {
-      const int e0 = e_frag0 + f * 16;
-      if (e0 >= e_wave1) break;
-      const int e = e0 + col;
-#pragma unroll
-      for (int rt = 0; rt < kRT; ++rt) {
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
-        if (e0 < nv_max) {
-#pragma unroll
-          for (int ks = 0; ks < kKS; ++ks) acc = mfma_fp4(a[rt][ks], sa[rt][ks], bk[f][ks], sb[f][ks], acc);
-        }
-        bool writer;
-        const float p = head_sum<kHI>(acc, wv[rt], g, writer);
-        const int q = q_block + (rt * 16 + 4 * g) / kHI;
-        if (writer && q < T_q && e < e_wave1) {
-          const size_t o = (size_t(b) * T_q + q) * cap + e;
-          if constexpr (kOut == kScoresF32) {
-            static_cast<float*>(out)[o] = e < nv_lane[rt] ? p : -INFINITY;
-          } else {
-            static_cast<uint16_t*>(out)[o] = e < nv_lane[rt] ? uint16_t(csa_sel::ordered_key(p) >> 16) : uint16_t(0);
-          }
-        }
+  for (int rt = 0; rt < kRT; ++rt) {
+    const int q = q_block + (rt * 16 + 4 * g) / kHI;
+    q_in[rt] = q < T_q;
+    orow[rt] = (size_t(b) * T_q + (q < T_q ? q : 0)) * cap;
+  }
+  auto put = [&](int rt, int e, float p) {
+    if (q_in[rt] && e < e_wave1) {
+      const bool vis = e < nv_lane[rt];
+      if constexpr (kOut == kScoresF32) {
+        static_cast<float*>(out)[orow[rt] + e] = vis ? p : -INFINITY;
+      } else {
+        static_cast<uint16_t*>(out)[orow[rt] + e] = vis ? uint16_t(csa_sel::ordered_key(p) >> 16) : uint16_t(0);
       }
     }
+  };
+
+  // key fragments of the next batch load while the current one computes
+  u32x4 bk[kFrag][kKS];
+  int sb[kFrag][kKS];
+#pragma unroll
+  for (int f = 0; f < kFrag; ++f) {
+    const int e = e_wave0 + f * 16 + col;
+    load_b<kKS, kStream>(kc_seq, ke_seq, e, e < nv_max, g, nblk, row_bytes, bk[f], sb[f]);
+  }
+  for (int e_frag0 = e_wave0; e_frag0 < e_wave1; e_frag0 += 16 * kFrag) {
+    u32x4 bn[kFrag][kKS];
+    int sn[kFrag][kKS];
+    const bool more = e_frag0 + 16 * kFrag < e_wave1;
+#pragma unroll
+    for (int f = 0; f < kFrag; ++f) {
+      const int e = e_frag0 + 16 * kFrag + f * 16 + col;
+      load_b<kKS, kStream>(kc_seq, ke_seq, e, more && e < nv_max, g, nblk, row_bytes, bn[f], sn[f]);
+    }
+    // every MFMA of the batch first, into its own accumulator; entries past
+    // every query's visibility carry zero operands and their scores are
+    // computed (and discarded) like any other
+    v4f acc[kFrag][kRT];
+#pragma unroll
+    for (int f = 0; f < kFrag; ++f)
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) {
+        acc[f][rt] = mfma_fp4(a[rt][0], sa[rt][0], bk[f][0], sb[f][0], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int ks = 1; ks < kKS; ++ks) acc[f][rt] = mfma_fp4(a[rt][ks], sa[rt][ks], bk[f][ks], sb[f][ks], acc[f][rt]);
+      }
+    if constexpr (kHI == 8 && kFrag % 2 == 0) {
+      // both lane halves of a query hold its sum after head_sum: the even one
+      // stores fragment f, the odd one fragment f + 1
+      const bool odd = (g & 1) != 0;
+#pragma unroll
+      for (int f = 0; f < kFrag; f += 2)
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) {
+          bool writer;
+          const float p0 = head_sum<kHI>(acc[f][rt], wv[rt], g, writer);
+          const float p1 = head_sum<kHI>(acc[f + 1][rt], wv[rt], g, writer);
+          put(rt, e_frag0 + (f + (odd ? 1 : 0)) * 16 + col, odd ? p1 : p0);
+        }
+    } else {
+#pragma unroll
+      for (int f = 0; f < kFrag; ++f)
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) {
+          bool writer;
+          const float p = head_sum<kHI>(acc[f][rt], wv[rt], g, writer);
+          if (writer) put(rt, e_frag0 + f * 16 + col, p);
+        }
+    }
+#pragma unroll
+    for (int f = 0; f < kFrag; ++f)
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        bk[f][ks] = bn[f][ks];
+        sb[f][ks] = sn[f][ks];
+      }
   }
 }
 
