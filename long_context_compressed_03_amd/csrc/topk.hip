@@ -19,10 +19,12 @@
 //  1. load + key transform + an LDS histogram of the top 14 key bits (sign,
 //     exponent, 5 mantissa bits: a fixed, range-free bucketing);
 //     one wave then finds the bucket holding the k-th largest key;
-//  2. the keys of that bucket (usually a few hundred) are appended to an LDS
-//     list with one atomic per wave, and an exact radix select over the list
-//     finds the k-th key and how many keys equal to it are still needed
-//     (rows whose bucket is too crowded take radix passes over all keys);
+//  2. the keys of that bucket (usually under a few hundred) are appended to
+//     an LDS list with one atomic per wave; a list of at most 1024 keys is
+//     ranked exactly, one key per thread (a longer one takes an exact radix
+//     select), to find the k-th key
+//     and how many keys equal to it are still needed (rows whose bucket is
+//     too crowded for the list take radix passes over all keys);
 //  3. emission: ballots of "greater" and "equal" give the bitmaps directly;
 //     thread w then owns 32 consecutive indices, and one block scan of the
 //     packed counts gives each selected index its slot: #greater before it +
@@ -40,6 +42,7 @@ constexpr int kWords = kSuper / 32;            // bitmap words per super-tile
 constexpr int kBucketShift = 18;               // 14-bit buckets
 constexpr int kBuckets = 1 << (32 - kBucketShift);
 constexpr int kCand = 4096;                    // capacity of the threshold-bucket list
+constexpr int kRankMax = 1024;                 // lists up to this size are ranked one entry per lane
 
 struct Shared {
   uint32_t hist[kBuckets];
@@ -155,10 +158,42 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
       }
       __syncthreads();
       const int nc = int(sh.n_cand);
-      auto each_cand = [&](auto fn) {
-        for (int x = tid; x < nc; x += kThreads) fn(sh.cand[x]);
-      };
-      refine(each_cand, prefix, mask, remaining, sh);
+      if (nc <= kRankMax) {
+        // few candidates: each lane of the first waves ranks one of them
+        // exactly against the whole list (read as broadcast 16-byte words,
+        // zero-padded: key 0 is neither greater than nor equal to a
+        // candidate); the k-th key x has #(greater) < remaining <=
+        // #(greater) + #(equal)
+        const int padded = (nc + 7) & ~7;
+        if (tid >= nc && tid < padded) sh.cand[tid] = 0u;
+        __syncthreads();
+        if (tid < nc) {
+          const uint32_t mine = sh.cand[tid];
+          uint32_t n_gt = 0u, n_eq = 0u;
+          const u32x4* c4 = reinterpret_cast<const u32x4*>(sh.cand);
+          for (int x = 0; x < padded / 4; x += 2) {
+            const u32x4 o0 = c4[x], o1 = c4[x + 1];
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+              n_gt += (o0[y] > mine ? 1u : 0u) + (o1[y] > mine ? 1u : 0u);
+              n_eq += (o0[y] == mine ? 1u : 0u) + (o1[y] == mine ? 1u : 0u);
+            }
+          }
+          if (n_gt < remaining && remaining <= n_gt + n_eq) {
+            sh.sel.bin = mine;
+            sh.sel.remaining = remaining - n_gt;
+          }
+        }
+        __syncthreads();
+        prefix = sh.sel.bin;
+        mask = 0xFFFFFFFFu;
+        remaining = sh.sel.remaining;
+      } else {
+        auto each_cand = [&](auto fn) {
+          for (int x = tid; x < nc; x += kThreads) fn(sh.cand[x]);
+        };
+        refine(each_cand, prefix, mask, remaining, sh);
+      }
     } else {
       refine(each_key, prefix, mask, remaining, sh);
     }
@@ -167,6 +202,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   // ---- pass 3: emission in index order
   uint32_t gt_off = 0u, eq_off = 0u;
   const int w = tid >> 6;
+  // bitmap words of the wave's 64 keys (indices j*4096 + c*1024 + 64w + l):
+  // a per-wave base plus (j*4096 + c*1024)/32
+  uint32_t* const gt_w = sh.bm_gt + 2 * w;
+  uint32_t* const eq_w = sh.bm_eq + 2 * w;
 #pragma unroll 1
   for (int st = 0; st < n_super; ++st) {
     if (n_super > 1) load_keys(src, nv, st, key);
@@ -178,13 +217,12 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
         const uint32_t km = key[j][c] & mask;
         const uint64_t g = __ballot(key[j][c] && km > prefix);
         const uint64_t e = __ballot(key[j][c] && km == prefix);
-        // this wave's 64 keys are indices j*4096 + c*1024 + 64w + lane: two bitmap words
-        const int word = (j * kRound + c * kThreads + 64 * w) >> 5;
+        const int word = (j * kRound + c * kThreads) >> 5;
         if (lane == 0) {
-          sh.bm_gt[word] = uint32_t(g);
-          sh.bm_gt[word + 1] = uint32_t(g >> 32);
-          sh.bm_eq[word] = uint32_t(e);
-          sh.bm_eq[word + 1] = uint32_t(e >> 32);
+          gt_w[word] = uint32_t(g);
+          gt_w[word + 1] = uint32_t(g >> 32);
+          eq_w[word] = uint32_t(e);
+          eq_w[word + 1] = uint32_t(e >> 32);
         }
       }
     __syncthreads();
