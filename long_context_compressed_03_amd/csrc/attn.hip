@@ -411,8 +411,7 @@ void attn_kernel(AttnArgs a) {
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) cmax = fmaxf(cmax, x[kk][r]);
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      cmax = column_max(cmax);
       // lazy running max: it moves only when a logit exceeds it by more than
       // 8 (log2 domain), so exponentials stay below 2^8 and waves whose lanes
       // all keep their max skip the rescale of o and l
@@ -473,8 +472,7 @@ void attn_kernel(AttnArgs a) {
   float l_tot[kHTW];
 #pragma unroll
   for (int ht = 0; ht < kHTW; ++ht) {
-    l_tot[ht] = l_run[ht] + __shfl_xor(l_run[ht], 16);
-    l_tot[ht] += __shfl_xor(l_tot[ht], 32);
+    l_tot[ht] = column_sum(l_run[ht]);
   }
   // hand the second key half to the first
   LdsHalf<kHTW>& hf = *reinterpret_cast<LdsHalf<kHTW>*>(smem);
@@ -735,8 +733,7 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) cmax = fmaxf(cmax, x[ht][kt][r]);
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+      cmax = column_max(cmax);
       // lazy running max, as in the one-query kernel
       const bool grow = cmax > m_run[ht] + 8.f;
       const float m_new = grow ? cmax : m_run[ht];
@@ -793,8 +790,7 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
   if (!q_ok) return;
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
-    float L = l_run[ht] + __shfl_xor(l_run[ht], 16);
-    L += __shfl_xor(L, 32);
+    const float L = column_sum(l_run[ht]);
     const int head = ((wid % kWPQ) * 2 + ht) * 16 + col;
     const long orow = (long(b) * a.T_q + i) * a.H + head;
     const float inv = L > 0.f ? 1.f / L : 0.f;

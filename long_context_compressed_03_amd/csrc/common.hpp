@@ -69,6 +69,30 @@ CSA_DEV uint32_t f32_to_e4m3(float x) {
 }
 
 // ------------------------------------------------------ wave reductions --
+// v combined over the lane pairs (l, l ^ 16) (kX == 16) or (l, l ^ 32)
+// (kX == 32) as op(value of the lower lane, value of the upper lane), the same
+// on both lanes, through the CDNA4 row-swap permutes (no LDS round trip).
+template <int kX, typename Op>
+CSA_DEV float swap_combine(float v, Op op) {
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (kX == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+}
+// max / sum over the four lanes l % 16 + {0, 16, 32, 48} (one MFMA C column)
+CSA_DEV float column_max(float v) {
+  auto mx = [](float x, float y) { return fmaxf(x, y); };
+  return swap_combine<32>(swap_combine<16>(v, mx), mx);
+}
+CSA_DEV float column_sum(float v) {
+  auto add = [](float x, float y) { return x + y; };
+  return swap_combine<32>(swap_combine<16>(v, add), add);
+}
+
 CSA_DEV float wave_max_xor(float v, int lane_mask) { return fmaxf(v, __shfl_xor(v, lane_mask)); }
 
 template <int kLanes>
