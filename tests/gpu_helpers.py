@@ -4,7 +4,10 @@ Tolerances (derived from the arithmetic; the attention bounds are the ones the
 project targets):
   * indexer scores, top-k indices: exact (value equality; -0 == +0);
   * attention outputs: max-abs 2e-2 with bf16 I/O and fp32 accumulation,
-    1e-5 with fp32 I/O;
+    1e-5 with fp32 I/O, each on top of half a unit in the last place of the
+    output format at |O| (the rounding of the stored output itself, which no
+    kernel can avoid: outputs of heavy-tailed inputs reach magnitudes where a
+    bf16 half-unit alone exceeds 2e-2);
   * compressed entries: the GPU pools in fp32, so its pre-rounding value x32
     differs from the exact pool x by at most eps = (m + 4) * 2^-24 * max_j |K_j|
     (m products and m additions, each within half an fp32 ulp of a partial
@@ -73,6 +76,13 @@ def compress_tolerance(x_exact, dtype, eps, scale=None):
         y = ax / s
         return s * np.exp2(np.maximum(binade(y), -6) - 3) * 1.001 + 2 * eps
     raise ValueError(dtype)
+
+
+def attention_tolerance(O_exact, io_dtype):
+    """Allowed |out_gpu - O_exact| per element (see the module docstring)."""
+    if io_dtype == "bf16":
+        return 2e-2 + np.exp2(np.maximum(binade(O_exact), -133) - 8)
+    return 1e-5 + np.exp2(np.maximum(binade(O_exact), -149) - 24)
 
 
 def exact_equal(a, b):

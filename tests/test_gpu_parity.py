@@ -13,8 +13,8 @@ import torch
 
 from csa_synth import (attn_inputs, compress_inputs, indexer_inputs, random_scores,
                        random_topk_idx)
-from gpu_helpers import (compress_tolerance, exact_equal, h, h_bf16, say, t_bf16, t_f32, t_i32,
-                         t_kv, t_u8)
+from gpu_helpers import (attention_tolerance, compress_tolerance, exact_equal, h, h_bf16, say, t_bf16,
+                         t_f32, t_i32, t_kv, t_u8)
 from oracle.attention import decode_kv, dense_attn, sparse_attn
 from oracle.compress import compress_values, store
 from oracle.formats import bf16_decode, e4m3_decode
@@ -201,10 +201,6 @@ def _oracle_kv(x, io_dt, ckv_dt):
     return q, cK, cV, decode_kv(x["Kw"], io_dt), decode_kv(x["Vw"], io_dt)
 
 
-def _tol(io_dt):
-    return 2e-2 if io_dt == "bf16" else 1e-5
-
-
 def _out_host(out, io_dt):
     return bf16_decode(h_bf16(out)) if io_dt == "bf16" else h(out).astype(np.float64)
 
@@ -243,9 +239,9 @@ def test_sparse_attn(csa, io, ckv, B, T, H, cap, k, W, L_raw, pos):
     out = csa.csa_sparse_attn(dq, ck, cv, t_i32(idx), kw, vw, t_i32(raw0), t_i32(pos), W,
                               ck_scale=cks, cv_scale=cvs, lse=lse_g)
     torch.cuda.synchronize()
-    err = np.abs(_out_host(out, io) - O).max()
-    say(f"  max-abs err {err:.3e}")
-    assert err <= _tol(io)
+    diff = np.abs(_out_host(out, io) - O)
+    say(f"  max-abs err {diff.max():.3e}")
+    assert np.all(diff <= attention_tolerance(O, io))
     fin = np.isfinite(lse)
     assert np.array_equal(np.isfinite(h(lse_g)), fin)
     assert np.abs(h(lse_g)[fin] - lse[fin]).max() <= (1e-3 if io == "bf16" else 1e-5)
@@ -283,9 +279,9 @@ def test_dense_attn(csa, io, ckv, B, T, H, mp, cap, W, L_raw, pos):
     out = csa.hca_dense_attn(dq, ck, cv, mp, kw, vw, t_i32(raw0), t_i32(pos), W,
                              ck_scale=cks, cv_scale=cvs, lse=lse_g)
     torch.cuda.synchronize()
-    err = np.abs(_out_host(out, io) - O).max()
-    say(f"  max-abs err {err:.3e}")
-    assert err <= _tol(io)
+    diff = np.abs(_out_host(out, io) - O)
+    say(f"  max-abs err {diff.max():.3e}")
+    assert np.all(diff <= attention_tolerance(O, io))
     fin = np.isfinite(lse)
     assert np.array_equal(np.isfinite(h(lse_g)), fin)
     if fin.any():
@@ -353,3 +349,36 @@ def test_runs_are_bitwise_reproducible(csa):
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
     assert torch.equal(dense[0].view(torch.int16), dense[1].view(torch.int16))
     assert torch.equal(sc[0], sc[1])
+
+
+def test_layer_pair_small(csa):
+    """A CSA layer then an HCA layer on the same query tokens (decode rows and a chunk),
+    against the oracle's layer pair."""
+    from oracle.attention import layer_pair
+    say("layer pair: CSA (m=4, top-k 48, W 32) then HCA (m'=32, W 32), fp8 caches")
+    B, T, H, W = 1, 40, 64, 32
+    pos = np.array([3000], np.int32)
+    L_raw = T + W
+    raw0 = (pos + T - L_raw).astype(np.int32)
+    m, k, cap_c = 4, 48, 760
+    mp, cap_h = 32, 96
+    xc = attn_inputs(B, T, H, cap_c, L_raw, "bf16", "fp8", seed=91, outliers=True)
+    xh = attn_inputs(B, T, H, cap_h, L_raw, "bf16", "fp8", seed=92, outliers=True)
+    nv = np.minimum(nvis(pos[:, None] + np.arange(T)[None], m), cap_c)
+    idx = random_topk_idx(nv, k, cap_c, seed=93)
+    qc, cKc, cVc, Kwc, Vwc = _oracle_kv(xc, "bf16", "fp8")
+    qh, cKh, cVh, Kwh, Vwh = _oracle_kv(xh, "bf16", "fp8")
+    (Oc, _), (Oh, _) = layer_pair(
+        dict(q=qc, cK=cKc, cV=cVc, idx=idx, Kw=Kwc, Vw=Vwc, raw_pos0=raw0, q_pos0=pos, W=W),
+        dict(q=qh, cK=cKh, cV=cVh, m_prime=mp, Kw=Kwh, Vw=Vwh, raw_pos0=raw0, q_pos0=pos, W=W))
+    dq, ck, cv, cks, cvs, kw, vw = _attn_inputs_dev(xc, "bf16", "fp8")
+    oc = csa.csa_sparse_attn(dq, ck, cv, t_i32(idx), kw, vw, t_i32(raw0), t_i32(pos), W,
+                             ck_scale=cks, cv_scale=cvs)
+    dq, ck, cv, cks, cvs, kw, vw = _attn_inputs_dev(xh, "bf16", "fp8")
+    oh = csa.hca_dense_attn(dq, ck, cv, mp, kw, vw, t_i32(raw0), t_i32(pos), W, ck_scale=cks,
+                            cv_scale=cvs)
+    torch.cuda.synchronize()
+    d1 = np.abs(_out_host(oc, "bf16") - Oc)
+    d2 = np.abs(_out_host(oh, "bf16") - Oh)
+    say(f"  CSA err {d1.max():.2e}, HCA err {d2.max():.2e} (|O| up to {np.abs(Oc).max():.1f})")
+    assert np.all(d1 <= attention_tolerance(Oc, "bf16")) and np.all(d2 <= attention_tolerance(Oh, "bf16"))
