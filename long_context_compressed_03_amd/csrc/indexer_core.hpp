@@ -266,7 +266,12 @@ hipError_t launch_indexer_ks(const uint8_t* qc, const uint8_t* qe, const float* 
   constexpr int kQPT = 16 / kHI;
   const int entries_per_wave = kStream ? 64 : 256;
   const int per_block = entries_per_wave * kWavesPerBlock;
-  dim3 grid((cap + per_block - 1) / per_block, (T_q + kRT * kQPT - 1) / (kRT * kQPT), B);
+  // Blocks are dealt to the 8 XCDs round-robin in linear order (x fastest);
+  // with the entry dimension padded to a multiple of 8, entry block x always
+  // runs on XCD x % 8, so each XCD's L2 holds a fixed eighth of the keys
+  // while the query tiles stream past it.  Padding blocks exit at once.
+  const int n_eb = ((cap + per_block - 1) / per_block + 7) / 8 * 8;
+  dim3 grid(n_eb, (T_q + kRT * kQPT - 1) / (kRT * kQPT), B);
   hipLaunchKernelGGL((indexer_kernel<kHI, kRT, kKS, kFrag, kStream, kOut>), grid, dim3(kBlock), 0, st, qc, qe, w,
                      kc, ke, pos, T_q, d_I, cap, m, entries_per_wave, out);
   return hipGetLastError();
