@@ -528,53 +528,57 @@ void attn_kernel(AttnArgs a) {
 }
 
 // Merge of the key splits of one (query, head) by one wave: lane x reads
-// split x's (max, sum) (at most 64 splits), the wave reduces them, then lane
-// (h, d4) accumulates splits h, h+2, ... of float4 d4 with the weights taken
-// from the owning lanes; the two halves are added at the end.  Fixed order.
+// split x's (max, sum) (at most 64 splits); the wave-wide max and the
+// weighted sum go through permutes and DPP rotations (no LDS round trips),
+// the per-split weights through a 64-entry LDS array.  Lane (h, d4)
+// accumulates splits h, h+2, ... of float4 d4 (their loads issued before the
+// reductions), and the two halves are added at the end.  Fixed order.
 template <int kIO>
 __global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict__ part_ml,
                                                         const float* __restrict__ part_o, int n_splits, int H,
                                                         void* out, float* lse) {
+  __shared__ float wsh[64];
   const long hid = blockIdx.x;                  // query row * H + head
   const int lane = threadIdx.x;
   const long qrow = hid / H;
   const int head = int(hid - qrow * H);
   const long base = qrow * n_splits * H + head; // slot of split 0; split x adds x*H
+  const int half = lane >> 5;
+  const int d4 = lane & 31;
+  constexpr int kU = 8;
+  auto load_batch = [&](int x0, v4f (&pv)[kU]) {
+#pragma unroll
+    for (int y = 0; y < kU; ++y) {
+      const int x = x0 + 2 * y + half;
+      pv[y] = x < n_splits ? *reinterpret_cast<const v4f*>(part_o + (base + long(x) * H) * kHeadDim + d4 * 4)
+                           : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  v4f pv[kU];
+  load_batch(0, pv);
   float mx = -INFINITY, lx = 0.f;
   if (lane < n_splits) {
     mx = part_ml[(base + long(lane) * H) * 2];
     lx = part_ml[(base + long(lane) * H) * 2 + 1];
   }
-  float M = mx;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const float M = wave_max_all(mx);
   const float Mu = M == -INFINITY ? 0.f : M;
   const float fx = lane < n_splits ? exp2f(mx - Mu) : 0.f;
-  float L = lx * fx;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
-
-  const int half = lane >> 5;
-  const int d4 = lane & 31;
+  const float L = wave_sum_all(lx * fx);
+  wsh[lane] = fx;
+  __syncthreads();
   v4f acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int kU = 8;
-  for (int x0 = half; x0 < n_splits; x0 += 2 * kU) {
-    v4f pv[kU];
+  for (int x0 = 0; x0 < n_splits; x0 += 2 * kU) {
+    if (x0 > 0) load_batch(x0, pv);
 #pragma unroll
     for (int y = 0; y < kU; ++y) {
-      const int x = x0 + 2 * y;
-      pv[y] = x < n_splits ? *reinterpret_cast<const v4f*>(part_o + (base + long(x) * H) * kHeadDim + d4 * 4)
-                           : v4f{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int y = 0; y < kU; ++y) {
-      const int x = x0 + 2 * y;
-      const float f = __shfl(fx, x < n_splits ? x : 0);
-      if (x < n_splits) acc += pv[y] * f;
+      const int x = x0 + 2 * y + half;
+      if (x < n_splits) acc += pv[y] * wsh[x];
     }
   }
+  auto add = [](float u, float w) { return u + w; };
 #pragma unroll
-  for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], 32);
+  for (int c = 0; c < 4; ++c) acc[c] = swap_combine<32>(acc[c], add);
   if (half == 0) {
     const float inv = L > 0.f ? 1.f / L : 0.f;
     store_out4<kIO>(out, hid, d4, acc * inv);

@@ -92,6 +92,28 @@ CSA_DEV float column_sum(float v) {
   auto add = [](float x, float y) { return x + y; };
   return swap_combine<32>(swap_combine<16>(v, add), add);
 }
+// v of the lane n places along its 16-lane row (DPP row rotation).
+template <int kN>
+CSA_DEV float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + kN, 0xF, 0xF, false));
+}
+// max / sum over all 64 lanes: the column combine, then rotations by 8, 4, 2, 1
+// within each row; every lane forms the same pairwise tree, so all lanes hold
+// bit-identical results.
+CSA_DEV float wave_max_all(float v) {
+  v = column_max(v);
+  v = fmaxf(v, row_ror<8>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  return fmaxf(v, row_ror<1>(v));
+}
+CSA_DEV float wave_sum_all(float v) {
+  v = column_sum(v);
+  v = v + row_ror<8>(v);
+  v = v + row_ror<4>(v);
+  v = v + row_ror<2>(v);
+  return v + row_ror<1>(v);
+}
 
 CSA_DEV float wave_max_xor(float v, int lane_mask) { return fmaxf(v, __shfl_xor(v, lane_mask)); }
 
