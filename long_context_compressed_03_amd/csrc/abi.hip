@@ -3,12 +3,13 @@
 
 size_t csa_attn_workspace_size(long rows, int H, int n_list);
 size_t csa_indexer_topk_workspace_size(long rows, int cap);
+size_t csa_topk_workspace_size(long rows, int cap);
 
 extern "C" size_t csa_workspace_size(int32_t op, int32_t B, int32_t T_q, int32_t H, int32_t d, int32_t n_keys) {
   if (B < 0 || T_q < 0 || n_keys < 0) return size_t(-1);
   switch (op) {
     case CSA_OP_TOPK:
-      return 0;
+      return csa_topk_workspace_size(long(B) * T_q, n_keys);
     case CSA_OP_INDEXER_TOPK:
       return csa_indexer_topk_workspace_size(long(B) * T_q, n_keys);
     case CSA_OP_SPARSE_ATTN:

@@ -9,7 +9,7 @@
 // One 1024-thread block per query row.  Scores become order-preserving
 // uint32 keys (negative floats bit-inverted, non-negative ones with the sign
 // bit set, -0 folded onto +0); key 0 (a NaN pattern) marks "not a candidate".
-// A row is held in registers, 32768 keys at a time: each thread holds 32
+// A row is held in registers, 16384 keys at a time: each thread holds 16
 // keys, and the element a lane loads is chosen so that every wave-wide load
 // covers 64 consecutive indices (coalesced 256-byte reads) and every wave
 // ballot of a per-key predicate IS two words of an index-ordered bitmap.
@@ -26,18 +26,38 @@
 //     and how many keys equal to it are still needed (rows whose bucket is
 //     too crowded for the list take radix passes over all keys);
 //  3. emission: ballots of "greater" and "equal" give the bitmaps directly;
-//     thread w then owns 32 consecutive indices, and one block scan of the
+//     thread w < 512 then owns 32 consecutive indices, and one block scan of the
 //     packed counts gives each selected index its slot: #greater before it +
 //     min(#equal before it, equal keys still needed).
+//
+// Few long rows (decode) would leave most of the chip idle with one block per
+// row: one CU both reads the row slowly (a lone CU draws a small share of
+// HBM bandwidth) and does every per-key step.  They take a split path of
+// three launches, exact for any input:
+//  a. per 2048-key slice s (n_s of the row's nv keys), one block finds a
+//     lower bound v_s with at least q_s = ceil(k n_s / nv) of the slice's keys
+//     >= v_s (the lower edge of the 14-bit bucket that holds the slice's
+//     q_s-th key).  The quotas sum to at least k, so the row has at least k
+//     keys >= T = min v_s;
+//  b. per slice, one block compacts the keys >= T and their indices in index
+//     order into the slice's buffer;
+//  c. per row, one block gathers the candidates (usually barely more than k)
+//     into an LDS list, one histogram pass relative to T finds the bucket of
+//     the k-th key, the keys of that bucket are ranked exactly, and the list
+//     is emitted in order.  A slice over its buffer or a row over the list
+//     (crowded ties) continues with the one-block algorithm above.
+// Each thread holds 16 keys per register tile (not 32), so that no kernel
+// here needs scratch memory: a kernel with scratch waits several
+// microseconds longer for its dispatch.
 #include "select.hpp"
 
 namespace {
 
 using namespace csa_sel;
 
-constexpr int kPer = 8;                        // rounds of 4 keys per thread
+constexpr int kPer = 4;                        // rounds of 4 keys per thread
 constexpr int kRound = kThreads * 4;           // 4096 consecutive keys per round
-constexpr int kSuper = kRound * kPer;          // 32768 keys in registers
+constexpr int kSuper = kRound * kPer;          // 16384 keys in registers
 constexpr int kWords = kSuper / 32;            // bitmap words per super-tile
 constexpr int kBucketShift = 18;               // 14-bit buckets
 constexpr int kBuckets = 1 << (32 - kBucketShift);
@@ -53,6 +73,70 @@ struct Shared {
   uint32_t n_cand;
   Sel sel;
 };
+
+// split path
+constexpr int kSlice = 2048;                   // keys per slice
+constexpr int kSliceThreads = 256;
+constexpr int kSlicePer = kSlice / kSliceThreads;
+constexpr int kSliceCap = 512;                 // candidates kept per slice
+constexpr int kWindow = 1024;                  // buckets below the slice's top bucket
+constexpr int kList = 8192;                    // candidates per row held in LDS
+constexpr int kListBuckets = 2048;
+constexpr int kSplitMaxRows = 128;
+constexpr int kSplitMinCap = 8192;
+constexpr int kMaxSlices = 1024;
+constexpr int kPreSlices = 4;                  // slices per wave whose first entries load with the counts
+constexpr int kPreEntries = 2;                 // entries per lane and slice loaded early
+
+struct ListShared {
+  uint32_t key[kList];
+  int32_t idx[kList];
+  uint32_t hist[kListBuckets];                 // also the radix passes of refine (<= 11 bits)
+  uint32_t off[kMaxSlices];
+  uint32_t cnt[kMaxSlices];
+  uint32_t wred[32];                           // per-wave min bound / max key
+  uint32_t rank[kRankMax];
+  uint32_t n_rank;
+  uint32_t smem[32];
+  Sel sel, sel2;
+};
+
+union RowShared {
+  Shared full;
+  ListShared list;
+};
+
+int n_slices(int cap) { return (cap + kSlice - 1) / kSlice; }
+bool use_split(long rows, int cap) {
+  return rows <= kSplitMaxRows && cap >= kSplitMinCap && n_slices(cap) <= kMaxSlices;
+}
+
+// Workspace of the split path: bounds [rows][G], counts [rows][G], candidate
+// keys and indices [rows][G][kSliceCap].
+struct SplitWs {
+  uint32_t* bound;
+  uint32_t* count;
+  uint32_t* key;
+  int32_t* idx;
+};
+size_t split_ws_bytes(long rows, int cap) {
+  return size_t(rows) * n_slices(cap) * (2 * sizeof(uint32_t) + kSliceCap * (sizeof(uint32_t) + sizeof(int32_t)));
+}
+SplitWs split_ws(void* ws, long rows, int cap) {
+  const size_t n = size_t(rows) * n_slices(cap);
+  SplitWs w;
+  w.bound = static_cast<uint32_t*>(ws);
+  w.count = w.bound + n;
+  w.key = w.count + n;
+  w.idx = reinterpret_cast<int32_t*>(w.key + n * kSliceCap);
+  return w;
+}
+
+CSA_DEV int visible_entries(const int32_t* q_pos0, int T_q, int row, int cap, int m) {
+  const int b = row / T_q;
+  const int t = q_pos0[b] + (row - b * T_q);
+  return max(0, min((t + 1) / m, cap));
+}
 
 // Index of key (j, c) of this thread within its super-tile.
 CSA_DEV int key_index(int j, int c) { return j * kRound + c * kThreads + threadIdx.x; }
@@ -74,11 +158,315 @@ CSA_DEV void load_keys(const float* __restrict__ src, int nv, int st, uint32_t (
     for (int c = 0; c < 4; ++c) key[j][c] = base + key_index(j, c) < nv ? ordered_key(v[j][c]) : 0u;
 }
 
+// Keys of slice s: thread t holds indices base + j*256 + t (coalesced, and a
+// wave ballot over key j covers 64 consecutive indices).
+CSA_DEV void load_slice(const float* __restrict__ src, int base, int n_s, uint32_t (&key)[kSlicePer]) {
+  float v[kSlicePer];
+#pragma unroll
+  for (int j = 0; j < kSlicePer; ++j) {
+    const int x = j * kSliceThreads + int(threadIdx.x);
+    v[j] = x < n_s ? src[base + x] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < kSlicePer; ++j)
+    key[j] = j * kSliceThreads + int(threadIdx.x) < n_s ? ordered_key(v[j]) : 0u;
+}
+
+// Pass a: bound[row][s] = v_s (0xFFFFFFFF for an empty slice, 1 = every key
+// when the window below the slice's top bucket holds fewer than q_s keys).
+__global__ __launch_bounds__(kSliceThreads) void slice_bound_kernel(const float* __restrict__ scores,
+                                                                    const int32_t* __restrict__ q_pos0, int T_q,
+                                                                    int cap, int m, int k, int G,
+                                                                    uint32_t* __restrict__ bound) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kWindow];
+  __shared__ uint32_t smem[32];
+  const int row = blockIdx.y, sl = blockIdx.x, tid = threadIdx.x;
+  const int nv = visible_entries(q_pos0, T_q, row, cap, m);
+  if (nv <= k) return;
+  const int base = sl * kSlice;
+  const int n_s = min(kSlice, nv - base);
+  uint32_t* out = bound + size_t(row) * G + sl;
+  if (n_s <= 0) {
+    if (tid == 0) *out = 0xFFFFFFFFu;
+    return;
+  }
+  const uint32_t quota = uint32_t((uint64_t(k) * uint32_t(n_s) + uint32_t(nv) - 1u) / uint32_t(nv));
+  uint32_t key[kSlicePer];
+  load_slice(scores + size_t(row) * cap, base, n_s, key);
+  reinterpret_cast<u32x4*>(hist)[tid] = u32x4{0u, 0u, 0u, 0u};
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int j = 0; j < kSlicePer; ++j) mx = max(mx, key[j]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, uint32_t(__shfl_xor(int(mx), o)));
+  if ((tid & 63) == 0) smem[tid >> 6] = mx;
+  __syncthreads();
+  mx = max(max(smem[0], smem[1]), max(smem[2], smem[3]));
+  const int top = int(mx >> kBucketShift);
+#pragma unroll
+  for (int j = 0; j < kSlicePer; ++j) {
+    const int rel = top - int(key[j] >> kBucketShift);
+    if (key[j] && rel < kWindow) atomicAdd(&hist[rel], 1u);
+  }
+  __syncthreads();
+  const u32x4 c = reinterpret_cast<const u32x4*>(hist)[tid];   // buckets top-4t .. top-4t-3
+  const uint32_t sum = c[0] + c[1] + c[2] + c[3];
+  uint32_t tot;
+  const uint32_t excl = block_exclusive_scan(sum, smem + 8, &tot);
+  if (tot < quota) {
+    if (tid == 0) *out = 1u;
+  } else if (excl < quota && quota <= excl + sum) {
+    uint32_t run = excl;
+    int r = 4 * tid;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      run += c[y];
+      if (run >= quota) { r = 4 * tid + y; break; }
+    }
+    *out = uint32_t(top - r) << kBucketShift;
+  }
+}
+
+// Pass b: the slice's keys >= min over the row's bounds, with their indices,
+// in index order (at most kSliceCap stored; count[row][s] is the full count).
+__global__ __launch_bounds__(kSliceThreads) void slice_compact_kernel(const float* __restrict__ scores,
+                                                                      const int32_t* __restrict__ q_pos0, int T_q,
+                                                                      int cap, int m, int k, int G, SplitWs ws) {
+  __shared__ uint32_t wc[kSlicePer * 4];
+  const int row = blockIdx.y, sl = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int nv = visible_entries(q_pos0, T_q, row, cap, m);
+  if (nv <= k) return;
+  const int base = sl * kSlice;
+  const int n_s = min(kSlice, nv - base);
+  const size_t slot = size_t(row) * G + sl;
+  if (n_s <= 0) {
+    if (tid == 0) ws.count[slot] = 0u;
+    return;
+  }
+  uint32_t lo = 0xFFFFFFFFu;
+  for (int x = lane; x < G; x += 64) lo = min(lo, ws.bound[size_t(row) * G + x]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lo = min(lo, uint32_t(__shfl_xor(int(lo), o)));
+  uint32_t key[kSlicePer];
+  load_slice(scores + size_t(row) * cap, base, n_s, key);
+  uint64_t bal[kSlicePer];
+#pragma unroll
+  for (int j = 0; j < kSlicePer; ++j) {
+    bal[j] = __ballot(key[j] != 0u && key[j] >= lo);
+    if (lane == 0) wc[j * 4 + w] = uint32_t(__popcll(bal[j]));
+  }
+  __syncthreads();
+  // exclusive offsets of the 32 (key j, wave) groups in index order
+  const uint32_t c = lane < kSlicePer * 4 ? wc[lane] : 0u;
+  uint32_t incl = c;
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) {
+    const uint32_t t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  const uint32_t excl = incl - c;
+  const uint64_t below = (uint64_t(1) << lane) - 1u;
+  uint32_t* const ck = ws.key + slot * kSliceCap;
+  int32_t* const ci = ws.idx + slot * kSliceCap;
+#pragma unroll
+  for (int j = 0; j < kSlicePer; ++j) {
+    const uint32_t pos = uint32_t(__shfl(int(excl), j * 4 + w)) + uint32_t(__popcll(bal[j] & below));
+    if (((bal[j] >> lane) & 1u) && pos < uint32_t(kSliceCap)) {
+      ck[pos] = key[j];
+      ci[pos] = base + j * kSliceThreads + tid;
+    }
+  }
+  const uint32_t total = uint32_t(__shfl(int(incl), kSlicePer * 4 - 1));   // all lanes take part
+  if (tid == 0) ws.count[slot] = total;
+}
+
+// Pass c, gathering: the row's candidates into the LDS list in index order.
+// The counts, the bounds and the first entries of each wave's first slices
+// are loaded together (entries past a slice's count are read but unused).
+// Returns the list size, or -1 (block-uniform) when the candidates do not
+// fit; lo = min bound, top = max candidate key.
+CSA_DEV int gather_list(const SplitWs& ws, int row, int G, int k, ListShared& sh, uint32_t& lo, uint32_t& top) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int kWaves = kThreads / 64;
+  const size_t rbase = size_t(row) * G;
+  const uint32_t c = tid < G ? ws.count[rbase + tid] : 0u;
+  uint32_t b = tid < G ? ws.bound[rbase + tid] : 0xFFFFFFFFu;
+  uint32_t pk[kPreSlices][kPreEntries];
+  int32_t pi[kPreSlices][kPreEntries];
+#pragma unroll
+  for (int q = 0; q < kPreSlices; ++q)
+#pragma unroll
+    for (int e = 0; e < kPreEntries; ++e) {
+      const int sl = w + kWaves * q;
+      const size_t at = (rbase + (sl < G ? sl : 0)) * kSliceCap + lane + 64 * e;
+      pk[q][e] = sl < G ? ws.key[at] : 0u;
+      pi[q][e] = sl < G ? ws.idx[at] : 0;
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) b = min(b, uint32_t(__shfl_xor(int(b), o)));
+  if (lane == 0) sh.wred[w] = b;
+  if (tid < G) sh.cnt[tid] = c;
+  uint32_t total;
+  const uint32_t excl = block_exclusive_scan(c, sh.smem, &total);   // its barriers publish wred, cnt
+  if (tid < G) sh.off[tid] = excl;
+  lo = sh.wred[0];
+#pragma unroll
+  for (int x = 1; x < kWaves; ++x) lo = min(lo, sh.wred[x]);
+  const bool over = __syncthreads_or(c > uint32_t(kSliceCap));
+  if (over || total > uint32_t(kList) || total < uint32_t(k)) return -1;
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int q = 0; q < kPreSlices; ++q) {
+    const int sl = w + kWaves * q;
+    if (sl < G) {
+      const uint32_t o = sh.off[sl], n = sh.cnt[sl];
+#pragma unroll
+      for (int e = 0; e < kPreEntries; ++e) {
+        const uint32_t x = uint32_t(lane + 64 * e);
+        if (x < n) {
+          sh.key[o + x] = pk[q][e];
+          sh.idx[o + x] = pi[q][e];
+          mx = max(mx, pk[q][e]);
+        }
+      }
+    }
+  }
+  // the rest: entries past the early ones, and the slices beyond them
+  for (int sl = w; sl < G; sl += kWaves) {
+    const uint32_t o = sh.off[sl], n = sh.cnt[sl];
+    const uint32_t x0 = sl < w + kWaves * kPreSlices ? uint32_t(64 * kPreEntries) : 0u;
+    for (uint32_t x = x0 + lane; x < n; x += 64) {
+      const uint32_t kk = ws.key[(rbase + sl) * kSliceCap + x];
+      sh.key[o + x] = kk;
+      sh.idx[o + x] = ws.idx[(rbase + sl) * kSliceCap + x];
+      mx = max(mx, kk);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, uint32_t(__shfl_xor(int(mx), o)));
+  if (lane == 0) sh.wred[16 + w] = mx;
+  __syncthreads();
+  top = sh.wred[16];
+#pragma unroll
+  for (int x = 1; x < kWaves; ++x) top = max(top, sh.wred[16 + x]);
+  return int(total);
+}
+
+// Pass c, selection: the k largest of the nc list keys (all >= lo, at most
+// top; nc >= k), written to out in list order (= index order).  One
+// histogram pass over [lo, top] in at most 2048 buckets; one wave finds the
+// bucket of the k-th largest; that bucket's keys are ranked exactly (a
+// crowded bucket takes the exact radix refinement over the list instead).
+CSA_DEV void list_select_emit(int nc, uint32_t lo, uint32_t top, int k, int32_t* __restrict__ out, ListShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int j = tid; j < kListBuckets; j += kThreads) sh.hist[j] = 0u;
+  if (tid == 0) sh.n_rank = 0u;
+  __syncthreads();
+  const uint32_t range = top - lo;
+  const int bits = range == 0u ? 0 : 32 - __clz(range);
+  const int shift = bits > 11 ? bits - 11 : 0;
+  for (int x = tid; x < nc; x += kThreads) atomicAdd(&sh.hist[(sh.key[x] - lo) >> shift], 1u);
+  __syncthreads();
+  if (w == 0) {
+    // lane l holds the 32 buckets below hi = 2047 - 32 l, in registers
+    const int hi = kListBuckets - 1 - 32 * lane;
+    const u32x4* h4 = reinterpret_cast<const u32x4*>(sh.hist + hi - 31);
+    u32x4 hv[8];
+    uint32_t sum = 0u;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      hv[q] = h4[q];
+      sum += hv[q][0] + hv[q][1] + hv[q][2] + hv[q][3];
+    }
+    uint32_t incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    const uint32_t excl = incl - sum;
+    if (excl < uint32_t(k) && uint32_t(k) <= incl) {
+      uint32_t run = excl;
+      bool found = false;
+#pragma unroll
+      for (int y = 31; y >= 0; --y) {          // bucket hi - 31 + y, from the top down
+        const uint32_t cy = hv[y >> 2][y & 3];
+        if (!found && run + cy >= uint32_t(k)) {
+          sh.sel.bin = uint32_t(hi - 31 + y);
+          sh.sel.remaining = uint32_t(k) - run;
+          sh.sel.bincount = cy;
+          found = true;
+        }
+        run += cy;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t B = sh.sel.bin, r = sh.sel.remaining, cB = sh.sel.bincount;
+  uint32_t prefix, mask = 0xFFFFFFFFu, remaining;
+  if (cB <= uint32_t(kRankMax)) {
+    for (int x = tid; x < nc; x += kThreads) {
+      const uint32_t kk = sh.key[x];
+      if (((kk - lo) >> shift) == B) sh.rank[atomicAdd(&sh.n_rank, 1u)] = kk;
+    }
+    __syncthreads();
+    if (uint32_t(tid) < cB) {
+      const uint32_t mine = sh.rank[tid];
+      uint32_t n_gt = 0u, n_eq = 0u;
+      for (uint32_t y = 0; y < cB; ++y) {
+        const uint32_t o = sh.rank[y];
+        n_gt += o > mine ? 1u : 0u;
+        n_eq += o == mine ? 1u : 0u;
+      }
+      if (n_gt < r && r <= n_gt + n_eq) {   // equal keys write equal values
+        sh.sel2.bin = mine;
+        sh.sel2.remaining = r - n_gt;
+      }
+    }
+    __syncthreads();
+    prefix = sh.sel2.bin;
+    remaining = sh.sel2.remaining;
+  } else {
+    prefix = 0u;
+    mask = 0u;
+    remaining = uint32_t(k);
+    auto each_cand = [&](auto fn) {
+      for (int x = tid; x < nc; x += kThreads) fn(sh.key[x]);
+    };
+    refine(each_cand, prefix, mask, remaining, sh);
+  }
+  // emission: thread t walks list entries [t*per, t*per + per) in index order
+  const int per = (nc + kThreads - 1) / kThreads;
+  const int x0 = tid * per, x1 = min(nc, x0 + per);
+  uint32_t n_gt = 0u, n_eq = 0u;
+  for (int x = x0; x < x1; ++x) {
+    const uint32_t km = sh.key[x] & mask;
+    n_gt += km > prefix ? 1u : 0u;
+    n_eq += km == prefix ? 1u : 0u;
+  }
+  uint32_t tot;
+  const uint32_t ex = block_exclusive_scan((n_eq << 16) | n_gt, sh.smem, &tot);
+  uint32_t gt_before = ex & 0xFFFFu, eq_before = ex >> 16;
+  for (int x = x0; x < x1; ++x) {
+    const uint32_t km = sh.key[x] & mask;
+    if (km > prefix) {
+      out[gt_before + min(eq_before, remaining)] = sh.idx[x];
+      ++gt_before;
+    } else if (km == prefix) {
+      if (eq_before < remaining) out[gt_before + eq_before] = sh.idx[x];
+      ++eq_before;
+    }
+  }
+}
+
+template <bool kSplit>
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores,
                                                         const int32_t* __restrict__ q_pos0, int T_q, int cap, int m,
-                                                        int k, int32_t* __restrict__ idx) {
+                                                        int k, int32_t* __restrict__ idx, SplitWs ws, int G) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  Shared& sh = *reinterpret_cast<Shared*>(smem_raw);
+  RowShared& rs = *reinterpret_cast<RowShared*>(smem_raw);
+  Shared& sh = rs.full;
 
   const int row = blockIdx.x;
   const int b = row / T_q;
@@ -94,6 +482,15 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     return;
   }
   const float* src = scores + size_t(row) * cap;
+  if constexpr (kSplit) {
+    uint32_t lo, top;
+    const int nc = gather_list(ws, row, G, k, rs.list, lo, top);
+    if (nc >= 0) {
+      list_select_emit(nc, lo, top, k, out, rs.list);
+      return;
+    }
+    __syncthreads();
+  }
   const int n_super = (nv + kSuper - 1) / kSuper;
   const uint64_t lanes_below = (uint64_t(1) << lane) - 1u;
 
@@ -226,8 +623,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
         }
       }
     __syncthreads();
-    const uint32_t wg = sh.bm_gt[tid];
-    const uint32_t we = sh.bm_eq[tid];
+    const uint32_t wg = tid < kWords ? sh.bm_gt[tid] : 0u;   // thread t owns word t (32 indices)
+    const uint32_t we = tid < kWords ? sh.bm_eq[tid] : 0u;
     uint32_t tot;
     const uint32_t ex = block_exclusive_scan((uint32_t(__popc(we)) << 16) | uint32_t(__popc(wg)), sh.smem, &tot);
     uint32_t gt_before = gt_off + (ex & 0xFFFFu);
@@ -250,17 +647,34 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   }
 }
 
+template <bool kSplit>
+hipError_t set_lds_limit() {
+  static bool done = false;   // more than 64 KB of LDS needs the opt-in
+  if (done) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_kernel<kSplit>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(RowShared)));
+  done = e == hipSuccess;
+  return e;
+}
+
 hipError_t launch_topk(long rows, hipStream_t st, const float* scores, const int32_t* q_pos0, int T_q, int cap, int m,
-                       int k, int32_t* idx) {
-  static bool attr = false;   // more than 64 KB of LDS needs the opt-in
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(Shared)));
+                       int k, int32_t* idx, void* ws) {
+  if (!use_split(rows, cap)) {
+    hipError_t e = set_lds_limit<false>();
     if (e != hipSuccess) return e;
-    attr = true;
+    hipLaunchKernelGGL(topk_kernel<false>, dim3(unsigned(rows)), dim3(kThreads), sizeof(RowShared), st, scores, q_pos0,
+                       T_q, cap, m, k, idx, SplitWs{}, 0);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL(topk_kernel, dim3(unsigned(rows)), dim3(kThreads), sizeof(Shared), st, scores, q_pos0, T_q, cap,
-                     m, k, idx);
+  hipError_t e = set_lds_limit<true>();
+  if (e != hipSuccess) return e;
+  const int G = n_slices(cap);
+  const SplitWs w = split_ws(ws, rows, cap);
+  const dim3 grid{unsigned(G), unsigned(rows), 1u};
+  hipLaunchKernelGGL(slice_bound_kernel, grid, dim3(kSliceThreads), 0, st, scores, q_pos0, T_q, cap, m, k, G, w.bound);
+  hipLaunchKernelGGL(slice_compact_kernel, grid, dim3(kSliceThreads), 0, st, scores, q_pos0, T_q, cap, m, k, G, w);
+  hipLaunchKernelGGL(topk_kernel<true>, dim3(unsigned(rows)), dim3(kThreads), sizeof(RowShared), st, scores, q_pos0,
+                     T_q, cap, m, k, idx, w, G);
   return hipGetLastError();
 }
 
@@ -268,13 +682,14 @@ hipError_t launch_topk(long rows, hipStream_t st, const float* scores, const int
 
 extern "C" csa_status_t csa_topk(const float* scores, const int32_t* q_pos0, int32_t B, int32_t T_q, int32_t cap,
                                  int32_t m, int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (!scores || !q_pos0 || !idx) return CSA_EINVAL;
   if (B < 0 || T_q < 0 || cap < 0 || m < 1 || k < 1) return CSA_EINVAL;
   const long rows = long(B) * T_q;
   if (rows == 0) return CSA_OK;
   if (rows > 0x7FFFFFFFL) return CSA_ENOTSUP;
-  const hipError_t e = launch_topk(rows, static_cast<hipStream_t>(stream), scores, q_pos0, T_q, cap, m, k, idx);
+  if (use_split(rows, cap) && (!ws || ws_bytes < split_ws_bytes(rows, cap))) return CSA_EWORKSPACE;
+  const hipError_t e = launch_topk(rows, static_cast<hipStream_t>(stream), scores, q_pos0, T_q, cap, m, k, idx, ws);
   return e == hipSuccess ? CSA_OK : CSA_EHIP;
 }
+
+size_t csa_topk_workspace_size(long rows, int cap) { return use_split(rows, cap) ? split_ws_bytes(rows, cap) : 0; }

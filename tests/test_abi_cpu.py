@@ -108,6 +108,13 @@ def test_topk_and_attention_reject_bad_arguments():
     lib = csa.load()
     assert lib.csa_topk(_p(), _p(), 1, 1, 10, 4, 0, _p(), None, 0, None) == csa.CSA_EINVAL
     assert lib.csa_topk(None, _p(), 1, 1, 10, 4, 3, _p(), None, 0, None) == csa.CSA_EINVAL
+    # few long rows are split over many blocks: that path needs the workspace
+    need = lib.csa_workspace_size(csa.CSA_OP_TOPK, 16, 1, 0, 128, 32768)
+    assert need > 0
+    assert lib.csa_topk(_p(), _p(), 16, 1, 32768, 4, 1024, _p(), None, 0, None) == csa.CSA_EWORKSPACE
+    assert lib.csa_topk(_p(), _p(), 16, 1, 32768, 4, 1024, _p(), _p(), need - 1, None) == csa.CSA_EWORKSPACE
+    assert lib.csa_workspace_size(csa.CSA_OP_TOPK, 200, 1, 0, 128, 32768) == 0   # many rows: one block each
+    assert lib.csa_workspace_size(csa.CSA_OP_TOPK, 1, 1, 0, 128, 5000) == 0      # short rows
 
     def sparse(H=64, d=128, k=1024, W=128, io=0, ckv=0, idx=_p(), ck_scale=None, ws=None, nws=0,
                B=1, T=1):

@@ -168,11 +168,33 @@ def test_topk_on_indexer_scores(csa):
     (2, 1, 4999, 100, [19995, 100], 50),          # unaligned rows; one row below k
     (1, 2, 20000, 1000, [79999], 3),              # crowded threshold bin: exact radix passes
     (3, 1, 32768, 1024, [131071] * 3, 1 << 16),   # the 128K decode shape, several rows
+    (1, 160, 9000, 300, [34000], 1 << 20),        # many rows: one block per row
+    (2, 1, 30001, 1024, [120003, 60001], 1 << 20),  # split rows with partial last slices
+    (4, 1, 262144, 1024, [1048575] * 4, 1 << 20), # the 1M decode row shape
+    (1, 1, 40000, 9000, [159999], 1 << 20),       # more candidates than the split list holds
 ])
 def test_topk_random(csa, B, T, cap, k, pos, distinct):
     say(f"topk B={B} T={T} cap={cap} k={k}")
     s = random_scores(B, T, cap, seed=cap, distinct=distinct)
     _topk_case(csa, s, np.array(pos, np.int32), 4, k)
+
+
+@pytest.mark.parametrize("order", ["ascending", "descending"])
+def test_topk_sorted_rows(csa, order):
+    # all of the top keys in one end of the row: far more candidates than the
+    # split path's per-slice buffers hold
+    s = np.arange(32768, dtype=np.float32)[None, None, :] / 7.0
+    if order == "descending":
+        s = s[:, :, ::-1].copy()
+    _topk_case(csa, np.ascontiguousarray(s), np.array([131071], np.int32), 4, 1024)
+
+
+def test_topk_wide_range_rows(csa):
+    # scores spanning far more octaves than one slice's bucket window
+    s = random_scores(2, 1, 32768, seed=17, distinct=1 << 20)
+    s[0, 0, ::997] = 1e30
+    s[1, 0, ::2] *= 1e-30
+    _topk_case(csa, s, np.array([131071, 131071], np.int32), 4, 1024)
 
 
 def test_topk_constant_rows(csa):
