@@ -811,12 +811,13 @@ struct Plan {
 };
 
 // The work split depends only on (rows, n_list): never on data or timing.
-// Enough blocks to give every CU about two; a split is a whole number of
-// 64-key chunks.
+// At most about one block per CU: past 256 blocks some CUs run two, whose
+// tail then sets the kernel time, and the partials to write back and merge
+// grow with the split count.  A split is a whole number of 64-key chunks.
 Plan make_plan(long rows, int n_list) {
   Plan p{};
   const long chunks = (max(n_list, 1) + kNK - 1) / kNK;
-  long want = (512 + rows - 1) / rows;
+  long want = (256 + rows - 1) / rows;
   if (want > chunks) want = chunks;
   if (want > kMaxSplits) want = kMaxSplits;
   if (want < 1) want = 1;
