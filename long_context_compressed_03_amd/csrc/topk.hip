@@ -32,20 +32,21 @@
 //
 // Few long rows (decode) would leave most of the chip idle with one block per
 // row: one CU both reads the row slowly (a lone CU draws a small share of
-// HBM bandwidth) and does every per-key step.  They take a split path of
-// three launches, exact for any input:
+// HBM bandwidth) and does every per-key step.  They take a split path of two
+// launches, exact for any input:
 //  a. per 2048-key slice s (n_s of the row's nv keys), one block finds a
-//     lower bound v_s with at least q_s = ceil(k n_s / nv) of the slice's keys
-//     >= v_s (the lower edge of the 14-bit bucket that holds the slice's
-//     q_s-th key).  The quotas sum to at least k, so the row has at least k
-//     keys >= T = min v_s;
-//  b. per slice, one block compacts the keys >= T and their indices in index
-//     order into the slice's buffer;
-//  c. per row, one block gathers the candidates (usually barely more than k)
-//     into an LDS list, one histogram pass relative to T finds the bucket of
-//     the k-th key, the keys of that bucket are ranked exactly, and the list
-//     is emitted in order.  A slice over its buffer or a row over the list
-//     (crowded ties) continues with the one-block algorithm above.
+//     local bound v_s: the lower edge of the 14-bit bucket that holds the
+//     slice's c_s-th largest key, c_s = min(n_s, 3 q_s) with the slice's
+//     share q_s = ceil(k n_s / nv); it stores every key >= v_s, with its
+//     index, in index order.  The shares sum to at least k, so the candidate
+//     set C holds at least k keys;
+//  b. per row, one block gathers C into an LDS list; one histogram pass finds
+//     the bucket of the k-th largest, whose keys are ranked exactly; the list
+//     is emitted in order.  C holds every key of the row >= max v_s, so when
+//     the selected keys are all >= max v_s the result is the row's (which
+//     fails only if one slice holds about three times its share of the top k,
+//     or the ties crowd a slice buffer or the list); otherwise the row
+//     continues with the one-block algorithm above.
 // Each thread holds 16 keys per register tile (not 32), so that no kernel
 // here needs scratch memory: a kernel with scratch waits several
 // microseconds longer for its dispatch.
@@ -80,6 +81,7 @@ constexpr int kSliceThreads = 256;
 constexpr int kSlicePer = kSlice / kSliceThreads;
 constexpr int kSliceCap = 512;                 // candidates kept per slice
 constexpr int kWindow = 1024;                  // buckets below the slice's top bucket
+constexpr uint32_t kLocal = 3;                 // a slice keeps about kLocal times its share of k
 constexpr int kList = 8192;                    // candidates per row held in LDS
 constexpr int kListBuckets = 2048;
 constexpr int kSplitMaxRows = 128;
@@ -94,7 +96,7 @@ struct ListShared {
   uint32_t hist[kListBuckets];                 // also the radix passes of refine (<= 11 bits)
   uint32_t off[kMaxSlices];
   uint32_t cnt[kMaxSlices];
-  uint32_t wred[32];                           // per-wave min bound / max key
+  uint32_t wred[48];                           // per-wave min bound, max bound, max key
   uint32_t rank[kRankMax];
   uint32_t n_rank;
   uint32_t smem[32];
@@ -172,25 +174,36 @@ CSA_DEV void load_slice(const float* __restrict__ src, int base, int n_s, uint32
     key[j] = j * kSliceThreads + int(threadIdx.x) < n_s ? ordered_key(v[j]) : 0u;
 }
 
-// Pass a: bound[row][s] = v_s (0xFFFFFFFF for an empty slice, 1 = every key
-// when the window below the slice's top bucket holds fewer than q_s keys).
-__global__ __launch_bounds__(kSliceThreads) void slice_bound_kernel(const float* __restrict__ scores,
-                                                                    const int32_t* __restrict__ q_pos0, int T_q,
-                                                                    int cap, int m, int k, int G,
-                                                                    uint32_t* __restrict__ bound) {
+// Pass a, one block per slice: v_s = the lower edge of the 14-bit bucket
+// that holds the slice's c_s-th largest key, c_s = min(n_s, kLocal * q_s)
+// with q_s = ceil(k n_s / nv) (1 = every key when the window below the top
+// bucket holds fewer than c_s keys); then the slice's keys >= v_s and their
+// indices, in index order, into its buffer (at most kSliceCap stored;
+// count[row][s] is the full count, bound[row][s] = v_s; an empty slice
+// stores count 0 and bound 0).
+__global__ __launch_bounds__(kSliceThreads) void slice_select_kernel(const float* __restrict__ scores,
+                                                                     const int32_t* __restrict__ q_pos0, int T_q,
+                                                                     int cap, int m, int k, int G, SplitWs ws) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[kWindow];
   __shared__ uint32_t smem[32];
+  __shared__ uint32_t wc[kSlicePer * 4];
+  __shared__ uint32_t v_sh;
   const int row = blockIdx.y, sl = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
   const int nv = visible_entries(q_pos0, T_q, row, cap, m);
   if (nv <= k) return;
   const int base = sl * kSlice;
   const int n_s = min(kSlice, nv - base);
-  uint32_t* out = bound + size_t(row) * G + sl;
+  const size_t slot = size_t(row) * G + sl;
   if (n_s <= 0) {
-    if (tid == 0) *out = 0xFFFFFFFFu;
+    if (tid == 0) {
+      ws.count[slot] = 0u;
+      ws.bound[slot] = 0u;
+    }
     return;
   }
   const uint32_t quota = uint32_t((uint64_t(k) * uint32_t(n_s) + uint32_t(nv) - 1u) / uint32_t(nv));
+  const uint32_t want = min(uint32_t(n_s), kLocal * quota);
   uint32_t key[kSlicePer];
   load_slice(scores + size_t(row) * cap, base, n_s, key);
   reinterpret_cast<u32x4*>(hist)[tid] = u32x4{0u, 0u, 0u, 0u};
@@ -199,7 +212,7 @@ __global__ __launch_bounds__(kSliceThreads) void slice_bound_kernel(const float*
   for (int j = 0; j < kSlicePer; ++j) mx = max(mx, key[j]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = max(mx, uint32_t(__shfl_xor(int(mx), o)));
-  if ((tid & 63) == 0) smem[tid >> 6] = mx;
+  if (lane == 0) smem[w] = mx;
   __syncthreads();
   mx = max(max(smem[0], smem[1]), max(smem[2], smem[3]));
   const int top = int(mx >> kBucketShift);
@@ -213,43 +226,20 @@ __global__ __launch_bounds__(kSliceThreads) void slice_bound_kernel(const float*
   const uint32_t sum = c[0] + c[1] + c[2] + c[3];
   uint32_t tot;
   const uint32_t excl = block_exclusive_scan(sum, smem + 8, &tot);
-  if (tot < quota) {
-    if (tid == 0) *out = 1u;
-  } else if (excl < quota && quota <= excl + sum) {
+  if (tot < want) {
+    if (tid == 0) v_sh = 1u;
+  } else if (excl < want && want <= excl + sum) {
     uint32_t run = excl;
     int r = 4 * tid;
 #pragma unroll
     for (int y = 0; y < 4; ++y) {
       run += c[y];
-      if (run >= quota) { r = 4 * tid + y; break; }
+      if (run >= want) { r = 4 * tid + y; break; }
     }
-    *out = uint32_t(top - r) << kBucketShift;
+    v_sh = uint32_t(top - r) << kBucketShift;
   }
-}
-
-// Pass b: the slice's keys >= min over the row's bounds, with their indices,
-// in index order (at most kSliceCap stored; count[row][s] is the full count).
-__global__ __launch_bounds__(kSliceThreads) void slice_compact_kernel(const float* __restrict__ scores,
-                                                                      const int32_t* __restrict__ q_pos0, int T_q,
-                                                                      int cap, int m, int k, int G, SplitWs ws) {
-  __shared__ uint32_t wc[kSlicePer * 4];
-  const int row = blockIdx.y, sl = blockIdx.x, tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
-  const int nv = visible_entries(q_pos0, T_q, row, cap, m);
-  if (nv <= k) return;
-  const int base = sl * kSlice;
-  const int n_s = min(kSlice, nv - base);
-  const size_t slot = size_t(row) * G + sl;
-  if (n_s <= 0) {
-    if (tid == 0) ws.count[slot] = 0u;
-    return;
-  }
-  uint32_t lo = 0xFFFFFFFFu;
-  for (int x = lane; x < G; x += 64) lo = min(lo, ws.bound[size_t(row) * G + x]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) lo = min(lo, uint32_t(__shfl_xor(int(lo), o)));
-  uint32_t key[kSlicePer];
-  load_slice(scores + size_t(row) * cap, base, n_s, key);
+  __syncthreads();
+  const uint32_t lo = v_sh;
   uint64_t bal[kSlicePer];
 #pragma unroll
   for (int j = 0; j < kSlicePer; ++j) {
@@ -258,40 +248,47 @@ __global__ __launch_bounds__(kSliceThreads) void slice_compact_kernel(const floa
   }
   __syncthreads();
   // exclusive offsets of the 32 (key j, wave) groups in index order
-  const uint32_t c = lane < kSlicePer * 4 ? wc[lane] : 0u;
-  uint32_t incl = c;
+  const uint32_t cw = lane < kSlicePer * 4 ? wc[lane] : 0u;
+  uint32_t incl = cw;
 #pragma unroll
   for (int o = 1; o < 32; o <<= 1) {
     const uint32_t t = __shfl_up(incl, o);
     if (lane >= o) incl += t;
   }
-  const uint32_t excl = incl - c;
+  const uint32_t ex = incl - cw;
   const uint64_t below = (uint64_t(1) << lane) - 1u;
   uint32_t* const ck = ws.key + slot * kSliceCap;
   int32_t* const ci = ws.idx + slot * kSliceCap;
 #pragma unroll
   for (int j = 0; j < kSlicePer; ++j) {
-    const uint32_t pos = uint32_t(__shfl(int(excl), j * 4 + w)) + uint32_t(__popcll(bal[j] & below));
+    const uint32_t pos = uint32_t(__shfl(int(ex), j * 4 + w)) + uint32_t(__popcll(bal[j] & below));
     if (((bal[j] >> lane) & 1u) && pos < uint32_t(kSliceCap)) {
       ck[pos] = key[j];
       ci[pos] = base + j * kSliceThreads + tid;
     }
   }
   const uint32_t total = uint32_t(__shfl(int(incl), kSlicePer * 4 - 1));   // all lanes take part
-  if (tid == 0) ws.count[slot] = total;
+  if (tid == 0) {
+    ws.count[slot] = total;
+    ws.bound[slot] = lo;
+  }
 }
 
 // Pass c, gathering: the row's candidates into the LDS list in index order.
 // The counts, the bounds and the first entries of each wave's first slices
 // are loaded together (entries past a slice's count are read but unused).
 // Returns the list size, or -1 (block-uniform) when the candidates do not
-// fit; lo = min bound, top = max candidate key.
-CSA_DEV int gather_list(const SplitWs& ws, int row, int G, int k, ListShared& sh, uint32_t& lo, uint32_t& top) {
+// fit; lo / hi = min / max over the slices' bounds (empty slices ignored),
+// top = max candidate key.
+CSA_DEV int gather_list(const SplitWs& ws, int row, int G, int k, ListShared& sh, uint32_t& lo, uint32_t& hi,
+                        uint32_t& top) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   constexpr int kWaves = kThreads / 64;
   const size_t rbase = size_t(row) * G;
   const uint32_t c = tid < G ? ws.count[rbase + tid] : 0u;
-  uint32_t b = tid < G ? ws.bound[rbase + tid] : 0xFFFFFFFFu;
+  const uint32_t bnd = tid < G ? ws.bound[rbase + tid] : 0u;
+  uint32_t b = bnd != 0u ? bnd : 0xFFFFFFFFu;
+  uint32_t bh = bnd;
   uint32_t pk[kPreSlices][kPreEntries];
   int32_t pi[kPreSlices][kPreEntries];
 #pragma unroll
@@ -304,15 +301,25 @@ CSA_DEV int gather_list(const SplitWs& ws, int row, int G, int k, ListShared& sh
       pi[q][e] = sl < G ? ws.idx[at] : 0;
     }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) b = min(b, uint32_t(__shfl_xor(int(b), o)));
-  if (lane == 0) sh.wred[w] = b;
+  for (int o = 32; o > 0; o >>= 1) {
+    b = min(b, uint32_t(__shfl_xor(int(b), o)));
+    bh = max(bh, uint32_t(__shfl_xor(int(bh), o)));
+  }
+  if (lane == 0) {
+    sh.wred[w] = b;
+    sh.wred[16 + w] = bh;
+  }
   if (tid < G) sh.cnt[tid] = c;
   uint32_t total;
   const uint32_t excl = block_exclusive_scan(c, sh.smem, &total);   // its barriers publish wred, cnt
   if (tid < G) sh.off[tid] = excl;
   lo = sh.wred[0];
+  hi = sh.wred[16];
 #pragma unroll
-  for (int x = 1; x < kWaves; ++x) lo = min(lo, sh.wred[x]);
+  for (int x = 1; x < kWaves; ++x) {
+    lo = min(lo, sh.wred[x]);
+    hi = max(hi, sh.wred[16 + x]);
+  }
   const bool over = __syncthreads_or(c > uint32_t(kSliceCap));
   if (over || total > uint32_t(kList) || total < uint32_t(k)) return -1;
   uint32_t mx = 0u;
@@ -345,11 +352,11 @@ CSA_DEV int gather_list(const SplitWs& ws, int row, int G, int k, ListShared& sh
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = max(mx, uint32_t(__shfl_xor(int(mx), o)));
-  if (lane == 0) sh.wred[16 + w] = mx;
+  if (lane == 0) sh.wred[32 + w] = mx;
   __syncthreads();
-  top = sh.wred[16];
+  top = sh.wred[32];
 #pragma unroll
-  for (int x = 1; x < kWaves; ++x) top = max(top, sh.wred[16 + x]);
+  for (int x = 1; x < kWaves; ++x) top = max(top, sh.wred[32 + x]);
   return int(total);
 }
 
@@ -358,7 +365,12 @@ CSA_DEV int gather_list(const SplitWs& ws, int row, int G, int k, ListShared& sh
 // histogram pass over [lo, top] in at most 2048 buckets; one wave finds the
 // bucket of the k-th largest; that bucket's keys are ranked exactly (a
 // crowded bucket takes the exact radix refinement over the list instead).
-CSA_DEV void list_select_emit(int nc, uint32_t lo, uint32_t top, int k, int32_t* __restrict__ out, ListShared& sh) {
+// The list holds every row key >= hi (each slice kept all of its keys >= its
+// bound, hi the largest bound), so when the selected keys are all >= hi the
+// list's top k are the row's top k, ties included.  Otherwise nothing is
+// written and false is returned (block-uniform).
+CSA_DEV bool list_select_emit(int nc, uint32_t lo, uint32_t hi, uint32_t top, int k, int32_t* __restrict__ out,
+                              ListShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   for (int j = tid; j < kListBuckets; j += kThreads) sh.hist[j] = 0u;
   if (tid == 0) sh.n_rank = 0u;
@@ -436,6 +448,8 @@ CSA_DEV void list_select_emit(int nc, uint32_t lo, uint32_t top, int k, int32_t*
     };
     refine(each_cand, prefix, mask, remaining, sh);
   }
+  // every selected key has (key & mask) >= prefix, so key >= prefix
+  if (prefix < hi) return false;
   // emission: thread t walks list entries [t*per, t*per + per) in index order
   const int per = (nc + kThreads - 1) / kThreads;
   const int x0 = tid * per, x1 = min(nc, x0 + per);
@@ -458,6 +472,7 @@ CSA_DEV void list_select_emit(int nc, uint32_t lo, uint32_t top, int k, int32_t*
       ++eq_before;
     }
   }
+  return true;
 }
 
 template <bool kSplit>
@@ -483,12 +498,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   }
   const float* src = scores + size_t(row) * cap;
   if constexpr (kSplit) {
-    uint32_t lo, top;
-    const int nc = gather_list(ws, row, G, k, rs.list, lo, top);
-    if (nc >= 0) {
-      list_select_emit(nc, lo, top, k, out, rs.list);
-      return;
-    }
+    uint32_t lo, hi, top;
+    const int nc = gather_list(ws, row, G, k, rs.list, lo, hi, top);
+    if (nc >= 0 && list_select_emit(nc, lo, hi, top, k, out, rs.list)) return;
     __syncthreads();
   }
   const int n_super = (nv + kSuper - 1) / kSuper;
@@ -671,8 +683,7 @@ hipError_t launch_topk(long rows, hipStream_t st, const float* scores, const int
   const int G = n_slices(cap);
   const SplitWs w = split_ws(ws, rows, cap);
   const dim3 grid{unsigned(G), unsigned(rows), 1u};
-  hipLaunchKernelGGL(slice_bound_kernel, grid, dim3(kSliceThreads), 0, st, scores, q_pos0, T_q, cap, m, k, G, w.bound);
-  hipLaunchKernelGGL(slice_compact_kernel, grid, dim3(kSliceThreads), 0, st, scores, q_pos0, T_q, cap, m, k, G, w);
+  hipLaunchKernelGGL(slice_select_kernel, grid, dim3(kSliceThreads), 0, st, scores, q_pos0, T_q, cap, m, k, G, w);
   hipLaunchKernelGGL(topk_kernel<true>, dim3(unsigned(rows)), dim3(kThreads), sizeof(RowShared), st, scores, q_pos0,
                      T_q, cap, m, k, idx, w, G);
   return hipGetLastError();
