@@ -130,6 +130,28 @@ CSA_DEV float group_sum(float v) {
   return v;
 }
 
+// v of the lane n places lower in its 16-lane row, 0 for the row's first n
+// lanes (DPP row shift).
+template <int kN>
+CSA_DEV uint32_t row_shr(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x110 + kN, 0xF, 0xF, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4, 8
+// inside each 16-lane row, then the totals of the rows below (read from
+// lanes 15, 31, 47) are added.  ALU only, no LDS round trip.
+CSA_DEV uint32_t wave_inclusive_scan(uint32_t v) {
+  v += row_shr<1>(v);
+  v += row_shr<2>(v);
+  v += row_shr<4>(v);
+  v += row_shr<8>(v);
+  const uint32_t r0 = uint32_t(__builtin_amdgcn_readlane(int(v), 15));
+  const uint32_t r1 = uint32_t(__builtin_amdgcn_readlane(int(v), 31));
+  const uint32_t r2 = uint32_t(__builtin_amdgcn_readlane(int(v), 47));
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
 // Block-wide exclusive prefix sum of one uint32 per thread (blockDim.x a
 // multiple of 64, at most 1024).  `smem` needs blockDim.x/64 + 1 words.
 // Returns the exclusive prefix; *total receives the block sum.
@@ -137,22 +159,12 @@ CSA_DEV uint32_t block_exclusive_scan(uint32_t v, uint32_t* smem, uint32_t* tota
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
+  const uint32_t incl = wave_inclusive_scan(v);
   if (lane == 63) smem[wid] = incl;
   __syncthreads();
   if (wid == 0) {
-    uint32_t x = lane < nw ? smem[lane] : 0u;
-    uint32_t xi = x;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      uint32_t t = __shfl_up(xi, o);
-      if (lane >= o) xi += t;
-    }
+    const uint32_t x = lane < nw ? smem[lane] : 0u;
+    const uint32_t xi = wave_inclusive_scan(x);
     if (lane < nw) smem[lane] = xi - x;  // exclusive wave offsets
     if (lane == nw - 1) smem[16] = xi;
   }

@@ -87,8 +87,7 @@ constexpr int kListBuckets = 2048;
 constexpr int kSplitMaxRows = 128;
 constexpr int kSplitMinCap = 8192;
 constexpr int kMaxSlices = 1024;
-constexpr int kPreSlices = 4;                  // slices per wave whose first entries load with the counts
-constexpr int kPreEntries = 2;                 // entries per lane and slice loaded early
+constexpr int kPreLoads = 8;                   // candidate entries per lane loaded with the counts
 
 struct ListShared {
   uint32_t key[kList];
@@ -249,12 +248,7 @@ __global__ __launch_bounds__(kSliceThreads) void slice_select_kernel(const float
   __syncthreads();
   // exclusive offsets of the 32 (key j, wave) groups in index order
   const uint32_t cw = lane < kSlicePer * 4 ? wc[lane] : 0u;
-  uint32_t incl = cw;
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) {
-    const uint32_t t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
+  const uint32_t incl = wave_inclusive_scan(cw);
   const uint32_t ex = incl - cw;
   const uint64_t below = (uint64_t(1) << lane) - 1u;
   uint32_t* const ck = ws.key + slot * kSliceCap;
@@ -275,8 +269,10 @@ __global__ __launch_bounds__(kSliceThreads) void slice_select_kernel(const float
 }
 
 // Pass c, gathering: the row's candidates into the LDS list in index order.
-// The counts, the bounds and the first entries of each wave's first slices
-// are loaded together (entries past a slice's count are read but unused).
+// The counts, the bounds and the first entries of each wave's slices are
+// loaded together: kPreLoads entries per lane spread over the wave's first
+// spw slices (spw = slices per wave, up to 8; 512/spw entries of each),
+// entries past a slice's count read but unused.
 // Returns the list size, or -1 (block-uniform) when the candidates do not
 // fit; lo / hi = min / max over the slices' bounds (empty slices ignored),
 // top = max candidate key.
@@ -289,17 +285,19 @@ CSA_DEV int gather_list(const SplitWs& ws, int row, int G, int k, ListShared& sh
   const uint32_t bnd = tid < G ? ws.bound[rbase + tid] : 0u;
   uint32_t b = bnd != 0u ? bnd : 0xFFFFFFFFu;
   uint32_t bh = bnd;
-  uint32_t pk[kPreSlices][kPreEntries];
-  int32_t pi[kPreSlices][kPreEntries];
+  // slices per wave (power of two, at most kPreLoads) and entries of each
+  const int spw_need = (G + kWaves - 1) / kWaves;
+  const int spw = spw_need <= 1 ? 1 : spw_need <= 2 ? 2 : spw_need <= 4 ? 4 : 8;
+  const int per = kPreLoads / spw;
+  uint32_t pk[kPreLoads];
+  int32_t pi[kPreLoads];
 #pragma unroll
-  for (int q = 0; q < kPreSlices; ++q)
-#pragma unroll
-    for (int e = 0; e < kPreEntries; ++e) {
-      const int sl = w + kWaves * q;
-      const size_t at = (rbase + (sl < G ? sl : 0)) * kSliceCap + lane + 64 * e;
-      pk[q][e] = sl < G ? ws.key[at] : 0u;
-      pi[q][e] = sl < G ? ws.idx[at] : 0;
-    }
+  for (int i = 0; i < kPreLoads; ++i) {
+    const int sl = w + kWaves * (i / per);
+    const size_t at = (rbase + (sl < G ? sl : 0)) * kSliceCap + lane + 64 * (i % per);
+    pk[i] = sl < G ? ws.key[at] : 0u;
+    pi[i] = sl < G ? ws.idx[at] : 0;
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     b = min(b, uint32_t(__shfl_xor(int(b), o)));
@@ -324,25 +322,22 @@ CSA_DEV int gather_list(const SplitWs& ws, int row, int G, int k, ListShared& sh
   if (over || total > uint32_t(kList) || total < uint32_t(k)) return -1;
   uint32_t mx = 0u;
 #pragma unroll
-  for (int q = 0; q < kPreSlices; ++q) {
-    const int sl = w + kWaves * q;
+  for (int i = 0; i < kPreLoads; ++i) {
+    const int sl = w + kWaves * (i / per);
     if (sl < G) {
       const uint32_t o = sh.off[sl], n = sh.cnt[sl];
-#pragma unroll
-      for (int e = 0; e < kPreEntries; ++e) {
-        const uint32_t x = uint32_t(lane + 64 * e);
-        if (x < n) {
-          sh.key[o + x] = pk[q][e];
-          sh.idx[o + x] = pi[q][e];
-          mx = max(mx, pk[q][e]);
-        }
+      const uint32_t x = uint32_t(lane + 64 * (i % per));
+      if (x < n) {
+        sh.key[o + x] = pk[i];
+        sh.idx[o + x] = pi[i];
+        mx = max(mx, pk[i]);
       }
     }
   }
   // the rest: entries past the early ones, and the slices beyond them
   for (int sl = w; sl < G; sl += kWaves) {
     const uint32_t o = sh.off[sl], n = sh.cnt[sl];
-    const uint32_t x0 = sl < w + kWaves * kPreSlices ? uint32_t(64 * kPreEntries) : 0u;
+    const uint32_t x0 = sl < w + kWaves * spw ? uint32_t(64 * per) : 0u;
     for (uint32_t x = x0 + lane; x < n; x += 64) {
       const uint32_t kk = ws.key[(rbase + sl) * kSliceCap + x];
       sh.key[o + x] = kk;
@@ -391,12 +386,7 @@ CSA_DEV bool list_select_emit(int nc, uint32_t lo, uint32_t hi, uint32_t top, in
       hv[q] = h4[q];
       sum += hv[q][0] + hv[q][1] + hv[q][2] + hv[q][3];
     }
-    uint32_t incl = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
-    }
+    const uint32_t incl = wave_inclusive_scan(sum);
     const uint32_t excl = incl - sum;
     if (excl < uint32_t(k) && uint32_t(k) <= incl) {
       uint32_t run = excl;
