@@ -83,7 +83,8 @@ constexpr int kSliceCap = 512;                 // candidates kept per slice
 constexpr int kWindow = 1024;                  // buckets below the slice's top bucket
 constexpr uint32_t kLocal = 3;                 // a slice keeps about kLocal times its share of k
 constexpr int kList = 8192;                    // candidates per row held in LDS
-constexpr int kListBuckets = 2048;
+constexpr int kListBits = 9;                   // list histogram: 512 buckets over [lo, top]
+constexpr int kListBuckets = 1 << kListBits;
 constexpr int kSplitMaxRows = 128;
 constexpr int kSplitMinCap = 8192;
 constexpr int kMaxSlices = 1024;
@@ -92,7 +93,7 @@ constexpr int kPreLoads = 8;                   // candidate entries per lane loa
 struct ListShared {
   uint32_t key[kList];
   int32_t idx[kList];
-  uint32_t hist[kListBuckets];                 // also the radix passes of refine (<= 11 bits)
+  uint32_t hist[2048];                         // the list histogram; the radix passes of refine (<= 11 bits)
   uint32_t off[kMaxSlices];
   uint32_t cnt[kMaxSlices];
   uint32_t wred[48];                           // per-wave min bound, max bound, max key
@@ -159,18 +160,15 @@ CSA_DEV void load_keys(const float* __restrict__ src, int nv, int st, uint32_t (
     for (int c = 0; c < 4; ++c) key[j][c] = base + key_index(j, c) < nv ? ordered_key(v[j][c]) : 0u;
 }
 
-// Keys of slice s: thread t holds indices base + j*256 + t (coalesced, and a
-// wave ballot over key j covers 64 consecutive indices).
-CSA_DEV void load_slice(const float* __restrict__ src, int base, int n_s, uint32_t (&key)[kSlicePer]) {
-  float v[kSlicePer];
+// Scores of slice s: thread t holds indices base + j*256 + t (coalesced, and
+// a wave ballot over key j covers 64 consecutive indices); n_load bounds the
+// loads (the row's end), the visible count masks them afterwards.
+CSA_DEV void load_slice(const float* __restrict__ src, int base, int n_load, float (&v)[kSlicePer]) {
 #pragma unroll
   for (int j = 0; j < kSlicePer; ++j) {
     const int x = j * kSliceThreads + int(threadIdx.x);
-    v[j] = x < n_s ? src[base + x] : 0.f;
+    v[j] = x < n_load ? src[base + x] : 0.f;
   }
-#pragma unroll
-  for (int j = 0; j < kSlicePer; ++j)
-    key[j] = j * kSliceThreads + int(threadIdx.x) < n_s ? ordered_key(v[j]) : 0u;
 }
 
 // Pass a, one block per slice: v_s = the lower edge of the 14-bit bucket
@@ -189,9 +187,13 @@ __global__ __launch_bounds__(kSliceThreads) void slice_select_kernel(const float
   __shared__ uint32_t v_sh;
   const int row = blockIdx.y, sl = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
-  const int nv = visible_entries(q_pos0, T_q, row, cap, m);
-  if (nv <= k) return;
   const int base = sl * kSlice;
+  // the scores load alongside the query position (they do not depend on it)
+  float v[kSlicePer];
+  load_slice(scores + size_t(row) * cap, base, min(kSlice, cap - base), v);
+  const int nv = visible_entries(q_pos0, T_q, row, cap, m);
+  asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
+  if (nv <= k) return;
   const int n_s = min(kSlice, nv - base);
   const size_t slot = size_t(row) * G + sl;
   if (n_s <= 0) {
@@ -204,7 +206,8 @@ __global__ __launch_bounds__(kSliceThreads) void slice_select_kernel(const float
   const uint32_t quota = uint32_t((uint64_t(k) * uint32_t(n_s) + uint32_t(nv) - 1u) / uint32_t(nv));
   const uint32_t want = min(uint32_t(n_s), kLocal * quota);
   uint32_t key[kSlicePer];
-  load_slice(scores + size_t(row) * cap, base, n_s, key);
+#pragma unroll
+  for (int j = 0; j < kSlicePer; ++j) key[j] = j * kSliceThreads + tid < n_s ? ordered_key(v[j]) : 0u;
   reinterpret_cast<u32x4*>(hist)[tid] = u32x4{0u, 0u, 0u, 0u};
   uint32_t mx = 0u;
 #pragma unroll
@@ -357,7 +360,7 @@ CSA_DEV int gather_list(const SplitWs& ws, int row, int G, int k, ListShared& sh
 
 // Pass c, selection: the k largest of the nc list keys (all >= lo, at most
 // top; nc >= k), written to out in list order (= index order).  One
-// histogram pass over [lo, top] in at most 2048 buckets; one wave finds the
+// histogram pass over [lo, top] in at most 512 buckets; one wave finds the
 // bucket of the k-th largest; that bucket's keys are ranked exactly (a
 // crowded bucket takes the exact radix refinement over the list instead).
 // The list holds every row key >= hi (each slice kept all of its keys >= its
@@ -372,17 +375,18 @@ CSA_DEV bool list_select_emit(int nc, uint32_t lo, uint32_t hi, uint32_t top, in
   __syncthreads();
   const uint32_t range = top - lo;
   const int bits = range == 0u ? 0 : 32 - __clz(range);
-  const int shift = bits > 11 ? bits - 11 : 0;
+  const int shift = bits > kListBits ? bits - kListBits : 0;
   for (int x = tid; x < nc; x += kThreads) atomicAdd(&sh.hist[(sh.key[x] - lo) >> shift], 1u);
   __syncthreads();
   if (w == 0) {
-    // lane l holds the 32 buckets below hi = 2047 - 32 l, in registers
-    const int hi = kListBuckets - 1 - 32 * lane;
-    const u32x4* h4 = reinterpret_cast<const u32x4*>(sh.hist + hi - 31);
-    u32x4 hv[8];
+    // lane l holds the kBL buckets below hi = kListBuckets - 1 - kBL l, in registers
+    constexpr int kBL = kListBuckets / 64;
+    const int hi = kListBuckets - 1 - kBL * lane;
+    const u32x4* h4 = reinterpret_cast<const u32x4*>(sh.hist + hi - (kBL - 1));
+    u32x4 hv[kBL / 4];
     uint32_t sum = 0u;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < kBL / 4; ++q) {
       hv[q] = h4[q];
       sum += hv[q][0] + hv[q][1] + hv[q][2] + hv[q][3];
     }
@@ -392,10 +396,10 @@ CSA_DEV bool list_select_emit(int nc, uint32_t lo, uint32_t hi, uint32_t top, in
       uint32_t run = excl;
       bool found = false;
 #pragma unroll
-      for (int y = 31; y >= 0; --y) {          // bucket hi - 31 + y, from the top down
+      for (int y = kBL - 1; y >= 0; --y) {     // bucket hi - (kBL - 1) + y, from the top down
         const uint32_t cy = hv[y >> 2][y & 3];
         if (!found && run + cy >= uint32_t(k)) {
-          sh.sel.bin = uint32_t(hi - 31 + y);
+          sh.sel.bin = uint32_t(hi - (kBL - 1) + y);
           sh.sel.remaining = uint32_t(k) - run;
           sh.sel.bincount = cy;
           found = true;
@@ -479,17 +483,22 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int t = q_pos0[b] + i;
+  int32_t* out = idx + size_t(row) * k;
+  // split path: the candidates are gathered before the visibility is known
+  // (their loads overlap the query position's); a row that needs no
+  // selection leaves them unused (its buffers then hold stale counts, which
+  // the gather's size checks reject before any is used as a size)
+  uint32_t lo = 0u, hi = 0u, top = 0u;
+  int nc = -1;
+  if constexpr (kSplit) nc = gather_list(ws, row, G, k, rs.list, lo, hi, top);
   int nv = (t + 1) / m;
   nv = max(0, min(nv, cap));
-  int32_t* out = idx + size_t(row) * k;
   if (nv <= k) {
     for (int j = tid; j < k; j += kThreads) out[j] = j < nv ? j : -1;
     return;
   }
   const float* src = scores + size_t(row) * cap;
   if constexpr (kSplit) {
-    uint32_t lo, hi, top;
-    const int nc = gather_list(ws, row, G, k, rs.list, lo, hi, top);
     if (nc >= 0 && list_select_emit(nc, lo, hi, top, k, out, rs.list)) return;
     __syncthreads();
   }
