@@ -125,19 +125,43 @@ struct Pre {
   int src[2];
 };
 
-template <int kDT>
-CSA_DEV void load_part(const void* base, long row, int dg, u32x4* dst) {
-  // 8 head dims [8*dg, 8*dg + 8) of `row`
-  if constexpr (kDT == CSA_FP8_E4M3) {
-    const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(base) + row * kHeadDim + dg * 8);
-    dst[0] = u32x4{w[0], w[1], 0u, 0u};
-  } else if constexpr (kDT == CSA_BF16) {
-    dst[0] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + row * kHeadDim + dg * 8);
-  } else {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + row * kHeadDim + dg * 8);
-    dst[0] = p[0];
-    dst[1] = p[1];
+// Loads of one gather slot x: the K and V parts (8 head dims [8 dg, 8 dg + 8))
+// of `row` in the compressed cache (src 1) or the raw window (src 2); an
+// empty slot (src 0) reads the start of the query buffer instead (always
+// valid; the value is never used).  Every lane issues the same loads with its
+// own address, with no branch: loads issued inside divergent branches make
+// the compiler wait for every load in flight (the two sides of the branch
+// share registers), which would end each prefetch before the compute it is
+// meant to overlap.  An fp8 part (8 bytes) is fetched as the aligned 16 bytes
+// that hold it (inside its 128-byte row); part_bf16 / part_f32 pick the half.
+// The fp8 scales are loaded raw and applied by store_chunk for src 1 only.
+template <int kIO, int kCKV>
+CSA_DEV void gather_slot(const AttnArgs& a, Pre<kIO>& pr, int x, int src, long row, int dg) {
+  constexpr long kCB = kCKV == CSA_F32 ? 4 : kCKV == CSA_BF16 ? 2 : 1;   // bytes per compressed value
+  constexpr long kWB = kIO == CSA_F32 ? 4 : 2;                           // bytes per window value
+  const char* safe = static_cast<const char*>(a.q);
+  const long coff = row * (kHeadDim * kCB) + (kCKV == CSA_FP8_E4M3 ? long(dg & ~1) * 8 : long(dg) * 8 * kCB);
+  const long woff = row * (kHeadDim * kWB) + long(dg) * 8 * kWB;
+  const char* pk = src == 1 ? static_cast<const char*>(a.ck) + coff
+                 : src == 2 ? static_cast<const char*>(a.k_win) + woff : safe;
+  const char* pv = src == 1 ? static_cast<const char*>(a.cv) + coff
+                 : src == 2 ? static_cast<const char*>(a.v_win) + woff : safe;
+  pr.k[x][0] = *reinterpret_cast<const u32x4*>(pk);
+  pr.v[x][0] = *reinterpret_cast<const u32x4*>(pv);
+  if constexpr (Pre<kIO>::R == 2) {
+    // second 16 bytes of a 32-byte part (fp32); a 16-byte compressed part reads the safe address
+    const bool wide = src == 2 || (src == 1 && kCKV == CSA_F32);
+    pr.k[x][1] = *reinterpret_cast<const u32x4*>(wide ? pk + 16 : safe);
+    pr.v[x][1] = *reinterpret_cast<const u32x4*>(wide ? pv + 16 : safe);
   }
+  if constexpr (kCKV == CSA_FP8_E4M3) {
+    pr.sk[x] = *(src == 1 ? a.ck_scale + row : reinterpret_cast<const float*>(safe));
+    pr.sv[x] = *(src == 1 ? a.cv_scale + row : reinterpret_cast<const float*>(safe));
+  } else {
+    pr.sk[x] = 1.f;
+    pr.sv[x] = 1.f;
+  }
+  pr.src[x] = src;
 }
 
 // Gather item of thread tid: key pair kp = tid % 32 (keys 2kp, 2kp+1 of the
@@ -146,6 +170,8 @@ CSA_DEV void load_part(const void* base, long row, int dg, u32x4* dst) {
 // Selected-entry indices of the item's two slots in chunk jc (sparse lists);
 // they are loaded one chunk ahead of the rows they name, so a row load never
 // waits on an index load issued in the same step.
+// The load is unconditional (position clamped into the list; slots past the
+// list or the split are never used), for the same reason as gather_slot.
 template <bool kDense>
 CSA_DEV void load_idx(const AttnArgs& a, int (&e)[2], int b, int i, int jc, int j_end) {
   e[0] = e[1] = -1;
@@ -155,9 +181,10 @@ CSA_DEV void load_idx(const AttnArgs& a, int (&e)[2], int b, int i, int jc, int 
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int j = jc + 2 * kp + x;
-      if (j < j_end && j < a.k) e[x] = ip[j];
+      e[x] = ip[min(j, a.k - 1)];
     }
   }
+  (void)j_end;
 }
 
 // Rows of the item's two slots of chunk jc (e: their indices from load_idx).
@@ -170,32 +197,19 @@ CSA_DEV void prefetch(const AttnArgs& a, Pre<kIO>& pr, const int (&e)[2], int b,
     const int j = jc + 2 * kp + x;
     long row = 0;
     const int src = j < j_end ? key_source<kDense>(a, b, t, raw0, j, e[x], &row) : 0;
-    pr.src[x] = src;
-    pr.sk[x] = 1.f;
-    pr.sv[x] = 1.f;
-    if (src == 1) {
-      load_part<kCKV>(a.ck, row, dg, pr.k[x]);
-      load_part<kCKV>(a.cv, row, dg, pr.v[x]);
-      if constexpr (kCKV == CSA_FP8_E4M3) {
-        pr.sk[x] = a.ck_scale[row];
-        pr.sv[x] = a.cv_scale[row];
-      }
-    } else if (src == 2) {
-      load_part<kIO>(a.k_win, row, dg, pr.k[x]);
-      load_part<kIO>(a.v_win, row, dg, pr.v[x]);
-    }
+    gather_slot<kIO, kCKV>(a, pr, x, src, row, dg);
   }
 }
 
 // 8 values of a gathered part as fp32 (src 0 -> zeros)
 template <int kIO, int kCKV>
-CSA_DEV void part_f32(const u32x4* w, int src, float* x) {
+CSA_DEV void part_f32(const u32x4* w, int src, int h, float* x) {
   if (src == 0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = 0.f;
   } else if (kCKV == CSA_FP8_E4M3 && src == 1) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = e4m3_to_f32((w[0][e >> 2] >> (8 * (e & 3))) & 0xFFu);
+    for (int e = 0; e < 8; ++e) x[e] = e4m3_to_f32((w[0][2 * h + (e >> 2)] >> (8 * (e & 3))) & 0xFFu);
   } else if constexpr (kIO == CSA_BF16) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -244,16 +258,21 @@ constexpr size_t lds_bytes() {
 // codes go through the CDNA4 fp8 -> bf16 conversion, which is exact (every
 // E4M3 value is a bf16 value); the per-entry scale is applied elsewhere.
 template <int kCKV>
-CSA_DEV u32x4 part_bf16(const u32x4* w, int src) {
-  if (src == 0) return u32x4{0u, 0u, 0u, 0u};
-  if (kCKV == CSA_FP8_E4M3 && src == 1) {
-    const uint32_t c0 = w[0][0], c1 = w[0][1];
-    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, 1.0f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, 1.0f, true)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, 1.0f, false)),
-                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, 1.0f, true))};
+CSA_DEV u32x4 part_bf16(const u32x4* w, int src, int h) {
+  // selects, not branches (see gather_slot): the result depends on src only
+  u32x4 r = w[0];
+  if constexpr (kCKV == CSA_FP8_E4M3) {
+    const uint32_t c0 = h ? w[0][2] : w[0][0], c1 = h ? w[0][3] : w[0][1];
+    const u32x4 cv = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, 1.0f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c0, 1.0f, true)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, 1.0f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, 1.0f, true))};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = src == 1 ? cv[q] : r[q];
   }
-  return w[0];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) r[q] = src == 0 ? 0u : r[q];
+  return r;
 }
 
 // sk_mul: factor folded into the stored K scale (the logit scale in the log2 domain).
@@ -266,8 +285,8 @@ CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr, float sk_mul) {
     u32x4 kw[2], vw[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      kw[e] = part_bf16<kCKV>(pr.k[e], pr.src[e]);
-      vw[e] = part_bf16<kCKV>(pr.v[e], pr.src[e]);
+      kw[e] = part_bf16<kCKV>(pr.k[e], pr.src[e], dg & 1);
+      vw[e] = part_bf16<kCKV>(pr.v[e], pr.src[e], dg & 1);
       *reinterpret_cast<u32x4*>(&s.K[2 * kp + e][dg * 8]) = kw[e];
     }
     // V^T: head dim x of keys 2kp and 2kp+1 as one bf16 pair
@@ -280,8 +299,8 @@ CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr, float sk_mul) {
     float xk[2][8], xv[2][8];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      part_f32<kIO, kCKV>(pr.k[e], pr.src[e], xk[e]);
-      part_f32<kIO, kCKV>(pr.v[e], pr.src[e], xv[e]);
+      part_f32<kIO, kCKV>(pr.k[e], pr.src[e], dg & 1, xk[e]);
+      part_f32<kIO, kCKV>(pr.v[e], pr.src[e], dg & 1, xv[e]);
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e)
@@ -294,8 +313,9 @@ CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr, float sk_mul) {
   if (dg == 0) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      s.sk[2 * kp + e] = pr.sk[e] * sk_mul;
-      s.sv[2 * kp + e] = pr.sv[e];
+      const bool scaled = kCKV == CSA_FP8_E4M3 && pr.src[e] == 1;
+      s.sk[2 * kp + e] = (scaled ? pr.sk[e] : 1.f) * sk_mul;
+      s.sv[2 * kp + e] = scaled ? pr.sv[e] : 1.f;
       s.valid[2 * kp + e] = pr.src[e] != 0;
     }
   }
@@ -334,8 +354,11 @@ CSA_DEV void store_out4(void* out, long orow, int d4, v4f v) {
 // 8 waves: wave w takes head tiles (w % 4) [+ 4 when kHTW == 2] and key half
 // w / 4 (keys [32*(w/4), 32*(w/4)+32) of every chunk); the two halves merge at
 // the end of the block through LDS.
-template <int kIO, int kCKV, bool kDense, int kHTW>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kIO == CSA_BF16 && kHTW == 1 ? 4 : 1)))
+// kDeep (split key lists, at most about one block per CU): two chunks in
+// flight instead of one, with the register budget of two waves per SIMD.
+template <int kIO, int kCKV, bool kDense, int kHTW, bool kDeep>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kIO == CSA_BF16 && kHTW == 1 ? (kDeep ? 2 : 4) : 1)))
 void attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   LdsChunk<kIO>& s = *reinterpret_cast<LdsChunk<kIO>*>(smem);
@@ -387,19 +410,8 @@ void attn_kernel(AttnArgs a) {
     l_run[ht] = 0.f;
   }
 
-  Pre<kIO> pr;
-  int e_nx[2];
-  load_idx<kDense>(a, e_nx, b, i, j_begin, j_end);
-  if (j_begin < j_end) prefetch<kIO, kCKV, kDense>(a, pr, e_nx, b, t, raw0, j_begin, j_end);
-  load_idx<kDense>(a, e_nx, b, i, j_begin + kNK, j_end);
-  for (int j0 = j_begin; j0 < j_end; j0 += kNK) {
-    __syncthreads();
-    store_chunk<kIO, kCKV>(s, pr, a.sm_log2);
-    __syncthreads();
-    if (j0 + kNK < j_end) {
-      prefetch<kIO, kCKV, kDense>(a, pr, e_nx, b, t, raw0, j0 + kNK, j_end);
-      load_idx<kDense>(a, e_nx, b, i, j0 + 2 * kNK, j_end);
-    }
+  // one chunk in LDS: logits, online softmax and P*V for this wave's tiles
+  auto compute = [&]() {
 #pragma unroll
     for (int ht = 0; ht < kHTW; ++ht) {
       if (!act[ht]) continue;
@@ -466,6 +478,49 @@ void attn_kernel(AttnArgs a) {
             for (int dt = 0; dt < 8; ++dt) o[ht][dt] = mfma_f32(s.V[key][dt * 16 + col], pv, o[ht][dt]);
           }
       }
+    }
+  };
+
+  Pre<kIO> pr;
+  int e_nx[2];
+  if constexpr (!kDeep) {
+    // every prefetch is issued, past the split too (empty slots read a dummy
+    // address): the same loads on every path keep the compiler's waits exact
+    load_idx<kDense>(a, e_nx, b, i, j_begin, j_end);
+    prefetch<kIO, kCKV, kDense>(a, pr, e_nx, b, t, raw0, j_begin, j_end);
+    load_idx<kDense>(a, e_nx, b, i, j_begin + kNK, j_end);
+    for (int j0 = j_begin; j0 < j_end; j0 += kNK) {
+      __syncthreads();
+      store_chunk<kIO, kCKV>(s, pr, a.sm_log2);
+      __syncthreads();
+      prefetch<kIO, kCKV, kDense>(a, pr, e_nx, b, t, raw0, j0 + kNK, j_end);
+      load_idx<kDense>(a, e_nx, b, i, j0 + 2 * kNK, j_end);
+      compute();
+    }
+  } else {
+    // two chunks in flight: buffers pr (even chunks) and pr2 (odd chunks)
+    Pre<kIO> pr2;
+    int e_nx2[2];
+    load_idx<kDense>(a, e_nx, b, i, j_begin, j_end);
+    load_idx<kDense>(a, e_nx2, b, i, j_begin + kNK, j_end);
+    prefetch<kIO, kCKV, kDense>(a, pr, e_nx, b, t, raw0, j_begin, j_end);
+    prefetch<kIO, kCKV, kDense>(a, pr2, e_nx2, b, t, raw0, j_begin + kNK, j_end);
+    load_idx<kDense>(a, e_nx, b, i, j_begin + 2 * kNK, j_end);
+    load_idx<kDense>(a, e_nx2, b, i, j_begin + 3 * kNK, j_end);
+    for (int j0 = j_begin; j0 < j_end; j0 += 2 * kNK) {
+      __syncthreads();
+      store_chunk<kIO, kCKV>(s, pr, a.sm_log2);
+      __syncthreads();
+      prefetch<kIO, kCKV, kDense>(a, pr, e_nx, b, t, raw0, j0 + 2 * kNK, j_end);
+      load_idx<kDense>(a, e_nx, b, i, j0 + 4 * kNK, j_end);
+      compute();
+      if (j0 + kNK >= j_end) break;
+      __syncthreads();
+      store_chunk<kIO, kCKV>(s, pr2, a.sm_log2);
+      __syncthreads();
+      prefetch<kIO, kCKV, kDense>(a, pr2, e_nx2, b, t, raw0, j0 + 3 * kNK, j_end);
+      load_idx<kDense>(a, e_nx2, b, i, j0 + 5 * kNK, j_end);
+      compute();
     }
   }
 
@@ -630,21 +685,8 @@ CSA_DEV void prefetch_mq(const AttnArgs& a, Pre<CSA_BF16>& pr, uint32_t (&vis)[2
         q_to = min(n_q - 1, p + a.W - 1 - t0);
       }
     }
-    pr.src[x] = src;
     vis[x] = q_from <= q_to ? ((2u << q_to) - 1u) & ~((1u << q_from) - 1u) : 0u;
-    pr.sk[x] = 1.f;
-    pr.sv[x] = 1.f;
-    if (src == 1) {
-      load_part<kCKV>(a.ck, row, dg, pr.k[x]);
-      load_part<kCKV>(a.cv, row, dg, pr.v[x]);
-      if constexpr (kCKV == CSA_FP8_E4M3) {
-        pr.sk[x] = a.ck_scale[row];
-        pr.sv[x] = a.cv_scale[row];
-      }
-    } else if (src == 2) {
-      load_part<CSA_BF16>(a.k_win, row, dg, pr.k[x]);
-      load_part<CSA_BF16>(a.v_win, row, dg, pr.v[x]);
-    }
+    gather_slot<CSA_BF16, kCKV>(a, pr, x, src, row, dg);
   }
 }
 
@@ -835,11 +877,11 @@ size_t plan_ws_bytes(const Plan& p, long rows, int H) {
   return ml + slots * kHeadDim * 4;
 }
 
-template <int kIO, int kCKV, bool kDense, int kHTW>
+template <int kIO, int kCKV, bool kDense, int kHTW, bool kDeep>
 hipError_t launch_attn(const AttnArgs& a, long blocks, hipStream_t st) {
   static bool attr = false;   // per instantiation; dynamic LDS above 64 KB needs the opt-in
   constexpr size_t bytes = lds_bytes<kIO, kHTW>();
-  auto fn = attn_kernel<kIO, kCKV, kDense, kHTW>;
+  auto fn = attn_kernel<kIO, kCKV, kDense, kHTW, kDeep>;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        int(bytes));
@@ -888,8 +930,15 @@ bool use_mq(int io_dtype, int H, int T_q, const Plan& p) {
 
 template <int kIO, int kCKV, bool kDense>
 hipError_t launch_tiles(const AttnArgs& a, long blocks, hipStream_t st) {
-  return a.H <= 64 ? launch_attn<kIO, kCKV, kDense, 1>(a, blocks, st)
-                   : launch_attn<kIO, kCKV, kDense, 2>(a, blocks, st);
+  // split key lists of more than two chunks take the two-chunk pipeline
+  // (fp32 queries over more than 64 heads would not fit its registers); with
+  // two chunks the one-ahead prefetch already overlaps the second
+  if (a.n_splits > 1 && a.split_len > 2 * kNK) {
+    if (a.H <= 64) return launch_attn<kIO, kCKV, kDense, 1, true>(a, blocks, st);
+    if constexpr (kIO == CSA_BF16) return launch_attn<kIO, kCKV, kDense, 2, true>(a, blocks, st);
+  }
+  return a.H <= 64 ? launch_attn<kIO, kCKV, kDense, 1, false>(a, blocks, st)
+                   : launch_attn<kIO, kCKV, kDense, 2, false>(a, blocks, st);
 }
 
 template <bool kDense>
