@@ -98,21 +98,29 @@ CSA_DEV void load_a(const uint8_t* __restrict__ q_codes, const uint8_t* __restri
   }
 }
 
-// B operand of one 16-entry fragment: lane column `col` is entry e (absent if !use).
+// Buffer resource over one sequence's key codes or scales: a load at an
+// offset past `bytes` returns zeros without touching memory.
+CSA_DEV __amdgpu_buffer_rsrc_t seq_rsrc(const uint8_t* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, bytes, 0x00020000);
+}
+
+// B operand of one 16-entry fragment: lane column `col` is entry e (absent if
+// !use).  An absent entry or contraction block reads past the resource and
+// gets zero codes and a zero scale byte (2^-127): a zero contribution.  Every
+// lane issues the same loads, with no branch: loads inside divergent branches
+// make the compiler wait for every load in flight at the join (the two sides
+// share registers), which would drain the next batch's loads early.
 template <int kKS, bool kStream>
-CSA_DEV void load_b(const uint8_t* __restrict__ kc_seq, const uint8_t* __restrict__ ke_seq, int e, bool use, int g,
-                    int nblk, int row_bytes, u32x4 (&bk)[kKS], int (&sb)[kKS]) {
+CSA_DEV void load_b(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t re, uint32_t c_bytes, uint32_t e_bytes, int e,
+                    bool use, int g, int nblk, int row_bytes, u32x4 (&bk)[kKS], int (&sb)[kKS]) {
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks) {
     const int c = ks * 4 + g;
-    if (use && c < nblk) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(kc_seq + size_t(e) * row_bytes + c * 16);
-      bk[ks] = kStream ? __builtin_nontemporal_load(p) : *p;
-      sb[ks] = ke_seq[size_t(e) * nblk + c];
-    } else {
-      bk[ks] = u32x4{0u, 0u, 0u, 0u};
-      sb[ks] = 127;
-    }
+    const bool ok = use && c < nblk;
+    const uint32_t oc = ok ? uint32_t(e) * uint32_t(row_bytes) + uint32_t(c) * 16u : c_bytes;
+    const uint32_t oe = ok ? uint32_t(e) * uint32_t(nblk) + uint32_t(c) : e_bytes;
+    bk[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, oc, 0, kStream ? 2 : 0));
+    sb[ks] = __builtin_amdgcn_raw_buffer_load_b8(re, oe, 0, 0);
   }
 }
 
@@ -175,6 +183,10 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
 
   const uint8_t* kc_seq = k_codes + size_t(b) * cap * row_bytes;
   const uint8_t* ke_seq = k_e8m0 + size_t(b) * cap * nblk;
+  const uint32_t c_bytes = uint32_t(cap) * uint32_t(row_bytes);   // < 2^31 (argument check)
+  const uint32_t e_bytes = uint32_t(cap) * uint32_t(nblk);
+  const __amdgpu_buffer_rsrc_t rc = seq_rsrc(kc_seq, c_bytes);
+  const __amdgpu_buffer_rsrc_t re = seq_rsrc(ke_seq, e_bytes);
 
   // output row of each row tile's query (the query whose rows the lane holds)
   bool q_in[kRT];
@@ -202,16 +214,20 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
 #pragma unroll
   for (int f = 0; f < kFrag; ++f) {
     const int e = e_wave0 + f * 16 + col;
-    load_b<kKS, kStream>(kc_seq, ke_seq, e, e < nv_max, g, nblk, row_bytes, bk[f], sb[f]);
+    load_b<kKS, kStream>(rc, re, c_bytes, e_bytes, e, e < nv_max, g, nblk, row_bytes, bk[f], sb[f]);
   }
   for (int e_frag0 = e_wave0; e_frag0 < e_wave1; e_frag0 += 16 * kFrag) {
+    // the next batch loads while this one computes (a streaming wave owns a
+    // single batch: nothing to prefetch)
     u32x4 bn[kFrag][kKS];
     int sn[kFrag][kKS];
-    const bool more = e_frag0 + 16 * kFrag < e_wave1;
+    if constexpr (!kStream) {
+      const bool more = e_frag0 + 16 * kFrag < e_wave1;
 #pragma unroll
-    for (int f = 0; f < kFrag; ++f) {
-      const int e = e_frag0 + 16 * kFrag + f * 16 + col;
-      load_b<kKS, kStream>(kc_seq, ke_seq, e, more && e < nv_max, g, nblk, row_bytes, bn[f], sn[f]);
+      for (int f = 0; f < kFrag; ++f) {
+        const int e = e_frag0 + 16 * kFrag + f * 16 + col;
+        load_b<kKS, kStream>(rc, re, c_bytes, e_bytes, e, more && e < nv_max, g, nblk, row_bytes, bn[f], sn[f]);
+      }
     }
     // every MFMA of the batch first, into its own accumulator; entries past
     // every query's visibility carry zero operands and their scores are
@@ -248,13 +264,15 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
           if (writer) put(rt, e_frag0 + f * 16 + col, p);
         }
     }
+    if constexpr (!kStream) {
 #pragma unroll
-    for (int f = 0; f < kFrag; ++f)
+      for (int f = 0; f < kFrag; ++f)
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        bk[f][ks] = bn[f][ks];
-        sb[f][ks] = sn[f][ks];
-      }
+        for (int ks = 0; ks < kKS; ++ks) {
+          bk[f][ks] = bn[f][ks];
+          sb[f][ks] = sn[f][ks];
+        }
+    }
   }
 }
 
@@ -264,7 +282,7 @@ hipError_t launch_indexer_ks(const uint8_t* qc, const uint8_t* qe, const float* 
                              void* out, hipStream_t st) {
   constexpr int kFrag = 4;
   constexpr int kQPT = 16 / kHI;
-  const int entries_per_wave = kStream ? 64 : 256;
+  const int entries_per_wave = kStream ? 16 * kFrag : 256;   // streaming: one batch per wave
   const int per_block = entries_per_wave * kWavesPerBlock;
   // Blocks are dealt to the 8 XCDs round-robin in linear order (x fastest);
   // with the entry dimension padded to a multiple of 8, entry block x always
@@ -309,6 +327,7 @@ inline csa_status_t check_indexer_args(const void* q_codes, const void* q_e8m0, 
   if (B < 0 || T_q < 0 || cap < 0 || m < 1) return CSA_EINVAL;
   if (H_I != 4 && H_I != 8 && H_I != 16) return CSA_ENOTSUP;
   if (B > 65535 || T_q > (1 << 24)) return CSA_ENOTSUP;
+  if (long(cap) * (d_I / 2) >= (1L << 31)) return CSA_ENOTSUP;   // one sequence's key codes under 2 GiB
   return CSA_OK;
 }
 

@@ -259,8 +259,8 @@ CSA_DEV void rescore_setup(Rescore<kHI, kKS>& R, const uint8_t* q_codes, const u
 // Exact keys of the listed entries cand_idx[0..n) into cand_key[0..n); the
 // 16 waves take 16-entry groups in turn.  Ends with a block barrier.
 template <int kHI, int kKS>
-CSA_DEV void rescore_list(const Rescore<kHI, kKS>& R, const uint8_t* kc_seq, const uint8_t* ke_seq, int n,
-                          int nblk, int row_bytes, Shared& sh) {
+CSA_DEV void rescore_list(const Rescore<kHI, kKS>& R, __amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t re,
+                          uint32_t c_bytes, uint32_t e_bytes, int n, int nblk, int row_bytes, Shared& sh) {
   const int lane = threadIdx.x & 63;
   const int col = lane & 15;
   const int g = lane >> 4;
@@ -270,7 +270,7 @@ CSA_DEV void rescore_list(const Rescore<kHI, kKS>& R, const uint8_t* kc_seq, con
     const int e = j < n ? sh.cand_idx[j] : 0;
     u32x4 bk[kKS];
     int sb[kKS];
-    load_b<kKS, false>(kc_seq, ke_seq, e, j < n, g, nblk, row_bytes, bk, sb);
+    load_b<kKS, false>(rc, re, c_bytes, e_bytes, e, j < n, g, nblk, row_bytes, bk, sb);
     v4f acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) acc = mfma_fp4(R.a[ks], R.sa[ks], bk[ks], sb[ks], acc);
@@ -315,6 +315,10 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const uint16_t* __rest
   const int row_bytes = d_I >> 1;
   const uint8_t* kc_seq = k_codes + size_t(b) * cap * row_bytes;
   const uint8_t* ke_seq = k_e8m0 + size_t(b) * cap * nblk;
+  const uint32_t c_bytes = uint32_t(cap) * uint32_t(row_bytes);   // < 2^31 (argument check)
+  const uint32_t e_bytes = uint32_t(cap) * uint32_t(nblk);
+  const __amdgpu_buffer_rsrc_t rc = seq_rsrc(kc_seq, c_bytes);
+  const __amdgpu_buffer_rsrc_t re = seq_rsrc(ke_seq, e_bytes);
 
   for (int j = tid; j < kBuckets; j += kThreads) sh.hist[j] = 0u;
   for (int j = tid; j < kS / 32; j += kThreads) sh.bm.eq[j] = 0u;
@@ -442,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const uint16_t* __rest
       }
       __syncthreads();
       const int nc = int(sh.n_cand);
-      rescore_list<kHI, kKS>(R, kc_seq, ke_seq, nc, nblk, row_bytes, sh);
+      rescore_list<kHI, kKS>(R, rc, re, c_bytes, e_bytes, nc, nblk, row_bytes, sh);
       auto each_listed = [&](auto fn) {
         for (int x = tid; x < nc; x += kThreads) fn(sh.cand_key[x]);
       };
@@ -458,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const uint16_t* __rest
                           nullptr, &sh.n_cand, nullptr, [] {});
             __syncthreads();
             const int nc = int(sh.n_cand);
-            rescore_list<kHI, kKS>(R, kc_seq, ke_seq, nc, nblk, row_bytes, sh);
+            rescore_list<kHI, kKS>(R, rc, re, c_bytes, e_bytes, nc, nblk, row_bytes, sh);
             for (int x = tid; x < nc; x += kThreads) fn(sh.cand_key[x]);
             __syncthreads();
           }
@@ -542,7 +546,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const uint16_t* __rest
                           nullptr, &sh.n_cand, nullptr, [] {});
             __syncthreads();
             const int nc = int(sh.n_cand);
-            rescore_list<kHI, kKS>(R, kc_seq, ke_seq, nc, nblk, row_bytes, sh);
+            rescore_list<kHI, kKS>(R, rc, re, c_bytes, e_bytes, nc, nblk, row_bytes, sh);
             for (int x = tid; x < nc; x += kThreads) mark(sh.cand_idx[x], sh.cand_key[x]);
             __syncthreads();
           }
