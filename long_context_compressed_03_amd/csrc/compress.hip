@@ -74,21 +74,26 @@ __global__ __launch_bounds__(kBlock) void compress_kernel(const void* __restrict
                                                           int ld_in, int m, void* k_out, void* v_out,
                                                           float* k_scale, float* v_scale, int ld_out) {
   const int lane_c = threadIdx.x & (kGroup - 1);
-  const long gid = long(blockIdx.x) * kEntriesPerBlock + (threadIdx.x / kGroup);
+  const long gid = long(blockIdx.x) * (blockDim.x / kGroup) + (threadIdx.x / kGroup);
   if (gid >= long(B) * n_entries) return;  // whole 16-lane groups exit together
   const int b = int(gid / n_entries);
   const int e = int(gid - long(b) * n_entries);
   const size_t row0 = size_t(b) * ld_in + size_t(e) * m;
   const float* z = logits + row0;
 
-  // softmax statistics of the block's logits, spread over the 16 lanes
-  float zmax = -INFINITY;
-  for (int j = lane_c; j < m; j += kGroup) zmax = fmaxf(zmax, z[j]);
-  zmax = group_max<kGroup>(zmax);
-  float zsum = 0.f;
-  for (int j = lane_c; j < m; j += kGroup) zsum += expf(z[j] - zmax);
-  zsum = group_sum<kGroup>(zsum);
-  const float inv = 1.f / zsum;
+  // softmax statistics of the block's logits, spread over the 16 lanes;
+  // computed after the first rows are requested, so the two memory round
+  // trips overlap
+  float zmax = 0.f, inv = 0.f;
+  auto stats = [&]() {
+    zmax = -INFINITY;
+    for (int x = lane_c; x < m; x += kGroup) zmax = fmaxf(zmax, z[x]);
+    zmax = group_max<kGroup>(zmax);
+    float zsum = 0.f;
+    for (int x = lane_c; x < m; x += kGroup) zsum += expf(z[x] - zmax);
+    zsum = group_sum<kGroup>(zsum);
+    inv = 1.f / zsum;
+  };
 
   float ak[8], av[8];
 #pragma unroll
@@ -103,6 +108,7 @@ __global__ __launch_bounds__(kBlock) void compress_kernel(const void* __restrict
       load_row8<kInF32>(k, row0 + j + u, lane_c, kr[u]);
       load_row8<kInF32>(v, row0 + j + u, lane_c, vr[u]);
     }
+    if (j == 0) stats();
 #pragma unroll
     for (int u = 0; u < kU; ++u) a[u] = expf(z[j + u] - zmax) * inv;
 #pragma unroll
@@ -114,6 +120,7 @@ __global__ __launch_bounds__(kBlock) void compress_kernel(const void* __restrict
       }
     }
   }
+  if (m < kU) stats();
   for (; j < m; ++j) {
     float kr[8], vr[8];
     load_row8<kInF32>(k, row0 + j, lane_c, kr);
@@ -190,31 +197,49 @@ __global__ __launch_bounds__(kBlock) void compress_long_kernel(const void* __res
     part[1][grp][lane_c * 8 + i] = av[i];
   }
   __syncthreads();
-  if (grp != 0) return;
+  // thread t adds the 16 partials of one output value (K for t < 128, V
+  // otherwise; head column t % 128) in group order and stores it
+  const int kv = threadIdx.x >> 7;
+  const int col = threadIdx.x & (kHeadDim - 1);
+  float x = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float sk = 0.f, sv = 0.f;
-    for (int r = 0; r < kEntriesPerBlock; ++r) {
-      sk += part[0][r][lane_c * 8 + i];
-      sv += part[1][r][lane_c * 8 + i];
-    }
-    ak[i] = sk;
-    av[i] = sv;
-  }
+  for (int r = 0; r < kEntriesPerBlock; ++r) x += part[kv][r][col];
   const size_t entry = size_t(b) * ld_out + e;
-  store_entry<kOut>(k_out, k_scale, entry, lane_c, ak);
-  store_entry<kOut>(v_out, v_scale, entry, lane_c, av);
+  void* out = kv ? v_out : k_out;
+  if constexpr (kOut == CSA_F32) {
+    static_cast<float*>(out)[entry * kHeadDim + col] = x;
+  } else if constexpr (kOut == CSA_BF16) {
+    static_cast<uint16_t*>(out)[entry * kHeadDim + col] = f32_to_bf16(x);
+  } else {
+    // per-entry scale from the max magnitude over the entry's 128 values (two waves)
+    __shared__ float wmax[kBlock / 64];
+    float amax = fabsf(x);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(wmax[2 * kv], wmax[2 * kv + 1]);
+    const float scale = amax > 0.f ? amax / 448.f : 1.f;
+    static_cast<uint8_t*>(out)[entry * kHeadDim + col] = uint8_t(f32_to_e4m3(x / scale));
+    if (col == 0) (kv ? v_scale : k_scale)[entry] = scale;
+  }
 }
 
 template <int kInF32, int kOut>
 hipError_t launch_one(dim3 grid_short, long total, hipStream_t st, const void* k, const void* v, const float* lg, int B,
                       int ne, int ld_in, int m, void* ko, void* vo, float* ks, float* vs, int ld_out) {
-  if (m >= 32)
+  (void)grid_short;
+  if (m >= 32) {
     hipLaunchKernelGGL((compress_long_kernel<kInF32, kOut>), dim3(unsigned(total)), dim3(kBlock), 0, st, k, v, lg, ne,
                        ld_in, m, ko, vo, ks, vs, ld_out);
-  else
-    hipLaunchKernelGGL((compress_kernel<kInF32, kOut>), grid_short, dim3(kBlock), 0, st, k, v, lg, B, ne, ld_in, m, ko,
-                       vo, ks, vs, ld_out);
+  } else {
+    // few entries (decoding): 4 per 64-thread block, so their rows are
+    // fetched by several CUs; otherwise 16 per 256-thread block
+    const int threads = total <= 256 ? 64 : kBlock;
+    const long per = threads / kGroup;
+    hipLaunchKernelGGL((compress_kernel<kInF32, kOut>), dim3(unsigned((total + per - 1) / per)), dim3(threads), 0, st,
+                       k, v, lg, B, ne, ld_in, m, ko, vo, ks, vs, ld_out);
+  }
   return hipGetLastError();
 }
 
