@@ -190,15 +190,20 @@ def add_layer(st, h, prefix, indexer="auto"):
             csa.csa_sparse_attn(c[p + "q"], c[p + "ck"], c[p + "cv"], c[p + "idx"], c[p + "kw"],
                                 c[p + "vw"], c[p + "raw0"], c[p + "pos"], W, ck_scale=c[p + "cks"],
                                 cv_scale=c[p + "cvs"], out=c[p + "out"])
-        fused = indexer == "fused" or (indexer == "auto" and wl.T_q > 1)
+        fused = indexer in ("fused", "auto")
         if fused:
             def f_fused(c):
                 csa.csa_indexer_topk(c[p + "qc"], c[p + "qe"], c[p + "w"], c[p + "kc"], c[p + "ke"],
                                      c[p + "pos"], m, k, c[p + "idx"])
-            # keys once, the 16-bit score keys written and read back, the indices
+            if wl.T_q == 1 and rows <= 128 and wl.cap >= 8192:
+                # decoding: keys once, the fp32 scores written (read back only by the
+                # exact fallback), the indices
+                inter = nvis_sum * 4
+            else:
+                # keys once, the 16-bit score keys written and read back, the indices
+                inter = rows * wl.cap * 2 + nvis_sum * 2
             st.add(Kernel(name("indexer_topk"), f_fused,
-                          B * wl.cap * idx_bytes + rows * wl.cap * 2 + nvis_sum * 2 + rows * k * 4
-                          + rows * wl.H_I * (idx_bytes + 4),
+                          B * wl.cap * idx_bytes + inter + rows * k * 4 + rows * wl.H_I * (idx_bytes + 4),
                           2 * wl.H_I * wl.d_I * nvis_sum, MXFP4_PEAK_TFLOPS, "indexer_topk"))
         else:
             st.add(Kernel(name("indexer_scores"), f_indexer,
@@ -374,9 +379,9 @@ def kernel_source_hash(names):
 
 KERNEL_SOURCES = {
     "indexer_scores": ["indexer.hip", "indexer_core.hpp", "select.hpp", "common.hpp"],
-    "indexer_topk": ["indexer_topk.hip", "indexer_core.hpp", "select.hpp", "common.hpp"],
+    "indexer_topk": ["indexer_topk.hip", "indexer_core.hpp", "split.hpp", "topk.hip", "select.hpp", "common.hpp"],
     "sparse_attn": ["attn.hip", "common.hpp"], "dense_attn": ["attn.hip", "common.hpp"],
-    "topk": ["topk.hip", "select.hpp", "common.hpp"], "compress_kv": ["compress.hip", "common.hpp"]}
+    "topk": ["topk.hip", "split.hpp", "select.hpp", "common.hpp"], "compress_kv": ["compress.hip", "common.hpp"]}
 
 
 def measured_traffic(workload, kernel):

@@ -153,18 +153,23 @@ csa_status_t csa_topk(const float* scores, const int32_t* q_pos0, int32_t B, int
  * ifanr repost, 百萬長上下文; CSA keeps the most relevant k entries,
  * blog.nickys.cn, 三大架构改动 §1 CSA).
  * Result: idx equals, bit for bit, csa_topk(csa_indexer_scores(...)) on the
- * same arguments, for any input values; the fp32 scores are never written.
- * The scoring pass stores 16-bit order-preserving score keys (2 bytes per
- * (query, entry) instead of 4); the selection re-scores only the entries
- * whose 16-bit key ties the k-th one, with the scoring pass's own arithmetic.
+ * same arguments, for any input values.  In general the scoring pass stores
+ * 16-bit order-preserving score keys (2 bytes per (query, entry) instead of
+ * 4) and the selection re-scores only the entries whose 16-bit key ties the
+ * k-th one, with the scoring pass's own arithmetic.  Decoding shapes score
+ * and pre-select each 2048-entry slice in one pass (the fp32 scores go to
+ * the workspace for the exact fallback), then select per row.
  *
  *   q_codes .. q_pos0, B .. m   as csa_indexer_scores (same layouts, limits
  *                               and preconditions)
  *   k         entries to keep; 1 <= k <= 32767 (larger: CSA_ENOTSUP)
  *   idx       [B, T_q, k] int32 (output), as csa_topk
  *   ws, ws_bytes  workspace of csa_workspace_size(CSA_OP_INDEXER_TOPK, B, T_q,
- *             0, 128, cap) = B*T_q*cap*2 bytes (no initial contents needed);
- *             calls that share a workspace must be ordered on one stream.
+ *             0, d_I, cap) bytes (no initial contents needed): B*T_q*cap*2 in
+ *             general; for decoding (T_q == 1, B <= 128, cap >= 8192,
+ *             d_I <= 256) the fp32 scores plus per-slice candidate lists
+ *             (about B*cap*8 bytes).
+ *             Calls that share a workspace must be ordered on one stream.
  * ------------------------------------------------------------------- */
 csa_status_t csa_indexer_topk(const uint8_t* q_codes, const uint8_t* q_e8m0, const float* w,
                               const uint8_t* k_codes, const uint8_t* k_e8m0,
@@ -227,8 +232,9 @@ csa_status_t hca_dense_attn(const void* q, int32_t io_dtype, const void* ck, con
                             void* stream);
 
 /* Workspace bytes a call needs.  n_keys = k + W (CSA) or cap + W (HCA);
- * for CSA_OP_TOPK and CSA_OP_INDEXER_TOPK pass T_q and n_keys = cap.  Returns 0 when none is needed
- * and (size_t)-1 for invalid arguments. */
+ * for CSA_OP_TOPK and CSA_OP_INDEXER_TOPK pass T_q and n_keys = cap (and, for
+ * CSA_OP_INDEXER_TOPK, d = d_I).  Returns 0 when none is needed and
+ * (size_t)-1 for invalid arguments. */
 size_t csa_workspace_size(int32_t op, int32_t B, int32_t T_q, int32_t H, int32_t d,
                           int32_t n_keys);
 

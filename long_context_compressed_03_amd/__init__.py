@@ -163,7 +163,7 @@ def csa_indexer_topk(q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, m, k, idx=None
     if idx is None:
         idx = torch.empty((B, T_q, k), dtype=torch.int32, device=q_codes.device)
     lib = load()
-    ws = _workspace(q_codes.device, lib.csa_workspace_size(CSA_OP_INDEXER_TOPK, B, T_q, 0, 128, cap))
+    ws = _workspace(q_codes.device, lib.csa_workspace_size(CSA_OP_INDEXER_TOPK, B, T_q, 0, 2 * half, cap))
     st = lib.csa_indexer_topk(_ptr(q_codes), _ptr(q_e8m0), _ptr(w), _ptr(k_codes), _ptr(k_e8m0),
                               _ptr(q_pos0), B, T_q, H_I, 2 * half, cap, m, k, _ptr(idx), _ws_ptr(ws),
                               _ws_len(ws), _stream(stream))

@@ -2,7 +2,7 @@
 #include "common.hpp"
 
 size_t csa_attn_workspace_size(long rows, int H, int n_list);
-size_t csa_indexer_topk_workspace_size(long rows, int cap);
+size_t csa_indexer_topk_workspace_size(long rows, int T_q, int d_I, int cap);
 size_t csa_topk_workspace_size(long rows, int cap);
 
 extern "C" size_t csa_workspace_size(int32_t op, int32_t B, int32_t T_q, int32_t H, int32_t d, int32_t n_keys) {
@@ -11,7 +11,7 @@ extern "C" size_t csa_workspace_size(int32_t op, int32_t B, int32_t T_q, int32_t
     case CSA_OP_TOPK:
       return csa_topk_workspace_size(long(B) * T_q, n_keys);
     case CSA_OP_INDEXER_TOPK:
-      return csa_indexer_topk_workspace_size(long(B) * T_q, n_keys);
+      return csa_indexer_topk_workspace_size(long(B) * T_q, T_q, d, n_keys);
     case CSA_OP_SPARSE_ATTN:
     case CSA_OP_DENSE_ATTN:
       if (d != kHeadDim || H < 16 || H > 128 || H % 16 != 0) return size_t(-1);

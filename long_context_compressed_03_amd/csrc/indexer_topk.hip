@@ -34,6 +34,7 @@
 //     e. emission as in csa_topk: bitmaps of "greater" and "equal" entries,
 //        one block scan, ascending output with the lower-index tie rule.
 #include "indexer_core.hpp"
+#include "split.hpp"
 
 namespace {
 
@@ -590,6 +591,119 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const uint16_t* __rest
   }
 }
 
+// Decoding (one query per sequence) with few rows: one block per (sequence,
+// 2048-entry slice).  The block scores its slice exactly as the scoring kernel
+// does (same instruction sequence, so the same bits), stores the fp32 scores
+// for the row pass's fallback, keeps their order-preserving keys in LDS and
+// runs the split path's slice pass on them: the scores are never read back
+// for the common case.
+constexpr int kFusedThreads = 1024;   // 16 waves x 128 entries: the whole slice's keys in flight at once
+
+template <int kHI, int kKS>
+__global__ __launch_bounds__(kFusedThreads) void indexer_slice_kernel(
+    const uint8_t* __restrict__ q_codes, const uint8_t* __restrict__ q_e8m0, const float* __restrict__ w,
+    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ k_e8m0, const int32_t* __restrict__ q_pos0,
+    int d_I, int cap, int m, int k, int G, float* __restrict__ scores, csa_split::SplitWs ws) {
+  using namespace csa_split;
+  constexpr int kFrag = 4;
+  constexpr int kBatch16 = 16 * kFrag;                      // entries per batch of a wave
+  constexpr int kPerWave = kSlice / (kFusedThreads / 64);   // 128 entries per wave
+  constexpr int kNB = kPerWave / kBatch16;                  // batches per wave, all loaded up front
+  __shared__ uint32_t skey[kSlice];
+  __shared__ SliceShared sh;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int col = lane & 15, g = lane >> 4;
+  const int b = blockIdx.y, sl = blockIdx.x;
+  const int nblk = d_I >> 5, row_bytes = d_I >> 1;
+  const int nv = min((q_pos0[b] + 1) / m, cap);
+  if (nv <= k) return;   // the row pass writes this row's output without selection
+  const int base = sl * kSlice;
+  const int n_s = min(kSlice, nv - base);
+  const size_t slot = size_t(b) * G + sl;
+  if (n_s <= 0) {
+    slice_empty(slot, ws);
+    return;
+  }
+  // A operand: tile rows r < kHI are (query, head r); the other rows are zero
+  u32x4 a[kKS];
+  int sa[kKS];
+  csa_ix::load_a<kHI, kKS>(q_codes, q_e8m0, size_t(b) * kHI + col, col < kHI, g, nblk, row_bytes, a, sa);
+  const int rc = 4 * g;            // first C row this lane holds
+  const bool mine = rc < kHI;      // C rows of the query (not of the zero rows)
+  float wv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wv[i] = mine ? w[size_t(b) * kHI + (rc + i) % kHI] : 0.f;
+  const uint8_t* kc_seq = k_codes + size_t(b) * cap * row_bytes;
+  const uint8_t* ke_seq = k_e8m0 + size_t(b) * cap * nblk;
+  const uint32_t c_bytes = uint32_t(cap) * uint32_t(row_bytes);   // < 2^31 (argument check)
+  const uint32_t e_bytes = uint32_t(cap) * uint32_t(nblk);
+  const __amdgpu_buffer_rsrc_t rc_k = csa_ix::seq_rsrc(kc_seq, c_bytes);
+  const __amdgpu_buffer_rsrc_t re_k = csa_ix::seq_rsrc(ke_seq, e_bytes);
+  float* srow = scores + size_t(b) * cap;
+
+  const int e_wave0 = base + wid * kPerWave;
+  u32x4 bk[kNB][kFrag][kKS];
+  int sb[kNB][kFrag][kKS];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+    for (int f = 0; f < kFrag; ++f) {
+      const int e = e_wave0 + nb * kBatch16 + f * 16 + col;
+      csa_ix::load_b<kKS, true>(rc_k, re_k, c_bytes, e_bytes, e, e < nv, g, nblk, row_bytes, bk[nb][f], sb[nb][f]);
+    }
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    v4f acc[kFrag];
+#pragma unroll
+    for (int f = 0; f < kFrag; ++f) {
+      acc[f] = csa_ix::mfma_fp4(a[0], sa[0], bk[nb][f][0], sb[nb][f][0], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int ks = 1; ks < kKS; ++ks)
+        acc[f] = csa_ix::mfma_fp4(a[ks], sa[ks], bk[nb][f][ks], sb[nb][f][ks], acc[f]);
+    }
+#pragma unroll
+    for (int f = 0; f < kFrag; ++f) {
+      bool writer;
+      const float p = csa_ix::head_sum<kHI>(acc[f], wv, g, writer);
+      const int e = e_wave0 + nb * kBatch16 + f * 16 + col;
+      if (writer && mine) {
+        const bool vis = e < nv;
+        skey[e - base] = vis ? ordered_key(p) : 0u;
+        if (vis) srow[e] = p;
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t key[kSlice / kFusedThreads];
+#pragma unroll
+  for (int j = 0; j < kSlice / kFusedThreads; ++j) key[j] = skey[j * kFusedThreads + threadIdx.x];
+  slice_finish<kFusedThreads>(key, base, n_s, nv, k, slot, ws, sh);
+}
+
+template <int kHI>
+hipError_t launch_indexer_slice_h(int ks, int B, hipStream_t st, const uint8_t* qc, const uint8_t* qe, const float* w,
+                                  const uint8_t* kc, const uint8_t* ke, const int32_t* pos, int d_I, int cap, int m,
+                                  int k, float* scores, const csa_split::SplitWs& sw) {
+  const int G = csa_split::n_slices(cap);
+  const dim3 grid{unsigned(G), unsigned(B), 1u};
+  const dim3 block(kFusedThreads);
+  if (ks == 1)
+    hipLaunchKernelGGL((indexer_slice_kernel<kHI, 1>), grid, block, 0, st, qc, qe, w, kc, ke, pos, d_I, cap, m, k, G,
+                       scores, sw);
+  else
+    hipLaunchKernelGGL((indexer_slice_kernel<kHI, 2>), grid, block, 0, st, qc, qe, w, kc, ke, pos, d_I, cap, m, k, G,
+                       scores, sw);
+  return hipGetLastError();
+}
+
+// Decoding with few long rows takes the split path (fp32 scores, then the
+// slice results, in the workspace); d_I <= 256 keeps a slice's key operands
+// in registers.
+bool use_fused_split(long rows, int T_q, int d_I, int cap) {
+  return T_q == 1 && d_I <= 256 && csa_split::use_split(rows, cap);
+}
+size_t split_scores_bytes(long rows, int cap) { return (size_t(rows) * size_t(cap) * 4u + 255u) / 256u * 256u; }
+
 template <int kHI, int kKS, int kJ>
 hipError_t launch_select_j(long rows, hipStream_t st, const uint16_t* key16, const uint8_t* qc, const uint8_t* qe,
                            const float* w, const uint8_t* kc, const uint8_t* ke, const int32_t* pos, int T_q,
@@ -632,7 +746,10 @@ hipError_t launch_select_h(int ks, long rows, hipStream_t st, const uint16_t* ke
 }  // namespace
 
 // Workspace of csa_indexer_topk: the 16-bit keys of every (query, entry).
-size_t csa_indexer_topk_workspace_size(long rows, int cap) { return size_t(rows) * size_t(cap) * 2u; }
+size_t csa_indexer_topk_workspace_size(long rows, int T_q, int d_I, int cap) {
+  if (use_fused_split(rows, T_q, d_I, cap)) return split_scores_bytes(rows, cap) + csa_split::split_ws_bytes(rows, cap);
+  return size_t(rows) * size_t(cap) * 2u;
+}
 
 extern "C" csa_status_t csa_indexer_topk(const uint8_t* q_codes, const uint8_t* q_e8m0, const float* w,
                                          const uint8_t* k_codes, const uint8_t* k_e8m0, const int32_t* q_pos0,
@@ -646,9 +763,24 @@ extern "C" csa_status_t csa_indexer_topk(const uint8_t* q_codes, const uint8_t* 
   const long rows = long(B) * T_q;
   if (rows == 0) return CSA_OK;
   if (rows > 0x7FFFFFFFL) return CSA_ENOTSUP;
-  const size_t need = csa_indexer_topk_workspace_size(rows, cap);
+  const size_t need = csa_indexer_topk_workspace_size(rows, T_q, d_I, cap);
   if (need > 0 && (!ws || ws_bytes < need)) return CSA_EWORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const int ks = (d_I + 127) / 128;
+  if (use_fused_split(rows, T_q, d_I, cap)) {
+    float* scores = static_cast<float*>(ws);
+    const csa_split::SplitWs sw =
+        csa_split::split_ws(static_cast<char*>(ws) + split_scores_bytes(rows, cap), rows, cap);
+    hipError_t e;
+    switch (H_I) {
+      case 4: e = launch_indexer_slice_h<4>(ks, B, st, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, d_I, cap, m, k, scores, sw); break;
+      case 8: e = launch_indexer_slice_h<8>(ks, B, st, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, d_I, cap, m, k, scores, sw); break;
+      default: e = launch_indexer_slice_h<16>(ks, B, st, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, d_I, cap, m, k, scores, sw); break;
+    }
+    if (e != hipSuccess) return CSA_EHIP;
+    e = csa_split::launch_topk_split_rows(rows, st, scores, q_pos0, 1, cap, m, k, idx, sw);
+    return e == hipSuccess ? CSA_OK : CSA_EHIP;
+  }
   uint16_t* key16 = static_cast<uint16_t*>(ws);
   hipError_t err = hipSuccess;
   if (cap > 0) {
@@ -656,7 +788,6 @@ extern "C" csa_status_t csa_indexer_topk(const uint8_t* q_codes, const uint8_t* 
                                                  m, key16, st);
     if (err != hipSuccess) return CSA_EHIP;
   }
-  const int ks = (d_I + 127) / 128;
   switch (H_I) {
     case 4: err = launch_select_h<4>(ks, rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_q, d_I, cap, m, k, idx); break;
     case 8: err = launch_select_h<8>(ks, rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_q, d_I, cap, m, k, idx); break;

@@ -1,0 +1,166 @@
+// The split top-k path for few long rows, shared by csa_topk (scores given)
+// and csa_indexer_topk (scores computed in the same kernel as the slice
+// pass): per 2048-entry slice, a local bound and the compacted candidates;
+// then one block per row selects among them (launched by
+// launch_topk_split_rows, defined with that kernel).
+//
+// Slice pass (exact for any input): with the slice's share q_s =
+// ceil(k n_s / nv) of the row's nv visible entries, v_s is the lower edge of
+// the 14-bit key bucket that holds the slice's c_s-th largest key, c_s =
+// min(n_s, kLocal q_s) (1 = every key when the window of kWindow buckets below
+// the slice's top bucket holds fewer than c_s keys); the slice stores every
+// key >= v_s with its index, in index order.  The shares sum to at least k,
+// so the candidates hold at least k keys, and they hold every key of the row
+// >= max v_s: when the selected keys are all >= max v_s the selection among
+// the candidates is the row's (the row kernel checks it and otherwise falls
+// back to the one-block algorithm over the row).
+#pragma once
+#include "select.hpp"
+
+namespace csa_split {
+
+constexpr int kSlice = 2048;                   // keys per slice
+constexpr int kSliceThreads = 256;             // slice pass over given scores
+constexpr int kSlicePer = kSlice / kSliceThreads;
+constexpr int kSliceCap = 512;                 // candidates kept per slice
+constexpr int kWindow = 1024;                  // buckets below the slice's top bucket
+constexpr int kBucketShift = 18;               // 14-bit buckets
+constexpr uint32_t kLocal = 3;                 // a slice keeps about kLocal times its share of k
+constexpr int kSplitMaxRows = 128;
+constexpr int kSplitMinCap = 8192;
+constexpr int kMaxSlices = 1024;
+
+inline int n_slices(int cap) { return (cap + kSlice - 1) / kSlice; }
+inline bool use_split(long rows, int cap) {
+  return rows <= kSplitMaxRows && cap >= kSplitMinCap && n_slices(cap) <= kMaxSlices;
+}
+
+// Workspace of the split path: bounds [rows][G], counts [rows][G], candidate
+// keys and indices [rows][G][kSliceCap].
+struct SplitWs {
+  uint32_t* bound;
+  uint32_t* count;
+  uint32_t* key;
+  int32_t* idx;
+};
+inline size_t split_ws_bytes(long rows, int cap) {
+  return size_t(rows) * n_slices(cap) * (2 * sizeof(uint32_t) + kSliceCap * (sizeof(uint32_t) + sizeof(int32_t)));
+}
+inline SplitWs split_ws(void* ws, long rows, int cap) {
+  const size_t n = size_t(rows) * n_slices(cap);
+  SplitWs w;
+  w.bound = static_cast<uint32_t*>(ws);
+  w.count = w.bound + n;
+  w.key = w.count + n;
+  w.idx = reinterpret_cast<int32_t*>(w.key + n * kSliceCap);
+  return w;
+}
+
+struct SliceShared {
+  uint32_t hist[kWindow];
+  uint32_t smax[16];
+  uint32_t smem[32];
+  uint32_t wc[32];
+  uint32_t v;
+};
+
+// The slice pass on keys already in registers, by a block of kT threads
+// (256 or 1024): thread t holds the keys of indices base + j*kT + t (0 for
+// entries past the visible count); n_s > 0 visible entries in the slice,
+// nv > k in the row.  Writes count[slot], bound[slot] and the slot's
+// candidates.  Every thread of the block calls it.
+template <int kT>
+CSA_DEV void slice_finish(const uint32_t (&key)[kSlice / kT], int base, int n_s, int nv, int k, size_t slot,
+                          const SplitWs& ws, SliceShared& sh) {
+  constexpr int kP = kSlice / kT;       // keys per thread
+  constexpr int kW = kT / 64;           // waves
+  constexpr int kBpt = kWindow / kT;    // window buckets per thread
+  static_assert(kP * kW == 32, "32 ballot groups per slice");
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint32_t quota = uint32_t((uint64_t(k) * uint32_t(n_s) + uint32_t(nv) - 1u) / uint32_t(nv));
+  const uint32_t want = min(uint32_t(n_s), kLocal * quota);
+#pragma unroll
+  for (int i = 0; i < kBpt; ++i) sh.hist[tid * kBpt + i] = 0u;
+  uint32_t mx = 0u;
+#pragma unroll
+  for (int j = 0; j < kP; ++j) mx = max(mx, key[j]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, uint32_t(__shfl_xor(int(mx), o)));
+  if (lane == 0) sh.smax[w] = mx;
+  __syncthreads();
+  mx = sh.smax[0];
+#pragma unroll
+  for (int x = 1; x < kW; ++x) mx = max(mx, sh.smax[x]);
+  const int top = int(mx >> kBucketShift);
+#pragma unroll
+  for (int j = 0; j < kP; ++j) {
+    const int rel = top - int(key[j] >> kBucketShift);
+    if (key[j] && rel < kWindow) atomicAdd(&sh.hist[rel], 1u);
+  }
+  __syncthreads();
+  uint32_t c[kBpt];                     // buckets top - kBpt t .. (relative kBpt t ..)
+  uint32_t sum = 0u;
+#pragma unroll
+  for (int i = 0; i < kBpt; ++i) {
+    c[i] = sh.hist[tid * kBpt + i];
+    sum += c[i];
+  }
+  uint32_t tot;
+  const uint32_t excl = block_exclusive_scan(sum, sh.smem, &tot);
+  if (tot < want) {
+    if (tid == 0) sh.v = 1u;
+  } else if (excl < want && want <= excl + sum) {
+    uint32_t run = excl;
+    int r = kBpt * tid;
+#pragma unroll
+    for (int y = 0; y < kBpt; ++y) {
+      run += c[y];
+      if (run >= want) { r = kBpt * tid + y; break; }
+    }
+    sh.v = uint32_t(top - r) << kBucketShift;
+  }
+  __syncthreads();
+  const uint32_t lo = sh.v;
+  uint64_t bal[kP];
+#pragma unroll
+  for (int j = 0; j < kP; ++j) {
+    bal[j] = __ballot(key[j] != 0u && key[j] >= lo);
+    if (lane == 0) sh.wc[j * kW + w] = uint32_t(__popcll(bal[j]));
+  }
+  __syncthreads();
+  // exclusive offsets of the 32 (key j, wave) groups in index order
+  const uint32_t cw = lane < 32 ? sh.wc[lane] : 0u;
+  const uint32_t incl = wave_inclusive_scan(cw);
+  const uint32_t ex = incl - cw;
+  const uint64_t below = (uint64_t(1) << lane) - 1u;
+  uint32_t* const ck = ws.key + slot * kSliceCap;
+  int32_t* const ci = ws.idx + slot * kSliceCap;
+#pragma unroll
+  for (int j = 0; j < kP; ++j) {
+    const uint32_t pos = uint32_t(__shfl(int(ex), j * kW + w)) + uint32_t(__popcll(bal[j] & below));
+    if (((bal[j] >> lane) & 1u) && pos < uint32_t(kSliceCap)) {
+      ck[pos] = key[j];
+      ci[pos] = base + j * kT + tid;
+    }
+  }
+  const uint32_t total = uint32_t(__shfl(int(incl), 31));   // all lanes take part
+  if (tid == 0) {
+    ws.count[slot] = total;
+    ws.bound[slot] = lo;
+  }
+}
+
+// Empty slice (no visible entry): no candidates, no bound.
+CSA_DEV void slice_empty(size_t slot, const SplitWs& ws) {
+  if (threadIdx.x == 0) {
+    ws.count[slot] = 0u;
+    ws.bound[slot] = 0u;
+  }
+}
+
+// The row pass of the split path (one 1024-thread block per row) over the
+// slice results in `ws`; `scores` [rows][cap] serve its fallback.
+hipError_t launch_topk_split_rows(long rows, hipStream_t st, const float* scores, const int32_t* q_pos0, int T_q,
+                                  int cap, int m, int k, int32_t* idx, const SplitWs& ws);
+
+}  // namespace csa_split

@@ -50,18 +50,18 @@
 // Each thread holds 16 keys per register tile (not 32), so that no kernel
 // here needs scratch memory: a kernel with scratch waits several
 // microseconds longer for its dispatch.
-#include "select.hpp"
+#include "split.hpp"
 
 namespace {
 
 using namespace csa_sel;
+using namespace csa_split;
 
 constexpr int kPer = 4;                        // rounds of 4 keys per thread
 constexpr int kRound = kThreads * 4;           // 4096 consecutive keys per round
 constexpr int kSuper = kRound * kPer;          // 16384 keys in registers
 constexpr int kWords = kSuper / 32;            // bitmap words per super-tile
-constexpr int kBucketShift = 18;               // 14-bit buckets
-constexpr int kBuckets = 1 << (32 - kBucketShift);
+constexpr int kBuckets = 1 << (32 - kBucketShift);   // 14-bit buckets
 constexpr int kCand = 4096;                    // capacity of the threshold-bucket list
 constexpr int kRankMax = 1024;                 // lists up to this size are ranked one entry per lane
 
@@ -75,19 +75,10 @@ struct Shared {
   Sel sel;
 };
 
-// split path
-constexpr int kSlice = 2048;                   // keys per slice
-constexpr int kSliceThreads = 256;
-constexpr int kSlicePer = kSlice / kSliceThreads;
-constexpr int kSliceCap = 512;                 // candidates kept per slice
-constexpr int kWindow = 1024;                  // buckets below the slice's top bucket
-constexpr uint32_t kLocal = 3;                 // a slice keeps about kLocal times its share of k
+// split path: the row pass
 constexpr int kList = 8192;                    // candidates per row held in LDS
 constexpr int kListBits = 9;                   // list histogram: 512 buckets over [lo, top]
 constexpr int kListBuckets = 1 << kListBits;
-constexpr int kSplitMaxRows = 128;
-constexpr int kSplitMinCap = 8192;
-constexpr int kMaxSlices = 1024;
 constexpr int kPreLoads = 8;                   // candidate entries per lane loaded with the counts
 
 struct ListShared {
@@ -107,32 +98,6 @@ union RowShared {
   Shared full;
   ListShared list;
 };
-
-int n_slices(int cap) { return (cap + kSlice - 1) / kSlice; }
-bool use_split(long rows, int cap) {
-  return rows <= kSplitMaxRows && cap >= kSplitMinCap && n_slices(cap) <= kMaxSlices;
-}
-
-// Workspace of the split path: bounds [rows][G], counts [rows][G], candidate
-// keys and indices [rows][G][kSliceCap].
-struct SplitWs {
-  uint32_t* bound;
-  uint32_t* count;
-  uint32_t* key;
-  int32_t* idx;
-};
-size_t split_ws_bytes(long rows, int cap) {
-  return size_t(rows) * n_slices(cap) * (2 * sizeof(uint32_t) + kSliceCap * (sizeof(uint32_t) + sizeof(int32_t)));
-}
-SplitWs split_ws(void* ws, long rows, int cap) {
-  const size_t n = size_t(rows) * n_slices(cap);
-  SplitWs w;
-  w.bound = static_cast<uint32_t*>(ws);
-  w.count = w.bound + n;
-  w.key = w.count + n;
-  w.idx = reinterpret_cast<int32_t*>(w.key + n * kSliceCap);
-  return w;
-}
 
 CSA_DEV int visible_entries(const int32_t* q_pos0, int T_q, int row, int cap, int m) {
   const int b = row / T_q;
@@ -181,12 +146,8 @@ CSA_DEV void load_slice(const float* __restrict__ src, int base, int n_load, flo
 __global__ __launch_bounds__(kSliceThreads) void slice_select_kernel(const float* __restrict__ scores,
                                                                      const int32_t* __restrict__ q_pos0, int T_q,
                                                                      int cap, int m, int k, int G, SplitWs ws) {
-  __shared__ __attribute__((aligned(16))) uint32_t hist[kWindow];
-  __shared__ uint32_t smem[32];
-  __shared__ uint32_t wc[kSlicePer * 4];
-  __shared__ uint32_t v_sh;
+  __shared__ SliceShared sh;
   const int row = blockIdx.y, sl = blockIdx.x, tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
   const int base = sl * kSlice;
   // the scores load alongside the query position (they do not depend on it)
   float v[kSlicePer];
@@ -197,78 +158,13 @@ __global__ __launch_bounds__(kSliceThreads) void slice_select_kernel(const float
   const int n_s = min(kSlice, nv - base);
   const size_t slot = size_t(row) * G + sl;
   if (n_s <= 0) {
-    if (tid == 0) {
-      ws.count[slot] = 0u;
-      ws.bound[slot] = 0u;
-    }
+    slice_empty(slot, ws);
     return;
   }
-  const uint32_t quota = uint32_t((uint64_t(k) * uint32_t(n_s) + uint32_t(nv) - 1u) / uint32_t(nv));
-  const uint32_t want = min(uint32_t(n_s), kLocal * quota);
   uint32_t key[kSlicePer];
 #pragma unroll
   for (int j = 0; j < kSlicePer; ++j) key[j] = j * kSliceThreads + tid < n_s ? ordered_key(v[j]) : 0u;
-  reinterpret_cast<u32x4*>(hist)[tid] = u32x4{0u, 0u, 0u, 0u};
-  uint32_t mx = 0u;
-#pragma unroll
-  for (int j = 0; j < kSlicePer; ++j) mx = max(mx, key[j]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = max(mx, uint32_t(__shfl_xor(int(mx), o)));
-  if (lane == 0) smem[w] = mx;
-  __syncthreads();
-  mx = max(max(smem[0], smem[1]), max(smem[2], smem[3]));
-  const int top = int(mx >> kBucketShift);
-#pragma unroll
-  for (int j = 0; j < kSlicePer; ++j) {
-    const int rel = top - int(key[j] >> kBucketShift);
-    if (key[j] && rel < kWindow) atomicAdd(&hist[rel], 1u);
-  }
-  __syncthreads();
-  const u32x4 c = reinterpret_cast<const u32x4*>(hist)[tid];   // buckets top-4t .. top-4t-3
-  const uint32_t sum = c[0] + c[1] + c[2] + c[3];
-  uint32_t tot;
-  const uint32_t excl = block_exclusive_scan(sum, smem + 8, &tot);
-  if (tot < want) {
-    if (tid == 0) v_sh = 1u;
-  } else if (excl < want && want <= excl + sum) {
-    uint32_t run = excl;
-    int r = 4 * tid;
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      run += c[y];
-      if (run >= want) { r = 4 * tid + y; break; }
-    }
-    v_sh = uint32_t(top - r) << kBucketShift;
-  }
-  __syncthreads();
-  const uint32_t lo = v_sh;
-  uint64_t bal[kSlicePer];
-#pragma unroll
-  for (int j = 0; j < kSlicePer; ++j) {
-    bal[j] = __ballot(key[j] != 0u && key[j] >= lo);
-    if (lane == 0) wc[j * 4 + w] = uint32_t(__popcll(bal[j]));
-  }
-  __syncthreads();
-  // exclusive offsets of the 32 (key j, wave) groups in index order
-  const uint32_t cw = lane < kSlicePer * 4 ? wc[lane] : 0u;
-  const uint32_t incl = wave_inclusive_scan(cw);
-  const uint32_t ex = incl - cw;
-  const uint64_t below = (uint64_t(1) << lane) - 1u;
-  uint32_t* const ck = ws.key + slot * kSliceCap;
-  int32_t* const ci = ws.idx + slot * kSliceCap;
-#pragma unroll
-  for (int j = 0; j < kSlicePer; ++j) {
-    const uint32_t pos = uint32_t(__shfl(int(ex), j * 4 + w)) + uint32_t(__popcll(bal[j] & below));
-    if (((bal[j] >> lane) & 1u) && pos < uint32_t(kSliceCap)) {
-      ck[pos] = key[j];
-      ci[pos] = base + j * kSliceThreads + tid;
-    }
-  }
-  const uint32_t total = uint32_t(__shfl(int(incl), kSlicePer * 4 - 1));   // all lanes take part
-  if (tid == 0) {
-    ws.count[slot] = total;
-    ws.bound[slot] = lo;
-  }
+  slice_finish<kSliceThreads>(key, base, n_s, nv, k, slot, ws, sh);
 }
 
 // Pass c, gathering: the row's candidates into the LDS list in index order.
@@ -677,18 +573,25 @@ hipError_t launch_topk(long rows, hipStream_t st, const float* scores, const int
                        T_q, cap, m, k, idx, SplitWs{}, 0);
     return hipGetLastError();
   }
-  hipError_t e = set_lds_limit<true>();
-  if (e != hipSuccess) return e;
   const int G = n_slices(cap);
   const SplitWs w = split_ws(ws, rows, cap);
   const dim3 grid{unsigned(G), unsigned(rows), 1u};
   hipLaunchKernelGGL(slice_select_kernel, grid, dim3(kSliceThreads), 0, st, scores, q_pos0, T_q, cap, m, k, G, w);
-  hipLaunchKernelGGL(topk_kernel<true>, dim3(unsigned(rows)), dim3(kThreads), sizeof(RowShared), st, scores, q_pos0,
-                     T_q, cap, m, k, idx, w, G);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_topk_split_rows(rows, st, scores, q_pos0, T_q, cap, m, k, idx, w);
 }
 
 }  // namespace
+
+hipError_t csa_split::launch_topk_split_rows(long rows, hipStream_t st, const float* scores, const int32_t* q_pos0,
+                                             int T_q, int cap, int m, int k, int32_t* idx, const SplitWs& ws) {
+  hipError_t e = set_lds_limit<true>();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_kernel<true>, dim3(unsigned(rows)), dim3(kThreads), sizeof(RowShared), st, scores, q_pos0,
+                     T_q, cap, m, k, idx, ws, n_slices(cap));
+  return hipGetLastError();
+}
 
 extern "C" csa_status_t csa_topk(const float* scores, const int32_t* q_pos0, int32_t B, int32_t T_q, int32_t cap,
                                  int32_t m, int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {

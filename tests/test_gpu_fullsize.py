@@ -4,7 +4,7 @@ Each test builds one workload exactly as bench.py does (same seeded inputs, same
 same order, same shapes), runs one step, and checks sampled outputs against the oracle,
 which can afford a few rows at these sizes:
   * pooled entries written by the step: within one storage unit of the exact pool;
-  * indexer scores of sampled rows (unfused decode): bit-exact;
+  * indexer scores of sampled rows (decode with separate indexer and top-k calls): bit-exact;
   * top-k indices of sampled rows (unfused and fused): bit-exact;
   * attention of sampled rows over the cache as the step left it: max-abs 2e-2 on top of
     the bf16 output's own half-unit rounding.
@@ -35,14 +35,14 @@ def csa():
     return m
 
 
-def run_workload(name):
+def run_workload(name, indexer="auto"):
     """Host inputs and the device state after one step of bench workload `name`."""
     parts = bench.LAYERS[name]
     wls = workloads()
     hosts = [(prefix, bench.host_layer(wls[w])) for prefix, w in parts]
     st = bench.Step(name, 0)
     for prefix, hl in hosts:
-        bench.add_layer(st, hl, prefix)
+        bench.add_layer(st, hl, prefix, indexer=indexer)
     dev = {}
     for prefix, hl in hosts:
         dev.update(bench.device_layer(hl, prefix))
@@ -139,9 +139,18 @@ def check_hca_rows(hl, dev, p, rows):
 def test_csa_decode_128k(csa):
     hosts, dev, st = run_workload("csa_decode_128k")
     (p, hl), = hosts
-    say("csa_decode_128k: pooled entry, scores, top-k and attention of sampled rows")
+    assert "indexer_topk" in st.order
+    say("csa_decode_128k: pooled entry, fused top-k and attention of sampled rows")
     check_compress(hl, dev, p, [0])
-    check_csa_rows(hl, dev, p, [(0, 0), (7, 0), (15, 0)], unfused=True)
+    check_csa_rows(hl, dev, p, [(0, 0), (7, 0), (15, 0)], unfused=False)
+
+
+def test_csa_decode_128k_unfused(csa):
+    hosts, dev, st = run_workload("csa_decode_128k", indexer="unfused")
+    (p, hl), = hosts
+    assert "indexer_scores" in st.order and "topk" in st.order
+    say("csa_decode_128k, separate calls: scores, top-k and attention of sampled rows")
+    check_csa_rows(hl, dev, p, [(0, 0), (9, 0)], unfused=True)
 
 
 def test_hca_decode_1m(csa):
@@ -166,7 +175,7 @@ def test_layer_pair_1m(csa):
     layers = dict(hosts)
     say("pair_1m: every layer's pooled entries and sampled rows")
     check_compress(layers["csa_decode."], dev, "csa_decode.", [0])
-    check_csa_rows(layers["csa_decode."], dev, "csa_decode.", [(3, 0)], unfused=True)
+    check_csa_rows(layers["csa_decode."], dev, "csa_decode.", [(3, 0)], unfused=False)
     check_compress(layers["csa_chunk."], dev, "csa_chunk.", [0, 511])
     check_csa_rows(layers["csa_chunk."], dev, "csa_chunk.", [(0, 0), (0, 2047)], unfused=False)
     check_compress(layers["hca_decode."], dev, "hca_decode.", [0])

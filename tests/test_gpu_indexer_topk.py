@@ -49,6 +49,10 @@ FUSED_CASES = [
     (2, 33, 5000, 8, 128, 4, 100, [19900, 300], False),            # ragged chunk rows; early rows < k
     (1, 4, 20000, 4, 64, 4, 500, [79990], True),                   # threshold among exact ties
     (1, 3, 3000, 16, 256, 2, 200, [5990], False),                  # 16 heads, two contraction steps
+    # decoding rows long enough for the per-slice split path
+    (2, 1, 9000, 4, 64, 4, 300, [35999, 20000], False),            # 4 heads, half-width vectors, partial slices
+    (2, 1, 10000, 16, 256, 2, 500, [19999, 15000], False),         # 16 heads, two contraction steps
+    (1, 1, 16384, 4, 64, 4, 500, [65535], True),                   # exact ties around the threshold
 ]
 
 
@@ -88,6 +92,32 @@ def test_fused_crowded_and_whole_buckets(csa):
     assert np.all(s[0, 0] == 0) and np.sum(s[0, 1] == 256.0) == k
     ref = topk(s.astype(np.float32), pos, m, k)
     assert np.array_equal(ref[0, 0], np.arange(k)) and np.array_equal(ref[0, 1], hot)
+    got = _fused(csa, x2, pos, m, k)
+    assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
+
+
+def test_fused_decode_crowded_rows(csa):
+    """Decoding rows on the split path: sequence 0 has a zero query (every entry ties
+    at 0: the slice buffers overflow and the row takes the one-block fallback),
+    sequence 1 has exactly k entries scoring above the rest (all in a few slices:
+    the candidate check fails and the row falls back), sequence 2 is random."""
+    say("indexer_topk decode crowded rows")
+    B, T, cap, H_I, d_I, m, k = 3, 1, 12000, 4, 64, 4, 300
+    x = indexer_inputs(B, T, cap, H_I, d_I, seed=78)
+    x["q_codes"][0] = 0
+    x["q_codes"][1] = 0x22
+    x["q_e8m0"][1] = 127
+    x["w"][1] = 1.0
+    kc = x["k_codes"].copy()
+    ke = x["k_e8m0"].copy()
+    kc[1] = 0
+    kc[1, 2000:2000 + k] = 0x22                              # k hot entries in one slice
+    ke[1] = 127
+    x2 = dict(x, k_codes=kc, k_e8m0=ke)
+    pos = np.array([4 * cap - 1] * B, np.int32)
+    s = indexer_scores(x2["q_codes"], x2["q_e8m0"], x2["w"], kc, ke, pos, m)
+    ref = topk(s.astype(np.float32), pos, m, k)
+    assert np.array_equal(ref[0, 0], np.arange(k)) and np.array_equal(ref[1, 0], np.arange(2000, 2000 + k))
     got = _fused(csa, x2, pos, m, k)
     assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
 
