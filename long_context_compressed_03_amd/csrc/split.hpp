@@ -7,13 +7,17 @@
 // Slice pass (exact for any input): with the slice's share q_s =
 // ceil(k n_s / nv) of the row's nv visible entries, v_s is the lower edge of
 // the 14-bit key bucket that holds the slice's c_s-th largest key, c_s =
-// min(n_s, kLocal q_s) (1 = every key when the window of kWindow buckets below
-// the slice's top bucket holds fewer than c_s keys); the slice stores every
-// key >= v_s with its index, in index order.  The shares sum to at least k,
-// so the candidates hold at least k keys, and they hold every key of the row
-// >= max v_s: when the selected keys are all >= max v_s the selection among
-// the candidates is the row's (the row kernel checks it and otherwise falls
-// back to the one-block algorithm over the row).
+// min(n_s, q_s + 6 sqrt(q_s) + 6) (1 = every key when the window of kWindow
+// buckets below the slice's top bucket holds fewer than c_s keys); the slice
+// stores every key >= v_s with its index, in index order.  The shares sum to
+// at least k, so the candidates hold at least k keys, and they hold every key
+// of the row >= max v_s: when the selected keys are all >= max v_s the
+// selection among the candidates is the row's (the row kernel checks it and
+// otherwise falls back to the one-block algorithm over the row).  The margin
+// over the share follows the spread of a Poisson count with mean q_s (about
+// six standard deviations): with scores spread evenly over the slices the
+// check almost never fails; inputs that crowd the top keys into a few slices
+// take the fallback.
 #pragma once
 #include "select.hpp"
 
@@ -25,7 +29,6 @@ constexpr int kSlicePer = kSlice / kSliceThreads;
 constexpr int kSliceCap = 512;                 // candidates kept per slice
 constexpr int kWindow = 1024;                  // buckets below the slice's top bucket
 constexpr int kBucketShift = 18;               // 14-bit buckets
-constexpr uint32_t kLocal = 3;                 // a slice keeps about kLocal times its share of k
 constexpr int kSplitMaxRows = 128;
 constexpr int kSplitMinCap = 8192;
 constexpr int kMaxSlices = 1024;
@@ -78,7 +81,7 @@ CSA_DEV void slice_finish(const uint32_t (&key)[kSlice / kT], int base, int n_s,
   static_assert(kP * kW == 32, "32 ballot groups per slice");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const uint32_t quota = uint32_t((uint64_t(k) * uint32_t(n_s) + uint32_t(nv) - 1u) / uint32_t(nv));
-  const uint32_t want = min(uint32_t(n_s), kLocal * quota);
+  const uint32_t want = min(uint32_t(n_s), quota + uint32_t(6.f * sqrtf(float(quota))) + 6u);
 #pragma unroll
   for (int i = 0; i < kBpt; ++i) sh.hist[tid * kBpt + i] = 0u;
   uint32_t mx = 0u;

@@ -36,7 +36,7 @@
 // launches, exact for any input:
 //  a. per 2048-key slice s (n_s of the row's nv keys), one block finds a
 //     local bound v_s: the lower edge of the 14-bit bucket that holds the
-//     slice's c_s-th largest key, c_s = min(n_s, 3 q_s) with the slice's
+//     slice's c_s-th largest key, c_s = min(n_s, q_s + 6 sqrt(q_s) + 6), with the slice's
 //     share q_s = ceil(k n_s / nv); it stores every key >= v_s, with its
 //     index, in index order.  The shares sum to at least k, so the candidate
 //     set C holds at least k keys;
@@ -44,7 +44,7 @@
 //     the bucket of the k-th largest, whose keys are ranked exactly; the list
 //     is emitted in order.  C holds every key of the row >= max v_s, so when
 //     the selected keys are all >= max v_s the result is the row's (which
-//     fails only if one slice holds about three times its share of the top k,
+//     fails only if one slice holds far more than its share of the top k,
 //     or the ties crowd a slice buffer or the list); otherwise the row
 //     continues with the one-block algorithm above.
 // Each thread holds 16 keys per register tile (not 32), so that no kernel
@@ -137,7 +137,7 @@ CSA_DEV void load_slice(const float* __restrict__ src, int base, int n_load, flo
 }
 
 // Pass a, one block per slice: v_s = the lower edge of the 14-bit bucket
-// that holds the slice's c_s-th largest key, c_s = min(n_s, kLocal * q_s)
+// that holds the slice's c_s-th largest key, c_s = min(n_s, q_s + 6 sqrt(q_s) + 6)
 // with q_s = ceil(k n_s / nv) (1 = every key when the window below the top
 // bucket holds fewer than c_s keys); then the slice's keys >= v_s and their
 // indices, in index order, into its buffer (at most kSliceCap stored;
