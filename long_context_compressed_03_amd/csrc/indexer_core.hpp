@@ -216,17 +216,16 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
     const int e = e_wave0 + f * 16 + col;
     load_b<kKS, kStream>(rc, re, c_bytes, e_bytes, e, e < nv_max, g, nblk, row_bytes, bk[f], sb[f]);
   }
-  for (int e_frag0 = e_wave0; e_frag0 < e_wave1; e_frag0 += 16 * kFrag) {
-    // the next batch loads while this one computes (a streaming wave owns a
-    // single batch: nothing to prefetch)
-    u32x4 bn[kFrag][kKS];
-    int sn[kFrag][kKS];
-    if constexpr (!kStream) {
+  // One batch: the keys of the batch after it load into (nk, ns) while this
+  // one computes from (ck, cs); two buffers swap roles from batch to batch (no
+  // register copies).  A streaming wave owns a single batch: nothing to prefetch.
+  auto batch = [&](auto& ck, auto& cs, auto& nk, auto& ns, int e_frag0, bool prefetch) {
+    if (prefetch) {
       const bool more = e_frag0 + 16 * kFrag < e_wave1;
 #pragma unroll
       for (int f = 0; f < kFrag; ++f) {
         const int e = e_frag0 + 16 * kFrag + f * 16 + col;
-        load_b<kKS, kStream>(rc, re, c_bytes, e_bytes, e, more && e < nv_max, g, nblk, row_bytes, bn[f], sn[f]);
+        load_b<kKS, kStream>(rc, re, c_bytes, e_bytes, e, more && e < nv_max, g, nblk, row_bytes, nk[f], ns[f]);
       }
     }
     // every MFMA of the batch first, into its own accumulator; entries past
@@ -237,9 +236,9 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
     for (int f = 0; f < kFrag; ++f)
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
-        acc[f][rt] = mfma_fp4(a[rt][0], sa[rt][0], bk[f][0], sb[f][0], v4f{0.f, 0.f, 0.f, 0.f});
+        acc[f][rt] = mfma_fp4(a[rt][0], sa[rt][0], ck[f][0], cs[f][0], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int ks = 1; ks < kKS; ++ks) acc[f][rt] = mfma_fp4(a[rt][ks], sa[rt][ks], bk[f][ks], sb[f][ks], acc[f][rt]);
+        for (int ks = 1; ks < kKS; ++ks) acc[f][rt] = mfma_fp4(a[rt][ks], sa[rt][ks], ck[f][ks], cs[f][ks], acc[f][rt]);
       }
     if constexpr (kHI == 8 && kFrag % 2 == 0) {
       // both lane halves of a query hold its sum after head_sum: the even one
@@ -264,14 +263,16 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
           if (writer) put(rt, e_frag0 + f * 16 + col, p);
         }
     }
-    if constexpr (!kStream) {
-#pragma unroll
-      for (int f = 0; f < kFrag; ++f)
-#pragma unroll
-        for (int ks = 0; ks < kKS; ++ks) {
-          bk[f][ks] = bn[f][ks];
-          sb[f][ks] = sn[f][ks];
-        }
+  };
+  if constexpr (kStream) {
+    batch(bk, sb, bk, sb, e_wave0, false);
+  } else {
+    u32x4 bn[kFrag][kKS];
+    int sn[kFrag][kKS];
+    for (int e_frag0 = e_wave0; e_frag0 < e_wave1; e_frag0 += 2 * 16 * kFrag) {
+      batch(bk, sb, bn, sn, e_frag0, true);
+      if (e_frag0 + 16 * kFrag >= e_wave1) break;
+      batch(bn, sn, bk, sb, e_frag0 + 16 * kFrag, true);
     }
   }
 }
