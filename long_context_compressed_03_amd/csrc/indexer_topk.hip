@@ -33,6 +33,8 @@
 //        entries than the list, it is re-scored in rounds of 4096 keys);
 //     e. emission as in csa_topk: bitmaps of "greater" and "equal" entries,
 //        one block scan, ascending output with the lower-index tie rule.
+#include <utility>
+
 #include "indexer_core.hpp"
 #include "split.hpp"
 
@@ -190,6 +192,27 @@ CSA_DEV void list_batch(Get get, int base, In in_window, Above above, int32_t* i
 // keys in [lo16, hi16] are appended to the wave's own region of the window
 // list at a wave-uniform running count (n_in; a count past the region's size
 // marks an overflow).  lo16 > 0, so absent keys (0) are in neither set.
+// `word` with lane L replaced by the wave-uniform `val` (V_WRITELANE_B32, no
+// exec-mask change).  `val` is usually a ballot just written by a vector
+// compare: reading such a scalar register in V_WRITELANE needs wait states,
+// which the compiler inserts for its own instructions but not inside asm, so
+// the asm carries them itself.
+template <int L>
+CSA_DEV uint32_t write_lane(uint32_t word, uint32_t val) {
+  asm("s_nop 4\n\tv_writelane_b32 %0, %1, %2" : "+v"(word) : "s"(val), "n"(L));
+  return word;
+}
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <typename F, int... I>
+CSA_DEV void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+CSA_DEV void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 template <int kR, typename Get>
 CSA_DEV void window_pass(Get get, int base, uint32_t lo16, uint32_t hi16, uint32_t* bm_above, uint32_t& n_in,
                          Shared& sh) {
@@ -197,30 +220,44 @@ CSA_DEV void window_pass(Get get, int base, uint32_t lo16, uint32_t hi16, uint32
   const int wv = threadIdx.x >> 6;
   const uint32_t span = hi16 - lo16;
   uint32_t n_above = 0u;                 // wave-uniform
+  // bitmap words collected in VGPR lanes: group i = 4j + c puts its two ballot
+  // words in lanes 2i and 2i + 1 (no exec-mask flips, no scalar registers
+  // held across the pass); one store per lane at the end
+  constexpr int kWords = (kR * 4 * 2 + 63) / 64;
+  uint32_t words[kWords];
 #pragma unroll
-  for (int j = 0; j < kR; ++j)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t kk = get(j, c);
-      const uint64_t bab = __ballot(kk > hi16);
-      n_above += uint32_t(__popcll(bab));
-      if (bm_above && lane == 0) {
-        // the wave's 64 keys are indices j*4096 + c*1024 + 64w + l: words
-        // 2w + (j*4096 + c*1024)/32 and the next (a per-wave base plus a constant)
-        uint32_t* wb = bm_above + 2 * wv;
-        wb[(j * kRound + c * kThreads) >> 5] = uint32_t(bab);
-        wb[((j * kRound + c * kThreads) >> 5) + 1] = uint32_t(bab >> 32);
-      }
-      const bool in = kk - lo16 <= span;
-      const uint64_t bin = __ballot(in);
-      const uint32_t slot =
-          n_in + __builtin_amdgcn_mbcnt_hi(uint32_t(bin >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(bin), 0u));
-      if (in && slot < uint32_t(kWinPer)) {
-        sh.win_idx[wv * kWinPer + slot] = base + key_offset(j, c);
-        sh.win_key[wv * kWinPer + slot] = uint16_t(kk);
-      }
-      n_in += uint32_t(__popcll(bin));
+  for (int q = 0; q < kWords; ++q) words[q] = 0u;
+  static_for<kR * 4>([&](auto I) {
+    constexpr int gi = decltype(I)::value;
+    const int j = gi / 4, c = gi % 4;
+    const uint32_t kk = get(j, c);
+    const uint64_t bab = __ballot(kk > hi16);
+    n_above += uint32_t(__popcll(bab));
+    if (bm_above) {
+      constexpr int i2 = 2 * gi;
+      words[i2 / 64] = write_lane<i2 % 64>(words[i2 / 64], uint32_t(bab));
+      words[(i2 + 1) / 64] = write_lane<(i2 + 1) % 64>(words[(i2 + 1) / 64], uint32_t(bab >> 32));
     }
+    const bool in = kk - lo16 <= span;
+    const uint64_t bin = __ballot(in);
+    const uint32_t slot =
+        n_in + __builtin_amdgcn_mbcnt_hi(uint32_t(bin >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(bin), 0u));
+    if (in && slot < uint32_t(kWinPer)) {
+      sh.win_idx[wv * kWinPer + slot] = base + key_offset(j, c);
+      sh.win_key[wv * kWinPer + slot] = uint16_t(kk);
+    }
+    n_in += uint32_t(__popcll(bin));
+  });
+  if (bm_above) {
+    // the wave's 64 keys of group (j, c) are indices j*4096 + c*1024 + 64w + l:
+    // bitmap words (j*4096 + c*1024)/32 + 2w and the next
+#pragma unroll
+    for (int q = 0; q < kWords; ++q) {
+      const int g2 = 64 * q + lane;   // 2 * group + half
+      const int gi = g2 >> 1;
+      if (gi < kR * 4) bm_above[(gi >> 2) * (kRound / 32) + (gi & 3) * (kThreads / 32) + 2 * wv + (g2 & 1)] = words[q];
+    }
+  }
   if (lane == 0 && n_above) atomicAdd(&sh.n_gt, n_above);
 }
 
