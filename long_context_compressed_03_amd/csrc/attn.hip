@@ -570,13 +570,14 @@ void attn_kernel(AttnArgs a) {
       if (a.lse && g == 0) a.lse[orow] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
     } else {
       // this split's unnormalised state; the merge kernel combines the splits
+      // (streaming stores: the partials are read once, by another kernel)
       const long slot = (qrow * a.n_splits + split) * a.H + head;
       float* po = a.part_o + slot * kHeadDim;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<v4f*>(po + dt * 16 + 4 * g) = oo[dt];
+      for (int dt = 0; dt < 8; ++dt) __builtin_nontemporal_store(oo[dt], reinterpret_cast<v4f*>(po + dt * 16 + 4 * g));
       if (g == 0) {
-        a.part_ml[slot * 2] = M;
-        a.part_ml[slot * 2 + 1] = L;
+        __builtin_nontemporal_store(M, &a.part_ml[slot * 2]);
+        __builtin_nontemporal_store(L, &a.part_ml[slot * 2 + 1]);
       }
     }
   }

@@ -11,9 +11,9 @@
 // segment.  Short blocks (m < 32, the CSA case): one group owns one entry and
 // a 256-thread block covers 16 entries, walking rows with 4 loads in flight
 // per lane for each of K and V.  Long blocks (the HCA case, m' = 128): the 16
-// groups of a block share one entry, group r taking rows r, r+16, ..., so all
-// rows are in flight at once; the 16 partial sums meet in LDS and are added in
-// group order.
+// groups of a block share one tensor (K or V) of one entry, group r taking
+// rows r, r+16, ..., so all rows are in flight at once; the 16 partial sums
+// meet in LDS and are added in group order.
 #include "common.hpp"
 
 namespace {
@@ -137,91 +137,115 @@ __global__ __launch_bounds__(kBlock) void compress_kernel(const void* __restrict
   store_entry<kOut>(v_out, v_scale, entry, lane_c, av);
 }
 
-// One entry per block: 16 groups split the rows, partial sums meet in LDS.
+// One tensor of one entry per block (blockIdx.y: 0 = K, 1 = V; each has its
+// own fp8 scale, so the two never meet): 16 groups split the rows, partial
+// sums meet in LDS.  The softmax statistics are reduced over the block.
 template <int kInF32, int kOut>
 __global__ __launch_bounds__(kBlock) void compress_long_kernel(const void* __restrict__ k, const void* __restrict__ v,
                                                                const float* __restrict__ logits, int n_entries,
                                                                int ld_in, int m, void* k_out, void* v_out,
                                                                float* k_scale, float* v_scale, int ld_out) {
-  __shared__ float part[2][kEntriesPerBlock][kHeadDim + 4];
+  __shared__ float part[kEntriesPerBlock][kHeadDim + 4];
+  __shared__ float wz[kBlock];              // exp(z_r - max) of the first 256 rows
+  __shared__ float red[2][kBlock / 64];
   const int lane_c = threadIdx.x & (kGroup - 1);
   const int grp = threadIdx.x / kGroup;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int b = blockIdx.x / n_entries;
   const int e = blockIdx.x - b * n_entries;
+  const int kv = blockIdx.y;
+  const void* src = kv ? v : k;
   const size_t row0 = size_t(b) * ld_in + size_t(e) * m;
   const float* z = logits + row0;
 
-  float ak[8], av[8];
+  float ak[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) { ak[i] = 0.f; av[i] = 0.f; }
-  // rows of the first batch are requested before the logit statistics so the
-  // two memory round trips overlap (every group takes part in the first batch)
+  for (int i = 0; i < 8; ++i) ak[i] = 0.f;
   constexpr int kU = 8;
-  float zmax = 0.f, inv = 0.f;
-  for (int j = grp; j < m; j += kU * kEntriesPerBlock) {
-    float kr[kU][8], vr[kU][8];
+  constexpr int kStride = kU * kEntriesPerBlock;   // rows per batch of the block
+  float kr[kU][8];
+  // rows past the block are read as its last row and weighted 0 (no branches
+  // around the loads, so the waits for them stay exact)
+  auto load_batch = [&](int j) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int r = j + u * kEntriesPerBlock;
-      if (r < m) {
-        load_row8<kInF32>(k, row0 + r, lane_c, kr[u]);
-        load_row8<kInF32>(v, row0 + r, lane_c, vr[u]);
-      }
+      load_row8<kInF32>(src, row0 + min(r, m - 1), lane_c, kr[u]);
     }
-    if (j == grp) {
-      // softmax statistics over all m logits (every group computes the same values)
-      zmax = -INFINITY;
-      for (int x = lane_c; x < m; x += kGroup) zmax = fmaxf(zmax, z[x]);
-      zmax = group_max<kGroup>(zmax);
-      float zsum = 0.f;
-      for (int x = lane_c; x < m; x += kGroup) zsum += expf(z[x] - zmax);
-      zsum = group_sum<kGroup>(zsum);
-      inv = 1.f / zsum;
-    }
+  };
+  float zmax, inv;
+  auto add_batch = [&](int j) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int r = j + u * kEntriesPerBlock;
-      if (r < m) {
-        const float a = expf(z[r] - zmax) * inv;
+      const float a = r >= m ? 0.f : (r < kBlock ? wz[r] : expf(z[r] - zmax)) * inv;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          ak[i] = fmaf(a, kr[u][i], ak[i]);
-          av[i] = fmaf(a, vr[u][i], av[i]);
-        }
-      }
+      for (int i = 0; i < 8; ++i) ak[i] = fmaf(a, kr[u][i], ak[i]);
     }
+  };
+
+  // softmax statistics over the block: thread t takes logits t, t + 256, ...;
+  // its first logit is requested before the rows, so the statistics wait for
+  // the logits only and are done while the rows arrive
+  const float z0 = z[int(threadIdx.x) < m ? int(threadIdx.x) : 0];
+  const float zt = int(threadIdx.x) < m ? z0 : -INFINITY;
+  load_batch(grp);   // m >= 32: every group has rows in the first batch
+  {
+    float zm = zt;
+    for (int x = threadIdx.x + kBlock; x < m; x += kBlock) zm = fmaxf(zm, z[x]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) zm = fmaxf(zm, __shfl_xor(zm, o));
+    if (lane == 0) red[0][wv] = zm;
+    __syncthreads();
+    zmax = red[0][0];
+#pragma unroll
+    for (int x = 1; x < kBlock / 64; ++x) zmax = fmaxf(zmax, red[0][x]);
+    const float et = int(threadIdx.x) < m ? expf(zt - zmax) : 0.f;
+    wz[threadIdx.x] = et;
+    float zs = et;
+    for (int x = threadIdx.x + kBlock; x < m; x += kBlock) zs += expf(z[x] - zmax);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) zs += __shfl_xor(zs, o);
+    if (lane == 0) red[1][wv] = zs;
+    __syncthreads();
+    float sum = red[1][0];
+#pragma unroll
+    for (int x = 1; x < kBlock / 64; ++x) sum += red[1][x];
+    inv = 1.f / sum;
+  }
+  add_batch(grp);
+  for (int j = grp + kStride; j < m; j += kStride) {
+    load_batch(j);
+    add_batch(j);
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    part[0][grp][lane_c * 8 + i] = ak[i];
-    part[1][grp][lane_c * 8 + i] = av[i];
-  }
+  for (int i = 0; i < 8; ++i) part[grp][lane_c * 8 + i] = ak[i];
   __syncthreads();
-  // thread t adds the 16 partials of one output value (K for t < 128, V
-  // otherwise; head column t % 128) in group order and stores it
-  const int kv = threadIdx.x >> 7;
+  // thread t < 128 adds the 16 partials of head column t in group order and
+  // stores it (the upper half of the block repeats the sums and stores nothing)
   const int col = threadIdx.x & (kHeadDim - 1);
+  const bool own = threadIdx.x < kHeadDim;
   float x = 0.f;
 #pragma unroll
-  for (int r = 0; r < kEntriesPerBlock; ++r) x += part[kv][r][col];
+  for (int r = 0; r < kEntriesPerBlock; ++r) x += part[r][col];
   const size_t entry = size_t(b) * ld_out + e;
   void* out = kv ? v_out : k_out;
   if constexpr (kOut == CSA_F32) {
-    static_cast<float*>(out)[entry * kHeadDim + col] = x;
+    if (own) static_cast<float*>(out)[entry * kHeadDim + col] = x;
   } else if constexpr (kOut == CSA_BF16) {
-    static_cast<uint16_t*>(out)[entry * kHeadDim + col] = f32_to_bf16(x);
+    if (own) static_cast<uint16_t*>(out)[entry * kHeadDim + col] = f32_to_bf16(x);
   } else {
-    // per-entry scale from the max magnitude over the entry's 128 values (two waves)
+    // per-entry scale from the max magnitude over the entry's 128 values (waves 0 and 1)
     __shared__ float wmax[kBlock / 64];
     float amax = fabsf(x);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
     if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
     __syncthreads();
-    amax = fmaxf(wmax[2 * kv], wmax[2 * kv + 1]);
+    amax = fmaxf(wmax[0], wmax[1]);
     const float scale = amax > 0.f ? amax / 448.f : 1.f;
-    static_cast<uint8_t*>(out)[entry * kHeadDim + col] = uint8_t(f32_to_e4m3(x / scale));
-    if (col == 0) (kv ? v_scale : k_scale)[entry] = scale;
+    if (own) static_cast<uint8_t*>(out)[entry * kHeadDim + col] = uint8_t(f32_to_e4m3(x / scale));
+    if (col == 0 && own) (kv ? v_scale : k_scale)[entry] = scale;
   }
 }
 
@@ -230,7 +254,7 @@ hipError_t launch_one(dim3 grid_short, long total, hipStream_t st, const void* k
                       int ne, int ld_in, int m, void* ko, void* vo, float* ks, float* vs, int ld_out) {
   (void)grid_short;
   if (m >= 32) {
-    hipLaunchKernelGGL((compress_long_kernel<kInF32, kOut>), dim3(unsigned(total)), dim3(kBlock), 0, st, k, v, lg, ne,
+    hipLaunchKernelGGL((compress_long_kernel<kInF32, kOut>), dim3(unsigned(total), 2u), dim3(kBlock), 0, st, k, v, lg, ne,
                        ld_in, m, ko, vo, ks, vs, ld_out);
   } else {
     // few entries (decoding): 4 per 64-thread block, so their rows are
