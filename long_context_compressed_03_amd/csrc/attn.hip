@@ -41,7 +41,8 @@ namespace {
 constexpr int kNK = 64;                       // keys per chunk
 constexpr int kThreads = 512;                 // 8 waves
 constexpr int kKRow = kHeadDim + 8;           // bf16 per K row in LDS
-constexpr int kVRow = kNK + 8;                // bf16 per V^T row in LDS
+constexpr int kVRow = kNK + 16;               // bf16 per V^T row in LDS
+constexpr int kVGroup = 8 * kVRow + 8;         // bf16 per group of 8 V^T rows (rows, then a pad)
 constexpr int kFRow = kHeadDim + 4;           // fp32 per K/V row in LDS (fp32 path)
 constexpr int kMaxSplits = 64;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -164,8 +165,12 @@ CSA_DEV void gather_slot(const AttnArgs& a, Pre<kIO>& pr, int x, int src, long r
   pr.src[x] = src;
 }
 
-// Gather item of thread tid: key pair kp = tid % 32 (keys 2kp, 2kp+1 of the
-// chunk), head dims [8*dg, 8*dg+8) with dg = tid / 32.
+// Gather item of thread t: key pair kp = t / 16 (keys 2kp, 2kp+1 of the
+// chunk), head dims [8*dg, 8*dg+8) with dg = t % 16.  A wave's load for one
+// slot covers 4 whole rows, so each row's cache lines are requested by one
+// wave (not by all eight).
+CSA_DEV int item_kp() { return int(threadIdx.x) >> 4; }
+CSA_DEV int item_dg() { return int(threadIdx.x) & 15; }
 //
 // Selected-entry indices of the item's two slots in chunk jc (sparse lists);
 // they are loaded one chunk ahead of the rows they name, so a row load never
@@ -176,7 +181,7 @@ template <bool kDense>
 CSA_DEV void load_idx(const AttnArgs& a, int (&e)[2], int b, int i, int jc, int j_end) {
   e[0] = e[1] = -1;
   if constexpr (!kDense) {
-    const int kp = threadIdx.x & 31;
+    const int kp = item_kp();
     const int32_t* ip = a.idx + (long(b) * a.T_q + i) * a.k;
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
@@ -190,8 +195,8 @@ CSA_DEV void load_idx(const AttnArgs& a, int (&e)[2], int b, int i, int jc, int 
 // Rows of the item's two slots of chunk jc (e: their indices from load_idx).
 template <int kIO, int kCKV, bool kDense>
 CSA_DEV void prefetch(const AttnArgs& a, Pre<kIO>& pr, const int (&e)[2], int b, int t, int raw0, int jc, int j_end) {
-  const int kp = threadIdx.x & 31;
-  const int dg = threadIdx.x >> 5;
+  const int kp = item_kp();
+  const int dg = item_dg();
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int j = jc + 2 * kp + x;
@@ -226,7 +231,10 @@ CSA_DEV void part_f32(const u32x4* w, int src, int h, float* x) {
 // LDS layout of one chunk
 struct LdsBf16 {
   uint16_t K[kNK][kKRow];
-  uint16_t Vt[kHeadDim][kVRow];
+  // V^T, head dim x key: rows of 40 words, 4 words of pad after every 8 rows.
+  // A wave's writes (16 row groups x 4 key pairs) then fall in distinct
+  // banks and the 8-byte reads of the P*V products take two passes.
+  uint16_t Vt[kHeadDim / 8][kVGroup];
   float sk[kNK];
   float sv[kNK];
   int valid[kNK];
@@ -278,8 +286,8 @@ CSA_DEV u32x4 part_bf16(const u32x4* w, int src, int h) {
 // sk_mul: factor folded into the stored K scale (the logit scale in the log2 domain).
 template <int kIO, int kCKV>
 CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr, float sk_mul) {
-  const int kp = threadIdx.x & 31;
-  const int dg = threadIdx.x >> 5;
+  const int kp = item_kp();
+  const int dg = item_dg();
   if constexpr (kIO == CSA_BF16) {
     // values are exact in bf16 (bf16 inputs or E4M3 codes)
     u32x4 kw[2], vw[2];
@@ -292,8 +300,9 @@ CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr, float sk_mul) {
     // V^T: head dim x of keys 2kp and 2kp+1 as one bf16 pair
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      *reinterpret_cast<uint32_t*>(&s.Vt[dg * 8 + 2 * x][2 * kp]) = (vw[0][x] & 0xFFFFu) | (vw[1][x] << 16);
-      *reinterpret_cast<uint32_t*>(&s.Vt[dg * 8 + 2 * x + 1][2 * kp]) = (vw[0][x] >> 16) | (vw[1][x] & 0xFFFF0000u);
+      uint16_t* vt = &s.Vt[dg][2 * x * kVRow + 2 * kp];   // rows 8 dg + 2x and 8 dg + 2x + 1
+      *reinterpret_cast<uint32_t*>(vt) = (vw[0][x] & 0xFFFFu) | (vw[1][x] << 16);
+      *reinterpret_cast<uint32_t*>(vt + kVRow) = (vw[0][x] >> 16) | (vw[1][x] & 0xFFFF0000u);
     }
   } else {
     float xk[2][8], xv[2][8];
@@ -354,11 +363,12 @@ CSA_DEV void store_out4(void* out, long orow, int d4, v4f v) {
 // 8 waves: wave w takes head tiles (w % 4) [+ 4 when kHTW == 2] and key half
 // w / 4 (keys [32*(w/4), 32*(w/4)+32) of every chunk); the two halves merge at
 // the end of the block through LDS.
-// kDeep (split key lists, at most about one block per CU): two chunks in
-// flight instead of one, with the register budget of two waves per SIMD.
-template <int kIO, int kCKV, bool kDense, int kHTW, bool kDeep>
+// kDepth > 1 (split key lists, at most about one block per CU): that many
+// chunks in flight instead of one, with the register budget of two waves per
+// SIMD.
+template <int kIO, int kCKV, bool kDense, int kHTW, int kDepth>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(kIO == CSA_BF16 && kHTW == 1 ? (kDeep ? 2 : 4) : 1)))
+__attribute__((amdgpu_waves_per_eu(kIO == CSA_BF16 && kHTW == 1 ? (kDepth > 1 ? 2 : 4) : 1)))
 void attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   LdsChunk<kIO>& s = *reinterpret_cast<LdsChunk<kIO>*>(smem);
@@ -463,8 +473,9 @@ void attn_kernel(AttnArgs a) {
         const int k0 = kh * 32 + 4 * g;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(&s.Vt[dt * 16 + col][k0]);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(&s.Vt[dt * 16 + col][k0 + 16]);
+          const uint16_t* vt = &s.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0];   // row dt*16 + col
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vt);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + 16);
           o[ht][dt] = mfma_k32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, o[ht][dt]);
         }
       } else {
@@ -481,45 +492,28 @@ void attn_kernel(AttnArgs a) {
     }
   };
 
-  Pre<kIO> pr;
-  int e_nx[2];
-  if constexpr (!kDeep) {
-    // every prefetch is issued, past the split too (empty slots read a dummy
-    // address): the same loads on every path keep the compiler's waits exact
-    load_idx<kDense>(a, e_nx, b, i, j_begin, j_end);
-    prefetch<kIO, kCKV, kDense>(a, pr, e_nx, b, t, raw0, j_begin, j_end);
-    load_idx<kDense>(a, e_nx, b, i, j_begin + kNK, j_end);
-    for (int j0 = j_begin; j0 < j_end; j0 += kNK) {
+  // kDepth chunks in flight: buffer d holds chunks d, d + kDepth, ...  Every
+  // prefetch is issued, past the split too (empty slots read a dummy
+  // address): the same loads on every path keep the compiler's waits exact.
+  // Indices run one round of chunks ahead of the rows they name.
+  Pre<kIO> pr[kDepth];
+  int e_nx[kDepth][2];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) load_idx<kDense>(a, e_nx[d], b, i, j_begin + d * kNK, j_end);
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) {
+    prefetch<kIO, kCKV, kDense>(a, pr[d], e_nx[d], b, t, raw0, j_begin + d * kNK, j_end);
+    load_idx<kDense>(a, e_nx[d], b, i, j_begin + (d + kDepth) * kNK, j_end);
+  }
+  for (int j0 = j_begin; j0 < j_end; j0 += kDepth * kNK) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+      if (d > 0 && j0 + d * kNK >= j_end) break;
       __syncthreads();
-      store_chunk<kIO, kCKV>(s, pr, a.sm_log2);
+      store_chunk<kIO, kCKV>(s, pr[d], a.sm_log2);
       __syncthreads();
-      prefetch<kIO, kCKV, kDense>(a, pr, e_nx, b, t, raw0, j0 + kNK, j_end);
-      load_idx<kDense>(a, e_nx, b, i, j0 + 2 * kNK, j_end);
-      compute();
-    }
-  } else {
-    // two chunks in flight: buffers pr (even chunks) and pr2 (odd chunks)
-    Pre<kIO> pr2;
-    int e_nx2[2];
-    load_idx<kDense>(a, e_nx, b, i, j_begin, j_end);
-    load_idx<kDense>(a, e_nx2, b, i, j_begin + kNK, j_end);
-    prefetch<kIO, kCKV, kDense>(a, pr, e_nx, b, t, raw0, j_begin, j_end);
-    prefetch<kIO, kCKV, kDense>(a, pr2, e_nx2, b, t, raw0, j_begin + kNK, j_end);
-    load_idx<kDense>(a, e_nx, b, i, j_begin + 2 * kNK, j_end);
-    load_idx<kDense>(a, e_nx2, b, i, j_begin + 3 * kNK, j_end);
-    for (int j0 = j_begin; j0 < j_end; j0 += 2 * kNK) {
-      __syncthreads();
-      store_chunk<kIO, kCKV>(s, pr, a.sm_log2);
-      __syncthreads();
-      prefetch<kIO, kCKV, kDense>(a, pr, e_nx, b, t, raw0, j0 + 2 * kNK, j_end);
-      load_idx<kDense>(a, e_nx, b, i, j0 + 4 * kNK, j_end);
-      compute();
-      if (j0 + kNK >= j_end) break;
-      __syncthreads();
-      store_chunk<kIO, kCKV>(s, pr2, a.sm_log2);
-      __syncthreads();
-      prefetch<kIO, kCKV, kDense>(a, pr2, e_nx2, b, t, raw0, j0 + 3 * kNK, j_end);
-      load_idx<kDense>(a, e_nx2, b, i, j0 + 5 * kNK, j_end);
+      prefetch<kIO, kCKV, kDense>(a, pr[d], e_nx[d], b, t, raw0, j0 + (d + kDepth) * kNK, j_end);
+      load_idx<kDense>(a, e_nx[d], b, i, j0 + (d + 2 * kDepth) * kNK, j_end);
       compute();
     }
   }
@@ -664,8 +658,8 @@ struct LdsMQ {
 template <int kCKV>
 CSA_DEV void prefetch_mq(const AttnArgs& a, Pre<CSA_BF16>& pr, uint32_t (&vis)[2], int b, int raw0, int nv_max,
                          int p_lo, int n_list, int jc, int t0, int n_q) {
-  const int kp = threadIdx.x & 31;
-  const int dg = threadIdx.x >> 5;
+  const int kp = item_kp();
+  const int dg = item_dg();
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
     const int j = jc + 2 * kp + x;
@@ -745,9 +739,9 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
   auto step = [&](Pre<CSA_BF16>& prc, uint32_t (&tgc)[2], int j0) {
     __syncthreads();
     store_chunk<CSA_BF16, kCKV>(s.c, prc, a.sm_log2);
-    if ((threadIdx.x >> 5) == 0) {
-      s.vis[2 * (threadIdx.x & 31)] = tgc[0];
-      s.vis[2 * (threadIdx.x & 31) + 1] = tgc[1];
+    if (item_dg() == 0) {
+      s.vis[2 * item_kp()] = tgc[0];
+      s.vis[2 * item_kp() + 1] = tgc[1];
     }
     __syncthreads();
     if (j0 + 2 * kNK < n_list)
@@ -822,8 +816,9 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
       const u32x4 pb1 = {pw[1][st][0], pw[1][st][1], pw[1][st][2], pw[1][st][3]};
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(&s.c.Vt[dt * 16 + col][k0]);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(&s.c.Vt[dt * 16 + col][k0 + 16]);
+        const uint16_t* vt = &s.c.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0];   // row dt*16 + col
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vt);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + 16);
         const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
         o[0][dt] = mfma_k32(vf, pb0, o[0][dt]);
         o[1][dt] = mfma_k32(vf, pb1, o[1][dt]);
@@ -878,11 +873,11 @@ size_t plan_ws_bytes(const Plan& p, long rows, int H) {
   return ml + slots * kHeadDim * 4;
 }
 
-template <int kIO, int kCKV, bool kDense, int kHTW, bool kDeep>
+template <int kIO, int kCKV, bool kDense, int kHTW, int kDepth>
 hipError_t launch_attn(const AttnArgs& a, long blocks, hipStream_t st) {
   static bool attr = false;   // per instantiation; dynamic LDS above 64 KB needs the opt-in
   constexpr size_t bytes = lds_bytes<kIO, kHTW>();
-  auto fn = attn_kernel<kIO, kCKV, kDense, kHTW, kDeep>;
+  auto fn = attn_kernel<kIO, kCKV, kDense, kHTW, kDepth>;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        int(bytes));
@@ -933,13 +928,14 @@ template <int kIO, int kCKV, bool kDense>
 hipError_t launch_tiles(const AttnArgs& a, long blocks, hipStream_t st) {
   // split key lists of more than two chunks take the two-chunk pipeline
   // (fp32 queries over more than 64 heads would not fit its registers); with
-  // two chunks the one-ahead prefetch already overlaps the second
+  // two chunks the one-ahead prefetch already overlaps the second, and more
+  // chunks in flight only delay the first (a CU's loads in flight are few)
   if (a.n_splits > 1 && a.split_len > 2 * kNK) {
-    if (a.H <= 64) return launch_attn<kIO, kCKV, kDense, 1, true>(a, blocks, st);
-    if constexpr (kIO == CSA_BF16) return launch_attn<kIO, kCKV, kDense, 2, true>(a, blocks, st);
+    if (a.H <= 64) return launch_attn<kIO, kCKV, kDense, 1, 2>(a, blocks, st);
+    if constexpr (kIO == CSA_BF16) return launch_attn<kIO, kCKV, kDense, 2, 2>(a, blocks, st);
   }
-  return a.H <= 64 ? launch_attn<kIO, kCKV, kDense, 1, false>(a, blocks, st)
-                   : launch_attn<kIO, kCKV, kDense, 2, false>(a, blocks, st);
+  return a.H <= 64 ? launch_attn<kIO, kCKV, kDense, 1, 1>(a, blocks, st)
+                   : launch_attn<kIO, kCKV, kDense, 2, 1>(a, blocks, st);
 }
 
 template <bool kDense>
