@@ -677,6 +677,7 @@ __global__ __launch_bounds__(kFusedThreads) void indexer_slice_kernel(
   const __amdgpu_buffer_rsrc_t rc_k = csa_ix::seq_rsrc(kc_seq, c_bytes);
   const __amdgpu_buffer_rsrc_t re_k = csa_ix::seq_rsrc(ke_seq, e_bytes);
   float* srow = scores + size_t(b) * cap;
+  clear_window<kFusedThreads>(sh);   // published by the barrier after the scores
 
   const int e_wave0 = base + wid * kPerWave;
   u32x4 bk[kNB][kFrag][kKS];
@@ -688,6 +689,7 @@ __global__ __launch_bounds__(kFusedThreads) void indexer_slice_kernel(
       const int e = e_wave0 + nb * kBatch16 + f * 16 + col;
       csa_ix::load_b<kKS, true>(rc_k, re_k, c_bytes, e_bytes, e, e < nv, g, nblk, row_bytes, bk[nb][f], sb[nb][f]);
     }
+  uint32_t kmax = 0u;   // largest key this lane writes
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     v4f acc[kFrag];
@@ -705,11 +707,15 @@ __global__ __launch_bounds__(kFusedThreads) void indexer_slice_kernel(
       const int e = e_wave0 + nb * kBatch16 + f * 16 + col;
       if (writer && mine) {
         const bool vis = e < nv;
-        skey[e - base] = vis ? ordered_key(p) : 0u;
+        const uint32_t kk = vis ? ordered_key(p) : 0u;
+        skey[e - base] = kk;
+        kmax = max(kmax, kk);
         if (vis) srow[e] = p;
       }
     }
   }
+  kmax = wave_umax(kmax);
+  if (lane == 0) sh.smax[wid] = kmax;
   __syncthreads();
   uint32_t key[kSlice / kFusedThreads];
 #pragma unroll

@@ -59,39 +59,46 @@ inline SplitWs split_ws(void* ws, long rows, int cap) {
   return w;
 }
 
-struct SliceShared {
+struct alignas(16) SliceShared {   // hist is read as 16-byte words
   uint32_t hist[kWindow];
   uint32_t smax[16];
-  uint32_t smem[32];
   uint32_t wc[32];
   uint32_t v;
 };
+
+// Largest key over a wave (every lane receives it).
+CSA_DEV uint32_t wave_umax(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, uint32_t(__shfl_xor(int(v), o)));
+  return v;
+}
+
+// What slice_finish expects before its call, behind a barrier: the window
+// histogram cleared and sh.smax[w] = the largest key wave w holds (or wrote).
+// clear_window: every thread of a block of kT threads calls it.
+template <int kT>
+CSA_DEV void clear_window(SliceShared& sh) {
+#pragma unroll
+  for (int i = 0; i < kWindow / kT; ++i) sh.hist[threadIdx.x * (kWindow / kT) + i] = 0u;
+}
 
 // The slice pass on keys already in registers, by a block of kT threads
 // (256 or 1024): thread t holds the keys of indices base + j*kT + t (0 for
 // entries past the visible count); n_s > 0 visible entries in the slice,
 // nv > k in the row.  Writes count[slot], bound[slot] and the slot's
-// candidates.  Every thread of the block calls it.
+// candidates.  Every thread of the block calls it, after a barrier that
+// follows clear_window and the waves' sh.smax writes.
 template <int kT>
 CSA_DEV void slice_finish(const uint32_t (&key)[kSlice / kT], int base, int n_s, int nv, int k, size_t slot,
                           const SplitWs& ws, SliceShared& sh) {
   constexpr int kP = kSlice / kT;       // keys per thread
   constexpr int kW = kT / 64;           // waves
-  constexpr int kBpt = kWindow / kT;    // window buckets per thread
   static_assert(kP * kW == 32, "32 ballot groups per slice");
+  static_assert(kWindow % 256 == 0, "rounds of 256 buckets");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const uint32_t quota = uint32_t((uint64_t(k) * uint32_t(n_s) + uint32_t(nv) - 1u) / uint32_t(nv));
   const uint32_t want = min(uint32_t(n_s), quota + uint32_t(6.f * sqrtf(float(quota))) + 6u);
-#pragma unroll
-  for (int i = 0; i < kBpt; ++i) sh.hist[tid * kBpt + i] = 0u;
-  uint32_t mx = 0u;
-#pragma unroll
-  for (int j = 0; j < kP; ++j) mx = max(mx, key[j]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = max(mx, uint32_t(__shfl_xor(int(mx), o)));
-  if (lane == 0) sh.smax[w] = mx;
-  __syncthreads();
-  mx = sh.smax[0];
+  uint32_t mx = sh.smax[0];
 #pragma unroll
   for (int x = 1; x < kW; ++x) mx = max(mx, sh.smax[x]);
   const int top = int(mx >> kBucketShift);
@@ -101,26 +108,30 @@ CSA_DEV void slice_finish(const uint32_t (&key)[kSlice / kT], int base, int n_s,
     if (key[j] && rel < kWindow) atomicAdd(&sh.hist[rel], 1u);
   }
   __syncthreads();
-  uint32_t c[kBpt];                     // buckets top - kBpt t .. (relative kBpt t ..)
-  uint32_t sum = 0u;
+  // wave 0 finds the bound: four rounds over 256 buckets each, lane l taking
+  // buckets [4l, 4l + 4) of the round (contiguous 16-byte reads, no bank
+  // conflicts), a prefix sum over the wave plus the rounds before; the lane
+  // where the count reaches `want` names the bucket
+  if (w == 0) {
+    uint32_t v = 1u;                    // fewer than `want` keys in the window: every key
+    uint32_t carry = 0u;
 #pragma unroll
-  for (int i = 0; i < kBpt; ++i) {
-    c[i] = sh.hist[tid * kBpt + i];
-    sum += c[i];
-  }
-  uint32_t tot;
-  const uint32_t excl = block_exclusive_scan(sum, sh.smem, &tot);
-  if (tot < want) {
-    if (tid == 0) sh.v = 1u;
-  } else if (excl < want && want <= excl + sum) {
-    uint32_t run = excl;
-    int r = kBpt * tid;
-#pragma unroll
-    for (int y = 0; y < kBpt; ++y) {
-      run += c[y];
-      if (run >= want) { r = kBpt * tid + y; break; }
+    for (int q = 0; q < kWindow / 256; ++q) {
+      const u32x4 h = *reinterpret_cast<const u32x4*>(&sh.hist[256 * q + 4 * lane]);
+      const uint32_t s4 = h[0] + h[1] + h[2] + h[3];
+      const uint32_t incl = carry + wave_inclusive_scan(s4);
+      const uint32_t excl = incl - s4;
+      const uint64_t hit = __ballot(excl < want && want <= incl);
+      if (hit) {
+        const uint32_t c0 = excl + h[0], c1 = c0 + h[1], c2 = c1 + h[2];
+        const int y = c0 >= want ? 0 : c1 >= want ? 1 : c2 >= want ? 2 : 3;
+        const int r = __shfl(256 * q + 4 * lane + y, int(__ffsll(static_cast<long long>(hit))) - 1);
+        v = uint32_t(top - r) << kBucketShift;
+        break;
+      }
+      carry = uint32_t(__shfl(int(incl), 63));
     }
-    sh.v = uint32_t(top - r) << kBucketShift;
+    if (lane == 0) sh.v = v;
   }
   __syncthreads();
   const uint32_t lo = sh.v;
@@ -133,8 +144,8 @@ CSA_DEV void slice_finish(const uint32_t (&key)[kSlice / kT], int base, int n_s,
   __syncthreads();
   // exclusive offsets of the 32 (key j, wave) groups in index order
   const uint32_t cw = lane < 32 ? sh.wc[lane] : 0u;
-  const uint32_t incl = wave_inclusive_scan(cw);
-  const uint32_t ex = incl - cw;
+  const uint32_t gincl = wave_inclusive_scan(cw);
+  const uint32_t ex = gincl - cw;
   const uint64_t below = (uint64_t(1) << lane) - 1u;
   uint32_t* const ck = ws.key + slot * kSliceCap;
   int32_t* const ci = ws.idx + slot * kSliceCap;
@@ -146,7 +157,7 @@ CSA_DEV void slice_finish(const uint32_t (&key)[kSlice / kT], int base, int n_s,
       ci[pos] = base + j * kT + tid;
     }
   }
-  const uint32_t total = uint32_t(__shfl(int(incl), 31));   // all lanes take part
+  const uint32_t total = uint32_t(__shfl(int(gincl), 31));   // all lanes take part
   if (tid == 0) {
     ws.count[slot] = total;
     ws.bound[slot] = lo;

@@ -162,8 +162,16 @@ __global__ __launch_bounds__(kSliceThreads) void slice_select_kernel(const float
     return;
   }
   uint32_t key[kSlicePer];
+  uint32_t mx = 0u;
 #pragma unroll
-  for (int j = 0; j < kSlicePer; ++j) key[j] = j * kSliceThreads + tid < n_s ? ordered_key(v[j]) : 0u;
+  for (int j = 0; j < kSlicePer; ++j) {
+    key[j] = j * kSliceThreads + tid < n_s ? ordered_key(v[j]) : 0u;
+    mx = max(mx, key[j]);
+  }
+  mx = wave_umax(mx);
+  if ((tid & 63) == 0) sh.smax[tid >> 6] = mx;
+  clear_window<kSliceThreads>(sh);
+  __syncthreads();
   slice_finish<kSliceThreads>(key, base, n_s, nv, k, slot, ws, sh);
 }
 
