@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--workload", default="csa_decode_128k",
                    choices=["csa_decode_128k", "hca_decode_1m", "csa_prefill_256k", "pair_1m"])
     p.add_argument("--rotate", type=int, default=0, help="input copies (0 = auto)")
-    p.add_argument("--indexer", default="auto", choices=["auto", "fused", "unfused"],
+    p.add_argument("--indexer", default="auto", choices=["auto", "combined", "fused", "unfused"],
                    help="CSA scoring + selection as one fused call or as csa_indexer_scores then "
                         "csa_topk (auto: fused for prefill chunks, unfused for decode)")
     p.add_argument("--no-graph", action="store_true")
@@ -172,8 +172,12 @@ def add_layer(st, h, prefix, indexer="auto"):
     def f_compress(c):
         csa.csa_compress_kv(c[p + "kw"], c[p + "vw"], c[p + "logits"], m, c[p + "ck"], c[p + "cv"],
                             c[p + "cks"], c[p + "cvs"], L=L, row0=row0, entry0=entry0)
-    st.add(Kernel(name("compress_kv"), f_compress, B * (L * 516 + (L // m) * ent), 0,
-                  BF16_PEAK_TFLOPS, "compress_kv"))
+    compress_bytes = B * (L * 516 + (L // m) * ent)
+    decode_split = wl.kind == "csa" and wl.T_q == 1 and rows <= 128 and wl.cap >= 8192 and wl.d_I <= 256
+    # decoding: the compression rides in the indexer top-k call (one launch fewer)
+    combined = decode_split and m < 32 and indexer in ("auto", "combined")
+    if not combined:
+        st.add(Kernel(name("compress_kv"), f_compress, compress_bytes, 0, BF16_PEAK_TFLOPS, "compress_kv"))
     q_bytes = rows * H * 128 * 4          # bf16 query in + bf16 output
     if wl.kind == "csa":
         k = wl.k
@@ -190,12 +194,24 @@ def add_layer(st, h, prefix, indexer="auto"):
             csa.csa_sparse_attn(c[p + "q"], c[p + "ck"], c[p + "cv"], c[p + "idx"], c[p + "kw"],
                                 c[p + "vw"], c[p + "raw0"], c[p + "pos"], W, ck_scale=c[p + "cks"],
                                 cv_scale=c[p + "cvs"], out=c[p + "out"])
-        fused = indexer in ("fused", "auto")
-        if fused:
+        fused = indexer in ("fused", "auto", "combined")
+        if combined:
+            def f_combined(c):
+                csa.csa_compress_indexer_topk(c[p + "kw"], c[p + "vw"], c[p + "logits"], c[p + "ck"],
+                                              c[p + "cv"], c[p + "cks"], c[p + "cvs"], c[p + "qc"],
+                                              c[p + "qe"], c[p + "w"], c[p + "kc"], c[p + "ke"],
+                                              c[p + "pos"], m, k, idx=c[p + "idx"], L=L, row0=row0,
+                                              entry0=entry0)
+            # keys once, the fp32 scores written, the indices; plus the compression's rows and entries
+            st.add(Kernel(name("compress_indexer_topk"), f_combined,
+                          compress_bytes + B * wl.cap * idx_bytes + nvis_sum * 4 + rows * k * 4
+                          + rows * wl.H_I * (idx_bytes + 4),
+                          2 * wl.H_I * wl.d_I * nvis_sum, MXFP4_PEAK_TFLOPS, "compress_indexer_topk"))
+        elif fused:
             def f_fused(c):
                 csa.csa_indexer_topk(c[p + "qc"], c[p + "qe"], c[p + "w"], c[p + "kc"], c[p + "ke"],
                                      c[p + "pos"], m, k, c[p + "idx"])
-            if wl.T_q == 1 and rows <= 128 and wl.cap >= 8192:
+            if decode_split:
                 # decoding: keys once, the fp32 scores written (read back only by the
                 # exact fallback), the indices
                 inter = nvis_sum * 4
@@ -277,7 +293,8 @@ def build(args):
                      **{prefix.rstrip("."): layer_config(h["wl"]) for prefix, h in hosts}}
     else:
         st.config = {"workload": args.workload, **layer_config(hosts[0][1]["wl"])}
-    st.config["indexer_topk"] = "fused" if any(n.endswith("indexer_topk") for n in st.order) else "unfused"
+    st.config["indexer_topk"] = ("combined with the compression" if any(n.endswith("compress_indexer_topk") for n in st.order)
+                                 else "fused" if any(n.endswith("indexer_topk") for n in st.order) else "unfused")
     return st
 
 
@@ -379,9 +396,13 @@ def kernel_source_hash(names):
 
 KERNEL_SOURCES = {
     "indexer_scores": ["indexer.hip", "indexer_core.hpp", "select.hpp", "common.hpp"],
-    "indexer_topk": ["indexer_topk.hip", "indexer_core.hpp", "split.hpp", "topk.hip", "select.hpp", "common.hpp"],
+    "indexer_topk": ["indexer_topk.hip", "indexer_core.hpp", "split.hpp", "topk.hip", "select.hpp",
+                     "compress_core.hpp", "common.hpp"],
     "sparse_attn": ["attn.hip", "common.hpp"], "dense_attn": ["attn.hip", "common.hpp"],
-    "topk": ["topk.hip", "split.hpp", "select.hpp", "common.hpp"], "compress_kv": ["compress.hip", "common.hpp"]}
+    "topk": ["topk.hip", "split.hpp", "select.hpp", "compress_core.hpp", "common.hpp"],
+    "compress_kv": ["compress.hip", "compress_core.hpp", "common.hpp"],
+    "compress_indexer_topk": ["indexer_topk.hip", "indexer_core.hpp", "split.hpp", "topk.hip", "select.hpp",
+                              "compress_core.hpp", "compress.hip", "common.hpp"]}
 
 
 def measured_traffic(workload, kernel):

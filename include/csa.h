@@ -178,6 +178,43 @@ csa_status_t csa_indexer_topk(const uint8_t* q_codes, const uint8_t* q_e8m0, con
                               void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------
+ * csa_compress_indexer_topk -- a CSA layer's compression and its indexer
+ * top-k in one call.
+ *
+ * Passages: as csa_compress_kv (every m tokens' K/V become one entry,
+ * blog.nickys.cn, 三大架构改动 §1 CSA) and csa_indexer_topk.
+ * Result: exactly that of
+ *   csa_compress_kv(k, v, in_dtype, logits, B, L, ld_in, d, m, k_out, v_out,
+ *                   k_scale_out, v_scale_out, ld_out, out_dtype, stream);
+ *   csa_indexer_topk(q_codes, ..., B, T_q, H_I, d_I, cap, m, k_sel, idx, ws,
+ *                    ws_bytes, stream);
+ * on the same arguments (B and m are shared: the layer's sequences and its
+ * compression ratio).  The two parts are independent (the compression writes
+ * the attention's entries, the indexer reads its own keys), so for decoding
+ * shapes (those of the csa_indexer_topk decode path, with m < 32) the
+ * compression runs inside the selection's launch on CUs the selection leaves
+ * idle, saving a launch on the decode critical path; otherwise the two run
+ * as two launches.
+ *
+ *   k .. out_dtype    as csa_compress_kv (without B, m)
+ *   q_codes .. idx    as csa_indexer_topk (k_sel = its k)
+ *   ws, ws_bytes      as csa_indexer_topk (same size)
+ * Precondition: k_out, v_out and the scales overlap none of the indexer's
+ * inputs, idx or the workspace.  Argument errors of either part are reported
+ * before anything runs.
+ * ------------------------------------------------------------------- */
+csa_status_t csa_compress_indexer_topk(const void* k, const void* v, int32_t in_dtype,
+                                       const float* logits, int32_t L, int32_t ld_in, int32_t d,
+                                       void* k_out, void* v_out, float* k_scale_out,
+                                       float* v_scale_out, int32_t ld_out, int32_t out_dtype,
+                                       const uint8_t* q_codes, const uint8_t* q_e8m0,
+                                       const float* w, const uint8_t* k_codes,
+                                       const uint8_t* k_e8m0, const int32_t* q_pos0, int32_t B,
+                                       int32_t T_q, int32_t H_I, int32_t d_I, int32_t cap,
+                                       int32_t m, int32_t k_sel, int32_t* idx, void* ws,
+                                       size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
  * csa_sparse_attn -- attention over the selected entries plus the window.
  *
  * Passage: attention runs only over the k selected compressed entries, with a

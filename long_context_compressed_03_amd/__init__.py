@@ -24,8 +24,8 @@ CSA_BF16, CSA_F32, CSA_FP8_E4M3 = 0, 1, 2
 CSA_OP_TOPK, CSA_OP_SPARSE_ATTN, CSA_OP_DENSE_ATTN, CSA_OP_INDEXER_TOPK = 0, 1, 2, 3
 DTYPES = {"bf16": CSA_BF16, "f32": CSA_F32, "fp8": CSA_FP8_E4M3}
 
-EXPORTS = ["csa_compress_kv", "csa_indexer_scores", "csa_indexer_topk", "csa_topk", "csa_sparse_attn",
-           "hca_dense_attn", "csa_workspace_size", "csa_status_str", "csa_abi_version"]
+EXPORTS = ["csa_compress_kv", "csa_indexer_scores", "csa_indexer_topk", "csa_compress_indexer_topk", "csa_topk",
+           "csa_sparse_attn", "hca_dense_attn", "csa_workspace_size", "csa_status_str", "csa_abi_version"]
 
 _lib = None
 _P = ctypes.c_void_p
@@ -52,13 +52,16 @@ def load(path=LIB_PATH):
     lib.csa_indexer_scores.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]
     lib.csa_indexer_topk.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _S,
                                      _P]
+    lib.csa_compress_indexer_topk.argtypes = [_P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _P, _I, _I,
+                                              _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P,
+                                              _P, _S, _P]
     lib.csa_topk.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _S, _P]
     lib.csa_sparse_attn.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _P, _I, _P, _P, _P, _I, _P, _I,
                                     _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
     lib.hca_dense_attn.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _P, _I,
                                    _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
-    for fn in ["csa_compress_kv", "csa_indexer_scores", "csa_indexer_topk", "csa_topk", "csa_sparse_attn",
-               "hca_dense_attn"]:
+    for fn in ["csa_compress_kv", "csa_indexer_scores", "csa_indexer_topk", "csa_compress_indexer_topk",
+               "csa_topk", "csa_sparse_attn", "hca_dense_attn"]:
         getattr(lib, fn).restype = _I
     lib.csa_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
     lib.csa_workspace_size.restype = _S
@@ -106,6 +109,22 @@ def _dt_of(t):
 
 # ---------------------------------------------------------------- calls --
 
+def _compress_ptrs(k, v, logits, m, k_out, v_out, k_scale_out, v_scale_out, L, row0, entry0):
+    """Pointer arguments of a compression call (rows row0.., entries entry0..)."""
+    B, ld_in, d = k.shape
+    ld_out = k_out.shape[1]
+    L = ld_in - row0 if L is None else L
+    if row0 < 0 or entry0 < 0 or row0 + L > ld_in or entry0 + L // max(m, 1) > ld_out:
+        raise ValueError("row or entry range outside the buffers")
+
+    def off(t, n):
+        return None if t is None else ctypes.c_void_p(_ptr(t).value + n * t.element_size())
+    return dict(B=B, L=L, ld_in=ld_in, d=d, ld_out=ld_out, in_dt=_dt_of(k), out_dt=_dt_of(k_out),
+                k=off(k, row0 * d), v=off(v, row0 * d), logits=off(logits, row0),
+                k_out=off(k_out, entry0 * d), v_out=off(v_out, entry0 * d),
+                k_scale=off(k_scale_out, entry0), v_scale=off(v_scale_out, entry0))
+
+
 def csa_compress_kv(k, v, logits, m, k_out, v_out, k_scale_out=None, v_scale_out=None, L=None,
                     row0=0, entry0=0, stream=None):
     """Pool every complete block of m rows of k/v [B, ld_in, 128] into k_out/v_out [B, ld_out, 128].
@@ -115,20 +134,36 @@ def csa_compress_kv(k, v, logits, m, k_out, v_out, k_scale_out=None, v_scale_out
     dtype (bf16, f32, or uint8 = fp8 with per-entry scales in k_scale_out/v_scale_out
     [B, ld_out]).
     """
-    B, ld_in, d = k.shape
-    ld_out = k_out.shape[1]
-    L = ld_in - row0 if L is None else L
-    if row0 < 0 or entry0 < 0 or row0 + L > ld_in or entry0 + L // max(m, 1) > ld_out:
-        raise ValueError("row or entry range outside the buffers")
-    out_dt = _dt_of(k_out)
-
-    def off(t, n):
-        return None if t is None else ctypes.c_void_p(_ptr(t).value + n * t.element_size())
-    st = load().csa_compress_kv(off(k, row0 * d), off(v, row0 * d), _dt_of(k), off(logits, row0),
-                                B, L, ld_in, d, m, off(k_out, entry0 * d), off(v_out, entry0 * d),
-                                off(k_scale_out, entry0), off(v_scale_out, entry0), ld_out, out_dt,
-                                _stream(stream))
+    c = _compress_ptrs(k, v, logits, m, k_out, v_out, k_scale_out, v_scale_out, L, row0, entry0)
+    st = load().csa_compress_kv(c["k"], c["v"], c["in_dt"], c["logits"], c["B"], c["L"], c["ld_in"], c["d"],
+                                m, c["k_out"], c["v_out"], c["k_scale"], c["v_scale"], c["ld_out"],
+                                c["out_dt"], _stream(stream))
     _check("csa_compress_kv", st)
+
+
+def csa_compress_indexer_topk(k, v, logits, k_out, v_out, k_scale_out, v_scale_out, q_codes, q_e8m0, w,
+                              k_codes, k_e8m0, q_pos0, m, k_sel, idx=None, L=None, row0=0, entry0=0,
+                              stream=None):
+    """csa_compress_kv(k, v, logits, m, k_out, ...) and csa_indexer_topk(q_codes, ..., m, k_sel) in one call.
+
+    The compression's sequences are the indexer's (k.shape[0] == q_codes.shape[0]); returns idx.
+    """
+    B, T_q, H_I, half = q_codes.shape
+    cap = k_codes.shape[1]
+    c = _compress_ptrs(k, v, logits, m, k_out, v_out, k_scale_out, v_scale_out, L, row0, entry0)
+    if c["B"] != B:
+        raise ValueError("the compression and the indexer must cover the same sequences")
+    if idx is None:
+        idx = torch.empty((B, T_q, k_sel), dtype=torch.int32, device=q_codes.device)
+    lib = load()
+    ws = _workspace(q_codes.device, lib.csa_workspace_size(CSA_OP_INDEXER_TOPK, B, T_q, 0, 2 * half, cap))
+    st = lib.csa_compress_indexer_topk(c["k"], c["v"], c["in_dt"], c["logits"], c["L"], c["ld_in"], c["d"],
+                                       c["k_out"], c["v_out"], c["k_scale"], c["v_scale"], c["ld_out"],
+                                       c["out_dt"], _ptr(q_codes), _ptr(q_e8m0), _ptr(w), _ptr(k_codes),
+                                       _ptr(k_e8m0), _ptr(q_pos0), B, T_q, H_I, 2 * half, cap, m, k_sel,
+                                       _ptr(idx), _ws_ptr(ws), _ws_len(ws), _stream(stream))
+    _check("csa_compress_indexer_topk", st)
+    return idx
 
 
 def csa_indexer_scores(q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, m, scores=None, stream=None):

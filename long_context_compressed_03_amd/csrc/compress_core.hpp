@@ -1,0 +1,153 @@
+// Softmax-pool compression of short blocks (m < 32), one entry per 16-lane
+// group: shared by the compression kernels and by the launch that runs the
+// compression beside the decode indexer pass.
+//
+// The pages (blog.nickys.cn DeepSeek-V4 post, 三大架构改动 §1 CSA and §2 HCA)
+// state that every m (resp. m') tokens' K/V become one entry; the pooling rule
+// (softmax weights from one logit per token, shared by K and V) is this
+// library's reading.
+#pragma once
+#include "common.hpp"
+
+namespace csa_cmp {
+
+constexpr int kGroup = 16;            // lanes per entry
+constexpr int kColsPerLane = 8;       // 16 lanes x 8 = 128 head columns
+
+template <int kInF32>
+CSA_DEV void load_row8(const void* base, size_t row, int lane_c, float* out) {
+  if constexpr (kInF32) {
+    const v4f* p = reinterpret_cast<const v4f*>(static_cast<const float*>(base) + row * kHeadDim + lane_c * 8);
+    v4f a = __builtin_nontemporal_load(p);
+    v4f b = __builtin_nontemporal_load(p + 1);
+    out[0] = a[0]; out[1] = a[1]; out[2] = a[2]; out[3] = a[3];
+    out[4] = b[0]; out[5] = b[1]; out[6] = b[2]; out[7] = b[3];
+  } else {
+    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + row * kHeadDim + lane_c * 8);
+    u32x4 a = __builtin_nontemporal_load(p);
+    uint32_t w[4] = {a[0], a[1], a[2], a[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+}
+
+template <int kOut>
+CSA_DEV void store_entry(void* out, float* scale_out, size_t entry, int lane_c, const float* x) {
+  if constexpr (kOut == CSA_F32) {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + entry * kHeadDim + lane_c * 8);
+    p[0] = make_float4(x[0], x[1], x[2], x[3]);
+    p[1] = make_float4(x[4], x[5], x[6], x[7]);
+  } else if constexpr (kOut == CSA_BF16) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = uint32_t(f32_to_bf16(x[2 * i])) | (uint32_t(f32_to_bf16(x[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + entry * kHeadDim + lane_c * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    amax = group_max<kGroup>(amax);
+    const float scale = amax > 0.f ? amax / 448.f : 1.f;
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i >> 2] |= f32_to_e4m3(x[i] / scale) << (8 * (i & 3));
+    *reinterpret_cast<uint2*>(static_cast<uint8_t*>(out) + entry * kHeadDim + lane_c * 8) = make_uint2(w[0], w[1]);
+    if (lane_c == 0) scale_out[entry] = scale;
+  }
+}
+
+// Entry gid (< B * n_entries) by the 16-lane group whose lane lane_c owns
+// head columns [8 lane_c, 8 lane_c + 8); rows are walked with 4 loads in
+// flight per lane for each of K and V.
+template <int kInF32, int kOut>
+CSA_DEV void compress_group(const void* __restrict__ k, const void* __restrict__ v, const float* __restrict__ logits,
+                            int n_entries, int ld_in, int m, void* k_out, void* v_out, float* k_scale, float* v_scale,
+                            int ld_out, long gid, int lane_c) {
+  const int b = int(gid / n_entries);
+  const int e = int(gid - long(b) * n_entries);
+  const size_t row0 = size_t(b) * ld_in + size_t(e) * m;
+  const float* z = logits + row0;
+
+  // softmax statistics of the block's logits, spread over the 16 lanes;
+  // computed after the first rows are requested, so the two memory round
+  // trips overlap
+  float zmax = 0.f, inv = 0.f;
+  auto stats = [&]() {
+    zmax = -INFINITY;
+    for (int x = lane_c; x < m; x += kGroup) zmax = fmaxf(zmax, z[x]);
+    zmax = group_max<kGroup>(zmax);
+    float zsum = 0.f;
+    for (int x = lane_c; x < m; x += kGroup) zsum += expf(z[x] - zmax);
+    zsum = group_sum<kGroup>(zsum);
+    inv = 1.f / zsum;
+  };
+
+  float ak[8], av[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { ak[i] = 0.f; av[i] = 0.f; }
+
+  constexpr int kU = 4;
+  int j = 0;
+  for (; j + kU <= m; j += kU) {
+    float kr[kU][8], vr[kU][8], a[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      load_row8<kInF32>(k, row0 + j + u, lane_c, kr[u]);
+      load_row8<kInF32>(v, row0 + j + u, lane_c, vr[u]);
+    }
+    if (j == 0) stats();
+#pragma unroll
+    for (int u = 0; u < kU; ++u) a[u] = expf(z[j + u] - zmax) * inv;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ak[i] = fmaf(a[u], kr[u][i], ak[i]);
+        av[i] = fmaf(a[u], vr[u][i], av[i]);
+      }
+    }
+  }
+  if (m < kU) stats();
+  for (; j < m; ++j) {
+    float kr[8], vr[8];
+    load_row8<kInF32>(k, row0 + j, lane_c, kr);
+    load_row8<kInF32>(v, row0 + j, lane_c, vr);
+    const float a = expf(z[j] - zmax) * inv;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ak[i] = fmaf(a, kr[i], ak[i]);
+      av[i] = fmaf(a, vr[i], av[i]);
+    }
+  }
+  const size_t entry = size_t(b) * ld_out + e;
+  store_entry<kOut>(k_out, k_scale, entry, lane_c, ak);
+  store_entry<kOut>(v_out, v_scale, entry, lane_c, av);
+}
+
+// The arguments of one compression call.
+struct CompressArgs {
+  const void* k;
+  const void* v;
+  const float* logits;
+  int in_dtype, B, L, ld_in, m, ld_out, out_dtype;
+  void* k_out;
+  void* v_out;
+  float* k_scale;
+  float* v_scale;
+};
+
+inline csa_status_t check_compress_args(const CompressArgs& c, int d) {
+  if (!c.k || !c.v || !c.logits || !c.k_out || !c.v_out) return CSA_EINVAL;
+  if (c.in_dtype != CSA_BF16 && c.in_dtype != CSA_F32) return CSA_EINVAL;
+  if (!csa_dtype_ok(c.out_dtype)) return CSA_EINVAL;
+  if (d != kHeadDim || c.m < 1 || c.B < 0 || c.L < 0 || c.L % c.m != 0 || c.ld_in < c.L) return CSA_EINVAL;
+  if (c.ld_out < c.L / c.m) return CSA_EINVAL;
+  if (c.out_dtype == CSA_FP8_E4M3 && (!c.k_scale || !c.v_scale)) return CSA_EINVAL;
+  if (long(c.B) * (c.L / c.m) > 0x7FFFFFFFL) return CSA_EINVAL;
+  return CSA_OK;
+}
+
+}  // namespace csa_cmp

@@ -794,21 +794,33 @@ size_t csa_indexer_topk_workspace_size(long rows, int T_q, int d_I, int cap) {
   return size_t(rows) * size_t(cap) * 2u;
 }
 
-extern "C" csa_status_t csa_indexer_topk(const uint8_t* q_codes, const uint8_t* q_e8m0, const float* w,
-                                         const uint8_t* k_codes, const uint8_t* k_e8m0, const int32_t* q_pos0,
-                                         int32_t B, int32_t T_q, int32_t H_I, int32_t d_I, int32_t cap, int32_t m,
-                                         int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+// csa_indexer_topk, with an optional short-block compression (arguments
+// already checked) that runs before the selection's results are needed: on
+// the decode path it rides in the row pass's launch, otherwise it is its own
+// launch ahead of the indexer.
+csa_status_t indexer_topk_impl(const uint8_t* q_codes, const uint8_t* q_e8m0, const float* w, const uint8_t* k_codes,
+                               const uint8_t* k_e8m0, const int32_t* q_pos0, int32_t B, int32_t T_q, int32_t H_I,
+                               int32_t d_I, int32_t cap, int32_t m, int32_t k, int32_t* idx, void* ws,
+                               size_t ws_bytes, hipStream_t st, const csa_cmp::CompressArgs* ride) {
   if (!idx || k < 1) return CSA_EINVAL;
   const csa_status_t s = csa_ix::check_indexer_args(q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, B, T_q, H_I, d_I,
                                                     cap, m);
   if (s != CSA_OK) return s;
   if (k > 32767) return CSA_ENOTSUP;
   const long rows = long(B) * T_q;
-  if (rows == 0) return CSA_OK;
   if (rows > 0x7FFFFFFFL) return CSA_ENOTSUP;
-  const size_t need = csa_indexer_topk_workspace_size(rows, T_q, d_I, cap);
+  const size_t need = rows == 0 ? 0 : csa_indexer_topk_workspace_size(rows, T_q, d_I, cap);
   if (need > 0 && (!ws || ws_bytes < need)) return CSA_EWORKSPACE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool ride_along = ride && rows > 0 && ride->m < 32 && use_fused_split(rows, T_q, d_I, cap);
+  if (ride && !ride_along) {
+    const csa_status_t c = csa_compress_kv(ride->k, ride->v, ride->in_dtype, ride->logits, ride->B, ride->L,
+                                           ride->ld_in, kHeadDim, ride->m, ride->k_out, ride->v_out, ride->k_scale,
+                                           ride->v_scale, ride->ld_out, ride->out_dtype, st);
+    if (c != CSA_OK) return c;
+  }
+  if (rows == 0) return CSA_OK;
   const int ks = (d_I + 127) / 128;
   if (use_fused_split(rows, T_q, d_I, cap)) {
     float* scores = static_cast<float*>(ws);
@@ -821,7 +833,8 @@ extern "C" csa_status_t csa_indexer_topk(const uint8_t* q_codes, const uint8_t* 
       default: e = launch_indexer_slice_h<16>(ks, B, st, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, d_I, cap, m, k, scores, sw); break;
     }
     if (e != hipSuccess) return CSA_EHIP;
-    e = csa_split::launch_topk_split_rows(rows, st, scores, q_pos0, 1, cap, m, k, idx, sw);
+    e = csa_split::launch_topk_split_rows(rows, st, scores, q_pos0, 1, cap, m, k, idx, sw,
+                                          ride_along ? ride : nullptr);
     return e == hipSuccess ? CSA_OK : CSA_EHIP;
   }
   uint16_t* key16 = static_cast<uint16_t*>(ws);
@@ -837,4 +850,30 @@ extern "C" csa_status_t csa_indexer_topk(const uint8_t* q_codes, const uint8_t* 
     default: err = launch_select_h<16>(ks, rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_q, d_I, cap, m, k, idx); break;
   }
   return err == hipSuccess ? CSA_OK : CSA_EHIP;
+}
+
+}  // namespace
+
+extern "C" csa_status_t csa_indexer_topk(const uint8_t* q_codes, const uint8_t* q_e8m0, const float* w,
+                                         const uint8_t* k_codes, const uint8_t* k_e8m0, const int32_t* q_pos0,
+                                         int32_t B, int32_t T_q, int32_t H_I, int32_t d_I, int32_t cap, int32_t m,
+                                         int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  return indexer_topk_impl(q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, B, T_q, H_I, d_I, cap, m, k, idx, ws,
+                           ws_bytes, static_cast<hipStream_t>(stream), nullptr);
+}
+
+extern "C" csa_status_t csa_compress_indexer_topk(const void* k, const void* v, int32_t in_dtype, const float* logits,
+                                                  int32_t L, int32_t ld_in, int32_t d, void* k_out, void* v_out,
+                                                  float* k_scale_out, float* v_scale_out, int32_t ld_out,
+                                                  int32_t out_dtype, const uint8_t* q_codes, const uint8_t* q_e8m0,
+                                                  const float* w, const uint8_t* k_codes, const uint8_t* k_e8m0,
+                                                  const int32_t* q_pos0, int32_t B, int32_t T_q, int32_t H_I,
+                                                  int32_t d_I, int32_t cap, int32_t m, int32_t k_sel, int32_t* idx,
+                                                  void* ws, size_t ws_bytes, void* stream) {
+  const csa_cmp::CompressArgs ca{k, v, logits, in_dtype, B, L, ld_in, m, ld_out, out_dtype,
+                                 k_out, v_out, k_scale_out, v_scale_out};
+  const csa_status_t c = csa_cmp::check_compress_args(ca, d);
+  if (c != CSA_OK) return c;
+  return indexer_topk_impl(q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, B, T_q, H_I, d_I, cap, m, k_sel, idx, ws,
+                           ws_bytes, static_cast<hipStream_t>(stream), &ca);
 }

@@ -20,6 +20,7 @@
 // take the fallback.
 #pragma once
 #include "select.hpp"
+#include "compress_core.hpp"
 
 namespace csa_split {
 
@@ -173,8 +174,12 @@ CSA_DEV void slice_empty(size_t slot, const SplitWs& ws) {
 }
 
 // The row pass of the split path (one 1024-thread block per row) over the
-// slice results in `ws`; `scores` [rows][cap] serve its fallback.
+// slice results in `ws`; `scores` [rows][cap] serve its fallback.  `ride`, if
+// not null, is a short-block compression (m < 32, arguments already checked)
+// run by extra blocks of the same launch; it must touch nothing the row pass
+// reads or writes.
 hipError_t launch_topk_split_rows(long rows, hipStream_t st, const float* scores, const int32_t* q_pos0, int T_q,
-                                  int cap, int m, int k, int32_t* idx, const SplitWs& ws);
+                                  int cap, int m, int k, int32_t* idx, const SplitWs& ws,
+                                  const csa_cmp::CompressArgs* ride = nullptr);
 
 }  // namespace csa_split

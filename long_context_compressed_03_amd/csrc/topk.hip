@@ -51,6 +51,7 @@
 // here needs scratch memory: a kernel with scratch waits several
 // microseconds longer for its dispatch.
 #include "split.hpp"
+#include "compress_core.hpp"
 
 namespace {
 
@@ -373,14 +374,45 @@ CSA_DEV bool list_select_emit(int nc, uint32_t lo, uint32_t hi, uint32_t top, in
   return true;
 }
 
+// Blocks past the rows of a split-path launch: a short-block compression
+// (m < 32) that rides along on CUs the rows leave idle, 64 entries per block
+// (one 16-lane group each).  The launch that adds these blocks guarantees that
+// the compression touches nothing the selection reads or writes.
+CSA_DEV void compress_part(const csa_cmp::CompressArgs& c, int blk) {
+  using namespace csa_cmp;
+  const int ne = c.L / c.m;
+  const long gid = long(blk) * (kThreads / kGroup) + int(threadIdx.x) / kGroup;
+  if (gid >= long(c.B) * ne) return;   // whole 16-lane groups leave together
+  const int lane_c = threadIdx.x & (kGroup - 1);
+#define CSA_RIDE(F, O) \
+  compress_group<F, O>(c.k, c.v, c.logits, ne, c.ld_in, c.m, c.k_out, c.v_out, c.k_scale, c.v_scale, c.ld_out, gid, lane_c)
+  if (c.in_dtype == CSA_F32) {
+    if (c.out_dtype == CSA_F32) CSA_RIDE(1, CSA_F32);
+    else if (c.out_dtype == CSA_BF16) CSA_RIDE(1, CSA_BF16);
+    else CSA_RIDE(1, CSA_FP8_E4M3);
+  } else {
+    if (c.out_dtype == CSA_F32) CSA_RIDE(0, CSA_F32);
+    else if (c.out_dtype == CSA_BF16) CSA_RIDE(0, CSA_BF16);
+    else CSA_RIDE(0, CSA_FP8_E4M3);
+  }
+#undef CSA_RIDE
+}
+
 template <bool kSplit>
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores,
                                                         const int32_t* __restrict__ q_pos0, int T_q, int cap, int m,
-                                                        int k, int32_t* __restrict__ idx, SplitWs ws, int G) {
+                                                        int k, int32_t* __restrict__ idx, SplitWs ws, int G, int rows,
+                                                        csa_cmp::CompressArgs ride) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   RowShared& rs = *reinterpret_cast<RowShared*>(smem_raw);
   Shared& sh = rs.full;
 
+  if constexpr (kSplit) {
+    if (int(blockIdx.x) >= rows) {
+      compress_part(ride, int(blockIdx.x) - rows);
+      return;
+    }
+  }
   const int row = blockIdx.x;
   const int b = row / T_q;
   const int i = row - b * T_q;
@@ -578,7 +610,7 @@ hipError_t launch_topk(long rows, hipStream_t st, const float* scores, const int
     hipError_t e = set_lds_limit<false>();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_kernel<false>, dim3(unsigned(rows)), dim3(kThreads), sizeof(RowShared), st, scores, q_pos0,
-                       T_q, cap, m, k, idx, SplitWs{}, 0);
+                       T_q, cap, m, k, idx, SplitWs{}, 0, int(rows), csa_cmp::CompressArgs{});
     return hipGetLastError();
   }
   const int G = n_slices(cap);
@@ -593,11 +625,19 @@ hipError_t launch_topk(long rows, hipStream_t st, const float* scores, const int
 }  // namespace
 
 hipError_t csa_split::launch_topk_split_rows(long rows, hipStream_t st, const float* scores, const int32_t* q_pos0,
-                                             int T_q, int cap, int m, int k, int32_t* idx, const SplitWs& ws) {
+                                             int T_q, int cap, int m, int k, int32_t* idx, const SplitWs& ws,
+                                             const csa_cmp::CompressArgs* ride) {
   hipError_t e = set_lds_limit<true>();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_kernel<true>, dim3(unsigned(rows)), dim3(kThreads), sizeof(RowShared), st, scores, q_pos0,
-                     T_q, cap, m, k, idx, ws, n_slices(cap));
+  long extra = 0;
+  csa_cmp::CompressArgs c{};
+  if (ride) {
+    c = *ride;
+    const long entries = long(c.B) * (c.L / c.m);
+    extra = (entries + kThreads / csa_cmp::kGroup - 1) / (kThreads / csa_cmp::kGroup);
+  }
+  hipLaunchKernelGGL(topk_kernel<true>, dim3(unsigned(rows + extra)), dim3(kThreads), sizeof(RowShared), st, scores,
+                     q_pos0, T_q, cap, m, k, idx, ws, n_slices(cap), int(rows), c);
   return hipGetLastError();
 }
 

@@ -5,7 +5,7 @@ same order, same shapes), runs one step, and checks sampled outputs against the 
 which can afford a few rows at these sizes:
   * pooled entries written by the step: within one storage unit of the exact pool;
   * indexer scores of sampled rows (decode with separate indexer and top-k calls): bit-exact;
-  * top-k indices of sampled rows (unfused and fused): bit-exact;
+  * top-k indices of sampled rows (unfused, fused, and combined with the compression): bit-exact;
   * attention of sampled rows over the cache as the step left it: max-abs 2e-2 on top of
     the bf16 output's own half-unit rounding.
 The 1M layer pair is checked layer by layer the same way.
@@ -136,11 +136,12 @@ def check_hca_rows(hl, dev, p, rows):
         assert np.all(diff <= attention_tolerance(O[0, 0], "bf16"))
 
 
-def test_csa_decode_128k(csa):
-    hosts, dev, st = run_workload("csa_decode_128k")
+@pytest.mark.parametrize("indexer,call", [("auto", "compress_indexer_topk"), ("fused", "indexer_topk")])
+def test_csa_decode_128k(csa, indexer, call):
+    hosts, dev, st = run_workload("csa_decode_128k", indexer=indexer)
     (p, hl), = hosts
-    assert "indexer_topk" in st.order
-    say("csa_decode_128k: pooled entry, fused top-k and attention of sampled rows")
+    assert call in st.order
+    say(f"csa_decode_128k ({call}): pooled entry, fused top-k and attention of sampled rows")
     check_compress(hl, dev, p, [0])
     check_csa_rows(hl, dev, p, [(0, 0), (7, 0), (15, 0)], unfused=False)
 
