@@ -39,23 +39,25 @@ inline bool use_split(long rows, int cap) {
   return rows <= kSplitMaxRows && cap >= kSplitMinCap && n_slices(cap) <= kMaxSlices;
 }
 
-// Workspace of the split path: bounds [rows][G], counts [rows][G], candidate
-// keys and indices [rows][G][kSliceCap].
+// Workspace of the split path: bounds [rows][G], counts [rows][G], largest
+// keys [rows][G], candidate keys and indices [rows][G][kSliceCap].
 struct SplitWs {
   uint32_t* bound;
   uint32_t* count;
+  uint32_t* top;
   uint32_t* key;
   int32_t* idx;
 };
 inline size_t split_ws_bytes(long rows, int cap) {
-  return size_t(rows) * n_slices(cap) * (2 * sizeof(uint32_t) + kSliceCap * (sizeof(uint32_t) + sizeof(int32_t)));
+  return size_t(rows) * n_slices(cap) * (3 * sizeof(uint32_t) + kSliceCap * (sizeof(uint32_t) + sizeof(int32_t)));
 }
 inline SplitWs split_ws(void* ws, long rows, int cap) {
   const size_t n = size_t(rows) * n_slices(cap);
   SplitWs w;
   w.bound = static_cast<uint32_t*>(ws);
   w.count = w.bound + n;
-  w.key = w.count + n;
+  w.top = w.count + n;
+  w.key = w.top + n;
   w.idx = reinterpret_cast<int32_t*>(w.key + n * kSliceCap);
   return w;
 }
@@ -73,6 +75,11 @@ CSA_DEV uint32_t wave_umax(uint32_t v) {
   for (int o = 32; o > 0; o >>= 1) v = max(v, uint32_t(__shfl_xor(int(v), o)));
   return v;
 }
+CSA_DEV uint32_t wave_umin(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, uint32_t(__shfl_xor(int(v), o)));
+  return v;
+}
 
 // What slice_finish expects before its call, behind a barrier: the window
 // histogram cleared and sh.smax[w] = the largest key wave w holds (or wrote).
@@ -86,8 +93,8 @@ CSA_DEV void clear_window(SliceShared& sh) {
 // The slice pass on keys already in registers, by a block of kT threads
 // (256 or 1024): thread t holds the keys of indices base + j*kT + t (0 for
 // entries past the visible count); n_s > 0 visible entries in the slice,
-// nv > k in the row.  Writes count[slot], bound[slot] and the slot's
-// candidates.  Every thread of the block calls it, after a barrier that
+// nv > k in the row.  Writes count[slot], bound[slot], top[slot] (the
+// slice's largest key, one of its candidates) and the slot's candidates.  Every thread of the block calls it, after a barrier that
 // follows clear_window and the waves' sh.smax writes.
 template <int kT>
 CSA_DEV void slice_finish(const uint32_t (&key)[kSlice / kT], int base, int n_s, int nv, int k, size_t slot,
@@ -162,6 +169,7 @@ CSA_DEV void slice_finish(const uint32_t (&key)[kSlice / kT], int base, int n_s,
   if (tid == 0) {
     ws.count[slot] = total;
     ws.bound[slot] = lo;
+    ws.top[slot] = mx;
   }
 }
 
@@ -170,6 +178,7 @@ CSA_DEV void slice_empty(size_t slot, const SplitWs& ws) {
   if (threadIdx.x == 0) {
     ws.count[slot] = 0u;
     ws.bound[slot] = 0u;
+    ws.top[slot] = 0u;
   }
 }
 

@@ -184,11 +184,72 @@ __global__ __launch_bounds__(kSliceThreads) void slice_select_kernel(const float
 // Returns the list size, or -1 (block-uniform) when the candidates do not
 // fit; lo / hi = min / max over the slices' bounds (empty slices ignored),
 // top = max candidate key.
+// Pass c, gathering, for rows of at most 64 slices: every wave reads the
+// counts, bounds and largest keys of all the row's slices itself (lane x:
+// slice x) and takes their prefix sums, the bounds and the largest key with
+// wave operations, so the only barrier is the one that publishes the list.
+// Same results and contract as gather_list.
+CSA_DEV int gather_list_wave(const SplitWs& ws, int row, int G, int k, ListShared& sh, uint32_t& lo, uint32_t& hi,
+                             uint32_t& top) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int kWaves = kThreads / 64;
+  const size_t rbase = size_t(row) * G;
+  const bool own = lane < G;
+  const size_t at_s = rbase + (own ? lane : 0);   // address-selected: every lane loads
+  const uint32_t c_raw = ws.count[at_s], b_raw = ws.bound[at_s], t_raw = ws.top[at_s];
+  const int spw_need = (G + kWaves - 1) / kWaves;
+  const int spw = spw_need <= 1 ? 1 : spw_need <= 2 ? 2 : spw_need <= 4 ? 4 : 8;
+  const int per = kPreLoads / spw;
+  uint32_t pk[kPreLoads];
+  int32_t pi[kPreLoads];
+#pragma unroll
+  for (int i = 0; i < kPreLoads; ++i) {
+    const int sl = w + kWaves * (i / per);
+    const size_t at = (rbase + (sl < G ? sl : 0)) * kSliceCap + lane + 64 * (i % per);
+    pk[i] = sl < G ? ws.key[at] : 0u;
+    pi[i] = sl < G ? ws.idx[at] : 0;
+  }
+  const uint32_t cl = own ? c_raw : 0u;
+  const uint32_t bl = own ? b_raw : 0u;
+  const uint32_t incl = wave_inclusive_scan(cl);
+  const uint32_t total = uint32_t(__shfl(int(incl), 63));
+  const uint32_t excl = incl - cl;
+  lo = wave_umin(bl != 0u ? bl : 0xFFFFFFFFu);
+  hi = wave_umax(bl);
+  top = wave_umax(own ? t_raw : 0u);
+  const bool over = __ballot(cl > uint32_t(kSliceCap)) != 0ull;
+  if (over || total > uint32_t(kList) || total < uint32_t(k)) return -1;   // every wave sees the same
+#pragma unroll
+  for (int i = 0; i < kPreLoads; ++i) {
+    const int sl = w + kWaves * (i / per);
+    if (sl < G) {
+      const uint32_t o = uint32_t(__shfl(int(excl), sl)), n = uint32_t(__shfl(int(cl), sl));
+      const uint32_t x = uint32_t(lane + 64 * (i % per));
+      if (x < n) {
+        sh.key[o + x] = pk[i];
+        sh.idx[o + x] = pi[i];
+      }
+    }
+  }
+  // the rest: entries past the early ones, and the slices beyond them
+  for (int sl = w; sl < G; sl += kWaves) {
+    const uint32_t o = uint32_t(__shfl(int(excl), sl)), n = uint32_t(__shfl(int(cl), sl));
+    const uint32_t x0 = sl < w + kWaves * spw ? uint32_t(64 * per) : 0u;
+    for (uint32_t x = x0 + lane; x < n; x += 64) {
+      sh.key[o + x] = ws.key[(rbase + sl) * kSliceCap + x];
+      sh.idx[o + x] = ws.idx[(rbase + sl) * kSliceCap + x];
+    }
+  }
+  __syncthreads();
+  return int(total);
+}
+
 CSA_DEV int gather_list(const SplitWs& ws, int row, int G, int k, ListShared& sh, uint32_t& lo, uint32_t& hi,
                         uint32_t& top) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   constexpr int kWaves = kThreads / 64;
   const size_t rbase = size_t(row) * G;
+  if (G <= 64) return gather_list_wave(ws, row, G, k, sh, lo, hi, top);
   const uint32_t c = tid < G ? ws.count[rbase + tid] : 0u;
   const uint32_t bnd = tid < G ? ws.bound[rbase + tid] : 0u;
   uint32_t b = bnd != 0u ? bnd : 0xFFFFFFFFu;
