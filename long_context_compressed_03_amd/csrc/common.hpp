@@ -154,8 +154,10 @@ CSA_DEV uint32_t wave_inclusive_scan(uint32_t v) {
 
 // Block-wide exclusive prefix sum of one uint32 per thread (blockDim.x a
 // multiple of 64, at most 1024).  `smem` needs blockDim.x/64 + 1 words.
-// Returns the exclusive prefix; *total receives the block sum.
-CSA_DEV uint32_t block_exclusive_scan(uint32_t v, uint32_t* smem, uint32_t* total) {
+// Returns the exclusive prefix; *total receives the block sum.  tail_sync:
+// end with a barrier so that `smem` may be written again right away (a last
+// use of `smem` in the kernel can skip it).
+CSA_DEV uint32_t block_exclusive_scan(uint32_t v, uint32_t* smem, uint32_t* total, bool tail_sync = true) {
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
@@ -171,7 +173,7 @@ CSA_DEV uint32_t block_exclusive_scan(uint32_t v, uint32_t* smem, uint32_t* tota
   __syncthreads();
   uint32_t r = smem[wid] + incl - v;
   *total = smem[16];
-  __syncthreads();
+  if (tail_sync) __syncthreads();
   return r;
 }
 

@@ -184,6 +184,13 @@ __global__ __launch_bounds__(kSliceThreads) void slice_select_kernel(const float
 // Returns the list size, or -1 (block-uniform) when the candidates do not
 // fit; lo / hi = min / max over the slices' bounds (empty slices ignored),
 // top = max candidate key.
+// The selection's histogram and rank counter start at zero: cleared by the
+// gathers before their last barrier (the list does not overlap them).
+CSA_DEV void clear_list_hist(ListShared& sh) {
+  for (int j = threadIdx.x; j < kListBuckets; j += kThreads) sh.hist[j] = 0u;
+  if (threadIdx.x == 0) sh.n_rank = 0u;
+}
+
 // Pass c, gathering, for rows of at most 64 slices: every wave reads the
 // counts, bounds and largest keys of all the row's slices itself (lane x:
 // slice x) and takes their prefix sums, the bounds and the largest key with
@@ -231,6 +238,7 @@ CSA_DEV int gather_list_wave(const SplitWs& ws, int row, int G, int k, ListShare
       }
     }
   }
+  clear_list_hist(sh);
   // the rest: entries past the early ones, and the slices beyond them
   for (int sl = w; sl < G; sl += kWaves) {
     const uint32_t o = uint32_t(__shfl(int(excl), sl)), n = uint32_t(__shfl(int(cl), sl));
@@ -317,6 +325,7 @@ CSA_DEV int gather_list(const SplitWs& ws, int row, int G, int k, ListShared& sh
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = max(mx, uint32_t(__shfl_xor(int(mx), o)));
   if (lane == 0) sh.wred[32 + w] = mx;
+  clear_list_hist(sh);
   __syncthreads();
   top = sh.wred[32];
 #pragma unroll
@@ -336,9 +345,7 @@ CSA_DEV int gather_list(const SplitWs& ws, int row, int G, int k, ListShared& sh
 CSA_DEV bool list_select_emit(int nc, uint32_t lo, uint32_t hi, uint32_t top, int k, int32_t* __restrict__ out,
                               ListShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int j = tid; j < kListBuckets; j += kThreads) sh.hist[j] = 0u;
-  if (tid == 0) sh.n_rank = 0u;
-  __syncthreads();
+  // sh.hist and sh.n_rank were cleared by the gather, behind its last barrier
   const uint32_t range = top - lo;
   const int bits = range == 0u ? 0 : 32 - __clz(range);
   const int shift = bits > kListBits ? bits - kListBits : 0;
@@ -420,7 +427,7 @@ CSA_DEV bool list_select_emit(int nc, uint32_t lo, uint32_t hi, uint32_t top, in
     n_eq += km == prefix ? 1u : 0u;
   }
   uint32_t tot;
-  const uint32_t ex = block_exclusive_scan((n_eq << 16) | n_gt, sh.smem, &tot);
+  const uint32_t ex = block_exclusive_scan((n_eq << 16) | n_gt, sh.smem, &tot, false);   // last use of smem
   uint32_t gt_before = ex & 0xFFFFu, eq_before = ex >> 16;
   for (int x = x0; x < x1; ++x) {
     const uint32_t km = sh.key[x] & mask;
