@@ -48,7 +48,7 @@ constexpr int kBatch = 4;              // rounds streamed per batch (16 loads in
 constexpr int kList = 4096;            // capacity of the LDS entry lists
 constexpr int kWinPer = kList / (kThreads / 64);   // window-list slots of each wave
 constexpr int kBuckets = 1 << 14;      // 14-bit buckets of the 16-bit keys
-constexpr int kMaxJ = 16;              // rounds held in registers, largest variant
+constexpr int kMaxJ = 20;              // rounds held in registers, largest variant
 constexpr int kMaxWords = kMaxJ * kRound / 32;
 static_assert(kMaxJ % kBatch == 0, "chunks are whole batches of rounds");
 
@@ -331,7 +331,8 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const uint16_t* __rest
                                                           const int32_t* __restrict__ q_pos0, int T_q, int d_I,
                                                           int cap, int m, int k, int32_t* __restrict__ idx) {
   constexpr int kS = kJ * kRound;          // keys per chunk; chunk 0 stays in registers
-  constexpr int kWPT = kS / 32 / kThreads;  // bitmap words per thread
+  constexpr int kWPT = (kS / 32 + kThreads - 1) / kThreads;  // bitmap words per thread (the last ones may be past the chunk)
+  static_assert(kS < (1 << 17), "a chunk's equal counts fit 17 bits");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   Shared& sh = *reinterpret_cast<Shared*>(smem_raw);
 
@@ -592,14 +593,16 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const uint16_t* __rest
       }
       __syncthreads();
     }
-    // thread t owns bitmap words [t*kWPT, (t+1)*kWPT); greater counts fit 15
-    // bits (at most k < 32768) and equal counts 17 bits (<= keys per chunk)
+    // thread t owns bitmap words [t*kWPT, (t+1)*kWPT) (words past the chunk's
+    // kS/32 read as empty); greater counts fit 15 bits (at most k < 32768) and
+    // equal counts 17 bits (<= keys per chunk)
     uint32_t wg[kWPT], we[kWPT];
     uint32_t n_g = 0u, n_e = 0u;
 #pragma unroll
     for (int x = 0; x < kWPT; ++x) {
-      wg[x] = sh.bm.gt[tid * kWPT + x];
-      we[x] = sh.bm.eq[tid * kWPT + x];
+      const int wi = tid * kWPT + x;
+      wg[x] = wi < kS / 32 ? sh.bm.gt[wi] : 0u;
+      we[x] = wi < kS / 32 ? sh.bm.eq[wi] : 0u;
       n_g += __popc(wg[x]);
       n_e += __popc(we[x]);
     }
@@ -768,9 +771,12 @@ hipError_t launch_select_ks(long rows, hipStream_t st, const uint16_t* key16, co
                             const float* w, const uint8_t* kc, const uint8_t* ke, const int32_t* pos, int T_q,
                             int d_I, int cap, int m, int k, int32_t* idx) {
   // rows of up to 32768 keys are held whole in 8 rounds of registers; longer
-  // rows keep their first 65536 keys in 16 rounds and read the rest
+  // rows keep their first 81920 keys in 20 rounds (65536 in 16 when d_I > 128
+  // leaves fewer registers free) and read the rest
   if (cap <= 8 * kRound)
     return launch_select_j<kHI, kKS, 8>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx);
+  if constexpr (kKS == 1)
+    return launch_select_j<kHI, kKS, 20>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx);
   return launch_select_j<kHI, kKS, 16>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx);
 }
 

@@ -45,7 +45,9 @@ FUSED_CASES = [
     # B, T, cap, H_I, d_I, m, k, pos0 list, tie_heavy
     (1, 1, 1024, 4, 64, 4, 64, [4095], False),                     # tiny decode shape
     (3, 1, 32768, 8, 128, 4, 1024, [131071, 100000, 2000], False),  # 128K decode rows; one row < k
-    (1, 6, 70000, 8, 128, 4, 2048, [279990], False),               # rows past the register chunk
+    (1, 6, 70000, 8, 128, 4, 2048, [279990], False),               # rows held whole in 20 register rounds
+    (1, 3, 90000, 8, 128, 4, 2048, [359990], False),               # rows past the 20-round register chunk
+    (1, 3, 70000, 16, 256, 4, 1000, [279990], False),              # d_I = 256: rows past its 16-round chunk
     (2, 33, 5000, 8, 128, 4, 100, [19900, 300], False),            # ragged chunk rows; early rows < k
     (1, 4, 20000, 4, 64, 4, 500, [79990], True),                   # threshold among exact ties
     (1, 3, 3000, 16, 256, 2, 200, [5990], False),                  # 16 heads, two contraction steps
@@ -123,7 +125,8 @@ def test_fused_decode_crowded_rows(csa):
 
 
 @pytest.mark.parametrize("B,T,cap,k,pos", [
-    (1, 64, 70000, 2048, [279900]),     # prefill chunk rows past the register chunk
+    (1, 64, 70000, 2048, [279900]),     # prefill chunk rows held whole in registers
+    (1, 16, 90000, 2048, [359900]),     # prefill chunk rows past the register chunk
     (4, 1, 32768, 1024, [131071] * 4),  # decode rows
 ])
 def test_fused_equals_unfused_on_inexact_scores(csa, B, T, cap, k, pos):
