@@ -67,6 +67,34 @@ def test_compress_rejects_bad_arguments():
     assert call(B=0) == csa.CSA_OK                # empty: nothing to do, nothing launched
 
 
+def test_compress_indexer_topk_rejects_bad_arguments():
+    """Either part's argument errors are reported before anything is enqueued (no device
+    work: these calls run on the host alone); B = 0 is an empty call."""
+    import long_context_compressed_03_amd as csa
+    lib = csa.load()
+    ok = dict(k=_p(), v=_p(), in_dt=0, lg=_p(), L=4, ld_in=8, d=128, ko=_p(), vo=_p(), ks=None,
+              vs=None, ld_out=2, out_dt=0, q=_p(), B=2, T=1, H_I=8, d_I=128, cap=16384, m=4, ksel=64,
+              idx=_p(), ws=None, wsb=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.csa_compress_indexer_topk(a["k"], a["v"], a["in_dt"], a["lg"], a["L"], a["ld_in"],
+                                             a["d"], a["ko"], a["vo"], a["ks"], a["vs"], a["ld_out"],
+                                             a["out_dt"], a["q"], _p(), _p(), _p(), _p(), _p(), a["B"],
+                                             a["T"], a["H_I"], a["d_I"], a["cap"], a["m"], a["ksel"],
+                                             a["idx"], a["ws"], a["wsb"], None)
+    assert call(k=None) == csa.CSA_EINVAL          # compression part
+    assert call(L=6) == csa.CSA_EINVAL             # L % m != 0
+    assert call(out_dt=2) == csa.CSA_EINVAL        # fp8 entries need scale outputs
+    assert call(d=64) == csa.CSA_EINVAL
+    assert call(q=None) == csa.CSA_EINVAL          # indexer part
+    assert call(H_I=5) == csa.CSA_ENOTSUP          # head counts are 4, 8 or 16
+    assert call(ksel=0) == csa.CSA_EINVAL
+    assert call(idx=None) == csa.CSA_EINVAL
+    assert call() == csa.CSA_EWORKSPACE            # the decode path needs its workspace
+    assert call(B=0) == csa.CSA_OK                 # empty: nothing to do, nothing launched
+
+
 def test_indexer_rejects_bad_arguments():
     import long_context_compressed_03_amd as csa
     lib = csa.load()
