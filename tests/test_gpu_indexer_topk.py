@@ -55,6 +55,7 @@ FUSED_CASES = [
     (2, 1, 9000, 4, 64, 4, 300, [35999, 20000], False),            # 4 heads, half-width vectors, partial slices
     (2, 1, 10000, 16, 256, 2, 500, [19999, 15000], False),         # 16 heads, two contraction steps
     (1, 1, 16384, 4, 64, 4, 500, [65535], True),                   # exact ties around the threshold
+    (1, 1, 100000, 8, 128, 4, 2048, [399999], False),              # 49 slices: 4 per gather wave
 ]
 
 

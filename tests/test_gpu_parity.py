@@ -165,6 +165,8 @@ def test_topk_on_indexer_scores(csa):
     (1, 1, 32768, 1024, [131071], 1 << 20),       # the 128K decode row shape
     (1, 3, 700, 700, [2799], 3),                  # k == visible count on the last row
     (1, 2, 33333, 512, [133331], 10),             # unaligned rows, two register tiles
+    (2, 1, 100000, 2048, [399999, 300000], 1 << 20),  # split rows of 49 slices (4 per gather wave)
+    (1, 1, 131072, 1024, [524287], 1 << 20),      # split rows of exactly 64 slices
     (2, 1, 4999, 100, [19995, 100], 50),          # unaligned rows; one row below k
     (1, 2, 20000, 1000, [79999], 3),              # crowded threshold bin: exact radix passes
     (3, 1, 32768, 1024, [131071] * 3, 1 << 16),   # the 128K decode shape, several rows
