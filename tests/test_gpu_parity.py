@@ -375,6 +375,49 @@ def test_runs_are_bitwise_reproducible(csa):
     assert torch.equal(sc[0], sc[1])
 
 
+def test_compress_and_selection_calls_are_bitwise_reproducible(csa):
+    """Repeated calls give identical bits: both compression kernels (fp8 entries with their
+    scales), the fused indexer top-k on a chunk, and the combined decode call."""
+    say("determinism: compression, fused top-k, combined call")
+    B = 3
+    x = compress_inputs(B, 256, "bf16", seed=31, outliers=True)
+    kin, vin, lg = t_kv(x["K"], "bf16"), t_kv(x["V"], "bf16"), t_f32(x["logits"])
+
+    def pool(m):
+        n = 256 // m
+        ko = torch.zeros((B, n, 128), dtype=torch.uint8, device="cuda")
+        vo = torch.zeros_like(ko)
+        ks = torch.zeros((B, n), device="cuda")
+        vs = torch.zeros_like(ks)
+        csa.csa_compress_kv(kin, vin, lg, m, ko, vo, ks, vs)
+        return ko, vo, ks, vs
+    for m in (4, 128):
+        a, b = pool(m), pool(m)
+        torch.cuda.synchronize()
+        assert all(torch.equal(u, v) for u, v in zip(a, b)), m
+
+    ix = indexer_inputs(1, 40, 9000, 8, 128, seed=32)
+    d = (t_u8(ix["q_codes"]), t_u8(ix["q_e8m0"]), t_f32(ix["w"]), t_u8(ix["k_codes"]), t_u8(ix["k_e8m0"]))
+    pos = t_i32(np.array([35000], np.int32))
+    r = [csa.csa_indexer_topk(*d, pos, 4, 700).clone() for _ in range(2)]
+
+    ixd = indexer_inputs(B, 1, 16384, 8, 128, seed=33)
+    dd = (t_u8(ixd["q_codes"]), t_u8(ixd["q_e8m0"]), t_f32(ixd["w"]), t_u8(ixd["k_codes"]),
+          t_u8(ixd["k_e8m0"]), t_i32(np.array([65535, 60000, 40000], np.int32)))
+
+    def combined():
+        ko = torch.zeros((B, 8, 128), dtype=torch.bfloat16, device="cuda")
+        vo = torch.zeros_like(ko)
+        idx = csa.csa_compress_indexer_topk(kin, vin, lg, ko, vo, None, None, *dd, 4, 1024, L=4,
+                                            row0=252, entry0=5)
+        return idx.clone(), ko, vo
+    c1, c2 = combined(), combined()
+    torch.cuda.synchronize()
+    assert torch.equal(r[0], r[1])
+    assert all(torch.equal(u.view(torch.int16) if u.dtype == torch.bfloat16 else u,
+                           v.view(torch.int16) if v.dtype == torch.bfloat16 else v) for u, v in zip(c1, c2))
+
+
 def test_layer_pair_small(csa):
     """A CSA layer then an HCA layer on the same query tokens (decode rows and a chunk),
     against the oracle's layer pair."""
