@@ -13,7 +13,9 @@
 // gathered in chunks of 64 into LDS (K row-major; V transposed so a P*V
 // operand reads 4 or 8 keys of one head dimension as 8-byte words); the next
 // chunk's rows are already in flight in registers while the current one is
-// computed.  Per 16-head tile:
+// computed.  Thread t gathers key pair t/16 and 16-byte segment t%16, so a
+// wave's load covers whole rows and each row's cache lines are requested by
+// one wave.  Per 16-head tile:
 //   S^T[keys x 16 heads] = K * Q^T    (bf16 MFMA 16x16x32, Q held in VGPRs)
 //   online softmax per head in fp32, exp2 domain
 //   O^T[128 x 16 heads] += V^T * P^T  (P^T taken straight from S^T's C layout)

@@ -47,6 +47,9 @@
 //     fails only if one slice holds far more than its share of the top k,
 //     or the ties crowd a slice buffer or the list); otherwise the row
 //     continues with the one-block algorithm above.
+//     The row pass's launch leaves most CUs idle, so a short-block
+//     compression of the same step can ride in it as extra blocks
+//     (csa_compress_indexer_topk).
 // Each thread holds 16 keys per register tile (not 32), so that no kernel
 // here needs scratch memory: a kernel with scratch waits several
 // microseconds longer for its dispatch.
