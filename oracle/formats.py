@@ -158,3 +158,38 @@ def mxfp4_decode(packed, e8m0):
     if sc.shape[-1] != d // MX_BLOCK:
         raise ValueError("one scale per 32-element block")
     return vals * np.repeat(sc, MX_BLOCK, axis=-1)
+
+
+def mxfp4_encode(x):
+    """Real values -> MXFP4 (packed E2M1 codes [..., d/2] uint8, E8M0 scales [..., d/32] uint8).
+
+    OCP Microscaling v1.0 conversion, restated: for each 32-element block the
+    shared exponent is X = floor(log2(amax)) - 2 (2 being E2M1's largest
+    exponent), clamped to the E8M0 range [-127, 127]; an all-zero block takes
+    X = -127 (this library's reading: the spec leaves a zero block's scale
+    free).  Each element x / 2**X is rounded to the nearest E2M1 magnitude,
+    a tie going to the magnitude whose mantissa bit is 0, and magnitudes past
+    6 saturate to 6; the sign bit of x is kept (so -0 encodes as 0x8).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    if d % MX_BLOCK:
+        raise ValueError("MXFP4 length must be a multiple of 32")
+    blocks = x.reshape(x.shape[:-1] + (d // MX_BLOCK, MX_BLOCK))
+    amax = np.abs(blocks).max(axis=-1)
+    _, e = np.frexp(amax)                       # amax = f * 2**e, f in [0.5, 1): floor(log2) = e - 1
+    X = np.where(amax > 0, e - 1 - 2, -127)
+    X = np.clip(X, -127, 127)
+    v = np.ldexp(blocks, -X[..., None])         # exact: a power-of-two scaling
+    mag = np.abs(v)
+    # nearest magnitude; among equally near ones the even code (mantissa bit 0)
+    dist = np.abs(mag[..., None] - E2M1_MAGNITUDES)
+    best = dist.min(axis=-1, keepdims=True)
+    cand = dist == best
+    even = cand & ((np.arange(8) & 1) == 0)
+    code = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    code = np.where(mag > 6.0, 7, code)
+    sign = np.signbit(v).astype(np.int64) << 3
+    nib = (code | sign).reshape(x.shape).astype(np.uint8)
+    packed = (nib[..., 0::2] | (nib[..., 1::2] << 4)).astype(np.uint8)
+    return packed, (X + 127).astype(np.uint8)

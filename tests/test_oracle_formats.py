@@ -6,8 +6,9 @@ import pytest
 import torch
 
 from oracle import brute
+from csa_synth import mxfp4_random, streams
 from oracle.formats import (bf16_decode, bf16_encode, bf16_round, e2m1_decode, e4m3_decode,
-                            e4m3_encode, e4m3_round, mxfp4_decode, unpack_nibbles)
+                            e4m3_encode, e4m3_round, mxfp4_decode, mxfp4_encode, unpack_nibbles)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -124,3 +125,66 @@ def test_mxfp4_packing_and_block_scales():
     assert np.array_equal(v, np.array(brute.mxfp4_vector(codes, e8)))
     with pytest.raises(ValueError):
         mxfp4_decode(codes, np.array([255, 127], np.uint8))
+
+
+# ---------------------------------------------------------- MXFP4 encoder ----
+# OCP Microscaling v1.0 conversion: X = floor(log2(amax)) - 2, elements rounded
+# to nearest E2M1 (ties to the even mantissa bit), saturated at 6.
+
+def test_mxfp4_encode_hand_example():
+    """amax 6 gives X = 0 (E8M0 127); every tie of the E2M1 grid resolved by hand:
+    0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4 (even
+    mantissa bit), 5.5 -> 6 (nearer), -0 keeps its sign bit."""
+    x = np.zeros((1, 32))
+    x[0, :12] = [6.0, -3.0, 0.75, 0.25, 1.25, 1.75, 2.5, 3.5, 5.0, 5.5, -0.0, 0.1]
+    packed, e8 = mxfp4_encode(x)
+    assert e8.tolist() == [[127]]
+    want = [0xD7, 0x02, 0x42, 0x64, 0x76, 0x08] + [0] * 10   # codes 7,D 2,0 2,4 4,6 6,7 8,0
+    assert packed[0].tolist() == want
+
+
+@pytest.mark.parametrize("amax,code", [
+    (1.0, 125), (6.0, 127), (7.9, 127), (8.0, 128), (2.0 ** -10, 115), (2.0 ** 100, 225),
+    (0.0, 0), (2.0 ** -140, 0), (3.0 * 2.0 ** 200, 254)])
+def test_mxfp4_encode_scale_rule(amax, code):
+    x = np.zeros(32)
+    x[5] = -amax
+    packed, e8 = mxfp4_encode(x)
+    assert int(e8[0]) == code
+    v = mxfp4_decode(packed, e8)
+    if amax == 2.0 ** -140:
+        assert v[5] == 0.0                         # below the smallest scale's grid: rounds to zero
+    elif amax == 3.0 * 2.0 ** 200:
+        assert v[5] == -6.0 * 2.0 ** 127           # past the largest scale: saturated
+    else:
+        assert v[5] == -amax or (amax == 7.9 and v[5] == -6.0)
+
+
+def test_mxfp4_encode_round_trips_every_representable_block():
+    """Decoding, encoding and decoding again gives the same values, for blocks of
+    every code mix (full range, small magnitudes only, zeros) and many scales."""
+    rc, re = streams(71, 0, 2)
+    for codes in (None, [0, 1, 2, 3, 8, 9, 10, 11], [0, 1, 9], [0, 8]):
+        packed, e8 = mxfp4_random(rc, re, (64,), 128, codes=codes, exps=tuple(range(100, 160)))
+        v = mxfp4_decode(packed, e8)
+        p2, e2 = mxfp4_encode(v)
+        assert np.array_equal(mxfp4_decode(p2, e2), v)
+
+
+def test_mxfp4_encode_error_bound_and_monotone():
+    """Each element lands within half an E2M1 step of x (steps 0.5, 1, 2 times the
+    scale below 2, 4, 6) or saturates at 6; within a block the encoding is monotone."""
+    (r,) = streams(72, 0, 1)
+    x = r.standard_normal((200, 64)) * np.exp2(r.integers(-20, 20, (200, 1)))
+    packed, e8 = mxfp4_encode(x)
+    q = mxfp4_decode(packed, e8)
+    sc = np.repeat(np.exp2(e8.astype(np.int64) - 127.0), 32, axis=-1)
+    v = np.abs(x) / sc
+    step = np.where(v < 2, 0.5, np.where(v < 4, 1.0, 2.0))
+    err = np.abs(q - x) / sc
+    assert np.all((err <= step / 2) | ((v > 6) & (np.abs(q) / sc == 6.0)))
+    for row in range(0, 200, 17):
+        for b in range(2):
+            xb, qb = x[row, 32 * b:32 * b + 32], q[row, 32 * b:32 * b + 32]
+            o = np.argsort(xb, kind="stable")
+            assert np.all(np.diff(qb[o]) >= 0)
