@@ -103,6 +103,26 @@ csa_status_t csa_compress_kv(const void* k, const void* v, int32_t in_dtype,
                              int32_t out_dtype, void* stream);
 
 /* ---------------------------------------------------------------------
+ * csa_mxfp4_quantize -- real vectors to the indexer's MXFP4 operands.
+ *
+ * Passage: the indexer's query-key path is MXFP4 ("DeepSeek V4技术揭秘",
+ * §一 基础设施; sz-guanghua.com.cn ifanr repost, 百萬長上下文, FP4 scores).
+ * Conversion (OCP Microscaling v1.0, restated): per 32-element block,
+ * X = floor(log2(max |x|)) - 2 clamped to [-127, 127] (-127 for an all-zero
+ * block); code_i = E2M1 nearest to x_i / 2^X, ties to the even code,
+ * magnitudes past 6 saturated, sign bit of x_i kept; e8m0 = X + 127.
+ *
+ *   x      [n_vec, d] in in_dtype (CSA_BF16 or CSA_F32), finite values
+ *   codes  [n_vec, d/2] u8 (output): element 2i in the low nibble of byte i
+ *   e8m0   [n_vec, d/32] u8 (output)
+ * Limits: d a positive multiple of 32.  The outputs feed csa_indexer_scores,
+ * csa_indexer_topk and csa_compress_indexer_topk as q_codes / q_e8m0 or
+ * k_codes / k_e8m0 directly.
+ * ------------------------------------------------------------------- */
+csa_status_t csa_mxfp4_quantize(const void* x, int32_t in_dtype, int64_t n_vec, int32_t d,
+                                uint8_t* codes, uint8_t* e8m0, void* stream);
+
+/* ---------------------------------------------------------------------
  * csa_indexer_scores -- lightning-indexer relevance of every compressed entry.
  *
  * Passage: the indexer scores each query token against each compressed block

@@ -24,8 +24,9 @@ CSA_BF16, CSA_F32, CSA_FP8_E4M3 = 0, 1, 2
 CSA_OP_TOPK, CSA_OP_SPARSE_ATTN, CSA_OP_DENSE_ATTN, CSA_OP_INDEXER_TOPK = 0, 1, 2, 3
 DTYPES = {"bf16": CSA_BF16, "f32": CSA_F32, "fp8": CSA_FP8_E4M3}
 
-EXPORTS = ["csa_compress_kv", "csa_indexer_scores", "csa_indexer_topk", "csa_compress_indexer_topk", "csa_topk",
-           "csa_sparse_attn", "hca_dense_attn", "csa_workspace_size", "csa_status_str", "csa_abi_version"]
+EXPORTS = ["csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
+           "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn", "csa_workspace_size",
+           "csa_status_str", "csa_abi_version"]
 
 _lib = None
 _P = ctypes.c_void_p
@@ -49,6 +50,7 @@ def load(path=LIB_PATH):
         raise RuntimeError(f"{path} is not built; run `python -m long_context_compressed_03_amd.build`")
     lib = ctypes.CDLL(path)
     lib.csa_compress_kv.argtypes = [_P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _P]
+    lib.csa_mxfp4_quantize.argtypes = [_P, _I, ctypes.c_int64, _I, _P, _P, _P]
     lib.csa_indexer_scores.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]
     lib.csa_indexer_topk.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _S,
                                      _P]
@@ -60,8 +62,8 @@ def load(path=LIB_PATH):
                                     _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
     lib.hca_dense_attn.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _P, _I,
                                    _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
-    for fn in ["csa_compress_kv", "csa_indexer_scores", "csa_indexer_topk", "csa_compress_indexer_topk",
-               "csa_topk", "csa_sparse_attn", "hca_dense_attn"]:
+    for fn in ["csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
+               "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn"]:
         getattr(lib, fn).restype = _I
     lib.csa_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
     lib.csa_workspace_size.restype = _S
@@ -164,6 +166,23 @@ def csa_compress_indexer_topk(k, v, logits, k_out, v_out, k_scale_out, v_scale_o
                                        _ptr(idx), _ws_ptr(ws), _ws_len(ws), _stream(stream))
     _check("csa_compress_indexer_topk", st)
     return idx
+
+
+def csa_mxfp4_quantize(x, codes=None, e8m0=None, stream=None):
+    """Real vectors x [..., d] (bf16 or fp32, d a multiple of 32) -> MXFP4 (codes [..., d/2] u8,
+    e8m0 [..., d/32] u8), the layout the indexer calls take."""
+    d = x.shape[-1]
+    lead = tuple(x.shape[:-1])
+    if codes is None:
+        codes = torch.empty(lead + (d // 2,), dtype=torch.uint8, device=x.device)
+    if e8m0 is None:
+        e8m0 = torch.empty(lead + (d // 32,), dtype=torch.uint8, device=x.device)
+    if not x.is_contiguous() or not codes.is_contiguous() or not e8m0.is_contiguous():
+        raise ValueError("contiguous tensors expected")
+    n_vec = x.numel() // d if d else 0
+    st = load().csa_mxfp4_quantize(_ptr(x), _dt_of(x), n_vec, d, _ptr(codes), _ptr(e8m0), _stream(stream))
+    _check("csa_mxfp4_quantize", st)
+    return codes, e8m0
 
 
 def csa_indexer_scores(q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, m, scores=None, stream=None):

@@ -95,6 +95,21 @@ def test_compress_indexer_topk_rejects_bad_arguments():
     assert call(B=0) == csa.CSA_OK                 # empty: nothing to do, nothing launched
 
 
+def test_quantize_rejects_bad_arguments():
+    import long_context_compressed_03_amd as csa
+    lib = csa.load()
+
+    def call(x=_p(), dt=0, n=4, d=128, c=_p(), e=_p()):
+        return lib.csa_mxfp4_quantize(x, dt, n, d, c, e, None)
+    assert call(x=None) == csa.CSA_EINVAL
+    assert call(c=None) == csa.CSA_EINVAL
+    assert call(d=100) == csa.CSA_EINVAL          # blocks of 32
+    assert call(d=0) == csa.CSA_EINVAL
+    assert call(dt=2) == csa.CSA_EINVAL           # bf16 or fp32 inputs
+    assert call(n=-1) == csa.CSA_EINVAL
+    assert call(n=0) == csa.CSA_OK                # empty: nothing launched
+
+
 def test_indexer_rejects_bad_arguments():
     import long_context_compressed_03_amd as csa
     lib = csa.load()
