@@ -42,7 +42,8 @@ def parse():
     p.add_argument("--steps", type=int, default=240)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="csa_decode_128k",
-                   choices=["csa_decode_128k", "hca_decode_1m", "csa_prefill_256k", "pair_1m"])
+                   choices=["csa_decode_128k", "hca_decode_1m", "csa_prefill_256k", "pair_1m",
+                            "mxfp4_quantize_keys_128k"])
     p.add_argument("--rotate", type=int, default=0, help="input copies (0 = auto)")
     p.add_argument("--indexer", default="auto", choices=["auto", "combined", "fused", "unfused"],
                    help="CSA scoring + selection as one fused call or as csa_indexer_scores then "
@@ -265,9 +266,43 @@ LAYERS = {
 }
 
 
+QUANT_WORKLOAD = "mxfp4_quantize_keys_128k"
+QUANT_SHAPE = (16 * 32768, 128)     # the 128K decode shape's indexer keys
+
+
+def build_quant(args):
+    """The MXFP4 quantisation of the indexer keys of the 128K decode shape (16 sequences x
+    32768 entries x 128 dims, bf16 N(0,1) rows with per-row power-of-two spreads) in one call."""
+    import torch
+    from csa_synth import normal_kv, streams
+    import long_context_compressed_03_amd as csa
+    n, d = QUANT_SHAPE
+    (r,) = streams(91, 0, 1)
+    x = normal_kv(r, (n, d), "f32") * np.exp2(r.integers(-4, 5, (n, 1))).astype(np.float32)
+    from csa_synth import f32_to_bf16_bits
+    bits = f32_to_bf16_bits(x)
+    st = Step(QUANT_WORKLOAD, n)
+    nbytes = n * (2 * d + d // 2 + d // 32)
+
+    def f_quant(c):
+        csa.csa_mxfp4_quantize(c["x"], c["codes"], c["e8m0"])
+    st.add(Kernel("mxfp4_quantize", f_quant, nbytes, 0, BF16_PEAK_TFLOPS, "mxfp4_quantize"))
+    R = args.rotate or max(2, math.ceil(600e6 / nbytes))
+    base = {"x": torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda(),
+            "codes": torch.empty((n, d // 2), dtype=torch.uint8, device="cuda"),
+            "e8m0": torch.empty((n, d // 32), dtype=torch.uint8, device="cuda")}
+    st.copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
+    st.layers = [("", {"quant_sample": bits[:8192]})]
+    st.config = {"workload": QUANT_WORKLOAD, "vectors": n, "d": d, "input": "bf16",
+                 "output": "MXFP4 (E2M1 codes + E8M0 per 32)"}
+    return st
+
+
 def build(args):
     """Host inputs, R device copies and the step's launches for the chosen workload."""
     import torch
+    if args.workload == QUANT_WORKLOAD:
+        return build_quant(args)
     from csa_synth import workloads
     wls = workloads()
     parts = LAYERS[args.workload]
@@ -402,7 +437,8 @@ KERNEL_SOURCES = {
     "topk": ["topk.hip", "split.hpp", "select.hpp", "compress_core.hpp", "common.hpp"],
     "compress_kv": ["compress.hip", "compress_core.hpp", "common.hpp"],
     "compress_indexer_topk": ["indexer_topk.hip", "indexer_core.hpp", "split.hpp", "topk.hip", "select.hpp",
-                              "compress_core.hpp", "compress.hip", "common.hpp"]}
+                              "compress_core.hpp", "compress.hip", "common.hpp"],
+    "mxfp4_quantize": ["quant.hip", "common.hpp"]}
 
 
 def measured_traffic(workload, kernel):
@@ -424,6 +460,17 @@ def measured_traffic(workload, kernel):
 
 # --------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample of the same workload
+
+def cpu_baseline_quant(st):
+    """The oracle's MXFP4 encoder on 8192 of the workload's vectors, in vectors/s."""
+    from oracle.formats import bf16_decode, mxfp4_encode
+    sample = st.layers[0][1]["quant_sample"]
+    x = bf16_decode(sample)
+    t0 = time.perf_counter()
+    mxfp4_encode(x)
+    dt = time.perf_counter() - t0
+    return len(sample) / dt, f"fp64 numpy oracle encoder on {len(sample)} of the workload's vectors ({dt:.2f} s)"
+
 
 def cpu_baseline(st, budget_s):
     """The oracle, timed on the host on a sample of the step's query rows.
@@ -544,18 +591,21 @@ def main():
         kernels[n] = {"avg_us": round(kt[n]["avg_us"], 3), "algorithmic_bytes": kk.nbytes,
                       "algorithmic_flops": kk.flops, "bound": kk.bound, "achieved": round(a_, 1),
                       "unit": u_, "frac": round(a_ / p_, 4)}
+    quant = args.workload == QUANT_WORKLOAD
+    unit = "key-vectors/s" if quant else "query-tokens/s"
     cpu = None
     if not args.no_cpu_baseline:
-        v, desc = cpu_baseline(st, args.cpu_seconds)
-        cpu = {"value": round(v, 4), "unit": "query-tokens/s", "cores": 1, "kind": "oracle",
-               "sample": desc}
+        v, desc = cpu_baseline_quant(st) if quant else cpu_baseline(st, args.cpu_seconds)
+        cpu = {"value": round(v, 4), "unit": unit, "cores": 1, "kind": "oracle", "sample": desc}
     q_per_s = st.q_tokens / (ms * 1e-3)
-    line = {"metric": METRIC, "value": round(q_per_s, 1), "unit": "query-tokens/s", "n_gpus": 1,
+    metric = "MXFP4 quantisation of the indexer keys, key-vectors/s; % HBM roofline" if quant else METRIC
+    line = {"metric": metric, "value": round(q_per_s, 1), "unit": unit, "n_gpus": 1,
             "steps": done, "warmup": args.warmup, "ms_per_step": round(ms, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "mxfp4+bf16", "data": "synthetic (seeded; shapes of the pages' 128K-1M contexts)",
             "config": st.config, "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
-            "query_tokens_per_step": st.q_tokens, "rotation_copies": len(st.copies),
+            ("vectors_per_step" if quant else "query_tokens_per_step"): st.q_tokens,
+            "rotation_copies": len(st.copies),
             "graph": not args.no_graph, "wall_s_timed_region": round(wall, 4)}
     print(json.dumps(line), flush=True)
 

@@ -14,8 +14,8 @@
 // Every step is exact in fp32 (the maximum, the exponent of a float, scaling
 // by a power of two, comparisons with the midpoints of the E2M1 grid), so the
 // codes are those of the definition applied to the input values, bit for bit.
-// An HBM stream: one thread per 32-element block, 64 B (bf16) or 128 B (fp32)
-// read and 17 B written.
+// An HBM stream: 64 B (bf16) or 128 B (fp32) read and 17 B written per
+// 32-element block.
 #include "common.hpp"
 
 namespace {
@@ -31,49 +31,66 @@ CSA_DEV uint32_t e2m1_magnitude_code(float v) {
          uint32_t(v > 2.5f) + uint32_t(v >= 3.5f) + uint32_t(v > 5.0f);
 }
 
+// kL lanes per 32-element block (4 for bf16, 8 for fp32), each holding 16
+// contiguous input bytes, so a wave's load is one contiguous 1 KB span; a
+// thread takes kIter such lanes, kQThreads apart, with all their loads issued
+// first.  The block's maximum goes through kL lanes with xor shuffles, and
+// lane p writes the codes of its elements (bytes [p*kE/2, (p+1)*kE/2) of the
+// block's 16).
+constexpr int kIter = 4;
+
 template <int kInF32>
 __global__ __launch_bounds__(kQThreads) void mxfp4_quantize_kernel(const void* __restrict__ x, long n_blocks,
                                                                    uint8_t* __restrict__ codes,
                                                                    uint8_t* __restrict__ e8m0) {
-  const long blk = long(blockIdx.x) * kQThreads + threadIdx.x;
-  if (blk >= n_blocks) return;
-  float v[32];
-  if constexpr (kInF32) {
-    const v4f* p = reinterpret_cast<const v4f*>(static_cast<const float*>(x) + blk * 32);
+  constexpr int kL = kInF32 ? 8 : 4;       // lanes per block
+  constexpr int kE = 32 / kL;              // elements per lane
+  const long n_lanes = n_blocks * kL;
+  const long gl0 = long(blockIdx.x) * (kQThreads * kIter) + threadIdx.x;
+  u32x4 w[kIter];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const v4f w = __builtin_nontemporal_load(p + q);
+  for (int it = 0; it < kIter; ++it) {
+    const long gl = min(gl0 + long(it) * kQThreads, n_lanes - 1);   // lanes past the end re-read the last one
+    w[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(x) + gl * 16));
+  }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * q + e] = w[e];
-    }
-  } else {
-    const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + blk * 32);
+  for (int it = 0; it < kIter; ++it) {
+    const long gl = gl0 + long(it) * kQThreads;
+    const long blk = gl / kL;
+    const int part = int(gl % kL);
+    float v[kE];
+    if constexpr (kInF32) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const u32x4 w = __builtin_nontemporal_load(p + q);
+      for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(w[it][e]);
+    } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        v[8 * q + 2 * e] = __uint_as_float(w[e] << 16);
-        v[8 * q + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+        v[2 * e] = __uint_as_float(w[it][e] << 16);
+        v[2 * e + 1] = __uint_as_float(w[it][e] & 0xFFFF0000u);
       }
     }
-  }
-  float amax = 0.f;
+    float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  // X = floor(log2(amax)) - 2; for fp32 inputs floor(log2(amax)) <= 127, so
-  // X <= 125 and 2^-X is a normal float; a zero block takes X = -127
-  const int X = amax > 0.f ? max(ilogbf(amax) - 2, -127) : -127;
-  const float inv = __uint_as_float(uint32_t(127 - X) << 23);   // 2^-X, exact
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
+    for (int i = 0; i < kE; ++i) amax = fmaxf(amax, fabsf(v[i]));
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const uint32_t sign = (__float_as_uint(v[i]) >> 31) << 3;
-    const uint32_t c = sign | e2m1_magnitude_code(fabsf(v[i]) * inv);
-    w[i >> 3] |= c << (4 * (i & 7));
+    for (int o = 1; o < kL; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+    // X = floor(log2(amax)) - 2; for fp32 inputs floor(log2(amax)) <= 127, so
+    // X <= 125 and 2^-X is a normal float; a zero block takes X = -127
+    const int X = amax > 0.f ? max(ilogbf(amax) - 2, -127) : -127;
+    const float inv = __uint_as_float(uint32_t(127 - X) << 23);   // 2^-X, exact
+    uint32_t word = 0u;
+#pragma unroll
+    for (int i = 0; i < kE; ++i) {
+      const uint32_t sign = (__float_as_uint(v[i]) >> 31) << 3;
+      word |= (sign | e2m1_magnitude_code(fabsf(v[i]) * inv)) << (4 * i);
+    }
+    if (blk < n_blocks) {                  // whole groups of kL lanes alike
+      uint8_t* out = codes + blk * 16 + part * (kE / 2);
+      if constexpr (kE == 8) *reinterpret_cast<uint32_t*>(out) = word;
+      else *reinterpret_cast<uint16_t*>(out) = uint16_t(word);
+      if (part == 0) e8m0[blk] = uint8_t(X + 127);
+    }
   }
-  *reinterpret_cast<uint4*>(codes + blk * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-  e8m0[blk] = uint8_t(X + 127);
 }
 
 }  // namespace
@@ -85,7 +102,8 @@ extern "C" csa_status_t csa_mxfp4_quantize(const void* x, int32_t in_dtype, int6
   if (n_vec < 0 || d <= 0 || d % 32 != 0) return CSA_EINVAL;
   const long n_blocks = long(n_vec) * (d / 32);
   if (n_blocks == 0) return CSA_OK;
-  const long grid = (n_blocks + kQThreads - 1) / kQThreads;
+  const long lanes = n_blocks * (in_dtype == CSA_F32 ? 8 : 4);
+  const long grid = (lanes + kQThreads * kIter - 1) / (kQThreads * kIter);
   if (grid > 0x7FFFFFFFL) return CSA_ENOTSUP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (in_dtype == CSA_F32)
