@@ -86,9 +86,10 @@ __global__ __launch_bounds__(kQThreads) void mxfp4_quantize_kernel(const void* _
     }
     if (blk < n_blocks) {                  // whole groups of kL lanes alike
       uint8_t* out = codes + blk * 16 + part * (kE / 2);
-      if constexpr (kE == 8) *reinterpret_cast<uint32_t*>(out) = word;
-      else *reinterpret_cast<uint16_t*>(out) = uint16_t(word);
-      if (part == 0) e8m0[blk] = uint8_t(X + 127);
+      // streaming stores: the operands are read later, by another kernel
+      if constexpr (kE == 8) __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(out));
+      else __builtin_nontemporal_store(uint16_t(word), reinterpret_cast<uint16_t*>(out));
+      if (part == 0) __builtin_nontemporal_store(uint8_t(X + 127), e8m0 + blk);
     }
   }
 }
