@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--indexer", default="auto", choices=["auto", "combined", "fused", "unfused"],
                    help="CSA scoring + selection as one fused call or as csa_indexer_scores then "
                         "csa_topk (auto: fused for prefill chunks, unfused for decode)")
+    p.add_argument("--batch-invariant", action="store_true",
+                   help="attention through the batch-invariant calls (row bits independent of the batch)")
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -159,7 +161,7 @@ def visible(wl):
     return int(np.minimum((t + 1) // wl.m, wl.cap).sum())
 
 
-def add_layer(st, h, prefix, indexer="auto"):
+def add_layer(st, h, prefix, indexer="auto", batch_invariant=False):
     """The calls of one CSA or HCA layer: compress, (indexer, top-k,) attention."""
     import long_context_compressed_03_amd as csa
     wl = h["wl"]
@@ -194,7 +196,7 @@ def add_layer(st, h, prefix, indexer="auto"):
         def f_attn(c):
             csa.csa_sparse_attn(c[p + "q"], c[p + "ck"], c[p + "cv"], c[p + "idx"], c[p + "kw"],
                                 c[p + "vw"], c[p + "raw0"], c[p + "pos"], W, ck_scale=c[p + "cks"],
-                                cv_scale=c[p + "cvs"], out=c[p + "out"])
+                                cv_scale=c[p + "cvs"], out=c[p + "out"], batch_invariant=batch_invariant)
         fused = indexer in ("fused", "auto", "combined")
         if combined:
             def f_combined(c):
@@ -237,7 +239,7 @@ def add_layer(st, h, prefix, indexer="auto"):
         def f_attn(c):
             csa.hca_dense_attn(c[p + "q"], c[p + "ck"], c[p + "cv"], m, c[p + "kw"], c[p + "vw"],
                                c[p + "raw0"], c[p + "pos"], W, ck_scale=c[p + "cks"],
-                               cv_scale=c[p + "cvs"], out=c[p + "out"])
+                               cv_scale=c[p + "cvs"], out=c[p + "out"], batch_invariant=batch_invariant)
         nv_max = min((wl.q_pos0[0] + wl.T_q) // m, wl.cap)
         st.add(Kernel(name("dense_attn"), f_attn, B * nv_max * ent + B * wl.L_raw * 512 + q_bytes,
                       4 * H * 128 * (nvis_sum + rows * W), BF16_PEAK_TFLOPS, "dense_attn"))
@@ -313,7 +315,7 @@ def build(args):
         q_tokens = hosts[0][1]["wl"].B * hosts[0][1]["wl"].T_q
     st = Step(args.workload, q_tokens)
     for prefix, h in hosts:
-        add_layer(st, h, prefix, args.indexer)
+        add_layer(st, h, prefix, args.indexer, args.batch_invariant)
     per_copy = sum(k.nbytes for k in st.kernels.values())
     R = args.rotate or max(2, math.ceil(600e6 / per_copy))
     base = {}
@@ -330,6 +332,8 @@ def build(args):
         st.config = {"workload": args.workload, **layer_config(hosts[0][1]["wl"])}
     st.config["indexer_topk"] = ("combined with the compression" if any(n.endswith("compress_indexer_topk") for n in st.order)
                                  else "fused" if any(n.endswith("indexer_topk") for n in st.order) else "unfused")
+    if args.batch_invariant:
+        st.config["attention"] = "batch-invariant calls"
     return st
 
 

@@ -70,7 +70,9 @@ typedef enum {
   CSA_OP_TOPK = 0,
   CSA_OP_SPARSE_ATTN = 1,
   CSA_OP_DENSE_ATTN = 2,
-  CSA_OP_INDEXER_TOPK = 3
+  CSA_OP_INDEXER_TOPK = 3,
+  CSA_OP_SPARSE_ATTN_BATCH_INVARIANT = 4,
+  CSA_OP_DENSE_ATTN_BATCH_INVARIANT = 5
 } csa_op_t;
 
 /* ---------------------------------------------------------------------
@@ -287,6 +289,40 @@ csa_status_t hca_dense_attn(const void* q, int32_t io_dtype, const void* ck, con
                             int32_t W, int32_t B, int32_t T_q, int32_t H, int32_t d,
                             float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* ---------------------------------------------------------------------
+ * csa_sparse_attn_batch_invariant, hca_dense_attn_batch_invariant -- the
+ * same attention as csa_sparse_attn / hca_dense_attn (same arguments, same
+ * limits, same results to the same tolerance), with one more guarantee: the
+ * bits of a query row's out and lse depend only on that row's inputs and on
+ * n_keys (k + W, resp. cap + W), never on B, T_q or the other rows.  A row
+ * computed in a batch of one and in a batch of many, or in prefill chunks of
+ * any length, comes out bit-identical.
+ *
+ * The plain calls choose how many pieces to split each key list into from
+ * the number of rows (to fill the chip) and, for many-query dense prefill, a
+ * different kernel; each choice sums the softmax in another order.  These
+ * calls fix the split at ceil(n_keys / 64) chunks of 64 keys cut into pieces
+ * of max(2, ceil(chunks / 64)) chunks, and always use the split kernel: small
+ * batches then run fewer, longer blocks than the plain calls and are slower.
+ * Passage: the pages define the operation (see csa_sparse_attn); the
+ * ordering guarantee is this library's.
+ * ws: csa_workspace_size(CSA_OP_SPARSE_ATTN_BATCH_INVARIANT, ...) resp.
+ * (CSA_OP_DENSE_ATTN_BATCH_INVARIANT, ...) with the same other arguments as
+ * for the plain call.
+ * ------------------------------------------------------------------- */
+csa_status_t csa_sparse_attn_batch_invariant(
+    const void* q, int32_t io_dtype, const void* ck, const void* cv, const float* ck_scale,
+    const float* cv_scale, int32_t ckv_dtype, int32_t cap, const int32_t* idx, int32_t k,
+    const void* k_win, const void* v_win, const int32_t* raw_pos0, int32_t L_raw,
+    const int32_t* q_pos0, int32_t W, int32_t B, int32_t T_q, int32_t H, int32_t d,
+    float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+csa_status_t hca_dense_attn_batch_invariant(
+    const void* q, int32_t io_dtype, const void* ck, const void* cv, const float* ck_scale,
+    const float* cv_scale, int32_t ckv_dtype, int32_t cap, int32_t m_prime, const void* k_win,
+    const void* v_win, const int32_t* raw_pos0, int32_t L_raw, const int32_t* q_pos0, int32_t W,
+    int32_t B, int32_t T_q, int32_t H, int32_t d, float sm_scale, void* out, float* lse,
+    void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes a call needs.  n_keys = k + W (CSA) or cap + W (HCA);
  * for CSA_OP_TOPK and CSA_OP_INDEXER_TOPK pass T_q and n_keys = cap (and, for

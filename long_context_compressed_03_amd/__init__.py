@@ -22,10 +22,12 @@ LIB_PATH = os.path.join(HERE, "libcsa.so")
 CSA_OK, CSA_EINVAL, CSA_ENOTSUP, CSA_EHIP, CSA_EWORKSPACE = range(5)
 CSA_BF16, CSA_F32, CSA_FP8_E4M3 = 0, 1, 2
 CSA_OP_TOPK, CSA_OP_SPARSE_ATTN, CSA_OP_DENSE_ATTN, CSA_OP_INDEXER_TOPK = 0, 1, 2, 3
+CSA_OP_SPARSE_ATTN_BATCH_INVARIANT, CSA_OP_DENSE_ATTN_BATCH_INVARIANT = 4, 5
 DTYPES = {"bf16": CSA_BF16, "f32": CSA_F32, "fp8": CSA_FP8_E4M3}
 
 EXPORTS = ["csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
-           "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn", "csa_workspace_size",
+           "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn",
+           "csa_sparse_attn_batch_invariant", "hca_dense_attn_batch_invariant", "csa_workspace_size",
            "csa_status_str", "csa_abi_version"]
 
 _lib = None
@@ -58,12 +60,15 @@ def load(path=LIB_PATH):
                                               _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P,
                                               _P, _S, _P]
     lib.csa_topk.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P, _S, _P]
-    lib.csa_sparse_attn.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _P, _I, _P, _P, _P, _I, _P, _I,
-                                    _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
-    lib.hca_dense_attn.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _P, _I,
-                                   _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
+    for fn in ["csa_sparse_attn", "csa_sparse_attn_batch_invariant"]:
+        getattr(lib, fn).argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _P, _I, _P, _P, _P, _I, _P, _I,
+                                     _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
+    for fn in ["hca_dense_attn", "hca_dense_attn_batch_invariant"]:
+        getattr(lib, fn).argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _P, _I,
+                                     _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
     for fn in ["csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
-               "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn"]:
+               "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn",
+               "csa_sparse_attn_batch_invariant", "hca_dense_attn_batch_invariant"]:
         getattr(lib, fn).restype = _I
     lib.csa_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
     lib.csa_workspace_size.restype = _S
@@ -258,34 +263,55 @@ def _attn_common(q, ck, ck_scale, out, lse):
 
 
 def csa_sparse_attn(q, ck, cv, idx, k_win, v_win, raw_pos0, q_pos0, W, ck_scale=None,
-                    cv_scale=None, sm_scale=None, out=None, lse=None, stream=None):
-    """CSA attention over idx-selected compressed entries plus window(t)."""
+                    cv_scale=None, sm_scale=None, out=None, lse=None, stream=None,
+                    batch_invariant=False):
+    """CSA attention over idx-selected compressed entries plus window(t).
+
+    batch_invariant=True calls csa_sparse_attn_batch_invariant: a row's bits then
+    do not depend on the batch around it."""
     B, T_q, H, d, out = _attn_common(q, ck, ck_scale, out, lse)
     k = idx.shape[-1]
     cap = ck.shape[1]
     sm = d ** -0.5 if sm_scale is None else sm_scale
     lib = load()
-    ws = _workspace(q.device, lib.csa_workspace_size(CSA_OP_SPARSE_ATTN, B, T_q, H, d, k + W))
-    st = lib.csa_sparse_attn(_ptr(q), _dt_of(q), _ptr(ck), _ptr(cv), _ptr(ck_scale),
+    name = "csa_sparse_attn_batch_invariant" if batch_invariant else "csa_sparse_attn"
+    op = CSA_OP_SPARSE_ATTN_BATCH_INVARIANT if batch_invariant else CSA_OP_SPARSE_ATTN
+    ws = _workspace(q.device, lib.csa_workspace_size(op, B, T_q, H, d, k + W))
+    st = getattr(lib, name)(_ptr(q), _dt_of(q), _ptr(ck), _ptr(cv), _ptr(ck_scale),
                              _ptr(cv_scale), _dt_of(ck), cap, _ptr(idx), k, _ptr(k_win),
                              _ptr(v_win), _ptr(raw_pos0), k_win.shape[1], _ptr(q_pos0), W, B,
                              T_q, H, d, sm, _ptr(out), _ptr(lse), _ws_ptr(ws), _ws_len(ws),
                              _stream(stream))
-    _check("csa_sparse_attn", st)
+    _check(name, st)
     return out
 
 
 def hca_dense_attn(q, ck, cv, m_prime, k_win, v_win, raw_pos0, q_pos0, W, ck_scale=None,
-                   cv_scale=None, sm_scale=None, out=None, lse=None, stream=None):
-    """HCA attention over all visible compressed entries plus window(t)."""
+                   cv_scale=None, sm_scale=None, out=None, lse=None, stream=None,
+                   batch_invariant=False):
+    """HCA attention over all visible compressed entries plus window(t).
+
+    batch_invariant=True calls hca_dense_attn_batch_invariant."""
     B, T_q, H, d, out = _attn_common(q, ck, ck_scale, out, lse)
     cap = ck.shape[1]
     sm = d ** -0.5 if sm_scale is None else sm_scale
     lib = load()
-    ws = _workspace(q.device, lib.csa_workspace_size(CSA_OP_DENSE_ATTN, B, T_q, H, d, cap + W))
-    st = lib.hca_dense_attn(_ptr(q), _dt_of(q), _ptr(ck), _ptr(cv), _ptr(ck_scale),
+    name = "hca_dense_attn_batch_invariant" if batch_invariant else "hca_dense_attn"
+    op = CSA_OP_DENSE_ATTN_BATCH_INVARIANT if batch_invariant else CSA_OP_DENSE_ATTN
+    ws = _workspace(q.device, lib.csa_workspace_size(op, B, T_q, H, d, cap + W))
+    st = getattr(lib, name)(_ptr(q), _dt_of(q), _ptr(ck), _ptr(cv), _ptr(ck_scale),
                             _ptr(cv_scale), _dt_of(ck), cap, m_prime, _ptr(k_win), _ptr(v_win),
                             _ptr(raw_pos0), k_win.shape[1], _ptr(q_pos0), W, B, T_q, H, d, sm,
                             _ptr(out), _ptr(lse), _ws_ptr(ws), _ws_len(ws), _stream(stream))
-    _check("hca_dense_attn", st)
+    _check(name, st)
     return out
+
+
+def csa_sparse_attn_batch_invariant(*args, **kwargs):
+    """csa_sparse_attn whose row results do not depend on the batch around them."""
+    return csa_sparse_attn(*args, batch_invariant=True, **kwargs)
+
+
+def hca_dense_attn_batch_invariant(*args, **kwargs):
+    """hca_dense_attn whose row results do not depend on the batch around them."""
+    return hca_dense_attn(*args, batch_invariant=True, **kwargs)

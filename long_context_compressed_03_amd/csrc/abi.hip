@@ -1,7 +1,7 @@
 // Host-only entry points of the C ABI: workspace sizing, status text, version.
 #include "common.hpp"
 
-size_t csa_attn_workspace_size(long rows, int H, int n_list);
+size_t csa_attn_workspace_size(long rows, int H, int n_list, bool invariant);
 size_t csa_indexer_topk_workspace_size(long rows, int T_q, int d_I, int cap);
 size_t csa_topk_workspace_size(long rows, int cap);
 
@@ -14,8 +14,11 @@ extern "C" size_t csa_workspace_size(int32_t op, int32_t B, int32_t T_q, int32_t
       return csa_indexer_topk_workspace_size(long(B) * T_q, T_q, d, n_keys);
     case CSA_OP_SPARSE_ATTN:
     case CSA_OP_DENSE_ATTN:
+    case CSA_OP_SPARSE_ATTN_BATCH_INVARIANT:
+    case CSA_OP_DENSE_ATTN_BATCH_INVARIANT:
       if (d != kHeadDim || H < 16 || H > 128 || H % 16 != 0) return size_t(-1);
-      return csa_attn_workspace_size(long(B) * T_q, H, n_keys);
+      return csa_attn_workspace_size(long(B) * T_q, H, n_keys,
+                                     op == CSA_OP_SPARSE_ATTN_BATCH_INVARIANT || op == CSA_OP_DENSE_ATTN_BATCH_INVARIANT);
     default:
       return size_t(-1);
   }
@@ -32,4 +35,4 @@ extern "C" const char* csa_status_str(int32_t status) {
   }
 }
 
-extern "C" int32_t csa_abi_version(void) { return 101; }
+extern "C" int32_t csa_abi_version(void) { return 102; }

@@ -850,13 +850,23 @@ struct Plan {
   long blocks;
 };
 
-// The work split depends only on (rows, n_list): never on data or timing.
+// The default work split depends only on (rows, n_list): never on data or timing.
 // At most about one block per CU: past 256 blocks some CUs run two, whose
 // tail then sets the kernel time, and the partials to write back and merge
 // grow with the split count.  A split is a whole number of 64-key chunks.
-Plan make_plan(long rows, int n_list) {
+// invariant: the split length depends on the key-list length only (at least
+// two chunks per split, at most kMaxSplits splits), so a row's splits, and
+// with them its result bits, are the same whatever the batch around it.
+Plan make_plan(long rows, int n_list, bool invariant) {
   Plan p{};
   const long chunks = (max(n_list, 1) + kNK - 1) / kNK;
+  if (invariant) {
+    const long per = max(2L, (chunks + kMaxSplits - 1) / kMaxSplits);
+    p.split_len = int(per * kNK);
+    p.n_splits = int((chunks + per - 1) / per);
+    p.blocks = rows * p.n_splits;
+    return p;
+  }
   long want = (256 + rows - 1) / rows;
   if (want > chunks) want = chunks;
   if (want > kMaxSplits) want = kMaxSplits;
@@ -941,10 +951,11 @@ hipError_t launch_tiles(const AttnArgs& a, long blocks, hipStream_t st) {
 }
 
 template <bool kDense>
-csa_status_t run_attn(AttnArgs a, int io_dtype, int ckv_dtype, int B, void* ws, size_t ws_size, hipStream_t st) {
+csa_status_t run_attn(AttnArgs a, int io_dtype, int ckv_dtype, int B, void* ws, size_t ws_size, hipStream_t st,
+                      bool invariant) {
   const long rows = long(B) * a.T_q;
   if (rows == 0) return CSA_OK;
-  const Plan p = make_plan(rows, a.n_list);
+  const Plan p = make_plan(rows, a.n_list, invariant);
   if (p.blocks > 0x7FFFFFFFL) return CSA_ENOTSUP;
   a.n_splits = p.n_splits;
   a.split_len = p.split_len;
@@ -958,7 +969,8 @@ csa_status_t run_attn(AttnArgs a, int io_dtype, int ckv_dtype, int B, void* ws, 
     a.part_o = reinterpret_cast<float*>(w + ml);
   }
   hipError_t err;
-  if (kDense && use_mq(io_dtype, a.H, a.T_q, p) && (ckv_dtype == CSA_BF16 || ckv_dtype == CSA_FP8_E4M3)) {
+  if (kDense && !invariant && use_mq(io_dtype, a.H, a.T_q, p) &&
+      (ckv_dtype == CSA_BF16 || ckv_dtype == CSA_FP8_E4M3)) {
     err = ckv_dtype == CSA_BF16 ? launch_mq<CSA_BF16>(a, B, st) : launch_mq<CSA_FP8_E4M3>(a, B, st);
     return err == hipSuccess ? CSA_OK : CSA_EHIP;
   }
@@ -990,16 +1002,18 @@ csa_status_t check_common(const void* q, int io_dtype, const void* ck, const voi
 
 }  // namespace
 
-size_t csa_attn_workspace_size(long rows, int H, int n_list) {
-  return plan_ws_bytes(make_plan(rows, n_list), rows, H);
+size_t csa_attn_workspace_size(long rows, int H, int n_list, bool invariant) {
+  return plan_ws_bytes(make_plan(rows, n_list, invariant), rows, H);
 }
 
-extern "C" csa_status_t csa_sparse_attn(const void* q, int32_t io_dtype, const void* ck, const void* cv,
-                                        const float* ck_scale, const float* cv_scale, int32_t ckv_dtype, int32_t cap,
-                                        const int32_t* idx, int32_t k, const void* k_win, const void* v_win,
-                                        const int32_t* raw_pos0, int32_t L_raw, const int32_t* q_pos0, int32_t W,
-                                        int32_t B, int32_t T_q, int32_t H, int32_t d, float sm_scale, void* out,
-                                        float* lse, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+csa_status_t sparse_attn_impl(const void* q, int32_t io_dtype, const void* ck, const void* cv, const float* ck_scale,
+                              const float* cv_scale, int32_t ckv_dtype, int32_t cap, const int32_t* idx, int32_t k,
+                              const void* k_win, const void* v_win, const int32_t* raw_pos0, int32_t L_raw,
+                              const int32_t* q_pos0, int32_t W, int32_t B, int32_t T_q, int32_t H, int32_t d,
+                              float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes, void* stream,
+                              bool invariant) {
   csa_status_t c = check_common(q, io_dtype, ck, cv, ck_scale, cv_scale, ckv_dtype, cap, k_win, v_win, raw_pos0, L_raw,
                                 q_pos0, W, B, T_q, H, d, out);
   if (c != CSA_OK) return c;
@@ -1010,15 +1024,15 @@ extern "C" csa_status_t csa_sparse_attn(const void* q, int32_t io_dtype, const v
   a.idx = idx; a.k = k; a.k_win = k_win; a.v_win = v_win; a.raw_pos0 = raw_pos0; a.L_raw = L_raw;
   a.q_pos0 = q_pos0; a.W = W; a.T_q = T_q; a.H = H; a.sm_log2 = sm_scale * kLog2e; a.out = out; a.lse = lse;
   a.n_list = k + W;
-  return run_attn<false>(a, io_dtype, ckv_dtype, B, ws, ws_bytes, static_cast<hipStream_t>(stream));
+  return run_attn<false>(a, io_dtype, ckv_dtype, B, ws, ws_bytes, static_cast<hipStream_t>(stream), invariant);
 }
 
-extern "C" csa_status_t hca_dense_attn(const void* q, int32_t io_dtype, const void* ck, const void* cv,
-                                       const float* ck_scale, const float* cv_scale, int32_t ckv_dtype, int32_t cap,
-                                       int32_t m_prime, const void* k_win, const void* v_win, const int32_t* raw_pos0,
-                                       int32_t L_raw, const int32_t* q_pos0, int32_t W, int32_t B, int32_t T_q,
-                                       int32_t H, int32_t d, float sm_scale, void* out, float* lse, void* ws,
-                                       size_t ws_bytes, void* stream) {
+csa_status_t dense_attn_impl(const void* q, int32_t io_dtype, const void* ck, const void* cv, const float* ck_scale,
+                             const float* cv_scale, int32_t ckv_dtype, int32_t cap, int32_t m_prime,
+                             const void* k_win, const void* v_win, const int32_t* raw_pos0, int32_t L_raw,
+                             const int32_t* q_pos0, int32_t W, int32_t B, int32_t T_q, int32_t H, int32_t d,
+                             float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes, void* stream,
+                             bool invariant) {
   csa_status_t c = check_common(q, io_dtype, ck, cv, ck_scale, cv_scale, ckv_dtype, cap, k_win, v_win, raw_pos0, L_raw,
                                 q_pos0, W, B, T_q, H, d, out);
   if (c != CSA_OK) return c;
@@ -1029,5 +1043,33 @@ extern "C" csa_status_t hca_dense_attn(const void* q, int32_t io_dtype, const vo
   a.idx = nullptr; a.k = m_prime; a.k_win = k_win; a.v_win = v_win; a.raw_pos0 = raw_pos0; a.L_raw = L_raw;
   a.q_pos0 = q_pos0; a.W = W; a.T_q = T_q; a.H = H; a.sm_log2 = sm_scale * kLog2e; a.out = out; a.lse = lse;
   a.n_list = cap + W;
-  return run_attn<true>(a, io_dtype, ckv_dtype, B, ws, ws_bytes, static_cast<hipStream_t>(stream));
+  return run_attn<true>(a, io_dtype, ckv_dtype, B, ws, ws_bytes, static_cast<hipStream_t>(stream), invariant);
+}
+
+}  // namespace
+
+#define CSA_SPARSE_ARGS                                                                                          \
+  const void *q, int32_t io_dtype, const void *ck, const void *cv, const float *ck_scale, const float *cv_scale, \
+      int32_t ckv_dtype, int32_t cap, const int32_t *idx, int32_t k, const void *k_win, const void *v_win,      \
+      const int32_t *raw_pos0, int32_t L_raw, const int32_t *q_pos0, int32_t W, int32_t B, int32_t T_q,         \
+      int32_t H, int32_t d, float sm_scale, void *out, float *lse, void *ws, size_t ws_bytes, void *stream
+#define CSA_SPARSE_PASS                                                                                     \
+  q, io_dtype, ck, cv, ck_scale, cv_scale, ckv_dtype, cap, idx, k, k_win, v_win, raw_pos0, L_raw, q_pos0, W, \
+      B, T_q, H, d, sm_scale, out, lse, ws, ws_bytes, stream
+#define CSA_DENSE_ARGS                                                                                           \
+  const void *q, int32_t io_dtype, const void *ck, const void *cv, const float *ck_scale, const float *cv_scale, \
+      int32_t ckv_dtype, int32_t cap, int32_t m_prime, const void *k_win, const void *v_win,                    \
+      const int32_t *raw_pos0, int32_t L_raw, const int32_t *q_pos0, int32_t W, int32_t B, int32_t T_q,         \
+      int32_t H, int32_t d, float sm_scale, void *out, float *lse, void *ws, size_t ws_bytes, void *stream
+#define CSA_DENSE_PASS                                                                                    \
+  q, io_dtype, ck, cv, ck_scale, cv_scale, ckv_dtype, cap, m_prime, k_win, v_win, raw_pos0, L_raw, q_pos0, \
+      W, B, T_q, H, d, sm_scale, out, lse, ws, ws_bytes, stream
+
+extern "C" csa_status_t csa_sparse_attn(CSA_SPARSE_ARGS) { return sparse_attn_impl(CSA_SPARSE_PASS, false); }
+extern "C" csa_status_t csa_sparse_attn_batch_invariant(CSA_SPARSE_ARGS) {
+  return sparse_attn_impl(CSA_SPARSE_PASS, true);
+}
+extern "C" csa_status_t hca_dense_attn(CSA_DENSE_ARGS) { return dense_attn_impl(CSA_DENSE_PASS, false); }
+extern "C" csa_status_t hca_dense_attn_batch_invariant(CSA_DENSE_ARGS) {
+  return dense_attn_impl(CSA_DENSE_PASS, true);
 }

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 def test_status_strings_and_version():
     import long_context_compressed_03_amd as csa
     lib = csa.load()
-    assert lib.csa_abi_version() == 101
+    assert lib.csa_abi_version() == 102
     for s in range(5):
         assert lib.csa_status_str(s).decode().startswith("CSA_")
 
@@ -180,6 +180,40 @@ def test_topk_and_attention_reject_bad_arguments():
     assert lib.hca_dense_attn(_p(), 0, _p(), _p(), None, None, 0, 16, 0, _p(), _p(), _p(), 8,
                               _p(), 4, 1, 1, 64, 128, 0.1, _p(), None, None, 0,
                               None) == csa.CSA_EINVAL  # m_prime < 1
+
+
+def test_batch_invariant_attention_plan():
+    """The batch-invariant calls split a key list of n keys into pieces of
+    max(2, ceil(chunks/64)) chunks of 64 keys, whatever the number of rows: their
+    workspace is the same per row for every batch size (partial m, l and o per
+    piece and head)."""
+    import long_context_compressed_03_amd as csa
+    lib = csa.load()
+
+    def expected(rows, H, n):
+        chunks = max(-(-n // 64), 1)
+        per = max(2, -(-chunks // 64))
+        pieces = -(-chunks // per)
+        if pieces <= 1:
+            return 0
+        slots = rows * pieces * H
+        return -(-slots * 8 // 256) * 256 + slots * 128 * 4
+
+    for op in (csa.CSA_OP_SPARSE_ATTN_BATCH_INVARIANT, csa.CSA_OP_DENSE_ATTN_BATCH_INVARIANT):
+        for B, T, H, n in [(1, 1, 64, 2048 + 128), (16, 1, 64, 2048 + 128), (300, 1, 128, 2048 + 128),
+                           (1, 4096, 64, 8192 + 128), (4, 1, 64, 262144 + 128), (1, 1, 16, 128),
+                           (7, 3, 32, 129), (2, 1, 64, 1)]:
+            assert lib.csa_workspace_size(op, B, T, H, 128, n) == expected(B * T, H, n), (op, B, T, H, n)
+        assert lib.csa_workspace_size(op, 1, 1, 24, 128, 12) == ctypes.c_size_t(-1).value
+    # the plain call splits one decode row more finely (one block per CU)
+    assert lib.csa_workspace_size(csa.CSA_OP_SPARSE_ATTN, 1, 1, 64, 128, 2048 + 128) > \
+        lib.csa_workspace_size(csa.CSA_OP_SPARSE_ATTN_BATCH_INVARIANT, 1, 1, 64, 128, 2048 + 128)
+    assert lib.csa_sparse_attn_batch_invariant(_p(), 0, _p(), _p(), None, None, 0, 16, _p(), 1024,
+                                               _p(), _p(), _p(), 8, _p(), 128, 1, 1, 64, 128, 0.1,
+                                               _p(), None, None, 0, None) == csa.CSA_EWORKSPACE
+    assert lib.hca_dense_attn_batch_invariant(_p(), 0, _p(), _p(), None, None, 0, 16, 0, _p(), _p(),
+                                              _p(), 8, _p(), 4, 1, 1, 64, 128, 0.1, _p(), None,
+                                              None, 0, None) == csa.CSA_EINVAL  # m_prime < 1
 
 
 def test_binding_fails_loudly_without_gpu_tensors():
