@@ -72,7 +72,8 @@ typedef enum {
   CSA_OP_DENSE_ATTN = 2,
   CSA_OP_INDEXER_TOPK = 3,
   CSA_OP_SPARSE_ATTN_BATCH_INVARIANT = 4,
-  CSA_OP_DENSE_ATTN_BATCH_INVARIANT = 5
+  CSA_OP_DENSE_ATTN_BATCH_INVARIANT = 5,
+  CSA_OP_KV_CACHE_APPEND = 6
 } csa_op_t;
 
 /* ---------------------------------------------------------------------
@@ -323,6 +324,46 @@ csa_status_t hca_dense_attn_batch_invariant(
     const void* v_win, const int32_t* raw_pos0, int32_t L_raw, const int32_t* q_pos0, int32_t W,
     int32_t B, int32_t T_q, int32_t H, int32_t d, float sm_scale, void* out, float* lse,
     void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * csa_kv_cache_append -- one decode step's token into a layer's KV cache.
+ *
+ * Passage: the newest uncompressed tokens are kept in bf16 beside compressed
+ * entries that may be fp8 (ferris DeepSeek-V4 analysis, 工程层, heterogeneous
+ * KV cache); every m tokens' K/V become one entry (blog.nickys.cn, 三大架构改动
+ * §1 CSA, §2 HCA).  The ring layout is this library's.
+ *
+ * For each sequence b with pos[b] >= 0 (its new token's position; < 0 = idle,
+ * nothing written):
+ *   - the token's K, V rows and logit are written to ring rows pos mod L_ring
+ *     and pos mod L_ring + L_ring;
+ *   - when pos + 1 is a multiple of m and entry (pos + 1)/m - 1 < cap, the m
+ *     rows of the completed block are pooled into that entry exactly as
+ *     csa_compress_kv pools a block (bit-identical results);
+ *   - raw_pos0[b] is set so that the attention calls, given k_win = k_ring,
+ *     v_win = v_ring, L_raw = 2 * L_ring, read the window of a query at pos
+ *     from the ring: raw_pos0 = q0 - (q0 mod L_ring), q0 = max(0, pos-L_ring+1)
+ *     (0 for idle sequences).  Valid for windows W <= L_ring.
+ *
+ *   k_new, v_new  [B, d] in io_dtype (CSA_BF16 or CSA_F32);  z_new [B] fp32
+ *   pos           [B] int32 (device)
+ *   k_ring, v_ring [B, 2*L_ring, d] io_dtype;  z_ring [B, 2*L_ring] fp32;
+ *                 caller-owned, persistent across calls, no initial contents
+ *   ck, cv        [B, cap, d] compressed cache in ckv_dtype (BF16, F32, or
+ *                 FP8_E4M3 with ck_scale, cv_scale [B, cap])
+ *   raw_pos0      [B] int32 output (device)
+ *   ws            csa_workspace_size(CSA_OP_KV_CACHE_APPEND, B, 0, 0, 0, 0)
+ *                 bytes; calls sharing it must be ordered on one stream.
+ * Limits: d = 128, m <= L_ring, B * 2 * L_ring < 2^31.
+ * Preconditions: each sequence's positions advance by one per call (the
+ * ring holds what earlier calls wrote).
+ * ------------------------------------------------------------------- */
+csa_status_t csa_kv_cache_append(const void* k_new, const void* v_new, const float* z_new,
+                                 int32_t io_dtype, const int32_t* pos, int32_t B, int32_t d,
+                                 int32_t L_ring, void* k_ring, void* v_ring, float* z_ring,
+                                 int32_t m, int32_t cap, int32_t ckv_dtype, void* ck, void* cv,
+                                 float* ck_scale, float* cv_scale, int32_t* raw_pos0, void* ws,
+                                 size_t ws_bytes, void* stream);
 
 /* Workspace bytes a call needs.  n_keys = k + W (CSA) or cap + W (HCA);
  * for CSA_OP_TOPK and CSA_OP_INDEXER_TOPK pass T_q and n_keys = cap (and, for

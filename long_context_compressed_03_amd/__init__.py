@@ -23,11 +23,13 @@ CSA_OK, CSA_EINVAL, CSA_ENOTSUP, CSA_EHIP, CSA_EWORKSPACE = range(5)
 CSA_BF16, CSA_F32, CSA_FP8_E4M3 = 0, 1, 2
 CSA_OP_TOPK, CSA_OP_SPARSE_ATTN, CSA_OP_DENSE_ATTN, CSA_OP_INDEXER_TOPK = 0, 1, 2, 3
 CSA_OP_SPARSE_ATTN_BATCH_INVARIANT, CSA_OP_DENSE_ATTN_BATCH_INVARIANT = 4, 5
+CSA_OP_KV_CACHE_APPEND = 6
 DTYPES = {"bf16": CSA_BF16, "f32": CSA_F32, "fp8": CSA_FP8_E4M3}
 
 EXPORTS = ["csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
            "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn",
-           "csa_sparse_attn_batch_invariant", "hca_dense_attn_batch_invariant", "csa_workspace_size",
+           "csa_sparse_attn_batch_invariant", "hca_dense_attn_batch_invariant", "csa_kv_cache_append",
+           "csa_workspace_size",
            "csa_status_str", "csa_abi_version"]
 
 _lib = None
@@ -66,7 +68,9 @@ def load(path=LIB_PATH):
     for fn in ["hca_dense_attn", "hca_dense_attn_batch_invariant"]:
         getattr(lib, fn).argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _P, _I,
                                      _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
-    for fn in ["csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
+    lib.csa_kv_cache_append.argtypes = [_P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P,
+                                        _P, _P, _P, _P, _S, _P]
+    for fn in ["csa_kv_cache_append", "csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
                "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn",
                "csa_sparse_attn_batch_invariant", "hca_dense_attn_batch_invariant"]:
         getattr(lib, fn).restype = _I
@@ -315,3 +319,25 @@ def csa_sparse_attn_batch_invariant(*args, **kwargs):
 def hca_dense_attn_batch_invariant(*args, **kwargs):
     """hca_dense_attn whose row results do not depend on the batch around them."""
     return hca_dense_attn(*args, batch_invariant=True, **kwargs)
+
+
+def csa_kv_cache_append(k_new, v_new, z_new, pos, k_ring, v_ring, z_ring, m, ck, cv, ck_scale=None,
+                        cv_scale=None, raw_pos0=None, stream=None):
+    """Append one token per sequence (k_new, v_new [B, d]; z_new [B]; pos [B] int32, < 0 = idle)
+    to a ring (k_ring, v_ring [B, 2L, d]; z_ring [B, 2L]) and, when a block of m completes,
+    its pooled entry to the compressed cache ck, cv [B, cap, d].  Returns raw_pos0 [B] int32:
+    the window base for the attention calls over the ring (L_raw = 2L)."""
+    B, d = k_new.shape
+    L2 = k_ring.shape[1]
+    if L2 % 2:
+        raise ValueError("the ring holds 2 * L_ring rows per sequence")
+    if raw_pos0 is None:
+        raw_pos0 = torch.empty(B, dtype=torch.int32, device=k_new.device)
+    lib = load()
+    ws = _workspace(k_new.device, lib.csa_workspace_size(CSA_OP_KV_CACHE_APPEND, B, 0, 0, 0, 0))
+    st = lib.csa_kv_cache_append(_ptr(k_new), _ptr(v_new), _ptr(z_new), _dt_of(k_new), _ptr(pos), B, d,
+                                 L2 // 2, _ptr(k_ring), _ptr(v_ring), _ptr(z_ring), m, ck.shape[1],
+                                 _dt_of(ck), _ptr(ck), _ptr(cv), _ptr(ck_scale), _ptr(cv_scale),
+                                 _ptr(raw_pos0), _ws_ptr(ws), _ws_len(ws), _stream(stream))
+    _check("csa_kv_cache_append", st)
+    return raw_pos0

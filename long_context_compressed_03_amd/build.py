@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa.so")
-SOURCES = ["abi.hip", "compress.hip", "indexer.hip", "indexer_topk.hip", "topk.hip", "attn.hip", "quant.hip"]
+SOURCES = ["abi.hip", "compress.hip", "indexer.hip", "indexer_topk.hip", "topk.hip", "attn.hip", "quant.hip", "cache.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument"]

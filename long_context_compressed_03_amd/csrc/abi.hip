@@ -2,6 +2,7 @@
 #include "common.hpp"
 
 size_t csa_attn_workspace_size(long rows, int H, int n_list, bool invariant);
+size_t csa_kv_append_workspace_size(int B);
 size_t csa_indexer_topk_workspace_size(long rows, int T_q, int d_I, int cap);
 size_t csa_topk_workspace_size(long rows, int cap);
 
@@ -19,6 +20,8 @@ extern "C" size_t csa_workspace_size(int32_t op, int32_t B, int32_t T_q, int32_t
       if (d != kHeadDim || H < 16 || H > 128 || H % 16 != 0) return size_t(-1);
       return csa_attn_workspace_size(long(B) * T_q, H, n_keys,
                                      op == CSA_OP_SPARSE_ATTN_BATCH_INVARIANT || op == CSA_OP_DENSE_ATTN_BATCH_INVARIANT);
+    case CSA_OP_KV_CACHE_APPEND:
+      return csa_kv_append_workspace_size(B);
     default:
       return size_t(-1);
   }

@@ -34,25 +34,53 @@ __global__ __launch_bounds__(kBlock) void compress_kernel(const void* __restrict
   compress_group<kInF32, kOut>(k, v, logits, n_entries, ld_in, m, k_out, v_out, k_scale, v_scale, ld_out, gid, lane_c);
 }
 
+// Cache append, short blocks: group b pools sequence b's planned block.
+template <int kInF32, int kOut>
+__global__ __launch_bounds__(kBlock) void compress_append_kernel(const void* __restrict__ k, const void* __restrict__ v,
+                                                                 const float* __restrict__ logits, int B, int ld_in,
+                                                                 int m, void* k_out, void* v_out, float* k_scale,
+                                                                 float* v_scale, int ld_out,
+                                                                 const int32_t* __restrict__ plan) {
+  const int lane_c = threadIdx.x & (kGroup - 1);
+  const int b = int(blockIdx.x) * int(blockDim.x / kGroup) + int(threadIdx.x / kGroup);
+  if (b >= B) return;                      // whole 16-lane groups exit together
+  const int e = plan[B + b];
+  if (e < 0) return;
+  compress_group_at<kInF32, kOut>(k, v, logits, size_t(b) * ld_in + plan[b], m, k_out, v_out, k_scale, v_scale,
+                                  size_t(b) * ld_out + e, lane_c);
+}
+
 // One tensor of one entry per block (blockIdx.y: 0 = K, 1 = V; each has its
 // own fp8 scale, so the two never meet): 16 groups split the rows, partial
 // sums meet in LDS.  The softmax statistics are reduced over the block.
-template <int kInF32, int kOut>
+// kAppend: block x pools sequence x's planned block (plan as for
+// compress_append_kernel), or does nothing when it has none.
+template <int kInF32, int kOut, bool kAppend>
 __global__ __launch_bounds__(kBlock) void compress_long_kernel(const void* __restrict__ k, const void* __restrict__ v,
                                                                const float* __restrict__ logits, int n_entries,
                                                                int ld_in, int m, void* k_out, void* v_out,
-                                                               float* k_scale, float* v_scale, int ld_out) {
+                                                               float* k_scale, float* v_scale, int ld_out,
+                                                               const int32_t* __restrict__ plan) {
   __shared__ float part[kEntriesPerBlock][kHeadDim + 4];
   __shared__ float wz[kBlock];              // exp(z_r - max) of the first 256 rows
   __shared__ float red[2][kBlock / 64];
   const int lane_c = threadIdx.x & (kGroup - 1);
   const int grp = threadIdx.x / kGroup;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int b = blockIdx.x / n_entries;
-  const int e = blockIdx.x - b * n_entries;
+  int b, e;
+  size_t row0;
+  if constexpr (kAppend) {
+    b = blockIdx.x;                       // n_entries is the batch here
+    e = plan[n_entries + b];
+    if (e < 0) return;                    // the whole block, before any barrier
+    row0 = size_t(b) * ld_in + plan[b];
+  } else {
+    b = blockIdx.x / n_entries;
+    e = blockIdx.x - b * n_entries;
+    row0 = size_t(b) * ld_in + size_t(e) * m;
+  }
   const int kv = blockIdx.y;
   const void* src = kv ? v : k;
-  const size_t row0 = size_t(b) * ld_in + size_t(e) * m;
   const float* z = logits + row0;
 
   float ak[8];
@@ -151,8 +179,8 @@ hipError_t launch_one(dim3 grid_short, long total, hipStream_t st, const void* k
                       int ne, int ld_in, int m, void* ko, void* vo, float* ks, float* vs, int ld_out) {
   (void)grid_short;
   if (m >= 32) {
-    hipLaunchKernelGGL((compress_long_kernel<kInF32, kOut>), dim3(unsigned(total), 2u), dim3(kBlock), 0, st, k, v, lg, ne,
-                       ld_in, m, ko, vo, ks, vs, ld_out);
+    hipLaunchKernelGGL((compress_long_kernel<kInF32, kOut, false>), dim3(unsigned(total), 2u), dim3(kBlock), 0, st, k, v,
+                       lg, ne, ld_in, m, ko, vo, ks, vs, ld_out, static_cast<const int32_t*>(nullptr));
   } else {
     // few entries (decoding): 4 per 64-thread block, so their rows are
     // fetched by several CUs; otherwise 16 per 256-thread block
@@ -178,7 +206,43 @@ hipError_t launch_compress(int out_dt, dim3 grid, long total, hipStream_t st, co
   }
 }
 
+template <int kInF32, int kOut>
+hipError_t launch_append_one(const void* k, const void* v, const float* lg, int B, int ld_in, int m, void* ko,
+                             void* vo, float* ks, float* vs, int ld_out, const int32_t* plan, hipStream_t st) {
+  if (m >= 32) {
+    hipLaunchKernelGGL((compress_long_kernel<kInF32, kOut, true>), dim3(unsigned(B), 2u), dim3(kBlock), 0, st, k, v, lg,
+                       B, ld_in, m, ko, vo, ks, vs, ld_out, plan);
+  } else {
+    constexpr int kPer = 64 / kGroup;    // 4 sequences per 64-thread block
+    hipLaunchKernelGGL((compress_append_kernel<kInF32, kOut>), dim3(unsigned((B + kPer - 1) / kPer)), dim3(64), 0, st,
+                       k, v, lg, B, ld_in, m, ko, vo, ks, vs, ld_out, plan);
+  }
+  return hipGetLastError();
+}
+
+template <int kInF32>
+hipError_t launch_append(int out_dt, const void* k, const void* v, const float* lg, int B, int ld_in, int m, void* ko,
+                         void* vo, float* ks, float* vs, int ld_out, const int32_t* plan, hipStream_t st) {
+  switch (out_dt) {
+    case CSA_BF16:
+      return launch_append_one<kInF32, CSA_BF16>(k, v, lg, B, ld_in, m, ko, vo, ks, vs, ld_out, plan, st);
+    case CSA_F32:
+      return launch_append_one<kInF32, CSA_F32>(k, v, lg, B, ld_in, m, ko, vo, ks, vs, ld_out, plan, st);
+    default:
+      return launch_append_one<kInF32, CSA_FP8_E4M3>(k, v, lg, B, ld_in, m, ko, vo, ks, vs, ld_out, plan, st);
+  }
+}
+
 }  // namespace
+
+hipError_t csa_cmp::launch_compress_append(int in_dtype, int out_dtype, const void* k, const void* v,
+                                           const float* logits, int B, int ld_in, int m, void* k_out, void* v_out,
+                                           float* k_scale, float* v_scale, int ld_out, const int32_t* plan,
+                                           hipStream_t st) {
+  return in_dtype == CSA_F32
+             ? launch_append<1>(out_dtype, k, v, logits, B, ld_in, m, k_out, v_out, k_scale, v_scale, ld_out, plan, st)
+             : launch_append<0>(out_dtype, k, v, logits, B, ld_in, m, k_out, v_out, k_scale, v_scale, ld_out, plan, st);
+}
 
 extern "C" csa_status_t csa_compress_kv(const void* k, const void* v, int32_t in_dtype, const float* logits,
                                         int32_t B, int32_t L, int32_t ld_in, int32_t d, int32_t m, void* k_out,

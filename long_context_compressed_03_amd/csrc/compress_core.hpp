@@ -59,16 +59,14 @@ CSA_DEV void store_entry(void* out, float* scale_out, size_t entry, int lane_c, 
   }
 }
 
-// Entry gid (< B * n_entries) by the 16-lane group whose lane lane_c owns
-// head columns [8 lane_c, 8 lane_c + 8); rows are walked with 4 loads in
-// flight per lane for each of K and V.
+// The entry pooled from rows [row0, row0 + m) (and their logits) into
+// output slot `entry`, by the 16-lane group whose lane lane_c owns head
+// columns [8 lane_c, 8 lane_c + 8); rows are walked with 4 loads in flight
+// per lane for each of K and V.
 template <int kInF32, int kOut>
-CSA_DEV void compress_group(const void* __restrict__ k, const void* __restrict__ v, const float* __restrict__ logits,
-                            int n_entries, int ld_in, int m, void* k_out, void* v_out, float* k_scale, float* v_scale,
-                            int ld_out, long gid, int lane_c) {
-  const int b = int(gid / n_entries);
-  const int e = int(gid - long(b) * n_entries);
-  const size_t row0 = size_t(b) * ld_in + size_t(e) * m;
+CSA_DEV void compress_group_at(const void* __restrict__ k, const void* __restrict__ v,
+                               const float* __restrict__ logits, size_t row0, int m, void* k_out, void* v_out,
+                               float* k_scale, float* v_scale, size_t entry, int lane_c) {
   const float* z = logits + row0;
 
   // softmax statistics of the block's logits, spread over the 16 lanes;
@@ -122,10 +120,27 @@ CSA_DEV void compress_group(const void* __restrict__ k, const void* __restrict__
       av[i] = fmaf(a, vr[i], av[i]);
     }
   }
-  const size_t entry = size_t(b) * ld_out + e;
   store_entry<kOut>(k_out, k_scale, entry, lane_c, ak);
   store_entry<kOut>(v_out, v_scale, entry, lane_c, av);
 }
+
+// Entry gid (< B * n_entries): sequence b's block e, rows b * ld_in + e * m.
+template <int kInF32, int kOut>
+CSA_DEV void compress_group(const void* __restrict__ k, const void* __restrict__ v, const float* __restrict__ logits,
+                            int n_entries, int ld_in, int m, void* k_out, void* v_out, float* k_scale, float* v_scale,
+                            int ld_out, long gid, int lane_c) {
+  const int b = int(gid / n_entries);
+  const int e = int(gid - long(b) * n_entries);
+  compress_group_at<kInF32, kOut>(k, v, logits, size_t(b) * ld_in + size_t(e) * m, m, k_out, v_out, k_scale, v_scale,
+                                  size_t(b) * ld_out + e, lane_c);
+}
+
+// Pools, for each sequence b < B with plan[B + b] >= 0, the m rows starting
+// at row plan[b] of its input (rows b * ld_in + plan[b] ...) into entry
+// plan[B + b] of its output; the cache append's second launch.
+hipError_t launch_compress_append(int in_dtype, int out_dtype, const void* k, const void* v, const float* logits,
+                                  int B, int ld_in, int m, void* k_out, void* v_out, float* k_scale, float* v_scale,
+                                  int ld_out, const int32_t* plan, hipStream_t st);
 
 // The arguments of one compression call.
 struct CompressArgs {

@@ -1,0 +1,182 @@
+"""GPU parity of the decode KV cache append (csa_kv_cache_append) with the cache oracle.
+
+Sequences start at different positions (multiples of m) and one of them idles every third
+step. After a few hundred one-token steps:
+  * every written ring row holds, bit for bit, the token the oracle's ring state names;
+  * every appended compressed entry equals, bit for bit, the entry csa_compress_kv pools
+    from the linear history, and lies within the compression tolerance of the oracle's
+    pool; entries the run did not complete stay untouched;
+  * raw_pos0 is the oracle's window base, and attention read through the ring
+    (L_raw = 2L) gives the same bits as attention over the linear history.
+Inputs: the seeded compression inputs (normal K/V, normal logits) of the parity tests.
+"""
+import numpy as np
+import pytest
+import torch
+
+from csa_synth import attn_inputs, compress_inputs, random_topk_idx
+from gpu_helpers import compress_tolerance, h, h_bf16, say, t_f32, t_i32, t_kv
+from oracle.cache import appended_entries, ring_rows, window_base
+from oracle.compress import compress_values, store
+from oracle.formats import bf16_decode, e4m3_decode
+from oracle.indexer import nvis
+
+pytestmark = pytest.mark.gpu
+
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.uint8}
+
+
+@pytest.fixture(scope="module")
+def csa():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import long_context_compressed_03_amd as m
+    m.load()
+    return m
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16 if t.element_size() == 2 else
+                               (torch.uint8 if t.element_size() == 1 else torch.int32)).cpu().numpy()
+
+
+def _host_values(x, dt):
+    return bf16_decode(x) if dt == "bf16" else x.astype(np.float64)
+
+
+CASES = [
+    # io, ckv, B, m, L, cap, starts, steps, idle sequence (None: none)
+    ("bf16", "bf16", 3, 4, 128, 64, [0, 40, 200], 300, 1),
+    ("bf16", "fp8", 2, 128, 128, 8, [0, 128], 420, None),      # HCA-sized blocks
+    ("f32", "f32", 2, 4, 16, 100, [0, 8], 99, 0),
+    ("bf16", "fp8", 5, 4, 128, 40, [0, 4, 8, 12, 100], 60, 4),
+]
+
+
+@pytest.mark.parametrize("io,ckv,B,m,L,cap,starts,steps,idle", CASES)
+def test_cache_append(csa, io, ckv, B, m, L, cap, starts, steps, idle):
+    say(f"kv cache append io={io} ckv={ckv} B={B} m={m} L={L} cap={cap} steps={steps}")
+    assert (steps - 1) % 3 != 1                  # every sequence appends at the last step
+    n_total = max(starts) + steps + 1
+    n_total += (-n_total) % m
+    x = compress_inputs(B, n_total, io, seed=B * m + L)
+    K_d, V_d, Z_d = t_kv(x["K"], io), t_kv(x["V"], io), t_f32(x["logits"])
+    ring_k = torch.zeros((B, 2 * L, 128), dtype=TDT[io], device="cuda")
+    ring_v = torch.zeros_like(ring_k)
+    ring_z = torch.zeros((B, 2 * L), dtype=torch.float32, device="cuda")
+    ck = torch.zeros((B, cap, 128), dtype=TDT[ckv], device="cuda")
+    cv = torch.zeros_like(ck)
+    cks = cvs = None
+    if ckv == "fp8":
+        cks = torch.full((B, cap), -1.0, device="cuda")
+        cvs = torch.full((B, cap), -1.0, device="cuda")
+    nxt = np.array(starts, np.int64)
+    ar = torch.arange(B, device="cuda")
+    raw0 = None
+    for s in range(steps):
+        active = np.array([not (idle is not None and b == idle and s % 3 == 1) for b in range(B)])
+        pos = np.where(active, nxt, -1).astype(np.int32)
+        pos_d = t_i32(pos)
+        src = pos_d.long().clamp(min=0)
+        raw0 = csa.csa_kv_cache_append(K_d[ar, src].contiguous(), V_d[ar, src].contiguous(),
+                                       Z_d[ar, src].contiguous(), pos_d, ring_k, ring_v, ring_z, m, ck, cv,
+                                       ck_scale=cks, cv_scale=cvs)
+        nxt += active
+    torch.cuda.synchronize()
+    last = nxt - 1
+
+    # window bases
+    assert np.array_equal(h(raw0), np.array([window_base(int(p), L) for p in last], np.int32))
+
+    # ring rows, bit for bit
+    kb, vb, zb = _bits(ring_k), _bits(ring_v), _bits(ring_z)
+    Kb, Vb = _bits(K_d), _bits(V_d)
+    Zb = _bits(Z_d)
+    for b in range(B):
+        for got, hist in ((kb, Kb), (vb, Vb), (zb, Zb)):
+            want, written = ring_rows(hist[b], int(nxt[b]), L, starts[b])
+            assert np.array_equal(got[b][written], want[written]), b
+
+    # entries: bit for bit against csa_compress_kv over the linear history
+    n_ent = n_total // m
+    lk = torch.zeros((B, n_ent, 128), dtype=TDT[ckv], device="cuda")
+    lv = torch.zeros_like(lk)
+    lks = lvs = None
+    if ckv == "fp8":
+        lks = torch.zeros((B, n_ent), device="cuda")
+        lvs = torch.zeros((B, n_ent), device="cuda")
+    csa.csa_compress_kv(K_d, V_d, Z_d, m, lk, lv, lks, lvs)
+    torch.cuda.synchronize()
+    ckb, cvb, lkb, lvb = _bits(ck), _bits(cv), _bits(lk), _bits(lv)
+    Kx, Vx = _host_values(x["K"], io), _host_values(x["V"], io)
+    for b in range(B):
+        ents = appended_entries(int(nxt[b]), m, cap, starts[b])
+        assert len(ents) > 0
+        e = np.array(ents)
+        assert np.array_equal(ckb[b, e], lkb[b, e]) and np.array_equal(cvb[b, e], lvb[b, e]), b
+        rest = np.setdiff1d(np.arange(cap), e)
+        assert np.all(ckb[b, rest] == 0) and np.all(cvb[b, rest] == 0), b
+        if ckv == "fp8":
+            assert np.array_equal(_bits(cks)[b, e], _bits(lks)[b, e])
+            assert np.all(h(cks)[b, rest] == -1.0)
+        # the oracle's pool of the same blocks
+        rows = (e[:, None] * m + np.arange(m)[None]).reshape(-1)
+        Kh, Vh = compress_values(Kx[b, rows][None], Vx[b, rows][None], x["logits"][b, rows][None], m)
+        for X, out, sc in ((Kh[0], ck, cks), (Vh[0], cv, cvs)):
+            amax = np.abs(np.stack([Kx[b, rows], Vx[b, rows]])).max()
+            eps = (m + 4) * 2.0 ** -24 * amax
+            if ckv == "fp8":
+                gs = h(sc)[b, e].astype(np.float64)
+                g = e4m3_decode(h(out)[b, e]) * gs[:, None]
+                codes, scale = store(X, "fp8")
+                o = e4m3_decode(codes) * scale[:, None].astype(np.float64)
+                tol = compress_tolerance(X, "fp8", eps, scale)
+            elif ckv == "bf16":
+                g, o = bf16_decode(h_bf16(out)[b, e]), bf16_decode(store(X, "bf16"))
+                tol = compress_tolerance(X, "bf16", eps)
+            else:
+                g, o = h(out)[b, e].astype(np.float64), store(X, "f32").astype(np.float64)
+                tol = compress_tolerance(X, "f32", eps)
+            assert np.all(np.abs(g - o) <= tol), np.abs(g - o).max()
+
+    # attention through the ring = attention over the linear history, bit for bit; the
+    # tokens before a sequence's first append were never written to its ring (zeros there)
+    K_lin, V_lin = K_d.clone(), V_d.clone()
+    for b in range(B):
+        K_lin[b, :starts[b]] = 0
+        V_lin[b, :starts[b]] = 0
+    H, W = 16, L
+    q_pos = last.astype(np.int32)
+    a = attn_inputs(B, 1, H, 8, 1, io, "bf16" if io == "bf16" else "f32", seed=3)
+    q = t_kv(a["q"], io)
+    if m >= 32:
+        o_ring = csa.hca_dense_attn(q, ck, cv, m, ring_k, ring_v, raw0, t_i32(q_pos), W,
+                                    ck_scale=cks, cv_scale=cvs)
+        o_lin = csa.hca_dense_attn(q, ck, cv, m, K_lin, V_lin, t_i32(np.zeros(B, np.int32)), t_i32(q_pos), W,
+                                   ck_scale=cks, cv_scale=cvs)
+    else:
+        k = 16
+        idx = t_i32(random_topk_idx(np.minimum(nvis(q_pos[:, None], m), cap), k, cap, seed=1))
+        o_ring = csa.csa_sparse_attn(q, ck, cv, idx, ring_k, ring_v, raw0, t_i32(q_pos), W,
+                                     ck_scale=cks, cv_scale=cvs)
+        o_lin = csa.csa_sparse_attn(q, ck, cv, idx, K_lin, V_lin, t_i32(np.zeros(B, np.int32)), t_i32(q_pos), W,
+                                    ck_scale=cks, cv_scale=cvs)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(o_ring), _bits(o_lin))
+
+
+def test_cache_append_rejects_bad_arguments(csa):
+    say("kv cache append: argument errors")
+    lib = csa.load()
+    B, L = 2, 8
+    z = torch.zeros((B, 128), dtype=torch.bfloat16, device="cuda")
+    ring = torch.zeros((B, 2 * L, 128), dtype=torch.bfloat16, device="cuda")
+    rz = torch.zeros((B, 2 * L), device="cuda")
+    pos = t_i32(np.zeros(B, np.int32))
+    ck = torch.zeros((B, 4, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(csa.CsaError):
+        csa.csa_kv_cache_append(z, z, rz[:, 0].contiguous(), pos, ring, ring, rz, 16, ck, ck)   # m > L
+    with pytest.raises(csa.CsaError):
+        csa.csa_kv_cache_append(z, z, rz[:, 0].contiguous(), pos, ring, ring, rz, 4,
+                                ck.to(torch.uint8), ck.to(torch.uint8))                   # fp8 without scales
+    assert lib.csa_workspace_size(csa.CSA_OP_KV_CACHE_APPEND, 3, 0, 0, 0, 0) == 256
