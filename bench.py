@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="csa_decode_128k",
                    choices=["csa_decode_128k", "hca_decode_1m", "csa_prefill_256k", "pair_1m",
-                            "mxfp4_quantize_keys_128k"])
+                            "mxfp4_quantize_keys_128k", "kv_append_decode_128k"])
     p.add_argument("--rotate", type=int, default=0, help="input copies (0 = auto)")
     p.add_argument("--indexer", default="auto", choices=["auto", "combined", "fused", "unfused"],
                    help="CSA scoring + selection as one fused call or as csa_indexer_scores then "
@@ -300,11 +300,55 @@ def build_quant(args):
     return st
 
 
+APPEND_WORKLOAD = "kv_append_decode_128k"
+APPEND_SHAPE = dict(B=16, L=128, m=4, cap=32768, pos=131071)
+
+
+def build_append(args):
+    """One decode step's KV cache append for the 128K decode shape: 16 sequences, each
+    appending its token at position 131071 (which completes a block of m = 4, so the
+    block is pooled into fp8 entry 32767) to a 128-token bf16 window ring."""
+    import torch
+    from csa_synth import compress_inputs
+    import long_context_compressed_03_amd as csa
+    B, L, m, cap, p = (APPEND_SHAPE[k] for k in ("B", "L", "m", "cap", "pos"))
+    x = compress_inputs(B, 2 * L + 1, "bf16", seed=17)
+    st = Step(APPEND_WORKLOAD, B)
+    # per sequence: the new K/V rows and logit read; 2 copies of each written; the block's
+    # m K/V rows and logits read back; the fp8 entries and scales written; pos, plan, base
+    nbytes = B * (2 * 256 + 4 + 2 * (2 * 256 + 4) + m * (2 * 256 + 4) + 2 * (128 + 4) + 4 + 8 + 8 + 4)
+
+    def f_append(c):
+        csa.csa_kv_cache_append(c["k_new"], c["v_new"], c["z_new"], c["pos"], c["rk"], c["rv"], c["rz"], m,
+                                c["ck"], c["cv"], ck_scale=c["cks"], cv_scale=c["cvs"], raw_pos0=c["raw0"])
+    st.add(Kernel("kv_cache_append", f_append, nbytes, 0, BF16_PEAK_TFLOPS, "kv_cache_append"))
+    K = torch.from_numpy(x["K"].view(np.int16)).view(torch.bfloat16).cuda()
+    V = torch.from_numpy(x["V"].view(np.int16)).view(torch.bfloat16).cuda()
+    Z = torch.from_numpy(x["logits"]).cuda()
+    base = {"rk": K[:, :2 * L].contiguous(), "rv": V[:, :2 * L].contiguous(), "rz": Z[:, :2 * L].contiguous(),
+            "k_new": K[:, 2 * L].contiguous(), "v_new": V[:, 2 * L].contiguous(),
+            "z_new": Z[:, 2 * L].contiguous(),
+            "pos": torch.full((B,), p, dtype=torch.int32, device="cuda"),
+            "ck": torch.zeros((B, cap, 128), dtype=torch.uint8, device="cuda"),
+            "cv": torch.zeros((B, cap, 128), dtype=torch.uint8, device="cuda"),
+            "cks": torch.zeros((B, cap), device="cuda"), "cvs": torch.zeros((B, cap), device="cuda"),
+            "raw0": torch.empty((B,), dtype=torch.int32, device="cuda")}
+    R = args.rotate or 4
+    st.copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
+    st.layers = [("", {"append_sample": {k: x[k][:, :2 * L + 1] for k in ("K", "V", "logits")}})]
+    st.config = {"workload": APPEND_WORKLOAD, "batch": B, "position": p, "ring_tokens": L,
+                 "block_m": m, "compressed_entries": cap, "window_kv": "bf16",
+                 "compressed_kv": "fp8_e4m3+fp32 scale", "pooling": "every step (the block completes)"}
+    return st
+
+
 def build(args):
     """Host inputs, R device copies and the step's launches for the chosen workload."""
     import torch
     if args.workload == QUANT_WORKLOAD:
         return build_quant(args)
+    if args.workload == APPEND_WORKLOAD:
+        return build_append(args)
     from csa_synth import workloads
     wls = workloads()
     parts = LAYERS[args.workload]
@@ -442,7 +486,8 @@ KERNEL_SOURCES = {
     "compress_kv": ["compress.hip", "compress_core.hpp", "common.hpp"],
     "compress_indexer_topk": ["indexer_topk.hip", "indexer_core.hpp", "split.hpp", "topk.hip", "select.hpp",
                               "compress_core.hpp", "compress.hip", "common.hpp"],
-    "mxfp4_quantize": ["quant.hip", "common.hpp"]}
+    "mxfp4_quantize": ["quant.hip", "common.hpp"],
+    "kv_cache_append": ["cache.hip", "compress.hip", "compress_core.hpp", "common.hpp"]}
 
 
 def measured_traffic(workload, kernel):
@@ -474,6 +519,31 @@ def cpu_baseline_quant(st):
     mxfp4_encode(x)
     dt = time.perf_counter() - t0
     return len(sample) / dt, f"fp64 numpy oracle encoder on {len(sample)} of the workload's vectors ({dt:.2f} s)"
+
+
+def cpu_baseline_append(st, budget_s=10.0):
+    """The oracle's cache append (ring writes as the step-by-step definition states them,
+    then the pool of the completed block) for the workload's 16 sequences, repeated within
+    the budget; appended tokens/s."""
+    from oracle.cache import append_step_by_step
+    from oracle.compress import compress_kv
+    from oracle.formats import bf16_decode
+    x = st.layers[0][1]["append_sample"]
+    L, m, p = APPEND_SHAPE["L"], APPEND_SHAPE["m"], APPEND_SHAPE["pos"]
+    K, V, Z = bf16_decode(x["K"]), bf16_decode(x["V"]), x["logits"]
+    B = K.shape[0]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for b in range(B):
+            for X in (K[b], V[b], Z[b]):
+                append_step_by_step(X, X.shape[0], L, start=X.shape[0] - 1)   # the newest token
+            compress_kv(K[b:b + 1, -m:], V[b:b + 1, -m:], Z[b:b + 1, -m:], m, "fp8")
+        reps += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return reps * B / dt, (f"fp64 numpy oracle: {reps} appends of the workload's {B} tokens at "
+                           f"position {p} (ring writes + fp8 pooling of the completed block), {dt:.1f} s")
 
 
 def cpu_baseline(st, budget_s):
@@ -596,19 +666,26 @@ def main():
                       "algorithmic_flops": kk.flops, "bound": kk.bound, "achieved": round(a_, 1),
                       "unit": u_, "frac": round(a_ / p_, 4)}
     quant = args.workload == QUANT_WORKLOAD
-    unit = "key-vectors/s" if quant else "query-tokens/s"
+    append = args.workload == APPEND_WORKLOAD
+    unit = "key-vectors/s" if quant else "appended-tokens/s" if append else "query-tokens/s"
     cpu = None
     if not args.no_cpu_baseline:
-        v, desc = cpu_baseline_quant(st) if quant else cpu_baseline(st, args.cpu_seconds)
+        if quant:
+            v, desc = cpu_baseline_quant(st)
+        elif append:
+            v, desc = cpu_baseline_append(st, args.cpu_seconds)
+        else:
+            v, desc = cpu_baseline(st, args.cpu_seconds)
         cpu = {"value": round(v, 4), "unit": unit, "cores": 1, "kind": "oracle", "sample": desc}
     q_per_s = st.q_tokens / (ms * 1e-3)
-    metric = "MXFP4 quantisation of the indexer keys, key-vectors/s; % HBM roofline" if quant else METRIC
+    metric = ("MXFP4 quantisation of the indexer keys, key-vectors/s; % HBM roofline" if quant else
+              "decode KV cache append (window ring + block pooling), appended tokens/s" if append else METRIC)
     line = {"metric": metric, "value": round(q_per_s, 1), "unit": unit, "n_gpus": 1,
             "steps": done, "warmup": args.warmup, "ms_per_step": round(ms, 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "mxfp4+bf16", "data": "synthetic (seeded; shapes of the pages' 128K-1M contexts)",
             "config": st.config, "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
-            ("vectors_per_step" if quant else "query_tokens_per_step"): st.q_tokens,
+            ("vectors_per_step" if quant else "tokens_per_step" if append else "query_tokens_per_step"): st.q_tokens,
             "rotation_copies": len(st.copies),
             "graph": not args.no_graph, "wall_s_timed_region": round(wall, 4)}
     print(json.dumps(line), flush=True)
