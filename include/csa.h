@@ -352,8 +352,9 @@ csa_status_t hca_dense_attn_batch_invariant(
  *   ck, cv        [B, cap, d] compressed cache in ckv_dtype (BF16, F32, or
  *                 FP8_E4M3 with ck_scale, cv_scale [B, cap])
  *   raw_pos0      [B] int32 output (device)
- *   ws            csa_workspace_size(CSA_OP_KV_CACHE_APPEND, B, 0, 0, 0, 0)
- *                 bytes; calls sharing it must be ordered on one stream.
+ *   ws, ws_bytes  unused (csa_workspace_size(CSA_OP_KV_CACHE_APPEND, ...) is 0);
+ *                 may be NULL, 0.  Calls on one cache must be ordered on one
+ *                 stream.
  * Limits: d = 128, m <= L_ring, B * 2 * L_ring < 2^31.
  * Preconditions: each sequence's positions advance by one per call (the
  * ring holds what earlier calls wrote).

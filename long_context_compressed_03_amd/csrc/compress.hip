@@ -34,54 +34,105 @@ __global__ __launch_bounds__(kBlock) void compress_kernel(const void* __restrict
   compress_group<kInF32, kOut>(k, v, logits, n_entries, ld_in, m, k_out, v_out, k_scale, v_scale, ld_out, gid, lane_c);
 }
 
-// Cache append, short blocks: group b pools sequence b's planned block.
+// Cache append, short blocks (m < 32): 16-lane group g serves sequence
+// 4 * blockIdx.x + g.  It writes the token's K/V rows (both ring copies;
+// lane c its 8 columns) and logit, the window base, and pools the block the
+// token completes with its newest row read from the input (the ring rows it
+// reads hold older tokens, never the two rows being written).
 template <int kInF32, int kOut>
-__global__ __launch_bounds__(kBlock) void compress_append_kernel(const void* __restrict__ k, const void* __restrict__ v,
-                                                                 const float* __restrict__ logits, int B, int ld_in,
-                                                                 int m, void* k_out, void* v_out, float* k_scale,
-                                                                 float* v_scale, int ld_out,
-                                                                 const int32_t* __restrict__ plan) {
+__global__ __launch_bounds__(64) void cache_append_short_kernel(AppendArgs a) {
   const int lane_c = threadIdx.x & (kGroup - 1);
   const int b = int(blockIdx.x) * int(blockDim.x / kGroup) + int(threadIdx.x / kGroup);
-  if (b >= B) return;                      // whole 16-lane groups exit together
-  const int e = plan[B + b];
-  if (e < 0) return;
-  compress_group_at<kInF32, kOut>(k, v, logits, size_t(b) * ld_in + plan[b], m, k_out, v_out, k_scale, v_scale,
-                                  size_t(b) * ld_out + e, lane_c);
+  if (b >= a.B) return;                    // whole 16-lane groups exit together
+  const int p = a.pos[b];
+  const AppendPlan pl = append_plan(p, a.L, a.m, a.cap);
+  constexpr int kEl = kInF32 ? 4 : 2;
+  constexpr int kLaneBytes = kColsPerLane * kEl;
+  const size_t ring0 = size_t(b) * 2 * a.L;
+  const uint8_t* kn = static_cast<const uint8_t*>(a.k_new) + size_t(b) * kHeadDim * kEl;
+  const uint8_t* vn = static_cast<const uint8_t*>(a.v_new) + size_t(b) * kHeadDim * kEl;
+  if (p >= 0) {
+    const int s = p % a.L;
+#pragma unroll
+    for (int h = 0; h < kLaneBytes / 16; ++h) {
+      const uint4 xk = *reinterpret_cast<const uint4*>(kn + lane_c * kLaneBytes + h * 16);
+      const uint4 xv = *reinterpret_cast<const uint4*>(vn + lane_c * kLaneBytes + h * 16);
+#pragma unroll
+      for (int copy = 0; copy < 2; ++copy) {
+        const size_t off = (ring0 + s + size_t(copy) * a.L) * kHeadDim * kEl + lane_c * kLaneBytes + h * 16;
+        *reinterpret_cast<uint4*>(static_cast<uint8_t*>(a.k_ring) + off) = xk;
+        *reinterpret_cast<uint4*>(static_cast<uint8_t*>(a.v_ring) + off) = xv;
+      }
+    }
+    if (lane_c < 2) a.z_ring[ring0 + s + size_t(lane_c) * a.L] = a.z_new[b];
+  }
+  if (lane_c == 0) a.raw_pos0[b] = pl.base;
+  if (!pl.done) return;
+  compress_group_at<kInF32, kOut, true>(a.k_ring, a.v_ring, a.z_ring, ring0 + pl.first_row, a.m, a.ck, a.cv,
+                                        a.ck_scale, a.cv_scale, size_t(b) * a.cap + pl.entry, lane_c, kn, vn,
+                                        a.z_new + b);
 }
 
 // One tensor of one entry per block (blockIdx.y: 0 = K, 1 = V; each has its
 // own fp8 scale, so the two never meet): 16 groups split the rows, partial
 // sums meet in LDS.  The softmax statistics are reduced over the block.
-// kAppend: block x pools sequence x's planned block (plan as for
-// compress_append_kernel), or does nothing when it has none.
+// kAppend (the cache append, m >= 32): block (x, t) writes tensor t's rows
+// of sequence x's new token (both ring copies; the logit and window base with
+// t = 0) and pools the block the token completes, its newest row read from
+// the input, as the short kernel does.
 template <int kInF32, int kOut, bool kAppend>
 __global__ __launch_bounds__(kBlock) void compress_long_kernel(const void* __restrict__ k, const void* __restrict__ v,
                                                                const float* __restrict__ logits, int n_entries,
                                                                int ld_in, int m, void* k_out, void* v_out,
                                                                float* k_scale, float* v_scale, int ld_out,
-                                                               const int32_t* __restrict__ plan) {
+                                                               AppendArgs app) {
   __shared__ float part[kEntriesPerBlock][kHeadDim + 4];
   __shared__ float wz[kBlock];              // exp(z_r - max) of the first 256 rows
   __shared__ float red[2][kBlock / 64];
   const int lane_c = threadIdx.x & (kGroup - 1);
   const int grp = threadIdx.x / kGroup;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int kv = blockIdx.y;
   int b, e;
   size_t row0;
+  const void* newest = nullptr;           // kAppend: the token's row and logit
+  const float* znew = nullptr;
   if constexpr (kAppend) {
-    b = blockIdx.x;                       // n_entries is the batch here
-    e = plan[n_entries + b];
-    if (e < 0) return;                    // the whole block, before any barrier
-    row0 = size_t(b) * ld_in + plan[b];
+    b = blockIdx.x;
+    const int p = app.pos[b];
+    const AppendPlan pl = append_plan(p, app.L, app.m, app.cap);
+    constexpr int kEl = kInF32 ? 4 : 2;
+    constexpr int kChunks = kHeadDim * kEl / 16;   // 16-B pieces per row
+    const size_t ring0 = size_t(b) * 2 * app.L;
+    const uint8_t* nrow = static_cast<const uint8_t*>(kv ? app.v_new : app.k_new) + size_t(b) * kHeadDim * kEl;
+    if (p >= 0) {
+      const int s = p % app.L;
+      if (int(threadIdx.x) < 2 * kChunks) {
+        const int c = threadIdx.x % kChunks;
+        const int copy = threadIdx.x / kChunks;
+        uint8_t* dst = static_cast<uint8_t*>(kv ? app.v_ring : app.k_ring) +
+                       (ring0 + s + size_t(copy) * app.L) * kHeadDim * kEl + c * 16;
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(nrow + c * 16);
+      }
+      if (kv == 0 && threadIdx.x < 2) app.z_ring[ring0 + s + size_t(threadIdx.x) * app.L] = app.z_new[b];
+    }
+    if (kv == 0 && threadIdx.x == 0) app.raw_pos0[b] = pl.base;
+    if (!pl.done) return;                 // the whole block, before any barrier
+    e = pl.entry;
+    row0 = ring0 + pl.first_row;
+    newest = nrow;
+    znew = app.z_new + b;
   } else {
     b = blockIdx.x / n_entries;
     e = blockIdx.x - b * n_entries;
     row0 = size_t(b) * ld_in + size_t(e) * m;
   }
-  const int kv = blockIdx.y;
   const void* src = kv ? v : k;
   const float* z = logits + row0;
+  auto zat = [&](int x) -> float {
+    if constexpr (kAppend) return *(x == m - 1 ? znew : z + x);
+    else return z[x];
+  };
 
   float ak[8];
 #pragma unroll
@@ -95,7 +146,13 @@ __global__ __launch_bounds__(kBlock) void compress_long_kernel(const void* __res
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int r = j + u * kEntriesPerBlock;
-      load_row8<kInF32>(src, row0 + min(r, m - 1), lane_c, kr[u]);
+      const int rc = min(r, m - 1);
+      if constexpr (kAppend) {
+        const bool nw = rc == m - 1;
+        load_row8<kInF32>(nw ? newest : src, nw ? size_t(0) : row0 + rc, lane_c, kr[u]);
+      } else {
+        load_row8<kInF32>(src, row0 + rc, lane_c, kr[u]);
+      }
     }
   };
   float zmax, inv;
@@ -103,7 +160,7 @@ __global__ __launch_bounds__(kBlock) void compress_long_kernel(const void* __res
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int r = j + u * kEntriesPerBlock;
-      const float a = r >= m ? 0.f : (r < kBlock ? wz[r] : expf(z[r] - zmax)) * inv;
+      const float a = r >= m ? 0.f : (r < kBlock ? wz[r] : expf(zat(r) - zmax)) * inv;
 #pragma unroll
       for (int i = 0; i < 8; ++i) ak[i] = fmaf(a, kr[u][i], ak[i]);
     }
@@ -112,12 +169,12 @@ __global__ __launch_bounds__(kBlock) void compress_long_kernel(const void* __res
   // softmax statistics over the block: thread t takes logits t, t + 256, ...;
   // its first logit is requested before the rows, so the statistics wait for
   // the logits only and are done while the rows arrive
-  const float z0 = z[int(threadIdx.x) < m ? int(threadIdx.x) : 0];
+  const float z0 = zat(int(threadIdx.x) < m ? int(threadIdx.x) : 0);
   const float zt = int(threadIdx.x) < m ? z0 : -INFINITY;
   load_batch(grp);   // m >= 32: every group has rows in the first batch
   {
     float zm = zt;
-    for (int x = threadIdx.x + kBlock; x < m; x += kBlock) zm = fmaxf(zm, z[x]);
+    for (int x = threadIdx.x + kBlock; x < m; x += kBlock) zm = fmaxf(zm, zat(x));
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) zm = fmaxf(zm, __shfl_xor(zm, o));
     if (lane == 0) red[0][wv] = zm;
@@ -128,7 +185,7 @@ __global__ __launch_bounds__(kBlock) void compress_long_kernel(const void* __res
     const float et = int(threadIdx.x) < m ? expf(zt - zmax) : 0.f;
     wz[threadIdx.x] = et;
     float zs = et;
-    for (int x = threadIdx.x + kBlock; x < m; x += kBlock) zs += expf(z[x] - zmax);
+    for (int x = threadIdx.x + kBlock; x < m; x += kBlock) zs += expf(zat(x) - zmax);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) zs += __shfl_xor(zs, o);
     if (lane == 0) red[1][wv] = zs;
@@ -180,7 +237,7 @@ hipError_t launch_one(dim3 grid_short, long total, hipStream_t st, const void* k
   (void)grid_short;
   if (m >= 32) {
     hipLaunchKernelGGL((compress_long_kernel<kInF32, kOut, false>), dim3(unsigned(total), 2u), dim3(kBlock), 0, st, k, v,
-                       lg, ne, ld_in, m, ko, vo, ks, vs, ld_out, static_cast<const int32_t*>(nullptr));
+                       lg, ne, ld_in, m, ko, vo, ks, vs, ld_out, AppendArgs{});
   } else {
     // few entries (decoding): 4 per 64-thread block, so their rows are
     // fetched by several CUs; otherwise 16 per 256-thread block
@@ -207,41 +264,31 @@ hipError_t launch_compress(int out_dt, dim3 grid, long total, hipStream_t st, co
 }
 
 template <int kInF32, int kOut>
-hipError_t launch_append_one(const void* k, const void* v, const float* lg, int B, int ld_in, int m, void* ko,
-                             void* vo, float* ks, float* vs, int ld_out, const int32_t* plan, hipStream_t st) {
-  if (m >= 32) {
-    hipLaunchKernelGGL((compress_long_kernel<kInF32, kOut, true>), dim3(unsigned(B), 2u), dim3(kBlock), 0, st, k, v, lg,
-                       B, ld_in, m, ko, vo, ks, vs, ld_out, plan);
+hipError_t launch_cache_append_one(const AppendArgs& a, hipStream_t st) {
+  if (a.m >= 32) {
+    hipLaunchKernelGGL((compress_long_kernel<kInF32, kOut, true>), dim3(unsigned(a.B), 2u), dim3(kBlock), 0, st,
+                       a.k_ring, a.v_ring, a.z_ring, a.B, 2 * a.L, a.m, a.ck, a.cv, a.ck_scale, a.cv_scale, a.cap, a);
   } else {
     constexpr int kPer = 64 / kGroup;    // 4 sequences per 64-thread block
-    hipLaunchKernelGGL((compress_append_kernel<kInF32, kOut>), dim3(unsigned((B + kPer - 1) / kPer)), dim3(64), 0, st,
-                       k, v, lg, B, ld_in, m, ko, vo, ks, vs, ld_out, plan);
+    hipLaunchKernelGGL((cache_append_short_kernel<kInF32, kOut>), dim3(unsigned((a.B + kPer - 1) / kPer)), dim3(64),
+                       0, st, a);
   }
   return hipGetLastError();
 }
 
 template <int kInF32>
-hipError_t launch_append(int out_dt, const void* k, const void* v, const float* lg, int B, int ld_in, int m, void* ko,
-                         void* vo, float* ks, float* vs, int ld_out, const int32_t* plan, hipStream_t st) {
-  switch (out_dt) {
-    case CSA_BF16:
-      return launch_append_one<kInF32, CSA_BF16>(k, v, lg, B, ld_in, m, ko, vo, ks, vs, ld_out, plan, st);
-    case CSA_F32:
-      return launch_append_one<kInF32, CSA_F32>(k, v, lg, B, ld_in, m, ko, vo, ks, vs, ld_out, plan, st);
-    default:
-      return launch_append_one<kInF32, CSA_FP8_E4M3>(k, v, lg, B, ld_in, m, ko, vo, ks, vs, ld_out, plan, st);
+hipError_t launch_cache_append_in(int ckv_dtype, const AppendArgs& a, hipStream_t st) {
+  switch (ckv_dtype) {
+    case CSA_BF16: return launch_cache_append_one<kInF32, CSA_BF16>(a, st);
+    case CSA_F32: return launch_cache_append_one<kInF32, CSA_F32>(a, st);
+    default: return launch_cache_append_one<kInF32, CSA_FP8_E4M3>(a, st);
   }
 }
 
 }  // namespace
 
-hipError_t csa_cmp::launch_compress_append(int in_dtype, int out_dtype, const void* k, const void* v,
-                                           const float* logits, int B, int ld_in, int m, void* k_out, void* v_out,
-                                           float* k_scale, float* v_scale, int ld_out, const int32_t* plan,
-                                           hipStream_t st) {
-  return in_dtype == CSA_F32
-             ? launch_append<1>(out_dtype, k, v, logits, B, ld_in, m, k_out, v_out, k_scale, v_scale, ld_out, plan, st)
-             : launch_append<0>(out_dtype, k, v, logits, B, ld_in, m, k_out, v_out, k_scale, v_scale, ld_out, plan, st);
+hipError_t csa_cmp::launch_cache_append(int io_dtype, int ckv_dtype, const AppendArgs& a, hipStream_t st) {
+  return io_dtype == CSA_F32 ? launch_cache_append_in<1>(ckv_dtype, a, st) : launch_cache_append_in<0>(ckv_dtype, a, st);
 }
 
 extern "C" csa_status_t csa_compress_kv(const void* k, const void* v, int32_t in_dtype, const float* logits,

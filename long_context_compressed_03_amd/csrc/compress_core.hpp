@@ -62,12 +62,37 @@ CSA_DEV void store_entry(void* out, float* scale_out, size_t entry, int lane_c, 
 // The entry pooled from rows [row0, row0 + m) (and their logits) into
 // output slot `entry`, by the 16-lane group whose lane lane_c owns head
 // columns [8 lane_c, 8 lane_c + 8); rows are walked with 4 loads in flight
-// per lane for each of K and V.
-template <int kInF32, int kOut>
+// per lane for each of K and V.  kNewest: the block's last row and logit
+// are read from k_new, v_new, z_new instead (the cache append pools a block
+// whose newest token it is writing in the same launch).
+template <int kInF32, int kOut, bool kNewest = false>
 CSA_DEV void compress_group_at(const void* __restrict__ k, const void* __restrict__ v,
                                const float* __restrict__ logits, size_t row0, int m, void* k_out, void* v_out,
-                               float* k_scale, float* v_scale, size_t entry, int lane_c) {
+                               float* k_scale, float* v_scale, size_t entry, int lane_c,
+                               const void* k_new = nullptr, const void* v_new = nullptr,
+                               const float* z_new = nullptr) {
   const float* z = logits + row0;
+  // row j of the block (address selected, no branch around the load)
+  auto krow = [&](int jj, float* out) {
+    if constexpr (kNewest) {
+      const bool nw = jj == m - 1;
+      load_row8<kInF32>(nw ? k_new : k, nw ? size_t(0) : row0 + jj, lane_c, out);
+    } else {
+      load_row8<kInF32>(k, row0 + jj, lane_c, out);
+    }
+  };
+  auto vrow = [&](int jj, float* out) {
+    if constexpr (kNewest) {
+      const bool nw = jj == m - 1;
+      load_row8<kInF32>(nw ? v_new : v, nw ? size_t(0) : row0 + jj, lane_c, out);
+    } else {
+      load_row8<kInF32>(v, row0 + jj, lane_c, out);
+    }
+  };
+  auto zat = [&](int x) -> float {
+    if constexpr (kNewest) return *(x == m - 1 ? z_new : z + x);
+    else return z[x];
+  };
 
   // softmax statistics of the block's logits, spread over the 16 lanes;
   // computed after the first rows are requested, so the two memory round
@@ -75,10 +100,10 @@ CSA_DEV void compress_group_at(const void* __restrict__ k, const void* __restric
   float zmax = 0.f, inv = 0.f;
   auto stats = [&]() {
     zmax = -INFINITY;
-    for (int x = lane_c; x < m; x += kGroup) zmax = fmaxf(zmax, z[x]);
+    for (int x = lane_c; x < m; x += kGroup) zmax = fmaxf(zmax, zat(x));
     zmax = group_max<kGroup>(zmax);
     float zsum = 0.f;
-    for (int x = lane_c; x < m; x += kGroup) zsum += expf(z[x] - zmax);
+    for (int x = lane_c; x < m; x += kGroup) zsum += expf(zat(x) - zmax);
     zsum = group_sum<kGroup>(zsum);
     inv = 1.f / zsum;
   };
@@ -93,12 +118,12 @@ CSA_DEV void compress_group_at(const void* __restrict__ k, const void* __restric
     float kr[kU][8], vr[kU][8], a[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      load_row8<kInF32>(k, row0 + j + u, lane_c, kr[u]);
-      load_row8<kInF32>(v, row0 + j + u, lane_c, vr[u]);
+      krow(j + u, kr[u]);
+      vrow(j + u, vr[u]);
     }
     if (j == 0) stats();
 #pragma unroll
-    for (int u = 0; u < kU; ++u) a[u] = expf(z[j + u] - zmax) * inv;
+    for (int u = 0; u < kU; ++u) a[u] = expf(zat(j + u) - zmax) * inv;
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
 #pragma unroll
@@ -111,9 +136,9 @@ CSA_DEV void compress_group_at(const void* __restrict__ k, const void* __restric
   if (m < kU) stats();
   for (; j < m; ++j) {
     float kr[8], vr[8];
-    load_row8<kInF32>(k, row0 + j, lane_c, kr);
-    load_row8<kInF32>(v, row0 + j, lane_c, vr);
-    const float a = expf(z[j] - zmax) * inv;
+    krow(j, kr);
+    vrow(j, vr);
+    const float a = expf(zat(j) - zmax) * inv;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       ak[i] = fmaf(a, kr[i], ak[i]);
@@ -135,12 +160,43 @@ CSA_DEV void compress_group(const void* __restrict__ k, const void* __restrict__
                                   size_t(b) * ld_out + e, lane_c);
 }
 
-// Pools, for each sequence b < B with plan[B + b] >= 0, the m rows starting
-// at row plan[b] of its input (rows b * ld_in + plan[b] ...) into entry
-// plan[B + b] of its output; the cache append's second launch.
-hipError_t launch_compress_append(int in_dtype, int out_dtype, const void* k, const void* v, const float* logits,
-                                  int B, int ld_in, int m, void* k_out, void* v_out, float* k_scale, float* v_scale,
-                                  int ld_out, const int32_t* plan, hipStream_t st);
+// One decode token per sequence into the mirrored window ring, and the pool
+// of a block it completes (the cache append; see cache.hip for the layout).
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  const float* z_new;
+  const int32_t* pos;
+  void* k_ring;
+  void* v_ring;
+  float* z_ring;
+  int32_t* raw_pos0;
+  int B, L, m, cap;
+  void* ck;
+  void* cv;
+  float* ck_scale;
+  float* cv_scale;
+};
+
+// Where sequence b's token at p goes and what it completes.
+struct AppendPlan {
+  bool done;       // a block ends at p and its entry is below the capacity
+  int entry;       // (p + 1) / m - 1
+  int first_row;   // ring row of the block's first token: (p - m + 1) mod L
+  int base;        // window base for a query at p
+};
+
+CSA_DEV AppendPlan append_plan(int p, int L, int m, int cap) {
+  AppendPlan a;
+  a.done = p >= 0 && (p + 1) % m == 0 && (p + 1) / m - 1 < cap;
+  a.entry = (p + 1) / m - 1;
+  a.first_row = a.done ? (p - m + 1) % L : 0;
+  const int q0 = max(0, p - L + 1);
+  a.base = p >= 0 ? q0 - q0 % L : 0;
+  return a;
+}
+
+hipError_t launch_cache_append(int io_dtype, int ckv_dtype, const AppendArgs& a, hipStream_t st);
 
 // The arguments of one compression call.
 struct CompressArgs {
