@@ -366,6 +366,27 @@ csa_status_t csa_kv_cache_append(const void* k_new, const void* v_new, const flo
                                  float* ck_scale, float* cv_scale, int32_t* raw_pos0, void* ws,
                                  size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------
+ * csa_mxfp4_quantize_appended -- the MXFP4 indexer key of each entry a
+ * cache append has just completed.
+ *
+ * Passage: as csa_mxfp4_quantize.  For each sequence b whose token at pos[b]
+ * completes a block by the rule of csa_kv_cache_append ((pos + 1) mod m = 0,
+ * entry e = (pos + 1)/m - 1 < cap), vector e of x[b] is converted exactly as
+ * csa_mxfp4_quantize converts it (bit-identical codes and scales) into
+ * codes[b, e] and e8m0[b, e]; nothing else is written.  Together with a
+ * csa_kv_cache_append on a ring of per-token indexer keys with fp32 entries,
+ * this appends the indexer's MXFP4 key cache.
+ *
+ *   x      [B, cap, d] in_dtype (CSA_BF16 or CSA_F32): the pooled keys
+ *   pos    [B] int32 (device), as passed to csa_kv_cache_append
+ *   codes  [B, cap, d/2] uint8;  e8m0 [B, cap, d/32] uint8
+ * Limits: d a positive multiple of 32.
+ * ------------------------------------------------------------------- */
+csa_status_t csa_mxfp4_quantize_appended(const void* x, int32_t in_dtype, const int32_t* pos,
+                                         int32_t B, int32_t cap, int32_t m, int32_t d,
+                                         uint8_t* codes, uint8_t* e8m0, void* stream);
+
 /* Workspace bytes a call needs.  n_keys = k + W (CSA) or cap + W (HCA);
  * for CSA_OP_TOPK and CSA_OP_INDEXER_TOPK pass T_q and n_keys = cap (and, for
  * CSA_OP_INDEXER_TOPK, d = d_I).  Returns 0 when none is needed and

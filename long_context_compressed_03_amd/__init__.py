@@ -29,6 +29,7 @@ DTYPES = {"bf16": CSA_BF16, "f32": CSA_F32, "fp8": CSA_FP8_E4M3}
 EXPORTS = ["csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
            "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn",
            "csa_sparse_attn_batch_invariant", "hca_dense_attn_batch_invariant", "csa_kv_cache_append",
+           "csa_mxfp4_quantize_appended",
            "csa_workspace_size",
            "csa_status_str", "csa_abi_version"]
 
@@ -70,7 +71,8 @@ def load(path=LIB_PATH):
                                      _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
     lib.csa_kv_cache_append.argtypes = [_P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P,
                                         _P, _P, _P, _P, _S, _P]
-    for fn in ["csa_kv_cache_append", "csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
+    lib.csa_mxfp4_quantize_appended.argtypes = [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P]
+    for fn in ["csa_mxfp4_quantize_appended", "csa_kv_cache_append", "csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
                "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn",
                "csa_sparse_attn_batch_invariant", "hca_dense_attn_batch_invariant"]:
         getattr(lib, fn).restype = _I
@@ -341,3 +343,13 @@ def csa_kv_cache_append(k_new, v_new, z_new, pos, k_ring, v_ring, z_ring, m, ck,
                                  _ptr(raw_pos0), _ws_ptr(ws), _ws_len(ws), _stream(stream))
     _check("csa_kv_cache_append", st)
     return raw_pos0
+
+
+def csa_mxfp4_quantize_appended(x, pos, m, codes, e8m0, stream=None):
+    """MXFP4-convert, for each sequence whose token at pos completes a block of m, the
+    entry it completes: x [B, cap, d] (bf16 or f32) into codes [B, cap, d/2] and
+    e8m0 [B, cap, d/32] (uint8), bit-identical to csa_mxfp4_quantize."""
+    B, cap, d = x.shape
+    st = load().csa_mxfp4_quantize_appended(_ptr(x), _dt_of(x), _ptr(pos), B, cap, m, d, _ptr(codes),
+                                            _ptr(e8m0), _stream(stream))
+    _check("csa_mxfp4_quantize_appended", st)

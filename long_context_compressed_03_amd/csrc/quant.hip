@@ -39,6 +39,43 @@ CSA_DEV uint32_t e2m1_magnitude_code(float v) {
 // block's 16).
 constexpr int kIter = 4;
 
+// One lane's 16 input bytes (kE elements of a 32-element block whose kL
+// lanes are adjacent and aligned): the block's shared exponent X (through
+// xor shuffles over the kL lanes) and the lane's kE E2M1 codes, element i in
+// bits [4i, 4i + 4).
+template <int kInF32>
+CSA_DEV uint32_t convert_lane(const u32x4& w, int& X) {
+  constexpr int kL = kInF32 ? 8 : 4;
+  constexpr int kE = 32 / kL;
+  float v[kE];
+  if constexpr (kInF32) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(w[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = __uint_as_float(w[e] << 16);
+      v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < kE; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int o = 1; o < kL; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  // X = floor(log2(amax)) - 2; for fp32 inputs floor(log2(amax)) <= 127, so
+  // X <= 125 and 2^-X is a normal float; a zero block takes X = -127
+  X = amax > 0.f ? max(ilogbf(amax) - 2, -127) : -127;
+  const float inv = __uint_as_float(uint32_t(127 - X) << 23);   // 2^-X, exact
+  uint32_t word = 0u;
+#pragma unroll
+  for (int i = 0; i < kE; ++i) {
+    const uint32_t sign = (__float_as_uint(v[i]) >> 31) << 3;
+    word |= (sign | e2m1_magnitude_code(fabsf(v[i]) * inv)) << (4 * i);
+  }
+  return word;
+}
+
 template <int kInF32>
 __global__ __launch_bounds__(kQThreads) void mxfp4_quantize_kernel(const void* __restrict__ x, long n_blocks,
                                                                    uint8_t* __restrict__ codes,
@@ -58,32 +95,8 @@ __global__ __launch_bounds__(kQThreads) void mxfp4_quantize_kernel(const void* _
     const long gl = gl0 + long(it) * kQThreads;
     const long blk = gl / kL;
     const int part = int(gl % kL);
-    float v[kE];
-    if constexpr (kInF32) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(w[it][e]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[2 * e] = __uint_as_float(w[it][e] << 16);
-        v[2 * e + 1] = __uint_as_float(w[it][e] & 0xFFFF0000u);
-      }
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < kE; ++i) amax = fmaxf(amax, fabsf(v[i]));
-#pragma unroll
-    for (int o = 1; o < kL; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-    // X = floor(log2(amax)) - 2; for fp32 inputs floor(log2(amax)) <= 127, so
-    // X <= 125 and 2^-X is a normal float; a zero block takes X = -127
-    const int X = amax > 0.f ? max(ilogbf(amax) - 2, -127) : -127;
-    const float inv = __uint_as_float(uint32_t(127 - X) << 23);   // 2^-X, exact
-    uint32_t word = 0u;
-#pragma unroll
-    for (int i = 0; i < kE; ++i) {
-      const uint32_t sign = (__float_as_uint(v[i]) >> 31) << 3;
-      word |= (sign | e2m1_magnitude_code(fabsf(v[i]) * inv)) << (4 * i);
-    }
+    int X;
+    const uint32_t word = convert_lane<kInF32>(w[it], X);
     if (blk < n_blocks) {                  // whole groups of kL lanes alike
       uint8_t* out = codes + blk * 16 + part * (kE / 2);
       // streaming stores: the operands are read later, by another kernel
@@ -92,6 +105,37 @@ __global__ __launch_bounds__(kQThreads) void mxfp4_quantize_kernel(const void* _
       if (part == 0) __builtin_nontemporal_store(uint8_t(X + 127), e8m0 + blk);
     }
   }
+}
+
+// The cache append's indexer keys: for each sequence whose token at pos[b]
+// completes a block (the rule of csa_kv_cache_append), vector
+// b * cap + (pos[b] + 1) / m - 1 of x is converted as above; lane mapping as
+// above, a vector's d / 32 blocks in consecutive lanes.
+template <int kInF32>
+__global__ __launch_bounds__(64) void mxfp4_quantize_appended_kernel(const void* __restrict__ x,
+                                                                     const int32_t* __restrict__ pos, int B, int cap,
+                                                                     int m, int d, uint8_t* __restrict__ codes,
+                                                                     uint8_t* __restrict__ e8m0) {
+  constexpr int kL = kInF32 ? 8 : 4;
+  constexpr int kE = 32 / kL;
+  const int per_vec = (d / 32) * kL;       // lanes per vector
+  const long gl = long(blockIdx.x) * 64 + threadIdx.x;
+  const int b = int(min(gl / per_vec, long(B) - 1));
+  const int p = pos[b];
+  const bool done = gl < long(B) * per_vec && p >= 0 && (p + 1) % m == 0 && (p + 1) / m - 1 < cap;
+  const long vec = long(b) * cap + (done ? (p + 1) / m - 1 : 0);
+  const int lane_in_vec = int(gl - long(b) * per_vec);
+  const int lv = done ? lane_in_vec : 0;
+  const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(x) + (vec * per_vec + lv) * 16);
+  int X;
+  const uint32_t word = convert_lane<kInF32>(w, X);   // every lane joins the shuffles
+  if (!done) return;
+  const long blk = vec * (d / 32) + lv / kL;
+  const int part = lv % kL;
+  uint8_t* out = codes + blk * 16 + part * (kE / 2);
+  if constexpr (kE == 8) *reinterpret_cast<uint32_t*>(out) = word;
+  else *reinterpret_cast<uint16_t*>(out) = uint16_t(word);
+  if (part == 0) e8m0[blk] = uint8_t(X + 127);
 }
 
 }  // namespace
@@ -113,5 +157,25 @@ extern "C" csa_status_t csa_mxfp4_quantize(const void* x, int32_t in_dtype, int6
   else
     hipLaunchKernelGGL(mxfp4_quantize_kernel<0>, dim3(unsigned(grid)), dim3(kQThreads), 0, st, x, n_blocks, codes,
                        e8m0);
+  return hipGetLastError() == hipSuccess ? CSA_OK : CSA_EHIP;
+}
+
+extern "C" csa_status_t csa_mxfp4_quantize_appended(const void* x, int32_t in_dtype, const int32_t* pos, int32_t B,
+                                                    int32_t cap, int32_t m, int32_t d, uint8_t* codes,
+                                                    uint8_t* e8m0, void* stream) {
+  if (!x || !pos || !codes || !e8m0) return CSA_EINVAL;
+  if (in_dtype != CSA_BF16 && in_dtype != CSA_F32) return CSA_EINVAL;
+  if (B < 0 || cap < 0 || m < 1 || d <= 0 || d % 32 != 0) return CSA_EINVAL;
+  if (B == 0 || cap == 0) return CSA_OK;
+  const long lanes = long(B) * (d / 32) * (in_dtype == CSA_F32 ? 8 : 4);
+  const long grid = (lanes + 63) / 64;
+  if (grid > 0x7FFFFFFFL || long(B) * cap * (d / 32) > 0x7FFFFFFFFFFFL) return CSA_ENOTSUP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (in_dtype == CSA_F32)
+    hipLaunchKernelGGL(mxfp4_quantize_appended_kernel<1>, dim3(unsigned(grid)), dim3(64), 0, st, x, pos, B, cap, m, d,
+                       codes, e8m0);
+  else
+    hipLaunchKernelGGL(mxfp4_quantize_appended_kernel<0>, dim3(unsigned(grid)), dim3(64), 0, st, x, pos, B, cap, m, d,
+                       codes, e8m0);
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_EHIP;
 }

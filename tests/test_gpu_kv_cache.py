@@ -18,7 +18,7 @@ from csa_synth import attn_inputs, compress_inputs, random_topk_idx
 from gpu_helpers import compress_tolerance, h, h_bf16, say, t_f32, t_i32, t_kv
 from oracle.cache import appended_entries, ring_rows, window_base
 from oracle.compress import compress_values, store
-from oracle.formats import bf16_decode, e4m3_decode
+from oracle.formats import bf16_decode, e4m3_decode, mxfp4_encode
 from oracle.indexer import nvis
 
 pytestmark = pytest.mark.gpu
@@ -165,6 +165,55 @@ def test_cache_append(csa, io, ckv, B, m, L, cap, starts, steps, idle):
                                     ck_scale=cks, cv_scale=cvs)
     torch.cuda.synchronize()
     assert np.array_equal(_bits(o_ring), _bits(o_lin))
+
+
+def test_indexer_key_append(csa):
+    """Per-token indexer keys through a ring with fp32 entries, then the MXFP4 conversion of
+    each new entry: codes and scales of every appended entry equal csa_mxfp4_quantize of the
+    same entries bit for bit (that call is bit-exact against the oracle's encoder), no other
+    entry is written, and they agree with the oracle's chain (fp64 pool, fp32 storage, MXFP4
+    encoding) except where the pool's last-bit rounding decides a code."""
+    B, m, L, cap, steps = 4, 4, 128, 64, 90
+    starts = [0, 4, 40, 100]
+    say(f"indexer key append B={B} m={m} cap={cap} steps={steps}")
+    n_total = max(starts) + steps + 1
+    n_total += (-n_total) % m
+    x = compress_inputs(B, n_total, "bf16", seed=77)
+    K_d, Z_d = t_kv(x["K"], "bf16"), t_f32(x["logits"])
+    ring = torch.zeros((B, 2 * L, 128), dtype=torch.bfloat16, device="cuda")
+    ring_v = torch.zeros_like(ring)
+    ring_z = torch.zeros((B, 2 * L), device="cuda")
+    ent = torch.zeros((B, cap, 128), device="cuda")
+    ent_v = torch.zeros_like(ent)
+    codes = torch.full((B, cap, 64), 0xAB, dtype=torch.uint8, device="cuda")
+    e8 = torch.full((B, cap, 4), 0xAB, dtype=torch.uint8, device="cuda")
+    ar = torch.arange(B, device="cuda")
+    nxt = np.array(starts, np.int64)
+    for _ in range(steps):
+        pos_d = t_i32(nxt.astype(np.int32))
+        src = pos_d.long()
+        k1 = K_d[ar, src].contiguous()
+        csa.csa_kv_cache_append(k1, k1, Z_d[ar, src].contiguous(), pos_d, ring, ring_v, ring_z, m, ent, ent_v)
+        csa.csa_mxfp4_quantize_appended(ent, pos_d, m, codes, e8)
+        nxt += 1
+    torch.cuda.synchronize()
+    ref_c, ref_e = csa.csa_mxfp4_quantize(ent.reshape(B * cap, 128))
+    torch.cuda.synchronize()
+    gc, ge = h(codes), h(e8)
+    rc, re_ = h(ref_c).reshape(B, cap, 64), h(ref_e).reshape(B, cap, 4)
+    Kx = bf16_decode(x["K"])
+    n_rounding = n_codes = 0
+    for b in range(B):
+        e = np.array(appended_entries(int(nxt[b]), m, cap, starts[b]))
+        rest = np.setdiff1d(np.arange(cap), e)
+        assert np.array_equal(gc[b, e], rc[b, e]) and np.array_equal(ge[b, e], re_[b, e]), b
+        assert np.all(gc[b, rest] == 0xAB) and np.all(ge[b, rest] == 0xAB), b
+        rows = (e[:, None] * m + np.arange(m)[None]).reshape(-1)
+        Kh, _ = compress_values(Kx[b, rows][None], Kx[b, rows][None], x["logits"][b, rows][None], m)
+        oc, oe = mxfp4_encode(store(Kh[0], "f32").astype(np.float64))
+        n_codes += oc.size
+        n_rounding += int(np.count_nonzero(oc != gc[b, e])) + 2 * int(np.count_nonzero(oe != ge[b, e]))
+    assert n_rounding <= 2, n_rounding
 
 
 def test_cache_append_rejects_bad_arguments(csa):
