@@ -326,6 +326,42 @@ csa_status_t hca_dense_attn_batch_invariant(
     void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------
+ * csa_sparse_attn_varlen, hca_dense_attn_varlen -- one call over query rows
+ * of any mix of sequences: decode rows and prefill chunks together.
+ *
+ * Passage: the operation is csa_sparse_attn's / hca_dense_attn's.  Query row
+ * r (r < n_rows) belongs to sequence row_seq[r] (in [0, B)) and sits at
+ * position row_pos[r]; its key set is the one those calls give a query of
+ * that sequence at that position.  The split plan is the batch-invariant
+ * one, so row r's bits equal those of the *_batch_invariant call on its own
+ * sequence.
+ *
+ *   q        [n_rows, H, d] io_dtype;  out [n_rows, H, d];  lse [n_rows, H] or NULL
+ *   idx      [n_rows, k] int32 (sparse)
+ *   ck, cv, ck_scale, cv_scale, k_win, v_win, raw_pos0: per sequence, as for
+ *            the plain calls ([B, cap, d], [B, L_raw, d], [B])
+ *   row_seq, row_pos  [n_rows] int32 (device)
+ *   ws       csa_workspace_size(CSA_OP_SPARSE_ATTN_BATCH_INVARIANT resp.
+ *            CSA_OP_DENSE_ATTN_BATCH_INVARIANT, n_rows, 1, H, d, n_keys)
+ * Limits as for the plain calls.  Preconditions: row_seq[r] in [0, B);
+ * row_pos[r] >= 0.
+ * ------------------------------------------------------------------- */
+csa_status_t csa_sparse_attn_varlen(const void* q, int32_t io_dtype, const void* ck, const void* cv,
+                                    const float* ck_scale, const float* cv_scale, int32_t ckv_dtype,
+                                    int32_t cap, const int32_t* idx, int32_t k, const void* k_win,
+                                    const void* v_win, const int32_t* raw_pos0, int32_t L_raw,
+                                    const int32_t* row_seq, const int32_t* row_pos, int32_t n_rows,
+                                    int32_t W, int32_t B, int32_t H, int32_t d, float sm_scale,
+                                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+csa_status_t hca_dense_attn_varlen(const void* q, int32_t io_dtype, const void* ck, const void* cv,
+                                   const float* ck_scale, const float* cv_scale, int32_t ckv_dtype,
+                                   int32_t cap, int32_t m_prime, const void* k_win, const void* v_win,
+                                   const int32_t* raw_pos0, int32_t L_raw, const int32_t* row_seq,
+                                   const int32_t* row_pos, int32_t n_rows, int32_t W, int32_t B,
+                                   int32_t H, int32_t d, float sm_scale, void* out, float* lse,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
  * csa_kv_cache_append -- one decode step's token into a layer's KV cache.
  *
  * Passage: the newest uncompressed tokens are kept in bf16 beside compressed

@@ -29,7 +29,7 @@ DTYPES = {"bf16": CSA_BF16, "f32": CSA_F32, "fp8": CSA_FP8_E4M3}
 EXPORTS = ["csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
            "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn",
            "csa_sparse_attn_batch_invariant", "hca_dense_attn_batch_invariant", "csa_kv_cache_append",
-           "csa_mxfp4_quantize_appended",
+           "csa_mxfp4_quantize_appended", "csa_sparse_attn_varlen", "hca_dense_attn_varlen",
            "csa_workspace_size",
            "csa_status_str", "csa_abi_version"]
 
@@ -72,7 +72,11 @@ def load(path=LIB_PATH):
     lib.csa_kv_cache_append.argtypes = [_P, _P, _P, _I, _P, _I, _I, _I, _P, _P, _P, _I, _I, _I, _P, _P,
                                         _P, _P, _P, _P, _S, _P]
     lib.csa_mxfp4_quantize_appended.argtypes = [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P]
-    for fn in ["csa_mxfp4_quantize_appended", "csa_kv_cache_append", "csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
+    lib.csa_sparse_attn_varlen.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P,
+                                           _I, _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
+    lib.hca_dense_attn_varlen.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _P, _P,
+                                          _I, _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
+    for fn in ["csa_sparse_attn_varlen", "hca_dense_attn_varlen", "csa_mxfp4_quantize_appended", "csa_kv_cache_append", "csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
                "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn",
                "csa_sparse_attn_batch_invariant", "hca_dense_attn_batch_invariant"]:
         getattr(lib, fn).restype = _I
@@ -353,3 +357,38 @@ def csa_mxfp4_quantize_appended(x, pos, m, codes, e8m0, stream=None):
     st = load().csa_mxfp4_quantize_appended(_ptr(x), _dt_of(x), _ptr(pos), B, cap, m, d, _ptr(codes),
                                             _ptr(e8m0), _stream(stream))
     _check("csa_mxfp4_quantize_appended", st)
+
+
+def _varlen(name, op, q, ck, cv, mid, n_keys, k_win, v_win, raw_pos0, row_seq, row_pos, W, ck_scale,
+            cv_scale, sm_scale, out, lse, stream):
+    n_rows, H, d = q.shape
+    B, cap = ck.shape[0], ck.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    sm = d ** -0.5 if sm_scale is None else sm_scale
+    lib = load()
+    ws = _workspace(q.device, lib.csa_workspace_size(op, n_rows, 1, H, d, n_keys))
+    st = getattr(lib, name)(_ptr(q), _dt_of(q), _ptr(ck), _ptr(cv), _ptr(ck_scale), _ptr(cv_scale),
+                            _dt_of(ck), cap, *mid, _ptr(k_win), _ptr(v_win), _ptr(raw_pos0),
+                            k_win.shape[1], _ptr(row_seq), _ptr(row_pos), n_rows, W, B, H, d, sm,
+                            _ptr(out), _ptr(lse), _ws_ptr(ws), _ws_len(ws), _stream(stream))
+    _check(name, st)
+    return out
+
+
+def csa_sparse_attn_varlen(q, ck, cv, idx, k_win, v_win, raw_pos0, row_seq, row_pos, W, ck_scale=None,
+                           cv_scale=None, sm_scale=None, out=None, lse=None, stream=None):
+    """CSA attention over query rows of mixed sequences: q [n_rows, H, d], idx [n_rows, k];
+    row r belongs to sequence row_seq[r] at position row_pos[r]."""
+    k = idx.shape[-1]
+    return _varlen("csa_sparse_attn_varlen", CSA_OP_SPARSE_ATTN_BATCH_INVARIANT, q, ck, cv,
+                   (_ptr(idx), k), k + W, k_win, v_win, raw_pos0, row_seq, row_pos, W, ck_scale,
+                   cv_scale, sm_scale, out, lse, stream)
+
+
+def hca_dense_attn_varlen(q, ck, cv, m_prime, k_win, v_win, raw_pos0, row_seq, row_pos, W, ck_scale=None,
+                          cv_scale=None, sm_scale=None, out=None, lse=None, stream=None):
+    """HCA attention over query rows of mixed sequences (as csa_sparse_attn_varlen)."""
+    return _varlen("hca_dense_attn_varlen", CSA_OP_DENSE_ATTN_BATCH_INVARIANT, q, ck, cv, (m_prime,),
+                   ck.shape[1] + W, k_win, v_win, raw_pos0, row_seq, row_pos, W, ck_scale, cv_scale,
+                   sm_scale, out, lse, stream)

@@ -73,6 +73,8 @@ struct AttnArgs {
   const void* v_win;
   const int32_t* raw_pos0;
   const int32_t* q_pos0;
+  const int32_t* row_seq;  // varlen: sequence of each query row (else null: row / T_q)
+  const int32_t* row_pos;  // varlen: position of each query row
   void* out;
   float* lse;
   float* part_ml;          // [rows, n_splits, H, 2]: running max (log2 domain), sum
@@ -180,11 +182,11 @@ CSA_DEV int item_dg() { return int(threadIdx.x) & 15; }
 // The load is unconditional (position clamped into the list; slots past the
 // list or the split are never used), for the same reason as gather_slot.
 template <bool kDense>
-CSA_DEV void load_idx(const AttnArgs& a, int (&e)[2], int b, int i, int jc, int j_end) {
+CSA_DEV void load_idx(const AttnArgs& a, int (&e)[2], long qrow, int jc, int j_end) {
   e[0] = e[1] = -1;
   if constexpr (!kDense) {
     const int kp = item_kp();
-    const int32_t* ip = a.idx + (long(b) * a.T_q + i) * a.k;
+    const int32_t* ip = a.idx + qrow * a.k;
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int j = jc + 2 * kp + x;
@@ -384,9 +386,14 @@ void attn_kernel(AttnArgs a) {
 
   const long qrow = blockIdx.x / a.n_splits;
   const int split = int(blockIdx.x - qrow * a.n_splits);
-  const int b = int(qrow / a.T_q);
-  const int i = int(qrow - long(b) * a.T_q);
-  const int t = a.q_pos0[b] + i;
+  int b, t;
+  if (a.row_seq) {                         // varlen rows
+    b = a.row_seq[qrow];
+    t = a.row_pos[qrow];
+  } else {
+    b = int(qrow / a.T_q);
+    t = a.q_pos0[b] + int(qrow - long(b) * a.T_q);
+  }
   const int raw0 = a.W > 0 ? a.raw_pos0[b] : 0;
   const int n_tiles = a.H / 16;
   const int j_begin = split * a.split_len;
@@ -501,11 +508,11 @@ void attn_kernel(AttnArgs a) {
   Pre<kIO> pr[kDepth];
   int e_nx[kDepth][2];
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) load_idx<kDense>(a, e_nx[d], b, i, j_begin + d * kNK, j_end);
+  for (int d = 0; d < kDepth; ++d) load_idx<kDense>(a, e_nx[d], qrow, j_begin + d * kNK, j_end);
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) {
     prefetch<kIO, kCKV, kDense>(a, pr[d], e_nx[d], b, t, raw0, j_begin + d * kNK, j_end);
-    load_idx<kDense>(a, e_nx[d], b, i, j_begin + (d + kDepth) * kNK, j_end);
+    load_idx<kDense>(a, e_nx[d], qrow, j_begin + (d + kDepth) * kNK, j_end);
   }
   for (int j0 = j_begin; j0 < j_end; j0 += kDepth * kNK) {
 #pragma unroll
@@ -515,7 +522,7 @@ void attn_kernel(AttnArgs a) {
       store_chunk<kIO, kCKV>(s, pr[d], a.sm_log2);
       __syncthreads();
       prefetch<kIO, kCKV, kDense>(a, pr[d], e_nx[d], b, t, raw0, j0 + (d + kDepth) * kNK, j_end);
-      load_idx<kDense>(a, e_nx[d], b, i, j0 + (d + 2 * kDepth) * kNK, j_end);
+      load_idx<kDense>(a, e_nx[d], qrow, j0 + (d + 2 * kDepth) * kNK, j_end);
       compute();
     }
   }
@@ -1046,7 +1053,63 @@ csa_status_t dense_attn_impl(const void* q, int32_t io_dtype, const void* ck, co
   return run_attn<true>(a, io_dtype, ckv_dtype, B, ws, ws_bytes, static_cast<hipStream_t>(stream), invariant);
 }
 
+// Varlen: n_rows query rows of any mix of sequences (decode rows and prefill
+// chunks together), row r of sequence row_seq[r] at position row_pos[r];
+// the batch-invariant plan, so each row's bits equal those of the
+// *_batch_invariant calls on its own sequence.
+csa_status_t varlen_attn(AttnArgs a, bool dense, int io_dtype, int ckv_dtype, const int32_t* row_seq,
+                         const int32_t* row_pos, int n_rows, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (n_rows > 0 && (!row_seq || !row_pos)) return CSA_EINVAL;
+  a.row_seq = row_seq;
+  a.row_pos = row_pos;
+  a.T_q = 1;
+  return dense ? run_attn<true>(a, io_dtype, ckv_dtype, n_rows, ws, ws_bytes, st, true)
+               : run_attn<false>(a, io_dtype, ckv_dtype, n_rows, ws, ws_bytes, st, true);
+}
+
 }  // namespace
+
+extern "C" csa_status_t csa_sparse_attn_varlen(const void* q, int32_t io_dtype, const void* ck, const void* cv,
+                                               const float* ck_scale, const float* cv_scale, int32_t ckv_dtype,
+                                               int32_t cap, const int32_t* idx, int32_t k, const void* k_win,
+                                               const void* v_win, const int32_t* raw_pos0, int32_t L_raw,
+                                               const int32_t* row_seq, const int32_t* row_pos, int32_t n_rows,
+                                               int32_t W, int32_t B, int32_t H, int32_t d, float sm_scale, void* out,
+                                               float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (n_rows < 0 || B < 0) return CSA_EINVAL;
+  csa_status_t c = check_common(q, io_dtype, ck, cv, ck_scale, cv_scale, ckv_dtype, cap, k_win, v_win, raw_pos0, L_raw,
+                                row_pos ? row_pos : reinterpret_cast<const int32_t*>(q), W, n_rows, 1, H, d, out);
+  if (c != CSA_OK) return c;
+  if (!idx || k < 1) return CSA_EINVAL;
+  AttnArgs a{};
+  a.q = q; a.ck = ck; a.cv = cv; a.ck_scale = ck_scale; a.cv_scale = cv_scale; a.cap = cap;
+  a.idx = idx; a.k = k; a.k_win = k_win; a.v_win = v_win; a.raw_pos0 = raw_pos0; a.L_raw = L_raw;
+  a.W = W; a.H = H; a.sm_log2 = sm_scale * kLog2e; a.out = out; a.lse = lse;
+  a.n_list = k + W;
+  return varlen_attn(a, false, io_dtype, ckv_dtype, row_seq, row_pos, n_rows, ws, ws_bytes,
+                     static_cast<hipStream_t>(stream));
+}
+
+extern "C" csa_status_t hca_dense_attn_varlen(const void* q, int32_t io_dtype, const void* ck, const void* cv,
+                                              const float* ck_scale, const float* cv_scale, int32_t ckv_dtype,
+                                              int32_t cap, int32_t m_prime, const void* k_win, const void* v_win,
+                                              const int32_t* raw_pos0, int32_t L_raw, const int32_t* row_seq,
+                                              const int32_t* row_pos, int32_t n_rows, int32_t W, int32_t B, int32_t H,
+                                              int32_t d, float sm_scale, void* out, float* lse, void* ws,
+                                              size_t ws_bytes, void* stream) {
+  if (n_rows < 0 || B < 0) return CSA_EINVAL;
+  csa_status_t c = check_common(q, io_dtype, ck, cv, ck_scale, cv_scale, ckv_dtype, cap, k_win, v_win, raw_pos0, L_raw,
+                                row_pos ? row_pos : reinterpret_cast<const int32_t*>(q), W, n_rows, 1, H, d, out);
+  if (c != CSA_OK) return c;
+  if (m_prime < 1) return CSA_EINVAL;
+  AttnArgs a{};
+  a.q = q; a.ck = ck; a.cv = cv; a.ck_scale = ck_scale; a.cv_scale = cv_scale; a.cap = cap;
+  a.idx = nullptr; a.k = m_prime; a.k_win = k_win; a.v_win = v_win; a.raw_pos0 = raw_pos0; a.L_raw = L_raw;
+  a.W = W; a.H = H; a.sm_log2 = sm_scale * kLog2e; a.out = out; a.lse = lse;
+  a.n_list = cap + W;
+  return varlen_attn(a, true, io_dtype, ckv_dtype, row_seq, row_pos, n_rows, ws, ws_bytes,
+                     static_cast<hipStream_t>(stream));
+}
 
 #define CSA_SPARSE_ARGS                                                                                          \
   const void *q, int32_t io_dtype, const void *ck, const void *cv, const float *ck_scale, const float *cv_scale, \

@@ -174,3 +174,53 @@ def test_long_list_and_plain_call_agree(csa):
                                                  cv_scale=cvs[sl])
         torch.cuda.synchronize()
         assert np.array_equal(_bits(o1), _bits(out_bi[sl])), r
+
+
+@pytest.mark.parametrize("dense", [False, True])
+def test_varlen_mixed_decode_and_prefill(csa, dense):
+    """Four decode rows (sequences 0-3) and a 200-query prefill chunk (sequence 4) in one
+    varlen call: each part's rows equal, bit for bit, the batch-invariant call on its own
+    sequences, and the oracle within the attention tolerance."""
+    io, ckv, H, cap, W, T, k, m, mp = "bf16", "fp8", 64, 800, 64, 200, 256, 4, 16
+    say(f"varlen mixed step dense={dense}: 4 decode rows + {T}-query chunk")
+    dec_pos = np.array([3199, 2000, 1500, 3100], np.int32)
+    c_pos0 = 2500
+    L_raw = T + W
+    pos0 = np.concatenate([dec_pos, [c_pos0]]).astype(np.int32)
+    last = np.concatenate([dec_pos, [c_pos0 + T - 1]])
+    raw0 = (last + 1 - L_raw).astype(np.int32)
+    x = attn_inputs(5, T, H, cap, L_raw, io, ckv, seed=123)
+    q, ck, cv, cks, cvs, kw, vw = _dev(x, io, ckv)
+    rows_pos = np.concatenate([dec_pos, c_pos0 + np.arange(T)]).astype(np.int32)
+    rows_seq = np.concatenate([np.arange(4), np.full(T, 4)]).astype(np.int32)
+    qv = torch.cat([q[0:4, 0], q[4, :T]]).contiguous()
+    lse_v = torch.empty((4 + T, H), device="cuda")
+    oq, oK, oV, oKw, oVw = _oracle_inputs(x, io, ckv)
+    if dense:
+        out_v = csa.hca_dense_attn_varlen(qv, ck, cv, mp, kw, vw, t_i32(raw0), t_i32(rows_seq), t_i32(rows_pos),
+                                          W, ck_scale=cks, cv_scale=cvs, lse=lse_v)
+    else:
+        idx_dec = random_topk_idx(np.minimum(nvis(dec_pos[:, None], m), cap), k, cap, seed=1)      # [4, 1, k]
+        idx_c = random_topk_idx(np.minimum(nvis(c_pos0 + np.arange(T)[None], m), cap), k, cap, seed=2)  # [1, T, k]
+        idx_v = np.ascontiguousarray(np.concatenate([idx_dec[:, 0], idx_c[0]]))
+        out_v = csa.csa_sparse_attn_varlen(qv, ck, cv, t_i32(idx_v), kw, vw, t_i32(raw0), t_i32(rows_seq),
+                                           t_i32(rows_pos), W, ck_scale=cks, cv_scale=cvs, lse=lse_v)
+    parts = [(slice(0, 4), slice(0, 1), slice(0, 4)), (slice(4, 5), slice(0, T), slice(4, 4 + T))]
+    for pi, (sb, st_, sr) in enumerate(parts):
+        lse_p = torch.empty((sb.stop - sb.start, st_.stop, H), device="cuda")
+        qq = q[sb, st_].contiguous()
+        kwargs = dict(ck_scale=cks[sb], cv_scale=cvs[sb], lse=lse_p)
+        if dense:
+            out_p = csa.hca_dense_attn_batch_invariant(qq, ck[sb], cv[sb], mp, kw[sb], vw[sb], t_i32(raw0[sb]),
+                                                       t_i32(pos0[sb]), W, **kwargs)
+            O, lse = dense_attn(oq[sb, st_], oK[sb], oV[sb], mp, oKw[sb], oVw[sb], raw0[sb], pos0[sb], W)
+        else:
+            ip = idx_dec if pi == 0 else idx_c
+            out_p = csa.csa_sparse_attn_batch_invariant(qq, ck[sb], cv[sb], t_i32(ip), kw[sb], vw[sb],
+                                                        t_i32(raw0[sb]), t_i32(pos0[sb]), W, **kwargs)
+            O, lse = sparse_attn(oq[sb, st_], oK[sb], oV[sb], ip, oKw[sb], oVw[sb], raw0[sb], pos0[sb], W)
+        torch.cuda.synchronize()
+        got = out_v[sr].reshape(out_p.shape)
+        assert np.array_equal(_bits(got), _bits(out_p)), pi
+        assert np.array_equal(_bits(lse_v[sr].reshape(lse_p.shape)), _bits(lse_p)), pi
+        _check_oracle(got, lse_v[sr].reshape(lse_p.shape), O, lse, io)
