@@ -370,7 +370,8 @@ CSA_DEV void store_out4(void* out, long orow, int d4, v4f v) {
 // kDepth > 1 (split key lists, at most about one block per CU): that many
 // chunks in flight instead of one, with the register budget of two waves per
 // SIMD.
-template <int kIO, int kCKV, bool kDense, int kHTW, int kDepth>
+// kVarlen: query rows are mapped through row_seq / row_pos (the varlen calls).
+template <int kIO, int kCKV, bool kDense, int kHTW, int kDepth, bool kVarlen>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kIO == CSA_BF16 && kHTW == 1 ? (kDepth > 1 ? 2 : 4) : 1)))
 void attn_kernel(AttnArgs a) {
@@ -387,7 +388,7 @@ void attn_kernel(AttnArgs a) {
   const long qrow = blockIdx.x / a.n_splits;
   const int split = int(blockIdx.x - qrow * a.n_splits);
   int b, t;
-  if (a.row_seq) {                         // varlen rows
+  if constexpr (kVarlen) {
     b = a.row_seq[qrow];
     t = a.row_pos[qrow];
   } else {
@@ -892,11 +893,11 @@ size_t plan_ws_bytes(const Plan& p, long rows, int H) {
   return ml + slots * kHeadDim * 4;
 }
 
-template <int kIO, int kCKV, bool kDense, int kHTW, int kDepth>
+template <int kIO, int kCKV, bool kDense, int kHTW, int kDepth, bool kVarlen>
 hipError_t launch_attn(const AttnArgs& a, long blocks, hipStream_t st) {
   static bool attr = false;   // per instantiation; dynamic LDS above 64 KB needs the opt-in
   constexpr size_t bytes = lds_bytes<kIO, kHTW>();
-  auto fn = attn_kernel<kIO, kCKV, kDense, kHTW, kDepth>;
+  auto fn = attn_kernel<kIO, kCKV, kDense, kHTW, kDepth, kVarlen>;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        int(bytes));
@@ -943,18 +944,29 @@ bool use_mq(int io_dtype, int H, int T_q, const Plan& p) {
   return io_dtype == CSA_BF16 && (H == 32 || H == 64 || H == 128) && T_q >= 64 && p.n_splits == 1;
 }
 
-template <int kIO, int kCKV, bool kDense>
+template <int kIO, int kCKV, bool kDense, bool kVarlen>
 hipError_t launch_tiles(const AttnArgs& a, long blocks, hipStream_t st) {
   // split key lists of more than two chunks take the two-chunk pipeline
   // (fp32 queries over more than 64 heads would not fit its registers); with
   // two chunks the one-ahead prefetch already overlaps the second, and more
   // chunks in flight only delay the first (a CU's loads in flight are few)
   if (a.n_splits > 1 && a.split_len > 2 * kNK) {
-    if (a.H <= 64) return launch_attn<kIO, kCKV, kDense, 1, 2>(a, blocks, st);
-    if constexpr (kIO == CSA_BF16) return launch_attn<kIO, kCKV, kDense, 2, 2>(a, blocks, st);
+    if (a.H <= 64) return launch_attn<kIO, kCKV, kDense, 1, 2, kVarlen>(a, blocks, st);
+    if constexpr (kIO == CSA_BF16) return launch_attn<kIO, kCKV, kDense, 2, 2, kVarlen>(a, blocks, st);
   }
-  return a.H <= 64 ? launch_attn<kIO, kCKV, kDense, 1, 1>(a, blocks, st)
-                   : launch_attn<kIO, kCKV, kDense, 2, 1>(a, blocks, st);
+  return a.H <= 64 ? launch_attn<kIO, kCKV, kDense, 1, 1, kVarlen>(a, blocks, st)
+                   : launch_attn<kIO, kCKV, kDense, 2, 1, kVarlen>(a, blocks, st);
+}
+
+template <bool kDense, bool kVarlen>
+csa_status_t tiles_for(const AttnArgs& a, int io_dtype, int ckv_dtype, long blocks, hipStream_t st) {
+  hipError_t err;
+  if (io_dtype == CSA_BF16 && ckv_dtype == CSA_BF16) err = launch_tiles<CSA_BF16, CSA_BF16, kDense, kVarlen>(a, blocks, st);
+  else if (io_dtype == CSA_BF16 && ckv_dtype == CSA_FP8_E4M3) err = launch_tiles<CSA_BF16, CSA_FP8_E4M3, kDense, kVarlen>(a, blocks, st);
+  else if (io_dtype == CSA_F32 && ckv_dtype == CSA_F32) err = launch_tiles<CSA_F32, CSA_F32, kDense, kVarlen>(a, blocks, st);
+  else if (io_dtype == CSA_F32 && ckv_dtype == CSA_FP8_E4M3) err = launch_tiles<CSA_F32, CSA_FP8_E4M3, kDense, kVarlen>(a, blocks, st);
+  else return CSA_ENOTSUP;
+  return err == hipSuccess ? CSA_OK : CSA_EHIP;
 }
 
 template <bool kDense>
@@ -981,12 +993,8 @@ csa_status_t run_attn(AttnArgs a, int io_dtype, int ckv_dtype, int B, void* ws, 
     err = ckv_dtype == CSA_BF16 ? launch_mq<CSA_BF16>(a, B, st) : launch_mq<CSA_FP8_E4M3>(a, B, st);
     return err == hipSuccess ? CSA_OK : CSA_EHIP;
   }
-  if (io_dtype == CSA_BF16 && ckv_dtype == CSA_BF16) err = launch_tiles<CSA_BF16, CSA_BF16, kDense>(a, p.blocks, st);
-  else if (io_dtype == CSA_BF16 && ckv_dtype == CSA_FP8_E4M3) err = launch_tiles<CSA_BF16, CSA_FP8_E4M3, kDense>(a, p.blocks, st);
-  else if (io_dtype == CSA_F32 && ckv_dtype == CSA_F32) err = launch_tiles<CSA_F32, CSA_F32, kDense>(a, p.blocks, st);
-  else if (io_dtype == CSA_F32 && ckv_dtype == CSA_FP8_E4M3) err = launch_tiles<CSA_F32, CSA_FP8_E4M3, kDense>(a, p.blocks, st);
-  else return CSA_ENOTSUP;
-  return err == hipSuccess ? CSA_OK : CSA_EHIP;
+  return a.row_seq ? tiles_for<kDense, true>(a, io_dtype, ckv_dtype, p.blocks, st)
+                   : tiles_for<kDense, false>(a, io_dtype, ckv_dtype, p.blocks, st);
 }
 
 csa_status_t check_common(const void* q, int io_dtype, const void* ck, const void* cv, const float* ck_scale,
