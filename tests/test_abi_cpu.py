@@ -216,6 +216,45 @@ def test_batch_invariant_attention_plan():
                                               None, 0, None) == csa.CSA_EINVAL  # m_prime < 1
 
 
+def test_cache_varlen_and_appended_quantize_reject_bad_arguments():
+    import long_context_compressed_03_amd as csa
+    lib = csa.load()
+
+    def append(d=128, L=8, m=4, io=0, ckv=0, scales=None, k_new=_p(), raw=_p()):
+        return lib.csa_kv_cache_append(k_new, _p(), _p(), io, _p(), 2, d, L, _p(), _p(), _p(), m, 16, ckv,
+                                       _p(), _p(), scales, scales, raw, None, 0, None)
+    assert append(d=64) == csa.CSA_EINVAL
+    assert append(m=16) == csa.CSA_EINVAL             # the block is longer than the ring
+    assert append(io=2) == csa.CSA_EINVAL             # the ring holds bf16 or fp32 rows
+    assert append(ckv=2) == csa.CSA_EINVAL            # fp8 entries without scales
+    assert append(k_new=None) == csa.CSA_EINVAL
+    assert append(raw=None) == csa.CSA_EINVAL
+    assert lib.csa_workspace_size(csa.CSA_OP_KV_CACHE_APPEND, 4, 0, 0, 0, 0) == 0
+
+    def quant(dt=0, d=128, m=4, pos=_p()):
+        return lib.csa_mxfp4_quantize_appended(_p(), dt, pos, 2, 16, m, d, _p(), _p(), None)
+    assert quant(dt=2) == csa.CSA_EINVAL
+    assert quant(d=100) == csa.CSA_EINVAL
+    assert quant(m=0) == csa.CSA_EINVAL
+    assert quant(pos=None) == csa.CSA_EINVAL
+
+    def sparse_vl(H=64, k=64, row_seq=_p(), row_pos=_p(), n_rows=3, ws=None, nws=0):
+        return lib.csa_sparse_attn_varlen(_p(), 0, _p(), _p(), None, None, 0, 16, _p(), k, _p(), _p(), _p(), 8,
+                                          row_seq, row_pos, n_rows, 4, 2, H, 128, 0.1, _p(), None, ws, nws, None)
+    assert sparse_vl(H=24) == csa.CSA_ENOTSUP
+    assert sparse_vl(k=0) == csa.CSA_EINVAL
+    assert sparse_vl(row_seq=None) == csa.CSA_EINVAL
+    assert sparse_vl(row_pos=None) == csa.CSA_EINVAL
+    assert sparse_vl(n_rows=-1) == csa.CSA_EINVAL
+    # a 1024 + 128 key list is cut into pieces: the workspace is mandatory
+    need = lib.csa_workspace_size(csa.CSA_OP_SPARSE_ATTN_BATCH_INVARIANT, 3, 1, 64, 128, 1024 + 4)
+    assert need > 0
+    assert sparse_vl(k=1024) == csa.CSA_EWORKSPACE
+    assert sparse_vl(k=1024, ws=_p(), nws=need - 1) == csa.CSA_EWORKSPACE
+    assert lib.hca_dense_attn_varlen(_p(), 0, _p(), _p(), None, None, 0, 16, 0, _p(), _p(), _p(), 8, _p(), _p(),
+                                     3, 4, 2, 64, 128, 0.1, _p(), None, None, 0, None) == csa.CSA_EINVAL
+
+
 def test_binding_fails_loudly_without_gpu_tensors():
     import torch
     import long_context_compressed_03_amd as csa
