@@ -305,14 +305,17 @@ APPEND_SHAPE = dict(B=16, L=128, m=4, cap=32768, pos=131071)
 
 
 def build_append(args):
-    """One decode step's KV cache append for the 128K decode shape: 16 sequences, each
-    appending its token at position 131071 (which completes a block of m = 4, so the
-    block is pooled into fp8 entry 32767) to a 128-token bf16 window ring."""
+    """One decode step's cache append for a CSA layer of the 128K decode shape: 16 sequences,
+    each appending its token at position 131071, which completes a block of m = 4.  The K/V
+    token goes to a 128-token bf16 window ring and the block is pooled into fp8 entry 32767;
+    the token's indexer key goes to its own ring, is pooled into an fp32 entry, and that entry
+    is converted to the indexer's MXFP4 key cache."""
     import torch
     from csa_synth import compress_inputs
     import long_context_compressed_03_amd as csa
     B, L, m, cap, p = (APPEND_SHAPE[k] for k in ("B", "L", "m", "cap", "pos"))
     x = compress_inputs(B, 2 * L + 1, "bf16", seed=17)
+    xi = compress_inputs(B, 2 * L + 1, "bf16", seed=18)      # indexer keys
     st = Step(APPEND_WORKLOAD, B)
     # per sequence: the new K/V rows and logit read; 2 copies of each written; the block's
     # m K/V rows and logits read back; the fp8 entries and scales written; pos, plan, base
@@ -322,9 +325,24 @@ def build_append(args):
         csa.csa_kv_cache_append(c["k_new"], c["v_new"], c["z_new"], c["pos"], c["rk"], c["rv"], c["rz"], m,
                                 c["ck"], c["cv"], ck_scale=c["cks"], cv_scale=c["cvs"], raw_pos0=c["raw0"])
     st.add(Kernel("kv_cache_append", f_append, nbytes, 0, BF16_PEAK_TFLOPS, "kv_cache_append"))
+
+    def f_append_ix(c):
+        csa.csa_kv_cache_append(c["ik_new"], c["iv_new"], c["z_new"], c["pos"], c["irk"], c["irv"], c["rz_i"], m,
+                                c["ik"], c["iv"], raw_pos0=c["raw0_i"])
+    # as above with fp32 entries: 2 x (512 + 4) B written per sequence for the entries
+    nbytes_ix = B * (2 * 256 + 4 + 2 * (2 * 256 + 4) + m * (2 * 256 + 4) + 2 * 512 + 4 + 4)
+    st.add(Kernel("kv_cache_append_indexer", f_append_ix, nbytes_ix, 0, BF16_PEAK_TFLOPS,
+                  "kv_cache_append_indexer"))
+
+    def f_quant_ix(c):
+        csa.csa_mxfp4_quantize_appended(c["ik"], c["pos"], m, c["kc"], c["ke"])
+    # per sequence: pos, the fp32 entry read, 64 + 4 B written
+    st.add(Kernel("mxfp4_quantize_appended", f_quant_ix, B * (4 + 512 + 68), 0, BF16_PEAK_TFLOPS,
+                  "mxfp4_quantize_appended"))
     K = torch.from_numpy(x["K"].view(np.int16)).view(torch.bfloat16).cuda()
     V = torch.from_numpy(x["V"].view(np.int16)).view(torch.bfloat16).cuda()
     Z = torch.from_numpy(x["logits"]).cuda()
+    Vx = torch.from_numpy(xi["K"].view(np.int16)).view(torch.bfloat16).cuda()
     base = {"rk": K[:, :2 * L].contiguous(), "rv": V[:, :2 * L].contiguous(), "rz": Z[:, :2 * L].contiguous(),
             "k_new": K[:, 2 * L].contiguous(), "v_new": V[:, 2 * L].contiguous(),
             "z_new": Z[:, 2 * L].contiguous(),
@@ -332,13 +350,23 @@ def build_append(args):
             "ck": torch.zeros((B, cap, 128), dtype=torch.uint8, device="cuda"),
             "cv": torch.zeros((B, cap, 128), dtype=torch.uint8, device="cuda"),
             "cks": torch.zeros((B, cap), device="cuda"), "cvs": torch.zeros((B, cap), device="cuda"),
-            "raw0": torch.empty((B,), dtype=torch.int32, device="cuda")}
+            "raw0": torch.empty((B,), dtype=torch.int32, device="cuda"),
+            # the indexer keys' ring (d_I = 128; the V side of the append carries the same rows)
+            "irk": Vx[:, :2 * L].contiguous(), "irv": Vx[:, :2 * L].contiguous(),
+            "rz_i": Z[:, :2 * L].contiguous(),
+            "ik_new": Vx[:, 2 * L].contiguous(), "iv_new": Vx[:, 2 * L].contiguous(),
+            "ik": torch.zeros((B, cap, 128), device="cuda"), "iv": torch.zeros((B, cap, 128), device="cuda"),
+            "kc": torch.zeros((B, cap, 64), dtype=torch.uint8, device="cuda"),
+            "ke": torch.zeros((B, cap, 4), dtype=torch.uint8, device="cuda"),
+            "raw0_i": torch.empty((B,), dtype=torch.int32, device="cuda")}
     R = args.rotate or 4
     st.copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
-    st.layers = [("", {"append_sample": {k: x[k][:, :2 * L + 1] for k in ("K", "V", "logits")}})]
+    st.layers = [("", {"append_sample": {k: x[k][:, :2 * L + 1] for k in ("K", "V", "logits")},
+                        "append_sample_ix": xi["K"][:, :2 * L + 1]})]
     st.config = {"workload": APPEND_WORKLOAD, "batch": B, "position": p, "ring_tokens": L,
                  "block_m": m, "compressed_entries": cap, "window_kv": "bf16",
-                 "compressed_kv": "fp8_e4m3+fp32 scale", "pooling": "every step (the block completes)"}
+                 "compressed_kv": "fp8_e4m3+fp32 scale", "pooling": "every step (the block completes)",
+                 "indexer_keys": "own ring, fp32 entries, MXFP4 (E2M1 + E8M0 per 32) key cache"}
     return st
 
 
@@ -487,7 +515,9 @@ KERNEL_SOURCES = {
     "compress_indexer_topk": ["indexer_topk.hip", "indexer_core.hpp", "split.hpp", "topk.hip", "select.hpp",
                               "compress_core.hpp", "compress.hip", "common.hpp"],
     "mxfp4_quantize": ["quant.hip", "common.hpp"],
-    "kv_cache_append": ["cache.hip", "compress.hip", "compress_core.hpp", "common.hpp"]}
+    "kv_cache_append": ["cache.hip", "compress.hip", "compress_core.hpp", "common.hpp"],
+    "kv_cache_append_indexer": ["cache.hip", "compress.hip", "compress_core.hpp", "common.hpp"],
+    "mxfp4_quantize_appended": ["quant.hip", "common.hpp"]}
 
 
 def measured_traffic(workload, kernel):
@@ -523,27 +553,32 @@ def cpu_baseline_quant(st):
 
 def cpu_baseline_append(st, budget_s=10.0):
     """The oracle's cache append (ring writes as the step-by-step definition states them,
-    then the pool of the completed block) for the workload's 16 sequences, repeated within
-    the budget; appended tokens/s."""
+    the pool of the completed block, and the same for the indexer key with its MXFP4
+    encoding) for the workload's 16 sequences, repeated within the budget; appended
+    tokens/s."""
     from oracle.cache import append_step_by_step
     from oracle.compress import compress_kv
-    from oracle.formats import bf16_decode
+    from oracle.formats import bf16_decode, mxfp4_encode
     x = st.layers[0][1]["append_sample"]
     L, m, p = APPEND_SHAPE["L"], APPEND_SHAPE["m"], APPEND_SHAPE["pos"]
     K, V, Z = bf16_decode(x["K"]), bf16_decode(x["V"]), x["logits"]
+    KI = bf16_decode(st.layers[0][1]["append_sample_ix"])
     B = K.shape[0]
     reps, t0 = 0, time.perf_counter()
     while True:
         for b in range(B):
-            for X in (K[b], V[b], Z[b]):
+            for X in (K[b], V[b], Z[b], KI[b]):
                 append_step_by_step(X, X.shape[0], L, start=X.shape[0] - 1)   # the newest token
             compress_kv(K[b:b + 1, -m:], V[b:b + 1, -m:], Z[b:b + 1, -m:], m, "fp8")
+            ik, _ = compress_kv(KI[b:b + 1, -m:], KI[b:b + 1, -m:], Z[b:b + 1, -m:], m, "f32")
+            mxfp4_encode(ik.astype(np.float64))
         reps += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     return reps * B / dt, (f"fp64 numpy oracle: {reps} appends of the workload's {B} tokens at "
-                           f"position {p} (ring writes + fp8 pooling of the completed block), {dt:.1f} s")
+                           f"position {p} (ring writes, fp8 pooling of the completed block, the indexer "
+                           f"key's ring, fp32 pool and MXFP4 encoding), {dt:.1f} s")
 
 
 def cpu_baseline(st, budget_s):
