@@ -327,18 +327,11 @@ def build_append(args):
     st.add(Kernel("kv_cache_append", f_append, nbytes, 0, BF16_PEAK_TFLOPS, "kv_cache_append"))
 
     def f_append_ix(c):
-        csa.csa_kv_cache_append(c["ik_new"], c["iv_new"], c["z_new"], c["pos"], c["irk"], c["irv"], c["rz_i"], m,
-                                c["ik"], c["iv"], raw_pos0=c["raw0_i"])
-    # as above with fp32 entries: 2 x (512 + 4) B written per sequence for the entries
-    nbytes_ix = B * (2 * 256 + 4 + 2 * (2 * 256 + 4) + m * (2 * 256 + 4) + 2 * 512 + 4 + 4)
-    st.add(Kernel("kv_cache_append_indexer", f_append_ix, nbytes_ix, 0, BF16_PEAK_TFLOPS,
-                  "kv_cache_append_indexer"))
-
-    def f_quant_ix(c):
-        csa.csa_mxfp4_quantize_appended(c["ik"], c["pos"], m, c["kc"], c["ke"])
-    # per sequence: pos, the fp32 entry read, 64 + 4 B written
-    st.add(Kernel("mxfp4_quantize_appended", f_quant_ix, B * (4 + 512 + 68), 0, BF16_PEAK_TFLOPS,
-                  "mxfp4_quantize_appended"))
+        csa.csa_indexer_key_append(c["ik_new"], c["z_new"], c["pos"], c["irk"], c["rz_i"], m, c["kc"], c["ke"])
+    # per sequence: the key row and logit read, 2 copies written, the block's m rows and
+    # logits read back, the 64 + 4 B MXFP4 entry written; pos
+    nbytes_ix = B * (256 + 4 + 2 * (256 + 4) + m * (256 + 4) + 68 + 4)
+    st.add(Kernel("indexer_key_append", f_append_ix, nbytes_ix, 0, BF16_PEAK_TFLOPS, "indexer_key_append"))
     K = torch.from_numpy(x["K"].view(np.int16)).view(torch.bfloat16).cuda()
     V = torch.from_numpy(x["V"].view(np.int16)).view(torch.bfloat16).cuda()
     Z = torch.from_numpy(x["logits"]).cuda()
@@ -351,14 +344,11 @@ def build_append(args):
             "cv": torch.zeros((B, cap, 128), dtype=torch.uint8, device="cuda"),
             "cks": torch.zeros((B, cap), device="cuda"), "cvs": torch.zeros((B, cap), device="cuda"),
             "raw0": torch.empty((B,), dtype=torch.int32, device="cuda"),
-            # the indexer keys' ring (d_I = 128; the V side of the append carries the same rows)
-            "irk": Vx[:, :2 * L].contiguous(), "irv": Vx[:, :2 * L].contiguous(),
-            "rz_i": Z[:, :2 * L].contiguous(),
-            "ik_new": Vx[:, 2 * L].contiguous(), "iv_new": Vx[:, 2 * L].contiguous(),
-            "ik": torch.zeros((B, cap, 128), device="cuda"), "iv": torch.zeros((B, cap, 128), device="cuda"),
+            # the indexer keys' ring (d_I = 128) and MXFP4 key cache
+            "irk": Vx[:, :2 * L].contiguous(), "rz_i": Z[:, :2 * L].contiguous(),
+            "ik_new": Vx[:, 2 * L].contiguous(),
             "kc": torch.zeros((B, cap, 64), dtype=torch.uint8, device="cuda"),
-            "ke": torch.zeros((B, cap, 4), dtype=torch.uint8, device="cuda"),
-            "raw0_i": torch.empty((B,), dtype=torch.int32, device="cuda")}
+            "ke": torch.zeros((B, cap, 4), dtype=torch.uint8, device="cuda")}
     R = args.rotate or 4
     st.copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
     st.layers = [("", {"append_sample": {k: x[k][:, :2 * L + 1] for k in ("K", "V", "logits")},
@@ -514,10 +504,9 @@ KERNEL_SOURCES = {
     "compress_kv": ["compress.hip", "compress_core.hpp", "common.hpp"],
     "compress_indexer_topk": ["indexer_topk.hip", "indexer_core.hpp", "split.hpp", "topk.hip", "select.hpp",
                               "compress_core.hpp", "compress.hip", "common.hpp"],
-    "mxfp4_quantize": ["quant.hip", "common.hpp"],
-    "kv_cache_append": ["cache.hip", "compress.hip", "compress_core.hpp", "common.hpp"],
-    "kv_cache_append_indexer": ["cache.hip", "compress.hip", "compress_core.hpp", "common.hpp"],
-    "mxfp4_quantize_appended": ["quant.hip", "common.hpp"]}
+    "mxfp4_quantize": ["quant.hip", "mxfp4.hpp", "common.hpp"],
+    "kv_cache_append": ["cache.hip", "compress.hip", "compress_core.hpp", "mxfp4.hpp", "common.hpp"],
+    "indexer_key_append": ["cache.hip", "compress_core.hpp", "mxfp4.hpp", "common.hpp"]}
 
 
 def measured_traffic(workload, kernel):

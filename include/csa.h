@@ -423,6 +423,30 @@ csa_status_t csa_mxfp4_quantize_appended(const void* x, int32_t in_dtype, const 
                                          int32_t B, int32_t cap, int32_t m, int32_t d,
                                          uint8_t* codes, uint8_t* e8m0, void* stream);
 
+/* ---------------------------------------------------------------------
+ * csa_indexer_key_append -- one decode token's indexer key into the
+ * indexer's ring and, when it completes a block, its MXFP4 key entry.
+ *
+ * Passage: as csa_kv_cache_append (per-entry keys pooled from the tokens'
+ * keys) and csa_mxfp4_quantize (MXFP4 on the indexer path).  For each
+ * sequence b with pos[b] >= 0 the key row and logit go to ring rows
+ * pos mod L_ring and pos mod L_ring + L_ring; when pos + 1 is a multiple of m
+ * and e = (pos + 1)/m - 1 < cap, the block is pooled (the K side of
+ * csa_kv_cache_append with fp32 entries, bit for bit) and converted as
+ * csa_mxfp4_quantize converts it into codes[b, e], e8m0[b, e].  The same
+ * results as csa_kv_cache_append (fp32 entries) followed by
+ * csa_mxfp4_quantize_appended, in one launch and without a V side.
+ *
+ *   k_new [B, d] io_dtype (CSA_BF16 or CSA_F32);  z_new [B] fp32;  pos [B]
+ *   k_ring [B, 2*L_ring, d] io_dtype;  z_ring [B, 2*L_ring] fp32
+ *   codes [B, cap, d/2], e8m0 [B, cap, d/32] uint8
+ * Limits: d = 128; m < 32; m <= L_ring.
+ * ------------------------------------------------------------------- */
+csa_status_t csa_indexer_key_append(const void* k_new, const float* z_new, int32_t io_dtype,
+                                    const int32_t* pos, int32_t B, int32_t d, int32_t L_ring,
+                                    void* k_ring, float* z_ring, int32_t m, int32_t cap,
+                                    uint8_t* codes, uint8_t* e8m0, void* stream);
+
 /* Workspace bytes a call needs.  n_keys = k + W (CSA) or cap + W (HCA);
  * for CSA_OP_TOPK and CSA_OP_INDEXER_TOPK pass T_q and n_keys = cap (and, for
  * CSA_OP_INDEXER_TOPK, d = d_I).  Returns 0 when none is needed and

@@ -30,6 +30,7 @@ EXPORTS = ["csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_i
            "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn",
            "csa_sparse_attn_batch_invariant", "hca_dense_attn_batch_invariant", "csa_kv_cache_append",
            "csa_mxfp4_quantize_appended", "csa_sparse_attn_varlen", "hca_dense_attn_varlen",
+           "csa_indexer_key_append",
            "csa_workspace_size",
            "csa_status_str", "csa_abi_version"]
 
@@ -76,7 +77,9 @@ def load(path=LIB_PATH):
                                            _I, _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
     lib.hca_dense_attn_varlen.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _P, _P,
                                           _I, _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
-    for fn in ["csa_sparse_attn_varlen", "hca_dense_attn_varlen", "csa_mxfp4_quantize_appended", "csa_kv_cache_append", "csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
+    lib.csa_indexer_key_append.argtypes = [_P, _P, _I, _P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P]
+    for fn in ["csa_indexer_key_append", "csa_sparse_attn_varlen", "hca_dense_attn_varlen",
+               "csa_mxfp4_quantize_appended", "csa_kv_cache_append", "csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
                "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn",
                "csa_sparse_attn_batch_invariant", "hca_dense_attn_batch_invariant"]:
         getattr(lib, fn).restype = _I
@@ -392,3 +395,17 @@ def hca_dense_attn_varlen(q, ck, cv, m_prime, k_win, v_win, raw_pos0, row_seq, r
     return _varlen("hca_dense_attn_varlen", CSA_OP_DENSE_ATTN_BATCH_INVARIANT, q, ck, cv, (m_prime,),
                    ck.shape[1] + W, k_win, v_win, raw_pos0, row_seq, row_pos, W, ck_scale, cv_scale,
                    sm_scale, out, lse, stream)
+
+
+def csa_indexer_key_append(k_new, z_new, pos, k_ring, z_ring, m, codes, e8m0, stream=None):
+    """Append one indexer key per sequence (k_new [B, d], z_new [B], pos [B]) to its ring
+    (k_ring [B, 2L, d], z_ring [B, 2L]) and write the MXFP4 entry of a block it completes
+    into codes [B, cap, d/2] and e8m0 [B, cap, d/32]."""
+    B, d = k_new.shape
+    L2 = k_ring.shape[1]
+    if L2 % 2:
+        raise ValueError("the ring holds 2 * L_ring rows per sequence")
+    st = load().csa_indexer_key_append(_ptr(k_new), _ptr(z_new), _dt_of(k_new), _ptr(pos), B, d, L2 // 2,
+                                       _ptr(k_ring), _ptr(z_ring), m, codes.shape[1], _ptr(codes), _ptr(e8m0),
+                                       _stream(stream))
+    _check("csa_indexer_key_append", st)

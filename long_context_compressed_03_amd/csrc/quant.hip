@@ -16,20 +16,11 @@
 // codes are those of the definition applied to the input values, bit for bit.
 // An HBM stream: 64 B (bf16) or 128 B (fp32) read and 17 B written per
 // 32-element block.
-#include "common.hpp"
+#include "mxfp4.hpp"
 
 namespace {
 
 constexpr int kQThreads = 256;
-
-// E2M1 magnitude code of v >= 0 (v already divided by the block scale): the
-// count of grid midpoints below v, each midpoint going to the even code of
-// its two neighbours (0.25 -> 0, 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2.0,
-// 2.5 -> 2.0, 3.5 -> 4.0, 5 -> 4.0); past 5 everything is 6 (saturated).
-CSA_DEV uint32_t e2m1_magnitude_code(float v) {
-  return uint32_t(v > 0.25f) + uint32_t(v >= 0.75f) + uint32_t(v > 1.25f) + uint32_t(v >= 1.75f) +
-         uint32_t(v > 2.5f) + uint32_t(v >= 3.5f) + uint32_t(v > 5.0f);
-}
 
 // kL lanes per 32-element block (4 for bf16, 8 for fp32), each holding 16
 // contiguous input bytes, so a wave's load is one contiguous 1 KB span; a
@@ -63,10 +54,8 @@ CSA_DEV uint32_t convert_lane(const u32x4& w, int& X) {
   for (int i = 0; i < kE; ++i) amax = fmaxf(amax, fabsf(v[i]));
 #pragma unroll
   for (int o = 1; o < kL; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-  // X = floor(log2(amax)) - 2; for fp32 inputs floor(log2(amax)) <= 127, so
-  // X <= 125 and 2^-X is a normal float; a zero block takes X = -127
-  X = amax > 0.f ? max(ilogbf(amax) - 2, -127) : -127;
-  const float inv = __uint_as_float(uint32_t(127 - X) << 23);   // 2^-X, exact
+  X = mxfp4_block_exponent(amax);
+  const float inv = mxfp4_inv_scale(X);
   uint32_t word = 0u;
 #pragma unroll
   for (int i = 0; i < kE; ++i) {

@@ -231,6 +231,14 @@ def test_cache_varlen_and_appended_quantize_reject_bad_arguments():
     assert append(raw=None) == csa.CSA_EINVAL
     assert lib.csa_workspace_size(csa.CSA_OP_KV_CACHE_APPEND, 4, 0, 0, 0, 0) == 0
 
+    def ixapp(d=128, L=8, m=4, io=0, codes=_p()):
+        return lib.csa_indexer_key_append(_p(), _p(), io, _p(), 2, d, L, _p(), _p(), m, 16, codes, _p(), None)
+    assert ixapp(d=64) == csa.CSA_EINVAL
+    assert ixapp(m=16) == csa.CSA_EINVAL              # the block is longer than the ring
+    assert ixapp(m=32, L=64) == csa.CSA_ENOTSUP       # long blocks: no indexer at that rate
+    assert ixapp(io=2) == csa.CSA_EINVAL
+    assert ixapp(codes=None) == csa.CSA_EINVAL
+
     def quant(dt=0, d=128, m=4, pos=_p()):
         return lib.csa_mxfp4_quantize_appended(_p(), dt, pos, 2, 16, m, d, _p(), _p(), None)
     assert quant(dt=2) == csa.CSA_EINVAL

@@ -169,7 +169,8 @@ def test_cache_append(csa, io, ckv, B, m, L, cap, starts, steps, idle):
 
 def test_indexer_key_append(csa):
     """Per-token indexer keys through a ring with fp32 entries, then the MXFP4 conversion of
-    each new entry: codes and scales of every appended entry equal csa_mxfp4_quantize of the
+    each new entry; and csa_indexer_key_append, which must give the same rings, codes and
+    scales bit for bit in one launch.  Codes and scales of every appended entry equal csa_mxfp4_quantize of the
     same entries bit for bit (that call is bit-exact against the oracle's encoder), no other
     entry is written, and they agree with the oracle's chain (fp64 pool, fp32 storage, MXFP4
     encoding) except where the pool's last-bit rounding decides a code."""
@@ -189,14 +190,24 @@ def test_indexer_key_append(csa):
     e8 = torch.full((B, cap, 4), 0xAB, dtype=torch.uint8, device="cuda")
     ar = torch.arange(B, device="cuda")
     nxt = np.array(starts, np.int64)
+    # the one-launch form, on rings and key caches of its own
+    ring_f = torch.zeros_like(ring)
+    ring_zf = torch.zeros_like(ring_z)
+    codes_f = torch.full_like(codes, 0xAB)
+    e8_f = torch.full_like(e8, 0xAB)
     for _ in range(steps):
         pos_d = t_i32(nxt.astype(np.int32))
         src = pos_d.long()
         k1 = K_d[ar, src].contiguous()
-        csa.csa_kv_cache_append(k1, k1, Z_d[ar, src].contiguous(), pos_d, ring, ring_v, ring_z, m, ent, ent_v)
+        z1 = Z_d[ar, src].contiguous()
+        csa.csa_kv_cache_append(k1, k1, z1, pos_d, ring, ring_v, ring_z, m, ent, ent_v)
         csa.csa_mxfp4_quantize_appended(ent, pos_d, m, codes, e8)
+        csa.csa_indexer_key_append(k1, z1, pos_d, ring_f, ring_zf, m, codes_f, e8_f)
         nxt += 1
     torch.cuda.synchronize()
+    assert torch.equal(codes_f, codes) and torch.equal(e8_f, e8)
+    assert torch.equal(ring_f.view(torch.int16), ring.view(torch.int16))
+    assert torch.equal(ring_zf.view(torch.int32), ring_z.view(torch.int32))
     ref_c, ref_e = csa.csa_mxfp4_quantize(ent.reshape(B * cap, 128))
     torch.cuda.synchronize()
     gc, ge = h(codes), h(e8)
