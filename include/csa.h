@@ -39,8 +39,10 @@
  *     the host; they are documented as preconditions per call.
  *   - Results are bitwise reproducible run to run: work splits depend only
  *     on the shape arguments and every reduction has a fixed order.
- *   - The library keeps no state; calls on different streams may overlap
- *     provided their outputs and workspaces do not alias.
+ *   - The library keeps no state beyond a mutex-guarded host record of which
+ *     kernels have had their LDS limit raised on which device; calls on
+ *     different streams may overlap provided their outputs and workspaces do
+ *     not alias.
  */
 #ifndef CSA_H
 #define CSA_H

@@ -895,15 +895,9 @@ size_t plan_ws_bytes(const Plan& p, long rows, int H) {
 
 template <int kIO, int kCKV, bool kDense, int kHTW, int kDepth, bool kVarlen>
 hipError_t launch_attn(const AttnArgs& a, long blocks, hipStream_t st) {
-  static bool attr = false;   // per instantiation; dynamic LDS above 64 KB needs the opt-in
   constexpr size_t bytes = lds_bytes<kIO, kHTW>();
   auto fn = attn_kernel<kIO, kCKV, kDense, kHTW, kDepth, kVarlen>;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       int(bytes));
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  if (hipError_t e = csa_lds_opt_in(reinterpret_cast<const void*>(fn), bytes); e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3(unsigned(blocks)), dim3(kThreads), bytes, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
@@ -915,14 +909,10 @@ hipError_t launch_attn(const AttnArgs& a, long blocks, hipStream_t st) {
 
 template <int kCKV, int kQB>
 hipError_t launch_mq_q(const AttnArgs& a, int B, hipStream_t st) {
-  static bool attr = false;
   constexpr size_t bytes = sizeof(LdsMQ);
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_mq_kernel<kCKV, kQB>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  if (hipError_t e = csa_lds_opt_in(reinterpret_cast<const void*>(&attn_mq_kernel<kCKV, kQB>), bytes);
+      e != hipSuccess)
+    return e;
   const long blocks = long(B) * ((a.T_q + kQB - 1) / kQB);
   hipLaunchKernelGGL((attn_mq_kernel<kCKV, kQB>), dim3(unsigned(blocks)), dim3(kThreads), bytes, st, a);
   return hipGetLastError();
@@ -1144,3 +1134,4 @@ extern "C" csa_status_t hca_dense_attn(CSA_DENSE_ARGS) { return dense_attn_impl(
 extern "C" csa_status_t hca_dense_attn_batch_invariant(CSA_DENSE_ARGS) {
   return dense_attn_impl(CSA_DENSE_PASS, true);
 }
+

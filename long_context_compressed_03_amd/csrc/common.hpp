@@ -3,6 +3,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <set>
+#include <utility>
+
 #include "../../include/csa.h"
 
 #define CSA_DEV __device__ __forceinline__
@@ -205,5 +209,21 @@ CSA_DEV uint32_t block_reduce_or(uint32_t v, uint32_t* smem) {
   do {                                                       \
     if (hipGetLastError() != hipSuccess) return CSA_EHIP;    \
   } while (0)
+
+// Dynamic LDS above 64 KB needs a per-kernel opt-in.  It is set once per
+// (kernel, device) and the record of what was set is guarded by a mutex, so
+// host threads may launch concurrently.
+inline hipError_t csa_lds_opt_in(const void* fn, size_t bytes) {
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({fn, dev})) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+  if (e == hipSuccess) done.insert({fn, dev});
+  return e;
+}
 
 static inline bool csa_dtype_ok(int32_t dt) { return dt == CSA_BF16 || dt == CSA_F32 || dt == CSA_FP8_E4M3; }

@@ -754,13 +754,9 @@ template <int kHI, int kKS, int kJ>
 hipError_t launch_select_j(long rows, hipStream_t st, const uint16_t* key16, const uint8_t* qc, const uint8_t* qe,
                            const float* w, const uint8_t* kc, const uint8_t* ke, const int32_t* pos, int T_q,
                            int d_I, int cap, int m, int k, int32_t* idx) {
-  static bool attr = false;   // more than 64 KB of LDS needs the opt-in
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<kHI, kKS, kJ>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(Shared)));
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  if (hipError_t e = csa_lds_opt_in(reinterpret_cast<const void*>(&select_kernel<kHI, kKS, kJ>), sizeof(Shared));
+      e != hipSuccess)
+    return e;
   hipLaunchKernelGGL((select_kernel<kHI, kKS, kJ>), dim3(unsigned(rows)), dim3(kThreads), sizeof(Shared), st, key16, qc, qe, w, kc, ke, pos, T_q,
                      d_I, cap, m, k, idx);
   return hipGetLastError();

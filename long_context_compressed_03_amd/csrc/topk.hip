@@ -667,12 +667,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 
 template <bool kSplit>
 hipError_t set_lds_limit() {
-  static bool done = false;   // more than 64 KB of LDS needs the opt-in
-  if (done) return hipSuccess;
-  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_kernel<kSplit>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(sizeof(RowShared)));
-  done = e == hipSuccess;
-  return e;
+  return csa_lds_opt_in(reinterpret_cast<const void*>(&topk_kernel<kSplit>), sizeof(RowShared));
 }
 
 hipError_t launch_topk(long rows, hipStream_t st, const float* scores, const int32_t* q_pos0, int T_q, int cap, int m,
