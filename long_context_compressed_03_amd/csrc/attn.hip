@@ -21,7 +21,9 @@
 //   O^T[128 x 16 heads] += V^T * P^T  (P^T taken straight from S^T's C layout)
 // fp8 (E4M3FN) entries are widened to bf16 exactly by the hardware
 // conversion (fp32 variant: in software); the per-entry K scale
-// multiplies the logits and the V scale is folded into P.  The fp32 variant
+// multiplies the logits and the V scale is folded into P, which enters the
+// P*V product as two bf16 operands, hi + lo (16 significant bits: one bf16
+// rounding of P would cost 2^-9 of |V| per output).  The fp32 variant
 // runs the same data flow on the fp32 MFMA 16x16x4 (V row-major there).
 //
 // A block owns one query and one split of its key list; its 8 waves take the
@@ -471,22 +473,27 @@ void attn_kernel(AttnArgs a) {
       // O^T += V^T P^T (P carries the per-entry V scale)
       if constexpr (kIO == CSA_BF16) {
         // one 32-key step: contraction slot 8g+j <-> key 4g+j (j<4) / 16+4g+(j-4) of the half
-        uint32_t pw[4];
+        // P as bf16 hi + lo (two passes): a single bf16 rounding of P would
+        // cost 2^-9 of |V| per output, beyond the bf16 bound for large V
+        uint32_t ph[4], pl[4];
 #pragma unroll
         for (int h2 = 0; h2 < 4; ++h2) {
           const int kk = h2 >> 1;
           const int r0 = (h2 & 1) * 2;
           const int key = (2 * kh + kk) * 16 + 4 * g + r0;
-          pw[h2] = pack_bf16x2(p[kk][r0] * s.sv[key], p[kk][r0 + 1] * s.sv[key + 1]);
+          split_bf16x2(p[kk][r0] * s.sv[key], p[kk][r0 + 1] * s.sv[key + 1], &ph[h2], &pl[h2]);
         }
-        const u32x4 pb = {pw[0], pw[1], pw[2], pw[3]};
+        const u32x4 pbh = {ph[0], ph[1], ph[2], ph[3]};
+        const u32x4 pbl = {pl[0], pl[1], pl[2], pl[3]};
         const int k0 = kh * 32 + 4 * g;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
           const uint16_t* vt = &s.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0];   // row dt*16 + col
           const u32x2 lo = *reinterpret_cast<const u32x2*>(vt);
           const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + 16);
-          o[ht][dt] = mfma_k32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb, o[ht][dt]);
+          const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+          o[ht][dt] = mfma_k32(vf, pbh, o[ht][dt]);
+          o[ht][dt] = mfma_k32(vf, pbl, o[ht][dt]);
         }
       } else {
 #pragma unroll
@@ -776,7 +783,7 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
         for (int ht = 0; ht < 2; ++ht) x[ht][kt][r] = vis ? acc[ht][r] * scl : -INFINITY;
       }
     }
-    uint32_t pw[2][2][4];   // [ht][32-key step][pair]
+    uint32_t pw[2][2][4], pl[2][2][4];   // [ht][32-key step][pair]: P as bf16 hi + lo
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
       float cmax = -INFINITY;
@@ -815,7 +822,8 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
           const int kt = 2 * st + (h2 >> 1);
           const int r0 = (h2 & 1) * 2;
           const int key = kt * 16 + 4 * g + r0;
-          pw[ht][st][h2] = pack_bf16x2(p[kt][r0] * s.c.sv[key], p[kt][r0 + 1] * s.c.sv[key + 1]);
+          split_bf16x2(p[kt][r0] * s.c.sv[key], p[kt][r0 + 1] * s.c.sv[key + 1], &pw[ht][st][h2],
+                       &pl[ht][st][h2]);
         }
     }
     // O^T += V^T P^T; V^T fragments shared by both tiles
@@ -824,6 +832,8 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
       const int k0 = st * 32 + 4 * g;
       const u32x4 pb0 = {pw[0][st][0], pw[0][st][1], pw[0][st][2], pw[0][st][3]};
       const u32x4 pb1 = {pw[1][st][0], pw[1][st][1], pw[1][st][2], pw[1][st][3]};
+      const u32x4 pl0 = {pl[0][st][0], pl[0][st][1], pl[0][st][2], pl[0][st][3]};
+      const u32x4 pl1 = {pl[1][st][0], pl[1][st][1], pl[1][st][2], pl[1][st][3]};
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const uint16_t* vt = &s.c.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0];   // row dt*16 + col
@@ -832,6 +842,8 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
         const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
         o[0][dt] = mfma_k32(vf, pb0, o[0][dt]);
         o[1][dt] = mfma_k32(vf, pb1, o[1][dt]);
+        o[0][dt] = mfma_k32(vf, pl0, o[0][dt]);
+        o[1][dt] = mfma_k32(vf, pl1, o[1][dt]);
       }
     }
   };

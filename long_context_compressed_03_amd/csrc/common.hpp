@@ -33,6 +33,17 @@ CSA_DEV uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f_t{lo, hi}, v2bf_t));
 }
 
+// Two fp32 values split as hi + lo, both bf16 pairs: hi is the nearest bf16 of
+// each value and lo the nearest bf16 of the (exact, fp32) remainder, so hi + lo
+// carries 16 significant bits.  A product with a bf16 operand taken as
+// hi * x + lo * x (two matrix-core passes) then loses about 2^-17 of each value
+// instead of the 2^-9 of a single bf16 rounding.
+CSA_DEV void split_bf16x2(float a, float b, uint32_t* hi, uint32_t* lo) {
+  const uint32_t h = pack_bf16x2(a, b);
+  *hi = h;
+  *lo = pack_bf16x2(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xFFFF0000u));
+}
+
 // Round fp32 to the nearest bf16, ties to even (finite inputs).
 CSA_DEV uint16_t f32_to_bf16(float x) { return uint16_t(pack_bf16x2(x, 0.f)); }
 

@@ -15,7 +15,9 @@ Two kinds of case:
     where the pool's last bit decides a rounding (checked by the compression tests); those
     few flips move the outputs far less than the attention tolerance.
 Every attention call is checked in its plain, batch-invariant and varlen form.  Tolerances:
-2e-2 (bf16 I/O) / 1e-5 (fp32 I/O) plus half a unit of the output format at |O|.
+2e-2 (bf16 I/O) / 1e-5 (fp32 I/O) plus half a unit of the output format at |O|.  (These cases
+found that one bf16 rounding of P before the P*V product misses 2e-2 at |O| ~ 10 when a few
+outlier values dominate a row; P now enters that product as bf16 hi + lo.)
 """
 import numpy as np
 import pytest
@@ -43,8 +45,13 @@ def csa():
 
 
 def _inputs(B, T, H, cap, L_raw, io, seed):
-    """Queries and raw window (N(0,1) + outliers) and an fp8 cache quantised by the oracle's rule."""
+    """Queries and raw window (N(0,1) + outliers) and an fp8 cache quantised by the oracle's rule.
+
+    fp32 I/O cases draw no outliers: the layer-pair shapes that carry them are bf16, and with
+    |K| up to ~40 the fp32 logits alone are off by ~|logit| * 2^-22, which moves an output by
+    more than 1e-5 whatever the kernel does."""
     rq, rck, rcv, rkw, rvw, ro = streams(71, seed, 6)
+    ro = ro if io == "bf16" else None
     x = dict(q=normal_kv(rq, (B, T, H, D), io), Kw=normal_kv(rkw, (B, L_raw, D), io, ro),
              Vw=normal_kv(rvw, (B, L_raw, D), io, ro))
     x["cK"], x["cK_scale"] = store(normal_f32(rck, (B, cap, D), ro).astype(np.float64), "fp8")
