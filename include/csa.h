@@ -40,9 +40,9 @@
  *   - Results are bitwise reproducible run to run: work splits depend only
  *     on the shape arguments and every reduction has a fixed order.
  *   - The library keeps no state beyond a mutex-guarded host record of which
- *     kernels have had their LDS limit raised on which device; calls on
- *     different streams may overlap provided their outputs and workspaces do
- *     not alias.
+ *     kernels have had their LDS limit raised on which device, and the fixed
+ *     device scratch of csa_sparse_attn_noalloc; calls on different streams
+ *     may overlap provided their outputs and workspaces do not alias.
  */
 #ifndef CSA_H
 #define CSA_H
@@ -59,7 +59,8 @@ typedef enum {
   CSA_EINVAL = 1,     /* invalid argument (shape, pointer, enum)          */
   CSA_ENOTSUP = 2,    /* valid but unsupported combination               */
   CSA_EHIP = 3,       /* HIP runtime error while enqueueing               */
-  CSA_EWORKSPACE = 4  /* workspace missing or smaller than required       */
+  CSA_EWORKSPACE = 4, /* workspace missing or smaller than required       */
+  CSA_ESCRATCH = 5    /* beyond the fixed scratch of csa_sparse_attn_noalloc */
 } csa_status_t;
 
 typedef enum {
@@ -292,6 +293,31 @@ csa_status_t hca_dense_attn(const void* q, int32_t io_dtype, const void* ck, con
                             int32_t W, int32_t B, int32_t T_q, int32_t H, int32_t d,
                             float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* ---------------------------------------------------------------------
+ * csa_sparse_attn_noalloc -- csa_sparse_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).
+ *
+ * Same arguments, results (bit for bit) and limits as csa_sparse_attn,
+ * without ws / ws_bytes: the split partials go to a fixed 32 MiB device array
+ * inside the library (one per GPU, held until the process ends).  Nothing is
+ * allocated or freed; the first call on a device looks up that device's
+ * array address.  The array needs no initial contents.
+ * Errors: a call whose csa_workspace_size(CSA_OP_SPARSE_ATTN, ...) exceeds
+ * 32 MiB returns CSA_ESCRATCH before anything is enqueued (decode shapes need
+ * a few MiB: 16 rows x 64 heads over 1152 keys take 4.8 MiB).
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, or host threads without ordering) race and
+ * must not be issued.
+ * ------------------------------------------------------------------- */
+csa_status_t csa_sparse_attn_noalloc(const void* q, int32_t io_dtype, const void* ck, const void* cv,
+                                     const float* ck_scale, const float* cv_scale, int32_t ckv_dtype,
+                                     int32_t cap, const int32_t* idx, int32_t k, const void* k_win,
+                                     const void* v_win, const int32_t* raw_pos0, int32_t L_raw,
+                                     const int32_t* q_pos0, int32_t W, int32_t B, int32_t T_q,
+                                     int32_t H, int32_t d, float sm_scale, void* out, float* lse,
+                                     void* stream);
 
 /* ---------------------------------------------------------------------
  * csa_sparse_attn_batch_invariant, hca_dense_attn_batch_invariant -- the

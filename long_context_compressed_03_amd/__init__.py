@@ -19,7 +19,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcsa.so")
 
-CSA_OK, CSA_EINVAL, CSA_ENOTSUP, CSA_EHIP, CSA_EWORKSPACE = range(5)
+CSA_OK, CSA_EINVAL, CSA_ENOTSUP, CSA_EHIP, CSA_EWORKSPACE, CSA_ESCRATCH = range(6)
 CSA_BF16, CSA_F32, CSA_FP8_E4M3 = 0, 1, 2
 CSA_OP_TOPK, CSA_OP_SPARSE_ATTN, CSA_OP_DENSE_ATTN, CSA_OP_INDEXER_TOPK = 0, 1, 2, 3
 CSA_OP_SPARSE_ATTN_BATCH_INVARIANT, CSA_OP_DENSE_ATTN_BATCH_INVARIANT = 4, 5
@@ -30,7 +30,7 @@ EXPORTS = ["csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_i
            "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn",
            "csa_sparse_attn_batch_invariant", "hca_dense_attn_batch_invariant", "csa_kv_cache_append",
            "csa_mxfp4_quantize_appended", "csa_sparse_attn_varlen", "hca_dense_attn_varlen",
-           "csa_indexer_key_append",
+           "csa_indexer_key_append", "csa_sparse_attn_noalloc",
            "csa_workspace_size",
            "csa_status_str", "csa_abi_version"]
 
@@ -78,7 +78,9 @@ def load(path=LIB_PATH):
     lib.hca_dense_attn_varlen.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _P, _P,
                                           _I, _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
     lib.csa_indexer_key_append.argtypes = [_P, _P, _I, _P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P]
-    for fn in ["csa_indexer_key_append", "csa_sparse_attn_varlen", "hca_dense_attn_varlen",
+    lib.csa_sparse_attn_noalloc.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _P, _I, _P, _P, _P, _I, _P, _I,
+                                            _I, _I, _I, _I, _F, _P, _P, _P]
+    for fn in ["csa_indexer_key_append", "csa_sparse_attn_noalloc", "csa_sparse_attn_varlen", "hca_dense_attn_varlen",
                "csa_mxfp4_quantize_appended", "csa_kv_cache_append", "csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
                "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn",
                "csa_sparse_attn_batch_invariant", "hca_dense_attn_batch_invariant"]:
@@ -296,6 +298,22 @@ def csa_sparse_attn(q, ck, cv, idx, k_win, v_win, raw_pos0, q_pos0, W, ck_scale=
                              T_q, H, d, sm, _ptr(out), _ptr(lse), _ws_ptr(ws), _ws_len(ws),
                              _stream(stream))
     _check(name, st)
+    return out
+
+
+def csa_sparse_attn_noalloc(q, ck, cv, idx, k_win, v_win, raw_pos0, q_pos0, W, out, ck_scale=None,
+                            cv_scale=None, sm_scale=None, lse=None, stream=None):
+    """csa_sparse_attn for callers that cannot allocate: the caller passes `out` (and `lse`), and
+    the split partials go to the library's fixed per-GPU scratch.  Calls that may overlap on one
+    GPU must not be issued (they share that scratch)."""
+    B, T_q, H, d = q.shape
+    k = idx.shape[-1]
+    sm = d ** -0.5 if sm_scale is None else sm_scale
+    st = load().csa_sparse_attn_noalloc(_ptr(q), _dt_of(q), _ptr(ck), _ptr(cv), _ptr(ck_scale), _ptr(cv_scale),
+                                        _dt_of(ck), ck.shape[1], _ptr(idx), k, _ptr(k_win), _ptr(v_win),
+                                        _ptr(raw_pos0), k_win.shape[1], _ptr(q_pos0), W, B, T_q, H, d, sm,
+                                        _ptr(out), _ptr(lse), _stream(stream))
+    _check("csa_sparse_attn_noalloc", st)
     return out
 
 

@@ -34,8 +34,9 @@ extern "C" const char* csa_status_str(int32_t status) {
     case CSA_ENOTSUP: return "CSA_ENOTSUP: unsupported combination";
     case CSA_EHIP: return "CSA_EHIP: HIP runtime error";
     case CSA_EWORKSPACE: return "CSA_EWORKSPACE: workspace missing or too small";
+    case CSA_ESCRATCH: return "CSA_ESCRATCH: the call needs more than the allocation-free call's fixed scratch";
     default: return "unknown status";
   }
 }
 
-extern "C" int32_t csa_abi_version(void) { return 102; }
+extern "C" int32_t csa_abi_version(void) { return 103; }

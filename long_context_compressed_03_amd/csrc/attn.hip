@@ -1147,3 +1147,55 @@ extern "C" csa_status_t hca_dense_attn_batch_invariant(CSA_DENSE_ARGS) {
   return dense_attn_impl(CSA_DENSE_PASS, true);
 }
 
+// ------------------------------------------------ allocation-free entry --
+// csa_sparse_attn_noalloc keeps the split partials in a fixed device array
+// instead of a caller workspace, for callers that cannot allocate.  Each GPU
+// holds its own copy of the array until the process ends.  In host code the
+// array's name is only a host-side stand-in: its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is passed to kernels.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (set up on its first use).
+csa_status_t scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CSA_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return CSA_ENOTSUP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CSA_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" csa_status_t csa_sparse_attn_noalloc(const void* q, int32_t io_dtype, const void* ck, const void* cv,
+                                                const float* ck_scale, const float* cv_scale, int32_t ckv_dtype,
+                                                int32_t cap, const int32_t* idx, int32_t k, const void* k_win,
+                                                const void* v_win, const int32_t* raw_pos0, int32_t L_raw,
+                                                const int32_t* q_pos0, int32_t W, int32_t B, int32_t T_q, int32_t H,
+                                                int32_t d, float sm_scale, void* out, float* lse, void* stream) {
+  // the same argument checks as csa_sparse_attn come first, then the size check
+  csa_status_t c = check_common(q, io_dtype, ck, cv, ck_scale, cv_scale, ckv_dtype, cap, k_win, v_win, raw_pos0, L_raw,
+                                q_pos0, W, B, T_q, H, d, out);
+  if (c != CSA_OK) return c;
+  if (!idx || k < 1) return CSA_EINVAL;
+  if (long(k) + W > 0x7FFFFFFFL - kNK) return CSA_ENOTSUP;
+  if (csa_attn_workspace_size(long(B) * T_q, H, k + W, false) > kScratchBytes) return CSA_ESCRATCH;
+  void* ws = nullptr;
+  c = scratch_of_current_device(&ws);
+  if (c != CSA_OK) return c;
+  return sparse_attn_impl(q, io_dtype, ck, cv, ck_scale, cv_scale, ckv_dtype, cap, idx, k, k_win, v_win, raw_pos0,
+                          L_raw, q_pos0, W, B, T_q, H, d, sm_scale, out, lse, ws, kScratchBytes, stream, false);
+}

@@ -35,8 +35,8 @@ def test_every_declared_symbol_is_exported():
 def test_status_strings_and_version():
     import long_context_compressed_03_amd as csa
     lib = csa.load()
-    assert lib.csa_abi_version() == 102
-    for s in range(5):
+    assert lib.csa_abi_version() == 103
+    for s in range(6):
         assert lib.csa_status_str(s).decode().startswith("CSA_")
 
 
@@ -270,3 +270,22 @@ def test_binding_fails_loudly_without_gpu_tensors():
     with pytest.raises(ValueError):
         csa.csa_compress_kv(x, x, torch.zeros(1, 8), 4, torch.zeros(1, 2, 128, dtype=torch.bfloat16),
                             torch.zeros(1, 2, 128, dtype=torch.bfloat16))
+
+
+def test_noalloc_attention_rejects_what_its_scratch_cannot_hold():
+    """csa_sparse_attn_noalloc checks its arguments as csa_sparse_attn does, then rejects a call
+    whose split partials exceed the fixed 32 MiB scratch, before touching the device."""
+    import long_context_compressed_03_amd as csa
+    lib = csa.load()
+
+    def call(B=1, T_q=1, H=64, k=1024, W=128, idx=_p(), d=128):
+        return lib.csa_sparse_attn_noalloc(_p(), 0, _p(), _p(), None, None, 0, 4096, idx, k, _p(), _p(), _p(),
+                                           W, _p(), W, B, T_q, H, d, 0.088, _p(), None, None)
+    assert call(idx=None) == csa.CSA_EINVAL
+    assert call(d=64) == csa.CSA_EINVAL
+    assert call(H=8) == csa.CSA_ENOTSUP
+    # 255 rows of 128 heads split in two pieces each: 33.9 MB of partials
+    need = lib.csa_workspace_size(csa.CSA_OP_SPARSE_ATTN, 255, 1, 128, 128, 1024 + 128)
+    assert need > 32 << 20
+    assert call(B=255, H=128) == csa.CSA_ESCRATCH
+    assert lib.csa_workspace_size(csa.CSA_OP_SPARSE_ATTN, 16, 1, 64, 128, 1024 + 128) <= 32 << 20
