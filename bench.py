@@ -1,19 +1,28 @@
 """Benchmark of the CSA / HCA hot path on one MI355X.
 
 A step is one pass of the whole path over one batch of synthetic input.  The
-default workload is CSA decoding at a 128K context: 16 sequences, one query
-each at position 131071; the block of 4 tokens the query completes is pooled
-into compressed entry 32767, the MXFP4 indexer scores all 32768 entries (8
-heads x 128), the top 1024 are kept and 64-head attention runs over them plus
-the 128-token window.  Other workloads (--workload) cover HCA decoding at 1M,
-CSA prefill of a 4096-token chunk at 256K, and the 1M CSA+HCA layer pair.
+default run (--workload all) measures four full-size workloads, one after the
+other, and prints them in ONE JSON line:
+  * headline (value, steps, ms_per_step, roofline, cpu_baseline): the 1M-context
+    CSA + HCA layer pair -- a CSA layer (4 decode rows at 1M with 262144 fp8
+    entries, then a 2048-token chunk over 262656) followed by an HCA layer
+    (8192 / 8208 fp8 entries), 2052 query tokens per step;
+  * under "workloads": CSA decoding at 128K (16 sequences: pool the block the
+    query completes, MXFP4 indexer over 32768 entries, top-1024, 64-head
+    attention over them plus the 128-token window), HCA decoding at 1M (4
+    sequences, 8192 fp8 entries + window) and CSA prefill of a 4096-token chunk
+    at 256K (66560 entries, top-2048).
+--workload picks one of them (or the quantiser / cache-append workloads) alone.
 
-Inputs are resident in HBM before timing.  The step is captured once per input
-copy into a HIP graph; copies rotate so that one rotation touches well over
-twice the 256 MB Infinity Cache and reads are served by HBM.  Per-kernel
-durations come from HIP events around eager launches of each kernel on the
-stream it runs on.  The CPU oracle is timed on a bounded sample of the same
-workload on the host.
+Inputs are resident in HBM before timing.  Each input copy's step is captured
+into a HIP graph; copies rotate so that one rotation touches well over twice
+the 256 MB Infinity Cache and reads are served by HBM.  Exactly --steps steps
+are timed between two HIP events (after --warmup untimed ones); the median /
+p10 / p90 of the step time come from --dist-steps replays of the all-copies
+step graph, timed one by one.  Per-call
+durations come from HIP events around graph replays of each call alone on the
+stream it runs on.  The CPU oracle is timed on a bounded sample of the headline
+workload on the host's cores.
 
 Prints ONE JSON line.
 """
@@ -39,11 +48,15 @@ BF16_PEAK_TFLOPS = 2500.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=240)
+    p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="csa_decode_128k",
-                   choices=["csa_decode_128k", "hca_decode_1m", "csa_prefill_256k", "pair_1m",
-                            "mxfp4_quantize_keys_128k", "kv_append_decode_128k"])
+    p.add_argument("--workload", default="all",
+                   choices=["all", "csa_decode_128k", "hca_decode_1m", "csa_prefill_256k", "pair_1m",
+                            "mxfp4_quantize_keys_128k", "kv_append_decode_128k"],
+                   help="all (default): the 1M layer pair as the headline line, with the 128K CSA "
+                        "decode, 1M HCA decode and 256K CSA prefill workloads carried in it")
+    p.add_argument("--dist-steps", type=int, default=100,
+                   help="replays of the all-copies step graph, each timed alone, for the median / p10 / p90")
     p.add_argument("--rotate", type=int, default=0, help="input copies (0 = auto)")
     p.add_argument("--indexer", default="auto", choices=["auto", "combined", "fused", "unfused"],
                    help="CSA scoring + selection as one fused call or as csa_indexer_scores then "
@@ -65,9 +78,9 @@ class Kernel:
     """One ABI call of a step: fn(copy), its algorithmic bytes and flops, and the peak
     of the unit its flops run on (MXFP4 or bf16 matrix cores)."""
 
-    def __init__(self, name, fn, nbytes, flops, mfma_peak, src):
+    def __init__(self, name, fn, nbytes, flops, mfma_peak, src, hip=""):
         self.name, self.fn, self.nbytes, self.flops = name, fn, int(nbytes), int(flops)
-        self.mfma_peak, self.src = mfma_peak, src
+        self.mfma_peak, self.src, self.hip = mfma_peak, src, hip
 
     @property
     def bound(self):
@@ -180,7 +193,8 @@ def add_layer(st, h, prefix, indexer="auto", batch_invariant=False):
     # decoding: the compression rides in the indexer top-k call (one launch fewer)
     combined = decode_split and m < 32 and indexer in ("auto", "combined")
     if not combined:
-        st.add(Kernel(name("compress_kv"), f_compress, compress_bytes, 0, BF16_PEAK_TFLOPS, "compress_kv"))
+        st.add(Kernel(name("compress_kv"), f_compress, compress_bytes, 0, BF16_PEAK_TFLOPS, "compress_kv",
+                      "compress_long_kernel" if m >= 32 else "compress_kernel"))
     q_bytes = rows * H * 128 * 4          # bf16 query in + bf16 output
     if wl.kind == "csa":
         k = wl.k
@@ -209,7 +223,8 @@ def add_layer(st, h, prefix, indexer="auto", batch_invariant=False):
             st.add(Kernel(name("compress_indexer_topk"), f_combined,
                           compress_bytes + B * wl.cap * idx_bytes + nvis_sum * 4 + rows * k * 4
                           + rows * wl.H_I * (idx_bytes + 4),
-                          2 * wl.H_I * wl.d_I * nvis_sum, MXFP4_PEAK_TFLOPS, "compress_indexer_topk"))
+                          2 * wl.H_I * wl.d_I * nvis_sum, MXFP4_PEAK_TFLOPS, "compress_indexer_topk",
+                          "indexer_slice_kernel, topk_kernel<true> (with the compression blocks)"))
         elif fused:
             def f_fused(c):
                 csa.csa_indexer_topk(c[p + "qc"], c[p + "qe"], c[p + "w"], c[p + "kc"], c[p + "ke"],
@@ -223,18 +238,19 @@ def add_layer(st, h, prefix, indexer="auto", batch_invariant=False):
                 inter = rows * wl.cap * 2 + nvis_sum * 2
             st.add(Kernel(name("indexer_topk"), f_fused,
                           B * wl.cap * idx_bytes + inter + rows * k * 4 + rows * wl.H_I * (idx_bytes + 4),
-                          2 * wl.H_I * wl.d_I * nvis_sum, MXFP4_PEAK_TFLOPS, "indexer_topk"))
+                          2 * wl.H_I * wl.d_I * nvis_sum, MXFP4_PEAK_TFLOPS, "indexer_topk",
+                          "indexer_slice_kernel, topk_kernel<true>" if decode_split else "indexer_kernel, select_kernel"))
         else:
             st.add(Kernel(name("indexer_scores"), f_indexer,
                           B * wl.cap * idx_bytes + rows * wl.cap * 4 + rows * wl.H_I * (idx_bytes + 4),
-                          2 * wl.H_I * wl.d_I * nvis_sum, MXFP4_PEAK_TFLOPS, "indexer_scores"))
+                          2 * wl.H_I * wl.d_I * nvis_sum, MXFP4_PEAK_TFLOPS, "indexer_scores", "indexer_kernel"))
             st.add(Kernel(name("topk"), f_topk, nvis_sum * 4 + rows * k * 4, 0, BF16_PEAK_TFLOPS,
-                          "topk"))
+                          "topk", "slice_select_kernel, topk_kernel<true>" if decode_split else "topk_kernel"))
         # distinct bytes: every selected entry at most once per sequence, the window rows once
         sel = min(B * wl.cap, rows * k)
         st.add(Kernel(name("sparse_attn"), f_attn,
                       sel * ent + B * wl.L_raw * 512 + q_bytes + rows * k * 4,
-                      4 * H * 128 * rows * (k + W), BF16_PEAK_TFLOPS, "sparse_attn"))
+                      4 * H * 128 * rows * (k + W), BF16_PEAK_TFLOPS, "sparse_attn", attn_hip(rows, False, wl.T_q)))
     else:
         def f_attn(c):
             csa.hca_dense_attn(c[p + "q"], c[p + "ck"], c[p + "cv"], m, c[p + "kw"], c[p + "vw"],
@@ -242,7 +258,16 @@ def add_layer(st, h, prefix, indexer="auto", batch_invariant=False):
                                cv_scale=c[p + "cvs"], out=c[p + "out"], batch_invariant=batch_invariant)
         nv_max = min((wl.q_pos0[0] + wl.T_q) // m, wl.cap)
         st.add(Kernel(name("dense_attn"), f_attn, B * nv_max * ent + B * wl.L_raw * 512 + q_bytes,
-                      4 * H * 128 * (nvis_sum + rows * W), BF16_PEAK_TFLOPS, "dense_attn"))
+                      4 * H * 128 * (nvis_sum + rows * W), BF16_PEAK_TFLOPS, "dense_attn", attn_hip(rows, True, wl.T_q)))
+
+
+def attn_hip(rows, dense, T_q):
+    """HIP kernels of an attention call: key lists are split over blocks (and merged by a
+    second kernel) when the rows alone do not fill the chip; dense chunks of 64 queries or
+    more take the many-query kernel."""
+    if rows < 256:
+        return "attn_kernel, attn_merge_kernel"
+    return "attn_mq_kernel" if dense and T_q >= 64 else "attn_kernel"
 
 
 def layer_config(wl):
@@ -288,7 +313,7 @@ def build_quant(args):
 
     def f_quant(c):
         csa.csa_mxfp4_quantize(c["x"], c["codes"], c["e8m0"])
-    st.add(Kernel("mxfp4_quantize", f_quant, nbytes, 0, BF16_PEAK_TFLOPS, "mxfp4_quantize"))
+    st.add(Kernel("mxfp4_quantize", f_quant, nbytes, 0, BF16_PEAK_TFLOPS, "mxfp4_quantize", "mxfp4_quantize_kernel"))
     R = args.rotate or max(2, math.ceil(600e6 / nbytes))
     base = {"x": torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda(),
             "codes": torch.empty((n, d // 2), dtype=torch.uint8, device="cuda"),
@@ -324,14 +349,16 @@ def build_append(args):
     def f_append(c):
         csa.csa_kv_cache_append(c["k_new"], c["v_new"], c["z_new"], c["pos"], c["rk"], c["rv"], c["rz"], m,
                                 c["ck"], c["cv"], ck_scale=c["cks"], cv_scale=c["cvs"], raw_pos0=c["raw0"])
-    st.add(Kernel("kv_cache_append", f_append, nbytes, 0, BF16_PEAK_TFLOPS, "kv_cache_append"))
+    st.add(Kernel("kv_cache_append", f_append, nbytes, 0, BF16_PEAK_TFLOPS, "kv_cache_append",
+                  "cache_append_short_kernel"))
 
     def f_append_ix(c):
         csa.csa_indexer_key_append(c["ik_new"], c["z_new"], c["pos"], c["irk"], c["rz_i"], m, c["kc"], c["ke"])
     # per sequence: the key row and logit read, 2 copies written, the block's m rows and
     # logits read back, the 64 + 4 B MXFP4 entry written; pos
     nbytes_ix = B * (256 + 4 + 2 * (256 + 4) + m * (256 + 4) + 68 + 4)
-    st.add(Kernel("indexer_key_append", f_append_ix, nbytes_ix, 0, BF16_PEAK_TFLOPS, "indexer_key_append"))
+    st.add(Kernel("indexer_key_append", f_append_ix, nbytes_ix, 0, BF16_PEAK_TFLOPS, "indexer_key_append",
+                  "indexer_key_append_kernel"))
     K = torch.from_numpy(x["K"].view(np.int16)).view(torch.bfloat16).cuda()
     V = torch.from_numpy(x["V"].view(np.int16)).view(torch.bfloat16).cuda()
     Z = torch.from_numpy(x["logits"]).cuda()
@@ -402,13 +429,23 @@ def build(args):
 # --------------------------------------------------------------------------
 # Timing
 
-def time_step(st, steps, warmup, use_graph):
+def time_step(st, steps, warmup, use_graph, dist_steps):
+    """Time exactly `steps` steps after `warmup` untimed ones.
+
+    With graphs, the steps of all R input copies are captured into one graph, and
+    the steps of the first `steps mod R` copies into a second; the timed region
+    replays the first floor(steps / R) times and the second once, so exactly
+    `steps` steps run back to back between the two events, every copy in turn.
+    The distribution comes from `dist_steps` further replays of the R-step graph,
+    each between its own pair of events: per replay, the mean step time over
+    its R steps.  Returns (ms per step, steps, wall seconds, per-step stats)."""
     import torch
     R = len(st.copies)
     for i in range(warmup):
         st.run(st.copies[i % R])
     torch.cuda.synchronize()
-    graph = None
+    n_full, rem = divmod(steps, R)
+    full = part = None
     if use_graph:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -417,24 +454,30 @@ def time_step(st, steps, warmup, use_graph):
                 st.run(c)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
+        full = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(full):
             for c in st.copies:
                 st.run(c)
+        if rem:
+            part = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(part):
+                for c in st.copies[:rem]:
+                    st.run(c)
         torch.cuda.synchronize()
-        for _ in range(2):
-            graph.replay()
+        full.replay()
+        if part is not None:
+            part.replay()
         torch.cuda.synchronize()
-    n_rep = max(1, steps // R) if use_graph else steps
-    done = n_rep * R if use_graph else steps
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record()
     if use_graph:
-        for _ in range(n_rep):
-            graph.replay()
+        for _ in range(n_full):
+            full.replay()
+        if part is not None:
+            part.replay()
     else:
         for i in range(steps):
             st.run(st.copies[i % R])
@@ -442,7 +485,24 @@ def time_step(st, steps, warmup, use_graph):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1)
-    return ms / done, done, wall
+    n = max(dist_steps, 1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record()
+        if use_graph:
+            full.replay()
+        else:
+            for c in st.copies:
+                st.run(c)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 / R for a, b in ev])
+    stats = {"replays": n, "steps_per_replay": R, "median_us": round(float(np.median(us)), 3),
+             "p10_us": round(float(np.percentile(us, 10)), 3), "p90_us": round(float(np.percentile(us, 90)), 3),
+             "how": "mean step time of each replay of the all-copies step graph, each replay between its own "
+                    "pair of HIP events" if use_graph else "mean step time of each eager pass over the copies"}
+    del full, part
+    return ms / steps, steps, wall, stats
 
 
 def time_kernels(st, reps):
@@ -577,8 +637,9 @@ def cpu_baseline(st, budget_s):
     stored caches of one sequence are timed once; indexer, top-k and attention are
     timed per sampled query row (decode layers: one row per sequence, chunk layers:
     rows spread evenly over the chunk).  The step's oracle time is the fixed part
-    plus the mean row time times the step's rows, per layer.  BLAS is held to one
-    thread.  Returns (query-tokens/s, description).
+    plus the mean row time times the step's rows, per layer.  BLAS runs one
+    thread per host core it may run on (os.sched_getaffinity).  Returns
+    (query-tokens/s, description, threads).
     """
     from threadpoolctl import threadpool_limits
     import oracle.attention as oa
@@ -588,7 +649,8 @@ def cpu_baseline(st, budget_s):
     from oracle.formats import bf16_decode
     total, parts = 0.0, []
     share = budget_s / len(st.layers)
-    with threadpool_limits(limits=1):
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
         for prefix, h in st.layers:
             wl, kv, at, ix = h["wl"], h["kv"], h["at"], h.get("ix")
             L, row0, _ = pool_range(wl)
@@ -640,8 +702,15 @@ def cpu_baseline(st, budget_s):
             parts.append(f"{prefix.rstrip('.') or wl.name}: {len(t_rows)} of {n_step_rows} query rows "
                          f"({sum(t_rows):.1f} s) + pooling of the step's blocks")
     desc = ("fp64 numpy oracle (compress, indexer, top-k, attention) on a sample of the same "
-            "workload's query rows, scaled to one step; " + "; ".join(parts))
-    return st.q_tokens / total, desc
+            f"workload's query rows, scaled to one step, BLAS on {cores} threads (its einsum "
+            "reductions run on one); " + "; ".join(parts))
+    return st.q_tokens / total, desc, cores
+
+
+def hip_kernels(st, name):
+    """The HIP kernels a call of this step launches, by the shapes the library dispatches on
+    (for matching the call's event time against rocprofv3 kernel traces)."""
+    return st.kernels[name].hip
 
 
 def roofline_entry(k, avg_us):
@@ -649,6 +718,60 @@ def roofline_entry(k, avg_us):
     if k.bound == "hbm":
         return k.nbytes / s / 1e9, HBM_PEAK_GBS, "GB/s"
     return k.flops / s / 1e12, k.mfma_peak, "TFLOP/s"
+
+
+SUB_WORKLOADS = ["csa_decode_128k", "hca_decode_1m", "csa_prefill_256k"]
+HEADLINE = "pair_1m"
+
+
+def measure(args, workload, with_cpu):
+    """Build one workload, time it (exact steps, distribution, each call) and return its
+    figures as a dict; the device copies are freed before returning."""
+    import torch
+    args.workload = workload
+    st = build(args)
+    ms, done, wall, stats = time_step(st, args.steps, args.warmup, not args.no_graph, args.dist_steps)
+    kt = time_kernels(st, reps=max(10 * len(st.copies), 200))
+    # dominant call = largest share of the step
+    dom = max(st.order, key=lambda n: kt[n]["avg_us"])
+    k = st.kernels[dom]
+    achieved, peak, unit = roofline_entry(k, kt[dom]["avg_us"])
+    roof = {"kernel": dom, "hip_kernels": hip_kernels(st, dom), "bound": k.bound, "achieved": round(achieved, 1),
+            "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+            "traffic": measured_traffic(workload, k),
+            "algorithmic_bytes_per_launch": k.nbytes, "algorithmic_flops_per_launch": k.flops,
+            "avg_launch_us": round(kt[dom]["avg_us"], 3)}
+    kernels = {}
+    for n in st.order:
+        kk = st.kernels[n]
+        a_, p_, u_ = roofline_entry(kk, kt[n]["avg_us"])
+        kernels[n] = {"avg_us": round(kt[n]["avg_us"], 3), "hip_kernels": hip_kernels(st, n),
+                      "algorithmic_bytes": kk.nbytes, "algorithmic_flops": kk.flops, "bound": kk.bound,
+                      "achieved": round(a_, 1), "unit": u_, "frac": round(a_ / p_, 4)}
+    quant = workload == QUANT_WORKLOAD
+    append = workload == APPEND_WORKLOAD
+    unit_v = "key-vectors/s" if quant else "appended-tokens/s" if append else "query-tokens/s"
+    cpu = None
+    if with_cpu:
+        cores = 1
+        if quant:
+            v, desc = cpu_baseline_quant(st)
+        elif append:
+            v, desc = cpu_baseline_append(st, args.cpu_seconds)
+        else:
+            v, desc, cores = cpu_baseline(st, args.cpu_seconds)
+        cpu = {"value": round(v, 4), "unit": unit_v, "cores": cores, "kind": "oracle", "sample": desc}
+    res = {"value": round(st.q_tokens / (ms * 1e-3), 1), "unit": unit_v, "steps": done,
+           "ms_per_step": round(ms, 5), "step_stats": stats, "config": st.config, "roofline": roof,
+           "cpu_baseline": cpu, "kernels": kernels,
+           ("vectors_per_step" if quant else "tokens_per_step" if append else "query_tokens_per_step"): st.q_tokens,
+           "rotation_copies": len(st.copies), "graph": not args.no_graph, "wall_s_timed_region": round(wall, 4)}
+    st.copies = []
+    del st
+    import gc
+    gc.collect()
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -670,48 +793,28 @@ def main():
             c.copy_(a)
         torch.cuda.synchronize()
         del a, c
-    st = build(args)
-    ms, done, wall = time_step(st, args.steps, args.warmup, not args.no_graph)
-    kt = time_kernels(st, reps=max(10 * len(st.copies), 200))
-    # dominant call = largest share of the step
-    dom = max(st.order, key=lambda n: kt[n]["avg_us"])
-    k = st.kernels[dom]
-    achieved, peak, unit = roofline_entry(k, kt[dom]["avg_us"])
-    roof = {"kernel": dom, "bound": k.bound, "achieved": round(achieved, 1), "peak": peak,
-            "unit": unit, "frac": round(achieved / peak, 4),
-            "traffic": measured_traffic(args.workload, k),
-            "algorithmic_bytes_per_launch": k.nbytes, "algorithmic_flops_per_launch": k.flops,
-            "avg_launch_us": round(kt[dom]["avg_us"], 3)}
-    kernels = {}
-    for n in st.order:
-        kk = st.kernels[n]
-        a_, p_, u_ = roofline_entry(kk, kt[n]["avg_us"])
-        kernels[n] = {"avg_us": round(kt[n]["avg_us"], 3), "algorithmic_bytes": kk.nbytes,
-                      "algorithmic_flops": kk.flops, "bound": kk.bound, "achieved": round(a_, 1),
-                      "unit": u_, "frac": round(a_ / p_, 4)}
-    quant = args.workload == QUANT_WORKLOAD
-    append = args.workload == APPEND_WORKLOAD
-    unit = "key-vectors/s" if quant else "appended-tokens/s" if append else "query-tokens/s"
-    cpu = None
-    if not args.no_cpu_baseline:
-        if quant:
-            v, desc = cpu_baseline_quant(st)
-        elif append:
-            v, desc = cpu_baseline_append(st, args.cpu_seconds)
-        else:
-            v, desc = cpu_baseline(st, args.cpu_seconds)
-        cpu = {"value": round(v, 4), "unit": unit, "cores": 1, "kind": "oracle", "sample": desc}
-    q_per_s = st.q_tokens / (ms * 1e-3)
-    metric = ("MXFP4 quantisation of the indexer keys, key-vectors/s; % HBM roofline" if quant else
-              "decode KV cache append (window ring + block pooling), appended tokens/s" if append else METRIC)
-    line = {"metric": metric, "value": round(q_per_s, 1), "unit": unit, "n_gpus": 1,
-            "steps": done, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+    with_cpu = not args.no_cpu_baseline
+    subs = {}
+    if args.workload == "all":
+        for w in SUB_WORKLOADS:
+            print(f"# {w}", file=sys.stderr, flush=True)
+            subs[w] = measure(args, w, False)
+        print(f"# {HEADLINE}", file=sys.stderr, flush=True)
+        head, name = measure(args, HEADLINE, with_cpu), HEADLINE
+    else:
+        name = args.workload
+        head = measure(args, name, with_cpu)
+    metric = ("MXFP4 quantisation of the indexer keys, key-vectors/s; % HBM roofline" if name == QUANT_WORKLOAD else
+              "decode KV cache append (window ring + block pooling), appended tokens/s" if name == APPEND_WORKLOAD
+              else METRIC)
+    line = {"metric": metric, "value": head["value"], "unit": head["unit"], "n_gpus": 1,
+            "steps": head["steps"], "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "mxfp4+bf16", "data": "synthetic (seeded; shapes of the pages' 128K-1M contexts)",
-            "config": st.config, "roofline": roof, "cpu_baseline": cpu, "kernels": kernels,
-            ("vectors_per_step" if quant else "tokens_per_step" if append else "query_tokens_per_step"): st.q_tokens,
-            "rotation_copies": len(st.copies),
-            "graph": not args.no_graph, "wall_s_timed_region": round(wall, 4)}
+            "config": head["config"], "roofline": head["roofline"], "cpu_baseline": head["cpu_baseline"]}
+    line.update({k: v for k, v in head.items() if k not in line and k not in ("value", "unit")})
+    if subs:
+        line["workloads"] = subs
     print(json.dumps(line), flush=True)
 
 
