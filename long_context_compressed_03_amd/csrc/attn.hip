@@ -241,16 +241,18 @@ struct LdsBf16 {
   // A wave's writes (16 row groups x 4 key pairs) then fall in distinct
   // banks and the 8-byte reads of the P*V products take two passes.
   uint16_t Vt[kHeadDim / 8][kVGroup];
+  // per key: K scale x logit scale, V scale, and 0 (present) or -inf (absent:
+  // its K row is zeros, so logit = product * sk + bias needs no branch)
   float sk[kNK];
   float sv[kNK];
-  int valid[kNK];
+  float bias[kNK];
 };
 struct LdsF32 {
   float K[kNK][kFRow];
   float V[kNK][kFRow];
   float sk[kNK];
   float sv[kNK];
-  int valid[kNK];
+  float bias[kNK];
 };
 template <int kIO>
 using LdsChunk = typename std::conditional<kIO == CSA_BF16, LdsBf16, LdsF32>::type;
@@ -331,7 +333,7 @@ CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr, float sk_mul) {
       const bool scaled = kCKV == CSA_FP8_E4M3 && pr.src[e] == 1;
       s.sk[2 * kp + e] = (scaled ? pr.sk[e] : 1.f) * sk_mul;
       s.sv[2 * kp + e] = scaled ? pr.sv[e] : 1.f;
-      s.valid[2 * kp + e] = pr.src[e] != 0;
+      s.bias[2 * kp + e] = pr.src[e] != 0 ? 0.f : -INFINITY;
     }
   }
 }
@@ -348,11 +350,12 @@ CSA_DEV void logits_tile(const LdsChunk<kIO>& s, const u32x4* qb, const float* q
 #pragma unroll
     for (int ks = 0; ks < 32; ++ks) acc = mfma_f32(s.K[kt * 16 + col][ks * 4 + g], qf[ks], acc);
   }
+  // keys kt*16 + 4g .. +3: one 16-byte read each for the scales and biases,
+  // no branch (an absent key's product is 0, and 0 * sk + -inf = -inf)
+  const v4f skv = *reinterpret_cast<const v4f*>(&s.sk[kt * 16 + 4 * g]);
+  const v4f bv = *reinterpret_cast<const v4f*>(&s.bias[kt * 16 + 4 * g]);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int kk = kt * 16 + 4 * g + r;
-    x[r] = s.valid[kk] ? acc[r] * s.sk[kk] : -INFINITY;
-  }
+  for (int r = 0; r < 4; ++r) x[r] = __builtin_fmaf(acc[r], skv[r], bv[r]);
 }
 
 template <int kIO>
@@ -476,12 +479,13 @@ void attn_kernel(AttnArgs a) {
         // P as bf16 hi + lo (two passes): a single bf16 rounding of P would
         // cost 2^-9 of |V| per output, beyond the bf16 bound for large V
         uint32_t ph[4], pl[4];
+        const v4f svv[2] = {*reinterpret_cast<const v4f*>(&s.sv[(2 * kh) * 16 + 4 * g]),
+                            *reinterpret_cast<const v4f*>(&s.sv[(2 * kh + 1) * 16 + 4 * g])};
 #pragma unroll
         for (int h2 = 0; h2 < 4; ++h2) {
           const int kk = h2 >> 1;
           const int r0 = (h2 & 1) * 2;
-          const int key = (2 * kh + kk) * 16 + 4 * g + r0;
-          split_bf16x2(p[kk][r0] * s.sv[key], p[kk][r0 + 1] * s.sv[key + 1], &ph[h2], &pl[h2]);
+          split_bf16x2(p[kk][r0] * svv[kk][r0], p[kk][r0 + 1] * svv[kk][r0 + 1], &ph[h2], &pl[h2]);
         }
         const u32x4 pbh = {ph[0], ph[1], ph[2], ph[3]};
         const u32x4 pbl = {pl[0], pl[1], pl[2], pl[3]};
@@ -612,7 +616,7 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict_
   const long base = qrow * n_splits * H + head; // slot of split 0; split x adds x*H
   const int half = lane >> 5;
   const int d4 = lane & 31;
-  constexpr int kU = 8;
+  constexpr int kU = 16;   // 32 splits per batch of loads
   auto load_batch = [&](int x0, v4f (&pv)[kU]) {
 #pragma unroll
     for (int y = 0; y < kU; ++y) {
@@ -650,6 +654,194 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict_
     const float inv = L > 0.f ? 1.f / L : 0.f;
     store_out4<kIO>(out, hid, d4, acc * inv);
     if (lse && d4 == 0) lse[hid] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------- decode rows --
+// Few query rows over long key lists (decoding).  A block takes one split of
+// a row's key list (at most kDecChunks chunks, 256 keys) and one group of
+// kT 16-head tiles; all of the split's index and row loads are issued at
+// once, the whole split is staged in LDS behind one barrier, and the chip is
+// filled by splits and head groups rather than by a pipeline of chunks inside
+// a block.  The G head groups of one split run on the same XCD (block b runs
+// on XCD b % 8), so G-1 of the G gathers of each row are served by that
+// XCD's L2: a split count G times smaller for the same number of blocks, and
+// G times fewer partial outputs to write and merge.
+// Waves: tile slot w % kT (heads (group * kT + w % kT) * 16 ..), key part
+// p = w / kT of kP = 8 / kT parts: the 32-key steps s = p, p + kP, ... of the
+// split.  The parts fold into part 0 through LDS in part order, then the
+// block writes its row's output (one split) or its split's partial state.
+constexpr int kDecChunks = 4;
+
+struct DecFold {
+  float o[7][16][kHeadDim + 4];   // parts 1 .. kP-1 of one tile slot at a time
+  float m[7][16];
+  float l[7][16];
+};
+
+template <int kCKV, bool kDense, bool kVarlen>
+__global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a, int kT, int n_groups, long n_units) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  LdsBf16* ch = reinterpret_cast<LdsBf16*>(smem);
+
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int kP = 8 / kT;
+  const int ts = wid % kT;
+  const int part = wid / kT;
+
+  // block -> (unit = query row x split, head group); the groups of a unit share an XCD
+  const long bid = blockIdx.x;
+  const int xcd = int(bid & 7);
+  const long slot = bid >> 3;
+  const int grp = int(slot % n_groups);
+  const long unit = (slot / n_groups) * 8 + xcd;
+  if (unit >= n_units) return;
+  const long qrow = unit / a.n_splits;
+  const int split = int(unit - qrow * a.n_splits);
+  int b, t;
+  if constexpr (kVarlen) {
+    b = a.row_seq[qrow];
+    t = a.row_pos[qrow];
+  } else {
+    b = int(qrow / a.T_q);
+    t = a.q_pos0[b] + int(qrow - long(b) * a.T_q);
+  }
+  const int raw0 = a.W > 0 ? a.raw_pos0[b] : 0;
+  const int j_begin = split * a.split_len;
+  const int j_end = min(j_begin + a.split_len, a.n_list);
+  const int n_keys = j_end - j_begin;
+
+  // every index, then every row of the split in flight (empty slots read a
+  // dummy address; see gather_slot)
+  int e[kDecChunks][2];
+#pragma unroll
+  for (int c = 0; c < kDecChunks; ++c) load_idx<kDense>(a, e[c], qrow, j_begin + c * kNK, j_end);
+  Pre<CSA_BF16> pr[kDecChunks];
+#pragma unroll
+  for (int c = 0; c < kDecChunks; ++c) prefetch<CSA_BF16, kCKV, kDense>(a, pr[c], e[c], b, t, raw0, j_begin + c * kNK, j_end);
+  const int tile = grp * kT + ts;
+  const int head = tile * 16 + col;
+  u32x4 qb[4];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (qrow * a.H + head) * kHeadDim;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qb[ks] = *reinterpret_cast<const u32x4*>(qp + ks * 32 + g * 8);
+  }
+  // chunks past the split's keys are not staged (the LDS holds only the split)
+#pragma unroll
+  for (int c = 0; c < kDecChunks; ++c)
+    if (c * kNK < n_keys) store_chunk<CSA_BF16, kCKV>(ch[c], pr[c], a.sm_log2);
+  __syncthreads();
+
+  v4f o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  // 32-key steps of this wave's part; steps past the split's keys are skipped
+  for (int st = part; st * 32 < n_keys; st += kP) {
+    const LdsBf16& s = ch[st >> 1];
+    const int kh = st & 1;
+    float x[2][4];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) logits_tile<CSA_BF16>(s, qb, nullptr, 2 * kh + kk, col, g, x[kk]);
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cmax = fmaxf(cmax, x[kk][r]);
+    cmax = column_max(cmax);
+    // lazy running max, as in attn_kernel
+    const bool grow = cmax > m_run + 8.f;
+    const float m_new = grow ? cmax : m_run;
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    if (__ballot(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    }
+    m_run = m_new;
+    float p[2][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[kk][r] = __builtin_amdgcn_exp2f(x[kk][r] - m_use);
+        psum += p[kk][r];
+      }
+    l_run += psum;
+    uint32_t ph[4], pl[4];
+    const v4f svv[2] = {*reinterpret_cast<const v4f*>(&s.sv[(2 * kh) * 16 + 4 * g]),
+                        *reinterpret_cast<const v4f*>(&s.sv[(2 * kh + 1) * 16 + 4 * g])};
+#pragma unroll
+    for (int h2 = 0; h2 < 4; ++h2) {
+      const int kk = h2 >> 1;
+      const int r0 = (h2 & 1) * 2;
+      split_bf16x2(p[kk][r0] * svv[kk][r0], p[kk][r0 + 1] * svv[kk][r0 + 1], &ph[h2], &pl[h2]);
+    }
+    const u32x4 pbh = {ph[0], ph[1], ph[2], ph[3]};
+    const u32x4 pbl = {pl[0], pl[1], pl[2], pl[3]};
+    const int k0 = kh * 32 + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint16_t* vt = &s.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0];   // row dt*16 + col
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(vt);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + 16);
+      const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+      o[dt] = mfma_k32(vf, pbh, o[dt]);
+      o[dt] = mfma_k32(vf, pbl, o[dt]);
+    }
+  }
+  float l_tot = column_sum(l_run);
+
+  // fold parts 1 .. kP-1 into part 0, in part order
+  DecFold& fd = *reinterpret_cast<DecFold*>(smem);
+  for (int ts0 = 0; ts0 < kT; ++ts0) {
+    __syncthreads();
+    if (ts == ts0 && part > 0) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<v4f*>(&fd.o[part - 1][col][dt * 16 + 4 * g]) = o[dt];
+      if (g == 0) {
+        fd.m[part - 1][col] = m_run;
+        fd.l[part - 1][col] = l_tot;
+      }
+    }
+    __syncthreads();
+    if (ts == ts0 && part == 0) {
+      for (int q = 1; q < kP; ++q) {
+        const float m1 = fd.m[q - 1][col];
+        const float M = fmaxf(m_run, m1);
+        const float Mu = M == -INFINITY ? 0.f : M;
+        const float f0 = __builtin_amdgcn_exp2f(m_run - Mu);
+        const float f1 = __builtin_amdgcn_exp2f(m1 - Mu);
+        l_tot = l_tot * f0 + fd.l[q - 1][col] * f1;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          o[dt] = o[dt] * f0 + *reinterpret_cast<const v4f*>(&fd.o[q - 1][col][dt * 16 + 4 * g]) * f1;
+        m_run = M;
+      }
+    }
+  }
+  if (part > 0) return;
+  if (a.n_splits == 1) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const long orow = qrow * a.H + head;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) store_out4<CSA_BF16>(a.out, orow, dt * 4 + g, o[dt] * inv);
+    if (a.lse && g == 0) a.lse[orow] = l_tot > 0.f ? m_run * kLn2 + logf(l_tot) : -INFINITY;
+  } else {
+    const long pslot = (qrow * a.n_splits + split) * a.H + head;
+    float* po = a.part_o + pslot * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) __builtin_nontemporal_store(o[dt], reinterpret_cast<v4f*>(po + dt * 16 + 4 * g));
+    if (g == 0) {
+      __builtin_nontemporal_store(m_run, &a.part_ml[pslot * 2]);
+      __builtin_nontemporal_store(l_tot, &a.part_ml[pslot * 2 + 1]);
+    }
   }
 }
 
@@ -774,16 +966,21 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
         acc[0] = mfma_k32(kf, qb[0][ks], acc[0]);
         acc[1] = mfma_k32(kf, qb[1][ks], acc[1]);
       }
+      // keys kt*16 + 4g .. +3 (16-byte reads); a key the query does not see
+      // gets -inf as a selected bias, with no branch
+      const u32x4 vb = *reinterpret_cast<const u32x4*>(&s.vis[kt * 16 + 4 * g]);
+      const v4f scl = *reinterpret_cast<const v4f*>(&s.c.sk[kt * 16 + 4 * g]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int kk = kt * 16 + 4 * g + r;
-        const bool vis = (s.vis[kk] >> qi) & 1u;
-        const float scl = s.c.sk[kk];
+        const float bias = ((vb[r] >> qi) & 1u) ? 0.f : -INFINITY;
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht) x[ht][kt][r] = vis ? acc[ht][r] * scl : -INFINITY;
+        for (int ht = 0; ht < 2; ++ht) x[ht][kt][r] = __builtin_fmaf(acc[ht][r], scl[r], bias);
       }
     }
     uint32_t pw[2][2][4], pl[2][2][4];   // [ht][32-key step][pair]: P as bf16 hi + lo
+    v4f svv[4];                          // V scales of keys kt*16 + 4g .. +3
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) svv[kt] = *reinterpret_cast<const v4f*>(&s.c.sv[kt * 16 + 4 * g]);
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
       float cmax = -INFINITY;
@@ -821,8 +1018,7 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
         for (int h2 = 0; h2 < 4; ++h2) {
           const int kt = 2 * st + (h2 >> 1);
           const int r0 = (h2 & 1) * 2;
-          const int key = kt * 16 + 4 * g + r0;
-          split_bf16x2(p[kt][r0] * s.c.sv[key], p[kt][r0 + 1] * s.c.sv[key + 1], &pw[ht][st][h2],
+          split_bf16x2(p[kt][r0] * svv[kt][r0], p[kt][r0 + 1] * svv[kt][r0 + 1], &pw[ht][st][h2],
                        &pl[ht][st][h2]);
         }
     }
@@ -898,6 +1094,67 @@ Plan make_plan(long rows, int n_list, bool invariant) {
   return p;
 }
 
+// Decode plan (few rows, bf16 queries): (splits S, split length, head groups G)
+// for attn_decode_kernel.  A split holds at most kDecChunks chunks; the chip
+// holds 256 blocks per round (fewer LDS bytes per block: more).  Among G in
+// {1, 2, 4} (16-head tiles per block <= 4) the plan with the least estimated
+// time wins: the unique rows over HBM (~6.5 TB/s), a block's rows at a CU's
+// rate when its head groups share them through L2 (~95 GB/s; measured), and
+// the partial outputs written and read back by the merge (~5 TB/s each way).
+// The estimate depends on the shape only (rows, keys, heads), never on data.
+struct DecodePlan {
+  int n_splits = 0, split_len = 0, groups = 0, kT = 0, chunks = 0;
+  long units = 0, blocks = 0;
+  size_t lds = 0;
+};
+
+constexpr long kDecodeMaxRows = 64;
+
+size_t decode_lds_bytes(int chunks) {
+  const size_t c = size_t(chunks) * sizeof(LdsBf16);
+  return c > sizeof(DecFold) ? c : sizeof(DecFold);
+}
+
+DecodePlan make_decode_plan(long rows, int n_list, int H) {
+  DecodePlan best{};
+  double best_t = 1e30;
+  const int tiles = H / 16;
+  const long max_len = long(kDecChunks) * kNK;
+  const double row_bytes = 512.0;   // bf16 K + V rows (fp8 entries move half: the choice is the same)
+  for (int G = 4; G >= 1; G >>= 1) {
+    if (tiles % G || tiles / G > 4) continue;
+    long S = max((256 + rows * G - 1) / (rows * G), (long(n_list) + max_len - 1) / max_len);
+    long len = (n_list + S - 1) / S;
+    len = (len + 31) / 32 * 32;
+    S = (n_list + len - 1) / len;
+    const int chunks = int((len + kNK - 1) / kNK);
+    const size_t lds = decode_lds_bytes(chunks);
+    const long per_cu = max(1L, long((160 * 1024) / lds));
+    const long units = rows * S;
+    const long blocks = (units + 7) / 8 * 8 * G;
+    const double rounds = double((blocks + 256 * per_cu - 1) / (256 * per_cu));
+    const double t_read = max(double(rows) * n_list * row_bytes / 6.5e6, double(len) * row_bytes / 95e3);
+    const double partial = S > 1 ? double(rows) * S * H * (kHeadDim + 2) * 4 : 0.0;
+    const double t = rounds * t_read + 2.0 * partial / 5e6 + (S > 1 ? 1.65 : 0.0);
+    if (t < best_t) {
+      best_t = t;
+      best.n_splits = int(S);
+      best.split_len = int(len);
+      best.groups = G;
+      best.kT = tiles / G;
+      best.chunks = chunks;
+      best.units = units;
+      best.blocks = blocks;
+      best.lds = lds;
+    }
+  }
+  return best;
+}
+
+bool use_decode(int io_dtype, long rows, bool invariant) {
+  return !invariant && io_dtype == CSA_BF16 && rows <= kDecodeMaxRows;
+}
+
 size_t plan_ws_bytes(const Plan& p, long rows, int H) {
   if (p.n_splits <= 1) return 0;
   const size_t slots = size_t(rows) * p.n_splits * H;
@@ -971,11 +1228,52 @@ csa_status_t tiles_for(const AttnArgs& a, int io_dtype, int ckv_dtype, long bloc
   return err == hipSuccess ? CSA_OK : CSA_EHIP;
 }
 
+template <int kCKV, bool kDense, bool kVarlen>
+hipError_t launch_decode(const AttnArgs& a, const DecodePlan& d, hipStream_t st) {
+  auto fn = attn_decode_kernel<kCKV, kDense, kVarlen>;
+  if (hipError_t e = csa_lds_opt_in(reinterpret_cast<const void*>(fn), d.lds); e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, dim3(unsigned(d.blocks)), dim3(kThreads), d.lds, st, a, d.kT, d.groups, d.units);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_splits == 1) return e;
+  const long heads = d.units / a.n_splits * a.H;
+  hipLaunchKernelGGL(attn_merge_kernel<CSA_BF16>, dim3(unsigned(heads)), dim3(64), 0, st, a.part_ml, a.part_o,
+                     a.n_splits, a.H, a.out, a.lse);
+  return hipGetLastError();
+}
+
+// Decode rows: bf16 queries over bf16 or fp8 entries.
+template <bool kDense>
+csa_status_t run_decode(AttnArgs a, int ckv_dtype, long rows, void* ws, size_t ws_size, hipStream_t st) {
+  const DecodePlan d = make_decode_plan(rows, a.n_list, a.H);
+  a.n_splits = d.n_splits;
+  a.split_len = d.split_len;
+  Plan p{};
+  p.n_splits = d.n_splits;
+  const size_t need = plan_ws_bytes(p, rows, a.H);
+  if (need > 0) {
+    if (!ws || ws_size < need) return CSA_EWORKSPACE;
+    char* w = static_cast<char*>(ws);
+    const size_t slots = size_t(rows) * d.n_splits * a.H;
+    const size_t ml = ((slots * 2 * 4 + 255) / 256) * 256;
+    a.part_ml = reinterpret_cast<float*>(w);
+    a.part_o = reinterpret_cast<float*>(w + ml);
+  }
+  hipError_t err;
+  if (ckv_dtype == CSA_FP8_E4M3)
+    err = a.row_seq ? launch_decode<CSA_FP8_E4M3, kDense, true>(a, d, st) : launch_decode<CSA_FP8_E4M3, kDense, false>(a, d, st);
+  else if (ckv_dtype == CSA_BF16)
+    err = a.row_seq ? launch_decode<CSA_BF16, kDense, true>(a, d, st) : launch_decode<CSA_BF16, kDense, false>(a, d, st);
+  else
+    return CSA_ENOTSUP;
+  return err == hipSuccess ? CSA_OK : CSA_EHIP;
+}
+
 template <bool kDense>
 csa_status_t run_attn(AttnArgs a, int io_dtype, int ckv_dtype, int B, void* ws, size_t ws_size, hipStream_t st,
                       bool invariant) {
   const long rows = long(B) * a.T_q;
   if (rows == 0) return CSA_OK;
+  if (use_decode(io_dtype, rows, invariant)) return run_decode<kDense>(a, ckv_dtype, rows, ws, ws_size, st);
   const Plan p = make_plan(rows, a.n_list, invariant);
   if (p.blocks > 0x7FFFFFFFL) return CSA_ENOTSUP;
   a.n_splits = p.n_splits;
@@ -1019,8 +1317,16 @@ csa_status_t check_common(const void* q, int io_dtype, const void* ck, const voi
 
 }  // namespace
 
+// Workspace for either kernel family (the queries' type picks one; the size
+// covers both).
 size_t csa_attn_workspace_size(long rows, int H, int n_list, bool invariant) {
-  return plan_ws_bytes(make_plan(rows, n_list, invariant), rows, H);
+  size_t need = plan_ws_bytes(make_plan(rows, n_list, invariant), rows, H);
+  if (use_decode(CSA_BF16, rows, invariant) && rows > 0) {
+    Plan p{};
+    p.n_splits = make_decode_plan(rows, n_list, H).n_splits;
+    need = max(need, plan_ws_bytes(p, rows, H));
+  }
+  return need;
 }
 
 namespace {
