@@ -343,9 +343,11 @@ template <int kIO>
 CSA_DEV void logits_tile(const LdsChunk<kIO>& s, const u32x4* qb, const float* qf, int kt, int col, int g, float* x) {
   v4f acc = {0.f, 0.f, 0.f, 0.f};
   if constexpr (kIO == CSA_BF16) {
+    u32x4 kf[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      acc = mfma_k32(*reinterpret_cast<const u32x4*>(&s.K[kt * 16 + col][ks * 32 + g * 8]), qb[ks], acc);
+    for (int ks = 0; ks < 4; ++ks) kf[ks] = *reinterpret_cast<const u32x4*>(&s.K[kt * 16 + col][ks * 32 + g * 8]);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) acc = mfma_k32(kf[ks], qb[ks], acc);
   } else {
 #pragma unroll
     for (int ks = 0; ks < 32; ++ks) acc = mfma_f32(s.K[kt * 16 + col][ks * 4 + g], qf[ks], acc);
@@ -490,14 +492,31 @@ void attn_kernel(AttnArgs a) {
         const u32x4 pbh = {ph[0], ph[1], ph[2], ph[3]};
         const u32x4 pbl = {pl[0], pl[1], pl[2], pl[3]};
         const int k0 = kh * 32 + 4 * g;
+        if constexpr (kHTW == 1 && kDepth == 1) {
+          // 128-VGPR budget (two blocks per CU): one V^T fragment at a time
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          const uint16_t* vt = &s.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0];   // row dt*16 + col
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vt);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + 16);
-          const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-          o[ht][dt] = mfma_k32(vf, pbh, o[ht][dt]);
-          o[ht][dt] = mfma_k32(vf, pbl, o[ht][dt]);
+          for (int dt = 0; dt < 8; ++dt) {
+            const uint16_t* vt = &s.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0];   // row dt*16 + col
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(vt);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + 16);
+            const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+            o[ht][dt] = mfma_k32(vf, pbh, o[ht][dt]);
+            o[ht][dt] = mfma_k32(vf, pbl, o[ht][dt]);
+          }
+        } else {
+          // every V^T fragment requested first, then the hi products, then the lo ones
+          u32x4 vf[8];
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            const uint16_t* vt = &s.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0];   // row dt*16 + col
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(vt);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + 16);
+            vf[dt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          }
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) o[ht][dt] = mfma_k32(vf[dt], pbh, o[ht][dt]);
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) o[ht][dt] = mfma_k32(vf[dt], pbl, o[ht][dt]);
         }
       } else {
 #pragma unroll
@@ -674,13 +693,14 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict_
 constexpr int kDecChunks = 4;
 
 struct DecFold {
-  float o[7][16][kHeadDim + 4];   // parts 1 .. kP-1 of one tile slot at a time
+  float o[7][16][kHeadDim + 4];   // parts 1 .. kP-1 of every tile slot (kT * (kP - 1) <= 7)
   float m[7][16];
   float l[7][16];
 };
 
 template <int kCKV, bool kDense, bool kVarlen>
-__global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a, int kT, int n_groups, long n_units) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void attn_decode_kernel(AttnArgs a, int kT, int n_groups, long n_units) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   LdsBf16* ch = reinterpret_cast<LdsBf16*>(smem);
 
@@ -715,13 +735,17 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a, int k
   const int n_keys = j_end - j_begin;
 
   // every index, then every row of the split in flight (empty slots read a
-  // dummy address; see gather_slot)
+  // dummy address; see gather_slot).  Chunks past the split issue nothing: the
+  // branch is uniform over the block, so no load sits under a divergent mask.
+  const int n_ch = (n_keys + kNK - 1) / kNK;
   int e[kDecChunks][2];
 #pragma unroll
-  for (int c = 0; c < kDecChunks; ++c) load_idx<kDense>(a, e[c], qrow, j_begin + c * kNK, j_end);
+  for (int c = 0; c < kDecChunks; ++c)
+    if (c < n_ch) load_idx<kDense>(a, e[c], qrow, j_begin + c * kNK, j_end);
   Pre<CSA_BF16> pr[kDecChunks];
 #pragma unroll
-  for (int c = 0; c < kDecChunks; ++c) prefetch<CSA_BF16, kCKV, kDense>(a, pr[c], e[c], b, t, raw0, j_begin + c * kNK, j_end);
+  for (int c = 0; c < kDecChunks; ++c)
+    if (c < n_ch) prefetch<CSA_BF16, kCKV, kDense>(a, pr[c], e[c], b, t, raw0, j_begin + c * kNK, j_end);
   const int tile = grp * kT + ts;
   const int head = tile * 16 + col;
   u32x4 qb[4];
@@ -733,7 +757,7 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a, int k
   // chunks past the split's keys are not staged (the LDS holds only the split)
 #pragma unroll
   for (int c = 0; c < kDecChunks; ++c)
-    if (c * kNK < n_keys) store_chunk<CSA_BF16, kCKV>(ch[c], pr[c], a.sm_log2);
+    if (c < n_ch) store_chunk<CSA_BF16, kCKV>(ch[c], pr[c], a.sm_log2);
   __syncthreads();
 
   v4f o[8];
@@ -786,44 +810,50 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a, int k
     const u32x4 pbh = {ph[0], ph[1], ph[2], ph[3]};
     const u32x4 pbl = {pl[0], pl[1], pl[2], pl[3]};
     const int k0 = kh * 32 + 4 * g;
+    // every V^T fragment requested first, then the 8 hi products, then the 8
+    // lo ones (no product waits on the one before it)
+    u32x4 vf[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const uint16_t* vt = &s.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0];   // row dt*16 + col
       const u32x2 lo = *reinterpret_cast<const u32x2*>(vt);
       const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + 16);
-      const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-      o[dt] = mfma_k32(vf, pbh, o[dt]);
-      o[dt] = mfma_k32(vf, pbl, o[dt]);
+      vf[dt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] = mfma_k32(vf[dt], pbh, o[dt]);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] = mfma_k32(vf[dt], pbl, o[dt]);
   }
   float l_tot = column_sum(l_run);
 
-  // fold parts 1 .. kP-1 into part 0, in part order
+  // fold parts 1 .. kP-1 into part 0, in part order: every part > 0 of every
+  // tile slot parks its state at once (kT * (kP - 1) <= 7 slots), one barrier
   DecFold& fd = *reinterpret_cast<DecFold*>(smem);
-  for (int ts0 = 0; ts0 < kT; ++ts0) {
-    __syncthreads();
-    if (ts == ts0 && part > 0) {
+  __syncthreads();
+  if (part > 0) {
+    const int f = ts * (kP - 1) + part - 1;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<v4f*>(&fd.o[part - 1][col][dt * 16 + 4 * g]) = o[dt];
-      if (g == 0) {
-        fd.m[part - 1][col] = m_run;
-        fd.l[part - 1][col] = l_tot;
-      }
+    for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<v4f*>(&fd.o[f][col][dt * 16 + 4 * g]) = o[dt];
+    if (g == 0) {
+      fd.m[f][col] = m_run;
+      fd.l[f][col] = l_tot;
     }
-    __syncthreads();
-    if (ts == ts0 && part == 0) {
-      for (int q = 1; q < kP; ++q) {
-        const float m1 = fd.m[q - 1][col];
-        const float M = fmaxf(m_run, m1);
-        const float Mu = M == -INFINITY ? 0.f : M;
-        const float f0 = __builtin_amdgcn_exp2f(m_run - Mu);
-        const float f1 = __builtin_amdgcn_exp2f(m1 - Mu);
-        l_tot = l_tot * f0 + fd.l[q - 1][col] * f1;
+  }
+  __syncthreads();
+  if (part == 0) {
+    for (int q = 1; q < kP; ++q) {
+      const int f = ts * (kP - 1) + q - 1;
+      const float m1 = fd.m[f][col];
+      const float M = fmaxf(m_run, m1);
+      const float Mu = M == -INFINITY ? 0.f : M;
+      const float f0 = __builtin_amdgcn_exp2f(m_run - Mu);
+      const float f1 = __builtin_amdgcn_exp2f(m1 - Mu);
+      l_tot = l_tot * f0 + fd.l[f][col] * f1;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          o[dt] = o[dt] * f0 + *reinterpret_cast<const v4f*>(&fd.o[q - 1][col][dt * 16 + 4 * g]) * f1;
-        m_run = M;
-      }
+      for (int dt = 0; dt < 8; ++dt)
+        o[dt] = o[dt] * f0 + *reinterpret_cast<const v4f*>(&fd.o[f][col][dt * 16 + 4 * g]) * f1;
+      m_run = M;
     }
   }
   if (part > 0) return;
@@ -859,6 +889,10 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(AttnArgs a, int k
 struct LdsMQ {
   LdsBf16 c;
   uint32_t vis[kNK];   // bit q: the key is visible to the block's query q
+  // each wave's query fragments (2 head tiles x 4 contraction steps, one
+  // 16-byte word per lane), re-read for every chunk instead of held in
+  // registers through the P*V products
+  u32x4 q[8][2][4][64];
 };
 
 // Gather items of chunk jc of the union list, and for each key the mask of
@@ -921,13 +955,12 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
   const int t0 = pos0 + i0;
   const int n_q = i_last - i0 + 1;
 
-  u32x4 qb[2][4];
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     const int head = ((wid % kWPQ) * 2 + ht) * 16 + col;
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((long(b) * a.T_q + (q_ok ? i : i0)) * a.H + head) * kHeadDim;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qb[ht][ks] = *reinterpret_cast<const u32x4*>(qp + ks * 32 + g * 8);
+    for (int ks = 0; ks < 4; ++ks) s.q[wid][ht][ks][lane] = *reinterpret_cast<const u32x4*>(qp + ks * 32 + g * 8);
   }
   v4f o[2][8];
   float m_run[2], l_run[2];
@@ -955,32 +988,39 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
     __syncthreads();
     if (j0 + 2 * kNK < n_list)
       prefetch_mq<kCKV>(a, prc, tgc, b, raw0, nv_max, p_lo, n_list, j0 + 2 * kNK, t0, n_q);
-    // S^T for the 4 key tiles x 2 head tiles; K fragments shared by both tiles
+    // S^T for the 4 key tiles x 2 head tiles; K fragments shared by both tiles,
+    // contraction steps outermost so only one step's query fragments are live
     float x[2][4][4];
+    {
+      v4f acc[4][2];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      v4f acc[2] = {v4f{0.f, 0.f, 0.f, 0.f}, v4f{0.f, 0.f, 0.f, 0.f}};
+      for (int kt = 0; kt < 4; ++kt) acc[kt][0] = acc[kt][1] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(&s.c.K[kt * 16 + col][ks * 32 + g * 8]);
-        acc[0] = mfma_k32(kf, qb[0][ks], acc[0]);
-        acc[1] = mfma_k32(kf, qb[1][ks], acc[1]);
+        const u32x4 q0 = s.q[wid][0][ks][lane];
+        const u32x4 q1 = s.q[wid][1][ks][lane];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(&s.c.K[kt * 16 + col][ks * 32 + g * 8]);
+          acc[kt][0] = mfma_k32(kf, q0, acc[kt][0]);
+          acc[kt][1] = mfma_k32(kf, q1, acc[kt][1]);
+        }
       }
-      // keys kt*16 + 4g .. +3 (16-byte reads); a key the query does not see
-      // gets -inf as a selected bias, with no branch
-      const u32x4 vb = *reinterpret_cast<const u32x4*>(&s.vis[kt * 16 + 4 * g]);
-      const v4f scl = *reinterpret_cast<const v4f*>(&s.c.sk[kt * 16 + 4 * g]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float bias = ((vb[r] >> qi) & 1u) ? 0.f : -INFINITY;
+      for (int kt = 0; kt < 4; ++kt) {
+        // keys kt*16 + 4g .. +3 (16-byte reads); a key the query does not see
+        // gets -inf as a selected bias, with no branch
+        const u32x4 vb = *reinterpret_cast<const u32x4*>(&s.vis[kt * 16 + 4 * g]);
+        const v4f scl = *reinterpret_cast<const v4f*>(&s.c.sk[kt * 16 + 4 * g]);
 #pragma unroll
-        for (int ht = 0; ht < 2; ++ht) x[ht][kt][r] = __builtin_fmaf(acc[ht][r], scl[r], bias);
+        for (int r = 0; r < 4; ++r) {
+          const float bias = ((vb[r] >> qi) & 1u) ? 0.f : -INFINITY;
+#pragma unroll
+          for (int ht = 0; ht < 2; ++ht) x[ht][kt][r] = __builtin_fmaf(acc[kt][ht][r], scl[r], bias);
+        }
       }
     }
     uint32_t pw[2][2][4], pl[2][2][4];   // [ht][32-key step][pair]: P as bf16 hi + lo
-    v4f svv[4];                          // V scales of keys kt*16 + 4g .. +3
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) svv[kt] = *reinterpret_cast<const v4f*>(&s.c.sv[kt * 16 + 4 * g]);
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
       float cmax = -INFINITY;
@@ -1013,14 +1053,16 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
       // 32-key step st covers key tiles 2st, 2st+1: contraction slot 8g+j <->
       // key (2st)*16 + 4g + j (j < 4) / (2st+1)*16 + 4g + j - 4
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int kt = 0; kt < 4; ++kt) {
+        const v4f sv = *reinterpret_cast<const v4f*>(&s.c.sv[kt * 16 + 4 * g]);   // keys kt*16 + 4g .. +3
+        const int st = kt >> 1;
 #pragma unroll
-        for (int h2 = 0; h2 < 4; ++h2) {
-          const int kt = 2 * st + (h2 >> 1);
-          const int r0 = (h2 & 1) * 2;
-          split_bf16x2(p[kt][r0] * svv[kt][r0], p[kt][r0 + 1] * svv[kt][r0 + 1], &pw[ht][st][h2],
+        for (int hh = 0; hh < 2; ++hh) {
+          const int h2 = (kt & 1) * 2 + hh;
+          split_bf16x2(p[kt][2 * hh] * sv[2 * hh], p[kt][2 * hh + 1] * sv[2 * hh + 1], &pw[ht][st][h2],
                        &pl[ht][st][h2]);
         }
+      }
     }
     // O^T += V^T P^T; V^T fragments shared by both tiles
 #pragma unroll
