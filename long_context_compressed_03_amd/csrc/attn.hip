@@ -38,6 +38,7 @@
 // write back and invalidate the XCD's whole L2).  The split depends only on
 // the shape and every reduction has a fixed order: results are bitwise
 // reproducible run to run.
+#pragma clang fp contract(off)
 #include "common.hpp"
 
 namespace {
@@ -265,6 +266,14 @@ struct LdsHalf {
   float l[4 * kHTW][16];
 };
 
+// Running state of the batch-invariant fold (kFold), per head tile.
+template <int kHTW>
+struct LdsFold {
+  float o[4 * kHTW][16][kHeadDim + 4];
+  float m[4 * kHTW][16];
+  float l[4 * kHTW][16];
+};
+
 template <int kIO, int kHTW>
 constexpr size_t lds_bytes() {
   return sizeof(LdsChunk<kIO>) > sizeof(LdsHalf<kHTW>) ? sizeof(LdsChunk<kIO>) : sizeof(LdsHalf<kHTW>);
@@ -371,16 +380,35 @@ CSA_DEV void store_out4(void* out, long orow, int d4, v4f v) {
   }
 }
 
-// 8 waves: wave w takes head tiles (w % 4) [+ 4 when kHTW == 2] and key half
-// w / 4 (keys [32*(w/4), 32*(w/4)+32) of every chunk); the two halves merge at
-// the end of the block through LDS.
-// kDepth > 1 (split key lists, at most about one block per CU): that many
-// chunks in flight instead of one, with the register budget of two waves per
-// SIMD.
-// kVarlen: query rows are mapped through row_seq / row_pos (the varlen calls).
-template <int kIO, int kCKV, bool kDense, int kHTW, int kDepth, bool kVarlen>
+// Sequential fold of a piece's state (m, l, o) into a running one (Mr, Lr,
+// Or), used wherever the batch-invariant calls combine pieces: in a block
+// that walks a row's pieces (attn_kernel<..., kFold>) and in attn_fold_kernel
+// over the pieces' partials.  The same two functions in both places keep the
+// operations, and so the bits, identical.
+struct FoldW {
+  float fa, fb;   // weights of the running state and of the piece
+  float M, L;     // the new running max and sum
+};
+CSA_DEV FoldW fold_weights(float Mr, float Lr, float m, float l) {
+  FoldW w;
+  w.M = fmaxf(Mr, m);
+  const float Mu = w.M == -INFINITY ? 0.f : w.M;
+  w.fa = __builtin_amdgcn_exp2f(Mr - Mu);
+  w.fb = __builtin_amdgcn_exp2f(m - Mu);
+  w.L = __builtin_fmaf(Lr, w.fa, l * w.fb);
+  return w;
+}
+CSA_DEV float fold_elem(float Or, float o, const FoldW& w) { return __builtin_fmaf(Or, w.fa, o * w.fb); }
+
+// kFold (batch-invariant calls, one block per query row): the block walks
+// every piece (split) of its row in order and folds each piece's state into a
+// running one (fold_weights / fold_elem), as attn_fold_kernel folds the
+// pieces' partials when the pieces run as blocks of their own.
+template <int kIO, int kCKV, bool kDense, int kHTW, int kDepth, bool kVarlen, bool kFold>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(kIO == CSA_BF16 && kHTW == 1 ? (kDepth > 1 ? 2 : 4) : 1)))
+__attribute__((amdgpu_waves_per_eu(kIO == CSA_BF16 && kHTW == 1
+                                       ? (kDepth > 1 || (kFold && kCKV == CSA_FP8_E4M3) ? 2 : 4)
+                                       : 1)))
 void attn_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   LdsChunk<kIO>& s = *reinterpret_cast<LdsChunk<kIO>*>(smem);
@@ -392,8 +420,8 @@ void attn_kernel(AttnArgs a) {
   const int kh = wid >> 2;
   const int wt = wid & 3;
 
-  const long qrow = blockIdx.x / a.n_splits;
-  const int split = int(blockIdx.x - qrow * a.n_splits);
+  const long qrow = kFold ? long(blockIdx.x) : blockIdx.x / a.n_splits;
+  const int split = kFold ? 0 : int(blockIdx.x - qrow * a.n_splits);
   int b, t;
   if constexpr (kVarlen) {
     b = a.row_seq[qrow];
@@ -405,7 +433,7 @@ void attn_kernel(AttnArgs a) {
   const int raw0 = a.W > 0 ? a.raw_pos0[b] : 0;
   const int n_tiles = a.H / 16;
   const int j_begin = split * a.split_len;
-  const int j_end = min(j_begin + a.split_len, a.n_list);
+  const int j_end = kFold ? a.n_list : min(j_begin + a.split_len, a.n_list);
 
   bool act[kHTW];
   u32x4 qb[kHTW][4];
@@ -492,7 +520,7 @@ void attn_kernel(AttnArgs a) {
         const u32x4 pbh = {ph[0], ph[1], ph[2], ph[3]};
         const u32x4 pbl = {pl[0], pl[1], pl[2], pl[3]};
         const int k0 = kh * 32 + 4 * g;
-        if constexpr (kHTW == 1 && kDepth == 1) {
+        if constexpr (kHTW == 1 && kDepth == 1 && !(kFold && kCKV == CSA_FP8_E4M3)) {
           // 128-VGPR budget (two blocks per CU): one V^T fragment at a time
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) {
@@ -545,6 +573,74 @@ void attn_kernel(AttnArgs a) {
     prefetch<kIO, kCKV, kDense>(a, pr[d], e_nx[d], b, t, raw0, j_begin + d * kNK, j_end);
     load_idx<kDense>(a, e_nx[d], qrow, j_begin + (d + kDepth) * kNK, j_end);
   }
+  // The state of the keys walked since the last piece start: the second key
+  // half hands its (o, max, sum) to the first through LDS; the first-half
+  // waves (kh == 0) then merge it with their own, 16 head dims at a time, and
+  // hand each merged slice to `emit(ht, dt, oo)` after `head(ht, M, L)` gave
+  // the merged max and sum (no array of the merged state is held).
+  LdsHalf<kHTW>& hf = *reinterpret_cast<LdsHalf<kHTW>*>(smem);
+  auto piece_state = [&](auto&& head, auto&& emit) {
+    float l_tot[kHTW];
+#pragma unroll
+    for (int ht = 0; ht < kHTW; ++ht) l_tot[ht] = column_sum(l_run[ht]);
+    __syncthreads();
+    if (kh == 1) {
+#pragma unroll
+      for (int ht = 0; ht < kHTW; ++ht) {
+        if (!act[ht]) continue;
+        const int tile = wt + 4 * ht;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<v4f*>(&hf.o[tile][col][dt * 16 + 4 * g]) = o[ht][dt];
+        if (g == 0) {
+          hf.m[tile][col] = m_run[ht];
+          hf.l[tile][col] = l_tot[ht];
+        }
+      }
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int ht = 0; ht < kHTW; ++ht) {
+        if (!act[ht]) continue;
+        const int tile = wt + 4 * ht;
+        const float m1 = hf.m[tile][col];
+        const float M = fmaxf(m_run[ht], m1);
+        const float Mu = M == -INFINITY ? 0.f : M;
+        const float f0 = __builtin_amdgcn_exp2f(m_run[ht] - Mu);
+        const float f1 = __builtin_amdgcn_exp2f(m1 - Mu);
+        head(ht, M, __builtin_fmaf(l_tot[ht], f0, hf.l[tile][col] * f1));
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const v4f h1 = *reinterpret_cast<const v4f*>(&hf.o[tile][col][dt * 16 + 4 * g]);
+          v4f oo;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) oo[c] = __builtin_fmaf(o[ht][dt][c], f0, h1[c] * f1);
+          emit(ht, dt, oo);
+        }
+      }
+    }
+  };
+
+  // kFold: the running state of the pieces folded so far lives in LDS beside
+  // the chunk and hand-over areas (held in registers it would not fit)
+  LdsFold<kHTW>& fs = *reinterpret_cast<LdsFold<kHTW>*>(smem + lds_bytes<kIO, kHTW>());
+  int piece_end = kFold ? min(a.split_len, j_end) : j_end;
+  if constexpr (kFold) {
+    // the fold starts from the empty state (max -inf, sum 0, output 0), as
+    // attn_fold_kernel's does; each wave owns its own slots (no barrier needed)
+    if (kh == 0) {
+#pragma unroll
+      for (int ht = 0; ht < kHTW; ++ht) {
+        const int tile = wt + 4 * ht;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<v4f*>(&fs.o[tile][col][dt * 16 + 4 * g]) = v4f{0.f, 0.f, 0.f, 0.f};
+        if (g == 0) {
+          fs.m[tile][col] = -INFINITY;
+          fs.l[tile][col] = 0.f;
+        }
+      }
+    }
+  }
   for (int j0 = j_begin; j0 < j_end; j0 += kDepth * kNK) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
@@ -555,65 +651,82 @@ void attn_kernel(AttnArgs a) {
       prefetch<kIO, kCKV, kDense>(a, pr[d], e_nx[d], b, t, raw0, j0 + (d + kDepth) * kNK, j_end);
       load_idx<kDense>(a, e_nx[d], qrow, j0 + (d + 2 * kDepth) * kNK, j_end);
       compute();
+      if constexpr (kFold) {
+        if (j0 + (d + 1) * kNK >= piece_end) {   // last chunk of a piece (uniform)
+          // fold the piece into the running state, 16 head dims at a time
+          FoldW fw[kHTW];
+          piece_state(
+              [&](int ht, float M, float L) {
+                const int tile = wt + 4 * ht;
+                fw[ht] = fold_weights(fs.m[tile][col], fs.l[tile][col], M, L);
+                if (g == 0) {
+                  fs.m[tile][col] = fw[ht].M;
+                  fs.l[tile][col] = fw[ht].L;
+                }
+              },
+              [&](int ht, int dt, const v4f& oo) {
+                v4f* slot = reinterpret_cast<v4f*>(&fs.o[wt + 4 * ht][col][dt * 16 + 4 * g]);
+                const v4f Or = *slot;
+                v4f On;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) On[c] = fold_elem(Or[c], oo[c], fw[ht]);
+                *slot = On;
+              });
+          piece_end = min(piece_end + a.split_len, j_end);
+#pragma unroll
+          for (int ht = 0; ht < kHTW; ++ht) {
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) o[ht][dt] = v4f{0.f, 0.f, 0.f, 0.f};
+            m_run[ht] = -INFINITY;
+            l_run[ht] = 0.f;
+          }
+        }
+      }
     }
   }
-
-  float l_tot[kHTW];
-#pragma unroll
-  for (int ht = 0; ht < kHTW; ++ht) {
-    l_tot[ht] = column_sum(l_run[ht]);
-  }
-  // hand the second key half to the first
-  LdsHalf<kHTW>& hf = *reinterpret_cast<LdsHalf<kHTW>*>(smem);
-  __syncthreads();
-  if (kh == 1) {
+  if constexpr (kFold) {
+    // the row's output from the folded state (as attn_fold_kernel finishes it)
+    if (kh == 1) return;
 #pragma unroll
     for (int ht = 0; ht < kHTW; ++ht) {
       if (!act[ht]) continue;
       const int tile = wt + 4 * ht;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<v4f*>(&hf.o[tile][col][dt * 16 + 4 * g]) = o[ht][dt];
-      if (g == 0) {
-        hf.m[tile][col] = m_run[ht];
-        hf.l[tile][col] = l_tot[ht];
-      }
-    }
-  }
-  __syncthreads();
-  if (kh == 1) return;
-#pragma unroll
-  for (int ht = 0; ht < kHTW; ++ht) {
-    if (!act[ht]) continue;
-    const int tile = wt + 4 * ht;
-    const int head = tile * 16 + col;
-    const float m1 = hf.m[tile][col];
-    const float M = fmaxf(m_run[ht], m1);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    const float f0 = __builtin_amdgcn_exp2f(m_run[ht] - Mu);
-    const float f1 = __builtin_amdgcn_exp2f(m1 - Mu);
-    const float L = l_tot[ht] * f0 + hf.l[tile][col] * f1;
-    v4f oo[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      oo[dt] = o[ht][dt] * f0 + *reinterpret_cast<const v4f*>(&hf.o[tile][col][dt * 16 + 4 * g]) * f1;
-    if (a.n_splits == 1) {
+      const long orow = qrow * a.H + tile * 16 + col;
+      const float M = fs.m[tile][col], L = fs.l[tile][col];
       const float inv = L > 0.f ? 1.f / L : 0.f;
-      const long orow = qrow * a.H + head;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) store_out4<kIO>(a.out, orow, dt * 4 + g, oo[dt] * inv);
+      for (int dt = 0; dt < 8; ++dt)
+        store_out4<kIO>(a.out, orow, dt * 4 + g, *reinterpret_cast<const v4f*>(&fs.o[tile][col][dt * 16 + 4 * g]) * inv);
       if (a.lse && g == 0) a.lse[orow] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
-    } else {
-      // this split's unnormalised state; the merge kernel combines the splits
-      // (streaming stores: the partials are read once, by another kernel)
-      const long slot = (qrow * a.n_splits + split) * a.H + head;
-      float* po = a.part_o + slot * kHeadDim;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) __builtin_nontemporal_store(oo[dt], reinterpret_cast<v4f*>(po + dt * 16 + 4 * g));
-      if (g == 0) {
-        __builtin_nontemporal_store(M, &a.part_ml[slot * 2]);
-        __builtin_nontemporal_store(L, &a.part_ml[slot * 2 + 1]);
-      }
     }
+  } else {
+    float Ls[kHTW], invs[kHTW];
+    piece_state(
+        [&](int ht, float M, float L) {
+          const int tile = wt + 4 * ht;
+          const long orow = qrow * a.H + tile * 16 + col;
+          Ls[ht] = L;
+          invs[ht] = L > 0.f ? 1.f / L : 0.f;
+          if (a.n_splits == 1) {
+            if (a.lse && g == 0) a.lse[orow] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
+          } else if (g == 0) {
+            // this split's unnormalised state; the merge kernel combines the splits
+            // (streaming stores: the partials are read once, by another kernel)
+            const long slot = (qrow * a.n_splits + split) * a.H + tile * 16 + col;
+            __builtin_nontemporal_store(M, &a.part_ml[slot * 2]);
+            __builtin_nontemporal_store(L, &a.part_ml[slot * 2 + 1]);
+          }
+        },
+        [&](int ht, int dt, const v4f& oo) {
+          const int tile = wt + 4 * ht;
+          if (a.n_splits == 1) {
+            store_out4<kIO>(a.out, qrow * a.H + tile * 16 + col, dt * 4 + g, oo * invs[ht]);
+          } else {
+            const long slot = (qrow * a.n_splits + split) * a.H + tile * 16 + col;
+            __builtin_nontemporal_store(oo, reinterpret_cast<v4f*>(a.part_o + slot * kHeadDim + dt * 16 + 4 * g));
+          }
+        });
+    (void)Ls;
   }
 }
 
@@ -674,6 +787,61 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict_
     store_out4<kIO>(out, hid, d4, acc * inv);
     if (lse && d4 == 0) lse[hid] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
   }
+}
+
+// Fold of the pieces of one (query, head) for the batch-invariant calls, by
+// one wave: lane x holds piece x's (max, sum) (at most 64 pieces), lane l
+// the head dims 2l, 2l+1; pieces 0, 1, ... fold in order into the empty state
+// (max -inf, sum 0, output 0) with fold_weights / fold_elem -- as
+// attn_kernel<..., kFold> does when one block walks the pieces -- and the row
+// is normalised as there.
+template <int kIO>
+__global__ __launch_bounds__(64) void attn_fold_kernel(const float* __restrict__ part_ml,
+                                                       const float* __restrict__ part_o, int n_splits, int H,
+                                                       void* out, float* lse) {
+  const long hid = blockIdx.x;                  // query row * H + head
+  const int lane = threadIdx.x;
+  const long qrow = hid / H;
+  const int head = int(hid - qrow * H);
+  const long base = qrow * n_splits * H + head; // slot of piece 0; piece x adds x*H
+  float mx = -INFINITY, lx = 0.f;
+  if (lane < n_splits) {
+    mx = part_ml[(base + long(lane) * H) * 2];
+    lx = part_ml[(base + long(lane) * H) * 2 + 1];
+  }
+  constexpr int kU = 16;
+  v2f_t ov[kU];
+  auto load_batch = [&](int x0) {
+#pragma unroll
+    for (int y = 0; y < kU; ++y) {
+      const int x = min(x0 + y, n_splits - 1);
+      ov[y] = *reinterpret_cast<const v2f_t*>(part_o + (base + long(x) * H) * kHeadDim + 2 * lane);
+    }
+  };
+  load_batch(0);
+  float M = -INFINITY, L = 0.f;
+  v2f_t O = {0.f, 0.f};
+  for (int x0 = 0; x0 < n_splits; x0 += kU) {
+    if (x0 > 0) load_batch(x0);
+#pragma unroll
+    for (int y = 0; y < kU; ++y) {
+      const int x = x0 + y;
+      if (x >= n_splits) continue;
+      const FoldW fw = fold_weights(M, L, __shfl(mx, x), __shfl(lx, x));
+      O[0] = fold_elem(O[0], ov[y][0], fw);
+      O[1] = fold_elem(O[1], ov[y][1], fw);
+      M = fw.M;
+      L = fw.L;
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const v2f_t r = O * inv;
+  if constexpr (kIO == CSA_BF16) {
+    static_cast<uint32_t*>(out)[(hid * kHeadDim + 2 * lane) / 2] = pack_bf16x2(r[0], r[1]);
+  } else {
+    *reinterpret_cast<v2f_t*>(static_cast<float*>(out) + hid * kHeadDim + 2 * lane) = r;
+  }
+  if (lse && lane == 0) lse[hid] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
 }
 
 // ---------------------------------------------------------- decode rows --
@@ -1106,7 +1274,14 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
 struct Plan {
   int n_splits, split_len;
   long blocks;
+  bool invariant;   // pieces folded in order (batch-invariant calls)
+  bool fold;        // ... inside one block per row (no partials)
 };
+
+// Batch-invariant calls with at least this many rows walk each row's pieces
+// inside one block; fewer rows run the pieces as blocks of their own and
+// attn_fold_kernel folds their partials.  Both give the same bits.
+constexpr long kFoldRows = 128;
 
 // The default work split depends only on (rows, n_list): never on data or timing.
 // At most about one block per CU: past 256 blocks some CUs run two, whose
@@ -1119,10 +1294,14 @@ Plan make_plan(long rows, int n_list, bool invariant) {
   Plan p{};
   const long chunks = (max(n_list, 1) + kNK - 1) / kNK;
   if (invariant) {
-    const long per = max(2L, (chunks + kMaxSplits - 1) / kMaxSplits);
+    // pieces of max(8, ceil(chunks / 64)) chunks: a function of the list
+    // length alone
+    const long per = max(8L, (chunks + kMaxSplits - 1) / kMaxSplits);
     p.split_len = int(per * kNK);
     p.n_splits = int((chunks + per - 1) / per);
-    p.blocks = rows * p.n_splits;
+    p.invariant = true;
+    p.fold = p.n_splits > 1 && rows >= kFoldRows;
+    p.blocks = p.fold ? rows : rows * p.n_splits;
     return p;
   }
   long want = (256 + rows - 1) / rows;
@@ -1198,23 +1377,27 @@ bool use_decode(int io_dtype, long rows, bool invariant) {
 }
 
 size_t plan_ws_bytes(const Plan& p, long rows, int H) {
-  if (p.n_splits <= 1) return 0;
+  if (p.n_splits <= 1 || p.fold) return 0;
   const size_t slots = size_t(rows) * p.n_splits * H;
   const size_t ml = ((slots * 2 * 4 + 255) / 256) * 256;
   return ml + slots * kHeadDim * 4;
 }
 
-template <int kIO, int kCKV, bool kDense, int kHTW, int kDepth, bool kVarlen>
-hipError_t launch_attn(const AttnArgs& a, long blocks, hipStream_t st) {
-  constexpr size_t bytes = lds_bytes<kIO, kHTW>();
-  auto fn = attn_kernel<kIO, kCKV, kDense, kHTW, kDepth, kVarlen>;
+template <int kIO, int kCKV, bool kDense, int kHTW, int kDepth, bool kVarlen, bool kFold>
+hipError_t launch_attn(const AttnArgs& a, const Plan& p, hipStream_t st) {
+  constexpr size_t bytes = lds_bytes<kIO, kHTW>() + (kFold ? sizeof(LdsFold<kHTW>) : 0);
+  auto fn = attn_kernel<kIO, kCKV, kDense, kHTW, kDepth, kVarlen, kFold>;
   if (hipError_t e = csa_lds_opt_in(reinterpret_cast<const void*>(fn), bytes); e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(unsigned(blocks)), dim3(kThreads), bytes, st, a);
+  hipLaunchKernelGGL(fn, dim3(unsigned(p.blocks)), dim3(kThreads), bytes, st, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_splits == 1) return e;
-  const long heads = blocks / a.n_splits * a.H;
-  hipLaunchKernelGGL(attn_merge_kernel<kIO>, dim3(unsigned(heads)), dim3(64), 0, st, a.part_ml, a.part_o, a.n_splits,
-                     a.H, a.out, a.lse);
+  if (e != hipSuccess || a.n_splits == 1 || kFold) return e;
+  const long heads = p.blocks / a.n_splits * a.H;
+  if (p.invariant)
+    hipLaunchKernelGGL(attn_fold_kernel<kIO>, dim3(unsigned(heads)), dim3(64), 0, st, a.part_ml, a.part_o, a.n_splits,
+                       a.H, a.out, a.lse);
+  else
+    hipLaunchKernelGGL(attn_merge_kernel<kIO>, dim3(unsigned(heads)), dim3(64), 0, st, a.part_ml, a.part_o,
+                       a.n_splits, a.H, a.out, a.lse);
   return hipGetLastError();
 }
 
@@ -1246,26 +1429,30 @@ bool use_mq(int io_dtype, int H, int T_q, const Plan& p) {
 }
 
 template <int kIO, int kCKV, bool kDense, bool kVarlen>
-hipError_t launch_tiles(const AttnArgs& a, long blocks, hipStream_t st) {
+hipError_t launch_tiles(const AttnArgs& a, const Plan& p, hipStream_t st) {
+  // one block per row walking every piece (batch-invariant, many rows)
+  if (p.fold)
+    return a.H <= 64 ? launch_attn<kIO, kCKV, kDense, 1, 1, kVarlen, true>(a, p, st)
+                     : launch_attn<kIO, kCKV, kDense, 2, 1, kVarlen, true>(a, p, st);
   // split key lists of more than two chunks take the two-chunk pipeline
   // (fp32 queries over more than 64 heads would not fit its registers); with
   // two chunks the one-ahead prefetch already overlaps the second, and more
   // chunks in flight only delay the first (a CU's loads in flight are few)
   if (a.n_splits > 1 && a.split_len > 2 * kNK) {
-    if (a.H <= 64) return launch_attn<kIO, kCKV, kDense, 1, 2, kVarlen>(a, blocks, st);
-    if constexpr (kIO == CSA_BF16) return launch_attn<kIO, kCKV, kDense, 2, 2, kVarlen>(a, blocks, st);
+    if (a.H <= 64) return launch_attn<kIO, kCKV, kDense, 1, 2, kVarlen, false>(a, p, st);
+    if constexpr (kIO == CSA_BF16) return launch_attn<kIO, kCKV, kDense, 2, 2, kVarlen, false>(a, p, st);
   }
-  return a.H <= 64 ? launch_attn<kIO, kCKV, kDense, 1, 1, kVarlen>(a, blocks, st)
-                   : launch_attn<kIO, kCKV, kDense, 2, 1, kVarlen>(a, blocks, st);
+  return a.H <= 64 ? launch_attn<kIO, kCKV, kDense, 1, 1, kVarlen, false>(a, p, st)
+                   : launch_attn<kIO, kCKV, kDense, 2, 1, kVarlen, false>(a, p, st);
 }
 
 template <bool kDense, bool kVarlen>
-csa_status_t tiles_for(const AttnArgs& a, int io_dtype, int ckv_dtype, long blocks, hipStream_t st) {
+csa_status_t tiles_for(const AttnArgs& a, int io_dtype, int ckv_dtype, const Plan& p, hipStream_t st) {
   hipError_t err;
-  if (io_dtype == CSA_BF16 && ckv_dtype == CSA_BF16) err = launch_tiles<CSA_BF16, CSA_BF16, kDense, kVarlen>(a, blocks, st);
-  else if (io_dtype == CSA_BF16 && ckv_dtype == CSA_FP8_E4M3) err = launch_tiles<CSA_BF16, CSA_FP8_E4M3, kDense, kVarlen>(a, blocks, st);
-  else if (io_dtype == CSA_F32 && ckv_dtype == CSA_F32) err = launch_tiles<CSA_F32, CSA_F32, kDense, kVarlen>(a, blocks, st);
-  else if (io_dtype == CSA_F32 && ckv_dtype == CSA_FP8_E4M3) err = launch_tiles<CSA_F32, CSA_FP8_E4M3, kDense, kVarlen>(a, blocks, st);
+  if (io_dtype == CSA_BF16 && ckv_dtype == CSA_BF16) err = launch_tiles<CSA_BF16, CSA_BF16, kDense, kVarlen>(a, p, st);
+  else if (io_dtype == CSA_BF16 && ckv_dtype == CSA_FP8_E4M3) err = launch_tiles<CSA_BF16, CSA_FP8_E4M3, kDense, kVarlen>(a, p, st);
+  else if (io_dtype == CSA_F32 && ckv_dtype == CSA_F32) err = launch_tiles<CSA_F32, CSA_F32, kDense, kVarlen>(a, p, st);
+  else if (io_dtype == CSA_F32 && ckv_dtype == CSA_FP8_E4M3) err = launch_tiles<CSA_F32, CSA_FP8_E4M3, kDense, kVarlen>(a, p, st);
   else return CSA_ENOTSUP;
   return err == hipSuccess ? CSA_OK : CSA_EHIP;
 }
@@ -1335,8 +1522,8 @@ csa_status_t run_attn(AttnArgs a, int io_dtype, int ckv_dtype, int B, void* ws, 
     err = ckv_dtype == CSA_BF16 ? launch_mq<CSA_BF16>(a, B, st) : launch_mq<CSA_FP8_E4M3>(a, B, st);
     return err == hipSuccess ? CSA_OK : CSA_EHIP;
   }
-  return a.row_seq ? tiles_for<kDense, true>(a, io_dtype, ckv_dtype, p.blocks, st)
-                   : tiles_for<kDense, false>(a, io_dtype, ckv_dtype, p.blocks, st);
+  return a.row_seq ? tiles_for<kDense, true>(a, io_dtype, ckv_dtype, p, st)
+                   : tiles_for<kDense, false>(a, io_dtype, ckv_dtype, p, st);
 }
 
 csa_status_t check_common(const void* q, int io_dtype, const void* ck, const void* cv, const float* ck_scale,

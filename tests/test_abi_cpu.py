@@ -184,17 +184,18 @@ def test_topk_and_attention_reject_bad_arguments():
 
 def test_batch_invariant_attention_plan():
     """The batch-invariant calls split a key list of n keys into pieces of
-    max(2, ceil(chunks/64)) chunks of 64 keys, whatever the number of rows: their
-    workspace is the same per row for every batch size (partial m, l and o per
-    piece and head)."""
+    max(8, ceil(chunks/64)) chunks of 64 keys, whatever the number of rows.  Calls
+    of fewer than 128 rows run the pieces as blocks of their own and need a
+    workspace for their partial m, l and o (per piece and head); calls of 128 rows
+    or more fold the pieces inside one block per row and need none."""
     import long_context_compressed_03_amd as csa
     lib = csa.load()
 
     def expected(rows, H, n):
         chunks = max(-(-n // 64), 1)
-        per = max(2, -(-chunks // 64))
+        per = max(8, -(-chunks // 64))
         pieces = -(-chunks // per)
-        if pieces <= 1:
+        if pieces <= 1 or rows >= 128:
             return 0
         slots = rows * pieces * H
         return -(-slots * 8 // 256) * 256 + slots * 128 * 4

@@ -1,6 +1,11 @@
 """GPU tests of the batch-invariant attention calls (csa_sparse_attn_batch_invariant,
 hca_dense_attn_batch_invariant).
 
+These calls cut each row's key list into pieces whose length depends on the list length
+alone and fold the pieces' states in order.  Calls with many rows fold inside one block per
+row; calls with few rows run the pieces as blocks of their own and fold their partials in a
+second kernel.  Slicing a batch so that both forms occur must give the same bits.
+
 A row's out and lse must be bit-identical whether it is computed in a large batch, alone,
 or in prefill chunks of another length; and the results must match the oracle to the same
 tolerance as the plain calls.  Inputs are the seeded synthetic attention inputs of the
@@ -108,6 +113,10 @@ def _chunks_equal_whole(call, T, cuts, q, qpos, lse_whole, out_whole, H):
     ("bf16", "bf16", 512, 64, 16, 300, 64, 4200, [256]),      # the plain call takes another kernel here
     ("bf16", "fp8", 300, 32, 8, 700, 16, 4000, [1, 77, 200]),
     ("f32", "f32", 130, 16, 32, 200, 40, 5000, [64]),
+    # many pieces: the whole chunk folds them inside one block per row, the short chunks
+    # run them as blocks of their own and fold their partials in a second kernel
+    ("bf16", "fp8", 200, 64, 4, 700, 128, 2300, [20, 40, 60, 80, 100, 150, 180]),
+    ("f32", "fp8", 160, 32, 4, 700, 64, 2500, [10, 130]),
 ])
 def test_dense_prefill_rows_ignore_the_chunking(csa, io, ckv, T, H, mp, cap, W, pos, cuts):
     say(f"batch-invariant dense prefill io={io} ckv={ckv} T={T} H={H} m'={mp} cuts={cuts}")
