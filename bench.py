@@ -51,10 +51,11 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="all",
-                   choices=["all", "csa_decode_128k", "hca_decode_1m", "csa_prefill_256k", "pair_1m",
+                   choices=["all", "csa_decode_128k", "hca_decode_1m", "csa_prefill_256k", "pair_1m", "pair_1m_split",
                             "mxfp4_quantize_keys_128k", "kv_append_decode_128k"],
-                   help="all (default): the 1M layer pair as the headline line, with the 128K CSA "
-                        "decode, 1M HCA decode and 256K CSA prefill workloads carried in it")
+                   help="all (default): the 1M layer pair's mixed step (packed varlen calls) as the "
+                        "headline line, with the 128K CSA decode, 1M HCA decode, 256K CSA prefill and "
+                        "the pair's split-call step carried in it")
     p.add_argument("--dist-steps", type=int, default=100,
                    help="replays of the all-copies step graph, each timed alone, for the median / p10 / p90")
     p.add_argument("--rotate", type=int, default=0, help="input copies (0 = auto)")
@@ -288,9 +289,136 @@ LAYERS = {
     "csa_decode_128k": [("", "csa_decode_128k")],
     "hca_decode_1m": [("", "hca_decode_1m")],
     "csa_prefill_256k": [("", "csa_prefill_256k")],
-    "pair_1m": [("csa_decode.", "pair_csa_decode_1m"), ("csa_chunk.", "pair_csa_chunk_1m"),
-                ("hca_decode.", "pair_hca_decode_1m"), ("hca_chunk.", "pair_hca_chunk_1m")],
+    "pair_1m_split": [("csa_decode.", "pair_csa_decode_1m"), ("csa_chunk.", "pair_csa_chunk_1m"),
+                      ("hca_decode.", "pair_hca_decode_1m"), ("hca_chunk.", "pair_hca_chunk_1m")],
 }
+
+
+def pack_layer(dec, ch):
+    """One layer of the mixed step: the decode sequences' and the chunk's host inputs packed
+    into one batch of B_dec + 1 sequences (caches padded to the larger capacity, raw windows
+    to the chunk's length with every sequence's newest token in the last row) and query rows
+    packed decode rows first."""
+    wd, wc = dec["wl"], ch["wl"]
+    nd, B = wd.B, wd.B + 1
+    L_raw, cap = max(wd.L_raw, wc.L_raw), max(wd.cap, wc.cap)
+    off = L_raw - wd.L_raw
+
+    def raw(key, dt, extra=()):
+        a = np.zeros((B, L_raw) + extra, dt)
+        a[:nd, off:] = dec["kv"][key]
+        a[nd, L_raw - wc.L_raw:] = ch["kv"][key][0]
+        return a
+
+    def cache(src, key, dt, extra):
+        a = np.zeros((B, cap) + extra, dt)
+        a[:nd, :wd.cap] = dec[src][key]
+        a[nd, :wc.cap] = ch[src][key][0]
+        return a
+    p = {"K": raw("K", np.uint16, (128,)), "V": raw("V", np.uint16, (128,)), "logits": raw("logits", np.float32),
+         "raw0": np.array([r - off for r in wd.raw_pos0] + [wc.raw_pos0[0] - (L_raw - wc.L_raw)], np.int32),
+         "q": np.concatenate([dec["at"]["q"][:, 0], ch["at"]["q"][0]]), "L_raw": L_raw, "cap": cap}
+    ckv = wd.ckv
+    ext = (128,)
+    p["cK"] = cache("at", "cK", np.uint8 if ckv == "fp8" else np.uint16, ext)
+    p["cV"] = cache("at", "cV", np.uint8 if ckv == "fp8" else np.uint16, ext)
+    if ckv == "fp8":
+        p["cK_scale"] = cache("at", "cK_scale", np.float32, ())
+        p["cV_scale"] = cache("at", "cV_scale", np.float32, ())
+    n_rows = nd + wc.T_q
+    p["pos0"] = np.array(list(wd.q_pos0) + [wc.q_pos0[0]], np.int32)
+    p["cu_rows"] = np.array(list(range(nd + 1)) + [n_rows], np.int32)
+    # the blocks the step completes: the decode tokens' (pool_range) and the chunk's
+    Ld, r0d, e0d = pool_range(wd)
+    Lc, r0c, e0c = pool_range(wc)
+    n_d, n_c = Ld // wd.m, Lc // wc.m
+    p["cu_entries"] = np.array([i * n_d for i in range(nd + 1)] + [nd * n_d + n_c], np.int32)
+    p["row0"] = np.array([r0d + off] * nd + [r0c + (L_raw - wc.L_raw)], np.int32)
+    p["entry0"] = np.array([e0d] * nd + [e0c], np.int32)
+    p["n_entries"] = nd * n_d + n_c
+    if wd.kind == "csa":
+        for key in ("q_codes", "q_e8m0", "w"):
+            p[key] = np.concatenate([dec["ix"][key][:, 0], ch["ix"][key][0]])
+        p["k_codes"] = cache("ix", "k_codes", np.uint8, (wd.d_I // 2,))
+        p["k_e8m0"] = cache("ix", "k_e8m0", np.uint8, (wd.d_I // 32,))
+    return p
+
+
+def add_varlen_layer(st, dec, ch, prefix):
+    """The mixed step's calls of one layer: compression, (indexer top-k,) attention, each one
+    launch over all the step's sequences."""
+    import long_context_compressed_03_amd as csa
+    wd, wc = dec["wl"], ch["wl"]
+    p, m, W, H = prefix, wd.m, wd.W, wd.H
+    nd = wd.B
+    rows = nd + wc.T_q
+    ent = 264 if wd.ckv == "fp8" else 512
+    Ld, Lc = pool_range(wd)[0], pool_range(wc)[0]
+    nvis_d, nvis_c = visible(wd), visible(wc)
+
+    def f_compress(c):
+        csa.csa_compress_kv_varlen(c[p + "kw"], c[p + "vw"], c[p + "logits"], m, c[p + "ck"], c[p + "cv"],
+                                   c[p + "cu_entries"], c[p + "row0"], c[p + "entry0"], c[p + "n_entries"],
+                                   k_scale_out=c[p + "cks"], v_scale_out=c[p + "cvs"])
+    st.add(Kernel(p + "compress_kv", f_compress, nd * (Ld * 516 + (Ld // m) * ent) + Lc * 516 + (Lc // m) * ent, 0,
+                  BF16_PEAK_TFLOPS, "compress_kv", "compress_long_kernel" if m >= 32 else "compress_kernel"))
+    q_bytes = rows * H * 128 * 4
+    if wd.kind == "csa":
+        k = wd.k
+        idx_bytes = wd.d_I // 2 + wd.d_I // 32
+        cap = max(wd.cap, wc.cap)
+
+        def f_sel(c):
+            csa.csa_indexer_topk_varlen(c[p + "qc"], c[p + "qe"], c[p + "w"], c[p + "kc"], c[p + "ke"],
+                                        c[p + "cu_rows"], c[p + "pos"], m, k, c[p + "idx"])
+        # each sequence's keys once, the 16-bit score keys written and the visible ones read
+        # back, the indices, the queries and weights
+        st.add(Kernel(p + "indexer_topk", f_sel,
+                      (nd * wd.cap + wc.cap) * idx_bytes + rows * cap * 2 + (nvis_d + nvis_c) * 2 + rows * k * 4
+                      + rows * wd.H_I * (idx_bytes + 4),
+                      2 * wd.H_I * wd.d_I * (nvis_d + nvis_c), MXFP4_PEAK_TFLOPS, "indexer_topk",
+                      "indexer_kernel, select_kernel"))
+
+        def f_attn(c):
+            csa.csa_sparse_attn_varlen(c[p + "q"], c[p + "ck"], c[p + "cv"], c[p + "idx"], c[p + "kw"], c[p + "vw"],
+                                       c[p + "raw0"], c[p + "cu_rows"], c[p + "pos"], W, ck_scale=c[p + "cks"],
+                                       cv_scale=c[p + "cvs"], invariant=False, out=c[p + "out"])
+        sel = min(nd * wd.cap, nd * k) + min(wc.cap, wc.T_q * k)
+        st.add(Kernel(p + "sparse_attn", f_attn,
+                      sel * ent + (nd * wd.L_raw + wc.L_raw) * 512 + q_bytes + rows * k * 4,
+                      4 * H * 128 * rows * (k + W), BF16_PEAK_TFLOPS, "sparse_attn", "attn_kernel"))
+    else:
+        def f_attn(c):
+            csa.hca_dense_attn_varlen(c[p + "q"], c[p + "ck"], c[p + "cv"], m, c[p + "kw"], c[p + "vw"], c[p + "raw0"],
+                                      c[p + "cu_rows"], c[p + "pos"], W, ck_scale=c[p + "cks"],
+                                      cv_scale=c[p + "cvs"], invariant=False, out=c[p + "out"])
+        nv_d = min((wd.q_pos0[0] + 1) // m, wd.cap)
+        nv_c = min((wc.q_pos0[0] + wc.T_q) // m, wc.cap)
+        st.add(Kernel(p + "dense_attn", f_attn,
+                      (nd * nv_d + nv_c) * ent + (nd * wd.L_raw + wc.L_raw) * 512 + q_bytes,
+                      4 * H * 128 * (nvis_d + nvis_c + rows * W), BF16_PEAK_TFLOPS, "dense_attn",
+                      "attn_mq_kernel, attn_merge_kernel"))
+
+
+def device_packed(pk, prefix, kind, k=0):
+    """Packed host arrays of one layer -> dict of CPU tensors keyed prefix+name."""
+    import torch
+    T = dict(kw=_t(pk["K"], "bf16"), vw=_t(pk["V"], "bf16"), logits=_t(pk["logits"], "f32"),
+             q=_t(pk["q"], "bf16"), pos=_t(pk["pos0"], "i32"), raw0=_t(pk["raw0"], "i32"),
+             cu_rows=_t(pk["cu_rows"], "i32"),
+             cu_entries=_t(pk["cu_entries"], "i32"), row0=_t(pk["row0"], "i32"), entry0=_t(pk["entry0"], "i32"),
+             n_entries=int(pk["n_entries"]),
+             out=torch.empty(pk["q"].shape, dtype=torch.bfloat16))
+    if "cK_scale" in pk:
+        T.update(ck=_t(pk["cK"], "u8"), cv=_t(pk["cV"], "u8"), cks=_t(pk["cK_scale"], "f32"),
+                 cvs=_t(pk["cV_scale"], "f32"))
+    else:
+        T.update(ck=_t(pk["cK"], "bf16"), cv=_t(pk["cV"], "bf16"), cks=None, cvs=None)
+    if kind == "csa":
+        T.update(qc=_t(pk["q_codes"], "u8"), qe=_t(pk["q_e8m0"], "u8"), w=_t(pk["w"], "f32"),
+                 kc=_t(pk["k_codes"], "u8"), ke=_t(pk["k_e8m0"], "u8"),
+                 idx=torch.empty((pk["q"].shape[0], k), dtype=torch.int32))
+    return {prefix + n: v for n, v in T.items()}
 
 
 QUANT_WORKLOAD = "mxfp4_quantize_keys_128k"
@@ -396,9 +524,11 @@ def build(args):
         return build_append(args)
     from csa_synth import workloads
     wls = workloads()
+    if args.workload == "pair_1m":
+        return build_pair(args, wls)
     parts = LAYERS[args.workload]
     hosts = [(prefix, host_layer(wls[name])) for prefix, name in parts]
-    if args.workload == "pair_1m":
+    if args.workload == "pair_1m_split":
         q_tokens = wls["pair_csa_decode_1m"].B + wls["pair_csa_chunk_1m"].T_q
     else:
         q_tokens = hosts[0][1]["wl"].B * hosts[0][1]["wl"].T_q
@@ -414,8 +544,9 @@ def build(args):
     st.copies = [base] + [{k: (v.clone() if isinstance(v, torch.Tensor) else v)
                            for k, v in base.items()} for _ in range(R - 1)]
     st.layers = hosts
-    if args.workload == "pair_1m":
+    if args.workload == "pair_1m_split":
         st.config = {"workload": args.workload, "layers": "CSA then HCA, same query tokens",
+                     "step": "decode rows and the chunk in separate calls per op",
                      **{prefix.rstrip("."): layer_config(h["wl"]) for prefix, h in hosts}}
     else:
         st.config = {"workload": args.workload, **layer_config(hosts[0][1]["wl"])}
@@ -423,6 +554,37 @@ def build(args):
                                  else "fused" if any(n.endswith("indexer_topk") for n in st.order) else "unfused")
     if args.batch_invariant:
         st.config["attention"] = "batch-invariant calls"
+    return st
+
+
+def build_pair(args, wls):
+    """The 1M layer pair's mixed step: 4 decode rows and one 2048-token chunk packed into one
+    varlen call per op (compression, indexer top-k and sparse attention of the CSA layer;
+    compression and dense attention of the HCA layer), all captured in one graph."""
+    import torch
+    hosts = [(prefix, host_layer(wls[name])) for prefix, name in LAYERS["pair_1m_split"]]
+    hd = {prefix.rstrip("."): h for prefix, h in hosts}
+    q_tokens = wls["pair_csa_decode_1m"].B + wls["pair_csa_chunk_1m"].T_q
+    st = Step("pair_1m", q_tokens)
+    base = {}
+    for kind in ("csa", "hca"):
+        dec, ch = hd[kind + "_decode"], hd[kind + "_chunk"]
+        pk = pack_layer(dec, ch)
+        add_varlen_layer(st, dec, ch, kind + ".")
+        base.update(device_packed(pk, kind + ".", kind, dec["wl"].k))
+        del pk
+    per_copy = sum(k.nbytes for k in st.kernels.values())
+    R = args.rotate or max(2, math.ceil(600e6 / per_copy))
+    base = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in base.items()}
+    st.copies = [base] + [{k: (v.clone() if isinstance(v, torch.Tensor) else v)
+                           for k, v in base.items()} for _ in range(R - 1)]
+    st.layers = hosts
+    st.config = {"workload": "pair_1m", "layers": "CSA then HCA, same query tokens",
+                 "step": "4 decode rows + one 2048-token chunk packed into one call per op (varlen: "
+                         "compress, indexer top-k, sparse attention; compress, dense attention)",
+                 **{prefix.rstrip("."): layer_config(h["wl"]) for prefix, h in hosts}}
+    st.config["indexer_topk"] = "fused, packed rows"
+    st.config["attention"] = "varlen calls, plain plan (many-query kernel with split decode rows for HCA)"
     return st
 
 
@@ -720,7 +882,7 @@ def roofline_entry(k, avg_us):
     return k.flops / s / 1e12, k.mfma_peak, "TFLOP/s"
 
 
-SUB_WORKLOADS = ["csa_decode_128k", "hca_decode_1m", "csa_prefill_256k"]
+SUB_WORKLOADS = ["csa_decode_128k", "hca_decode_1m", "csa_prefill_256k", "pair_1m_split"]
 HEADLINE = "pair_1m"
 
 

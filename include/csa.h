@@ -76,7 +76,10 @@ typedef enum {
   CSA_OP_INDEXER_TOPK = 3,
   CSA_OP_SPARSE_ATTN_BATCH_INVARIANT = 4,
   CSA_OP_DENSE_ATTN_BATCH_INVARIANT = 5,
-  CSA_OP_KV_CACHE_APPEND = 6
+  CSA_OP_KV_CACHE_APPEND = 6,
+  CSA_OP_INDEXER_TOPK_VARLEN = 7,
+  CSA_OP_SPARSE_ATTN_VARLEN = 8,
+  CSA_OP_DENSE_ATTN_VARLEN = 9
 } csa_op_t;
 
 /* ---------------------------------------------------------------------
@@ -107,6 +110,32 @@ csa_status_t csa_compress_kv(const void* k, const void* v, int32_t in_dtype,
                              int32_t d, int32_t m, void* k_out, void* v_out,
                              float* k_scale_out, float* v_scale_out, int32_t ld_out,
                              int32_t out_dtype, void* stream);
+
+/* ---------------------------------------------------------------------
+ * csa_compress_kv_varlen -- the new entries of several sequences in one
+ * launch (decode rows that complete a block and prefill chunks together).
+ *
+ * Passage: as csa_compress_kv.  Sequence b has n_b = cu_entries[b+1] -
+ * cu_entries[b] new entries; its j-th (j < n_b) pools raw rows
+ * row0[b] + j*m .. row0[b] + j*m + m - 1 of k[b], v[b], logits[b] into entry
+ * entry0[b] + j of k_out[b], v_out[b] (and the scales), exactly as
+ * csa_compress_kv pools a block (bit-identical results).
+ *
+ *   k, v, logits, in_dtype, d, m, k_out .. out_dtype   as csa_compress_kv
+ *              ([B, ld_in, d], [B, ld_in], [B, ld_out, d], [B, ld_out])
+ *   cu_entries [B+1] int32 (device): cu_entries[0] = 0, non-decreasing,
+ *              cu_entries[B] = n_entries
+ *   row0, entry0 [B] int32 (device)
+ *   n_entries  all sequences' new entries (host value); 0 returns CSA_OK
+ * Preconditions: row0[b] >= 0, row0[b] + n_b*m <= ld_in; entry0[b] >= 0,
+ * entry0[b] + n_b <= ld_out.
+ * ------------------------------------------------------------------- */
+csa_status_t csa_compress_kv_varlen(const void* k, const void* v, int32_t in_dtype,
+                                    const float* logits, int32_t B, int32_t ld_in, int32_t d,
+                                    int32_t m, const int32_t* cu_entries, const int32_t* row0,
+                                    const int32_t* entry0, int32_t n_entries, void* k_out,
+                                    void* v_out, float* k_scale_out, float* v_scale_out,
+                                    int32_t ld_out, int32_t out_dtype, void* stream);
 
 /* ---------------------------------------------------------------------
  * csa_mxfp4_quantize -- real vectors to the indexer's MXFP4 operands.
@@ -202,6 +231,33 @@ csa_status_t csa_indexer_topk(const uint8_t* q_codes, const uint8_t* q_e8m0, con
                               const int32_t* q_pos0, int32_t B, int32_t T_q, int32_t H_I,
                               int32_t d_I, int32_t cap, int32_t m, int32_t k, int32_t* idx,
                               void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * csa_indexer_topk_varlen -- csa_indexer_topk over packed query rows of any
+ * mix of sequences: decode rows and prefill chunks in one call.
+ *
+ * Passages: as csa_indexer_topk.  Sequence b's query rows are packed rows
+ * cu_rows[b] .. cu_rows[b+1]-1, at positions q_pos0[b], q_pos0[b]+1, ...;
+ * each row's selection is, bit for bit, the one csa_indexer_topk gives that
+ * row in a call on its own sequence (any input values).
+ *
+ *   q_codes [n_rows, H_I, d_I/2] u8    q_e8m0 [n_rows, H_I, d_I/32] u8
+ *   w       [n_rows, H_I] fp32
+ *   k_codes [B, cap, d_I/2] u8         k_e8m0 [B, cap, d_I/32] u8
+ *   cu_rows [B+1] int32 (device)       q_pos0 [B] int32 (device)
+ *   idx     [n_rows, k] int32 (output), as csa_topk
+ *   ws, ws_bytes  csa_workspace_size(CSA_OP_INDEXER_TOPK_VARLEN, n_rows, 0, 0,
+ *                 0, cap) = n_rows*cap*2 bytes, no initial contents needed
+ * Limits: as csa_indexer_topk; ceil(n_rows / (64/H_I)) + B <= 65535.
+ * Preconditions: cu_rows[0] = 0, cu_rows non-decreasing, cu_rows[B] = n_rows;
+ * nvis(t) <= cap for every row.  n_rows = 0 returns CSA_OK at once.
+ * ------------------------------------------------------------------- */
+csa_status_t csa_indexer_topk_varlen(const uint8_t* q_codes, const uint8_t* q_e8m0, const float* w,
+                                     const uint8_t* k_codes, const uint8_t* k_e8m0,
+                                     const int32_t* cu_rows, const int32_t* q_pos0, int32_t B,
+                                     int32_t n_rows, int32_t H_I, int32_t d_I, int32_t cap,
+                                     int32_t m, int32_t k, int32_t* idx, void* ws, size_t ws_bytes,
+                                     void* stream);
 
 /* ---------------------------------------------------------------------
  * csa_compress_indexer_topk -- a CSA layer's compression and its indexer
@@ -354,40 +410,47 @@ csa_status_t hca_dense_attn_batch_invariant(
     void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------
- * csa_sparse_attn_varlen, hca_dense_attn_varlen -- one call over query rows
- * of any mix of sequences: decode rows and prefill chunks together.
+ * csa_sparse_attn_varlen, hca_dense_attn_varlen -- one call over the packed
+ * query rows of several sequences: decode rows and prefill chunks together.
  *
- * Passage: the operation is csa_sparse_attn's / hca_dense_attn's.  Query row
- * r (r < n_rows) belongs to sequence row_seq[r] (in [0, B)) and sits at
- * position row_pos[r]; its key set is the one those calls give a query of
- * that sequence at that position.  The split plan is the batch-invariant
- * one, so row r's bits equal those of the *_batch_invariant call on its own
- * sequence.
+ * Passage: the operation is csa_sparse_attn's / hca_dense_attn's.  Sequence
+ * b's query rows are packed rows cu_rows[b] .. cu_rows[b+1]-1 at positions
+ * q_pos0[b], q_pos0[b]+1, ...; each row's key set is the one those calls
+ * give a query of that sequence at that position.
+ * invariant != 0: the batch-invariant plan, so row r's bits equal those of
+ * the *_batch_invariant call on its own sequence.  invariant == 0: the
+ * kernels the plain calls would pick for a call of n_rows rows (bits may
+ * depend on the batch); with bf16 queries, H in {32, 64, 128} and at least
+ * 256 rows, the dense call runs the many-query kernel over tiles of each
+ * sequence's rows, with the key lists of sequences of at most 8 / 4 / 2 rows
+ * (H = 32 / 64 / 128) cut into pieces spread over the chip and merged after.
  *
  *   q        [n_rows, H, d] io_dtype;  out [n_rows, H, d];  lse [n_rows, H] or NULL
  *   idx      [n_rows, k] int32 (sparse)
  *   ck, cv, ck_scale, cv_scale, k_win, v_win, raw_pos0: per sequence, as for
  *            the plain calls ([B, cap, d], [B, L_raw, d], [B])
- *   row_seq, row_pos  [n_rows] int32 (device)
- *   ws       csa_workspace_size(CSA_OP_SPARSE_ATTN_BATCH_INVARIANT resp.
- *            CSA_OP_DENSE_ATTN_BATCH_INVARIANT, n_rows, 1, H, d, n_keys)
- * Limits as for the plain calls.  Preconditions: row_seq[r] in [0, B);
- * row_pos[r] >= 0.
+ *   cu_rows  [B+1] int32 (device): cu_rows[0] = 0, non-decreasing,
+ *            cu_rows[B] = n_rows;  q_pos0 [B] int32 (device), >= 0
+ *   ws       csa_workspace_size(CSA_OP_SPARSE_ATTN_VARLEN resp.
+ *            CSA_OP_DENSE_ATTN_VARLEN, n_rows, B, H, d, n_keys) bytes (either
+ *            mode), n_keys = k + W resp. cap + W
+ * Limits as for the plain calls.  n_rows = 0 returns CSA_OK at once.
  * ------------------------------------------------------------------- */
 csa_status_t csa_sparse_attn_varlen(const void* q, int32_t io_dtype, const void* ck, const void* cv,
                                     const float* ck_scale, const float* cv_scale, int32_t ckv_dtype,
                                     int32_t cap, const int32_t* idx, int32_t k, const void* k_win,
                                     const void* v_win, const int32_t* raw_pos0, int32_t L_raw,
-                                    const int32_t* row_seq, const int32_t* row_pos, int32_t n_rows,
+                                    const int32_t* cu_rows, const int32_t* q_pos0, int32_t n_rows,
                                     int32_t W, int32_t B, int32_t H, int32_t d, float sm_scale,
-                                    void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+                                    int32_t invariant, void* out, float* lse, void* ws,
+                                    size_t ws_bytes, void* stream);
 csa_status_t hca_dense_attn_varlen(const void* q, int32_t io_dtype, const void* ck, const void* cv,
                                    const float* ck_scale, const float* cv_scale, int32_t ckv_dtype,
                                    int32_t cap, int32_t m_prime, const void* k_win, const void* v_win,
-                                   const int32_t* raw_pos0, int32_t L_raw, const int32_t* row_seq,
-                                   const int32_t* row_pos, int32_t n_rows, int32_t W, int32_t B,
-                                   int32_t H, int32_t d, float sm_scale, void* out, float* lse,
-                                   void* ws, size_t ws_bytes, void* stream);
+                                   const int32_t* raw_pos0, int32_t L_raw, const int32_t* cu_rows,
+                                   const int32_t* q_pos0, int32_t n_rows, int32_t W, int32_t B,
+                                   int32_t H, int32_t d, float sm_scale, int32_t invariant,
+                                   void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------
  * csa_kv_cache_append -- one decode step's token into a layer's KV cache.

@@ -23,15 +23,16 @@ CSA_OK, CSA_EINVAL, CSA_ENOTSUP, CSA_EHIP, CSA_EWORKSPACE, CSA_ESCRATCH = range(
 CSA_BF16, CSA_F32, CSA_FP8_E4M3 = 0, 1, 2
 CSA_OP_TOPK, CSA_OP_SPARSE_ATTN, CSA_OP_DENSE_ATTN, CSA_OP_INDEXER_TOPK = 0, 1, 2, 3
 CSA_OP_SPARSE_ATTN_BATCH_INVARIANT, CSA_OP_DENSE_ATTN_BATCH_INVARIANT = 4, 5
-CSA_OP_KV_CACHE_APPEND = 6
+CSA_OP_KV_CACHE_APPEND, CSA_OP_INDEXER_TOPK_VARLEN = 6, 7
+CSA_OP_SPARSE_ATTN_VARLEN, CSA_OP_DENSE_ATTN_VARLEN = 8, 9
 DTYPES = {"bf16": CSA_BF16, "f32": CSA_F32, "fp8": CSA_FP8_E4M3}
 
 EXPORTS = ["csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
            "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn",
            "csa_sparse_attn_batch_invariant", "hca_dense_attn_batch_invariant", "csa_kv_cache_append",
            "csa_mxfp4_quantize_appended", "csa_sparse_attn_varlen", "hca_dense_attn_varlen",
-           "csa_indexer_key_append", "csa_sparse_attn_noalloc",
-           "csa_workspace_size",
+           "csa_indexer_key_append", "csa_sparse_attn_noalloc", "csa_compress_kv_varlen",
+           "csa_indexer_topk_varlen", "csa_workspace_size",
            "csa_status_str", "csa_abi_version"]
 
 _lib = None
@@ -74,13 +75,17 @@ def load(path=LIB_PATH):
                                         _P, _P, _P, _P, _S, _P]
     lib.csa_mxfp4_quantize_appended.argtypes = [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P]
     lib.csa_sparse_attn_varlen.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _P, _I, _P, _P, _P, _I, _P, _P,
-                                           _I, _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
+                                           _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _S, _P]
     lib.hca_dense_attn_varlen.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _P, _P,
-                                          _I, _I, _I, _I, _I, _F, _P, _P, _P, _S, _P]
+                                          _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _S, _P]
     lib.csa_indexer_key_append.argtypes = [_P, _P, _I, _P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P]
     lib.csa_sparse_attn_noalloc.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _P, _I, _P, _P, _P, _I, _P, _I,
                                             _I, _I, _I, _I, _F, _P, _P, _P]
-    for fn in ["csa_indexer_key_append", "csa_sparse_attn_noalloc", "csa_sparse_attn_varlen", "hca_dense_attn_varlen",
+    lib.csa_compress_kv_varlen.argtypes = [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _I,
+                                           _I, _P]
+    lib.csa_indexer_topk_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P,
+                                            _S, _P]
+    for fn in ["csa_compress_kv_varlen", "csa_indexer_topk_varlen", "csa_indexer_key_append", "csa_sparse_attn_noalloc", "csa_sparse_attn_varlen", "hca_dense_attn_varlen",
                "csa_mxfp4_quantize_appended", "csa_kv_cache_append", "csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_indexer_topk",
                "csa_compress_indexer_topk", "csa_topk", "csa_sparse_attn", "hca_dense_attn",
                "csa_sparse_attn_batch_invariant", "hca_dense_attn_batch_invariant"]:
@@ -245,6 +250,41 @@ def csa_indexer_topk(q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, m, k, idx=None
     return idx
 
 
+def csa_indexer_topk_varlen(q_codes, q_e8m0, w, k_codes, k_e8m0, cu_rows, q_pos0, m, k, idx=None,
+                            stream=None):
+    """Indexer top-k over packed query rows of B sequences: q_codes [n_rows, H_I, d_I/2],
+    k_codes [B, cap, d_I/2], cu_rows [B+1] (sequence b owns rows cu_rows[b] ..
+    cu_rows[b+1]-1, at positions q_pos0[b], q_pos0[b]+1, ...).  idx [n_rows, k] int32."""
+    n_rows, H_I, half = q_codes.shape
+    B, cap = k_codes.shape[0], k_codes.shape[1]
+    if cu_rows.numel() != B + 1 or q_pos0.numel() != B:
+        raise ValueError("cu_rows holds B + 1 offsets and q_pos0 B positions")
+    if idx is None:
+        idx = torch.empty((n_rows, k), dtype=torch.int32, device=q_codes.device)
+    lib = load()
+    ws = _workspace(q_codes.device, lib.csa_workspace_size(CSA_OP_INDEXER_TOPK_VARLEN, n_rows, 0, 0, 0, cap))
+    st = lib.csa_indexer_topk_varlen(_ptr(q_codes), _ptr(q_e8m0), _ptr(w), _ptr(k_codes), _ptr(k_e8m0),
+                                     _ptr(cu_rows), _ptr(q_pos0), B, n_rows, H_I, 2 * half, cap, m, k, _ptr(idx),
+                                     _ws_ptr(ws), _ws_len(ws), _stream(stream))
+    _check("csa_indexer_topk_varlen", st)
+    return idx
+
+
+def csa_compress_kv_varlen(k, v, logits, m, k_out, v_out, cu_entries, row0, entry0, n_entries,
+                           k_scale_out=None, v_scale_out=None, stream=None):
+    """New entries of B sequences in one launch: k, v [B, ld_in, 128], logits [B, ld_in];
+    sequence b's j-th new entry (j < cu_entries[b+1] - cu_entries[b]) pools rows
+    row0[b] + j*m .. into entry entry0[b] + j of k_out, v_out [B, ld_out, 128]."""
+    B, ld_in, d = k.shape
+    if cu_entries.numel() != B + 1 or row0.numel() != B or entry0.numel() != B:
+        raise ValueError("cu_entries holds B + 1 offsets, row0 and entry0 B values")
+    st = load().csa_compress_kv_varlen(_ptr(k), _ptr(v), _dt_of(k), _ptr(logits), B, ld_in, d, m, _ptr(cu_entries),
+                                       _ptr(row0), _ptr(entry0), int(n_entries), _ptr(k_out), _ptr(v_out),
+                                       _ptr(k_scale_out), _ptr(v_scale_out), k_out.shape[1], _dt_of(k_out),
+                                       _stream(stream))
+    _check("csa_compress_kv_varlen", st)
+
+
 _WS = {}
 
 
@@ -380,39 +420,42 @@ def csa_mxfp4_quantize_appended(x, pos, m, codes, e8m0, stream=None):
     _check("csa_mxfp4_quantize_appended", st)
 
 
-def _varlen(name, op, q, ck, cv, mid, n_keys, k_win, v_win, raw_pos0, row_seq, row_pos, W, ck_scale,
-            cv_scale, sm_scale, out, lse, stream):
+def _varlen(name, op, q, ck, cv, mid, n_keys, k_win, v_win, raw_pos0, cu_rows, q_pos0, W, ck_scale,
+            cv_scale, sm_scale, invariant, out, lse, stream):
     n_rows, H, d = q.shape
     B, cap = ck.shape[0], ck.shape[1]
+    if cu_rows.numel() != B + 1 or q_pos0.numel() != B:
+        raise ValueError("cu_rows holds B + 1 offsets and q_pos0 B positions (B = ck.shape[0])")
     if out is None:
         out = torch.empty_like(q)
     sm = d ** -0.5 if sm_scale is None else sm_scale
     lib = load()
-    ws = _workspace(q.device, lib.csa_workspace_size(op, n_rows, 1, H, d, n_keys))
+    ws = _workspace(q.device, lib.csa_workspace_size(op, n_rows, B, H, d, n_keys))
     st = getattr(lib, name)(_ptr(q), _dt_of(q), _ptr(ck), _ptr(cv), _ptr(ck_scale), _ptr(cv_scale),
                             _dt_of(ck), cap, *mid, _ptr(k_win), _ptr(v_win), _ptr(raw_pos0),
-                            k_win.shape[1], _ptr(row_seq), _ptr(row_pos), n_rows, W, B, H, d, sm,
-                            _ptr(out), _ptr(lse), _ws_ptr(ws), _ws_len(ws), _stream(stream))
+                            k_win.shape[1], _ptr(cu_rows), _ptr(q_pos0), n_rows, W, B, H, d, sm,
+                            int(bool(invariant)), _ptr(out), _ptr(lse), _ws_ptr(ws), _ws_len(ws), _stream(stream))
     _check(name, st)
     return out
 
 
-def csa_sparse_attn_varlen(q, ck, cv, idx, k_win, v_win, raw_pos0, row_seq, row_pos, W, ck_scale=None,
-                           cv_scale=None, sm_scale=None, out=None, lse=None, stream=None):
-    """CSA attention over query rows of mixed sequences: q [n_rows, H, d], idx [n_rows, k];
-    row r belongs to sequence row_seq[r] at position row_pos[r]."""
+def csa_sparse_attn_varlen(q, ck, cv, idx, k_win, v_win, raw_pos0, cu_rows, q_pos0, W, ck_scale=None,
+                           cv_scale=None, sm_scale=None, invariant=True, out=None, lse=None, stream=None):
+    """CSA attention over the packed query rows of B sequences: q [n_rows, H, d], idx
+    [n_rows, k]; sequence b owns rows cu_rows[b] .. cu_rows[b+1]-1 at positions q_pos0[b],
+    q_pos0[b]+1, ...  invariant: each row's bits equal the batch-invariant call's on its own
+    sequence; otherwise the plain calls' kernels for a call of n_rows rows."""
     k = idx.shape[-1]
-    return _varlen("csa_sparse_attn_varlen", CSA_OP_SPARSE_ATTN_BATCH_INVARIANT, q, ck, cv,
-                   (_ptr(idx), k), k + W, k_win, v_win, raw_pos0, row_seq, row_pos, W, ck_scale,
-                   cv_scale, sm_scale, out, lse, stream)
+    return _varlen("csa_sparse_attn_varlen", CSA_OP_SPARSE_ATTN_VARLEN, q, ck, cv, (_ptr(idx), k), k + W, k_win,
+                   v_win, raw_pos0, cu_rows, q_pos0, W, ck_scale, cv_scale, sm_scale, invariant, out, lse, stream)
 
 
-def hca_dense_attn_varlen(q, ck, cv, m_prime, k_win, v_win, raw_pos0, row_seq, row_pos, W, ck_scale=None,
-                          cv_scale=None, sm_scale=None, out=None, lse=None, stream=None):
-    """HCA attention over query rows of mixed sequences (as csa_sparse_attn_varlen)."""
-    return _varlen("hca_dense_attn_varlen", CSA_OP_DENSE_ATTN_BATCH_INVARIANT, q, ck, cv, (m_prime,),
-                   ck.shape[1] + W, k_win, v_win, raw_pos0, row_seq, row_pos, W, ck_scale, cv_scale,
-                   sm_scale, out, lse, stream)
+def hca_dense_attn_varlen(q, ck, cv, m_prime, k_win, v_win, raw_pos0, cu_rows, q_pos0, W, ck_scale=None,
+                          cv_scale=None, sm_scale=None, invariant=True, out=None, lse=None, stream=None):
+    """HCA attention over the packed query rows of B sequences (as csa_sparse_attn_varlen)."""
+    return _varlen("hca_dense_attn_varlen", CSA_OP_DENSE_ATTN_VARLEN, q, ck, cv, (m_prime,), ck.shape[1] + W,
+                   k_win, v_win, raw_pos0, cu_rows, q_pos0, W, ck_scale, cv_scale, sm_scale, invariant, out, lse,
+                   stream)
 
 
 def csa_indexer_key_append(k_new, z_new, pos, k_ring, z_ring, m, codes, e8m0, stream=None):

@@ -76,8 +76,8 @@ struct AttnArgs {
   const void* v_win;
   const int32_t* raw_pos0;
   const int32_t* q_pos0;
-  const int32_t* row_seq;  // varlen: sequence of each query row (else null: row / T_q)
-  const int32_t* row_pos;  // varlen: position of each query row
+  const int32_t* cu_rows;  // varlen: sequence b owns packed rows cu_rows[b] .. cu_rows[b+1]-1
+                           // at q_pos0[b], q_pos0[b]+1, ... (else null: row / T_q)
   void* out;
   float* lse;
   float* part_ml;          // [rows, n_splits, H, 2]: running max (log2 domain), sum
@@ -91,8 +91,17 @@ struct AttnArgs {
   int n_list;              // key-list length (k + W or cap + W)
   int split_len;           // keys per split (multiple of kNK)
   int n_splits;
+  int n_seq;               // varlen: sequences
+  int piece_len;           // varlen many-query: keys per piece of a one-tile sequence
+  int n_pieces;            // ... and pieces per such sequence
   float sm_log2;           // sm_scale * log2(e)
 };
+
+// Packed row r of a varlen call: its sequence and position.
+CSA_DEV void packed_row(const AttnArgs& a, long r, int* b, int* t) {
+  *b = csa_packed_seq(a.cu_rows, a.n_seq, int(r));
+  *t = a.q_pos0[*b] + int(r - a.cu_rows[*b]);
+}
 
 // Source of key-list slot j for query (b, i) at position t.
 // 0 = empty / invisible, 1 = compressed entry `row`, 2 = raw window `row`.
@@ -424,8 +433,7 @@ void attn_kernel(AttnArgs a) {
   const int split = kFold ? 0 : int(blockIdx.x - qrow * a.n_splits);
   int b, t;
   if constexpr (kVarlen) {
-    b = a.row_seq[qrow];
-    t = a.row_pos[qrow];
+    packed_row(a, qrow, &b, &t);
   } else {
     b = int(qrow / a.T_q);
     t = a.q_pos0[b] + int(qrow - long(b) * a.T_q);
@@ -739,13 +747,25 @@ void attn_kernel(AttnArgs a) {
 template <int kIO>
 __global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict__ part_ml,
                                                         const float* __restrict__ part_o, int n_splits, int H,
-                                                        void* out, float* lse) {
+                                                        void* out, float* lse, const int32_t* __restrict__ cu_rows,
+                                                        int kq) {
   __shared__ float wsh[64];
-  const long hid = blockIdx.x;                  // query row * H + head
+  const long hid = blockIdx.x;                  // partial row * H + head
   const int lane = threadIdx.x;
   const long qrow = hid / H;
   const int head = int(hid - qrow * H);
   const long base = qrow * n_splits * H + head; // slot of split 0; split x adds x*H
+  // cu_rows: partial row qrow is query qrow % kq of sequence qrow / kq, a
+  // sequence of at most kq rows (the pieces of the varlen many-query launch);
+  // rows of other sequences have no partials (the whole wave leaves)
+  long ohid = hid;
+  if (cu_rows) {
+    const int b = int(qrow / kq);
+    const int qi = int(qrow - long(b) * kq);
+    const int n = cu_rows[b + 1] - cu_rows[b];
+    if (n > kq || qi >= n) return;
+    ohid = (long(cu_rows[b]) + qi) * H + head;
+  }
   const int half = lane >> 5;
   const int d4 = lane & 31;
   constexpr int kU = 16;   // 32 splits per batch of loads
@@ -784,8 +804,8 @@ __global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict_
   for (int c = 0; c < 4; ++c) acc[c] = swap_combine<32>(acc[c], add);
   if (half == 0) {
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    store_out4<kIO>(out, hid, d4, acc * inv);
-    if (lse && d4 == 0) lse[hid] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
+    store_out4<kIO>(out, ohid, d4, acc * inv);
+    if (lse && d4 == 0) lse[ohid] = L > 0.f ? M * kLn2 + logf(L) : -INFINITY;
   }
 }
 
@@ -891,8 +911,7 @@ void attn_decode_kernel(AttnArgs a, int kT, int n_groups, long n_units) {
   const int split = int(unit - qrow * a.n_splits);
   int b, t;
   if constexpr (kVarlen) {
-    b = a.row_seq[qrow];
-    t = a.row_pos[qrow];
+    packed_row(a, qrow, &b, &t);
   } else {
     b = int(qrow / a.T_q);
     t = a.q_pos0[b] + int(qrow - long(b) * a.T_q);
@@ -1096,7 +1115,31 @@ CSA_DEV void prefetch_mq(const AttnArgs& a, Pre<CSA_BF16>& pr, uint32_t (&vis)[2
   }
 }
 
-template <int kCKV, int kQB>
+// Tile `tile` of a varlen many-query launch: the rows of every sequence with
+// more than kQB rows cut into tiles of kQB, sequences in order (sequences of
+// at most kQB rows are served by pieces instead).  False past the last tile.
+template <int kQB>
+CSA_DEV bool mq_tile(const int32_t* __restrict__ cu_rows, int n_seq, long tile, int* b, int* i0) {
+  long t = 0;
+  for (int x = 0; x < n_seq; ++x) {
+    const int n = cu_rows[x + 1] - cu_rows[x];
+    const long tiles = n > kQB ? (n + kQB - 1) / kQB : 0;
+    if (tile < t + tiles) {
+      *b = x;
+      *i0 = int(tile - t) * kQB;
+      return true;
+    }
+    t += tiles;
+  }
+  return false;
+}
+
+// kPacked (varlen calls): blocks [0, n_seq * n_pieces) take piece x of
+// sequence b's key list (b = block / n_pieces) when that sequence has at most
+// kQB rows, and write the piece's partial state for attn_merge_kernel; the
+// rest take the tiles of the longer sequences (mq_tile) whole.  A decode row
+// then spreads over many CUs instead of holding one for a whole tile's time.
+template <int kCKV, int kQB, bool kPacked>
 __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
   static_assert(kQB == 2 || kQB == 4 || kQB == 8, "two 16-head tiles per wave");
   constexpr int kWPQ = 8 / kQB;   // waves per query; each takes two 16-head tiles
@@ -1107,26 +1150,48 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
   const int wid = threadIdx.x >> 6;
   const int col = lane & 15;
   const int g = lane >> 4;
-  const int blocks_per_seq = (a.T_q + kQB - 1) / kQB;
-  const int b = int(blockIdx.x / blocks_per_seq);
-  const int i0 = int(blockIdx.x - long(b) * blocks_per_seq) * kQB;
+  int b, i0, T_b, piece = -1;
+  long row_base;   // packed row of the sequence's query 0
+  if constexpr (kPacked) {
+    const long n_piece_blocks = long(a.n_seq) * a.n_pieces;
+    if (long(blockIdx.x) < n_piece_blocks) {
+      b = int(blockIdx.x / a.n_pieces);
+      piece = int(blockIdx.x - long(b) * a.n_pieces);
+      T_b = a.cu_rows[b + 1] - a.cu_rows[b];
+      if (T_b == 0 || T_b > kQB) return;   // the whole block, before any barrier
+      i0 = 0;
+    } else {
+      if (!mq_tile<kQB>(a.cu_rows, a.n_seq, long(blockIdx.x) - n_piece_blocks, &b, &i0)) return;
+      T_b = a.cu_rows[b + 1] - a.cu_rows[b];
+    }
+    row_base = a.cu_rows[b];
+  } else {
+    const int blocks_per_seq = (a.T_q + kQB - 1) / kQB;
+    b = int(blockIdx.x / blocks_per_seq);
+    i0 = int(blockIdx.x - long(b) * blocks_per_seq) * kQB;
+    T_b = a.T_q;
+    row_base = long(b) * a.T_q;
+  }
   const int qi = wid / kWPQ;
   const int i = i0 + qi;
-  const bool q_ok = i < a.T_q;
+  const bool q_ok = i < T_b;
   const int pos0 = a.q_pos0[b];
   const int raw0 = a.W > 0 ? a.raw_pos0[b] : 0;
-  const int i_last = min(i0 + kQB, a.T_q) - 1;
+  const int i_last = min(i0 + kQB, T_b) - 1;
   const int nv_max = min((pos0 + i_last + 1) / a.k, a.cap);
   const int p_lo = pos0 + i0 - a.W + 1;
   const int n_win = a.W > 0 ? a.W + (i_last - i0) : 0;
   const int n_list = nv_max + n_win;
   const int t0 = pos0 + i0;
   const int n_q = i_last - i0 + 1;
+  // the slots of the union list this block walks: all, or one piece
+  const int j_lo = piece < 0 ? 0 : min(piece * a.piece_len, n_list);
+  const int j_hi = piece < 0 ? n_list : min(j_lo + a.piece_len, n_list);
 
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     const int head = ((wid % kWPQ) * 2 + ht) * 16 + col;
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((long(b) * a.T_q + (q_ok ? i : i0)) * a.H + head) * kHeadDim;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((row_base + (q_ok ? i : i0)) * a.H + head) * kHeadDim;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) s.q[wid][ht][ks][lane] = *reinterpret_cast<const u32x4*>(qp + ks * 32 + g * 8);
   }
@@ -1144,8 +1209,8 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
   // chunk c + 1 is still loading into the other
   Pre<CSA_BF16> pr[2];
   uint32_t tag[2][2];
-  if (n_list > 0) prefetch_mq<kCKV>(a, pr[0], tag[0], b, raw0, nv_max, p_lo, n_list, 0, t0, n_q);
-  if (n_list > kNK) prefetch_mq<kCKV>(a, pr[1], tag[1], b, raw0, nv_max, p_lo, n_list, kNK, t0, n_q);
+  if (j_lo < j_hi) prefetch_mq<kCKV>(a, pr[0], tag[0], b, raw0, nv_max, p_lo, n_list, j_lo, t0, n_q);
+  if (j_lo + kNK < j_hi) prefetch_mq<kCKV>(a, pr[1], tag[1], b, raw0, nv_max, p_lo, n_list, j_lo + kNK, t0, n_q);
   auto step = [&](Pre<CSA_BF16>& prc, uint32_t (&tgc)[2], int j0) {
     __syncthreads();
     store_chunk<CSA_BF16, kCKV>(s.c, prc, a.sm_log2);
@@ -1154,7 +1219,7 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
       s.vis[2 * item_kp() + 1] = tgc[1];
     }
     __syncthreads();
-    if (j0 + 2 * kNK < n_list)
+    if (j0 + 2 * kNK < j_hi)
       prefetch_mq<kCKV>(a, prc, tgc, b, raw0, nv_max, p_lo, n_list, j0 + 2 * kNK, t0, n_q);
     // S^T for the 4 key tiles x 2 head tiles; K fragments shared by both tiles,
     // contraction steps outermost so only one step's query fragments are live
@@ -1253,16 +1318,35 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
       }
     }
   };
-  for (int j0 = 0; j0 < n_list; j0 += 2 * kNK) {
+  for (int j0 = j_lo; j0 < j_hi; j0 += 2 * kNK) {
     step(pr[0], tag[0], j0);
-    if (j0 + kNK < n_list) step(pr[1], tag[1], j0 + kNK);
+    if (j0 + kNK < j_hi) step(pr[1], tag[1], j0 + kNK);
   }
   if (!q_ok) return;
+  if (kPacked && piece >= 0) {
+    // the piece's partial state (max in the log2 domain, sum, unnormalised
+    // output), in attn_merge_kernel's layout: partial row b * kQB + i, split
+    // `piece` (an empty piece writes max -inf, sum 0, output 0)
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) {
+      const float L = column_sum(l_run[ht]);
+      const int head = ((wid % kWPQ) * 2 + ht) * 16 + col;
+      const long slot = ((long(b) * kQB + i) * a.n_pieces + piece) * a.H + head;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<v4f*>(a.part_o + slot * kHeadDim + (dt * 4 + g) * 4) = o[ht][dt];
+      if (g == 0) {
+        a.part_ml[slot * 2] = m_run[ht];
+        a.part_ml[slot * 2 + 1] = L;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int ht = 0; ht < 2; ++ht) {
     const float L = column_sum(l_run[ht]);
     const int head = ((wid % kWPQ) * 2 + ht) * 16 + col;
-    const long orow = (long(b) * a.T_q + i) * a.H + head;
+    const long orow = (row_base + i) * a.H + head;
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) store_out4<CSA_BF16>(a.out, orow, dt * 4 + g, o[ht][dt] * inv);
@@ -1397,28 +1481,75 @@ hipError_t launch_attn(const AttnArgs& a, const Plan& p, hipStream_t st) {
                        a.H, a.out, a.lse);
   else
     hipLaunchKernelGGL(attn_merge_kernel<kIO>, dim3(unsigned(heads)), dim3(64), 0, st, a.part_ml, a.part_o,
-                       a.n_splits, a.H, a.out, a.lse);
+                       a.n_splits, a.H, a.out, a.lse, nullptr, 0);
   return hipGetLastError();
 }
 
+// B sequences of T_q rows; or, for a packed varlen call (a.cu_rows), B =
+// n_rows: a bound on the tiles plus the pieces, then the merge of the pieces.
 template <int kCKV, int kQB>
-hipError_t launch_mq_q(const AttnArgs& a, int B, hipStream_t st) {
+hipError_t launch_mq_q(const AttnArgs& a, long B, hipStream_t st) {
   constexpr size_t bytes = sizeof(LdsMQ);
-  if (hipError_t e = csa_lds_opt_in(reinterpret_cast<const void*>(&attn_mq_kernel<kCKV, kQB>), bytes);
+  if (!a.cu_rows) {
+    if (hipError_t e = csa_lds_opt_in(reinterpret_cast<const void*>(&attn_mq_kernel<kCKV, kQB, false>), bytes);
+        e != hipSuccess)
+      return e;
+    const long blocks = B * ((a.T_q + kQB - 1) / kQB);
+    hipLaunchKernelGGL((attn_mq_kernel<kCKV, kQB, false>), dim3(unsigned(blocks)), dim3(kThreads), bytes, st, a);
+    return hipGetLastError();
+  }
+  if (hipError_t e = csa_lds_opt_in(reinterpret_cast<const void*>(&attn_mq_kernel<kCKV, kQB, true>), bytes);
       e != hipSuccess)
     return e;
-  const long blocks = long(B) * ((a.T_q + kQB - 1) / kQB);
-  hipLaunchKernelGGL((attn_mq_kernel<kCKV, kQB>), dim3(unsigned(blocks)), dim3(kThreads), bytes, st, a);
+  const long blocks = long(a.n_seq) * a.n_pieces + (B + kQB - 1) / kQB + a.n_seq;
+  hipLaunchKernelGGL((attn_mq_kernel<kCKV, kQB, true>), dim3(unsigned(blocks)), dim3(kThreads), bytes, st, a);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  const long heads = long(a.n_seq) * kQB * a.H;
+  hipLaunchKernelGGL(attn_merge_kernel<CSA_BF16>, dim3(unsigned(heads)), dim3(64), 0, st, a.part_ml, a.part_o,
+                     a.n_pieces, a.H, a.out, a.lse, a.cu_rows, kQB);
   return hipGetLastError();
 }
 
 template <int kCKV>
-hipError_t launch_mq(const AttnArgs& a, int B, hipStream_t st) {
+hipError_t launch_mq(const AttnArgs& a, long B, hipStream_t st) {
   switch (a.H) {
     case 32: return launch_mq_q<kCKV, 8>(a, B, st);
     case 64: return launch_mq_q<kCKV, 4>(a, B, st);
     default: return launch_mq_q<kCKV, 2>(a, B, st);
   }
+}
+
+// Pieces of the varlen many-query launch: a sequence of at most kQB rows has
+// its union list (at most n_list + kQB - 1 slots) cut into n_pieces pieces of
+// piece_len slots (whole chunks, about kPieceChunks each, at most 64 pieces:
+// the merge kernel's limit).
+constexpr int kPieceChunks = 4;
+struct MQPieces {
+  int kqb, n_pieces, piece_len;
+};
+MQPieces mq_pieces(int H, int n_list) {
+  MQPieces m{};
+  m.kqb = H == 32 ? 8 : H == 64 ? 4 : 2;
+  const long chunks = (long(n_list) + m.kqb - 1 + kNK - 1) / kNK;
+  long S = (chunks + kPieceChunks - 1) / kPieceChunks;
+  S = S < 1 ? 1 : S > 64 ? 64 : S;
+  const long per = (chunks + S - 1) / S;
+  m.n_pieces = int((chunks + per - 1) / per);
+  m.piece_len = int(per * kNK);
+  return m;
+}
+size_t mq_pieces_ws_bytes(int n_seq, int H, int n_list) {
+  const MQPieces m = mq_pieces(H, n_list);
+  const size_t slots = size_t(n_seq) * m.kqb * m.n_pieces * H;
+  return ((slots * 2 * 4 + 255) / 256) * 256 + slots * kHeadDim * 4;
+}
+
+// The plain varlen dense call takes the many-query kernel (with pieces for
+// short sequences) for bf16 queries over bf16 / fp8 entries once the call has
+// enough rows to fill the chip.
+bool use_mq_varlen(int io_dtype, int ckv_dtype, int H, long n_rows) {
+  return io_dtype == CSA_BF16 && (ckv_dtype == CSA_BF16 || ckv_dtype == CSA_FP8_E4M3) &&
+         (H == 32 || H == 64 || H == 128) && n_rows >= 256;
 }
 
 // The many-query dense kernel serves bf16 queries with H in {32, 64, 128}
@@ -1466,7 +1597,7 @@ hipError_t launch_decode(const AttnArgs& a, const DecodePlan& d, hipStream_t st)
   if (e != hipSuccess || a.n_splits == 1) return e;
   const long heads = d.units / a.n_splits * a.H;
   hipLaunchKernelGGL(attn_merge_kernel<CSA_BF16>, dim3(unsigned(heads)), dim3(64), 0, st, a.part_ml, a.part_o,
-                     a.n_splits, a.H, a.out, a.lse);
+                     a.n_splits, a.H, a.out, a.lse, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -1489,9 +1620,9 @@ csa_status_t run_decode(AttnArgs a, int ckv_dtype, long rows, void* ws, size_t w
   }
   hipError_t err;
   if (ckv_dtype == CSA_FP8_E4M3)
-    err = a.row_seq ? launch_decode<CSA_FP8_E4M3, kDense, true>(a, d, st) : launch_decode<CSA_FP8_E4M3, kDense, false>(a, d, st);
+    err = a.cu_rows ? launch_decode<CSA_FP8_E4M3, kDense, true>(a, d, st) : launch_decode<CSA_FP8_E4M3, kDense, false>(a, d, st);
   else if (ckv_dtype == CSA_BF16)
-    err = a.row_seq ? launch_decode<CSA_BF16, kDense, true>(a, d, st) : launch_decode<CSA_BF16, kDense, false>(a, d, st);
+    err = a.cu_rows ? launch_decode<CSA_BF16, kDense, true>(a, d, st) : launch_decode<CSA_BF16, kDense, false>(a, d, st);
   else
     return CSA_ENOTSUP;
   return err == hipSuccess ? CSA_OK : CSA_EHIP;
@@ -1522,7 +1653,7 @@ csa_status_t run_attn(AttnArgs a, int io_dtype, int ckv_dtype, int B, void* ws, 
     err = ckv_dtype == CSA_BF16 ? launch_mq<CSA_BF16>(a, B, st) : launch_mq<CSA_FP8_E4M3>(a, B, st);
     return err == hipSuccess ? CSA_OK : CSA_EHIP;
   }
-  return a.row_seq ? tiles_for<kDense, true>(a, io_dtype, ckv_dtype, p, st)
+  return a.cu_rows ? tiles_for<kDense, true>(a, io_dtype, ckv_dtype, p, st)
                    : tiles_for<kDense, false>(a, io_dtype, ckv_dtype, p, st);
 }
 
@@ -1598,61 +1729,87 @@ csa_status_t dense_attn_impl(const void* q, int32_t io_dtype, const void* ck, co
   return run_attn<true>(a, io_dtype, ckv_dtype, B, ws, ws_bytes, static_cast<hipStream_t>(stream), invariant);
 }
 
-// Varlen: n_rows query rows of any mix of sequences (decode rows and prefill
-// chunks together), row r of sequence row_seq[r] at position row_pos[r];
-// the batch-invariant plan, so each row's bits equal those of the
-// *_batch_invariant calls on its own sequence.
-csa_status_t varlen_attn(AttnArgs a, bool dense, int io_dtype, int ckv_dtype, const int32_t* row_seq,
-                         const int32_t* row_pos, int n_rows, void* ws, size_t ws_bytes, hipStream_t st) {
-  if (n_rows > 0 && (!row_seq || !row_pos)) return CSA_EINVAL;
-  a.row_seq = row_seq;
-  a.row_pos = row_pos;
+// Varlen: n_rows packed query rows of B sequences (decode rows and prefill
+// chunks together).  invariant: the batch-invariant plan, so each row's bits
+// equal those of the *_batch_invariant calls on its own sequence; otherwise
+// the plain calls' kernels, chosen for the call as a whole.
+csa_status_t varlen_attn(AttnArgs a, bool dense, int io_dtype, int ckv_dtype, const int32_t* cu_rows, int n_rows,
+                         int B, bool invariant, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (n_rows == 0) return CSA_OK;
+  if (!cu_rows || B < 1) return CSA_EINVAL;
+  a.cu_rows = cu_rows;
+  a.n_seq = B;
   a.T_q = 1;
-  return dense ? run_attn<true>(a, io_dtype, ckv_dtype, n_rows, ws, ws_bytes, st, true)
-               : run_attn<false>(a, io_dtype, ckv_dtype, n_rows, ws, ws_bytes, st, true);
+  if (dense && !invariant && use_mq_varlen(io_dtype, ckv_dtype, a.H, n_rows)) {
+    const MQPieces m = mq_pieces(a.H, a.n_list);
+    const size_t need = mq_pieces_ws_bytes(B, a.H, a.n_list);
+    if (!ws || ws_bytes < need) return CSA_EWORKSPACE;
+    const size_t slots = size_t(B) * m.kqb * m.n_pieces * a.H;
+    a.part_ml = static_cast<float*>(ws);
+    a.part_o = reinterpret_cast<float*>(static_cast<char*>(ws) + ((slots * 2 * 4 + 255) / 256) * 256);
+    a.n_pieces = m.n_pieces;
+    a.piece_len = m.piece_len;
+    const long blocks = long(B) * m.n_pieces + (n_rows + m.kqb - 1) / m.kqb + B;
+    if (blocks > 0x7FFFFFFFL || long(B) * m.kqb * a.H > 0x7FFFFFFFL) return CSA_ENOTSUP;
+    const hipError_t err = ckv_dtype == CSA_BF16 ? launch_mq<CSA_BF16>(a, n_rows, st)
+                                                 : launch_mq<CSA_FP8_E4M3>(a, n_rows, st);
+    return err == hipSuccess ? CSA_OK : CSA_EHIP;
+  }
+  return dense ? run_attn<true>(a, io_dtype, ckv_dtype, n_rows, ws, ws_bytes, st, invariant)
+               : run_attn<false>(a, io_dtype, ckv_dtype, n_rows, ws, ws_bytes, st, invariant);
 }
 
 }  // namespace
+
+// Workspace of a varlen call in either mode (n_list = k + W or cap + W).
+size_t csa_attn_varlen_workspace_size(long n_rows, int n_seq, int H, int n_list, bool dense) {
+  size_t need = max(csa_attn_workspace_size(n_rows, H, n_list, true), csa_attn_workspace_size(n_rows, H, n_list, false));
+  if (dense && n_rows > 0) need = max(need, mq_pieces_ws_bytes(n_seq, H, n_list));
+  return need;
+}
 
 extern "C" csa_status_t csa_sparse_attn_varlen(const void* q, int32_t io_dtype, const void* ck, const void* cv,
                                                const float* ck_scale, const float* cv_scale, int32_t ckv_dtype,
                                                int32_t cap, const int32_t* idx, int32_t k, const void* k_win,
                                                const void* v_win, const int32_t* raw_pos0, int32_t L_raw,
-                                               const int32_t* row_seq, const int32_t* row_pos, int32_t n_rows,
-                                               int32_t W, int32_t B, int32_t H, int32_t d, float sm_scale, void* out,
-                                               float* lse, void* ws, size_t ws_bytes, void* stream) {
+                                               const int32_t* cu_rows, const int32_t* q_pos0, int32_t n_rows,
+                                               int32_t W, int32_t B, int32_t H, int32_t d, float sm_scale,
+                                               int32_t invariant, void* out, float* lse, void* ws, size_t ws_bytes,
+                                               void* stream) {
   if (n_rows < 0 || B < 0) return CSA_EINVAL;
   csa_status_t c = check_common(q, io_dtype, ck, cv, ck_scale, cv_scale, ckv_dtype, cap, k_win, v_win, raw_pos0, L_raw,
-                                row_pos ? row_pos : reinterpret_cast<const int32_t*>(q), W, n_rows, 1, H, d, out);
+                                q_pos0, W, n_rows, 1, H, d, out);
   if (c != CSA_OK) return c;
   if (!idx || k < 1) return CSA_EINVAL;
+  if (long(k) + W > 0x7FFFFFFFL - kNK) return CSA_ENOTSUP;
   AttnArgs a{};
   a.q = q; a.ck = ck; a.cv = cv; a.ck_scale = ck_scale; a.cv_scale = cv_scale; a.cap = cap;
   a.idx = idx; a.k = k; a.k_win = k_win; a.v_win = v_win; a.raw_pos0 = raw_pos0; a.L_raw = L_raw;
-  a.W = W; a.H = H; a.sm_log2 = sm_scale * kLog2e; a.out = out; a.lse = lse;
+  a.q_pos0 = q_pos0; a.W = W; a.H = H; a.sm_log2 = sm_scale * kLog2e; a.out = out; a.lse = lse;
   a.n_list = k + W;
-  return varlen_attn(a, false, io_dtype, ckv_dtype, row_seq, row_pos, n_rows, ws, ws_bytes,
+  return varlen_attn(a, false, io_dtype, ckv_dtype, cu_rows, n_rows, B, invariant != 0, ws, ws_bytes,
                      static_cast<hipStream_t>(stream));
 }
 
 extern "C" csa_status_t hca_dense_attn_varlen(const void* q, int32_t io_dtype, const void* ck, const void* cv,
                                               const float* ck_scale, const float* cv_scale, int32_t ckv_dtype,
                                               int32_t cap, int32_t m_prime, const void* k_win, const void* v_win,
-                                              const int32_t* raw_pos0, int32_t L_raw, const int32_t* row_seq,
-                                              const int32_t* row_pos, int32_t n_rows, int32_t W, int32_t B, int32_t H,
-                                              int32_t d, float sm_scale, void* out, float* lse, void* ws,
-                                              size_t ws_bytes, void* stream) {
+                                              const int32_t* raw_pos0, int32_t L_raw, const int32_t* cu_rows,
+                                              const int32_t* q_pos0, int32_t n_rows, int32_t W, int32_t B, int32_t H,
+                                              int32_t d, float sm_scale, int32_t invariant, void* out, float* lse,
+                                              void* ws, size_t ws_bytes, void* stream) {
   if (n_rows < 0 || B < 0) return CSA_EINVAL;
   csa_status_t c = check_common(q, io_dtype, ck, cv, ck_scale, cv_scale, ckv_dtype, cap, k_win, v_win, raw_pos0, L_raw,
-                                row_pos ? row_pos : reinterpret_cast<const int32_t*>(q), W, n_rows, 1, H, d, out);
+                                q_pos0, W, n_rows, 1, H, d, out);
   if (c != CSA_OK) return c;
   if (m_prime < 1) return CSA_EINVAL;
+  if (long(cap) + W > 0x7FFFFFFFL - kNK) return CSA_ENOTSUP;
   AttnArgs a{};
   a.q = q; a.ck = ck; a.cv = cv; a.ck_scale = ck_scale; a.cv_scale = cv_scale; a.cap = cap;
   a.idx = nullptr; a.k = m_prime; a.k_win = k_win; a.v_win = v_win; a.raw_pos0 = raw_pos0; a.L_raw = L_raw;
-  a.W = W; a.H = H; a.sm_log2 = sm_scale * kLog2e; a.out = out; a.lse = lse;
+  a.q_pos0 = q_pos0; a.W = W; a.H = H; a.sm_log2 = sm_scale * kLog2e; a.out = out; a.lse = lse;
   a.n_list = cap + W;
-  return varlen_attn(a, true, io_dtype, ckv_dtype, row_seq, row_pos, n_rows, ws, ws_bytes,
+  return varlen_attn(a, true, io_dtype, ckv_dtype, cu_rows, n_rows, B, invariant != 0, ws, ws_bytes,
                      static_cast<hipStream_t>(stream));
 }
 

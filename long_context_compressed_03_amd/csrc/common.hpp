@@ -216,6 +216,19 @@ CSA_DEV uint32_t block_reduce_or(uint32_t v, uint32_t* smem) {
 }
 
 // --------------------------------------------------------------- status --
+// Packed items of several sequences (the varlen calls): sequence b owns items
+// cu[b] .. cu[b + 1] - 1 (cu[0] = 0, non-decreasing).  Sequence of item r
+// (r < cu[B]), by binary search over the B + 1 offsets.
+CSA_DEV int csa_packed_seq(const int32_t* __restrict__ cu, int B, int r) {
+  int lo = 0, hi = B;   // cu[lo] <= r < cu[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= r) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
 #define CSA_CHECK_LAUNCH()                                   \
   do {                                                       \
     if (hipGetLastError() != hipSuccess) return CSA_EHIP;    \

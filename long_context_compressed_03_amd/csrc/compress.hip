@@ -27,10 +27,17 @@ template <int kInF32, int kOut>
 __global__ __launch_bounds__(kBlock) void compress_kernel(const void* __restrict__ k, const void* __restrict__ v,
                                                           const float* __restrict__ logits, int B, int n_entries,
                                                           int ld_in, int m, void* k_out, void* v_out,
-                                                          float* k_scale, float* v_scale, int ld_out) {
+                                                          float* k_scale, float* v_scale, int ld_out,
+                                                          PackedEntries pk) {
   const int lane_c = threadIdx.x & (kGroup - 1);
   const long gid = long(blockIdx.x) * (blockDim.x / kGroup) + (threadIdx.x / kGroup);
   if (gid >= long(B) * n_entries) return;  // whole 16-lane groups exit together
+  if (pk.cu) {   // packed: B = 1, n_entries = all sequences' entries
+    size_t row, entry;
+    packed_entry(pk, int(gid), ld_in, m, ld_out, &row, &entry);
+    compress_group_at<kInF32, kOut>(k, v, logits, row, m, k_out, v_out, k_scale, v_scale, entry, lane_c);
+    return;
+  }
   compress_group<kInF32, kOut>(k, v, logits, n_entries, ld_in, m, k_out, v_out, k_scale, v_scale, ld_out, gid, lane_c);
 }
 
@@ -85,7 +92,7 @@ __global__ __launch_bounds__(kBlock) void compress_long_kernel(const void* __res
                                                                const float* __restrict__ logits, int n_entries,
                                                                int ld_in, int m, void* k_out, void* v_out,
                                                                float* k_scale, float* v_scale, int ld_out,
-                                                               AppendArgs app) {
+                                                               AppendArgs app, PackedEntries pk) {
   __shared__ float part[kEntriesPerBlock][kHeadDim + 4];
   __shared__ float wz[kBlock];              // exp(z_r - max) of the first 256 rows
   __shared__ float red[2][kBlock / 64];
@@ -122,6 +129,11 @@ __global__ __launch_bounds__(kBlock) void compress_long_kernel(const void* __res
     row0 = ring0 + pl.first_row;
     newest = nrow;
     znew = app.z_new + b;
+  } else if (pk.cu) {   // packed: the entry's sequence b and slot e within it
+    b = csa_packed_seq(pk.cu, pk.B, int(blockIdx.x));
+    const int j = int(blockIdx.x) - pk.cu[b];
+    e = pk.entry0[b] + j;
+    row0 = size_t(b) * ld_in + size_t(pk.row0[b]) + size_t(j) * m;
   } else {
     b = blockIdx.x / n_entries;
     e = blockIdx.x - b * n_entries;
@@ -231,35 +243,35 @@ __global__ __launch_bounds__(kBlock) void compress_long_kernel(const void* __res
   }
 }
 
+// total = B * ne entries (packed: B = 1, ne = all entries, pk.cu set)
 template <int kInF32, int kOut>
-hipError_t launch_one(dim3 grid_short, long total, hipStream_t st, const void* k, const void* v, const float* lg, int B,
-                      int ne, int ld_in, int m, void* ko, void* vo, float* ks, float* vs, int ld_out) {
-  (void)grid_short;
+hipError_t launch_one(long total, hipStream_t st, const void* k, const void* v, const float* lg, int B, int ne,
+                      int ld_in, int m, void* ko, void* vo, float* ks, float* vs, int ld_out, const PackedEntries& pk) {
   if (m >= 32) {
     hipLaunchKernelGGL((compress_long_kernel<kInF32, kOut, false>), dim3(unsigned(total), 2u), dim3(kBlock), 0, st, k, v,
-                       lg, ne, ld_in, m, ko, vo, ks, vs, ld_out, AppendArgs{});
+                       lg, ne, ld_in, m, ko, vo, ks, vs, ld_out, AppendArgs{}, pk);
   } else {
     // few entries (decoding): 4 per 64-thread block, so their rows are
     // fetched by several CUs; otherwise 16 per 256-thread block
     const int threads = total <= 256 ? 64 : kBlock;
     const long per = threads / kGroup;
     hipLaunchKernelGGL((compress_kernel<kInF32, kOut>), dim3(unsigned((total + per - 1) / per)), dim3(threads), 0, st,
-                       k, v, lg, B, ne, ld_in, m, ko, vo, ks, vs, ld_out);
+                       k, v, lg, B, ne, ld_in, m, ko, vo, ks, vs, ld_out, pk);
   }
   return hipGetLastError();
 }
 
 template <int kInF32>
-hipError_t launch_compress(int out_dt, dim3 grid, long total, hipStream_t st, const void* k, const void* v,
-                           const float* lg, int B, int ne, int ld_in, int m, void* ko, void* vo, float* ks, float* vs,
-                           int ld_out) {
+hipError_t launch_compress(int out_dt, long total, hipStream_t st, const void* k, const void* v, const float* lg, int B,
+                           int ne, int ld_in, int m, void* ko, void* vo, float* ks, float* vs, int ld_out,
+                           const PackedEntries& pk = PackedEntries{}) {
   switch (out_dt) {
     case CSA_BF16:
-      return launch_one<kInF32, CSA_BF16>(grid, total, st, k, v, lg, B, ne, ld_in, m, ko, vo, ks, vs, ld_out);
+      return launch_one<kInF32, CSA_BF16>(total, st, k, v, lg, B, ne, ld_in, m, ko, vo, ks, vs, ld_out, pk);
     case CSA_F32:
-      return launch_one<kInF32, CSA_F32>(grid, total, st, k, v, lg, B, ne, ld_in, m, ko, vo, ks, vs, ld_out);
+      return launch_one<kInF32, CSA_F32>(total, st, k, v, lg, B, ne, ld_in, m, ko, vo, ks, vs, ld_out, pk);
     default:
-      return launch_one<kInF32, CSA_FP8_E4M3>(grid, total, st, k, v, lg, B, ne, ld_in, m, ko, vo, ks, vs, ld_out);
+      return launch_one<kInF32, CSA_FP8_E4M3>(total, st, k, v, lg, B, ne, ld_in, m, ko, vo, ks, vs, ld_out, pk);
   }
 }
 
@@ -267,7 +279,8 @@ template <int kInF32, int kOut>
 hipError_t launch_cache_append_one(const AppendArgs& a, hipStream_t st) {
   if (a.m >= 32) {
     hipLaunchKernelGGL((compress_long_kernel<kInF32, kOut, true>), dim3(unsigned(a.B), 2u), dim3(kBlock), 0, st,
-                       a.k_ring, a.v_ring, a.z_ring, a.B, 2 * a.L, a.m, a.ck, a.cv, a.ck_scale, a.cv_scale, a.cap, a);
+                       a.k_ring, a.v_ring, a.z_ring, a.B, 2 * a.L, a.m, a.ck, a.cv, a.ck_scale, a.cv_scale, a.cap, a,
+                       PackedEntries{});
   } else {
     constexpr int kPer = 64 / kGroup;    // 4 sequences per 64-thread block
     hipLaunchKernelGGL((cache_append_short_kernel<kInF32, kOut>), dim3(unsigned((a.B + kPer - 1) / kPer)), dim3(64),
@@ -306,9 +319,34 @@ extern "C" csa_status_t csa_compress_kv(const void* k, const void* v, int32_t in
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (total > 0x7FFFFFFFL) return CSA_EINVAL;
   hipError_t err = in_dtype == CSA_F32
-                       ? launch_compress<1>(out_dtype, dim3(unsigned(blocks)), total, st, k, v, logits, B, ne, ld_in, m,
-                                            k_out, v_out, k_scale_out, v_scale_out, ld_out)
-                       : launch_compress<0>(out_dtype, dim3(unsigned(blocks)), total, st, k, v, logits, B, ne, ld_in, m,
-                                            k_out, v_out, k_scale_out, v_scale_out, ld_out);
+                       ? launch_compress<1>(out_dtype, total, st, k, v, logits, B, ne, ld_in, m, k_out, v_out,
+                                            k_scale_out, v_scale_out, ld_out)
+                       : launch_compress<0>(out_dtype, total, st, k, v, logits, B, ne, ld_in, m, k_out, v_out,
+                                            k_scale_out, v_scale_out, ld_out);
+  return err == hipSuccess ? CSA_OK : CSA_EHIP;
+}
+
+// New entries of several sequences in one launch (a mixed decode/prefill
+// step): entry j of sequence b pools its rows row0[b] + j*m .. into slot
+// entry0[b] + j, exactly as csa_compress_kv pools a block.
+extern "C" csa_status_t csa_compress_kv_varlen(const void* k, const void* v, int32_t in_dtype, const float* logits,
+                                               int32_t B, int32_t ld_in, int32_t d, int32_t m,
+                                               const int32_t* cu_entries, const int32_t* row0,
+                                               const int32_t* entry0, int32_t n_entries, void* k_out, void* v_out,
+                                               float* k_scale_out, float* v_scale_out, int32_t ld_out,
+                                               int32_t out_dtype, void* stream) {
+  const CompressArgs ca{k, v, logits, in_dtype, B, 0, ld_in, m, ld_out, out_dtype, k_out, v_out, k_scale_out, v_scale_out};
+  const csa_status_t chk = check_compress_args(ca, d);
+  if (chk != CSA_OK) return chk;
+  if (n_entries < 0 || ld_in < m || ld_out < 1) return CSA_EINVAL;
+  if (n_entries == 0) return CSA_OK;
+  if (B < 1 || !cu_entries || !row0 || !entry0) return CSA_EINVAL;
+  const PackedEntries pk{cu_entries, row0, entry0, B};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err = in_dtype == CSA_F32
+                       ? launch_compress<1>(out_dtype, n_entries, st, k, v, logits, 1, n_entries, ld_in, m, k_out,
+                                            v_out, k_scale_out, v_scale_out, ld_out, pk)
+                       : launch_compress<0>(out_dtype, n_entries, st, k, v, logits, 1, n_entries, ld_in, m, k_out,
+                                            v_out, k_scale_out, v_scale_out, ld_out, pk);
   return err == hipSuccess ? CSA_OK : CSA_EHIP;
 }

@@ -160,6 +160,26 @@ CSA_DEV void compress_group(const void* __restrict__ k, const void* __restrict__
                                   size_t(b) * ld_out + e, lane_c);
 }
 
+// Packed new entries of several sequences (csa_compress_kv_varlen): sequence
+// b's entries are items cu[b] .. cu[b + 1] - 1; its j-th pools raw rows
+// row0[b] + j*m .. of that sequence into entry entry0[b] + j.  cu == nullptr:
+// the plain layout (B sequences of n_entries entries from row 0 / entry 0).
+struct PackedEntries {
+  const int32_t* cu;
+  const int32_t* row0;
+  const int32_t* entry0;
+  int B;
+};
+
+// Raw row of the block and output slot of packed entry gid.
+CSA_DEV void packed_entry(const PackedEntries& p, int gid, int ld_in, int m, int ld_out, size_t* row,
+                          size_t* entry) {
+  const int b = csa_packed_seq(p.cu, p.B, gid);
+  const int j = gid - p.cu[b];
+  *row = size_t(b) * ld_in + size_t(p.row0[b]) + size_t(j) * m;
+  *entry = size_t(b) * ld_out + size_t(p.entry0[b]) + j;
+}
+
 // One decode token per sequence into the mirrored window ring, and the pool
 // of a block it completes (the cache append; see cache.hip for the layout).
 struct AppendArgs {

@@ -124,6 +124,25 @@ CSA_DEV void load_b(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t re, uint32
   }
 }
 
+// Row tile `tile` of a packed batch: sequence b's rows are cut into tiles of
+// `per` rows each, sequences in order; sets the tile's sequence and its first
+// row within it.  False past the last tile (the grid is a bound: at most
+// ceil(n_rows / per) + B tiles).
+CSA_DEV bool tile_of_packed(const int32_t* __restrict__ cu_rows, int B, int per, int tile, int* b, int* q_first) {
+  int t = 0;
+  for (int s = 0; s < B; ++s) {
+    const int n = cu_rows[s + 1] - cu_rows[s];
+    const int tiles = (n + per - 1) / per;
+    if (tile < t + tiles) {
+      *b = s;
+      *q_first = (tile - t) * per;
+      return true;
+    }
+    t += tiles;
+  }
+  return false;
+}
+
 // kHI: indexer heads (4, 8 or 16); kRT: 16-row tiles per block; kKS: 128-wide
 // contraction steps; kFrag: 16-entry fragments per wave per batch of loads;
 // kStream: keys read once (decode) with non-temporal loads; kOut: fp32
@@ -140,14 +159,27 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
                                                          const uint8_t* __restrict__ k_codes,
                                                          const uint8_t* __restrict__ k_e8m0,
                                                          const int32_t* __restrict__ q_pos0, int T_q, int d_I,
-                                                         int cap, int m, int entries_per_wave, void* __restrict__ out) {
+                                                         int cap, int m, int entries_per_wave, void* __restrict__ out,
+                                                         const int32_t* __restrict__ cu_rows, int n_seq) {
   constexpr int kQPT = 16 / kHI;  // queries per row tile
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int col = lane & 15;
   const int g = lane >> 4;
-  const int b = blockIdx.z;
-  const int q_block = blockIdx.y * kRT * kQPT;
+  // this block's sequence b, its queries q_block .. (T_q of them), and the
+  // packed row of its query 0 (row_base); packed batches (cu_rows) find the
+  // sequence from the tile index
+  int b, q_block;
+  size_t row_base;
+  if (cu_rows) {
+    if (!tile_of_packed(cu_rows, n_seq, kRT * kQPT, blockIdx.y, &b, &q_block)) return;
+    row_base = size_t(cu_rows[b]);
+    T_q = cu_rows[b + 1] - cu_rows[b];
+  } else {
+    b = blockIdx.z;
+    q_block = blockIdx.y * kRT * kQPT;
+    row_base = size_t(b) * T_q;
+  }
   const int nblk = d_I >> 5;            // 32-element blocks per vector
   const int row_bytes = d_I >> 1;
   const int pos0 = q_pos0[b];
@@ -162,13 +194,13 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
     const int r = rt * 16 + col;
     const int q = q_block + r / kHI;
     const int h = r % kHI;
-    load_a<kHI, kKS>(q_codes, q_e8m0, (size_t(b) * T_q + q) * kHI + h, q < T_q, g, nblk, row_bytes, a[rt], sa[rt]);
+    load_a<kHI, kKS>(q_codes, q_e8m0, (row_base + q) * kHI + h, q < T_q, g, nblk, row_bytes, a[rt], sa[rt]);
     const int rc = rt * 16 + 4 * g;  // first C row this lane holds
     const int qc = q_block + rc / kHI;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hh = (rc + i) % kHI;
-      wv[rt][i] = qc < T_q ? w[(size_t(b) * T_q + qc) * kHI + hh] : 0.f;
+      wv[rt][i] = qc < T_q ? w[(row_base + qc) * kHI + hh] : 0.f;
     }
     int nv = 0;
     if (qc < T_q) nv = min((pos0 + qc + 1) / m, cap);
@@ -195,7 +227,7 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
   for (int rt = 0; rt < kRT; ++rt) {
     const int q = q_block + (rt * 16 + 4 * g) / kHI;
     q_in[rt] = q < T_q;
-    orow[rt] = (size_t(b) * T_q + (q < T_q ? q : 0)) * cap;
+    orow[rt] = (row_base + (q < T_q ? q : 0)) * cap;
   }
   auto put = [&](int rt, int e, float p) {
     if (q_in[rt] && e < e_wave1) {
@@ -280,7 +312,7 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
 template <int kHI, int kRT, int kKS, bool kStream, int kOut>
 hipError_t launch_indexer_ks(const uint8_t* qc, const uint8_t* qe, const float* w, const uint8_t* kc,
                              const uint8_t* ke, const int32_t* pos, int B, int T_q, int d_I, int cap, int m,
-                             void* out, hipStream_t st) {
+                             void* out, hipStream_t st, const int32_t* cu_rows, int n_rows) {
   constexpr int kFrag = 4;
   constexpr int kQPT = 16 / kHI;
   const int entries_per_wave = kStream ? 16 * kFrag : 256;   // streaming: one batch per wave
@@ -290,33 +322,36 @@ hipError_t launch_indexer_ks(const uint8_t* qc, const uint8_t* qe, const float* 
   // runs on XCD x % 8, so each XCD's L2 holds a fixed eighth of the keys
   // while the query tiles stream past it.  Padding blocks exit at once.
   const int n_eb = ((cap + per_block - 1) / per_block + 7) / 8 * 8;
-  dim3 grid(n_eb, (T_q + kRT * kQPT - 1) / (kRT * kQPT), B);
+  // packed batches (cu_rows): a bound on the tiles, sequences found in the kernel
+  const dim3 grid = cu_rows ? dim3(n_eb, (n_rows + kRT * kQPT - 1) / (kRT * kQPT) + B, 1)
+                            : dim3(n_eb, (T_q + kRT * kQPT - 1) / (kRT * kQPT), B);
   hipLaunchKernelGGL((indexer_kernel<kHI, kRT, kKS, kFrag, kStream, kOut>), grid, dim3(kBlock), 0, st, qc, qe, w,
-                     kc, ke, pos, T_q, d_I, cap, m, entries_per_wave, out);
+                     kc, ke, pos, T_q, d_I, cap, m, entries_per_wave, out, cu_rows, B);
   return hipGetLastError();
 }
 
 template <int kHI, int kRT, bool kStream, int kOut>
 hipError_t launch_indexer_rt(int ks, const uint8_t* qc, const uint8_t* qe, const float* w, const uint8_t* kc,
                              const uint8_t* ke, const int32_t* pos, int B, int T_q, int d_I, int cap, int m,
-                             void* out, hipStream_t st) {
+                             void* out, hipStream_t st, const int32_t* cu_rows, int n_rows) {
   switch (ks) {
-    case 1: return launch_indexer_ks<kHI, kRT, 1, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
-    case 2: return launch_indexer_ks<kHI, kRT, 2, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
-    case 3: return launch_indexer_ks<kHI, kRT, 3, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
-    default: return launch_indexer_ks<kHI, kRT, 4, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
+    case 1: return launch_indexer_ks<kHI, kRT, 1, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
+    case 2: return launch_indexer_ks<kHI, kRT, 2, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
+    case 3: return launch_indexer_ks<kHI, kRT, 3, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
+    default: return launch_indexer_ks<kHI, kRT, 4, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
   }
 }
 
 template <int kHI, int kOut>
 hipError_t launch_indexer_h(int ks, const uint8_t* qc, const uint8_t* qe, const float* w, const uint8_t* kc,
                             const uint8_t* ke, const int32_t* pos, int B, int T_q, int d_I, int cap, int m,
-                            void* out, hipStream_t st) {
+                            void* out, hipStream_t st, const int32_t* cu_rows, int n_rows) {
   // one row tile when the whole call has at most one tile of queries (decode);
-  // several otherwise so every key fragment feeds several MFMAs
-  if (T_q * kHI <= 16)
-    return launch_indexer_rt<kHI, 1, true, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
-  return launch_indexer_rt<kHI, 4, false, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
+  // several otherwise so every key fragment feeds several MFMAs (packed batches
+  // always take the several-tile form)
+  if (!cu_rows && T_q * kHI <= 16)
+    return launch_indexer_rt<kHI, 1, true, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
+  return launch_indexer_rt<kHI, 4, false, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
 }
 
 // Shared argument checks of the two indexer entry points.
@@ -332,15 +367,17 @@ inline csa_status_t check_indexer_args(const void* q_codes, const void* q_e8m0, 
   return CSA_OK;
 }
 
+// cu_rows (device, or null): packed rows of B sequences, n_rows in all (T_q
+// unused); otherwise B sequences of T_q rows each.
 template <int kOut>
 hipError_t launch_indexer(int H_I, const uint8_t* qc, const uint8_t* qe, const float* w, const uint8_t* kc,
                           const uint8_t* ke, const int32_t* pos, int B, int T_q, int d_I, int cap, int m, void* out,
-                          hipStream_t st) {
+                          hipStream_t st, const int32_t* cu_rows = nullptr, int n_rows = 0) {
   const int ks = (d_I + 127) / 128;
   switch (H_I) {
-    case 4: return launch_indexer_h<4, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
-    case 8: return launch_indexer_h<8, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
-    default: return launch_indexer_h<16, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st);
+    case 4: return launch_indexer_h<4, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
+    case 8: return launch_indexer_h<8, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
+    default: return launch_indexer_h<16, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
   }
 }
 

@@ -329,16 +329,18 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const uint16_t* __rest
                                                           const uint8_t* __restrict__ k_codes,
                                                           const uint8_t* __restrict__ k_e8m0,
                                                           const int32_t* __restrict__ q_pos0, int T_q, int d_I,
-                                                          int cap, int m, int k, int32_t* __restrict__ idx) {
+                                                          int cap, int m, int k, int32_t* __restrict__ idx,
+                                                          const int32_t* __restrict__ cu_rows, int n_seq) {
   constexpr int kS = kJ * kRound;          // keys per chunk; chunk 0 stays in registers
   constexpr int kWPT = (kS / 32 + kThreads - 1) / kThreads;  // bitmap words per thread (the last ones may be past the chunk)
   static_assert(kS < (1 << 17), "a chunk's equal counts fit 17 bits");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   Shared& sh = *reinterpret_cast<Shared*>(smem_raw);
 
+  // row = packed row (sequence b, query i of it); cu_rows: packed batches
   const int row = blockIdx.x;
-  const int b = row / T_q;
-  const int i = row - b * T_q;
+  const int b = cu_rows ? csa_packed_seq(cu_rows, n_seq, row) : row / T_q;
+  const int i = cu_rows ? row - cu_rows[b] : row - b * T_q;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int t = q_pos0[b] + i;
@@ -461,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const uint16_t* __rest
   // ---- d: exact keys of T's class, radix refinement
   Rescore<kHI, kKS> R;
   if (!whole) {
-    rescore_setup<kHI, kKS>(R, q_codes, q_e8m0, w, size_t(b) * T_q + i, i, nblk, row_bytes);
+    rescore_setup<kHI, kKS>(R, q_codes, q_e8m0, w, size_t(row), i, nblk, row_bytes);
     if (!crowded) {
       if (hit) {
         // the class is a subset of the window list
@@ -753,38 +755,39 @@ size_t split_scores_bytes(long rows, int cap) { return (size_t(rows) * size_t(ca
 template <int kHI, int kKS, int kJ>
 hipError_t launch_select_j(long rows, hipStream_t st, const uint16_t* key16, const uint8_t* qc, const uint8_t* qe,
                            const float* w, const uint8_t* kc, const uint8_t* ke, const int32_t* pos, int T_q,
-                           int d_I, int cap, int m, int k, int32_t* idx) {
+                           int d_I, int cap, int m, int k, int32_t* idx, const int32_t* cu_rows, int n_seq) {
   if (hipError_t e = csa_lds_opt_in(reinterpret_cast<const void*>(&select_kernel<kHI, kKS, kJ>), sizeof(Shared));
       e != hipSuccess)
     return e;
   hipLaunchKernelGGL((select_kernel<kHI, kKS, kJ>), dim3(unsigned(rows)), dim3(kThreads), sizeof(Shared), st, key16, qc, qe, w, kc, ke, pos, T_q,
-                     d_I, cap, m, k, idx);
+                     d_I, cap, m, k, idx, cu_rows, n_seq);
   return hipGetLastError();
 }
 
 template <int kHI, int kKS>
 hipError_t launch_select_ks(long rows, hipStream_t st, const uint16_t* key16, const uint8_t* qc, const uint8_t* qe,
                             const float* w, const uint8_t* kc, const uint8_t* ke, const int32_t* pos, int T_q,
-                            int d_I, int cap, int m, int k, int32_t* idx) {
+                            int d_I, int cap, int m, int k, int32_t* idx, const int32_t* cu_rows, int n_seq) {
   // rows of up to 32768 keys are held whole in 8 rounds of registers; longer
   // rows keep their first 81920 keys in 20 rounds (65536 in 16 when d_I > 128
   // leaves fewer registers free) and read the rest
   if (cap <= 8 * kRound)
-    return launch_select_j<kHI, kKS, 8>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx);
+    return launch_select_j<kHI, kKS, 8>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq);
   if constexpr (kKS == 1)
-    return launch_select_j<kHI, kKS, 20>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx);
-  return launch_select_j<kHI, kKS, 16>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx);
+    return launch_select_j<kHI, kKS, 20>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq);
+  return launch_select_j<kHI, kKS, 16>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq);
 }
 
 template <int kHI>
 hipError_t launch_select_h(int ks, long rows, hipStream_t st, const uint16_t* key16, const uint8_t* qc,
                            const uint8_t* qe, const float* w, const uint8_t* kc, const uint8_t* ke,
-                           const int32_t* pos, int T_q, int d_I, int cap, int m, int k, int32_t* idx) {
+                           const int32_t* pos, int T_q, int d_I, int cap, int m, int k, int32_t* idx,
+                           const int32_t* cu_rows, int n_seq) {
   switch (ks) {
-    case 1: return launch_select_ks<kHI, 1>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx);
-    case 2: return launch_select_ks<kHI, 2>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx);
-    case 3: return launch_select_ks<kHI, 3>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx);
-    default: return launch_select_ks<kHI, 4>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx);
+    case 1: return launch_select_ks<kHI, 1>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq);
+    case 2: return launch_select_ks<kHI, 2>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq);
+    case 3: return launch_select_ks<kHI, 3>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq);
+    default: return launch_select_ks<kHI, 4>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq);
   }
 }
 
@@ -847,9 +850,9 @@ csa_status_t indexer_topk_impl(const uint8_t* q_codes, const uint8_t* q_e8m0, co
     if (err != hipSuccess) return CSA_EHIP;
   }
   switch (H_I) {
-    case 4: err = launch_select_h<4>(ks, rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_q, d_I, cap, m, k, idx); break;
-    case 8: err = launch_select_h<8>(ks, rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_q, d_I, cap, m, k, idx); break;
-    default: err = launch_select_h<16>(ks, rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_q, d_I, cap, m, k, idx); break;
+    case 4: err = launch_select_h<4>(ks, rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_q, d_I, cap, m, k, idx, nullptr, 0); break;
+    case 8: err = launch_select_h<8>(ks, rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_q, d_I, cap, m, k, idx, nullptr, 0); break;
+    default: err = launch_select_h<16>(ks, rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_q, d_I, cap, m, k, idx, nullptr, 0); break;
   }
   return err == hipSuccess ? CSA_OK : CSA_EHIP;
 }
@@ -878,4 +881,40 @@ extern "C" csa_status_t csa_compress_indexer_topk(const void* k, const void* v, 
   if (c != CSA_OK) return c;
   return indexer_topk_impl(q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, B, T_q, H_I, d_I, cap, m, k_sel, idx, ws,
                            ws_bytes, static_cast<hipStream_t>(stream), &ca);
+}
+
+// Packed rows of several sequences (decode rows and prefill chunks together):
+// the indexer over row tiles of one sequence each, then the per-row select,
+// exactly as csa_indexer_topk does for one sequence's chunk.
+extern "C" csa_status_t csa_indexer_topk_varlen(const uint8_t* q_codes, const uint8_t* q_e8m0, const float* w,
+                                                const uint8_t* k_codes, const uint8_t* k_e8m0, const int32_t* cu_rows,
+                                                const int32_t* q_pos0, int32_t B, int32_t n_rows, int32_t H_I,
+                                                int32_t d_I, int32_t cap, int32_t m, int32_t k, int32_t* idx,
+                                                void* ws, size_t ws_bytes, void* stream) {
+  if (!idx || !cu_rows || k < 1 || n_rows < 0) return CSA_EINVAL;
+  const csa_status_t s = csa_ix::check_indexer_args(q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, B, 1, H_I, d_I,
+                                                    cap, m);
+  if (s != CSA_OK) return s;
+  if (k > 32767) return CSA_ENOTSUP;
+  if (n_rows == 0) return CSA_OK;
+  if (B < 1) return CSA_EINVAL;
+  const int per_tile = 64 / H_I;   // queries per row tile of the packed indexer launch
+  if ((long(n_rows) + per_tile - 1) / per_tile + B > 65535) return CSA_ENOTSUP;
+  const size_t need = size_t(n_rows) * size_t(cap) * 2u;
+  if (need > 0 && (!ws || ws_bytes < need)) return CSA_EWORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int ks = (d_I + 127) / 128;
+  uint16_t* key16 = static_cast<uint16_t*>(ws);
+  hipError_t err = hipSuccess;
+  if (cap > 0) {
+    err = csa_ix::launch_indexer<csa_ix::kKey16>(H_I, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, B, 1, d_I, cap, m,
+                                                 key16, st, cu_rows, n_rows);
+    if (err != hipSuccess) return CSA_EHIP;
+  }
+  switch (H_I) {
+    case 4: err = launch_select_h<4>(ks, n_rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, 1, d_I, cap, m, k, idx, cu_rows, B); break;
+    case 8: err = launch_select_h<8>(ks, n_rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, 1, d_I, cap, m, k, idx, cu_rows, B); break;
+    default: err = launch_select_h<16>(ks, n_rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, 1, d_I, cap, m, k, idx, cu_rows, B); break;
+  }
+  return err == hipSuccess ? CSA_OK : CSA_EHIP;
 }

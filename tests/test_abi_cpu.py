@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 def test_status_strings_and_version():
     import long_context_compressed_03_amd as csa
     lib = csa.load()
-    assert lib.csa_abi_version() == 103
+    assert lib.csa_abi_version() == 104
     for s in range(6):
         assert lib.csa_status_str(s).decode().startswith("CSA_")
 
@@ -247,21 +247,68 @@ def test_cache_varlen_and_appended_quantize_reject_bad_arguments():
     assert quant(m=0) == csa.CSA_EINVAL
     assert quant(pos=None) == csa.CSA_EINVAL
 
-    def sparse_vl(H=64, k=64, row_seq=_p(), row_pos=_p(), n_rows=3, ws=None, nws=0):
+    def sparse_vl(H=64, k=64, cu=_p(), pos=_p(), n_rows=3, B=2, inv=1, ws=None, nws=0):
         return lib.csa_sparse_attn_varlen(_p(), 0, _p(), _p(), None, None, 0, 16, _p(), k, _p(), _p(), _p(), 8,
-                                          row_seq, row_pos, n_rows, 4, 2, H, 128, 0.1, _p(), None, ws, nws, None)
+                                          cu, pos, n_rows, 4, B, H, 128, 0.1, inv, _p(), None, ws, nws, None)
     assert sparse_vl(H=24) == csa.CSA_ENOTSUP
     assert sparse_vl(k=0) == csa.CSA_EINVAL
-    assert sparse_vl(row_seq=None) == csa.CSA_EINVAL
-    assert sparse_vl(row_pos=None) == csa.CSA_EINVAL
+    assert sparse_vl(cu=None) == csa.CSA_EINVAL
+    assert sparse_vl(pos=None) == csa.CSA_EINVAL
     assert sparse_vl(n_rows=-1) == csa.CSA_EINVAL
-    # a 1024 + 128 key list is cut into pieces: the workspace is mandatory
-    need = lib.csa_workspace_size(csa.CSA_OP_SPARSE_ATTN_BATCH_INVARIANT, 3, 1, 64, 128, 1024 + 4)
-    assert need > 0
-    assert sparse_vl(k=1024) == csa.CSA_EWORKSPACE
-    assert sparse_vl(k=1024, ws=_p(), nws=need - 1) == csa.CSA_EWORKSPACE
+    assert sparse_vl(B=0) == csa.CSA_EINVAL            # rows but no sequences
+    assert sparse_vl(n_rows=0, cu=None) == csa.CSA_OK   # no rows: nothing launched
+    # a 1024 + 128 key list is cut into pieces: the workspace is mandatory, in either mode
+    need = lib.csa_workspace_size(csa.CSA_OP_SPARSE_ATTN_VARLEN, 3, 2, 64, 128, 1024 + 4)
+    assert need >= lib.csa_workspace_size(csa.CSA_OP_SPARSE_ATTN_BATCH_INVARIANT, 3, 1, 64, 128, 1024 + 4) > 0
+    for inv, op in ((0, csa.CSA_OP_SPARSE_ATTN), (1, csa.CSA_OP_SPARSE_ATTN_BATCH_INVARIANT)):
+        own = lib.csa_workspace_size(op, 3, 1, 64, 128, 1024 + 4)    # what this mode itself needs
+        assert 0 < own <= need
+        assert sparse_vl(k=1024, inv=inv) == csa.CSA_EWORKSPACE
+        assert sparse_vl(k=1024, inv=inv, ws=_p(), nws=own - 1) == csa.CSA_EWORKSPACE
     assert lib.hca_dense_attn_varlen(_p(), 0, _p(), _p(), None, None, 0, 16, 0, _p(), _p(), _p(), 8, _p(), _p(),
-                                     3, 4, 2, 64, 128, 0.1, _p(), None, None, 0, None) == csa.CSA_EINVAL
+                                     3, 4, 2, 64, 128, 0.1, 1, _p(), None, None, 0, None) == csa.CSA_EINVAL
+    # the plain dense mode of many rows: the many-query kernel's pieces need their partials
+    n_mq = lib.csa_workspace_size(csa.CSA_OP_DENSE_ATTN_VARLEN, 300, 5, 64, 128, 8192 + 128)
+    assert n_mq > 0
+    assert lib.hca_dense_attn_varlen(_p(), 0, _p(), _p(), None, None, 0, 8192, 128, _p(), _p(), _p(), 2176, _p(),
+                                     _p(), 300, 128, 5, 64, 128, 0.1, 0, _p(), None, _p(), n_mq - 1,
+                                     None) == csa.CSA_EWORKSPACE
+
+
+def test_varlen_compress_and_selection_reject_bad_arguments():
+    import long_context_compressed_03_amd as csa
+    lib = csa.load()
+
+    def comp(B=3, ld_in=16, d=128, m=4, cu=_p(), r0=_p(), e0=_p(), n=5, ld_out=8, out_dt=0, ks=None):
+        return lib.csa_compress_kv_varlen(_p(), _p(), 0, _p(), B, ld_in, d, m, cu, r0, e0, n, _p(), _p(), ks, ks,
+                                          ld_out, out_dt, None)
+    assert comp(d=64) == csa.CSA_EINVAL
+    assert comp(m=0) == csa.CSA_EINVAL
+    assert comp(ld_in=2) == csa.CSA_EINVAL            # not one block of rows per sequence
+    assert comp(cu=None) == csa.CSA_EINVAL
+    assert comp(r0=None) == csa.CSA_EINVAL
+    assert comp(e0=None) == csa.CSA_EINVAL
+    assert comp(n=-1) == csa.CSA_EINVAL
+    assert comp(out_dt=2) == csa.CSA_EINVAL           # fp8 entries without scales
+    assert comp(B=0) == csa.CSA_EINVAL                # entries but no sequences
+    assert comp(n=0, cu=None) == csa.CSA_OK           # nothing to pool, nothing launched
+
+    def sel(B=2, n_rows=5, H_I=8, d_I=128, cap=64, k=16, cu=_p(), idx=_p(), ws=None, nws=0):
+        return lib.csa_indexer_topk_varlen(_p(), _p(), _p(), _p(), _p(), cu, _p(), B, n_rows, H_I, d_I, cap, 4, k,
+                                           idx, ws, nws, None)
+    assert sel(H_I=6) == csa.CSA_ENOTSUP
+    assert sel(d_I=48) == csa.CSA_EINVAL
+    assert sel(k=0) == csa.CSA_EINVAL
+    assert sel(k=40000) == csa.CSA_ENOTSUP
+    assert sel(cu=None) == csa.CSA_EINVAL
+    assert sel(idx=None) == csa.CSA_EINVAL
+    assert sel(n_rows=-1) == csa.CSA_EINVAL
+    assert sel(n_rows=0) == csa.CSA_OK                 # no rows: nothing launched
+    need = lib.csa_workspace_size(csa.CSA_OP_INDEXER_TOPK_VARLEN, 5, 0, 0, 0, 64)
+    assert need == 5 * 64 * 2
+    assert sel() == csa.CSA_EWORKSPACE
+    assert sel(ws=_p(), nws=need - 1) == csa.CSA_EWORKSPACE
+    assert sel(B=60000, n_rows=200000, ws=_p(), nws=1 << 40) == csa.CSA_ENOTSUP   # too many row tiles
 
 
 def test_binding_fails_loudly_without_gpu_tensors():

@@ -200,20 +200,19 @@ def test_varlen_mixed_decode_and_prefill(csa, dense):
     raw0 = (last + 1 - L_raw).astype(np.int32)
     x = attn_inputs(5, T, H, cap, L_raw, io, ckv, seed=123)
     q, ck, cv, cks, cvs, kw, vw = _dev(x, io, ckv)
-    rows_pos = np.concatenate([dec_pos, c_pos0 + np.arange(T)]).astype(np.int32)
-    rows_seq = np.concatenate([np.arange(4), np.full(T, 4)]).astype(np.int32)
+    cu_rows = np.array([0, 1, 2, 3, 4, 4 + T], np.int32)
     qv = torch.cat([q[0:4, 0], q[4, :T]]).contiguous()
     lse_v = torch.empty((4 + T, H), device="cuda")
     oq, oK, oV, oKw, oVw = _oracle_inputs(x, io, ckv)
     if dense:
-        out_v = csa.hca_dense_attn_varlen(qv, ck, cv, mp, kw, vw, t_i32(raw0), t_i32(rows_seq), t_i32(rows_pos),
-                                          W, ck_scale=cks, cv_scale=cvs, lse=lse_v)
+        out_v = csa.hca_dense_attn_varlen(qv, ck, cv, mp, kw, vw, t_i32(raw0), t_i32(cu_rows), t_i32(pos0), W,
+                                          ck_scale=cks, cv_scale=cvs, lse=lse_v)
     else:
         idx_dec = random_topk_idx(np.minimum(nvis(dec_pos[:, None], m), cap), k, cap, seed=1)      # [4, 1, k]
         idx_c = random_topk_idx(np.minimum(nvis(c_pos0 + np.arange(T)[None], m), cap), k, cap, seed=2)  # [1, T, k]
         idx_v = np.ascontiguousarray(np.concatenate([idx_dec[:, 0], idx_c[0]]))
-        out_v = csa.csa_sparse_attn_varlen(qv, ck, cv, t_i32(idx_v), kw, vw, t_i32(raw0), t_i32(rows_seq),
-                                           t_i32(rows_pos), W, ck_scale=cks, cv_scale=cvs, lse=lse_v)
+        out_v = csa.csa_sparse_attn_varlen(qv, ck, cv, t_i32(idx_v), kw, vw, t_i32(raw0), t_i32(cu_rows),
+                                           t_i32(pos0), W, ck_scale=cks, cv_scale=cvs, lse=lse_v)
     parts = [(slice(0, 4), slice(0, 1), slice(0, 4)), (slice(4, 5), slice(0, T), slice(4, 4 + T))]
     for pi, (sb, st_, sr) in enumerate(parts):
         lse_p = torch.empty((sb.stop - sb.start, st_.stop, H), device="cuda")

@@ -90,20 +90,20 @@ def _run_all_forms(csa, dense, x, io, mid, idx, raw0, pos, W, B, T, H, O, lse):
                                       cv_scale=cvs, lse=lse_g, batch_invariant=form != "plain")
         torch.cuda.synchronize()
         _check(form, out, lse_g, O, lse, io)
-    # varlen: every query row of every sequence in one call
-    row_seq = np.repeat(np.arange(B, dtype=np.int32), T)
-    row_pos = (pos[:, None] + np.arange(T)[None]).reshape(-1).astype(np.int32)
+    # varlen: every query row of every sequence in one call, in both modes
+    cu = t_i32(np.arange(B + 1, dtype=np.int32) * T)
     qv = q.reshape(B * T, H, D).contiguous()
-    lse_v = torch.empty((B * T, H), device="cuda")
-    if dense:
-        out = csa.hca_dense_attn_varlen(qv, ck, cv, mid, kw, vw, r0, t_i32(row_seq), t_i32(row_pos), W,
-                                        ck_scale=cks, cv_scale=cvs, lse=lse_v)
-    else:
-        iv = t_i32(idx.reshape(B * T, -1))
-        out = csa.csa_sparse_attn_varlen(qv, ck, cv, iv, kw, vw, r0, t_i32(row_seq), t_i32(row_pos), W,
-                                         ck_scale=cks, cv_scale=cvs, lse=lse_v)
-    torch.cuda.synchronize()
-    _check("varlen", out.reshape(B, T, H, D), lse_v.reshape(B, T, H), O, lse, io)
+    for inv in (True, False):
+        lse_v = torch.empty((B * T, H), device="cuda")
+        if dense:
+            out = csa.hca_dense_attn_varlen(qv, ck, cv, mid, kw, vw, r0, cu, p0, W, ck_scale=cks, cv_scale=cvs,
+                                            invariant=inv, lse=lse_v)
+        else:
+            iv = t_i32(idx.reshape(B * T, -1))
+            out = csa.csa_sparse_attn_varlen(qv, ck, cv, iv, kw, vw, r0, cu, p0, W, ck_scale=cks, cv_scale=cvs,
+                                             invariant=inv, lse=lse_v)
+        torch.cuda.synchronize()
+        _check(f"varlen invariant={inv}", out.reshape(B, T, H, D), lse_v.reshape(B, T, H), O, lse, io)
 
 
 STAGE_DENSE = [
