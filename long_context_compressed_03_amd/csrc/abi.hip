@@ -6,6 +6,7 @@ size_t csa_kv_append_workspace_size(int B);
 size_t csa_indexer_topk_workspace_size(long rows, int T_q, int d_I, int cap);
 size_t csa_topk_workspace_size(long rows, int cap);
 size_t csa_attn_varlen_workspace_size(long n_rows, int n_seq, int H, int n_list, bool dense);
+size_t csa_indexer_topk_varlen_workspace_size(long n_rows, int cap);
 
 extern "C" size_t csa_workspace_size(int32_t op, int32_t B, int32_t T_q, int32_t H, int32_t d, int32_t n_keys) {
   if (B < 0 || T_q < 0 || n_keys < 0) return size_t(-1);
@@ -24,7 +25,7 @@ extern "C" size_t csa_workspace_size(int32_t op, int32_t B, int32_t T_q, int32_t
     case CSA_OP_KV_CACHE_APPEND:
       return csa_kv_append_workspace_size(B);
     case CSA_OP_INDEXER_TOPK_VARLEN:   // B = n_rows
-      return size_t(B) * size_t(n_keys) * 2u;
+      return csa_indexer_topk_varlen_workspace_size(B, n_keys);
     case CSA_OP_SPARSE_ATTN_VARLEN:    // B = n_rows, T_q = sequences
     case CSA_OP_DENSE_ATTN_VARLEN:
       if (d != kHeadDim || H < 16 || H > 128 || H % 16 != 0) return size_t(-1);

@@ -10,6 +10,7 @@
 #include "../../include/csa.h"
 
 #define CSA_DEV __device__ __forceinline__
+#define CSA_DEV_HOST_INLINE __host__ __device__ __forceinline__
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));

@@ -31,7 +31,37 @@ constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kMaxKSteps = 4;  // d_I <= 512
 
-enum Out { kScoresF32 = 0, kKey16 = 1 };
+enum Out { kScoresF32 = 0, kKey16 = 1, kSample = 2, kCand = 3 };
+
+// Entries of the sample pass: the first 16-entry fragment of every group of
+// kSampleGroup entries (entries 0..15, 1024..1039, ...), so its loads stay
+// whole fragments.  Sampled entry j is entry (j / 16) * kSampleGroup + j % 16.
+constexpr int kSampleGroup = 1024;
+CSA_DEV_HOST_INLINE int sampled_count(int n) {   // sampled entries below n
+  return (n / kSampleGroup) * 16 + (n % kSampleGroup < 16 ? n % kSampleGroup : 16);
+}
+// Candidate slots per row of the threshold pass, and per (block, row) in LDS.
+constexpr int kCandCap = 8192;
+constexpr int kBlockCand = 128;
+
+// Extra arguments of the selection passes of csa_indexer_topk.
+//   gate   (any mode) null, or a flag: the launch does nothing while it is 0
+//   thr    (kCand) per row: the 32-bit order-preserving key a candidate reaches
+//   cnt    (kCand) per row: candidates found (atomic; past kCandCap: overflow)
+//   cand   (kCand) per row: kCandCap (key, entry) pairs, in no particular order
+struct IxExtra {
+  const uint32_t* gate;
+  const uint32_t* thr;
+  uint32_t* cnt;
+  uint2* cand;
+};
+
+// A block's candidates of its rows, staged in LDS before one global
+// reservation per (block, row).
+struct CandLds {
+  uint32_t n[64];               // [0, 16): staged count per row; [32, 48): its reserved base
+  uint2 item[16][kBlockCand];   // at most 16 rows per block (4 tiles of 16 / H_I queries)
+};
 
 CSA_DEV v4f mfma_fp4(u32x4 a, int sa, u32x4 b, int sb, v4f c) {
   v8i av = {int(a[0]), int(a[1]), int(a[2]), int(a[3]), 0, 0, 0, 0};
@@ -146,22 +176,41 @@ CSA_DEV bool tile_of_packed(const int32_t* __restrict__ cu_rows, int B, int per,
 // kHI: indexer heads (4, 8 or 16); kRT: 16-row tiles per block; kKS: 128-wide
 // contraction steps; kFrag: 16-entry fragments per wave per batch of loads;
 // kStream: keys read once (decode) with non-temporal loads; kOut: fp32
-// scores (-inf past nvis) or the top 16 bits of the order-preserving key
-// (0 past nvis).
+// scores (-inf past nvis), the top 16 bits of the order-preserving key (0
+// past nvis), the same 16-bit keys of the sampled entries only (kSample: row
+// stride sampled_count(cap)), or the (key, entry) pairs whose score reaches
+// the row's threshold (kCand).
 //
 // Work split: a block of 4 waves owns kRT row tiles of one sequence; each
 // wave walks its own run of entries, 16 per MFMA, with the A fragments
 // (queries) held in registers for the whole run.
-template <int kHI, int kRT, int kKS, int kFrag, bool kStream, int kOut>
+template <int kHI, int kRT, int kKS, int kFrag, bool kStream, int kOut, bool kWalk>
 __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restrict__ q_codes,
                                                          const uint8_t* __restrict__ q_e8m0,
                                                          const float* __restrict__ w,
                                                          const uint8_t* __restrict__ k_codes,
                                                          const uint8_t* __restrict__ k_e8m0,
-                                                         const int32_t* __restrict__ q_pos0, int T_q, int d_I,
+                                                         const int32_t* __restrict__ q_pos0, int T_q_all, int d_I,
                                                          int cap, int m, int entries_per_wave, void* __restrict__ out,
-                                                         const int32_t* __restrict__ cu_rows, int n_seq) {
+                                                         const int32_t* __restrict__ cu_rows, int n_seq, IxExtra x) {
   constexpr int kQPT = 16 / kHI;  // queries per row tile
+  // Head-major tiles (every batched launch): the kHI / 4 tiles of a query
+  // group hold heads 0-3, 4-7, ... of the same 4 queries, so each lane ends
+  // with whole scores (no cross-lane head sum) and the group's partial sums
+  // are added in the order head_sum uses (lower heads + upper heads, pairwise).
+  // Streaming (decode) launches have a single tile: 16 / kHI queries per tile,
+  // head fastest, summed with head_sum.
+  // (16 heads keep the tile-per-query form: built head-major, the second
+  // batch of each wave came out wrong on gfx950 -- cause not found, the
+  // index mapping checks out on the host -- while 4 and 8 heads are exact.)
+  constexpr int kGrp = kHI / 4;
+  constexpr bool kHM = !kStream && kRT % kGrp == 0 && kHI <= 8;
+  auto q_of = [](int rt, int r) { return kHM ? (rt / kGrp) * 4 + r / 4 : (rt * 16 + r) / kHI; };
+  auto h_of = [](int rt, int r) { return kHM ? (rt % kGrp) * 4 + r % 4 : (rt * 16 + r) % kHI; };
+  // entry space the waves walk: every entry, or the sampled ones
+  auto real_entry = [](int e) { return kOut == kSample ? (e >> 4) * kSampleGroup + (e & 15) : e; };
+  auto space = [](int n) { return kOut == kSample ? sampled_count(n) : n; };
+  if (x.gate && *x.gate == 0u) return;   // the whole block
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int col = lane & 15;
@@ -169,15 +218,20 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
   // this block's sequence b, its queries q_block .. (T_q of them), and the
   // packed row of its query 0 (row_base); packed batches (cu_rows) find the
   // sequence from the tile index
-  int b, q_block;
+  // row tile blockIdx.y; kWalk (the gated fallback launch, whose few blocks
+  // walk them all): blockIdx.y, + gridDim.y, ...
+  for (int tile = blockIdx.y;; tile += gridDim.y) {
+  int b, q_block, T_q;
   size_t row_base;
   if (cu_rows) {
-    if (!tile_of_packed(cu_rows, n_seq, kRT * kQPT, blockIdx.y, &b, &q_block)) return;
+    if (!tile_of_packed(cu_rows, n_seq, kRT * kQPT, tile, &b, &q_block)) break;
     row_base = size_t(cu_rows[b]);
     T_q = cu_rows[b + 1] - cu_rows[b];
   } else {
     b = blockIdx.z;
-    q_block = blockIdx.y * kRT * kQPT;
+    q_block = tile * kRT * kQPT;
+    if (q_block >= T_q_all) break;
+    T_q = T_q_all;
     row_base = size_t(b) * T_q;
   }
   const int nblk = d_I >> 5;            // 32-element blocks per vector
@@ -191,27 +245,26 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
   int nv_lane[kRT];  // visible entries of the query whose rows this lane holds in C
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
-    const int r = rt * 16 + col;
-    const int q = q_block + r / kHI;
-    const int h = r % kHI;
+    const int q = q_block + q_of(rt, col);
+    const int h = h_of(rt, col);
     load_a<kHI, kKS>(q_codes, q_e8m0, (row_base + q) * kHI + h, q < T_q, g, nblk, row_bytes, a[rt], sa[rt]);
-    const int rc = rt * 16 + 4 * g;  // first C row this lane holds
-    const int qc = q_block + rc / kHI;
+    const int qc = q_block + q_of(rt, 4 * g);   // the query of the C rows this lane holds
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int hh = (rc + i) % kHI;
+      const int hh = h_of(rt, 4 * g + i);
       wv[rt][i] = qc < T_q ? w[(row_base + qc) * kHI + hh] : 0.f;
     }
     int nv = 0;
     if (qc < T_q) nv = min((pos0 + qc + 1) / m, cap);
-    nv_lane[rt] = nv;
+    nv_lane[rt] = space(nv);
   }
   // largest visibility among the block's queries (the last valid one)
   const int q_last = min(q_block + kRT * kQPT, T_q) - 1;
-  const int nv_max = min((pos0 + q_last + 1) / m, cap);
+  const int nv_max = space(min((pos0 + q_last + 1) / m, cap));
+  const int ecap = space(cap);   // entries (sampled ones: row stride)
 
   const int e_wave0 = (blockIdx.x * kWavesPerBlock + wid) * entries_per_wave;
-  const int e_wave1 = min(e_wave0 + entries_per_wave, cap);
+  const int e_wave1 = min(e_wave0 + entries_per_wave, ecap);
 
   const uint8_t* kc_seq = k_codes + size_t(b) * cap * row_bytes;
   const uint8_t* ke_seq = k_e8m0 + size_t(b) * cap * nblk;
@@ -223,17 +276,36 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
   // output row of each row tile's query (the query whose rows the lane holds)
   bool q_in[kRT];
   size_t orow[kRT];
+  float thr[kRT];   // kCand: the threshold score of the lane's query
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
-    const int q = q_block + (rt * 16 + 4 * g) / kHI;
+    const int q = q_block + q_of(rt, 4 * g);
     q_in[rt] = q < T_q;
-    orow[rt] = (row_base + (q < T_q ? q : 0)) * cap;
+    orow[rt] = (row_base + (q < T_q ? q : 0)) * size_t(ecap);
+    thr[rt] = 0.f;
+    if constexpr (kOut == kCand) thr[rt] = __uint_as_float(x.thr[row_base + (q < T_q ? q : 0)]);
+  }
+  extern __shared__ __attribute__((aligned(16))) unsigned char ix_smem[];
+  CandLds& cl = *reinterpret_cast<CandLds*>(ix_smem);
+  constexpr int kRowsPerBlock = kRT * kQPT;
+  static_assert(kOut != kCand || kRowsPerBlock <= 16, "candidate staging holds 16 rows");
+  if constexpr (kOut == kCand) {
+    for (int i = threadIdx.x; i < kRowsPerBlock; i += kBlock) cl.n[i] = 0u;
+    __syncthreads();
   }
   auto put = [&](int rt, int e, float p) {
     if (q_in[rt] && e < e_wave1) {
       const bool vis = e < nv_lane[rt];
       if constexpr (kOut == kScoresF32) {
         static_cast<float*>(out)[orow[rt] + e] = vis ? p : -INFINITY;
+      } else if constexpr (kOut == kCand) {
+        // a float compare (the threshold is a score whose key is the
+        // row's 32-bit threshold key: same order, -0 == +0 included)
+        if (vis && p >= thr[rt]) {
+          const int lr = q_of(rt, 4 * g);   // the query's slot among the block's rows
+          const uint32_t slot = atomicAdd(&cl.n[lr], 1u);
+          if (slot < uint32_t(kBlockCand)) cl.item[lr][slot] = make_uint2(csa_sel::ordered_key(p), uint32_t(e));
+        }
       } else {
         static_cast<uint16_t*>(out)[orow[rt] + e] = vis ? uint16_t(csa_sel::ordered_key(p) >> 16) : uint16_t(0);
       }
@@ -246,7 +318,7 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
 #pragma unroll
   for (int f = 0; f < kFrag; ++f) {
     const int e = e_wave0 + f * 16 + col;
-    load_b<kKS, kStream>(rc, re, c_bytes, e_bytes, e, e < nv_max, g, nblk, row_bytes, bk[f], sb[f]);
+    load_b<kKS, kStream>(rc, re, c_bytes, e_bytes, real_entry(e), e < nv_max, g, nblk, row_bytes, bk[f], sb[f]);
   }
   // One batch: the keys of the batch after it load into (nk, ns) while this
   // one computes from (ck, cs); two buffers swap roles from batch to batch (no
@@ -257,7 +329,8 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
 #pragma unroll
       for (int f = 0; f < kFrag; ++f) {
         const int e = e_frag0 + 16 * kFrag + f * 16 + col;
-        load_b<kKS, kStream>(rc, re, c_bytes, e_bytes, e, more && e < nv_max, g, nblk, row_bytes, nk[f], ns[f]);
+        load_b<kKS, kStream>(rc, re, c_bytes, e_bytes, real_entry(e), more && e < nv_max, g, nblk, row_bytes, nk[f],
+                             ns[f]);
       }
     }
     // every MFMA of the batch first, into its own accumulator; entries past
@@ -272,7 +345,39 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
 #pragma unroll
         for (int ks = 1; ks < kKS; ++ks) acc[f][rt] = mfma_fp4(a[rt][ks], sa[rt][ks], ck[f][ks], cs[f][ks], acc[f][rt]);
       }
-    if constexpr (kHI == 8 && kFrag % 2 == 0) {
+    if constexpr (kHM) {
+      // each lane: the whole score of query (rt / kGrp) * 4 + g at entry
+      // e_frag0 + 16 f + col, one per (fragment, query group)
+#pragma unroll
+      for (int f = 0; f < kFrag; ++f)
+#pragma unroll
+        for (int gi = 0; gi < kRT / kGrp; ++gi) {
+          float part[kGrp];
+#pragma unroll
+          for (int hq = 0; hq < kGrp; ++hq) {
+            const v4f& c = acc[f][gi * kGrp + hq];
+            const float(&wq)[4] = wv[gi * kGrp + hq];
+            float p = wq[0] * relu(c[0]);
+            p = fmaf(wq[1], relu(c[1]), p);
+            p = fmaf(wq[2], relu(c[2]), p);
+            p = fmaf(wq[3], relu(c[3]), p);
+            part[hq] = p;
+          }
+          float p;
+          if constexpr (kGrp == 1) p = part[0];
+          else if constexpr (kGrp == 2) p = part[0] + part[1];
+          else p = (part[0] + part[1]) + (part[2 % kGrp] + part[3 % kGrp]);
+          const int rt = gi * kGrp;
+          const int e = e_frag0 + f * 16 + col;
+          if constexpr (kOut == kCand) {
+            // the wave takes the append path only when one of its lanes has a
+            // candidate here (rare); put re-checks everything
+            if (__ballot(p >= thr[rt])) put(rt, e, p);
+          } else {
+            put(rt, e, p);
+          }
+        }
+    } else if constexpr (kHI == 8 && kFrag % 2 == 0) {
       // both lane halves of a query hold its sum after head_sum: the even one
       // stores fragment f, the odd one fragment f + 1
       const bool odd = (g & 1) != 0;
@@ -307,51 +412,96 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
       batch(bn, sn, bk, sb, e_frag0 + 16 * kFrag, true);
     }
   }
+  if constexpr (kOut == kCand) {
+    // one reservation per (block, row), then the staged pairs copied out; a
+    // (block, row) whose staging overflowed pushes the row's count past the
+    // capacity, so the selection sees the overflow
+    __syncthreads();
+    if (int(threadIdx.x) < kRowsPerBlock) {
+      const int q = q_block + int(threadIdx.x);
+      const uint32_t n = cl.n[threadIdx.x];
+      uint32_t base = 0u;
+      if (q < T_q && n > 0u)
+        base = atomicAdd(&x.cnt[row_base + q], n > uint32_t(kBlockCand) ? uint32_t(kCandCap) + 1u : n);
+      cl.n[32 + threadIdx.x] = base;
+    }
+    __syncthreads();
+    for (int lr = 0; lr < kRowsPerBlock; ++lr) {
+      const int q = q_block + lr;
+      const uint32_t n = min(cl.n[lr], uint32_t(kBlockCand));
+      const uint32_t base = cl.n[32 + lr];
+      if (q >= T_q) break;
+      for (uint32_t i = threadIdx.x; i < n; i += kBlock)
+        if (base + i < uint32_t(kCandCap)) x.cand[(row_base + q) * size_t(kCandCap) + base + i] = cl.item[lr][i];
+    }
+    __syncthreads();   // the staging is reused by the next tile
+  }
+  if constexpr (!kWalk) break;
+  }   // tiles
 }
 
 template <int kHI, int kRT, int kKS, bool kStream, int kOut>
 hipError_t launch_indexer_ks(const uint8_t* qc, const uint8_t* qe, const float* w, const uint8_t* kc,
                              const uint8_t* ke, const int32_t* pos, int B, int T_q, int d_I, int cap, int m,
-                             void* out, hipStream_t st, const int32_t* cu_rows, int n_rows) {
+                             void* out, hipStream_t st, const int32_t* cu_rows, int n_rows, const IxExtra& x) {
   constexpr int kFrag = 4;
   constexpr int kQPT = 16 / kHI;
   const int entries_per_wave = kStream ? 16 * kFrag : 256;   // streaming: one batch per wave
   const int per_block = entries_per_wave * kWavesPerBlock;
+  const int ecap = kOut == kSample ? sampled_count(cap) : cap;
+  const size_t lds = kOut == kCand ? sizeof(CandLds) : 0;
+  if (lds) {
+    if (hipError_t e = csa_lds_opt_in(
+            reinterpret_cast<const void*>(&indexer_kernel<kHI, kRT, kKS, kFrag, kStream, kOut, false>), lds);
+        e != hipSuccess)
+      return e;
+  }
   // Blocks are dealt to the 8 XCDs round-robin in linear order (x fastest);
   // with the entry dimension padded to a multiple of 8, entry block x always
   // runs on XCD x % 8, so each XCD's L2 holds a fixed eighth of the keys
   // while the query tiles stream past it.  Padding blocks exit at once.
-  const int n_eb = ((cap + per_block - 1) / per_block + 7) / 8 * 8;
+  const int n_eb = ((ecap + per_block - 1) / per_block + 7) / 8 * 8;
   // packed batches (cu_rows): a bound on the tiles, sequences found in the kernel
-  const dim3 grid = cu_rows ? dim3(n_eb, (n_rows + kRT * kQPT - 1) / (kRT * kQPT) + B, 1)
-                            : dim3(n_eb, (T_q + kRT * kQPT - 1) / (kRT * kQPT), B);
-  hipLaunchKernelGGL((indexer_kernel<kHI, kRT, kKS, kFrag, kStream, kOut>), grid, dim3(kBlock), 0, st, qc, qe, w,
-                     kc, ke, pos, T_q, d_I, cap, m, entries_per_wave, out, cu_rows, B);
+  // the gated fallback launch: 2 tile blocks per (entry block, sequence),
+  // walking the tiles (cheap to dispatch when the gate keeps it idle)
+  const int tiles = cu_rows ? (n_rows + kRT * kQPT - 1) / (kRT * kQPT) + B : (T_q + kRT * kQPT - 1) / (kRT * kQPT);
+  const int ty = x.gate ? min(tiles, 2) : tiles;
+  const dim3 grid = cu_rows ? dim3(n_eb, ty, 1) : dim3(n_eb, ty, B);
+  if (x.gate) {
+    if constexpr (kOut == kKey16)
+      hipLaunchKernelGGL((indexer_kernel<kHI, kRT, kKS, kFrag, kStream, kOut, true>), grid, dim3(kBlock), lds, st, qc,
+                         qe, w, kc, ke, pos, T_q, d_I, cap, m, entries_per_wave, out, cu_rows, B, x);
+    else
+      return hipErrorInvalidValue;   // only the 16-bit-key pass serves as a gated fallback
+  } else {
+    hipLaunchKernelGGL((indexer_kernel<kHI, kRT, kKS, kFrag, kStream, kOut, false>), grid, dim3(kBlock), lds, st, qc,
+                       qe, w, kc, ke, pos, T_q, d_I, cap, m, entries_per_wave, out, cu_rows, B, x);
+  }
   return hipGetLastError();
 }
 
 template <int kHI, int kRT, bool kStream, int kOut>
 hipError_t launch_indexer_rt(int ks, const uint8_t* qc, const uint8_t* qe, const float* w, const uint8_t* kc,
                              const uint8_t* ke, const int32_t* pos, int B, int T_q, int d_I, int cap, int m,
-                             void* out, hipStream_t st, const int32_t* cu_rows, int n_rows) {
+                             void* out, hipStream_t st, const int32_t* cu_rows, int n_rows, const IxExtra& x) {
   switch (ks) {
-    case 1: return launch_indexer_ks<kHI, kRT, 1, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
-    case 2: return launch_indexer_ks<kHI, kRT, 2, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
-    case 3: return launch_indexer_ks<kHI, kRT, 3, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
-    default: return launch_indexer_ks<kHI, kRT, 4, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
+    case 1: return launch_indexer_ks<kHI, kRT, 1, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows, x);
+    case 2: return launch_indexer_ks<kHI, kRT, 2, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows, x);
+    case 3: return launch_indexer_ks<kHI, kRT, 3, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows, x);
+    default: return launch_indexer_ks<kHI, kRT, 4, kStream, kOut>(qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows, x);
   }
 }
 
 template <int kHI, int kOut>
 hipError_t launch_indexer_h(int ks, const uint8_t* qc, const uint8_t* qe, const float* w, const uint8_t* kc,
                             const uint8_t* ke, const int32_t* pos, int B, int T_q, int d_I, int cap, int m,
-                            void* out, hipStream_t st, const int32_t* cu_rows, int n_rows) {
+                            void* out, hipStream_t st, const int32_t* cu_rows, int n_rows, const IxExtra& x) {
   // one row tile when the whole call has at most one tile of queries (decode);
   // several otherwise so every key fragment feeds several MFMAs (packed batches
   // always take the several-tile form)
   if (!cu_rows && T_q * kHI <= 16)
-    return launch_indexer_rt<kHI, 1, true, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
-  return launch_indexer_rt<kHI, 4, false, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
+    return launch_indexer_rt<kHI, 1, true, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows, x);
+  return launch_indexer_rt<kHI, 4, false, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows, x);
 }
 
 // Shared argument checks of the two indexer entry points.
@@ -372,12 +522,13 @@ inline csa_status_t check_indexer_args(const void* q_codes, const void* q_e8m0, 
 template <int kOut>
 hipError_t launch_indexer(int H_I, const uint8_t* qc, const uint8_t* qe, const float* w, const uint8_t* kc,
                           const uint8_t* ke, const int32_t* pos, int B, int T_q, int d_I, int cap, int m, void* out,
-                          hipStream_t st, const int32_t* cu_rows = nullptr, int n_rows = 0) {
+                          hipStream_t st, const int32_t* cu_rows = nullptr, int n_rows = 0,
+                          const IxExtra& x = IxExtra{}) {
   const int ks = (d_I + 127) / 128;
   switch (H_I) {
-    case 4: return launch_indexer_h<4, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
-    case 8: return launch_indexer_h<8, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
-    default: return launch_indexer_h<16, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows);
+    case 4: return launch_indexer_h<4, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows, x);
+    case 8: return launch_indexer_h<8, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows, x);
+    default: return launch_indexer_h<16, kOut>(ks, qc, qe, w, kc, ke, pos, B, T_q, d_I, cap, m, out, st, cu_rows, n_rows, x);
   }
 }
 

@@ -330,13 +330,15 @@ __global__ __launch_bounds__(kThreads) void select_kernel(const uint16_t* __rest
                                                           const uint8_t* __restrict__ k_e8m0,
                                                           const int32_t* __restrict__ q_pos0, int T_q, int d_I,
                                                           int cap, int m, int k, int32_t* __restrict__ idx,
-                                                          const int32_t* __restrict__ cu_rows, int n_seq) {
+                                                          const int32_t* __restrict__ cu_rows, int n_seq,
+                                                          const uint32_t* __restrict__ gate) {
   constexpr int kS = kJ * kRound;          // keys per chunk; chunk 0 stays in registers
   constexpr int kWPT = (kS / 32 + kThreads - 1) / kThreads;  // bitmap words per thread (the last ones may be past the chunk)
   static_assert(kS < (1 << 17), "a chunk's equal counts fit 17 bits");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   Shared& sh = *reinterpret_cast<Shared*>(smem_raw);
 
+  if (gate && *gate == 0u) return;   // the whole block: the fallback launch has nothing to do
   // row = packed row (sequence b, query i of it); cu_rows: packed batches
   const int row = blockIdx.x;
   const int b = cu_rows ? csa_packed_seq(cu_rows, n_seq, row) : row / T_q;
@@ -755,49 +757,391 @@ size_t split_scores_bytes(long rows, int cap) { return (size_t(rows) * size_t(ca
 template <int kHI, int kKS, int kJ>
 hipError_t launch_select_j(long rows, hipStream_t st, const uint16_t* key16, const uint8_t* qc, const uint8_t* qe,
                            const float* w, const uint8_t* kc, const uint8_t* ke, const int32_t* pos, int T_q,
-                           int d_I, int cap, int m, int k, int32_t* idx, const int32_t* cu_rows, int n_seq) {
+                           int d_I, int cap, int m, int k, int32_t* idx, const int32_t* cu_rows, int n_seq,
+                           const uint32_t* gate) {
   if (hipError_t e = csa_lds_opt_in(reinterpret_cast<const void*>(&select_kernel<kHI, kKS, kJ>), sizeof(Shared));
       e != hipSuccess)
     return e;
   hipLaunchKernelGGL((select_kernel<kHI, kKS, kJ>), dim3(unsigned(rows)), dim3(kThreads), sizeof(Shared), st, key16, qc, qe, w, kc, ke, pos, T_q,
-                     d_I, cap, m, k, idx, cu_rows, n_seq);
+                     d_I, cap, m, k, idx, cu_rows, n_seq, gate);
   return hipGetLastError();
 }
 
 template <int kHI, int kKS>
 hipError_t launch_select_ks(long rows, hipStream_t st, const uint16_t* key16, const uint8_t* qc, const uint8_t* qe,
                             const float* w, const uint8_t* kc, const uint8_t* ke, const int32_t* pos, int T_q,
-                            int d_I, int cap, int m, int k, int32_t* idx, const int32_t* cu_rows, int n_seq) {
+                            int d_I, int cap, int m, int k, int32_t* idx, const int32_t* cu_rows, int n_seq,
+                            const uint32_t* gate) {
   // rows of up to 32768 keys are held whole in 8 rounds of registers; longer
   // rows keep their first 81920 keys in 20 rounds (65536 in 16 when d_I > 128
   // leaves fewer registers free) and read the rest
   if (cap <= 8 * kRound)
-    return launch_select_j<kHI, kKS, 8>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq);
+    return launch_select_j<kHI, kKS, 8>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq, gate);
   if constexpr (kKS == 1)
-    return launch_select_j<kHI, kKS, 20>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq);
-  return launch_select_j<kHI, kKS, 16>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq);
+    return launch_select_j<kHI, kKS, 20>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq, gate);
+  return launch_select_j<kHI, kKS, 16>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq, gate);
 }
 
 template <int kHI>
 hipError_t launch_select_h(int ks, long rows, hipStream_t st, const uint16_t* key16, const uint8_t* qc,
                            const uint8_t* qe, const float* w, const uint8_t* kc, const uint8_t* ke,
                            const int32_t* pos, int T_q, int d_I, int cap, int m, int k, int32_t* idx,
-                           const int32_t* cu_rows, int n_seq) {
+                           const int32_t* cu_rows, int n_seq, const uint32_t* gate = nullptr) {
   switch (ks) {
-    case 1: return launch_select_ks<kHI, 1>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq);
-    case 2: return launch_select_ks<kHI, 2>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq);
-    case 3: return launch_select_ks<kHI, 3>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq);
-    default: return launch_select_ks<kHI, 4>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq);
+    case 1: return launch_select_ks<kHI, 1>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq, gate);
+    case 2: return launch_select_ks<kHI, 2>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq, gate);
+    case 3: return launch_select_ks<kHI, 3>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq, gate);
+    default: return launch_select_ks<kHI, 4>(rows, st, key16, qc, qe, w, kc, ke, pos, T_q, d_I, cap, m, k, idx, cu_rows, n_seq, gate);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Threshold selection (rows of the row-tile path, k <= kCandMaxK).
+//
+// A sample pass scores the first 16 entries of every 1024
+// (indexer_kernel<kSample>) and cand_threshold_kernel takes, per row, the
+// 16-bit key of the r-th largest sampled score, r = k_s + 4 sqrt(k_s) + 16
+// with k_s the sample's share of k: more than k entries of the row reach it
+// unless the sample is far off.  The threshold pass (indexer_kernel<kCand>)
+// keeps the (key, entry) pairs at or above it, and cand_select_kernel finds
+// the k-th pair exactly (key descending, entry ascending) and writes the
+// first k in entry order.  A row with fewer than k pairs, or more than
+// kCandCap, sets the miss flag; the 16-bit-key pass and select_kernel then
+// run in full (they are launched behind a gate on that flag and do nothing
+// otherwise).  Every score is the indexer's own (same instruction sequence),
+// so the result is exactly csa_topk's on csa_indexer_scores, whichever way a
+// row goes.
+
+constexpr int kCandMaxK = csa_ix::kCandCap * 2 / 5;   // k beyond this: the 16-bit-key path only
+constexpr int kCandMaxCap = 1 << 19;                  // entries the output bitmap covers
+constexpr int kCandMinCap = 8 * kRound;               // shorter rows: select_kernel holds them whole
+constexpr int kTThreads = 256;                        // threshold and candidate selection kernels
+
+// Row `row` of a call: its sequence and query index (packed rows or B x T_q).
+CSA_DEV void row_of(int row, int T_q, const int32_t* __restrict__ cu_rows, int n_seq, int* b, int* i) {
+  *b = cu_rows ? csa_packed_seq(cu_rows, n_seq, row) : row / T_q;
+  *i = cu_rows ? row - cu_rows[*b] : row - *b * T_q;
+}
+
+// Radix selection over the block (kTThreads threads, values in registers):
+// the r-th largest (kDesc) or r-th smallest value among the elements for
+// which part(x) holds, one byte per pass from the top.  Each wave counts into
+// its own histogram (same-bin updates then collide only within a wave), the
+// waves' counts are added per bin, and wave 0 finds the byte.  Returns the
+// value; *n_at gets how many participating elements equal it and *rank_in
+// the rank it has among them (1-based, from the selection's side).
+struct RadixLds {
+  uint32_t hist[kTThreads / 64][256];
+  uint32_t tot[256];
+  uint32_t res[4];
+};
+
+template <bool kDesc>
+CSA_DEV void pick_bin(const uint32_t* tot, uint32_t r, uint32_t* res) {
+  const int lane = threadIdx.x & 63;
+  uint32_t c[4], sum = 0u;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int bin = kDesc ? 255 - (4 * lane + x) : 4 * lane + x;
+    c[x] = tot[bin];
+    sum += c[x];
+  }
+  uint32_t incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  const uint32_t excl = incl - sum;
+  const bool here = excl < r && incl >= r;
+  if (here) {
+    uint32_t run = excl;
+    int x = 0;
+    for (; x < 3; ++x) {
+      if (run + c[x] >= r) break;
+      run += c[x];
+    }
+    res[0] = uint32_t(kDesc ? 255 - (4 * lane + x) : 4 * lane + x);   // the bin
+    res[1] = run;                                                     // before it
+    res[2] = c[x];                                                    // in it
+  }
+}
+
+template <bool kDesc, int kPer, typename Part>
+CSA_DEV uint32_t radix_select(const uint32_t (&v)[kPer], Part part, uint32_t r, RadixLds& sh, uint32_t* n_at,
+                              uint32_t* rank_in) {
+  const int wv = threadIdx.x >> 6;
+  uint32_t prefix = 0u, mask = 0u;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int x = threadIdx.x; x < (kTThreads / 64) * 256; x += kTThreads) (&sh.hist[0][0])[x] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < kPer; ++x)
+      if (part(x) && (v[x] & mask) == prefix) atomicAdd(&sh.hist[wv][(v[x] >> shift) & 255u], 1u);
+    __syncthreads();
+    {
+      uint32_t t = 0u;
+#pragma unroll
+      for (int w = 0; w < kTThreads / 64; ++w) t += sh.hist[w][threadIdx.x];
+      sh.tot[threadIdx.x] = t;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) pick_bin<kDesc>(sh.tot, r, sh.res);
+    __syncthreads();
+    prefix |= sh.res[0] << shift;
+    mask |= 255u << shift;
+    r -= sh.res[1];
+    *n_at = sh.res[2];
+    __syncthreads();
+  }
+  *rank_in = r;
+  return prefix;
+}
+
+// The score whose order-preserving key is `key` (keys below -inf's: -inf).
+CSA_DEV float key_score(uint32_t key) {
+  if (key <= csa_sel::ordered_key(-INFINITY)) return -INFINITY;
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+constexpr int kSampleMax = kCandMaxCap / csa_ix::kSampleGroup * 16 + 16;   // sampled entries per row, at most
+constexpr int kSPer = (kSampleMax + kTThreads - 1) / kTThreads;
+
+__global__ __launch_bounds__(kTThreads) void cand_threshold_kernel(const uint16_t* __restrict__ sample, int n_s,
+                                                                   const int32_t* __restrict__ q_pos0, int T_q,
+                                                                   const int32_t* __restrict__ cu_rows, int n_seq,
+                                                                   int cap, int m, int k, uint32_t* __restrict__ thr,
+                                                                   uint32_t* __restrict__ cnt,
+                                                                   uint32_t* __restrict__ miss) {
+  __shared__ RadixLds sh;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  int b, i;
+  row_of(row, T_q, cu_rows, n_seq, &b, &i);
+  const int t = q_pos0[b] + i;
+  const int nv = max(0, min((t + 1) / m, cap));
+  if (tid == 0) {
+    cnt[row] = 0u;
+    if (row == 0) *miss = 0u;
+  }
+  const int nsv = csa_ix::sampled_count(nv);
+  const int k_s = nv > 0 ? int((long(k) * nsv + nv - 1) / nv) : 0;
+  const int r = k_s + 4 * int(sqrtf(float(k_s))) + 16;
+  if (nv <= k || r > nsv) {   // every entry is a candidate (or the row needs no selection)
+    if (tid == 0) thr[row] = __float_as_uint(-INFINITY);
+    return;
+  }
+  const uint16_t* src = sample + size_t(row) * n_s;
+  uint32_t v[kSPer];
+#pragma unroll
+  for (int x = 0; x < kSPer; ++x) {
+    const int j = tid + x * kTThreads;
+    v[x] = j < nsv ? uint32_t(src[j]) : 0u;
+  }
+  uint32_t n_at, rank_in;
+  const uint32_t key16 = radix_select<true>(v, [&](int x) { return tid + x * kTThreads < nsv; }, uint32_t(r), sh,
+                                            &n_at, &rank_in);
+  if (tid == 0) thr[row] = __float_as_uint(key_score(key16 << 16));
+}
+
+// LDS of cand_select_kernel: the radix histograms, then per group of 8
+// bitmap words the selected entries before it, then the bitmap of the
+// selected entries (both sized for the call's capacity).
+struct CandSelLds {
+  RadixLds rx;
+  uint32_t red[kTThreads / 64];
+};
+size_t cand_select_lds(int cap) {
+  const size_t words = (size_t(cap) + 31) / 32, groups = (words + 7) / 8;
+  return sizeof(CandSelLds) + groups * 4 + words * 4;
+}
+
+__global__ __launch_bounds__(kTThreads) void cand_select_kernel(const uint2* __restrict__ cand,
+                                                                const uint32_t* __restrict__ cnt,
+                                                                const int32_t* __restrict__ q_pos0, int T_q,
+                                                                const int32_t* __restrict__ cu_rows, int n_seq,
+                                                                int cap, int m, int k, int32_t* __restrict__ idx,
+                                                                uint32_t* __restrict__ miss) {
+  constexpr int kPer = csa_ix::kCandCap / kTThreads;
+  extern __shared__ __attribute__((aligned(16))) unsigned char cs_smem[];
+  CandSelLds& sh = *reinterpret_cast<CandSelLds*>(cs_smem);
+  const int cap_words = (cap + 31) / 32;
+  uint32_t* pre = reinterpret_cast<uint32_t*>(cs_smem + sizeof(CandSelLds));
+  uint32_t* bits = pre + (cap_words + 7) / 8;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  int b, i;
+  row_of(row, T_q, cu_rows, n_seq, &b, &i);
+  const int t = q_pos0[b] + i;
+  const int nv = max(0, min((t + 1) / m, cap));
+  int32_t* out = idx + size_t(row) * k;
+  if (nv <= k) {
+    for (int j = tid; j < k; j += kTThreads) out[j] = j < nv ? j : -1;
+    return;
+  }
+  const uint32_t n = cnt[row];
+  if (n < uint32_t(k) || n > uint32_t(csa_ix::kCandCap)) {
+    if (tid == 0) atomicOr(miss, 1u);
+    return;
+  }
+  const uint2* src = cand + size_t(row) * csa_ix::kCandCap;
+  uint32_t key[kPer], ent[kPer];
+#pragma unroll
+  for (int x = 0; x < kPer; ++x) {
+    const int j = tid + x * kTThreads;
+    const uint2 c = j < int(n) ? src[j] : make_uint2(0u, 0xFFFFFFFFu);
+    key[x] = c.x;
+    ent[x] = c.y;
+  }
+  auto valid = [&](int x) { return tid + x * kTThreads < int(n); };
+  // K: the k-th largest key; need: how many of key K the selection takes
+  uint32_t n_eq, need;
+  const uint32_t K = radix_select<true>(key, valid, uint32_t(k), sh.rx, &n_eq, &need);
+  // among the entries of key K, the need-th lowest index I (all of them: no limit)
+  uint32_t I = 0xFFFFFFFFu;
+  if (need < n_eq) {
+    uint32_t n_i, r_i;
+    I = radix_select<false>(ent, [&](int x) { return valid(x) && key[x] == K; }, need, sh.rx, &n_i, &r_i);
+  }
+  // the selected entries as a bitmap, then each one's rank among them
+  auto chosen = [&](int x) { return valid(x) && (key[x] > K || (key[x] == K && ent[x] <= I)); };
+  const int n_words = (nv + 31) / 32;
+  for (int w = tid; w < n_words; w += kTThreads) bits[w] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < kPer; ++x)
+    if (chosen(x)) atomicOr(&bits[ent[x] >> 5], 1u << (ent[x] & 31u));
+  __syncthreads();
+  // groups of 8 words: thread tid sums groups tid, tid + 256, ... (contiguous
+  // per thread: groups [tid * per, (tid + 1) * per))
+  const int n_groups = (n_words + 7) / 8;
+  const int per = (n_groups + kTThreads - 1) / kTThreads;
+  uint32_t mine = 0u;
+  for (int gi = tid * per; gi < min((tid + 1) * per, n_groups); ++gi)
+    for (int w = gi * 8; w < min(gi * 8 + 8, n_words); ++w) mine += __popc(bits[w]);
+  uint32_t incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(incl, o);
+    if ((tid & 63) >= o) incl += y;
+  }
+  if ((tid & 63) == 63) sh.red[tid >> 6] = incl;
+  __syncthreads();
+  uint32_t run = incl - mine;
+  for (int w = 0; w < (tid >> 6); ++w) run += sh.red[w];
+  for (int gi = tid * per; gi < min((tid + 1) * per, n_groups); ++gi) {
+    pre[gi] = run;
+    for (int w = gi * 8; w < min(gi * 8 + 8, n_words); ++w) run += __popc(bits[w]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < kPer; ++x) {
+    if (chosen(x)) {
+      const uint32_t e = ent[x];
+      const int w = int(e >> 5);
+      const int g0 = (w >> 3) << 3;
+      uint32_t slot = pre[w >> 3];
+      for (int y = g0; y < w; ++y) slot += __popc(bits[y]);
+      slot += __popc(bits[w] & ((1u << (e & 31u)) - 1u));
+      out[slot] = int32_t(e);
+    }
+  }
+}
+
+// Workspace of the row-tile path: the 16-bit keys (fallback), the sampled
+// keys, the candidates, and per row the threshold and count; the miss flag.
+struct TileWs {
+  uint16_t* key16;
+  uint16_t* sample;
+  uint2* cand;
+  uint32_t* thr;
+  uint32_t* cnt;
+  uint32_t* miss;
+};
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+size_t tile_ws_bytes(long rows, int cap) {
+  const size_t n_s = size_t(csa_ix::sampled_count(cap));
+  return align256(size_t(rows) * cap * 2) + align256(size_t(rows) * n_s * 2) +
+         align256(size_t(rows) * csa_ix::kCandCap * 8) + 2 * align256(size_t(rows) * 4) + 256;
+}
+TileWs tile_ws(void* ws, long rows, int cap) {
+  const size_t n_s = size_t(csa_ix::sampled_count(cap));
+  char* p = static_cast<char*>(ws);
+  TileWs w;
+  w.key16 = reinterpret_cast<uint16_t*>(p);
+  p += align256(size_t(rows) * cap * 2);
+  w.sample = reinterpret_cast<uint16_t*>(p);
+  p += align256(size_t(rows) * n_s * 2);
+  w.cand = reinterpret_cast<uint2*>(p);
+  p += align256(size_t(rows) * csa_ix::kCandCap * 8);
+  w.thr = reinterpret_cast<uint32_t*>(p);
+  p += align256(size_t(rows) * 4);
+  w.cnt = reinterpret_cast<uint32_t*>(p);
+  p += align256(size_t(rows) * 4);
+  w.miss = reinterpret_cast<uint32_t*>(p);
+  return w;
+}
+
+// Scoring and selection of `rows` rows (B sequences of T_q rows, or packed
+// rows when cu_rows is set) by row tiles: the threshold path when k allows
+// it, else (and as its fallback) the 16-bit keys and select_kernel.
+hipError_t tile_path(int H_I, long rows, const uint8_t* q_codes, const uint8_t* q_e8m0, const float* w,
+                     const uint8_t* k_codes, const uint8_t* k_e8m0, const int32_t* q_pos0, int B, int T_q,
+                     const int32_t* cu_rows, int d_I, int cap, int m, int k, int32_t* idx, void* ws, hipStream_t st) {
+  const int ks = (d_I + 127) / 128;
+  const TileWs tw = tile_ws(ws, rows, cap);
+  const int n_rows = cu_rows ? int(rows) : 0;
+  const int n_seq = cu_rows ? B : 0;
+  const int T_rows = cu_rows ? 1 : T_q;
+  const uint32_t* gate = nullptr;
+  hipError_t err = hipSuccess;
+  if (k <= kCandMaxK && cap > kCandMinCap && cap <= kCandMaxCap) {
+    const int n_s = csa_ix::sampled_count(cap);
+    err = csa_ix::launch_indexer<csa_ix::kSample>(H_I, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, B, T_q, d_I, cap,
+                                                  m, tw.sample, st, cu_rows, n_rows);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(cand_threshold_kernel, dim3(unsigned(rows)), dim3(kTThreads), 0, st, tw.sample, n_s, q_pos0,
+                       T_rows, cu_rows, n_seq, cap, m, k, tw.thr, tw.cnt, tw.miss);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    csa_ix::IxExtra x{};
+    x.thr = tw.thr;
+    x.cnt = tw.cnt;
+    x.cand = tw.cand;
+    err = csa_ix::launch_indexer<csa_ix::kCand>(H_I, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, B, T_q, d_I, cap,
+                                                m, nullptr, st, cu_rows, n_rows, x);
+    if (err != hipSuccess) return err;
+    const size_t lds = cand_select_lds(cap);
+    if ((err = csa_lds_opt_in(reinterpret_cast<const void*>(&cand_select_kernel), cand_select_lds(kCandMaxCap))) !=
+        hipSuccess)
+      return err;
+    hipLaunchKernelGGL(cand_select_kernel, dim3(unsigned(rows)), dim3(kTThreads), lds, st, tw.cand,
+                       tw.cnt, q_pos0, T_rows, cu_rows, n_seq, cap, m, k, idx, tw.miss);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    gate = tw.miss;
+  }
+  if (cap > 0) {
+    csa_ix::IxExtra x{};
+    x.gate = gate;
+    err = csa_ix::launch_indexer<csa_ix::kKey16>(H_I, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, B, T_q, d_I, cap,
+                                                 m, tw.key16, st, cu_rows, n_rows, x);
+    if (err != hipSuccess) return err;
+  }
+  switch (H_I) {
+    case 4: return launch_select_h<4>(ks, rows, st, tw.key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_rows, d_I, cap, m, k, idx, cu_rows, n_seq, gate);
+    case 8: return launch_select_h<8>(ks, rows, st, tw.key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_rows, d_I, cap, m, k, idx, cu_rows, n_seq, gate);
+    default: return launch_select_h<16>(ks, rows, st, tw.key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_rows, d_I, cap, m, k, idx, cu_rows, n_seq, gate);
   }
 }
 
 }  // namespace
 
-// Workspace of csa_indexer_topk: the 16-bit keys of every (query, entry).
+// Workspace of csa_indexer_topk: on the decode path the fp32 scores and the
+// slice lists; otherwise the row-tile path's buffers.
 size_t csa_indexer_topk_workspace_size(long rows, int T_q, int d_I, int cap) {
   if (use_fused_split(rows, T_q, d_I, cap)) return split_scores_bytes(rows, cap) + csa_split::split_ws_bytes(rows, cap);
-  return size_t(rows) * size_t(cap) * 2u;
+  return tile_ws_bytes(rows, cap);
 }
+size_t csa_indexer_topk_varlen_workspace_size(long n_rows, int cap) { return n_rows > 0 ? tile_ws_bytes(n_rows, cap) : 0; }
 
 namespace {
 
@@ -842,18 +1186,8 @@ csa_status_t indexer_topk_impl(const uint8_t* q_codes, const uint8_t* q_e8m0, co
                                           ride_along ? ride : nullptr);
     return e == hipSuccess ? CSA_OK : CSA_EHIP;
   }
-  uint16_t* key16 = static_cast<uint16_t*>(ws);
-  hipError_t err = hipSuccess;
-  if (cap > 0) {
-    err = csa_ix::launch_indexer<csa_ix::kKey16>(H_I, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, B, T_q, d_I, cap,
-                                                 m, key16, st);
-    if (err != hipSuccess) return CSA_EHIP;
-  }
-  switch (H_I) {
-    case 4: err = launch_select_h<4>(ks, rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_q, d_I, cap, m, k, idx, nullptr, 0); break;
-    case 8: err = launch_select_h<8>(ks, rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_q, d_I, cap, m, k, idx, nullptr, 0); break;
-    default: err = launch_select_h<16>(ks, rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, T_q, d_I, cap, m, k, idx, nullptr, 0); break;
-  }
+  const hipError_t err = tile_path(H_I, rows, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, B, T_q, nullptr, d_I, cap,
+                                   m, k, idx, ws, st);
   return err == hipSuccess ? CSA_OK : CSA_EHIP;
 }
 
@@ -900,21 +1234,9 @@ extern "C" csa_status_t csa_indexer_topk_varlen(const uint8_t* q_codes, const ui
   if (B < 1) return CSA_EINVAL;
   const int per_tile = 64 / H_I;   // queries per row tile of the packed indexer launch
   if ((long(n_rows) + per_tile - 1) / per_tile + B > 65535) return CSA_ENOTSUP;
-  const size_t need = size_t(n_rows) * size_t(cap) * 2u;
+  const size_t need = csa_indexer_topk_varlen_workspace_size(n_rows, cap);
   if (need > 0 && (!ws || ws_bytes < need)) return CSA_EWORKSPACE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int ks = (d_I + 127) / 128;
-  uint16_t* key16 = static_cast<uint16_t*>(ws);
-  hipError_t err = hipSuccess;
-  if (cap > 0) {
-    err = csa_ix::launch_indexer<csa_ix::kKey16>(H_I, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, B, 1, d_I, cap, m,
-                                                 key16, st, cu_rows, n_rows);
-    if (err != hipSuccess) return CSA_EHIP;
-  }
-  switch (H_I) {
-    case 4: err = launch_select_h<4>(ks, n_rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, 1, d_I, cap, m, k, idx, cu_rows, B); break;
-    case 8: err = launch_select_h<8>(ks, n_rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, 1, d_I, cap, m, k, idx, cu_rows, B); break;
-    default: err = launch_select_h<16>(ks, n_rows, st, key16, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, 1, d_I, cap, m, k, idx, cu_rows, B); break;
-  }
+  const hipError_t err = tile_path(H_I, n_rows, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, B, 1, cu_rows, d_I, cap,
+                                   m, k, idx, ws, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? CSA_OK : CSA_EHIP;
 }

@@ -129,7 +129,8 @@ def test_indexer_topk_rejects_bad_arguments():
     import long_context_compressed_03_amd as csa
     lib = csa.load()
     need = lib.csa_workspace_size(csa.CSA_OP_INDEXER_TOPK, 1, 2, 0, 128, 16)
-    assert need == 1 * 2 * 16 * 2                 # one 16-bit key per (query, entry)
+    # a 16-bit key per (query, entry) and 8192 (key, entry) candidate slots per query
+    assert need >= 1 * 2 * 16 * 2 + 1 * 2 * 8192 * 8
 
     def call(k=8, H_I=8, d_I=128, m=4, ws=_p(), nws=need, B=1, T=2, cap=16, idx=_p(), q=_p()):
         return lib.csa_indexer_topk(q, _p(), _p(), _p(), _p(), _p(), B, T, H_I, d_I, cap, m, k,
@@ -305,7 +306,8 @@ def test_varlen_compress_and_selection_reject_bad_arguments():
     assert sel(n_rows=-1) == csa.CSA_EINVAL
     assert sel(n_rows=0) == csa.CSA_OK                 # no rows: nothing launched
     need = lib.csa_workspace_size(csa.CSA_OP_INDEXER_TOPK_VARLEN, 5, 0, 0, 0, 64)
-    assert need == 5 * 64 * 2
+    assert need >= 5 * 64 * 2                          # at least the 16-bit keys of every (row, entry)
+    assert lib.csa_workspace_size(csa.CSA_OP_INDEXER_TOPK_VARLEN, 0, 0, 0, 0, 64) == 0
     assert sel() == csa.CSA_EWORKSPACE
     assert sel(ws=_p(), nws=need - 1) == csa.CSA_EWORKSPACE
     assert sel(B=60000, n_rows=200000, ws=_p(), nws=1 << 40) == csa.CSA_ENOTSUP   # too many row tiles

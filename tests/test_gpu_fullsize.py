@@ -8,7 +8,8 @@ which can afford a few rows at these sizes:
   * top-k indices of sampled rows (unfused, fused, and combined with the compression): bit-exact;
   * attention of sampled rows over the cache as the step left it: max-abs 2e-2 on top of
     the bf16 output's own half-unit rounding.
-The 1M layer pair is checked layer by layer the same way.
+The 1M layer pair is checked layer by layer the same way, both as the packed mixed step
+(one varlen call per op) and as separate calls per part.
 """
 import numpy as np
 import pytest
@@ -171,14 +172,65 @@ def test_csa_prefill_256k(csa):
     check_csa_rows(hl, dev, p, [(0, 0), (0, 2047), (0, 4095)], unfused=False)
 
 
-def test_layer_pair_1m(csa):
-    hosts, dev, st = run_workload("pair_1m")
+def test_layer_pair_1m_split(csa):
+    hosts, dev, st = run_workload("pair_1m_split")
     layers = dict(hosts)
-    say("pair_1m: every layer's pooled entries and sampled rows")
+    say("pair_1m_split: every layer's pooled entries and sampled rows")
     check_compress(layers["csa_decode."], dev, "csa_decode.", [0])
     check_csa_rows(layers["csa_decode."], dev, "csa_decode.", [(3, 0)], unfused=False)
     check_compress(layers["csa_chunk."], dev, "csa_chunk.", [0, 511])
     check_csa_rows(layers["csa_chunk."], dev, "csa_chunk.", [(0, 0), (0, 2047)], unfused=False)
+    check_compress(layers["hca_decode."], dev, "hca_decode.", [0])
+    check_hca_rows(layers["hca_decode."], dev, "hca_decode.", [(0, 0), (3, 0)])
+    check_compress(layers["hca_chunk."], dev, "hca_chunk.", [0, 15])
+    check_hca_rows(layers["hca_chunk."], dev, "hca_chunk.", [(0, 0), (0, 1000), (0, 2047)])
+
+
+def run_pair_packed():
+    """The 1M layer pair's mixed step as bench.py times it: 4 decode rows and the
+    2048-token chunk packed into one varlen call per op.  Returns the per-layer host
+    inputs and, per layer part, views of the packed device state in the per-part
+    layout the checks read ([B, ...] per part)."""
+    wls = workloads()
+    hosts = [(prefix, bench.host_layer(wls[w])) for prefix, w in bench.LAYERS["pair_1m_split"]]
+    hd = {prefix.rstrip("."): hl for prefix, hl in hosts}
+    st = bench.Step("pair_1m", 0)
+    dev = {}
+    for kind in ("csa", "hca"):
+        dec, ch = hd[kind + "_decode"], hd[kind + "_chunk"]
+        pk = bench.pack_layer(dec, ch)
+        bench.add_varlen_layer(st, dec, ch, kind + ".")
+        dev.update(bench.device_packed(pk, kind + ".", kind, dec["wl"].k))
+    dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in dev.items()}
+    say(f"pair_1m (packed): calls {st.order}")
+    st.run(dev)
+    torch.cuda.synchronize()
+    views = {}
+    for kind in ("csa", "hca"):
+        p = kind + "."
+        nd, T = hd[kind + "_decode"]["wl"].B, hd[kind + "_chunk"]["wl"].T_q
+        for part, sb, rows, shape_bt in (("_decode.", slice(0, nd), slice(0, nd), (nd, 1)),
+                                         ("_chunk.", slice(nd, nd + 1), slice(nd, nd + T), (1, T))):
+            v = {kind + part + n: dev[p + n][sb] for n in ("ck", "cv") if dev[p + n] is not None}
+            for n in ("cks", "cvs"):
+                v[kind + part + n] = None if dev[p + n] is None else dev[p + n][sb]
+            out = dev[p + "out"][rows]
+            v[kind + part + "out"] = out.reshape(shape_bt + tuple(out.shape[1:]))
+            if kind == "csa":
+                ix = dev[p + "idx"][rows]
+                v[kind + part + "idx"] = ix.reshape(shape_bt + tuple(ix.shape[1:]))
+            views.update(v)
+    return hosts, views
+
+
+def test_layer_pair_1m(csa):
+    hosts, dev = run_pair_packed()
+    layers = dict(hosts)
+    say("pair_1m (packed varlen calls): every layer's pooled entries and sampled rows")
+    check_compress(layers["csa_decode."], dev, "csa_decode.", [0])
+    check_csa_rows(layers["csa_decode."], dev, "csa_decode.", [(0, 0), (3, 0)], unfused=False)
+    check_compress(layers["csa_chunk."], dev, "csa_chunk.", [0, 511])
+    check_csa_rows(layers["csa_chunk."], dev, "csa_chunk.", [(0, 0), (0, 1023), (0, 2047)], unfused=False)
     check_compress(layers["hca_decode."], dev, "hca_decode.", [0])
     check_hca_rows(layers["hca_decode."], dev, "hca_decode.", [(0, 0), (3, 0)])
     check_compress(layers["hca_chunk."], dev, "hca_chunk.", [0, 15])

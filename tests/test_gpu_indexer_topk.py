@@ -56,6 +56,11 @@ FUSED_CASES = [
     (2, 1, 10000, 16, 256, 2, 500, [19999, 15000], False),         # 16 heads, two contraction steps
     (1, 1, 16384, 4, 64, 4, 500, [65535], True),                   # exact ties around the threshold
     (1, 1, 100000, 8, 128, 4, 2048, [399999], False),              # 49 slices: 4 per gather wave
+    # chunk rows on the threshold path (rows past 32768 entries)
+    (1, 3, 50000, 4, 64, 4, 800, [199990], True),                  # exact ties around the threshold
+    (2, 9, 45000, 16, 256, 4, 1500, [179990, 150000], False),      # 16 heads, two contraction steps
+    (1, 7, 40000, 16, 128, 4, 900, [159990], False),               # 16 heads, one contraction step
+    (1, 5, 3000, 16, 128, 4, 300, [11990], False),                 # the same on the 16-bit-key path
 ]
 
 
@@ -95,6 +100,36 @@ def test_fused_crowded_and_whole_buckets(csa):
     assert np.all(s[0, 0] == 0) and np.sum(s[0, 1] == 256.0) == k
     ref = topk(s.astype(np.float32), pos, m, k)
     assert np.array_equal(ref[0, 0], np.arange(k)) and np.array_equal(ref[0, 1], hot)
+    got = _fused(csa, x2, pos, m, k)
+    assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
+
+
+def test_fused_sample_above_the_kth_score(csa):
+    """Chunk rows on the threshold path: the sampled entries (the first 16 of every 1024)
+    score 256 and the rest 0, so the threshold taken from the sample leaves fewer than k
+    entries at or above it; the rows must fall back to the full pass and still select
+    exactly (the hot entries, then the lowest-index zeros).  A third row, random, rides
+    along, and a fourth has a zero query: every entry ties, more than the candidate
+    capacity."""
+    say("indexer_topk sample above the k-th score")
+    B, T, cap, H_I, d_I, m, k = 1, 4, 40000, 4, 64, 4, 1000
+    x = indexer_inputs(B, T, cap, H_I, d_I, seed=79)
+    x["q_codes"][0, :2] = 0x22                               # rows 0, 1: every element +1
+    x["q_e8m0"][0, :2] = 127
+    x["w"][0, :2] = 1.0
+    x["q_codes"][0, 3] = 0                                   # row 3: zero query
+    kc = x["k_codes"].copy()
+    ke = x["k_e8m0"].copy()
+    hot = np.array([e for e in range(cap) if e % 1024 < 16])
+    kc[0, :] = 0
+    kc[0, hot] = 0x22                                        # the sampled entries: +1
+    ke[0, :] = 127
+    x2 = dict(x, k_codes=kc, k_e8m0=ke)
+    pos = np.array([4 * cap - 4], np.int32)
+    s = indexer_scores(x2["q_codes"], x2["q_e8m0"], x2["w"], kc, ke, pos, m)
+    ref = topk(s.astype(np.float32), pos, m, k)
+    assert np.all(np.isin(hot, ref[0, 0])) and np.sum(s[0, 0] == 256.0) == hot.size < k
+    assert np.array_equal(ref[0, 3], np.arange(k))
     got = _fused(csa, x2, pos, m, k)
     assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
 

@@ -124,6 +124,7 @@ INDEXER_CASES = [
     (2, 3, 300, 16, 256, 2, [598, 100], False),
     (1, 9, 200, 8, 96, 1, [191], False),
     (1, 2, 1024, 4, 64, 4, [4094], True),
+    (2, 6, 500, 16, 128, 4, [1990, 700], False),
 ]
 
 
