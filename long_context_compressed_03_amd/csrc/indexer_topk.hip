@@ -867,17 +867,31 @@ CSA_DEV void pick_bin(const uint32_t* tot, uint32_t r, uint32_t* res) {
   }
 }
 
-template <bool kDesc, int kPer, typename Part>
+// One histogram update per element slot of the wave: the lanes whose bin is
+// the first active lane's add together through that lane (values of a row
+// mostly share their leading byte), the others each add their own.
+CSA_DEV void wave_hist_add(uint32_t* hist, bool on, uint32_t bin) {
+  const uint64_t act = __ballot(on);
+  if (!act) return;
+  const int lane = threadIdx.x & 63;
+  const int leader = __ffsll((unsigned long long)act) - 1;
+  const uint32_t lb = uint32_t(__shfl(int(bin), leader));
+  const uint64_t same = __ballot(on && bin == lb);
+  if (lane == leader) atomicAdd(&hist[lb], uint32_t(__popcll(same)));
+  else if (on && bin != lb) atomicAdd(&hist[bin], 1u);
+}
+
+template <bool kDesc, int kBits, int kPer, typename Part>
 CSA_DEV uint32_t radix_select(const uint32_t (&v)[kPer], Part part, uint32_t r, RadixLds& sh, uint32_t* n_at,
                               uint32_t* rank_in) {
   const int wv = threadIdx.x >> 6;
   uint32_t prefix = 0u, mask = 0u;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int shift = kBits - 8; shift >= 0; shift -= 8) {
     for (int x = threadIdx.x; x < (kTThreads / 64) * 256; x += kTThreads) (&sh.hist[0][0])[x] = 0u;
     __syncthreads();
 #pragma unroll
     for (int x = 0; x < kPer; ++x)
-      if (part(x) && (v[x] & mask) == prefix) atomicAdd(&sh.hist[wv][(v[x] >> shift) & 255u], 1u);
+      wave_hist_add(sh.hist[wv], part(x) && (v[x] & mask) == prefix, (v[x] >> shift) & 255u);
     __syncthreads();
     {
       uint32_t t = 0u;
@@ -939,8 +953,8 @@ __global__ __launch_bounds__(kTThreads) void cand_threshold_kernel(const uint16_
     v[x] = j < nsv ? uint32_t(src[j]) : 0u;
   }
   uint32_t n_at, rank_in;
-  const uint32_t key16 = radix_select<true>(v, [&](int x) { return tid + x * kTThreads < nsv; }, uint32_t(r), sh,
-                                            &n_at, &rank_in);
+  const uint32_t key16 = radix_select<true, 16>(v, [&](int x) { return tid + x * kTThreads < nsv; }, uint32_t(r),
+                                                sh, &n_at, &rank_in);
   if (tid == 0) thr[row] = __float_as_uint(key_score(key16 << 16));
 }
 
@@ -996,12 +1010,12 @@ __global__ __launch_bounds__(kTThreads) void cand_select_kernel(const uint2* __r
   auto valid = [&](int x) { return tid + x * kTThreads < int(n); };
   // K: the k-th largest key; need: how many of key K the selection takes
   uint32_t n_eq, need;
-  const uint32_t K = radix_select<true>(key, valid, uint32_t(k), sh.rx, &n_eq, &need);
+  const uint32_t K = radix_select<true, 32>(key, valid, uint32_t(k), sh.rx, &n_eq, &need);
   // among the entries of key K, the need-th lowest index I (all of them: no limit)
   uint32_t I = 0xFFFFFFFFu;
   if (need < n_eq) {
     uint32_t n_i, r_i;
-    I = radix_select<false>(ent, [&](int x) { return valid(x) && key[x] == K; }, need, sh.rx, &n_i, &r_i);
+    I = radix_select<false, 32>(ent, [&](int x) { return valid(x) && key[x] == K; }, need, sh.rx, &n_i, &r_i);
   }
   // the selected entries as a bitmap, then each one's rank among them
   auto chosen = [&](int x) { return valid(x) && (key[x] > K || (key[x] == K && ent[x] <= I)); };
