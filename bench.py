@@ -235,12 +235,13 @@ def add_layer(st, h, prefix, indexer="auto", batch_invariant=False):
                 # exact fallback), the indices
                 inter = nvis_sum * 4
             else:
-                # keys once, the 16-bit score keys written and read back, the indices
-                inter = rows * wl.cap * 2 + nvis_sum * 2
+                # keys once; the sampled 16-bit keys written and read back; the
+                # candidate (key, entry) pairs, about 2k per row, written and read back
+                inter = tile_inter_bytes(rows, wl.cap, k)
             st.add(Kernel(name("indexer_topk"), f_fused,
                           B * wl.cap * idx_bytes + inter + rows * k * 4 + rows * wl.H_I * (idx_bytes + 4),
                           2 * wl.H_I * wl.d_I * nvis_sum, MXFP4_PEAK_TFLOPS, "indexer_topk",
-                          "indexer_slice_kernel, topk_kernel<true>" if decode_split else "indexer_kernel, select_kernel"))
+                          "indexer_slice_kernel, topk_kernel<true>" if decode_split else TILE_TOPK_HIP))
         else:
             st.add(Kernel(name("indexer_scores"), f_indexer,
                           B * wl.cap * idx_bytes + rows * wl.cap * 4 + rows * wl.H_I * (idx_bytes + 4),
@@ -260,6 +261,23 @@ def add_layer(st, h, prefix, indexer="auto", batch_invariant=False):
         nv_max = min((wl.q_pos0[0] + wl.T_q) // m, wl.cap)
         st.add(Kernel(name("dense_attn"), f_attn, B * nv_max * ent + B * wl.L_raw * 512 + q_bytes,
                       4 * H * 128 * (nvis_sum + rows * W), BF16_PEAK_TFLOPS, "dense_attn", attn_hip(rows, True, wl.T_q)))
+
+
+# Kernels of the row-tile indexer top-k (threshold path; the 16-bit-key pass and
+# select_kernel sit behind the miss gate and return at once unless a row missed)
+TILE_TOPK_HIP = ("indexer_kernel (sample, candidates), cand_threshold_kernel, cand_select_kernel; "
+                 "indexer_kernel (16-bit keys), select_kernel behind the miss gate")
+
+
+def tile_inter_bytes(rows, cap, k):
+    """Bytes the threshold path moves besides the keys and indices: every row's sampled
+    16-bit keys (16 of every 1024 entries) written and read back, and its candidate
+    (key, entry) pairs, about 2k per row, written and read back."""
+    if not (k <= 3276 and 32768 < cap <= (1 << 19)):
+        # outside the threshold path's range: 16-bit keys of every entry written and read
+        return rows * cap * 2 * 2
+    sampled = (cap // 1024) * 16 + min(cap % 1024, 16)
+    return rows * sampled * 2 * 2 + rows * 2 * k * 8 * 2
 
 
 def attn_hip(rows, dense, T_q):
@@ -371,13 +389,13 @@ def add_varlen_layer(st, dec, ch, prefix):
         def f_sel(c):
             csa.csa_indexer_topk_varlen(c[p + "qc"], c[p + "qe"], c[p + "w"], c[p + "kc"], c[p + "ke"],
                                         c[p + "cu_rows"], c[p + "pos"], m, k, c[p + "idx"])
-        # each sequence's keys once, the 16-bit score keys written and the visible ones read
-        # back, the indices, the queries and weights
+        # each sequence's keys once, the sample and candidate traffic of the threshold
+        # path, the indices, the queries and weights
         st.add(Kernel(p + "indexer_topk", f_sel,
-                      (nd * wd.cap + wc.cap) * idx_bytes + rows * cap * 2 + (nvis_d + nvis_c) * 2 + rows * k * 4
+                      (nd * wd.cap + wc.cap) * idx_bytes + tile_inter_bytes(rows, cap, k) + rows * k * 4
                       + rows * wd.H_I * (idx_bytes + 4),
                       2 * wd.H_I * wd.d_I * (nvis_d + nvis_c), MXFP4_PEAK_TFLOPS, "indexer_topk",
-                      "indexer_kernel, select_kernel"))
+                      TILE_TOPK_HIP))
 
         def f_attn(c):
             csa.csa_sparse_attn_varlen(c[p + "q"], c[p + "ck"], c[p + "cv"], c[p + "idx"], c[p + "kw"], c[p + "vw"],
