@@ -291,7 +291,8 @@ constexpr size_t lds_bytes() {
 // 8 head dims of a gathered part as four bf16 pairs (src 0 -> zeros).  E4M3
 // codes go through the CDNA4 fp8 -> bf16 conversion, which is exact (every
 // E4M3 value is a bf16 value); the per-entry scale is applied elsewhere.
-template <int kCKV>
+// kAll: every slot holds a compressed entry (src 1), so no selects.
+template <int kCKV, bool kAll = false>
 CSA_DEV u32x4 part_bf16(const u32x4* w, int src, int h) {
   // selects, not branches (see gather_slot): the result depends on src only
   u32x4 r = w[0];
@@ -302,15 +303,18 @@ CSA_DEV u32x4 part_bf16(const u32x4* w, int src, int h) {
                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, 1.0f, false)),
                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c1, 1.0f, true))};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = src == 1 ? cv[q] : r[q];
+    for (int q = 0; q < 4; ++q) r[q] = kAll || src == 1 ? cv[q] : r[q];
   }
+  if constexpr (!kAll) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) r[q] = src == 0 ? 0u : r[q];
+    for (int q = 0; q < 4; ++q) r[q] = src == 0 ? 0u : r[q];
+  }
   return r;
 }
 
 // sk_mul: factor folded into the stored K scale (the logit scale in the log2 domain).
-template <int kIO, int kCKV>
+// kAll (bf16 path): the item's slots are compressed entries (prefetch_entries).
+template <int kIO, int kCKV, bool kAll = false>
 CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr, float sk_mul) {
   const int kp = item_kp();
   const int dg = item_dg();
@@ -319,8 +323,8 @@ CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr, float sk_mul) {
     u32x4 kw[2], vw[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      kw[e] = part_bf16<kCKV>(pr.k[e], pr.src[e], dg & 1);
-      vw[e] = part_bf16<kCKV>(pr.v[e], pr.src[e], dg & 1);
+      kw[e] = part_bf16<kCKV, kAll>(pr.k[e], pr.src[e], dg & 1);
+      vw[e] = part_bf16<kCKV, kAll>(pr.v[e], pr.src[e], dg & 1);
       *reinterpret_cast<u32x4*>(&s.K[2 * kp + e][dg * 8]) = kw[e];
     }
     // V^T: head dim x of keys 2kp and 2kp+1 as one bf16 pair
@@ -348,10 +352,10 @@ CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr, float sk_mul) {
   if (dg == 0) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const bool scaled = kCKV == CSA_FP8_E4M3 && pr.src[e] == 1;
+      const bool scaled = kCKV == CSA_FP8_E4M3 && (kAll || pr.src[e] == 1);
       s.sk[2 * kp + e] = (scaled ? pr.sk[e] : 1.f) * sk_mul;
       s.sv[2 * kp + e] = scaled ? pr.sv[e] : 1.f;
-      s.bias[2 * kp + e] = pr.src[e] != 0 ? 0.f : -INFINITY;
+      s.bias[2 * kp + e] = kAll || pr.src[e] != 0 ? 0.f : -INFINITY;
     }
   }
 }
@@ -1115,6 +1119,34 @@ CSA_DEV void prefetch_mq(const AttnArgs& a, Pre<CSA_BF16>& pr, uint32_t (&vis)[2
   }
 }
 
+// Rows of a chunk whose 64 slots are the compressed entries row0 .. row0 + 63,
+// every one seen by every query of the block (most chunks of a dense list):
+// no window rows, no empty slots, so neither source selects nor visibility
+// masks.  Same item mapping and loads as gather_slot with src 1.
+template <int kCKV>
+CSA_DEV void prefetch_entries(const AttnArgs& a, Pre<CSA_BF16>& pr, long row0) {
+  constexpr long kCB = kCKV == CSA_BF16 ? 2 : 1;   // bytes per compressed value (bf16 or fp8)
+  const int kp = item_kp();
+  const int dg = item_dg();
+  const long r = row0 + 2 * kp;
+  const long off = r * (kHeadDim * kCB) + (kCKV == CSA_FP8_E4M3 ? long(dg & ~1) * 8 : long(dg) * 8 * kCB);
+  const char* pk = static_cast<const char*>(a.ck) + off;
+  const char* pv = static_cast<const char*>(a.cv) + off;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    pr.k[x][0] = *reinterpret_cast<const u32x4*>(pk + x * kHeadDim * kCB);
+    pr.v[x][0] = *reinterpret_cast<const u32x4*>(pv + x * kHeadDim * kCB);
+    if constexpr (kCKV == CSA_FP8_E4M3) {
+      pr.sk[x] = a.ck_scale[r + x];
+      pr.sv[x] = a.cv_scale[r + x];
+    } else {
+      pr.sk[x] = 1.f;
+      pr.sv[x] = 1.f;
+    }
+    pr.src[x] = 1;
+  }
+}
+
 // Tile `tile` of a varlen many-query launch: the rows of every sequence with
 // more than kQB rows cut into tiles of kQB, sequences in order (sequences of
 // at most kQB rows are served by pieces instead).  False past the last tile.
@@ -1205,25 +1237,46 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
     l_run[ht] = 0.f;
   }
 
+  // Chunks [j_lo, j_full) hold only entries that every query of the block
+  // sees (entry e is seen from position (e+1)*m' - 1 on; the block's first
+  // query is the earliest): they are gathered without source selects and
+  // scored without visibility masks.  The rest (the last entries, the
+  // window) take the general path.
+  // (rounded down to whole pairs of chunks, as the walk takes them).
+  const int nv_all = min((t0 + 1) / a.k, a.cap);
+  const int j_full = j_lo + max(0, min(nv_all, j_hi) - j_lo) / (2 * kNK) * (2 * kNK);
+  const long row_b = long(b) * a.cap;
+  auto fetch = [&](Pre<CSA_BF16>& prc, uint32_t (&tgc)[2], int jc) {
+    if (jc < j_full)
+      prefetch_entries<kCKV>(a, prc, row_b + jc);
+    else
+      prefetch_mq<kCKV>(a, prc, tgc, b, raw0, nv_max, p_lo, n_list, jc, t0, n_q);
+  };
+
   // two chunks in flight: chunk c is stored from one register set while
   // chunk c + 1 is still loading into the other
   Pre<CSA_BF16> pr[2];
   uint32_t tag[2][2];
-  if (j_lo < j_hi) prefetch_mq<kCKV>(a, pr[0], tag[0], b, raw0, nv_max, p_lo, n_list, j_lo, t0, n_q);
-  if (j_lo + kNK < j_hi) prefetch_mq<kCKV>(a, pr[1], tag[1], b, raw0, nv_max, p_lo, n_list, j_lo + kNK, t0, n_q);
-  auto step = [&](Pre<CSA_BF16>& prc, uint32_t (&tgc)[2], int j0) {
+  if (j_lo < j_hi) fetch(pr[0], tag[0], j_lo);
+  if (j_lo + kNK < j_hi) fetch(pr[1], tag[1], j_lo + kNK);
+  auto step = [&](auto all_t, Pre<CSA_BF16>& prc, uint32_t (&tgc)[2], int j0) {
+    constexpr bool kAll = decltype(all_t)::value;
     __syncthreads();
-    store_chunk<CSA_BF16, kCKV>(s.c, prc, a.sm_log2);
-    if (item_dg() == 0) {
+    store_chunk<CSA_BF16, kCKV, kAll>(s.c, prc, a.sm_log2);
+    if (!kAll && item_dg() == 0) {
       s.vis[2 * item_kp()] = tgc[0];
       s.vis[2 * item_kp() + 1] = tgc[1];
     }
     __syncthreads();
-    if (j0 + 2 * kNK < j_hi)
-      prefetch_mq<kCKV>(a, prc, tgc, b, raw0, nv_max, p_lo, n_list, j0 + 2 * kNK, t0, n_q);
+    if (j0 + 2 * kNK < j_hi) fetch(prc, tgc, j0 + 2 * kNK);
     // S^T for the 4 key tiles x 2 head tiles; K fragments shared by both tiles,
     // contraction steps outermost so only one step's query fragments are live
     float x[2][4][4];
+    // logits relative to the running max, x = S * scale - m (one fma; m = 0
+    // before the first finite logit); a key the query does not see gets -inf
+    float mu[2];
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht) mu[ht] = m_run[ht] == -INFINITY ? 0.f : m_run[ht];
     {
       v4f acc[4][2];
 #pragma unroll
@@ -1241,15 +1294,22 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        // keys kt*16 + 4g .. +3 (16-byte reads); a key the query does not see
-        // gets -inf as a selected bias, with no branch
-        const u32x4 vb = *reinterpret_cast<const u32x4*>(&s.vis[kt * 16 + 4 * g]);
+        // keys kt*16 + 4g .. +3 (16-byte reads)
         const v4f scl = *reinterpret_cast<const v4f*>(&s.c.sk[kt * 16 + 4 * g]);
+        if constexpr (kAll) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float bias = ((vb[r] >> qi) & 1u) ? 0.f : -INFINITY;
+          for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int ht = 0; ht < 2; ++ht) x[ht][kt][r] = __builtin_fmaf(acc[kt][ht][r], scl[r], bias);
+            for (int ht = 0; ht < 2; ++ht) x[ht][kt][r] = __builtin_fmaf(acc[kt][ht][r], scl[r], -mu[ht]);
+        } else {
+          const u32x4 vb = *reinterpret_cast<const u32x4*>(&s.vis[kt * 16 + 4 * g]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool seen = (vb[r] >> qi) & 1u;
+#pragma unroll
+            for (int ht = 0; ht < 2; ++ht)
+              x[ht][kt][r] = __builtin_fmaf(acc[kt][ht][r], scl[r], seen ? -mu[ht] : -INFINITY);
+          }
         }
       }
     }
@@ -1262,24 +1322,29 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) cmax = fmaxf(cmax, x[ht][kt][r]);
       cmax = column_max(cmax);
-      // lazy running max, as in the one-query kernel
-      const bool grow = cmax > m_run[ht] + 8.f;
-      const float m_new = grow ? cmax : m_run[ht];
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      // lazy running max, as in the one-query kernel: it moves only for a
+      // first finite logit or one more than 2^8 above it (P stays <= 2^8)
+      const bool grow = m_run[ht] == -INFINITY ? cmax > -INFINITY : cmax > 8.f;
       if (__ballot(grow)) {
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[ht] - m_use) : 1.f;
+        const float m_new = grow ? mu[ht] + cmax : m_run[ht];
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[ht] - m_new) : 1.f;   // 0 from -inf
+        const float sh = grow ? cmax : 0.f;
         l_run[ht] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[ht][dt] *= alpha;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[ht][kt][r] -= sh;
+        m_run[ht] = m_new;
       }
-      m_run[ht] = m_new;
       float psum = 0.f;
       float p[4][4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          p[kt][r] = __builtin_amdgcn_exp2f(x[ht][kt][r] - m_use);
+          p[kt][r] = __builtin_amdgcn_exp2f(x[ht][kt][r]);
           psum += p[kt][r];
         }
       l_run[ht] += psum;
@@ -1318,9 +1383,16 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
       }
     }
   };
-  for (int j0 = j_lo; j0 < j_hi; j0 += 2 * kNK) {
-    step(pr[0], tag[0], j0);
-    if (j0 + kNK < j_hi) step(pr[1], tag[1], j0 + kNK);
+  const std::true_type all_entries;
+  const std::false_type general;
+  int j0 = j_lo;
+  for (; j0 < j_full; j0 += 2 * kNK) {
+    step(all_entries, pr[0], tag[0], j0);
+    step(all_entries, pr[1], tag[1], j0 + kNK);
+  }
+  for (; j0 < j_hi; j0 += 2 * kNK) {
+    step(general, pr[0], tag[0], j0);
+    if (j0 + kNK < j_hi) step(general, pr[1], tag[1], j0 + kNK);
   }
   if (!q_ok) return;
   if (kPacked && piece >= 0) {
