@@ -64,6 +64,15 @@ CSA_DEV v4f mfma_k16(const u32x2& a, const u32x2& b, v4f c) {
                                                    0);
 }
 CSA_DEV v4f mfma_f32(float a, float b, v4f c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+CSA_DEV v4f mfma_h32(const u32x4& a, const u32x4& b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+}
+// Two fp32 values rounded to the nearest fp16 (ties to even), packed low/high.
+CSA_DEV uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f_t{lo, hi}, v2h));
+}
 
 struct AttnArgs {
   const void* q;
@@ -312,8 +321,20 @@ CSA_DEV u32x4 part_bf16(const u32x4* w, int src, int h) {
   return r;
 }
 
+// 8 head dims of a gathered fp8 entry part as four fp16 pairs: every E4M3
+// value is an fp16 value (exponents -9 .. 8), so the conversion is exact.
+CSA_DEV u32x4 part_f16_fp8(const u32x4* w, int h) {
+  const uint32_t c0 = h ? w[0][2] : w[0][0], c1 = h ? w[0][3] : w[0][1];
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c1, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c1, 1.0f, true))};
+}
+
 // sk_mul: factor folded into the stored K scale (the logit scale in the log2 domain).
-// kAll (bf16 path): the item's slots are compressed entries (prefetch_entries).
+// kAll (bf16 path): the item's slots are compressed entries (prefetch_entries);
+// with fp8 entries V^T is then stored as fp16 (exact) for the one-product
+// P*V of the many-query kernel.
 template <int kIO, int kCKV, bool kAll = false>
 CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr, float sk_mul) {
   const int kp = item_kp();
@@ -324,7 +345,10 @@ CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr, float sk_mul) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       kw[e] = part_bf16<kCKV, kAll>(pr.k[e], pr.src[e], dg & 1);
-      vw[e] = part_bf16<kCKV, kAll>(pr.v[e], pr.src[e], dg & 1);
+      if constexpr (kAll && kCKV == CSA_FP8_E4M3)
+        vw[e] = part_f16_fp8(pr.v[e], dg & 1);
+      else
+        vw[e] = part_bf16<kCKV, kAll>(pr.v[e], pr.src[e], dg & 1);
       *reinterpret_cast<u32x4*>(&s.K[2 * kp + e][dg * 8]) = kw[e];
     }
     // V^T: head dim x of keys 2kp and 2kp+1 as one bf16 pair
@@ -1236,6 +1260,11 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
     m_run[ht] = -INFINITY;
     l_run[ht] = 0.f;
   }
+  // fp8 entries: o is kept in units of vref, a power of two at or above
+  // every V scale seen so far (within 2^7), so that P x V scale / vref stays
+  // below 2^15 and enters the fp16 product of an all-entries chunk unrounded
+  // in range; vref moves up lazily (o rescaled exactly by a power of two)
+  float vref = 0.f, vinv = 0.f;
 
   // Chunks [j_lo, j_full) hold only entries that every query of the block
   // sees (entry e is seen from position (e+1)*m' - 1 on; the block's first
@@ -1313,7 +1342,36 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
         }
       }
     }
-    uint32_t pw[2][2][4], pl[2][2][4];   // [ht][32-key step][pair]: P as bf16 hi + lo
+    // all-entries chunks of fp8 entries: V^T is fp16 (exact) and P one fp16
+    // operand (11 significant bits, about 2^-12 of |P V| per product); other
+    // chunks: bf16 V^T and P as bf16 hi + lo
+    constexpr bool kF16 = decltype(all_t)::value && kCKV == CSA_FP8_E4M3;
+    // V scales of the chunk's keys (kt*16 + 4g .. +3), over vref
+    v4f svk[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) svk[kt] = *reinterpret_cast<const v4f*>(&s.c.sv[kt * 16 + 4 * g]);
+    if constexpr (kCKV == CSA_FP8_E4M3) {
+      float smax = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) smax = fmaxf(smax, svk[kt][r]);
+      smax = column_max(smax);   // every lane: the chunk's largest V scale
+      if (smax > vref * 128.f) {
+        // the power of two at or above smax (at most 2^127)
+        const float nref = __uint_as_float(min((__float_as_uint(smax) + 0x007FFFFFu) & 0x7F800000u, 0x7F000000u));
+        const float f = vref / nref;   // 0 before the first reference (o is 0 then)
+#pragma unroll
+        for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) o[ht][dt] *= f;
+        vref = nref;
+        vinv = 1.f / nref;
+      }
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) svk[kt] *= vinv;
+    }
+    uint32_t pw[2][2][4], pl[2][2][4];   // [ht][32-key step][pair]: P (fp16, or bf16 hi + lo)
 #pragma unroll
     for (int ht = 0; ht < 2; ++ht) {
       float cmax = -INFINITY;
@@ -1352,13 +1410,16 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
       // key (2st)*16 + 4g + j (j < 4) / (2st+1)*16 + 4g + j - 4
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const v4f sv = *reinterpret_cast<const v4f*>(&s.c.sv[kt * 16 + 4 * g]);   // keys kt*16 + 4g .. +3
         const int st = kt >> 1;
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int h2 = (kt & 1) * 2 + hh;
-          split_bf16x2(p[kt][2 * hh] * sv[2 * hh], p[kt][2 * hh + 1] * sv[2 * hh + 1], &pw[ht][st][h2],
-                       &pl[ht][st][h2]);
+          const float a0 = p[kt][2 * hh] * svk[kt][2 * hh];
+          const float a1 = p[kt][2 * hh + 1] * svk[kt][2 * hh + 1];
+          if constexpr (kF16)
+            pw[ht][st][h2] = pack_f16x2(a0, a1);
+          else
+            split_bf16x2(a0, a1, &pw[ht][st][h2], &pl[ht][st][h2]);
         }
       }
     }
@@ -1376,10 +1437,15 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
         const u32x2 lo = *reinterpret_cast<const u32x2*>(vt);
         const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + 16);
         const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
-        o[0][dt] = mfma_k32(vf, pb0, o[0][dt]);
-        o[1][dt] = mfma_k32(vf, pb1, o[1][dt]);
-        o[0][dt] = mfma_k32(vf, pl0, o[0][dt]);
-        o[1][dt] = mfma_k32(vf, pl1, o[1][dt]);
+        if constexpr (kF16) {
+          o[0][dt] = mfma_h32(vf, pb0, o[0][dt]);
+          o[1][dt] = mfma_h32(vf, pb1, o[1][dt]);
+        } else {
+          o[0][dt] = mfma_k32(vf, pb0, o[0][dt]);
+          o[1][dt] = mfma_k32(vf, pb1, o[1][dt]);
+          o[0][dt] = mfma_k32(vf, pl0, o[0][dt]);
+          o[1][dt] = mfma_k32(vf, pl1, o[1][dt]);
+        }
       }
     }
   };
@@ -1395,6 +1461,12 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
     if (j0 + kNK < j_hi) step(general, pr[1], tag[1], j0 + kNK);
   }
   if (!q_ok) return;
+  if constexpr (kCKV == CSA_FP8_E4M3) {
+#pragma unroll
+    for (int ht = 0; ht < 2; ++ht)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[ht][dt] *= vref;
+  }
   if (kPacked && piece >= 0) {
     // the piece's partial state (max in the log2 domain, sum, unnormalised
     // output), in attn_merge_kernel's layout: partial row b * kQB + i, split
