@@ -1260,10 +1260,12 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
     m_run[ht] = -INFINITY;
     l_run[ht] = 0.f;
   }
-  // fp8 entries: o is kept in units of vref, a power of two at or above
-  // every V scale seen so far (within 2^7), so that P x V scale / vref stays
-  // below 2^15 and enters the fp16 product of an all-entries chunk unrounded
-  // in range; vref moves up lazily (o rescaled exactly by a power of two)
+  // fp8 entries: o is kept in units of vref, a power of two within 2^7 of
+  // the current chunk's largest V scale (2^-126 .. 2^126), so that P x V
+  // scale / vref stays below 2^15 and, for the chunk's larger scales, above
+  // fp16's subnormal range in the one fp16 product of an all-entries chunk;
+  // vref follows the scales lazily, o rescaled by an exact power of two (at
+  // most 2^64 up per chunk)
   float vref = 0.f, vinv = 0.f;
 
   // Chunks [j_lo, j_full) hold only entries that every query of the block
@@ -1357,16 +1359,21 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) smax = fmaxf(smax, svk[kt][r]);
       smax = column_max(smax);   // every lane: the chunk's largest V scale
-      if (smax > vref * 128.f) {
-        // the power of two at or above smax (at most 2^127)
-        const float nref = __uint_as_float(min((__float_as_uint(smax) + 0x007FFFFFu) & 0x7F800000u, 0x7F000000u));
-        const float f = vref / nref;   // 0 before the first reference (o is 0 then)
+      const bool down = smax > 0.f && smax * 128.f < vref;
+      if (smax > vref * 128.f || down) {
+        // the power of two at or above smax (2^-126 .. 2^126), at most 2^64
+        // below the old one; its inverse (exponent field 254 - E) and the
+        // rescale of o are exact
+        uint32_t eb = min((__float_as_uint(smax) + 0x007FFFFFu) & 0x7F800000u, 0x7E800000u);
+        if (down) eb = max(eb, max(__float_as_uint(vref), 0x20800000u) - 0x20000000u);
+        const float ninv = __uint_as_float(0x7F000000u - eb);
+        const float f = vref * ninv;   // 0 before the first reference (o is 0 then)
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht)
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) o[ht][dt] *= f;
-        vref = nref;
-        vinv = 1.f / nref;
+        vref = __uint_as_float(eb);
+        vinv = ninv;
       }
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) svk[kt] *= vinv;

@@ -240,3 +240,38 @@ def test_chain_cache_append_fp8_then_sparse(csa):
                                   cv_scale=cvs, lse=lse_g, batch_invariant=form != "plain")
         torch.cuda.synchronize()
         _check(form, out, lse_g, O, lse, io)
+
+
+def test_dense_many_query_scale_swings(csa):
+    """The many-query dense kernel (plain call, >= 256 query rows) over fp8 entries whose V
+    scales swing across chunks of 64 entries: 2^20 (with keys pointing away from every query,
+    so their weights are ~2^-70 and their products vanish), 2^-12, and 1 elsewhere.  The kernel
+    carries its output in units of a power-of-two V-scale reference that must follow the scales
+    down again after a large chunk, or the fp16 P of the following chunks would fall into
+    fp16's subnormal range; the check is the usual element-wise one against the oracle."""
+    from csa_synth.gen import f32_to_bf16_bits
+    io, B, T, H, mp, cap, W = "bf16", 1, 256, 64, 16, 1024, 64
+    say(f"fp8 V-scale swings: dense many-query T={T} H={H} m'={mp} cap={cap} W={W}")
+    pos = np.array([cap * mp - T], np.int32)   # the last query sees all cap entries
+    L_raw = T + W
+    raw0 = (pos + T - L_raw).astype(np.int32)
+    rq, rk, rv, rkw, rvw, ru = streams(75, 0, 6)
+    u = ru.standard_normal(D).astype(np.float32)
+    u /= np.linalg.norm(u)
+    q = f32_to_bf16_bits(normal_f32(rq, (B, T, H, D)) + 8.0 * u)
+    factor = np.ones(cap // 64, np.float32)
+    far = np.zeros(cap // 64, bool)
+    factor[[1, 7]] = 2.0 ** 20
+    far[[1, 7]] = True
+    factor[6] = 2.0 ** -12
+    Kt = normal_f32(rk, (B, cap, D))
+    Kt[:, np.repeat(far, 64)] = -200.0 * u
+    Vt = normal_f32(rv, (B, cap, D)) * np.repeat(factor, 64)[None, :, None]
+    cK, cKs = store(Kt.astype(np.float64), "fp8")
+    cV, cVs = store(Vt.astype(np.float64), "fp8")
+    Kw, Vw = normal_kv(rkw, (B, L_raw, D), io), normal_kv(rvw, (B, L_raw, D), io)
+    O, lse = dense_attn(decode_kv(q, io), decode_kv(cK, "fp8", cKs), decode_kv(cV, "fp8", cVs), mp,
+                        decode_kv(Kw, io), decode_kv(Vw, io), raw0, pos, W)
+    assert np.abs(O).max() < 20.0   # the far chunks' products do vanish
+    x = dict(q=q, cK=cK, cK_scale=cKs, cV=cV, cV_scale=cVs, Kw=Kw, Vw=Vw)
+    _run_all_forms(csa, True, x, io, mp, None, raw0, pos, W, B, T, H, O, lse)
