@@ -492,19 +492,19 @@ def build_append(args):
     # m K/V rows and logits read back; the fp8 entries and scales written; pos, plan, base
     nbytes = B * (2 * 256 + 4 + 2 * (2 * 256 + 4) + m * (2 * 256 + 4) + 2 * (128 + 4) + 4 + 8 + 8 + 4)
 
-    def f_append(c):
-        csa.csa_kv_cache_append(c["k_new"], c["v_new"], c["z_new"], c["pos"], c["rk"], c["rv"], c["rz"], m,
-                                c["ck"], c["cv"], ck_scale=c["cks"], cv_scale=c["cvs"], raw_pos0=c["raw0"])
-    st.add(Kernel("kv_cache_append", f_append, nbytes, 0, BF16_PEAK_TFLOPS, "kv_cache_append",
-                  "cache_append_short_kernel"))
+    # per sequence: the K/V token's rows and logit read, 2 copies written, the block's m K/V
+    # rows and logits read back, the fp8 entries and scales written; the indexer key's row and
+    # logit read, 2 copies written, its block's m rows and logits read back, the 64 + 4 B MXFP4
+    # entry written; pos and the window base
+    nbytes = B * ((2 * 256 + 4 + 2 * (2 * 256 + 4) + m * (2 * 256 + 4) + 2 * (128 + 4))
+                  + (256 + 4 + 2 * (256 + 4) + m * (256 + 4) + 68) + 4 + 4)
 
-    def f_append_ix(c):
-        csa.csa_indexer_key_append(c["ik_new"], c["z_new"], c["pos"], c["irk"], c["rz_i"], m, c["kc"], c["ke"])
-    # per sequence: the key row and logit read, 2 copies written, the block's m rows and
-    # logits read back, the 64 + 4 B MXFP4 entry written; pos
-    nbytes_ix = B * (256 + 4 + 2 * (256 + 4) + m * (256 + 4) + 68 + 4)
-    st.add(Kernel("indexer_key_append", f_append_ix, nbytes_ix, 0, BF16_PEAK_TFLOPS, "indexer_key_append",
-                  "indexer_key_append_kernel"))
+    def f_append(c):
+        csa.csa_decode_append(c["k_new"], c["v_new"], c["z_new"], c["ik_new"], c["z_new"], c["pos"], c["rk"],
+                              c["rv"], c["rz"], m, c["ck"], c["cv"], c["irk"], c["rz_i"], c["kc"], c["ke"],
+                              ck_scale=c["cks"], cv_scale=c["cvs"], raw_pos0=c["raw0"])
+    st.add(Kernel("decode_append", f_append, nbytes, 0, BF16_PEAK_TFLOPS, "decode_append",
+                  "decode_append_kernel"))
     K = torch.from_numpy(x["K"].view(np.int16)).view(torch.bfloat16).cuda()
     V = torch.from_numpy(x["V"].view(np.int16)).view(torch.bfloat16).cuda()
     Z = torch.from_numpy(x["logits"]).cuda()
@@ -746,7 +746,8 @@ KERNEL_SOURCES = {
                               "compress_core.hpp", "compress.hip", "common.hpp"],
     "mxfp4_quantize": ["quant.hip", "mxfp4.hpp", "common.hpp"],
     "kv_cache_append": ["cache.hip", "compress.hip", "compress_core.hpp", "mxfp4.hpp", "common.hpp"],
-    "indexer_key_append": ["cache.hip", "compress_core.hpp", "mxfp4.hpp", "common.hpp"]}
+    "indexer_key_append": ["cache.hip", "compress_core.hpp", "mxfp4.hpp", "common.hpp"],
+    "decode_append": ["cache.hip", "compress_core.hpp", "mxfp4.hpp", "common.hpp"]}
 
 
 def measured_traffic(workload, kernel):

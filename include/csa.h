@@ -538,6 +538,34 @@ csa_status_t csa_indexer_key_append(const void* k_new, const float* z_new, int32
                                     void* k_ring, float* z_ring, int32_t m, int32_t cap,
                                     uint8_t* codes, uint8_t* e8m0, void* stream);
 
+/* ---------------------------------------------------------------------
+ * csa_decode_append -- both cache appends of a CSA layer's decode token
+ * (its K/V and its indexer key) in one launch.
+ *
+ * Passage: as csa_kv_cache_append and csa_indexer_key_append.  The results
+ * are exactly those of
+ *   csa_kv_cache_append(k_new, v_new, z_new, io_dtype, pos, B, d, L_ring,
+ *                       k_ring, v_ring, z_ring, m, cap, ckv_dtype, ck, cv,
+ *                       ck_scale, cv_scale, raw_pos0, NULL, 0, stream)
+ * followed by
+ *   csa_indexer_key_append(ki_new, zi_new, io_dtype, pos, B, d, Li_ring,
+ *                          ki_ring, zi_ring, m, cap, codes, e8m0, stream),
+ * bit for bit: the two appends touch disjoint buffers and run as the two
+ * halves of one grid with the same code.  Arguments, layouts, ownership and
+ * preconditions as in those two calls (the indexer keys have their own
+ * logits zi_new [B], ring ki_ring [B, 2*Li_ring, d], zi_ring [B, 2*Li_ring]).
+ * Limits: d = 128; m < 32; m <= L_ring, Li_ring; B * 2 * max(L_ring,
+ * Li_ring) < 2^31.  Errors as those calls; nothing is enqueued on an
+ * argument error.
+ * ------------------------------------------------------------------- */
+csa_status_t csa_decode_append(const void* k_new, const void* v_new, const float* z_new,
+                               const void* ki_new, const float* zi_new, int32_t io_dtype,
+                               const int32_t* pos, int32_t B, int32_t d, int32_t m, int32_t cap,
+                               int32_t L_ring, void* k_ring, void* v_ring, float* z_ring,
+                               int32_t ckv_dtype, void* ck, void* cv, float* ck_scale,
+                               float* cv_scale, int32_t* raw_pos0, int32_t Li_ring, void* ki_ring,
+                               float* zi_ring, uint8_t* codes, uint8_t* e8m0, void* stream);
+
 /* Workspace bytes a call needs.  n_keys = k + W (CSA) or cap + W (HCA);
  * for CSA_OP_TOPK and CSA_OP_INDEXER_TOPK pass T_q and n_keys = cap (and, for
  * CSA_OP_INDEXER_TOPK, d = d_I).  Returns 0 when none is needed and

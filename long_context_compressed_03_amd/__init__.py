@@ -32,7 +32,7 @@ EXPORTS = ["csa_compress_kv", "csa_mxfp4_quantize", "csa_indexer_scores", "csa_i
            "csa_sparse_attn_batch_invariant", "hca_dense_attn_batch_invariant", "csa_kv_cache_append",
            "csa_mxfp4_quantize_appended", "csa_sparse_attn_varlen", "hca_dense_attn_varlen",
            "csa_indexer_key_append", "csa_sparse_attn_noalloc", "csa_compress_kv_varlen",
-           "csa_indexer_topk_varlen", "csa_workspace_size",
+           "csa_indexer_topk_varlen", "csa_decode_append", "csa_workspace_size",
            "csa_status_str", "csa_abi_version"]
 
 _lib = None
@@ -79,6 +79,8 @@ def load(path=LIB_PATH):
     lib.hca_dense_attn_varlen.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _I, _P, _P,
                                           _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _S, _P]
     lib.csa_indexer_key_append.argtypes = [_P, _P, _I, _P, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P]
+    lib.csa_decode_append.argtypes = [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P,
+                                      _P, _P, _I, _P, _P, _P, _P, _P]
     lib.csa_sparse_attn_noalloc.argtypes = [_P, _I, _P, _P, _P, _P, _I, _I, _P, _I, _P, _P, _P, _I, _P, _I,
                                             _I, _I, _I, _I, _F, _P, _P, _P]
     lib.csa_compress_kv_varlen.argtypes = [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P, _P, _P, _I,
@@ -456,6 +458,27 @@ def hca_dense_attn_varlen(q, ck, cv, m_prime, k_win, v_win, raw_pos0, cu_rows, q
     return _varlen("hca_dense_attn_varlen", CSA_OP_DENSE_ATTN_VARLEN, q, ck, cv, (m_prime,), ck.shape[1] + W,
                    k_win, v_win, raw_pos0, cu_rows, q_pos0, W, ck_scale, cv_scale, sm_scale, invariant, out, lse,
                    stream)
+
+
+def csa_decode_append(k_new, v_new, z_new, ki_new, zi_new, pos, k_ring, v_ring, z_ring, m, ck, cv,
+                      ki_ring, zi_ring, codes, e8m0, ck_scale=None, cv_scale=None, raw_pos0=None, stream=None):
+    """Both appends of a CSA layer's decode token in one launch: exactly csa_kv_cache_append
+    (k_new, v_new, z_new into the K/V ring and cache ck, cv) followed by csa_indexer_key_append
+    (ki_new, zi_new into the indexer ring ki_ring, zi_ring and the MXFP4 keys codes, e8m0).
+    Returns raw_pos0 [B] int32."""
+    B, d = k_new.shape
+    L2, Li2 = k_ring.shape[1], ki_ring.shape[1]
+    if L2 % 2 or Li2 % 2:
+        raise ValueError("a ring holds 2 * L_ring rows per sequence")
+    if raw_pos0 is None:
+        raw_pos0 = torch.empty(B, dtype=torch.int32, device=k_new.device)
+    st = load().csa_decode_append(_ptr(k_new), _ptr(v_new), _ptr(z_new), _ptr(ki_new), _ptr(zi_new),
+                                  _dt_of(k_new), _ptr(pos), B, d, m, ck.shape[1], L2 // 2, _ptr(k_ring),
+                                  _ptr(v_ring), _ptr(z_ring), _dt_of(ck), _ptr(ck), _ptr(cv), _ptr(ck_scale),
+                                  _ptr(cv_scale), _ptr(raw_pos0), Li2 // 2, _ptr(ki_ring), _ptr(zi_ring),
+                                  _ptr(codes), _ptr(e8m0), _stream(stream))
+    _check("csa_decode_append", st)
+    return raw_pos0
 
 
 def csa_indexer_key_append(k_new, z_new, pos, k_ring, z_ring, m, codes, e8m0, stream=None):

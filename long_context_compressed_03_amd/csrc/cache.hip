@@ -32,15 +32,30 @@ using namespace csa_cmp;
 // pools its K side (the same operations in the same order, newest row from
 // the input), and stores the pooled fp32 entry in MXFP4: lane c holds
 // columns [8c, 8c + 8), so a 32-column block is 4 adjacent lanes.
+struct IxAppendArgs {
+  const void* k_new;
+  const float* z_new;
+  const int32_t* pos;
+  int B, L, m, cap;
+  void* k_ring;
+  float* z_ring;
+  uint8_t* codes;
+  uint8_t* e8m0;
+};
+
 template <int kInF32>
-__global__ __launch_bounds__(64) void indexer_key_append_kernel(const void* __restrict__ k_new,
-                                                               const float* __restrict__ z_new,
-                                                               const int32_t* __restrict__ pos, int B, int L, int m,
-                                                               int cap, void* k_ring, float* z_ring, uint8_t* codes,
-                                                               uint8_t* e8m0) {
+CSA_DEV void indexer_key_append_at(const IxAppendArgs& x, int blk) {
+  const void* __restrict__ k_new = x.k_new;
+  const float* __restrict__ z_new = x.z_new;
+  const int32_t* __restrict__ pos = x.pos;
+  const int B = x.B, L = x.L, m = x.m, cap = x.cap;
+  void* k_ring = x.k_ring;
+  float* z_ring = x.z_ring;
+  uint8_t* codes = x.codes;
+  uint8_t* e8m0 = x.e8m0;
   const int lane_c = threadIdx.x & (kGroup - 1);
-  const int b = int(blockIdx.x) * int(blockDim.x / kGroup) + int(threadIdx.x / kGroup);
-  if (b >= B) return;                      // whole 16-lane groups exit together
+  const int b = blk * 4 + int(threadIdx.x / kGroup);
+  if (b >= B) return;                      // whole 16-lane groups leave together
   const int p = pos[b];
   const AppendPlan pl = append_plan(p, L, m, cap);
   constexpr int kEl = kInF32 ? 4 : 2;
@@ -123,6 +138,35 @@ __global__ __launch_bounds__(64) void indexer_key_append_kernel(const void* __re
   if ((lane_c & 3) == 0) e8m0[entry * (kHeadDim / 32) + (lane_c >> 2)] = uint8_t(X + 127);
 }
 
+template <int kInF32>
+__global__ __launch_bounds__(64) void indexer_key_append_kernel(IxAppendArgs x) {
+  indexer_key_append_at<kInF32>(x, int(blockIdx.x));
+}
+
+// Both appends of a CSA layer's decode token in one launch: blocks [0, nb)
+// take the K/V append (cache_append_short_at), blocks [nb, 2 nb) the indexer
+// key append, each on its own rings and caches (nothing one writes is read
+// by the other), with the same code as the two separate calls.
+template <int kInF32, int kOut>
+__global__ __launch_bounds__(64) void decode_append_kernel(AppendArgs a, IxAppendArgs x, int nb) {
+  if (int(blockIdx.x) < nb)
+    cache_append_short_at<kInF32, kOut>(a, int(blockIdx.x));
+  else
+    indexer_key_append_at<kInF32>(x, int(blockIdx.x) - nb);
+}
+
+template <int kInF32>
+hipError_t launch_decode_append(int ckv_dtype, const AppendArgs& a, const IxAppendArgs& x, hipStream_t st) {
+  const int nb = (a.B + 3) / 4;
+  const dim3 grid(unsigned(2 * nb));
+  switch (ckv_dtype) {
+    case CSA_BF16: hipLaunchKernelGGL((decode_append_kernel<kInF32, CSA_BF16>), grid, dim3(64), 0, st, a, x, nb); break;
+    case CSA_F32: hipLaunchKernelGGL((decode_append_kernel<kInF32, CSA_F32>), grid, dim3(64), 0, st, a, x, nb); break;
+    default: hipLaunchKernelGGL((decode_append_kernel<kInF32, CSA_FP8_E4M3>), grid, dim3(64), 0, st, a, x, nb);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t csa_kv_append_workspace_size(int) { return 0; }
@@ -137,15 +181,13 @@ extern "C" csa_status_t csa_indexer_key_append(const void* k_new, const float* z
   if (m >= 32) return CSA_ENOTSUP;
   if (long(B) * 2 * L_ring > 0x7FFFFFFFL) return CSA_ENOTSUP;
   if (B == 0) return CSA_OK;
-  constexpr int kPer = 64 / csa_cmp::kGroup;
-  const dim3 grid(unsigned((B + kPer - 1) / kPer));
+  const dim3 grid(unsigned((B + 3) / 4));
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const IxAppendArgs x{k_new, z_new, pos, B, L_ring, m, cap, k_ring, z_ring, codes, e8m0};
   if (io_dtype == CSA_F32)
-    hipLaunchKernelGGL(indexer_key_append_kernel<1>, grid, dim3(64), 0, st, k_new, z_new, pos, B, L_ring, m, cap,
-                       k_ring, z_ring, codes, e8m0);
+    hipLaunchKernelGGL(indexer_key_append_kernel<1>, grid, dim3(64), 0, st, x);
   else
-    hipLaunchKernelGGL(indexer_key_append_kernel<0>, grid, dim3(64), 0, st, k_new, z_new, pos, B, L_ring, m, cap,
-                       k_ring, z_ring, codes, e8m0);
+    hipLaunchKernelGGL(indexer_key_append_kernel<0>, grid, dim3(64), 0, st, x);
   return hipGetLastError() == hipSuccess ? CSA_OK : CSA_EHIP;
 }
 
@@ -167,5 +209,31 @@ extern "C" csa_status_t csa_kv_cache_append(const void* k_new, const void* v_new
   const csa_cmp::AppendArgs a{k_new, v_new, z_new, pos, k_ring, v_ring, z_ring, raw_pos0, B, L_ring, m, cap,
                               ck, cv, ck_scale, cv_scale};
   const hipError_t e = csa_cmp::launch_cache_append(io_dtype, ckv_dtype, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CSA_OK : CSA_EHIP;
+}
+
+extern "C" csa_status_t csa_decode_append(const void* k_new, const void* v_new, const float* z_new,
+                                          const void* ki_new, const float* zi_new, int32_t io_dtype,
+                                          const int32_t* pos, int32_t B, int32_t d, int32_t m, int32_t cap,
+                                          int32_t L_ring, void* k_ring, void* v_ring, float* z_ring,
+                                          int32_t ckv_dtype, void* ck, void* cv, float* ck_scale, float* cv_scale,
+                                          int32_t* raw_pos0, int32_t Li_ring, void* ki_ring, float* zi_ring,
+                                          uint8_t* codes, uint8_t* e8m0, void* stream) {
+  if (!k_new || !v_new || !z_new || !ki_new || !zi_new || !pos || !k_ring || !v_ring || !z_ring || !ck || !cv ||
+      !raw_pos0 || !ki_ring || !zi_ring || !codes || !e8m0)
+    return CSA_EINVAL;
+  if (io_dtype != CSA_BF16 && io_dtype != CSA_F32) return CSA_EINVAL;
+  if (!csa_dtype_ok(ckv_dtype)) return CSA_EINVAL;
+  if (ckv_dtype == CSA_FP8_E4M3 && (!ck_scale || !cv_scale)) return CSA_EINVAL;
+  if (d != kHeadDim || B < 0 || m < 1 || cap < 0 || L_ring < m || Li_ring < m) return CSA_EINVAL;
+  if (m >= 32) return CSA_ENOTSUP;
+  if (long(B) * 2 * L_ring > 0x7FFFFFFFL || long(B) * 2 * Li_ring > 0x7FFFFFFFL) return CSA_ENOTSUP;
+  if (B == 0) return CSA_OK;
+  const csa_cmp::AppendArgs a{k_new, v_new, z_new, pos, k_ring, v_ring, z_ring, raw_pos0, B, L_ring, m, cap,
+                              ck, cv, ck_scale, cv_scale};
+  const IxAppendArgs x{ki_new, zi_new, pos, B, Li_ring, m, cap, ki_ring, zi_ring, codes, e8m0};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = io_dtype == CSA_F32 ? launch_decode_append<1>(ckv_dtype, a, x, st)
+                                           : launch_decode_append<0>(ckv_dtype, a, x, st);
   return e == hipSuccess ? CSA_OK : CSA_EHIP;
 }

@@ -218,6 +218,45 @@ CSA_DEV AppendPlan append_plan(int p, int L, int m, int cap) {
 
 hipError_t launch_cache_append(int io_dtype, int ckv_dtype, const AppendArgs& a, hipStream_t st);
 
+// Cache append, short blocks (m < 32), for block `blk` of 64 threads:
+// 16-lane group g serves sequence 4 * blk + g.  It writes the token's K/V rows
+// (both ring copies; lane c its 8 columns) and logit, the window base, and
+// pools the block the token completes with its newest row read from the input
+// (the ring rows it reads hold older tokens, never the two rows being written).
+template <int kInF32, int kOut>
+CSA_DEV void cache_append_short_at(const AppendArgs& a, int blk) {
+  const int lane_c = threadIdx.x & (kGroup - 1);
+  const int b = blk * 4 + int(threadIdx.x / kGroup);
+  if (b >= a.B) return;                    // whole 16-lane groups leave together
+  const int p = a.pos[b];
+  const AppendPlan pl = append_plan(p, a.L, a.m, a.cap);
+  constexpr int kEl = kInF32 ? 4 : 2;
+  constexpr int kLaneBytes = kColsPerLane * kEl;
+  const size_t ring0 = size_t(b) * 2 * a.L;
+  const uint8_t* kn = static_cast<const uint8_t*>(a.k_new) + size_t(b) * kHeadDim * kEl;
+  const uint8_t* vn = static_cast<const uint8_t*>(a.v_new) + size_t(b) * kHeadDim * kEl;
+  if (p >= 0) {
+    const int s = p % a.L;
+#pragma unroll
+    for (int h = 0; h < kLaneBytes / 16; ++h) {
+      const uint4 xk = *reinterpret_cast<const uint4*>(kn + lane_c * kLaneBytes + h * 16);
+      const uint4 xv = *reinterpret_cast<const uint4*>(vn + lane_c * kLaneBytes + h * 16);
+#pragma unroll
+      for (int copy = 0; copy < 2; ++copy) {
+        const size_t off = (ring0 + s + size_t(copy) * a.L) * kHeadDim * kEl + lane_c * kLaneBytes + h * 16;
+        *reinterpret_cast<uint4*>(static_cast<uint8_t*>(a.k_ring) + off) = xk;
+        *reinterpret_cast<uint4*>(static_cast<uint8_t*>(a.v_ring) + off) = xv;
+      }
+    }
+    if (lane_c < 2) a.z_ring[ring0 + s + size_t(lane_c) * a.L] = a.z_new[b];
+  }
+  if (lane_c == 0) a.raw_pos0[b] = pl.base;
+  if (!pl.done) return;
+  compress_group_at<kInF32, kOut, true>(a.k_ring, a.v_ring, a.z_ring, ring0 + pl.first_row, a.m, a.ck, a.cv,
+                                        a.ck_scale, a.cv_scale, size_t(b) * a.cap + pl.entry, lane_c, kn, vn,
+                                        a.z_new + b);
+}
+
 // The arguments of one compression call.
 struct CompressArgs {
   const void* k;

@@ -241,6 +241,19 @@ def test_cache_varlen_and_appended_quantize_reject_bad_arguments():
     assert ixapp(io=2) == csa.CSA_EINVAL
     assert ixapp(codes=None) == csa.CSA_EINVAL
 
+    def both(d=128, L=8, Li=8, m=4, io=0, ckv=0, scales=None, ki=_p(), codes=_p(), raw=_p()):
+        return lib.csa_decode_append(_p(), _p(), _p(), ki, _p(), io, _p(), 2, d, m, 16, L, _p(), _p(), _p(), ckv,
+                                     _p(), _p(), scales, scales, raw, Li, _p(), _p(), codes, _p(), None)
+    assert both(d=64) == csa.CSA_EINVAL
+    assert both(m=16) == csa.CSA_EINVAL               # the block is longer than the K/V ring
+    assert both(Li=2) == csa.CSA_EINVAL               # ... or than the indexer ring
+    assert both(m=32, L=64, Li=64) == csa.CSA_ENOTSUP
+    assert both(io=2) == csa.CSA_EINVAL
+    assert both(ckv=2) == csa.CSA_EINVAL              # fp8 entries without scales
+    assert both(ki=None) == csa.CSA_EINVAL
+    assert both(codes=None) == csa.CSA_EINVAL
+    assert both(raw=None) == csa.CSA_EINVAL
+
     def quant(dt=0, d=128, m=4, pos=_p()):
         return lib.csa_mxfp4_quantize_appended(_p(), dt, pos, 2, 16, m, d, _p(), _p(), None)
     assert quant(dt=2) == csa.CSA_EINVAL

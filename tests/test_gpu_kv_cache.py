@@ -283,6 +283,62 @@ def _mxfp4_agree_but_at_boundaries(x, eps, g_codes, g_e8m0):
     return n_cmp, n_bnd
 
 
+@pytest.mark.parametrize("ckv", ["fp8", "bf16"])
+def test_decode_append_equals_the_two_calls(csa, ckv):
+    """csa_decode_append (both appends of a CSA layer's token in one launch) against
+    csa_kv_cache_append followed by csa_indexer_key_append on buffers of their own: rings,
+    logits, compressed entries and scales, MXFP4 codes and scales, and window bases bit for bit
+    after every step, with one sequence idling at times and B not a multiple of 4."""
+    B, m, L, Li, cap, steps = 7, 4, 32, 16, 64, 70
+    starts = [0, 3, 9, 40, 100, 1, 61]
+    say(f"decode append (one launch) vs the two calls: ckv={ckv} B={B} m={m} L={L} Li={Li} steps={steps}")
+    n_total = max(starts) + steps + 1
+    x = compress_inputs(B, n_total, "bf16", seed=81, outliers=True)
+    xi = compress_inputs(B, n_total, "bf16", seed=82)
+    K, V, Z = t_kv(x["K"], "bf16"), t_kv(x["V"], "bf16"), t_f32(x["logits"])
+    Ki, Zi = t_kv(xi["K"], "bf16"), t_f32(xi["logits"])
+    cdt = torch.uint8 if ckv == "fp8" else torch.bfloat16
+
+    def state():
+        return dict(rk=torch.zeros((B, 2 * L, 128), dtype=torch.bfloat16, device="cuda"),
+                    rv=torch.zeros((B, 2 * L, 128), dtype=torch.bfloat16, device="cuda"),
+                    rz=torch.zeros((B, 2 * L), device="cuda"),
+                    ck=torch.zeros((B, cap, 128), dtype=cdt, device="cuda"),
+                    cv=torch.zeros((B, cap, 128), dtype=cdt, device="cuda"),
+                    cks=torch.ones((B, cap), device="cuda"), cvs=torch.ones((B, cap), device="cuda"),
+                    raw=torch.full((B,), -7, dtype=torch.int32, device="cuda"),
+                    irk=torch.zeros((B, 2 * Li, 128), dtype=torch.bfloat16, device="cuda"),
+                    irz=torch.zeros((B, 2 * Li), device="cuda"),
+                    codes=torch.full((B, cap, 64), 0xAB, dtype=torch.uint8, device="cuda"),
+                    e8=torch.full((B, cap, 4), 0xAB, dtype=torch.uint8, device="cuda"))
+    one, two = state(), state()
+    scales = (lambda s: dict(ck_scale=s["cks"], cv_scale=s["cvs"])) if ckv == "fp8" else (lambda s: {})
+    ar = torch.arange(B, device="cuda")
+    nxt = np.array(starts, np.int64)
+    for step in range(steps):
+        active = np.array([not (b == 2 and step % 3 == 1) for b in range(B)])
+        pos = np.where(active, nxt, -1).astype(np.int32)
+        pd = t_i32(pos)
+        src = pd.long().clamp(min=0)
+        kn, vn, zn = K[ar, src].contiguous(), V[ar, src].contiguous(), Z[ar, src].contiguous()
+        kin, zin = Ki[ar, src].contiguous(), Zi[ar, src].contiguous()
+        csa.csa_decode_append(kn, vn, zn, kin, zin, pd, one["rk"], one["rv"], one["rz"], m, one["ck"], one["cv"],
+                              one["irk"], one["irz"], one["codes"], one["e8"], raw_pos0=one["raw"], **scales(one))
+        csa.csa_kv_cache_append(kn, vn, zn, pd, two["rk"], two["rv"], two["rz"], m, two["ck"], two["cv"],
+                                raw_pos0=two["raw"], **scales(two))
+        csa.csa_indexer_key_append(kin, zin, pd, two["irk"], two["irz"], m, two["codes"], two["e8"])
+        torch.cuda.synchronize()
+        for name in one:
+            a_, b_ = one[name], two[name]
+            if a_.dtype == torch.bfloat16:
+                a_, b_ = a_.view(torch.int16), b_.view(torch.int16)
+            elif a_.dtype == torch.float32:
+                a_, b_ = a_.view(torch.int32), b_.view(torch.int32)
+            assert torch.equal(a_, b_), (step, name)
+        nxt += active
+    assert int((h(one["e8"]) != 0xAB).sum()) > 0     # entries were completed and converted
+
+
 def test_cache_append_rejects_bad_arguments(csa):
     say("kv cache append: argument errors")
     lib = csa.load()
