@@ -58,8 +58,9 @@ def test_rows_ignore_the_batch(csa, H_I, d_I, cap, T, P, k):
     sel_whole = h(csa.csa_indexer_topk(*_dev(x), t_i32(pos), m, k))
     torch.cuda.synchronize()
     nv = np.minimum((P + np.arange(T) + 1) // m, cap)
-    assert not np.array_equal(whole[0, 0, :nv[0]].astype(np.float64),
-                              whole[0, 0, :nv[0]].astype(np.float16).astype(np.float64))   # a real spread
+    with np.errstate(over="ignore"):   # scores beyond fp16's range become inf: still unequal
+        assert not np.array_equal(whole[0, 0, :nv[0]].astype(np.float64),
+                                  whole[0, 0, :nv[0]].astype(np.float16).astype(np.float64))   # a real spread
 
     def same_scores(got, rows):
         for gi, i in enumerate(rows):
