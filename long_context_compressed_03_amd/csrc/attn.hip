@@ -1102,8 +1102,8 @@ void attn_decode_kernel(AttnArgs a, int kT, int n_groups, long n_units) {
 // from LDS.  Each key takes part exactly as in the one-query kernel, so the
 // arithmetic per (query, head) is the same online softmax over 64-key chunks.
 struct LdsMQ {
-  LdsBf16 c;
-  uint32_t vis[kNK];   // bit q: the key is visible to the block's query q
+  LdsBf16 c[2];           // two chunk buffers: one computed while the next is stored
+  uint32_t vis[2][kNK];   // bit q: the key is visible to the block's query q
   // each wave's query fragments (2 head tiles x 4 contraction steps, one
   // 16-byte word per lane), re-read for every chunk instead of held in
   // registers through the P*V products
@@ -1273,9 +1273,8 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
   // query is the earliest): they are gathered without source selects and
   // scored without visibility masks.  The rest (the last entries, the
   // window) take the general path.
-  // (rounded down to whole pairs of chunks, as the walk takes them).
   const int nv_all = min((t0 + 1) / a.k, a.cap);
-  const int j_full = j_lo + max(0, min(nv_all, j_hi) - j_lo) / (2 * kNK) * (2 * kNK);
+  const int j_full = j_lo + max(0, min(nv_all, j_hi) - j_lo) / kNK * kNK;
   const long row_b = long(b) * a.cap;
   auto fetch = [&](Pre<CSA_BF16>& prc, uint32_t (&tgc)[2], int jc) {
     if (jc < j_full)
@@ -1283,23 +1282,24 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
     else
       prefetch_mq<kCKV>(a, prc, tgc, b, raw0, nv_max, p_lo, n_list, jc, t0, n_q);
   };
-
-  // two chunks in flight: chunk c is stored from one register set while
-  // chunk c + 1 is still loading into the other
-  Pre<CSA_BF16> pr[2];
-  uint32_t tag[2][2];
-  if (j_lo < j_hi) fetch(pr[0], tag[0], j_lo);
-  if (j_lo + kNK < j_hi) fetch(pr[1], tag[1], j_lo + kNK);
-  auto step = [&](auto all_t, Pre<CSA_BF16>& prc, uint32_t (&tgc)[2], int j0) {
+  // Pipeline: while chunk c is computed from LDS buffer c % 2, chunk c + 1
+  // (loaded into registers during chunk c - 1) is stored into the other
+  // buffer and chunk c + 2 loads into the registers; one barrier per chunk
+  // separates the computing of chunk c from the overwriting of its buffer
+  // and publishes chunk c + 1.
+  Pre<CSA_BF16> pr;
+  uint32_t tag[2];
+  auto store = [&](auto all_t, int buf) {
     constexpr bool kAll = decltype(all_t)::value;
-    __syncthreads();
-    store_chunk<CSA_BF16, kCKV, kAll>(s.c, prc, a.sm_log2);
+    store_chunk<CSA_BF16, kCKV, kAll>(s.c[buf], pr, a.sm_log2);
     if (!kAll && item_dg() == 0) {
-      s.vis[2 * item_kp()] = tgc[0];
-      s.vis[2 * item_kp() + 1] = tgc[1];
+      s.vis[buf][2 * item_kp()] = tag[0];
+      s.vis[buf][2 * item_kp() + 1] = tag[1];
     }
-    __syncthreads();
-    if (j0 + 2 * kNK < j_hi) fetch(prc, tgc, j0 + 2 * kNK);
+  };
+  auto compute = [&](auto all_t, int buf) {
+    constexpr bool kAll = decltype(all_t)::value;
+    const LdsBf16& c = s.c[buf];
     // S^T for the 4 key tiles x 2 head tiles; K fragments shared by both tiles,
     // contraction steps outermost so only one step's query fragments are live
     float x[2][4][4];
@@ -1314,11 +1314,12 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
       for (int kt = 0; kt < 4; ++kt) acc[kt][0] = acc[kt][1] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
+        // one contraction step's fragments requested together, then its 8 products
         const u32x4 q0 = s.q[wid][0][ks][lane];
         const u32x4 q1 = s.q[wid][1][ks][lane];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(&s.c.K[kt * 16 + col][ks * 32 + g * 8]);
+          const u32x4 kf = *reinterpret_cast<const u32x4*>(&c.K[kt * 16 + col][ks * 32 + g * 8]);
           acc[kt][0] = mfma_k32(kf, q0, acc[kt][0]);
           acc[kt][1] = mfma_k32(kf, q1, acc[kt][1]);
         }
@@ -1326,14 +1327,14 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         // keys kt*16 + 4g .. +3 (16-byte reads)
-        const v4f scl = *reinterpret_cast<const v4f*>(&s.c.sk[kt * 16 + 4 * g]);
+        const v4f scl = *reinterpret_cast<const v4f*>(&c.sk[kt * 16 + 4 * g]);
         if constexpr (kAll) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int ht = 0; ht < 2; ++ht) x[ht][kt][r] = __builtin_fmaf(acc[kt][ht][r], scl[r], -mu[ht]);
         } else {
-          const u32x4 vb = *reinterpret_cast<const u32x4*>(&s.vis[kt * 16 + 4 * g]);
+          const u32x4 vb = *reinterpret_cast<const u32x4*>(&s.vis[buf][kt * 16 + 4 * g]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const bool seen = (vb[r] >> qi) & 1u;
@@ -1351,7 +1352,7 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
     // V scales of the chunk's keys (kt*16 + 4g .. +3), over vref
     v4f svk[4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) svk[kt] = *reinterpret_cast<const v4f*>(&s.c.sv[kt * 16 + 4 * g]);
+    for (int kt = 0; kt < 4; ++kt) svk[kt] = *reinterpret_cast<const v4f*>(&c.sv[kt * 16 + 4 * g]);
     if constexpr (kCKV == CSA_FP8_E4M3) {
       float smax = 0.f;
 #pragma unroll
@@ -1440,7 +1441,7 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
       const u32x4 pl1 = {pl[1][st][0], pl[1][st][1], pl[1][st][2], pl[1][st][3]};
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const uint16_t* vt = &s.c.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0];   // row dt*16 + col
+        const uint16_t* vt = &c.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0];   // row dt*16 + col
         const u32x2 lo = *reinterpret_cast<const u32x2*>(vt);
         const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + 16);
         const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
@@ -1458,14 +1459,43 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
   };
   const std::true_type all_entries;
   const std::false_type general;
-  int j0 = j_lo;
-  for (; j0 < j_full; j0 += 2 * kNK) {
-    step(all_entries, pr[0], tag[0], j0);
-    step(all_entries, pr[1], tag[1], j0 + kNK);
+  // A chunk is stored and computed in the same form (all-entries chunks hold
+  // fp16 V^T for fp8 entries), and each form of a step sits in a loop of its
+  // own: the walk over all-entries chunks, the one step where the next chunk
+  // is general, then the general chunks.
+  int buf = 0;
+  if (j_lo < j_hi) {
+    fetch(pr, tag, j_lo);
+    if (j_lo < j_full) store(all_entries, 0); else store(general, 0);
+    if (j_lo + kNK < j_hi) fetch(pr, tag, j_lo + kNK);
   }
-  for (; j0 < j_hi; j0 += 2 * kNK) {
-    step(general, pr[0], tag[0], j0);
-    if (j0 + kNK < j_hi) step(general, pr[1], tag[1], j0 + kNK);
+  __syncthreads();
+  int j0 = j_lo;
+  for (; j0 + kNK < j_full; j0 += kNK) {
+    store(all_entries, buf ^ 1);
+    if (j0 + 2 * kNK < j_hi) fetch(pr, tag, j0 + 2 * kNK);
+    compute(all_entries, buf);
+    __syncthreads();
+    buf ^= 1;
+  }
+  if (j0 < j_full) {
+    if (j0 + kNK < j_hi) {
+      store(general, buf ^ 1);
+      if (j0 + 2 * kNK < j_hi) fetch(pr, tag, j0 + 2 * kNK);
+    }
+    compute(all_entries, buf);
+    __syncthreads();
+    buf ^= 1;
+    j0 += kNK;
+  }
+  for (; j0 < j_hi; j0 += kNK) {
+    if (j0 + kNK < j_hi) {
+      store(general, buf ^ 1);
+      if (j0 + 2 * kNK < j_hi) fetch(pr, tag, j0 + 2 * kNK);
+    }
+    compute(general, buf);
+    __syncthreads();
+    buf ^= 1;
   }
   if (!q_ok) return;
   if constexpr (kCKV == CSA_FP8_E4M3) {

@@ -40,6 +40,11 @@ constexpr int kSampleGroup = 1024;
 CSA_DEV_HOST_INLINE int sampled_count(int n) {   // sampled entries below n
   return (n / kSampleGroup) * 16 + (n % kSampleGroup < 16 ? n % kSampleGroup : 16);
 }
+// Entries a wave walks in the batched (non-streaming) launches, about.
+#ifndef CSA_IX_WAVE_ENTRIES
+#define CSA_IX_WAVE_ENTRIES 1024
+#endif
+constexpr int kWaveEntries = CSA_IX_WAVE_ENTRIES;
 // Candidate slots per row of the threshold pass, and per (block, row) in LDS.
 constexpr int kCandCap = 8192;
 constexpr int kBlockCand = 128;
@@ -49,11 +54,13 @@ constexpr int kBlockCand = 128;
 //   thr    (kCand) per row: the 32-bit order-preserving key a candidate reaches
 //   cnt    (kCand) per row: candidates found (atomic; past kCandCap: overflow)
 //   cand   (kCand) per row: kCandCap (key, entry) pairs, in no particular order
+//   wave_entries  (batched launches) about how many entries a wave walks; 0: kWaveEntries
 struct IxExtra {
   const uint32_t* gate;
   const uint32_t* thr;
   uint32_t* cnt;
   uint2* cand;
+  int wave_entries;
 };
 
 // A block's candidates of its rows, staged in LDS before one global
@@ -304,7 +311,16 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
         if (vis && p >= thr[rt]) {
           const int lr = q_of(rt, 4 * g);   // the query's slot among the block's rows
           const uint32_t slot = atomicAdd(&cl.n[lr], 1u);
-          if (slot < uint32_t(kBlockCand)) cl.item[lr][slot] = make_uint2(csa_sel::ordered_key(p), uint32_t(e));
+          const uint2 item = make_uint2(csa_sel::ordered_key(p), uint32_t(e));
+          if (slot < uint32_t(kBlockCand)) {
+            cl.item[lr][slot] = item;
+          } else {
+            // the (block, row) staging is full: this pair takes a slot of
+            // the row's list directly (past kCandCap the row overflows)
+            const size_t row = row_base + size_t(q_block + lr);
+            const uint32_t gs = atomicAdd(&x.cnt[row], 1u);
+            if (gs < uint32_t(kCandCap)) x.cand[row * size_t(kCandCap) + gs] = item;
+          }
         }
       } else {
         static_cast<uint16_t*>(out)[orow[rt] + e] = vis ? uint16_t(csa_sel::ordered_key(p) >> 16) : uint16_t(0);
@@ -348,10 +364,11 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
     if constexpr (kHM) {
       // each lane: the whole score of query (rt / kGrp) * 4 + g at entry
       // e_frag0 + 16 f + col, one per (fragment, query group)
+      constexpr int kQG = kRT / kGrp;
 #pragma unroll
       for (int f = 0; f < kFrag; ++f)
 #pragma unroll
-        for (int gi = 0; gi < kRT / kGrp; ++gi) {
+        for (int gi = 0; gi < kQG; ++gi) {
           float part[kGrp];
 #pragma unroll
           for (int hq = 0; hq < kGrp; ++hq) {
@@ -371,7 +388,9 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
           const int e = e_frag0 + f * 16 + col;
           if constexpr (kOut == kCand) {
             // the wave takes the append path only when one of its lanes has a
-            // candidate here (rare); put re-checks everything
+            // candidate here (rare); put re-checks everything.  (One test per
+            // batch instead keeps every score of the batch live at once: 156
+            // VGPRs, one wave fewer per SIMD, measured slower.)
             if (__ballot(p >= thr[rt])) put(rt, e, p);
           } else {
             put(rt, e, p);
@@ -413,16 +432,15 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
     }
   }
   if constexpr (kOut == kCand) {
-    // one reservation per (block, row), then the staged pairs copied out; a
-    // (block, row) whose staging overflowed pushes the row's count past the
-    // capacity, so the selection sees the overflow
+    // one reservation per (block, row), then the staged pairs copied out
+    // (pairs past the staging took their slots one by one); a row whose
+    // count passes kCandCap overflows, and the selection sees it
     __syncthreads();
     if (int(threadIdx.x) < kRowsPerBlock) {
       const int q = q_block + int(threadIdx.x);
       const uint32_t n = cl.n[threadIdx.x];
       uint32_t base = 0u;
-      if (q < T_q && n > 0u)
-        base = atomicAdd(&x.cnt[row_base + q], n > uint32_t(kBlockCand) ? uint32_t(kCandCap) + 1u : n);
+      if (q < T_q && n > 0u) base = atomicAdd(&x.cnt[row_base + q], min(n, uint32_t(kBlockCand)));
       cl.n[32 + threadIdx.x] = base;
     }
     __syncthreads();
@@ -446,9 +464,21 @@ hipError_t launch_indexer_ks(const uint8_t* qc, const uint8_t* qe, const float* 
                              void* out, hipStream_t st, const int32_t* cu_rows, int n_rows, const IxExtra& x) {
   constexpr int kFrag = 4;
   constexpr int kQPT = 16 / kHI;
-  const int entries_per_wave = kStream ? 16 * kFrag : 256;   // streaming: one batch per wave
-  const int per_block = entries_per_wave * kWavesPerBlock;
   const int ecap = kOut == kSample ? sampled_count(cap) : cap;
+  // streaming: one batch per wave.  Otherwise a wave walks about
+  // kWaveEntries entries (its block's set-up -- query fragments, weights,
+  // thresholds, the candidate reservation -- is paid once per walk), the
+  // walk length chosen so the entry blocks come to a whole number of rounds
+  // over the 8 XCDs (a function of the shape only)
+  int entries_per_wave = 16 * kFrag;
+  if constexpr (!kStream) {
+    const int target = x.wave_entries > 0 ? x.wave_entries : kWaveEntries;
+    const int per_xcd_round = 8 * kWavesPerBlock;   // waves in one entry block per XCD
+    const int rounds = max(1, (ecap + per_xcd_round * target - 1) / (per_xcd_round * target));
+    const int step = 16 * kFrag;                     // one batch
+    entries_per_wave = ((ecap + per_xcd_round * rounds - 1) / (per_xcd_round * rounds) + step - 1) / step * step;
+  }
+  const int per_block = entries_per_wave * kWavesPerBlock;
   const size_t lds = kOut == kCand ? sizeof(CandLds) : 0;
   if (lds) {
     if (hipError_t e = csa_lds_opt_in(
