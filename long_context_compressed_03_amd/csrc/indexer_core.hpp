@@ -42,7 +42,7 @@ CSA_DEV_HOST_INLINE int sampled_count(int n) {   // sampled entries below n
 }
 // Entries a wave walks in the batched (non-streaming) launches, about.
 #ifndef CSA_IX_WAVE_ENTRIES
-#define CSA_IX_WAVE_ENTRIES 1024
+#define CSA_IX_WAVE_ENTRIES 2048
 #endif
 constexpr int kWaveEntries = CSA_IX_WAVE_ENTRIES;
 // Candidate slots per row of the threshold pass, and per (block, row) in LDS.
