@@ -47,7 +47,7 @@ CSA_DEV_HOST_INLINE int sampled_count(int n) {   // sampled entries below n
 constexpr int kWaveEntries = CSA_IX_WAVE_ENTRIES;
 // Candidate slots per row of the threshold pass, and per (block, row) in LDS.
 constexpr int kCandCap = 8192;
-constexpr int kBlockCand = 128;
+constexpr int kBlockCand = 256;
 
 // Extra arguments of the selection passes of csa_indexer_topk.
 //   gate   (any mode) null, or a flag: the launch does nothing while it is 0
@@ -311,16 +311,7 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
         if (vis && p >= thr[rt]) {
           const int lr = q_of(rt, 4 * g);   // the query's slot among the block's rows
           const uint32_t slot = atomicAdd(&cl.n[lr], 1u);
-          const uint2 item = make_uint2(csa_sel::ordered_key(p), uint32_t(e));
-          if (slot < uint32_t(kBlockCand)) {
-            cl.item[lr][slot] = item;
-          } else {
-            // the (block, row) staging is full: this pair takes a slot of
-            // the row's list directly (past kCandCap the row overflows)
-            const size_t row = row_base + size_t(q_block + lr);
-            const uint32_t gs = atomicAdd(&x.cnt[row], 1u);
-            if (gs < uint32_t(kCandCap)) x.cand[row * size_t(kCandCap) + gs] = item;
-          }
+          if (slot < uint32_t(kBlockCand)) cl.item[lr][slot] = make_uint2(csa_sel::ordered_key(p), uint32_t(e));
         }
       } else {
         static_cast<uint16_t*>(out)[orow[rt] + e] = vis ? uint16_t(csa_sel::ordered_key(p) >> 16) : uint16_t(0);
@@ -432,15 +423,16 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
     }
   }
   if constexpr (kOut == kCand) {
-    // one reservation per (block, row), then the staged pairs copied out
-    // (pairs past the staging took their slots one by one); a row whose
-    // count passes kCandCap overflows, and the selection sees it
+    // one reservation per (block, row), then the staged pairs copied out; a
+    // (block, row) whose staging overflowed pushes the row's count past the
+    // capacity, so the selection sees the overflow
     __syncthreads();
     if (int(threadIdx.x) < kRowsPerBlock) {
       const int q = q_block + int(threadIdx.x);
       const uint32_t n = cl.n[threadIdx.x];
       uint32_t base = 0u;
-      if (q < T_q && n > 0u) base = atomicAdd(&x.cnt[row_base + q], min(n, uint32_t(kBlockCand)));
+      if (q < T_q && n > 0u)
+        base = atomicAdd(&x.cnt[row_base + q], n > uint32_t(kBlockCand) ? uint32_t(kCandCap) + 1u : n);
       cl.n[32 + threadIdx.x] = base;
     }
     __syncthreads();

@@ -1122,10 +1122,10 @@ hipError_t tile_path(int H_I, long rows, const uint8_t* q_codes, const uint8_t* 
     x.cnt = tw.cnt;
     x.cand = tw.cand;
     // a wave's walk sized so a (block, row) expects at most about 55 of its
-    // row's ~1.75 k candidates (staging holds kBlockCand = 128; past that a
-    // pair takes a slot of the row's list by a global atomic).  Measured on
-    // the 1M chunk (k = 1024 of 262656): walks of ~1000 entries 715 us,
-    // ~1700 entries 676 us, ~2700 entries 861 us; twice the staging, no change.
+    // row's ~1.75 k candidates (the staging holds kBlockCand = 256; a
+    // (block, row) past it sends the row to the fallback).  Measured on the
+    // 1M chunk (k = 1024 of 262656): walks of ~1000 entries 715 us, ~1700
+    // entries 676 us, ~2700 entries 861 us.
     x.wave_entries = max(256, min(csa_ix::kWaveEntries, int(8L * cap / k) / 64 * 64));
     err = csa_ix::launch_indexer<csa_ix::kCand>(H_I, q_codes, q_e8m0, w, k_codes, k_e8m0, q_pos0, B, T_q, d_I, cap,
                                                 m, nullptr, st, cu_rows, n_rows, x);
