@@ -161,6 +161,32 @@ CSA_DEV void load_b(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t re, uint32
   }
 }
 
+// The kFrag fragments of one batch of a wave's walk over consecutive entries
+// e .. e + 16 kFrag - 1 (lane column `col` adds to e; the caller passes
+// e = cap when there is no batch to load).  Offsets past the resource read
+// zeros, so no per-fragment selects: an entry at or past cap, and a lane
+// whose contraction block is absent (its lane offset is the resource size),
+// read zeros; entries between the block's visibility and cap are read and
+// their scores discarded.  Offsets stay below 2^32: cap * row_bytes < 2^31.
+template <int kKS, int kFrag>
+CSA_DEV void load_b_run(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t re, uint32_t e, const uint32_t (&oc)[kKS],
+                        const uint32_t (&oe)[kKS], int row_bytes, int nblk, u32x4 (&bk)[kFrag][kKS],
+                        int (&sb)[kFrag][kKS]) {
+  const uint32_t c0 = e * uint32_t(row_bytes), e0 = e * uint32_t(nblk);
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+    const uint32_t cb = c0 + oc[ks], eb = e0 + oe[ks];
+#pragma unroll
+    for (int f = 0; f < kFrag; ++f) {
+      // the fragment's distance goes into the range-checked vector offset
+      // (a buffer load's scalar offset is not range-checked)
+      bk[f][ks] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, cb + uint32_t(f * 16 * row_bytes), 0, 0));
+      sb[f][ks] = __builtin_amdgcn_raw_buffer_load_b8(re, eb + uint32_t(f * 16 * nblk), 0, 0);
+    }
+  }
+}
+
 // Row tile `tile` of a packed batch: sequence b's rows are cut into tiles of
 // `per` rows each, sequences in order; sets the tile's sequence and its first
 // row within it.  False past the last tile (the grid is a bound: at most
@@ -319,13 +345,32 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
     }
   };
 
-  // key fragments of the next batch load while the current one computes
+  // key fragments of the next batch load while the current one computes.
+  // Walks over consecutive entries (not the sample pass, not streaming) load
+  // a batch with load_b_run: per lane, the offsets of its contraction blocks
+  // (the resource size for a block past d_I).
+  constexpr bool kRun = !kStream && kOut != kSample;
+  uint32_t oc_lane[kKS], oe_lane[kKS];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+    const int c = ks * 4 + g;
+    oc_lane[ks] = c < nblk ? uint32_t(c) * 16u : c_bytes;
+    oe_lane[ks] = c < nblk ? uint32_t(c) : e_bytes;
+  }
+  auto run_entry = [&](int e0, bool any) {   // the lane's entry of a batch starting at e0, or cap
+    return any ? uint32_t(min(e0 + col, cap)) : uint32_t(cap);
+  };
   u32x4 bk[kFrag][kKS];
   int sb[kFrag][kKS];
+  if constexpr (kRun) {
+    load_b_run<kKS, kFrag>(rc, re, run_entry(e_wave0, e_wave0 < nv_max), oc_lane, oe_lane, row_bytes,
+                           nblk, bk, sb);
+  } else {
 #pragma unroll
-  for (int f = 0; f < kFrag; ++f) {
-    const int e = e_wave0 + f * 16 + col;
-    load_b<kKS, kStream>(rc, re, c_bytes, e_bytes, real_entry(e), e < nv_max, g, nblk, row_bytes, bk[f], sb[f]);
+    for (int f = 0; f < kFrag; ++f) {
+      const int e = e_wave0 + f * 16 + col;
+      load_b<kKS, kStream>(rc, re, c_bytes, e_bytes, real_entry(e), e < nv_max, g, nblk, row_bytes, bk[f], sb[f]);
+    }
   }
   // One batch: the keys of the batch after it load into (nk, ns) while this
   // one computes from (ck, cs); two buffers swap roles from batch to batch (no
@@ -333,11 +378,17 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
   auto batch = [&](auto& ck, auto& cs, auto& nk, auto& ns, int e_frag0, bool prefetch) {
     if (prefetch) {
       const bool more = e_frag0 + 16 * kFrag < e_wave1;
+      if constexpr (kRun) {
+        const int en = e_frag0 + 16 * kFrag;
+        load_b_run<kKS, kFrag>(rc, re, run_entry(en, more && en < nv_max), oc_lane, oe_lane, row_bytes,
+                               nblk, nk, ns);
+      } else {
 #pragma unroll
-      for (int f = 0; f < kFrag; ++f) {
-        const int e = e_frag0 + 16 * kFrag + f * 16 + col;
-        load_b<kKS, kStream>(rc, re, c_bytes, e_bytes, real_entry(e), more && e < nv_max, g, nblk, row_bytes, nk[f],
-                             ns[f]);
+        for (int f = 0; f < kFrag; ++f) {
+          const int e = e_frag0 + 16 * kFrag + f * 16 + col;
+          load_b<kKS, kStream>(rc, re, c_bytes, e_bytes, real_entry(e), more && e < nv_max, g, nblk, row_bytes,
+                               nk[f], ns[f]);
+        }
       }
     }
     // every MFMA of the batch first, into its own accumulator; entries past
