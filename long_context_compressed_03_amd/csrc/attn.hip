@@ -45,7 +45,9 @@ namespace {
 
 constexpr int kNK = 64;                       // keys per chunk
 constexpr int kThreads = 512;                 // 8 waves
-constexpr int kKRow = kHeadDim + 8;           // bf16 per K row in LDS
+constexpr int kKRow = kHeadDim + 16;          // bf16 per K row in LDS (288-byte rows: the
+                                              // K fragment reads are free of bank conflicts,
+                                              // measured; 272-byte rows cost 4 cycles a read)
 constexpr int kVRow = kNK + 16;               // bf16 per V^T row in LDS
 constexpr int kVGroup = 8 * kVRow + 8;         // bf16 per group of 8 V^T rows (rows, then a pad)
 constexpr int kFRow = kHeadDim + 4;           // fp32 per K/V row in LDS (fp32 path)
@@ -253,12 +255,22 @@ CSA_DEV void part_f32(const u32x4* w, int src, int h, float* x) {
   }
 }
 
+// Position of key `kk` of a chunk in a V^T row.  A P*V operand lane (column
+// group g of 32-key step st) takes keys 32 st + 4 g .. +3 and 32 st + 16 + 4 g
+// .. +3 (the key order of S^T's C layout); they are stored side by side at
+// 32 st + 8 g .. +7, so the lane reads them as one 16-byte word.  Key pairs
+// (2i, 2i + 1) stay adjacent.
+CSA_DEV int vt_key_pos(int kk) {
+  return (kk & ~31) + 8 * ((kk & 15) >> 2) + 4 * ((kk >> 4) & 1) + (kk & 3);
+}
+
 // LDS layout of one chunk
 struct LdsBf16 {
   uint16_t K[kNK][kKRow];
-  // V^T, head dim x key: rows of 40 words, 4 words of pad after every 8 rows.
-  // A wave's writes (16 row groups x 4 key pairs) then fall in distinct
-  // banks and the 8-byte reads of the P*V products take two passes.
+  // V^T, head dim x key (keys at vt_key_pos): rows of 40 words, 4 words of
+  // pad after every 8 rows.  Measured bank conflicts per wave instruction:
+  // 2 cycles for the transposed key-pair writes, 4 for the 16-byte operand
+  // reads (8 with the keys in order, read as two 8-byte halves).
   uint16_t Vt[kHeadDim / 8][kVGroup];
   // per key: K scale x logit scale, V scale, and 0 (present) or -inf (absent:
   // its K row is zeros, so logit = product * sk + bias needs no branch)
@@ -354,7 +366,7 @@ CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr, float sk_mul) {
     // V^T: head dim x of keys 2kp and 2kp+1 as one bf16 pair
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      uint16_t* vt = &s.Vt[dg][2 * x * kVRow + 2 * kp];   // rows 8 dg + 2x and 8 dg + 2x + 1
+      uint16_t* vt = &s.Vt[dg][2 * x * kVRow + vt_key_pos(2 * kp)];   // rows 8 dg + 2x and 8 dg + 2x + 1
       *reinterpret_cast<uint32_t*>(vt) = (vw[0][x] & 0xFFFFu) | (vw[1][x] << 16);
       *reinterpret_cast<uint32_t*>(vt + kVRow) = (vw[0][x] >> 16) | (vw[1][x] & 0xFFFF0000u);
     }
@@ -560,10 +572,8 @@ void attn_kernel(AttnArgs a) {
           // 128-VGPR budget (two blocks per CU): one V^T fragment at a time
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) {
-            const uint16_t* vt = &s.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0];   // row dt*16 + col
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vt);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + 16);
-            const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+            // row dt*16 + col, keys k0 .. k0+3 and k0+16 .. k0+19 (one 16-byte word)
+            const u32x4 vf = *reinterpret_cast<const u32x4*>(&s.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0 + 4 * g]);
             o[ht][dt] = mfma_k32(vf, pbh, o[ht][dt]);
             o[ht][dt] = mfma_k32(vf, pbl, o[ht][dt]);
           }
@@ -572,10 +582,8 @@ void attn_kernel(AttnArgs a) {
           u32x4 vf[8];
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) {
-            const uint16_t* vt = &s.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0];   // row dt*16 + col
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vt);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + 16);
-            vf[dt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            // row dt*16 + col, keys k0 .. k0+3 and k0+16 .. k0+19 (one 16-byte word)
+            vf[dt] = *reinterpret_cast<const u32x4*>(&s.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0 + 4 * g]);
           }
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) o[ht][dt] = mfma_k32(vf[dt], pbh, o[ht][dt]);
@@ -1030,10 +1038,8 @@ void attn_decode_kernel(AttnArgs a, int kT, int n_groups, long n_units) {
     u32x4 vf[8];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const uint16_t* vt = &s.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0];   // row dt*16 + col
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(vt);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + 16);
-      vf[dt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      // row dt*16 + col, keys k0 .. k0+3 and k0+16 .. k0+19 (one 16-byte word)
+      vf[dt] = *reinterpret_cast<const u32x4*>(&s.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0 + 4 * g]);
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[dt] = mfma_k32(vf[dt], pbh, o[dt]);
@@ -1441,10 +1447,8 @@ __global__ __launch_bounds__(kThreads) void attn_mq_kernel(AttnArgs a) {
       const u32x4 pl1 = {pl[1][st][0], pl[1][st][1], pl[1][st][2], pl[1][st][3]};
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const uint16_t* vt = &c.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0];   // row dt*16 + col
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vt);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + 16);
-        const u32x4 vf = {lo[0], lo[1], hi[0], hi[1]};
+        // row dt*16 + col, keys k0 .. k0+3 and k0+16 .. k0+19 (one 16-byte word)
+        const u32x4 vf = *reinterpret_cast<const u32x4*>(&c.Vt[2 * dt + (col >> 3)][(col & 7) * kVRow + k0 + 4 * g]);
         if constexpr (kF16) {
           o[0][dt] = mfma_h32(vf, pb0, o[0][dt]);
           o[1][dt] = mfma_h32(vf, pb1, o[1][dt]);
