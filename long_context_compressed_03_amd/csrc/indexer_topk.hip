@@ -958,16 +958,26 @@ __global__ __launch_bounds__(kTThreads) void cand_threshold_kernel(const uint16_
   if (tid == 0) thr[row] = __float_as_uint(key_score(key16 << 16));
 }
 
-// LDS of cand_select_kernel: the radix histograms, then per group of 8
-// bitmap words the selected entries before it, then the bitmap of the
-// selected entries (both sized for the call's capacity).
+// LDS of cand_select_kernel: the radix histograms, then the bitmap of the
+// selected entries (whole groups of 8 words, 16-byte aligned), then per
+// group the selected entries before it (both sized for the call's capacity).
 struct CandSelLds {
   RadixLds rx;
   uint32_t red[kTThreads / 64];
 };
+static_assert(sizeof(CandSelLds) % 16 == 0, "the bitmap after it is read as 16-byte words");
 size_t cand_select_lds(int cap) {
   const size_t words = (size_t(cap) + 31) / 32, groups = (words + 7) / 8;
-  return sizeof(CandSelLds) + groups * 4 + words * 4;
+  return sizeof(CandSelLds) + groups * 8 * 4 + groups * 4;
+}
+constexpr int kGroupsPerThread = (kCandMaxCap / 32 / 8 + kTThreads - 1) / kTThreads;   // bitmap groups a thread scans
+
+// Set bits of an 8-word bitmap group.
+CSA_DEV uint32_t group_popc(const uint32_t* g8) {
+  const u32x4 a = *reinterpret_cast<const u32x4*>(g8);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(g8 + 4);
+  return __popc(a[0]) + __popc(a[1]) + __popc(a[2]) + __popc(a[3]) + __popc(b[0]) + __popc(b[1]) + __popc(b[2]) +
+         __popc(b[3]);
 }
 
 __global__ __launch_bounds__(kTThreads) void cand_select_kernel(const uint2* __restrict__ cand,
@@ -979,9 +989,9 @@ __global__ __launch_bounds__(kTThreads) void cand_select_kernel(const uint2* __r
   constexpr int kPer = csa_ix::kCandCap / kTThreads;
   extern __shared__ __attribute__((aligned(16))) unsigned char cs_smem[];
   CandSelLds& sh = *reinterpret_cast<CandSelLds*>(cs_smem);
-  const int cap_words = (cap + 31) / 32;
-  uint32_t* pre = reinterpret_cast<uint32_t*>(cs_smem + sizeof(CandSelLds));
-  uint32_t* bits = pre + (cap_words + 7) / 8;
+  const int cap_groups = ((cap + 31) / 32 + 7) / 8;
+  uint32_t* bits = reinterpret_cast<uint32_t*>(cs_smem + sizeof(CandSelLds));
+  uint32_t* pre = bits + cap_groups * 8;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   int b, i;
@@ -1020,19 +1030,24 @@ __global__ __launch_bounds__(kTThreads) void cand_select_kernel(const uint2* __r
   // the selected entries as a bitmap, then each one's rank among them
   auto chosen = [&](int x) { return valid(x) && (key[x] > K || (key[x] == K && ent[x] <= I)); };
   const int n_words = (nv + 31) / 32;
-  for (int w = tid; w < n_words; w += kTThreads) bits[w] = 0u;
+  const int n_groups = (n_words + 7) / 8;
+  for (int w = tid; w < n_groups * 8; w += kTThreads) bits[w] = 0u;
   __syncthreads();
 #pragma unroll
   for (int x = 0; x < kPer; ++x)
     if (chosen(x)) atomicOr(&bits[ent[x] >> 5], 1u << (ent[x] & 31u));
   __syncthreads();
-  // groups of 8 words: thread tid sums groups tid, tid + 256, ... (contiguous
-  // per thread: groups [tid * per, (tid + 1) * per))
-  const int n_groups = (n_words + 7) / 8;
+  // groups of 8 words: thread tid counts groups [tid * per, (tid + 1) * per)
+  // (per <= kGroupsPerThread), each group read as two 16-byte words
   const int per = (n_groups + kTThreads - 1) / kTThreads;
+  uint32_t gc[kGroupsPerThread];
   uint32_t mine = 0u;
-  for (int gi = tid * per; gi < min((tid + 1) * per, n_groups); ++gi)
-    for (int w = gi * 8; w < min(gi * 8 + 8, n_words); ++w) mine += __popc(bits[w]);
+#pragma unroll
+  for (int q = 0; q < kGroupsPerThread; ++q) {
+    const int gi = tid * per + q;
+    gc[q] = q < per && gi < n_groups ? group_popc(bits + gi * 8) : 0u;
+    mine += gc[q];
+  }
   uint32_t incl = mine;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -1043,19 +1058,28 @@ __global__ __launch_bounds__(kTThreads) void cand_select_kernel(const uint2* __r
   __syncthreads();
   uint32_t run = incl - mine;
   for (int w = 0; w < (tid >> 6); ++w) run += sh.red[w];
-  for (int gi = tid * per; gi < min((tid + 1) * per, n_groups); ++gi) {
-    pre[gi] = run;
-    for (int w = gi * 8; w < min(gi * 8 + 8, n_words); ++w) run += __popc(bits[w]);
+#pragma unroll
+  for (int q = 0; q < kGroupsPerThread; ++q) {
+    const int gi = tid * per + q;
+    if (q < per && gi < n_groups) pre[gi] = run;
+    run += gc[q];
   }
   __syncthreads();
+  // each selected entry's rank: the selected entries of the groups before
+  // its group, then of the words before its word, then of the bits below it
 #pragma unroll
   for (int x = 0; x < kPer; ++x) {
     if (chosen(x)) {
       const uint32_t e = ent[x];
       const int w = int(e >> 5);
-      const int g0 = (w >> 3) << 3;
+      const uint32_t* g8 = bits + (w & ~7);
+      const u32x4 a = *reinterpret_cast<const u32x4*>(g8);
+      const u32x4 c = *reinterpret_cast<const u32x4*>(g8 + 4);
+      const uint32_t word[8] = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+      const int wi = w & 7;
       uint32_t slot = pre[w >> 3];
-      for (int y = g0; y < w; ++y) slot += __popc(bits[y]);
+#pragma unroll
+      for (int y = 0; y < 8; ++y) slot += y < wi ? __popc(word[y]) : 0u;
       slot += __popc(bits[w] & ((1u << (e & 31u)) - 1u));
       out[slot] = int32_t(e);
     }
