@@ -53,7 +53,7 @@ constexpr int kBlockCand = 256;
 //   gate   (any mode) null, or a flag: the launch does nothing while it is 0
 //   thr    (kCand) per row: the 32-bit order-preserving key a candidate reaches
 //   cnt    (kCand) per row: candidates found (atomic; past kCandCap: overflow)
-//   cand   (kCand) per row: kCandCap (key, entry) pairs, in no particular order
+//   cand   (kCand) per row: kCandCap (score bits, entry) pairs, in no particular order
 //   wave_entries  (batched launches) about how many entries a wave walks; 0: kWaveEntries
 struct IxExtra {
   const uint32_t* gate;
@@ -327,18 +327,22 @@ __global__ __launch_bounds__(kBlock) void indexer_kernel(const uint8_t* __restri
     __syncthreads();
   }
   auto put = [&](int rt, int e, float p) {
-    if (q_in[rt] && e < e_wave1) {
+    if constexpr (kOut == kCand) {
+      // a float compare (the threshold is a score whose key is the row's
+      // 32-bit threshold key: same order, -0 == +0 included).  Visibility
+      // alone bounds the test: a lane of a query past T_q sees no entry, and
+      // a batch (64 entries, walks of whole batches) never crosses into the
+      // next wave's walk.  The score's bits are staged; the selection turns
+      // them into order-preserving keys.
+      if (e < nv_lane[rt] && p >= thr[rt]) {
+        const int lr = q_of(rt, 4 * g);   // the query's slot among the block's rows
+        const uint32_t slot = atomicAdd(&cl.n[lr], 1u);
+        if (slot < uint32_t(kBlockCand)) cl.item[lr][slot] = make_uint2(__float_as_uint(p), uint32_t(e));
+      }
+    } else if (q_in[rt] && e < e_wave1) {
       const bool vis = e < nv_lane[rt];
       if constexpr (kOut == kScoresF32) {
         static_cast<float*>(out)[orow[rt] + e] = vis ? p : -INFINITY;
-      } else if constexpr (kOut == kCand) {
-        // a float compare (the threshold is a score whose key is the
-        // row's 32-bit threshold key: same order, -0 == +0 included)
-        if (vis && p >= thr[rt]) {
-          const int lr = q_of(rt, 4 * g);   // the query's slot among the block's rows
-          const uint32_t slot = atomicAdd(&cl.n[lr], 1u);
-          if (slot < uint32_t(kBlockCand)) cl.item[lr][slot] = make_uint2(csa_sel::ordered_key(p), uint32_t(e));
-        }
       } else {
         static_cast<uint16_t*>(out)[orow[rt] + e] = vis ? uint16_t(csa_sel::ordered_key(p) >> 16) : uint16_t(0);
       }

@@ -1014,7 +1014,7 @@ __global__ __launch_bounds__(kTThreads) void cand_select_kernel(const uint2* __r
   for (int x = 0; x < kPer; ++x) {
     const int j = tid + x * kTThreads;
     const uint2 c = j < int(n) ? src[j] : make_uint2(0u, 0xFFFFFFFFu);
-    key[x] = c.x;
+    key[x] = j < int(n) ? csa_sel::ordered_key(__uint_as_float(c.x)) : 0u;   // staged as score bits
     ent[x] = c.y;
   }
   auto valid = [&](int x) { return tid + x * kTThreads < int(n); };
