@@ -183,3 +183,34 @@ def test_fused_equals_unfused_on_inexact_scores(csa, B, T, cap, k, pos):
     got = h(csa.csa_indexer_topk(*d, t_i32(pos), m, k))
     torch.cuda.synchronize()
     assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
+
+
+@pytest.mark.parametrize("cap,cluster,k", [
+    (60000, 600, 500),     # the cluster overflows its (block, row) candidate staging: fallback path
+    (200000, 100, 60),     # the cluster fits the staging: the selection resolves the tie class
+])
+def test_fused_clustered_candidates(csa, cap, cluster, k):
+    """Chunk rows on the threshold path whose best entries sit together: rows 0 and 1
+    have an all-ones query (w = 1), so a run of `cluster` consecutive keys with every
+    element 24 scores the maximum, all tied, and the rest score by their random keys.  With
+    600 such entries one block of the candidate pass finds more than its staging
+    holds and the row must take the full fallback; with 100 they fit and the
+    selection orders the tie class by entry.  Row 2 has a random query."""
+    say(f"indexer_topk clustered candidates cap={cap} cluster={cluster} k={k}")
+    B, T, H_I, d_I, m = 1, 3, 4, 64, 4
+    x = indexer_inputs(B, T, cap, H_I, d_I, seed=cap + cluster)
+    x["q_codes"][0, :2] = 0x22                               # rows 0, 1: every element +1
+    x["q_e8m0"][0, :2] = 127
+    x["w"][0, :2] = 1.0
+    kc = x["k_codes"].copy()
+    ke = x["k_e8m0"].copy()
+    c0 = 20100
+    kc[0, c0:c0 + cluster] = 0x77                            # the cluster: every element 6 * 2^2,
+    ke[0, c0:c0 + cluster] = 129                             # above any random key's sum
+    x2 = dict(x, k_codes=kc, k_e8m0=ke)
+    pos = np.array([4 * cap - 4], np.int32)
+    s = indexer_scores(x2["q_codes"], x2["q_e8m0"], x2["w"], kc, ke, pos, m)
+    ref = topk(s.astype(np.float32), pos, m, k)
+    assert np.array_equal(ref[0, 0], np.arange(c0, c0 + k))   # the lowest-index k of the tied cluster
+    got = _fused(csa, x2, pos, m, k)
+    assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
