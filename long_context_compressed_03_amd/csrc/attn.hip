@@ -233,6 +233,33 @@ CSA_DEV void prefetch(const AttnArgs& a, Pre<kIO>& pr, const int (&e)[2], int b,
   }
 }
 
+// Rows of the item's two slots of a chunk made of selected-entry slots only
+// (sparse lists, slots below k): the rows come straight from the indices,
+// with no source selects; an empty slot (-1, or an index past cap) reads
+// entry 0 of its sequence and is masked by its bias (src 0), so its finite
+// values contribute exactly nothing.  Requires cap > 0.
+template <int kCKV>
+CSA_DEV void prefetch_sel(const AttnArgs& a, Pre<CSA_BF16>& pr, const int (&e)[2], int b) {
+  constexpr long kCB = kCKV == CSA_BF16 ? 2 : 1;   // bytes per compressed value (bf16 or fp8)
+  const int dg = item_dg();
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const bool ok = unsigned(e[x]) < unsigned(a.cap);
+    const long row = long(b) * a.cap + (ok ? e[x] : 0);
+    const long off = row * (kHeadDim * kCB) + (kCKV == CSA_FP8_E4M3 ? long(dg & ~1) * 8 : long(dg) * 8 * kCB);
+    pr.k[x][0] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.ck) + off);
+    pr.v[x][0] = *reinterpret_cast<const u32x4*>(static_cast<const char*>(a.cv) + off);
+    if constexpr (kCKV == CSA_FP8_E4M3) {
+      pr.sk[x] = a.ck_scale[row];
+      pr.sv[x] = a.cv_scale[row];
+    } else {
+      pr.sk[x] = 1.f;
+      pr.sv[x] = 1.f;
+    }
+    pr.src[x] = ok ? 1 : 0;
+  }
+}
+
 // 8 values of a gathered part as fp32 (src 0 -> zeros)
 template <int kIO, int kCKV>
 CSA_DEV void part_f32(const u32x4* w, int src, int h, float* x) {
@@ -347,8 +374,12 @@ CSA_DEV u32x4 part_f16_fp8(const u32x4* w, int h) {
 // kAll (bf16 path): the item's slots are compressed entries (prefetch_entries);
 // with fp8 entries V^T is then stored as fp16 (exact) for the one-product
 // P*V of the many-query kernel.
-template <int kIO, int kCKV, bool kAll = false>
+// kVF16 (all-entries chunks of fp8 entries in the many-query kernel): V^T as
+// fp16 instead of bf16.  kSrcBias: an empty slot (src 0) gets the -inf bias
+// (an all-entries chunk of the many-query kernel has none).
+template <int kIO, int kCKV, bool kAll = false, bool kVF16 = kAll && kCKV == CSA_FP8_E4M3, bool kSrcBias = !kAll>
 CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr, float sk_mul) {
+  static_assert(!kVF16 || (kAll && kCKV == CSA_FP8_E4M3), "fp16 V^T holds fp8 entries only");
   const int kp = item_kp();
   const int dg = item_dg();
   if constexpr (kIO == CSA_BF16) {
@@ -357,7 +388,7 @@ CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr, float sk_mul) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       kw[e] = part_bf16<kCKV, kAll>(pr.k[e], pr.src[e], dg & 1);
-      if constexpr (kAll && kCKV == CSA_FP8_E4M3)
+      if constexpr (kVF16)
         vw[e] = part_f16_fp8(pr.v[e], dg & 1);
       else
         vw[e] = part_bf16<kCKV, kAll>(pr.v[e], pr.src[e], dg & 1);
@@ -391,7 +422,7 @@ CSA_DEV void store_chunk(LdsChunk<kIO>& s, const Pre<kIO>& pr, float sk_mul) {
       const bool scaled = kCKV == CSA_FP8_E4M3 && (kAll || pr.src[e] == 1);
       s.sk[2 * kp + e] = (scaled ? pr.sk[e] : 1.f) * sk_mul;
       s.sv[2 * kp + e] = scaled ? pr.sv[e] : 1.f;
-      s.bias[2 * kp + e] = kAll || pr.src[e] != 0 ? 0.f : -INFINITY;
+      s.bias[2 * kp + e] = !kSrcBias || pr.src[e] != 0 ? 0.f : -INFINITY;
     }
   }
 }
@@ -610,11 +641,23 @@ void attn_kernel(AttnArgs a) {
   // Indices run one round of chunks ahead of the rows they name.
   Pre<kIO> pr[kDepth];
   int e_nx[kDepth][2];
+  // kSel (sparse lists, bf16 queries, one chunk in flight, no fold): chunks
+  // [j_begin, j_sel) hold selected-entry slots only and take prefetch_sel and
+  // the select-free store_chunk; the rest (the window) the general path
+  constexpr bool kSel = !kDense && kIO == CSA_BF16 && kDepth == 1 && !kFold;
+  const int j_sel = kSel && a.cap > 0 ? j_begin + max(0, min(a.k, j_end) - j_begin) / kNK * kNK : j_begin;
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) load_idx<kDense>(a, e_nx[d], qrow, j_begin + d * kNK, j_end);
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) {
-    prefetch<kIO, kCKV, kDense>(a, pr[d], e_nx[d], b, t, raw0, j_begin + d * kNK, j_end);
+    if constexpr (kSel) {
+      if (j_begin < j_sel)
+        prefetch_sel<kCKV>(a, pr[d], e_nx[d], b);
+      else
+        prefetch<kIO, kCKV, kDense>(a, pr[d], e_nx[d], b, t, raw0, j_begin + d * kNK, j_end);
+    } else {
+      prefetch<kIO, kCKV, kDense>(a, pr[d], e_nx[d], b, t, raw0, j_begin + d * kNK, j_end);
+    }
     load_idx<kDense>(a, e_nx[d], qrow, j_begin + (d + kDepth) * kNK, j_end);
   }
   // The state of the keys walked since the last piece start: the second key
@@ -685,7 +728,23 @@ void attn_kernel(AttnArgs a) {
       }
     }
   }
-  for (int j0 = j_begin; j0 < j_end; j0 += kDepth * kNK) {
+  int j_gen = j_begin;   // first chunk of the general walk
+  if constexpr (kSel) {
+    // selected-entry chunks, each stored as it was fetched (the next one's
+    // form follows its own position)
+    for (; j_gen < j_sel; j_gen += kNK) {
+      __syncthreads();
+      store_chunk<kIO, kCKV, true, false, true>(s, pr[0], a.sm_log2);
+      __syncthreads();
+      if (j_gen + kNK < j_sel)
+        prefetch_sel<kCKV>(a, pr[0], e_nx[0], b);
+      else
+        prefetch<kIO, kCKV, kDense>(a, pr[0], e_nx[0], b, t, raw0, j_gen + kNK, j_end);
+      load_idx<kDense>(a, e_nx[0], qrow, j_gen + 2 * kNK, j_end);
+      compute();
+    }
+  }
+  for (int j0 = j_gen; j0 < j_end; j0 += kDepth * kNK) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
       if (d > 0 && j0 + d * kNK >= j_end) break;
