@@ -41,10 +41,7 @@ CSA_DEV_HOST_INLINE int sampled_count(int n) {   // sampled entries below n
   return (n / kSampleGroup) * 16 + (n % kSampleGroup < 16 ? n % kSampleGroup : 16);
 }
 // Entries a wave walks in the batched (non-streaming) launches, about.
-#ifndef CSA_IX_WAVE_ENTRIES
-#define CSA_IX_WAVE_ENTRIES 2048
-#endif
-constexpr int kWaveEntries = CSA_IX_WAVE_ENTRIES;
+constexpr int kWaveEntries = 2048;
 // Candidate slots per row of the threshold pass, and per (block, row) in LDS.
 constexpr int kCandCap = 8192;
 constexpr int kBlockCand = 256;
