@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from csa_synth import (attn_inputs, compress_inputs, indexer_inputs, random_scores,
-                       random_topk_idx)
+                       random_topk_idx, streams)
 from gpu_helpers import (attention_tolerance, compress_tolerance, exact_equal, h, h_bf16, say, t_bf16,
                          t_f32, t_i32, t_kv, t_u8)
 from oracle.attention import decode_kv, dense_attn, sparse_attn
@@ -450,3 +450,33 @@ def test_layer_pair_small(csa):
     d2 = np.abs(_out_host(oh, "bf16") - Oh)
     say(f"  CSA err {d1.max():.2e}, HCA err {d2.max():.2e} (|O| up to {np.abs(Oc).max():.1f})")
     assert np.all(d1 <= attention_tolerance(Oc, "bf16")) and np.all(d2 <= attention_tolerance(Oh, "bf16"))
+
+
+@pytest.mark.parametrize("io,ckv", [("bf16", "fp8"), ("bf16", "bf16")])
+def test_sparse_attn_empty_slots_anywhere(csa, io, ckv):
+    """Empty slots (-1) are not only a tail: a caller's list may leave any slot
+    empty, even in rows that see more than k entries.  Chunks of selected-entry
+    slots are gathered straight from the indices, so their empty slots must
+    still drop out (scattered -1s, a whole 64-slot chunk of them, and a row
+    whose list is empty but for its window)."""
+    say(f"sparse empty slots anywhere io={io} ckv={ckv}")
+    B, T, H, cap, k, W, L_raw, m = 1, 3, 64, 2000, 256, 128, 130, 4
+    pos = np.array([4 * cap - 3], np.int32)
+    raw0 = (pos + T - L_raw).astype(np.int32)
+    x = attn_inputs(B, T, H, cap, L_raw, io, ckv, seed=31)
+    nv = np.minimum(nvis(pos[:, None] + np.arange(T)[None], m), cap)
+    idx = random_topk_idx(nv, k, cap, seed=7)
+    assert np.all(idx >= 0)                             # every row sees more than k entries
+    (r,) = streams(123, 7, 1)
+    idx[0, 0, r.choice(k, size=40, replace=False)] = -1  # scattered empty slots
+    idx[0, 1, 64:128] = -1                              # a whole chunk of them
+    idx[0, 2, :] = -1                                   # only the window remains
+    q, cK, cV, Kw, Vw = _oracle_kv(x, io, ckv)
+    O, lse = sparse_attn(q, cK, cV, idx, Kw, Vw, raw0, pos, W)
+    dq, ck, cv, cks, cvs, kw, vw = _attn_inputs_dev(x, io, ckv)
+    out = csa.csa_sparse_attn(dq, ck, cv, t_i32(idx), kw, vw, t_i32(raw0), t_i32(pos), W,
+                              ck_scale=cks, cv_scale=cvs)
+    torch.cuda.synchronize()
+    diff = np.abs(_out_host(out, io) - O)
+    say(f"  max-abs err {diff.max():.3e}")
+    assert np.all(diff <= attention_tolerance(O, io))
